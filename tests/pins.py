@@ -1,0 +1,243 @@
+"""Property checks that pin the CPU oracle to facts outside itself.
+
+Each check returns (ok, detail).  They are used by test_oracle_pins.py on the oracle as
+written, and by the mutation tests on deliberately broken copies of it, which must fail
+at least one check.  None of them re-types the oracle's own formulas: they compare with
+closed forms (logsumexp / softmax over a node's whole span via SciPy), textbook routines
+(torch scaled_dot_product_attention), brute force, and the geometry the pages state.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import scipy.special as sp
+import torch
+
+from oracle import zha_oracle as zo
+
+
+def rand_tree(rng, n=203, d=8, r=3, b=4, levels=3, scale=1.0):
+    keys = rng.standard_normal((n, d)) * scale
+    refs = rng.standard_normal((r, d))
+    return zo.build_tree(keys, refs, b, levels, n), keys, refs
+
+
+def span(tree, level, node):
+    b = tree.block ** level
+    return np.arange(node * b, min((node + 1) * b, tree.n_tokens))
+
+
+def true_lse(keys, q, toks):
+    return sp.logsumexp(keys[toks] @ q / math.sqrt(q.shape[0]))
+
+
+# P2: every plane (hence the max over planes) lower-bounds the node's true log mass.
+def check_convexity(seed=0, n_q=20):
+    rng = np.random.default_rng(seed)
+    tree, keys, _ = rand_tree(rng)
+    worst = -np.inf
+    for lv in range(1, tree.n_levels + 1):
+        nodes = np.arange(tree.nodes(lv))
+        for _ in range(n_q):
+            q = rng.standard_normal(keys.shape[1]) * 3
+            sc = zo.node_scores(tree, lv, nodes, q)
+            tl = np.array([true_lse(keys, q, span(tree, lv, n)) for n in nodes])
+            worst = max(worst, np.max(sc - tl - 1e-12 * np.maximum(1, np.abs(tl))))
+    return worst <= 0, f"max(score - true LSE) = {worst:.3e}"
+
+
+# P3: plane j is exact at q = r_j (level 1 required; every level by the recursion).
+def check_exact_at_refs(seed=1):
+    rng = np.random.default_rng(seed)
+    tree, keys, refs = rand_tree(rng)
+    d = keys.shape[1]
+    worst = 0.0
+    for lv in range(1, tree.n_levels + 1):
+        s, c = tree.levels[lv - 1]
+        for n in range(tree.nodes(lv)):
+            for j in range(refs.shape[0]):
+                plane = refs[j] @ s[n, j] / math.sqrt(d) + c[n, j]
+                score = zo.node_scores(tree, lv, np.array([n]), refs[j])[0]
+                tl = true_lse(keys, refs[j], span(tree, lv, n))
+                worst = max(worst, abs(plane - tl), abs(score - tl))
+    return worst < 1e-10, f"max |plane_j(r_j) - LSE_j| = {worst:.3e}"
+
+
+# P4: recursion equals the direct per-span definition (softmax-weighted mean key, LSE).
+def check_recursion_direct(seed=2):
+    rng = np.random.default_rng(seed)
+    tree, keys, refs = rand_tree(rng, n=300, b=3, levels=4)
+    d = keys.shape[1]
+    worst = 0.0
+    for lv in range(1, tree.n_levels + 1):
+        s, c = tree.levels[lv - 1]
+        for n in range(tree.nodes(lv)):
+            toks = span(tree, lv, n)
+            for j in range(refs.shape[0]):
+                z = keys[toks] @ refs[j] / math.sqrt(d)
+                w = sp.softmax(z)
+                s_dir = w @ keys[toks]
+                lse_dir = sp.logsumexp(z)
+                lse = c[n, j] + refs[j] @ s[n, j] / math.sqrt(d)
+                worst = max(worst, np.max(np.abs(s[n, j] - s_dir)), abs(lse - lse_dir))
+    return worst < 1e-10, f"max |recursive - direct| = {worst:.3e}"
+
+
+# P5: single-key nodes are exact: s_j = k, c_j = 0, score = sigma q.k.
+def check_single_key(seed=3):
+    rng = np.random.default_rng(seed)
+    d = 8
+    keys = rng.standard_normal((37, d))
+    refs = rng.standard_normal((3, d))
+    t1 = zo.build_tree(keys, refs, 1, 1, 37)           # b = 1: every block one key
+    t4 = zo.build_tree(keys, refs, 4, 1, 37)           # last block of b = 4 holds one key
+    q = rng.standard_normal(d)
+    s1, c1 = t1.levels[0]
+    worst = max(np.max(np.abs(s1 - keys[:, None, :])), np.max(np.abs(c1)))
+    sc = zo.node_scores(t1, 1, np.arange(37), q)
+    worst = max(worst, np.max(np.abs(sc - keys @ q / math.sqrt(d))))
+    s4, c4 = t4.levels[0]
+    worst = max(worst, np.max(np.abs(s4[-1] - keys[36])), np.max(np.abs(c4[-1])))
+    return worst < 1e-12, f"max single-key error = {worst:.3e}"
+
+
+# P6: b = 1, L = 1 is textbook nucleus selection over the true attention distribution.
+def check_nucleus(seed=4, p=0.8):
+    rng = np.random.default_rng(seed)
+    d, n = 16, 200
+    keys = rng.standard_normal((n, d))
+    refs = rng.standard_normal((2, d))
+    tree = zo.build_tree(keys, refs, 1, 1, n)
+    bad = 0
+    for _ in range(10):
+        q = rng.standard_normal(d) * 4
+        probs = sp.softmax(keys @ q / math.sqrt(d))
+        idx = np.argsort(-probs, kind="stable")
+        k = int(np.searchsorted(np.cumsum(probs[idx]), p)) + 1
+        expect = np.union1d([0], idx[:k])
+        got = zo.route(tree, q, p)["tokens"]
+        bad += not np.array_equal(np.sort(expect), got)
+    return bad == 0, f"{bad} of 10 queries differ from nucleus selection"
+
+
+# P7: the kept set is minimal (brute force over all subsets) and heaviest among minimal sets.
+def check_minimal(seed=5, trials=40):
+    rng = np.random.default_rng(seed)
+    fails = 0
+    for t in range(trials):
+        f = int(rng.integers(1, 13))
+        scores = rng.standard_normal(f) * rng.uniform(0.1, 4)
+        if t % 5 == 0:
+            scores = np.round(scores)                     # force ties
+        frontier = np.sort(rng.choice(1000, size=f, replace=False))
+        p = float(rng.choice([0.3, 0.75, 0.95, 0.999, 1.0]))
+        probs = sp.softmax(scores)
+        best_k, best_mass = None, -1.0
+        for k in range(1, f + 1):
+            masses = [probs[list(c)].sum() for c in itertools.combinations(range(f), k)]
+            mx = max(masses)
+            if p >= 1.0:
+                if k == f:
+                    best_k, best_mass = k, mx
+            elif mx >= p - 1e-12:
+                best_k, best_mass = k, mx
+                break
+        sel = zo.top_p(frontier, scores, p)
+        kept_mass = probs[np.isin(frontier, sel["kept"])].sum()
+        if sel["k"] != best_k or abs(kept_mass - best_mass) > 1e-12:
+            fails += 1
+    return fails == 0, f"{fails} of {trials} frontiers not minimal/heaviest"
+
+
+# P8: mass conservation at every level.
+def check_mass_conservation(seed=6):
+    rng = np.random.default_rng(seed)
+    tree, keys, refs = rand_tree(rng, n=259, b=4, levels=4)
+    d = keys.shape[1]
+    worst = 0.0
+    for lv in range(1, tree.n_levels + 1):
+        s, c = tree.levels[lv - 1]
+        lse = c + np.einsum("nrd,rd->nr", s, refs) / math.sqrt(d)
+        for j in range(refs.shape[0]):
+            z = keys @ refs[j] / math.sqrt(d)
+            a = sp.logsumexp(lse[:, j])
+            b = sp.logsumexp(z)
+            m1 = np.exp(lse[:, j] - b) @ s[:, j]
+            m2 = np.exp(z - b) @ keys
+            worst = max(worst, abs(a - b), np.max(np.abs(m1 - m2)))
+    return worst < 1e-10, f"max conservation error = {worst:.3e}"
+
+
+# P9: build(N) + m appends equals build(N + m).
+def check_append(seed=7, n0=61, m=70, b=4, levels=4):
+    rng = np.random.default_rng(seed)
+    d = 8
+    keys = rng.standard_normal((n0 + m, d))
+    refs = rng.standard_normal((3, d))
+    t = zo.build_tree(keys.copy(), refs, b, levels, n0)
+    for i in range(m):
+        zo.append_token(t, keys[n0 + i])
+    full = zo.build_tree(keys, refs, b, levels, n0 + m)
+    worst = 0.0
+    for (sa, ca), (sb, cb) in zip(t.levels, full.levels):
+        if sa.shape != sb.shape:
+            return False, f"level shapes {sa.shape} vs {sb.shape}"
+        worst = max(worst, np.max(np.abs(sa - sb)), np.max(np.abs(ca - cb)))
+    return worst < 1e-12, f"max |append - rebuild| = {worst:.3e}"
+
+
+def _sdpa(keys, values, q, mask=None):
+    qt = torch.from_numpy(np.asarray(q, np.float64))[None, None, None, :]
+    kt = torch.from_numpy(np.asarray(keys, np.float64))[None, None]
+    vt = torch.from_numpy(np.asarray(values, np.float64))[None, None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None, None, :]
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m)[0, 0, 0].numpy()
+
+
+# P1: p = 1 reproduces dense attention (torch SDPA, float64 on the CPU).
+def check_dense_limit(seed=8):
+    rng = np.random.default_rng(seed)
+    hkv, hq, d, n = 2, 6, 16, 301
+    keys = rng.standard_normal((hkv, n, d))
+    vals = rng.standard_normal((hkv, n, d))
+    refs = rng.standard_normal((hkv, 3, d))
+    trees = [zo.build_tree(keys[h], refs[h], 4, 3, n) for h in range(hkv)]
+    q = rng.standard_normal((hq, d)) * 3
+    o = zo.decode(trees, vals, q, 1.0)
+    g = hq // hkv
+    ref = np.stack([_sdpa(keys[h // g], vals[h // g], q[h]) for h in range(hq)])
+    err = np.max(np.abs(o - ref))
+    return err < 1e-12, f"max |ZHA(p=1) - SDPA| = {err:.3e}"
+
+
+# P11: attention over a given set equals masked dense attention.
+def check_masked_attention(seed=9):
+    rng = np.random.default_rng(seed)
+    d, n = 16, 97
+    keys = rng.standard_normal((n, d))
+    vals = rng.standard_normal((n, d))
+    q = rng.standard_normal(d) * 2
+    toks = np.union1d([0], rng.choice(n, 30, replace=False))
+    mask = np.zeros(n, bool)
+    mask[toks] = True
+    err = np.max(np.abs(zo.attend(keys, vals, q, toks) - _sdpa(keys, vals, q, mask)))
+    return err < 1e-12, f"max |attend(S) - masked SDPA| = {err:.3e}"
+
+
+# Sink: token 0 is always attended, and only once.
+def check_sink(seed=10):
+    rng = np.random.default_rng(seed)
+    tree, keys, _ = rand_tree(rng, n=400)
+    ok = True
+    for _ in range(10):
+        q = rng.standard_normal(keys.shape[1]) * 4
+        toks = zo.route(tree, q, 0.5)["tokens"]
+        ok &= toks[0] == 0 and np.unique(toks).size == toks.size
+    return bool(ok), "sink present and unique"
+
+
+ALL = [check_dense_limit, check_convexity, check_exact_at_refs, check_recursion_direct,
+       check_single_key, check_nucleus, check_minimal, check_mass_conservation, check_append,
+       check_masked_attention, check_sink]
