@@ -1,0 +1,95 @@
+// Shared definitions of the ZHA HIP library (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zha {
+
+constexpr int MAXL = 16;        // max summary levels
+constexpr int GMAX = 8;         // max query heads per KV head (group size)
+constexpr int NB1 = 2048;       // coarse top-p bins over delta = max score - score
+constexpr float BINS_PER_UNIT = 64.f;   // coarse bins per unit of score (covers delta < 32)
+constexpr int NB2 = 2048;       // fine sub-bins inside the boundary coarse bin
+constexpr float MASS_SCALE = 1099511627776.0f;  // 2^40: fixed-point unit of probability mass
+constexpr int CAND_PAIRWISE = 256;  // boundary ties resolved pairwise in LDS up to this many
+constexpr int EXPAND_CHUNK = 1024;  // union-list entries per expand workgroup
+constexpr int MAX_SPLITS = 512;     // attention splits per KV head
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+struct bf16_t { uint16_t bits; };   // storage type of bfloat16 tensors
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x.bits << 16); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Order-preserving map float -> uint32 (a < b  <=>  key(a) < key(b)).
+__device__ __forceinline__ uint32_t f2key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Top-p binning of one score relative to the head's max: everything that decides a node's
+// fate goes through these two functions so every kernel takes the same decision.
+struct BinMass { uint32_t bin, sub; uint64_t mass; };
+__device__ __forceinline__ BinMass bin_mass(float score, float maxs) {
+  BinMass r;
+  float delta = maxs - score;                       // >= 0
+  float u = delta * BINS_PER_UNIT;
+  uint32_t bin = u < (float)(NB1 - 1) ? (uint32_t)u : (uint32_t)(NB1 - 1);
+  float frac = u - (float)bin;                      // in [0, 1) unless clamped
+  uint32_t sub = 0;
+  if (bin < (uint32_t)(NB1 - 1)) {
+    float f = frac * (float)NB2;
+    sub = f < (float)(NB2 - 1) ? (uint32_t)f : (uint32_t)(NB2 - 1);
+  }
+  r.bin = bin;
+  r.sub = sub;
+  r.mass = (uint64_t)(expf(-delta) * MASS_SCALE);   // in (0, 2^40]
+  return r;
+}
+
+// Per (level, query head) routing state.
+struct QState {
+  uint32_t maxkey;    // ordered key of the max score over the head's frontier
+  uint32_t b1;        // boundary coarse bin; NB1 => keep every frontier node
+  uint32_t b2;        // boundary fine sub-bin inside b1
+  uint32_t ncand;     // frontier nodes of this head that fell into bin b1
+  uint64_t total;     // sum of fixed-point masses (Z)
+  uint64_t target;    // ceil(p * Z): the kept prefix must reach this mass
+  uint64_t above1;    // mass of bins < b1
+  uint64_t above2;    // mass of bins < b1 and sub-bins < b2 of b1
+  uint32_t nties;     // nodes in (b1, b2)
+  uint32_t flags;     // bit 0: resolved through the radix path
+  uint32_t pad[2];
+};
+static_assert(sizeof(QState) == 64, "QState layout");
+
+// Device pointers of one handle's workspace (computed on the host).
+struct Dev {
+  // tree
+  float* s[MAXL + 1];       // level l: [Hkv][ncap[l]][R][D]
+  float* c[MAXL + 1];       // level l: [Hkv][ncap[l]][R]
+  float* lse[MAXL + 1];     // level l: [Hkv][ncap[l]][R] log mass at r_j (build/append only)
+  int64_t ncap[MAXL + 1];   // node capacity per level (index 0: gather list = ncap[1])
+  // router, per level l = 0..L (0 = kept level-1 blocks)
+  int32_t* node[MAXL + 1];  // [Hkv][ncap[l]]
+  uint32_t* mask[MAXL + 1]; // [Hkv][ncap[l]]
+  uint32_t* keep[MAXL + 1]; // [Hkv][ncap[l]]           (l >= 1)
+  float* score[MAXL + 1];   // [Hkv][GMAX][ncap[l]]     (l >= 1)
+  int32_t* part[MAXL + 1];  // [Hkv][nchunks(l)]        expand partial counts
+  int32_t* cnt;             // [MAXL + 1][Hkv]
+  QState* qs;               // [MAXL + 1][Hq]
+  uint64_t* mass1;          // [MAXL + 1][Hq][NB1]
+  uint64_t* mass2;          // [MAXL + 1][Hq][NB2]
+  int32_t* cand;            // [Hq][ncap[1]]
+  float* qf;                // [Hq][D] sigma * q in fp32
+  float* apart;             // [Hq][MAX_SPLITS][D + 2] attention partials (m, l, o)
+};
+
+}  // namespace zha

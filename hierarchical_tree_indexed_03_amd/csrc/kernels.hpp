@@ -1,0 +1,81 @@
+// Kernel argument blocks and host-side launchers of the ZHA HIP library.
+#pragma once
+#include "common.hpp"
+
+namespace zha {
+
+struct BuildArgs {
+  const void* K;      // [Hkv][cap][D]
+  const void* refs;   // [Hkv][R][D]
+  int64_t cap;
+  int64_t N;
+  int32_t b;
+  int32_t m;          // levels built inside one tile
+  float sigma;
+  Dev dev;
+};
+
+struct ParentArgs {
+  Dev dev;
+  int32_t level;      // level being built (>= 2)
+  int32_t b;
+  int64_t nparent;    // nodes at `level`
+  int64_t nchild;     // nodes at `level - 1`
+};
+
+struct AppendArgs {
+  void* K;
+  void* V;
+  const void* k_new;  // [Hkv][D]
+  const void* v_new;
+  const void* refs;
+  int64_t cap;
+  int64_t N;          // index of the new token (tokens before the append)
+  int32_t b;
+  int32_t levels;
+  float sigma;
+  Dev dev;
+};
+
+struct RouteArgs {
+  Dev dev;
+  const void* q;      // [Hq][D] input dtype
+  int64_t N;          // tokens
+  int32_t hkv, hq, g, b, levels;
+  int32_t level;      // level being routed
+  int64_t nlevel;     // nodes at `level` (upper bound of every union frontier there)
+  int64_t nbelow;     // nodes at level-1 (children existence); unused at level 1
+  float top_p;
+  float sigma;
+};
+
+struct AttnArgs {
+  Dev dev;
+  const void* K;
+  const void* V;
+  const void* q;
+  int64_t cap;
+  int64_t N;
+  int32_t hkv, hq, g, b;
+  int32_t splits;     // splits per KV head (grid.x)
+  int32_t keep_sink;
+  float sigma;
+  float* out;         // [Hq][D]
+};
+
+hipError_t launch_build_tile(const BuildArgs& a, bool bf16, int D, int R, int64_t ntiles, int hkv, int T,
+                             hipStream_t st);
+hipError_t launch_build_parent(const ParentArgs& a, int D, int R, int hkv, hipStream_t st);
+hipError_t launch_append(const AppendArgs& a, bool bf16, int D, int R, int hkv, hipStream_t st);
+
+// Routing: prep (q to fp32, state reset, top frontier) then per level the step sequence.
+hipError_t launch_route_prep(const RouteArgs& a, bool bf16, int D, hipStream_t st);
+hipError_t launch_route_level(const RouteArgs& a, int D, int R, hipStream_t st);
+hipError_t launch_route_expand(const RouteArgs& a, hipStream_t st);
+
+hipError_t launch_attend(const AttnArgs& a, bool bf16, int D, bool dense, hipStream_t st);
+// Same, and copies the per-level union sizes into `stats` ([levels + 1][Hkv], nullable).
+hipError_t launch_attend_full(const AttnArgs& a, bool bf16, int D, bool dense, int32_t* stats, int levels,
+                              hipStream_t st);
+
+}  // namespace zha

@@ -1,0 +1,448 @@
+// Host side of the ZHA C ABI: argument validation, workspace layout, launch sequencing.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/zha.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace zha;
+
+struct zha_tree {
+  zha_config cfg;
+  char* ws;
+  size_t ws_bytes;
+  Dev dev;
+  int64_t N;
+  bool built;
+  void* K;
+  void* V;
+  const void* refs;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+zha_status fail(zha_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+zha_status hip_fail(hipError_t e, const char* what) {
+  return fail(ZHA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t MAX_CAPACITY = (int64_t)1 << 31;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// b^l, saturating at 2^62.
+int64_t ipow_sat(int64_t b, int l) {
+  int64_t r = 1;
+  for (int i = 0; i < l; ++i) {
+    if (r > ((int64_t)1 << 62) / b) return (int64_t)1 << 62;
+    r *= b;
+  }
+  return r;
+}
+
+int64_t nodes_at(const zha_config& c, int level, int64_t n) { return ceil_div(n, ipow_sat(c.block, level)); }
+
+int tile_tokens(const zha_config& c) { return c.block <= 128 ? 128 : 256; }
+
+int tile_levels(const zha_config& c) {
+  const int T = tile_tokens(c);
+  int m = 0;
+  int64_t span = 1;
+  while (m < c.levels && span * c.block <= T) { span *= c.block; ++m; }
+  return m;
+}
+
+zha_status validate(const zha_config* c) {
+  if (!c) return fail(ZHA_E_INVALID, "config is null");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(ZHA_E_UNSUPPORTED, "head_dim %d not built (64 or 128)", c->head_dim);
+  if (c->num_kv_heads < 1) return fail(ZHA_E_INVALID, "num_kv_heads %d < 1", c->num_kv_heads);
+  if (c->num_q_heads < c->num_kv_heads || c->num_q_heads % c->num_kv_heads)
+    return fail(ZHA_E_INVALID, "num_q_heads %d is not a multiple of num_kv_heads %d", c->num_q_heads,
+                c->num_kv_heads);
+  if (c->num_q_heads / c->num_kv_heads > GMAX)
+    return fail(ZHA_E_UNSUPPORTED, "group size %d > %d", c->num_q_heads / c->num_kv_heads, GMAX);
+  if (c->block < 2 || c->block > 256) return fail(ZHA_E_INVALID, "block %d outside 2..256", c->block);
+  if (c->levels < 1 || c->levels > MAXL) return fail(ZHA_E_INVALID, "levels %d outside 1..%d", c->levels, MAXL);
+  if (c->num_ref != 1 && c->num_ref != 2 && c->num_ref != 4 && c->num_ref != 8 && c->num_ref != 16)
+    return fail(ZHA_E_UNSUPPORTED, "num_ref %d not built (1, 2, 4, 8, 16)", c->num_ref);
+  if (c->capacity < 1 || c->capacity >= MAX_CAPACITY)
+    return fail(ZHA_E_INVALID, "capacity %lld outside 1..2^31-1", (long long)c->capacity);
+  if (c->dtype != ZHA_F32 && c->dtype != ZHA_BF16) return fail(ZHA_E_INVALID, "dtype %d", c->dtype);
+  if (!(c->top_p > 0.f && c->top_p <= 1.f)) return fail(ZHA_E_INVALID, "top_p %g outside (0, 1]", c->top_p);
+  if (c->keep_sink != 0 && c->keep_sink != 1) return fail(ZHA_E_INVALID, "keep_sink %d", c->keep_sink);
+  if (c->dtype == ZHA_F32 && c->head_dim == 128 && c->block > 128)
+    return fail(ZHA_E_UNSUPPORTED, "float32 keys with head_dim 128 need block <= 128");
+  return ZHA_OK;
+}
+
+// Lays the workspace out; with base == nullptr only the size is computed.
+size_t layout(const zha_config& c, char* base, Dev* dev) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    off = (off + 255) & ~(size_t)255;
+    char* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  };
+  Dev d;
+  memset(&d, 0, sizeof d);
+  const int64_t H = c.num_kv_heads, Q = c.num_q_heads, R = c.num_ref, D = c.head_dim;
+  const int L = c.levels;
+  for (int l = 1; l <= L; ++l) d.ncap[l] = nodes_at(c, l, c.capacity);
+  d.ncap[0] = d.ncap[1];
+  for (int l = 1; l <= L; ++l) {
+    d.s[l] = (float*)take((size_t)(H * d.ncap[l] * R * D) * 4);
+    d.c[l] = (float*)take((size_t)(H * d.ncap[l] * R) * 4);
+    d.lse[l] = (float*)take((size_t)(H * d.ncap[l] * R) * 4);
+  }
+  for (int l = 0; l <= L; ++l) {
+    d.node[l] = (int32_t*)take((size_t)(H * d.ncap[l]) * 4);
+    d.mask[l] = (uint32_t*)take((size_t)(H * d.ncap[l]) * 4);
+    if (l >= 1) {
+      d.keep[l] = (uint32_t*)take((size_t)(H * d.ncap[l]) * 4);
+      d.score[l] = (float*)take((size_t)(H * GMAX * d.ncap[l]) * 4);
+      d.part[l] = (int32_t*)take((size_t)(H * ceil_div(d.ncap[l], EXPAND_CHUNK)) * 4);
+    }
+  }
+  d.cnt = (int32_t*)take((size_t)((MAXL + 1) * H) * 4);
+  d.qs = (QState*)take((size_t)((L + 1) * Q) * sizeof(QState));
+  d.mass1 = (uint64_t*)take((size_t)((L + 1) * Q * NB1) * 8);
+  d.mass2 = (uint64_t*)take((size_t)((L + 1) * Q * NB2) * 8);
+  d.cand = (int32_t*)take((size_t)(Q * d.ncap[1]) * 4);
+  d.qf = (float*)take((size_t)(Q * D) * 4);
+  d.apart = (float*)take((size_t)(Q * MAX_SPLITS * (D + 2)) * 4);
+  if (dev) *dev = d;
+  return (off + 255) & ~(size_t)255;
+}
+
+int attn_splits(int64_t tokens, int64_t per_split, int max_splits) {
+  int64_t s = ceil_div(tokens, per_split);
+  if (s < 1) s = 1;
+  if (s > max_splits) s = max_splits;
+  return (int)s;
+}
+
+RouteArgs route_args(const zha_tree* t, const void* q) {
+  RouteArgs a;
+  memset(&a, 0, sizeof a);
+  a.dev = t->dev;
+  a.q = q;
+  a.N = t->N;
+  a.hkv = t->cfg.num_kv_heads;
+  a.hq = t->cfg.num_q_heads;
+  a.g = a.hq / a.hkv;
+  a.b = t->cfg.block;
+  a.levels = t->cfg.levels;
+  a.top_p = t->cfg.top_p;
+  a.sigma = 1.0f / sqrtf((float)t->cfg.head_dim);
+  return a;
+}
+
+zha_status route_one_level(zha_tree* t, RouteArgs& a, int lv, hipStream_t st) {
+  a.level = lv;
+  a.nlevel = nodes_at(t->cfg, lv, t->N);
+  a.nbelow = lv > 1 ? nodes_at(t->cfg, lv - 1, t->N) : 0;
+  hipError_t e = launch_route_level(a, t->cfg.head_dim, t->cfg.num_ref, st);
+  if (e != hipSuccess) return hip_fail(e, "route level launch");
+  e = launch_route_expand(a, st);
+  if (e != hipSuccess) return hip_fail(e, "route expand launch");
+  return ZHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t zha_workspace_bytes(const zha_config* cfg) {
+  if (validate(cfg) != ZHA_OK) return 0;
+  return layout(*cfg, nullptr, nullptr);
+}
+
+zha_status zha_create(const zha_config* cfg, void* workspace, size_t workspace_bytes, zha_tree** out) {
+  zha_status s = validate(cfg);
+  if (s != ZHA_OK) return s;
+  if (!out) return fail(ZHA_E_INVALID, "out is null");
+  if (!workspace) return fail(ZHA_E_INVALID, "workspace is null");
+  if ((uintptr_t)workspace % 256) return fail(ZHA_E_INVALID, "workspace not 256-byte aligned");
+  const size_t need = layout(*cfg, nullptr, nullptr);
+  if (workspace_bytes < need)
+    return fail(ZHA_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  zha_tree* t = new (std::nothrow) zha_tree;
+  if (!t) return fail(ZHA_E_INVALID, "host allocation failed");
+  memset(t, 0, sizeof *t);
+  t->cfg = *cfg;
+  t->ws = (char*)workspace;
+  t->ws_bytes = workspace_bytes;
+  layout(*cfg, t->ws, &t->dev);
+  *out = t;
+  return ZHA_OK;
+}
+
+zha_status zha_tree_build(zha_tree* t, void* k_cache, void* v_cache, int64_t n_tokens, const void* ref_queries,
+                          hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!k_cache || !v_cache || !ref_queries) return fail(ZHA_E_INVALID, "null cache or reference-query pointer");
+  if (((uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)ref_queries) % 16)
+    return fail(ZHA_E_INVALID, "cache and reference-query pointers must be 16-byte aligned");
+  if (n_tokens < 1) return fail(ZHA_E_INVALID, "n_tokens %lld < 1", (long long)n_tokens);
+  if (n_tokens > t->cfg.capacity)
+    return fail(ZHA_E_CAPACITY, "n_tokens %lld > capacity %lld", (long long)n_tokens, (long long)t->cfg.capacity);
+  const zha_config& c = t->cfg;
+  BuildArgs a;
+  memset(&a, 0, sizeof a);
+  a.K = k_cache;
+  a.refs = ref_queries;
+  a.cap = c.capacity;
+  a.N = n_tokens;
+  a.b = c.block;
+  a.m = tile_levels(c);
+  a.sigma = 1.0f / sqrtf((float)c.head_dim);
+  a.dev = t->dev;
+  const int T = tile_tokens(c);
+  hipError_t e = launch_build_tile(a, c.dtype == ZHA_BF16, c.head_dim, c.num_ref, ceil_div(n_tokens, T),
+                                   c.num_kv_heads, T, stream);
+  if (e != hipSuccess) return hip_fail(e, "build tile launch");
+  for (int v = a.m + 1; v <= c.levels; ++v) {
+    ParentArgs p;
+    memset(&p, 0, sizeof p);
+    p.dev = t->dev;
+    p.level = v;
+    p.b = c.block;
+    p.nparent = nodes_at(c, v, n_tokens);
+    p.nchild = nodes_at(c, v - 1, n_tokens);
+    e = launch_build_parent(p, c.head_dim, c.num_ref, c.num_kv_heads, stream);
+    if (e != hipSuccess) return hip_fail(e, "build parent launch");
+  }
+  t->K = k_cache;
+  t->V = v_cache;
+  t->refs = ref_queries;
+  t->N = n_tokens;
+  t->built = true;
+  return ZHA_OK;
+}
+
+zha_status zha_tree_append(zha_tree* t, const void* k_new, const void* v_new, hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!t->built) return fail(ZHA_E_STATE, "append before build");
+  if (!k_new || !v_new) return fail(ZHA_E_INVALID, "null k_new or v_new");
+  if (t->N >= t->cfg.capacity) return fail(ZHA_E_CAPACITY, "cache full (%lld tokens)", (long long)t->N);
+  const zha_config& c = t->cfg;
+  AppendArgs a;
+  memset(&a, 0, sizeof a);
+  a.K = t->K;
+  a.V = t->V;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.refs = t->refs;
+  a.cap = c.capacity;
+  a.N = t->N;
+  a.b = c.block;
+  a.levels = c.levels;
+  a.sigma = 1.0f / sqrtf((float)c.head_dim);
+  a.dev = t->dev;
+  hipError_t e = launch_append(a, c.dtype == ZHA_BF16, c.head_dim, c.num_ref, c.num_kv_heads, stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  t->N += 1;
+  return ZHA_OK;
+}
+
+zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!t->built) return fail(ZHA_E_STATE, "decode before build");
+  if (!q || !out) return fail(ZHA_E_INVALID, "null q or out");
+  if ((uintptr_t)q % 16) return fail(ZHA_E_INVALID, "q must be 16-byte aligned");
+  const zha_config& c = t->cfg;
+  RouteArgs r = route_args(t, q);
+  r.nlevel = nodes_at(c, c.levels, t->N);
+  hipError_t e = launch_route_prep(r, c.dtype == ZHA_BF16, c.head_dim, stream);
+  if (e != hipSuccess) return hip_fail(e, "route prep launch");
+  for (int lv = c.levels; lv >= 1; --lv) {
+    zha_status s = route_one_level(t, r, lv, stream);
+    if (s != ZHA_OK) return s;
+  }
+  AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.dev = t->dev;
+  a.K = t->K;
+  a.V = t->V;
+  a.q = q;
+  a.cap = c.capacity;
+  a.N = t->N;
+  a.hkv = c.num_kv_heads;
+  a.hq = c.num_q_heads;
+  a.g = a.hq / a.hkv;
+  a.b = c.block;
+  a.splits = attn_splits(t->N, 4096, 256);
+  a.keep_sink = c.keep_sink;
+  a.sigma = 1.0f / sqrtf((float)c.head_dim);
+  a.out = out;
+  e = launch_attend_full(a, c.dtype == ZHA_BF16, c.head_dim, false, stats, c.levels, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ZHA_OK;
+}
+
+zha_status zha_decode_dense(zha_tree* t, const void* q, float* out, hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!t->built) return fail(ZHA_E_STATE, "decode before build");
+  if (!q || !out) return fail(ZHA_E_INVALID, "null q or out");
+  if ((uintptr_t)q % 16) return fail(ZHA_E_INVALID, "q must be 16-byte aligned");
+  const zha_config& c = t->cfg;
+  AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.dev = t->dev;
+  a.K = t->K;
+  a.V = t->V;
+  a.q = q;
+  a.cap = c.capacity;
+  a.N = t->N;
+  a.hkv = c.num_kv_heads;
+  a.hq = c.num_q_heads;
+  a.g = a.hq / a.hkv;
+  a.b = c.block;
+  a.splits = attn_splits(t->N, 2048, MAX_SPLITS);
+  a.keep_sink = 0;
+  a.sigma = 1.0f / sqrtf((float)c.head_dim);
+  a.out = out;
+  hipError_t e = launch_attend(a, c.dtype == ZHA_BF16, c.head_dim, true, stream);
+  if (e != hipSuccess) return hip_fail(e, "dense attention launch");
+  return ZHA_OK;
+}
+
+zha_status zha_debug_level(zha_tree* t, int32_t level, float* s_out, float* c_out, hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!t->built) return fail(ZHA_E_STATE, "no tree built");
+  if (level < 1 || level > t->cfg.levels) return fail(ZHA_E_INVALID, "level %d outside 1..%d", level, t->cfg.levels);
+  if (!s_out || !c_out) return fail(ZHA_E_INVALID, "null output");
+  const zha_config& c = t->cfg;
+  const int64_t n = nodes_at(c, level, t->N), cap = t->dev.ncap[level];
+  const size_t srow = (size_t)c.num_ref * c.head_dim * 4, crow = (size_t)c.num_ref * 4;
+  for (int kv = 0; kv < c.num_kv_heads; ++kv) {
+    hipError_t e = hipMemcpyAsync((char*)s_out + kv * n * srow, (char*)t->dev.s[level] + kv * cap * srow, n * srow,
+                                  hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync((char*)c_out + kv * n * crow, (char*)t->dev.c[level] + kv * cap * crow, n * crow,
+                         hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "level copy");
+  }
+  return ZHA_OK;
+}
+
+zha_status zha_debug_trace(zha_tree* t, int32_t level, int64_t cap, int32_t* nodes, uint32_t* masks, float* scores,
+                           uint32_t* keep, int32_t* counts, hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!t->built) return fail(ZHA_E_STATE, "no tree built");
+  const zha_config& c = t->cfg;
+  if (level < 0 || level > c.levels) return fail(ZHA_E_INVALID, "level %d outside 0..%d", level, c.levels);
+  if (!nodes || !masks || !counts) return fail(ZHA_E_INVALID, "null output");
+  const int64_t n = nodes_at(c, level == 0 ? 1 : level, t->N);
+  if (cap < n) return fail(ZHA_E_INVALID, "cap %lld < %lld nodes", (long long)cap, (long long)n);
+  const int64_t dcap = t->dev.ncap[level];
+  hipError_t e = hipSuccess;
+  for (int kv = 0; kv < c.num_kv_heads && e == hipSuccess; ++kv) {
+    e = hipMemcpyAsync(nodes + kv * cap, t->dev.node[level] + kv * dcap, n * 4, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(masks + kv * cap, t->dev.mask[level] + kv * dcap, n * 4, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess && keep && level >= 1)
+      e = hipMemcpyAsync(keep + kv * cap, t->dev.keep[level] + kv * dcap, n * 4, hipMemcpyDeviceToDevice, stream);
+    for (int gi = 0; gi < GMAX && e == hipSuccess && scores && level >= 1; ++gi)
+      e = hipMemcpyAsync(scores + ((int64_t)kv * GMAX + gi) * cap, t->dev.score[level] + ((int64_t)kv * GMAX + gi) * dcap,
+                         n * 4, hipMemcpyDeviceToDevice, stream);
+  }
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(counts, t->dev.cnt + (int64_t)level * c.num_kv_heads, c.num_kv_heads * 4,
+                       hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "trace copy");
+  return ZHA_OK;
+}
+
+zha_status zha_debug_route_level(zha_tree* t, int32_t level, const void* q, const int32_t* nodes,
+                                 const uint32_t* masks, const int32_t* counts, int64_t cap, hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!t->built) return fail(ZHA_E_STATE, "no tree built");
+  const zha_config& c = t->cfg;
+  if (level < 1 || level > c.levels) return fail(ZHA_E_INVALID, "level %d outside 1..%d", level, c.levels);
+  if (!q || !nodes || !masks || !counts) return fail(ZHA_E_INVALID, "null input");
+  const int64_t n = nodes_at(c, level, t->N);
+  const int H = c.num_kv_heads;
+  std::vector<int32_t> hc(H);
+  hipError_t e = hipMemcpyAsync(hc.data(), counts, H * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "count read");
+  for (int kv = 0; kv < H; ++kv) {
+    if (hc[kv] < 0 || hc[kv] > n || hc[kv] > cap)
+      return fail(ZHA_E_INVALID, "count %d for KV head %d outside 0..%lld", hc[kv], kv, (long long)n);
+    std::vector<int32_t> hn(hc[kv]);
+    if (hc[kv]) {
+      e = hipMemcpy(hn.data(), nodes + kv * cap, hc[kv] * 4, hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return hip_fail(e, "node read");
+    }
+    for (int i = 0; i < hc[kv]; ++i)
+      if (hn[i] < 0 || hn[i] >= n || (i && hn[i] <= hn[i - 1]))
+        return fail(ZHA_E_INVALID, "node list of KV head %d not ascending in 0..%lld", kv, (long long)n - 1);
+  }
+  RouteArgs r = route_args(t, q);
+  r.nlevel = nodes_at(c, c.levels, t->N);
+  e = launch_route_prep(r, c.dtype == ZHA_BF16, c.head_dim, stream);
+  if (e != hipSuccess) return hip_fail(e, "route prep launch");
+  const int64_t dcap = t->dev.ncap[level];
+  for (int kv = 0; kv < H && e == hipSuccess; ++kv) {
+    if (!hc[kv]) continue;
+    e = hipMemcpyAsync(t->dev.node[level] + kv * dcap, nodes + kv * cap, hc[kv] * 4, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(t->dev.mask[level] + kv * dcap, masks + kv * cap, hc[kv] * 4, hipMemcpyDeviceToDevice,
+                         stream);
+  }
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(t->dev.cnt + (int64_t)level * H, counts, H * 4, hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "frontier copy");
+  r.level = level;
+  r.nlevel = n;
+  r.nbelow = level > 1 ? nodes_at(c, level - 1, t->N) : 0;
+  e = launch_route_level(r, c.head_dim, c.num_ref, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "route level");
+  return ZHA_OK;
+}
+
+int64_t zha_num_tokens(const zha_tree* t) { return t ? t->N : -1; }
+
+zha_status zha_destroy(zha_tree* t) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  delete t;
+  return ZHA_OK;
+}
+
+const char* zha_status_string(zha_status s) {
+  switch (s) {
+    case ZHA_OK: return "ok";
+    case ZHA_E_INVALID: return "invalid argument";
+    case ZHA_E_UNSUPPORTED: return "unsupported configuration";
+    case ZHA_E_CAPACITY: return "capacity exceeded";
+    case ZHA_E_WORKSPACE: return "workspace too small";
+    case ZHA_E_STATE: return "call out of order";
+    case ZHA_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* zha_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,251 @@
+"""ctypes binding of libzha.so (include/zha.h): argument marshalling only.
+
+Every function keeps the C name and argument order; tensors may be passed where the C
+call takes a device pointer (their ``data_ptr()`` is used) and ``stream`` defaults to the
+current torch stream.  Errors raise ``ZhaError`` with the library's message.  There is no
+fallback: if libzha.so is missing the import of this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzha.so")
+
+ZHA_F32, ZHA_BF16 = 0, 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "capacity exceeded",
+          4: "workspace too small", 5: "call out of order", 6: "HIP runtime error"}
+GMAX = 8
+
+
+class ZhaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class zha_config(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("levels", ctypes.c_int32), ("num_ref", ctypes.c_int32),
+                ("capacity", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("top_p", ctypes.c_float), ("keep_sink", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m hierarchical_tree_indexed_03_amd.build_lib`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "zha_workspace_bytes": (SZ, [ctypes.POINTER(zha_config)]),
+        "zha_create": (I32, [ctypes.POINTER(zha_config), P, SZ, ctypes.POINTER(P)]),
+        "zha_tree_build": (I32, [P, P, P, I64, P, P]),
+        "zha_tree_append": (I32, [P, P, P, P]),
+        "zha_decode": (I32, [P, P, P, P, P]),
+        "zha_decode_dense": (I32, [P, P, P, P]),
+        "zha_debug_level": (I32, [P, I32, P, P, P]),
+        "zha_debug_trace": (I32, [P, I32, I64, P, P, P, P, P, P]),
+        "zha_debug_route_level": (I32, [P, I32, P, P, P, P, I64, P]),
+        "zha_num_tokens": (I64, [P]),
+        "zha_destroy": (I32, [P]),
+        "zha_status_string": (ctypes.c_char_p, [I32]),
+        "zha_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("zha_workspace_bytes", "zha_create", "zha_tree_build", "zha_tree_append", "zha_decode",
+            "zha_decode_dense", "zha_debug_level", "zha_debug_trace", "zha_debug_route_level",
+            "zha_num_tokens", "zha_destroy", "zha_status_string", "zha_last_error")
+
+
+def _p(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _s(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status: int):
+    if status != 0:
+        raise ZhaError(status, (_lib.zha_last_error() or b"").decode())
+
+
+def make_config(head_dim, num_kv_heads, num_q_heads, block, levels, num_ref, capacity, dtype, top_p,
+                keep_sink=True) -> zha_config:
+    dt = dtype if isinstance(dtype, int) else (ZHA_BF16 if dtype in ("bf16", torch.bfloat16) else ZHA_F32)
+    return zha_config(head_dim, num_kv_heads, num_q_heads, block, levels, num_ref, capacity, dt,
+                      float(top_p), int(bool(keep_sink)))
+
+
+def zha_workspace_bytes(cfg: zha_config) -> int:
+    return int(_lib.zha_workspace_bytes(ctypes.byref(cfg)))
+
+
+def zha_create(cfg: zha_config, workspace, workspace_bytes: int) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(_lib.zha_create(ctypes.byref(cfg), _p(workspace), workspace_bytes, ctypes.byref(h)))
+    return h
+
+
+def zha_tree_build(t, k_cache, v_cache, n_tokens: int, ref_queries, stream=None):
+    _check(_lib.zha_tree_build(t, _p(k_cache), _p(v_cache), int(n_tokens), _p(ref_queries), _s(stream)))
+
+
+def zha_tree_append(t, k_new, v_new, stream=None):
+    _check(_lib.zha_tree_append(t, _p(k_new), _p(v_new), _s(stream)))
+
+
+def zha_decode(t, q, out, stats=None, stream=None):
+    _check(_lib.zha_decode(t, _p(q), _p(out), _p(stats), _s(stream)))
+
+
+def zha_decode_dense(t, q, out, stream=None):
+    _check(_lib.zha_decode_dense(t, _p(q), _p(out), _s(stream)))
+
+
+def zha_debug_level(t, level: int, s_out, c_out, stream=None):
+    _check(_lib.zha_debug_level(t, int(level), _p(s_out), _p(c_out), _s(stream)))
+
+
+def zha_debug_trace(t, level: int, cap: int, nodes, masks, scores, keep, counts, stream=None):
+    _check(_lib.zha_debug_trace(t, int(level), int(cap), _p(nodes), _p(masks), _p(scores), _p(keep),
+                                _p(counts), _s(stream)))
+
+
+def zha_debug_route_level(t, level: int, q, nodes, masks, counts, cap: int, stream=None):
+    _check(_lib.zha_debug_route_level(t, int(level), _p(q), _p(nodes), _p(masks), _p(counts), int(cap),
+                                      _s(stream)))
+
+
+def zha_num_tokens(t) -> int:
+    return int(_lib.zha_num_tokens(t))
+
+
+def zha_destroy(t):
+    _check(_lib.zha_destroy(t))
+
+
+def zha_status_string(s: int) -> str:
+    return _lib.zha_status_string(int(s)).decode()
+
+
+def zha_last_error() -> str:
+    return (_lib.zha_last_error() or b"").decode()
+
+
+class Tree:
+    """One ZHA index over caller-owned caches: owns the device workspace (a torch tensor)."""
+
+    def __init__(self, cfg: zha_config, device="cuda"):
+        self.cfg = cfg
+        nbytes = zha_workspace_bytes(cfg)
+        if nbytes == 0:
+            # reproduce the validation error message
+            h = ctypes.c_void_p()
+            _check(_lib.zha_create(ctypes.byref(cfg), None, 0, ctypes.byref(h)))
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.handle = zha_create(cfg, self.workspace, nbytes)
+        self.group = cfg.num_q_heads // cfg.num_kv_heads
+        self._keep = []
+
+    def build(self, K, V, n_tokens, refs, stream=None):
+        self._keep = [K, V, refs]
+        zha_tree_build(self.handle, K, V, n_tokens, refs, stream)
+
+    def append(self, k_new, v_new, stream=None):
+        zha_tree_append(self.handle, k_new, v_new, stream)
+
+    def decode(self, q, out=None, stats=None, stream=None):
+        if out is None:
+            out = torch.empty(self.cfg.num_q_heads, self.cfg.head_dim, dtype=torch.float32, device=q.device)
+        zha_decode(self.handle, q, out, stats, stream)
+        return out
+
+    def decode_dense(self, q, out=None, stream=None):
+        if out is None:
+            out = torch.empty(self.cfg.num_q_heads, self.cfg.head_dim, dtype=torch.float32, device=q.device)
+        zha_decode_dense(self.handle, q, out, stream)
+        return out
+
+    @property
+    def n_tokens(self) -> int:
+        return zha_num_tokens(self.handle)
+
+    def nodes(self, level: int) -> int:
+        n = self.n_tokens
+        return -(-n // self.cfg.block ** level)
+
+    def level(self, level: int):
+        n = self.nodes(level)
+        c = self.cfg
+        s = torch.empty(c.num_kv_heads, n, c.num_ref, c.head_dim, dtype=torch.float32, device=self.workspace.device)
+        cc = torch.empty(c.num_kv_heads, n, c.num_ref, dtype=torch.float32, device=self.workspace.device)
+        zha_debug_level(self.handle, level, s, cc)
+        return s, cc
+
+    def trace(self, level: int):
+        """Routing trace of the last decode at ``level`` (0 = kept level-1 blocks): per KV
+        head (nodes, masks, scores [8, n], keep) as CPU tensors cut to the entry count."""
+        c = self.cfg
+        cap = self.nodes(max(level, 1))
+        dev = self.workspace.device
+        nodes = torch.empty(c.num_kv_heads, cap, dtype=torch.int32, device=dev)
+        masks = torch.empty(c.num_kv_heads, cap, dtype=torch.int32, device=dev)
+        scores = torch.empty(c.num_kv_heads, GMAX, cap, dtype=torch.float32, device=dev)
+        keep = torch.empty(c.num_kv_heads, cap, dtype=torch.int32, device=dev)
+        counts = torch.empty(c.num_kv_heads, dtype=torch.int32, device=dev)
+        zha_debug_trace(self.handle, level, cap, nodes, masks, scores if level else None,
+                        keep if level else None, counts)
+        out = []
+        for kv in range(c.num_kv_heads):
+            n = int(counts[kv])
+            out.append(dict(nodes=nodes[kv, :n].cpu(), masks=masks[kv, :n].cpu(),
+                            scores=scores[kv, :, :n].cpu() if level else None,
+                            keep=keep[kv, :n].cpu() if level else None))
+        return out
+
+    def route_level(self, level: int, q, frontiers):
+        """Teacher-forced routing of one level.  ``frontiers[kv]`` = (node ids ascending,
+        head masks) as int tensors; returns the trace of that level."""
+        c = self.cfg
+        cap = max(1, self.nodes(level))
+        dev = self.workspace.device
+        nodes = torch.zeros(c.num_kv_heads, cap, dtype=torch.int32, device=dev)
+        masks = torch.zeros(c.num_kv_heads, cap, dtype=torch.int32, device=dev)
+        counts = torch.zeros(c.num_kv_heads, dtype=torch.int32, device=dev)
+        for kv, (nd, mk) in enumerate(frontiers):
+            n = len(nd)
+            nodes[kv, :n] = torch.as_tensor(nd, dtype=torch.int32).to(dev)
+            masks[kv, :n] = torch.as_tensor(mk, dtype=torch.int64).to(torch.int32).to(dev)
+            counts[kv] = n
+        zha_debug_route_level(self.handle, level, q, nodes, masks, counts, cap)
+        return self.trace(level)
+
+    def close(self):
+        if getattr(self, "handle", None) is not None:
+            zha_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

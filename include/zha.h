@@ -1,0 +1,153 @@
+/*
+ * zha.h — C ABI of the ZHA (Zyphra Hierarchical Attention) decode hot path on MI355X.
+ *
+ * The method (arXiv 2610.42112, "Subquadratic Attention with a Hierarchical
+ * Tree-Structured Indexer"; Zyphra blog post "Zyphra Hierarchical Attention"):
+ *   - the full KV cache is kept; over its keys a tree of summaries is built: keys are cut
+ *     into contiguous blocks of `block` tokens and each block is summarised, then the
+ *     summaries are grouped `block` at a time and summarised again, `levels` times
+ *     (blog, "Building the tree");
+ *   - a summary is, for each of `num_ref` reference queries r_j, a tangent plane of the
+ *     node's log attention mass: a weighted-mean key s_j and an offset c_j; a query q
+ *     scores the node with max_j(q.s_j/sqrt(d) + c_j) (news summary, "Building the tree");
+ *   - a decode query scores the top level, keeps the smallest set of nodes holding a
+ *     fraction `top_p` of the estimated attention probability, expands only their children
+ *     and repeats down to the raw keys, then runs ordinary attention over the selected
+ *     blocks plus token 0, the attention sink (blog, "Routing through the tree"; news
+ *     summary, "How does top-p routing pick tokens?").
+ *
+ * Conventions shared by every call:
+ *   - Pointers marked (device) are HIP device memory; (host) are host memory.  The caller
+ *     owns every buffer.  The library never allocates or frees device memory and never
+ *     synchronises a stream, except where a call says so.
+ *   - Tensors are dense, row-major, with the shapes given.  `dtype` (zha_dtype) fixes the
+ *     element type of K, V, reference queries and decode queries: float32 or bfloat16.
+ *     Tree planes and outputs are float32.
+ *   - Every call validates its arguments on the host before enqueueing any work; on any
+ *     error it returns a non-zero zha_status, enqueues nothing and leaves the handle
+ *     unchanged.  zha_last_error() then describes the failure (thread-local string).
+ *   - Work is asynchronous on the given stream (0 = the null stream).  Faults inside
+ *     kernels surface at the caller's next synchronisation.  A handle is not thread-safe.
+ *   - Query head h reads KV head h / (num_q_heads / num_kv_heads) (contiguous groups).
+ */
+#ifndef ZHA_H
+#define ZHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ZHA_OK = 0,
+  ZHA_E_INVALID = 1,      /* bad argument: null pointer, out-of-range value        */
+  ZHA_E_UNSUPPORTED = 2,  /* valid but not built: head_dim, num_ref or group size   */
+  ZHA_E_CAPACITY = 3,     /* token count above the configured capacity             */
+  ZHA_E_WORKSPACE = 4,    /* workspace smaller than zha_workspace_bytes()          */
+  ZHA_E_STATE = 5,        /* call out of order (e.g. decode before build)          */
+  ZHA_E_HIP = 6           /* a HIP runtime call failed; see zha_last_error()       */
+} zha_status;
+
+typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1 } zha_dtype;
+
+typedef struct {
+  int32_t head_dim;       /* d: 64 or 128                                               */
+  int32_t num_kv_heads;   /* Hkv >= 1: one tree per KV head                             */
+  int32_t num_q_heads;    /* Hq: a multiple of Hkv with Hq/Hkv <= 8                     */
+  int32_t block;          /* b: 2..256 tokens per leaf block / children per node       */
+  int32_t levels;         /* L: 1..16 summary levels                                    */
+  int32_t num_ref;        /* R: 1, 2, 4, 8 or 16 reference queries per tree             */
+  int64_t capacity;       /* max tokens the caches (and the tree) may hold              */
+  int32_t dtype;          /* zha_dtype of K, V, reference and decode queries            */
+  float top_p;            /* p in (0, 1]; p = 1 keeps every node (dense attention)     */
+  int32_t keep_sink;      /* 1: token 0 is always attended                              */
+} zha_config;
+
+typedef struct zha_tree zha_tree;   /* opaque host-side handle */
+
+/* Device workspace needed by a handle: the tree planes at capacity (per level l,
+ * s [Hkv][ceil(capacity/b^l)][R][d] and c [Hkv][...][R], float32) plus router and
+ * attention scratch.  Returns 0 for an invalid or unsupported config. */
+size_t zha_workspace_bytes(const zha_config* cfg);
+
+/* Creates a handle over a caller-owned device `workspace` (>= zha_workspace_bytes,
+ * 256-byte aligned).  The workspace is borrowed until zha_destroy. */
+zha_status zha_create(const zha_config* cfg, void* workspace, size_t workspace_bytes,
+                      zha_tree** out);
+
+/* Builds the whole tree over keys [0, n_tokens) (blog, "Building the tree").
+ *   k_cache, v_cache  (device) [Hkv][capacity][d] dtype; borrowed until the next build
+ *                     or destroy (append writes row N into them; decode reads them).
+ *   n_tokens          1..capacity tokens already in the caches.
+ *   ref_queries       (device) [Hkv][R][d] dtype; borrowed likewise.
+ * Level 1: for block n and reference query r_j, z_t = r_j.k_t/sqrt(d) over the block's
+ * keys, LSE = logsumexp z, s_j = sum_t softmax(z)_t k_t, c_j = LSE - r_j.s_j/sqrt(d).
+ * Level l > 1: LSE_j = logsumexp over children of their log mass at r_j; s_j = the
+ * children's s_j weighted by softmax of those log masses; c_j as above. */
+zha_status zha_tree_build(zha_tree* t, void* k_cache, void* v_cache, int64_t n_tokens,
+                          const void* ref_queries, hipStream_t stream);
+
+/* Appends one token to every KV head: writes k_new/v_new ((device) [Hkv][d] dtype) into
+ * row N of the caches, then refreshes the one node per level whose span holds the new
+ * token.  ZHA_E_CAPACITY when N == capacity.  Equivalent to a rebuild over N+1 tokens. */
+zha_status zha_tree_append(zha_tree* t, const void* k_new, const void* v_new,
+                           hipStream_t stream);
+
+/* One decode step for all query heads (blog, "Routing through the tree").
+ *   q      (device) [Hq][d] dtype.
+ *   out    (device) [Hq][d] float32: softmax attention over the routed tokens.
+ *   stats  (device, nullable) int32 [levels + 1][Hkv]: row i < levels holds the size of
+ *          the union (over the group's query heads) of the frontier scored at level
+ *          levels - i; the last row holds the number of kept level-1 blocks (union).
+ * Routing state stays on the device; nothing is read back to the host. */
+zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats,
+                      hipStream_t stream);
+
+/* Dense decode over all N tokens (the baseline attention the method is compared with):
+ * out[h] = softmax(q_h.K^T/sqrt(d)) V for every query head. */
+zha_status zha_decode_dense(zha_tree* t, const void* q, float* out, hipStream_t stream);
+
+/* Copies level `level` (1..levels) of the tree into caller buffers:
+ *   s_out (device) float32 [Hkv][n_l][R][d], c_out (device) float32 [Hkv][n_l][R] with
+ *   n_l = ceil(N / block^level).  Enqueued copies only (no synchronisation). */
+zha_status zha_debug_level(zha_tree* t, int32_t level, float* s_out, float* c_out,
+                           hipStream_t stream);
+
+/* Routing trace of the last zha_decode / zha_debug_route_level on this handle, for level
+ * `level` (levels..1; 0 = the kept level-1 blocks).  Copies into caller device buffers
+ * sized for `cap` entries per KV head:
+ *   nodes  int32  [Hkv][cap]  node ids of the union frontier, ascending
+ *   masks  uint32 [Hkv][cap]  bit i set: query head (kv*group + i) has the node in its
+ *                             frontier (level 0: the head kept the block)
+ *   scores float32[Hkv][8][cap] router score of each node for each query head of the
+ *                             group (nullable; unused for level 0)
+ *   keep   uint32 [Hkv][cap]  bit i set: query head i of the group kept the node
+ *                             (nullable; unused for level 0)
+ *   counts int32  [Hkv]       entries per KV head
+ * ZHA_E_INVALID if cap is smaller than the level's node count. Synchronises `stream`. */
+zha_status zha_debug_trace(zha_tree* t, int32_t level, int64_t cap, int32_t* nodes,
+                           uint32_t* masks, float* scores, uint32_t* keep, int32_t* counts,
+                           hipStream_t stream);
+
+/* Teacher-forced routing of one level: scores the caller's union frontier (nodes/masks/
+ * counts in the zha_debug_trace layout, with cap entries per KV head, device) for the
+ * queries q and applies the per-head top-p; results are read with zha_debug_trace at
+ * the same level.  Synchronises `stream`. */
+zha_status zha_debug_route_level(zha_tree* t, int32_t level, const void* q,
+                                 const int32_t* nodes, const uint32_t* masks,
+                                 const int32_t* counts, int64_t cap, hipStream_t stream);
+
+/* Tokens currently in the tree (host-side count; no synchronisation). */
+int64_t zha_num_tokens(const zha_tree* t);
+
+zha_status zha_destroy(zha_tree* t);
+const char* zha_status_string(zha_status s);
+const char* zha_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZHA_H */

@@ -1,0 +1,113 @@
+"""CPU tests of the C ABI: the library loads, exports every function include/zha.h declares,
+and rejects bad arguments on the host before touching the GPU (state left unchanged)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zha.h")
+
+
+@pytest.fixture(scope="module")
+def zha():
+    from hierarchical_tree_indexed_03_amd import build_lib
+    if not os.path.exists(build_lib.OUT):
+        build_lib.build()
+    from hierarchical_tree_indexed_03_amd import zha as z
+    return z
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zha_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_match_header(zha):
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(zha.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in zha.h but not exported"
+    assert set(names) == set(zha.EXPORTED)
+
+
+def good(zha, **kw):
+    base = dict(head_dim=128, num_kv_heads=4, num_q_heads=32, block=4, levels=6, num_ref=16,
+                capacity=1 << 18, dtype="bf16", top_p=0.95, keep_sink=True)
+    base.update(kw)
+    return zha.make_config(**base)
+
+
+BAD = [
+    (dict(head_dim=96), 2), (dict(num_kv_heads=0), 1), (dict(num_q_heads=30), 1),
+    (dict(num_q_heads=4 * 9), 2), (dict(block=1), 1), (dict(block=257), 1), (dict(levels=0), 1),
+    (dict(levels=17), 1), (dict(num_ref=3), 2), (dict(capacity=0), 1), (dict(capacity=1 << 31), 1),
+    (dict(dtype=5), 1), (dict(top_p=0.0), 1), (dict(top_p=1.5), 1), (dict(top_p=float("nan")), 1),
+    (dict(dtype="f32", block=256), 2),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD, ids=[str(k) for k, _ in BAD])
+def test_invalid_configs(zha, kw, status):
+    cfg = good(zha, **kw)
+    assert zha.zha_workspace_bytes(cfg) == 0
+    with pytest.raises(zha.ZhaError) as e:
+        zha.zha_create(cfg, 0x100000, 1 << 40)
+    assert e.value.status == status
+    assert zha.zha_last_error()
+
+
+def test_workspace_and_handle_checks(zha):
+    cfg = good(zha)
+    need = zha.zha_workspace_bytes(cfg)
+    assert need > 0 and need % 256 == 0
+    with pytest.raises(zha.ZhaError) as e:
+        zha.zha_create(cfg, 0x100000, need - 1)
+    assert e.value.status == 4
+    with pytest.raises(zha.ZhaError) as e:
+        zha.zha_create(cfg, 0x100001, need)
+    assert e.value.status == 1
+    with pytest.raises(zha.ZhaError) as e:
+        zha.zha_create(cfg, None, need)
+    assert e.value.status == 1
+
+
+def test_workspace_grows_with_capacity(zha):
+    a = zha.zha_workspace_bytes(good(zha, capacity=1 << 16))
+    b = zha.zha_workspace_bytes(good(zha, capacity=1 << 18))
+    assert b > 3 * a
+
+
+def test_call_order_and_arguments(zha):
+    """Handle created on a fake (never dereferenced) address: every call below must fail
+    validation on the host and leave the handle as it was."""
+    cfg = good(zha, capacity=1000)
+    t = zha.zha_create(cfg, 0x100000, zha.zha_workspace_bytes(cfg))
+    try:
+        fake = 0x200000
+        for call, status in [
+            (lambda: zha.zha_decode(t, fake, fake), 5),
+            (lambda: zha.zha_decode_dense(t, fake, fake), 5),
+            (lambda: zha.zha_tree_append(t, fake, fake), 5),
+            (lambda: zha.zha_debug_level(t, 1, fake, fake), 5),
+            (lambda: zha.zha_tree_build(t, fake, fake, 1001, fake), 3),
+            (lambda: zha.zha_tree_build(t, fake, fake, 0, fake), 1),
+            (lambda: zha.zha_tree_build(t, None, fake, 10, fake), 1),
+            (lambda: zha.zha_tree_build(t, fake + 2, fake, 10, fake), 1),
+        ]:
+            with pytest.raises(zha.ZhaError) as e:
+                call()
+            assert e.value.status == status
+            assert zha.zha_num_tokens(t) == 0
+    finally:
+        zha.zha_destroy(t)
+
+
+def test_status_strings(zha):
+    for s in range(7):
+        assert zha.zha_status_string(s)

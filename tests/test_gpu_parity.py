@@ -1,0 +1,188 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on seeded inputs.
+
+Shapes: the tiny workload in full, and the deep / wide / light / ultra geometries at token
+counts the oracle finishes in seconds (several tiles, ragged tails), each over a few decode
+steps that append one token first.  Tolerances are those of tests/parity.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import parity as P
+from oracle import zha_oracle as zo
+from workloads import configs as wc, gen
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny": wc.TINY,
+    "deep_small": wc.DEEP.with_(n_tokens=16_384 + 37, steps=3),
+    "wide_small": wc.WIDE.with_(n_tokens=8_192 + 100, steps=3),
+    "light_small": wc.light(32_768, steps=3).with_(n_tokens=32_768 - 5),
+    "ultra_small": wc.ULTRA.with_(n_tokens=70_001, steps=2),
+}
+
+
+class Case:
+    def __init__(self, w: wc.Workload, top_p=None):
+        self.w = w
+        self.p = w.top_p if top_p is None else top_p
+        self.K, self.V, self.refs = P.host_inputs(w)
+        self.trees = P.oracle_trees(w, self.K, self.refs, w.n_tokens)
+        self.t = P.make_tree(w, top_p=self.p)
+        self.Kd, self.Vd, self.Rd = P.upload(self.K, w), P.upload(self.V, w), P.upload(self.refs, w)
+        self.t.build(self.Kd, self.Vd, w.n_tokens, self.Rd)
+        self.n = w.n_tokens
+
+    def append(self):
+        w, n = self.w, self.n
+        self.t.append(self.Kd[:, n].contiguous(), self.Vd[:, n].contiguous())
+        for h in range(w.num_kv_heads):
+            zo.append_token(self.trees[h], self.K[h, n])
+        self.n += 1
+
+    def queries(self, step):
+        return gen.step_queries(self.w, step, self.n, gen.host_fetch(self.K))
+
+    def decode(self, q):
+        qd = P.upload(q, self.w)
+        o = self.t.decode(qd)
+        torch.cuda.synchronize()
+        traces = {lv: self.t.trace(lv) for lv in range(0, self.w.levels + 1)}
+        return o.cpu().numpy(), traces
+
+
+_CACHE = {}
+
+
+def case(name) -> Case:
+    if name not in _CACHE:
+        _CACHE.clear()
+        _CACHE[name] = Case(SMALL[name])
+    return _CACHE[name]
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_planes_match_oracle(name):
+    c = case(name)
+    w = c.w
+    for lv in range(1, w.levels + 1):
+        s, cc = c.t.level(lv)
+        s, cc = s.cpu().numpy(), cc.cpu().numpy()
+        for h in range(w.num_kv_heads):
+            so, co = c.trees[h].levels[lv - 1]
+            es = np.max(np.abs(s[h] - so)) / max(1.0, np.max(np.abs(so)))
+            ec = np.max(np.abs(cc[h] - co))
+            assert es < 1e-4 and ec < 1e-3, f"level {lv} head {h}: s err {es:.2e}, c err {ec:.2e}"
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_teacher_forced_scores_and_sets(name):
+    c = case(name)
+    w = c.w
+    q = c.queries(100)
+    g = w.group
+    routes = [zo.route(c.trees[h // g], q[h], c.p, w.keep_sink) for h in range(w.num_q_heads)]
+    qd = P.upload(q, w)
+    worst = 0.0
+    for li in range(w.levels):
+        lv = w.levels - li
+        fronts = []
+        for kv in range(w.num_kv_heads):
+            fr = {}
+            for gi in range(g):
+                for n in routes[kv * g + gi]["levels"][li]["frontier"].tolist():
+                    fr[n] = fr.get(n, 0) | (1 << gi)
+            nodes = np.array(sorted(fr), dtype=np.int64)
+            fronts.append((nodes, np.array([fr[n] for n in nodes.tolist()], dtype=np.int64)))
+        tr = c.t.route_level(lv, qd, fronts)
+        for h in range(w.num_q_heads):
+            kv, gi = divmod(h, g)
+            rec = routes[h]["levels"][li]
+            gs = P.gpu_scores(tr[kv], gi)
+            sg = np.array([gs[n] for n in rec["frontier"].tolist()])
+            worst = max(worst, float(np.max(np.abs(sg - rec["scores"]))))
+            kept = P.gpu_kept(tr[kv], gi)
+            diff = np.array(sorted(set(kept.tolist()) ^ set(rec["kept"].tolist())), dtype=np.int64)
+            _, bad = P.exempt_nodes(rec, c.p, diff)
+            assert not bad, f"level {lv} head {h}: unexplained set mismatch {bad[:5]}"
+    assert worst <= P.SCORE_TOL, f"max score error {worst:.3e}"
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_end_to_end(name):
+    c = case(name)
+    w = c.w
+    g = w.group
+    for step in range(w.steps if w.steps else 1):
+        if w.appends:
+            c.append()
+        q = c.queries(step)
+        o, traces = c.decode(q)
+        o_ref, routes = zo.decode(c.trees, c.V, q, c.p, w.keep_sink, return_routes=True)
+        for h in range(w.num_q_heads):
+            kv, gi = divmod(h, g)
+            tr = {lv: traces[lv][kv] for lv in traces}
+            rep = P.compare_route(routes[h], tr, gi, w.block, c.p)
+            assert not rep["bad"], f"step {step} head {h}: {rep['bad'][:5]}"
+            toks = P.gpu_tokens(tr[0], gi, w.block, c.n, w.keep_sink)
+            o_given = zo.attend(c.K[kv][:c.n], c.V[kv][:c.n], q[h], toks)
+            e1 = P.out_err(o[h], o_given)
+            assert e1 <= P.OUT_RTOL, f"step {step} head {h}: attention over GPU set err {e1:.3e}"
+            if not rep["exempt"]:
+                e2 = P.out_err(o[h], o_ref[h])
+                assert e2 <= P.OUT_RTOL, f"step {step} head {h}: output err {e2:.3e}"
+
+
+@pytest.mark.parametrize("name", ["tiny", "deep_small", "wide_small"])
+def test_dense_decode(name):
+    c = case(name)
+    q = c.queries(7)
+    o = c.t.decode_dense(P.upload(q, c.w)).cpu().numpy()
+    ref = zo.dense_decode(c.K, c.V, q, c.n)
+    assert P.out_err(o, ref) <= P.OUT_RTOL
+
+
+@pytest.mark.parametrize("name", ["tiny", "deep_small", "light_small"])
+def test_p1_is_dense(name):
+    w = SMALL[name]
+    c = Case(w.with_(steps=0), top_p=1.0)
+    q = c.queries(3)
+    qd = P.upload(q, w)
+    o = c.t.decode(qd).cpu().numpy()
+    od = c.t.decode_dense(qd).cpu().numpy()
+    ref = zo.dense_decode(c.K, c.V, q, c.n)
+    assert P.out_err(o, ref) <= P.OUT_RTOL
+    assert P.out_err(o, od) <= 1e-4
+    tr0 = c.t.trace(0)
+    for kv in range(w.num_kv_heads):
+        assert len(tr0[kv]["nodes"]) == w.nodes(1, c.n)
+
+
+def test_deterministic():
+    c = case("deep_small")
+    q = c.queries(11)
+    o1, t1 = c.decode(q)
+    o2, t2 = c.decode(q)
+    assert np.array_equal(o1, o2)
+    for lv in t1:
+        for a, b in zip(t1[lv], t2[lv]):
+            assert torch.equal(a["nodes"], b["nodes"]) and torch.equal(a["masks"], b["masks"])
+            if a["keep"] is not None:
+                assert torch.equal(a["keep"], b["keep"])
+
+
+def test_append_equals_rebuild():
+    w = SMALL["deep_small"].with_(steps=70)
+    c = Case(w)
+    for _ in range(70):
+        c.append()
+    t2 = P.make_tree(w)
+    t2.build(c.Kd, c.Vd, c.n, c.Rd)
+    for lv in range(1, w.levels + 1):
+        s1, c1 = c.t.level(lv)
+        s2, c2 = t2.level(lv)
+        assert torch.allclose(s1, s2, atol=1e-4, rtol=1e-4), f"level {lv} s"
+        assert torch.allclose(c1, c2, atol=1e-3, rtol=1e-4), f"level {lv} c"
