@@ -1,0 +1,317 @@
+"""Benchmark of the ZHA decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload deep]
+
+A step is one pass of the whole decode path for one new token: zha_tree_append (one
+key/value per KV head, refreshing the rightmost node of every level) then zha_decode (the
+top-down top-p routing of all 32 query heads and the split-K attention over the routed
+blocks plus the sink).  Inputs (caches, reference queries, the per-step queries and new
+keys/values) are resident in HBM before the timed region.  The tree build over the
+initial cache is timed separately (build tokens/s), as is the dense flash-decode over the
+same cache (the baseline the method is compared with).
+
+Prints one JSON line (the measurement record) on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from workloads import configs as wc, gen  # noqa: E402
+
+METRIC = "ZHA decode queries/s per layer at 256K and 16M ctx; % HBM roofline; build tok/s"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="deep", help="deep | wide | ultra | light_<N> | tiny")
+    ap.add_argument("--build-reps", type=int, default=3)
+    ap.add_argument("--dense-reps", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of timed oracle decode")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration for traffic)")
+    return ap.parse_args()
+
+
+def kernel_bytes(key, w, stats_rows, n_tokens):
+    """Algorithmic HBM bytes of one launch of `key` given the routing stats of that step.
+
+    route_score.l<l>: per union-frontier node R*(d+1)*4 plane bytes + 8 bytes of list entry
+                      + 4 bytes per query head of the group for the score written;
+    attend:           per gathered token 2*d*2 bytes (K and V rows, bf16) + per KV head the
+                      sink row; partial results excluded;
+    dense_attend:     N * Hkv * 2 * d * 2 bytes.
+    """
+    R, d, g, L = w.num_ref, w.head_dim, w.group, w.levels
+    if key.startswith("route_score.l"):
+        lv = int(key.split(".l")[1])
+        u = stats_rows[L - lv].sum()
+        return float(u) * (R * (d + 1) * 4 + 8 + g * 4)
+    if key == "attend":
+        blocks = stats_rows[L].sum()
+        return float(blocks) * w.block * 2 * d * 2
+    if key == "dense_attend":
+        return float(n_tokens) * w.num_kv_heads * 2 * d * 2
+    return None
+
+
+def src_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "hierarchical_tree_indexed_03_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """Measured HBM bytes per launch from a committed counter summary, if it was taken on
+    the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("src_sha") != src_sha():
+        return None
+    return t.get("kernels", {}).get(kernel)
+
+
+def cpu_baseline(w, K, V, refs, queries, n0, budget):
+    """The oracle as written, timed on the host on a bounded sample: KV head 0's tree
+    (built first, untimed, with every host thread), then decode steps of that head's query
+    group on one thread (append + route + attend per step) until `budget` seconds."""
+    from threadpoolctl import threadpool_limits
+    from oracle import zha_oracle as zo
+    tb0 = time.perf_counter()
+    tree = zo.build_tree(K[0].copy(), refs[0], w.block, w.levels, n0)
+    tb = time.perf_counter() - tb0
+    steps = 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while steps < len(queries) and time.perf_counter() - t0 < budget:
+            if w.appends:
+                zo.append_token(tree, K[0, tree.n_tokens])
+            q = queries[steps]
+            for h in range(w.group):
+                r = zo.route(tree, q[h], w.top_p, w.keep_sink)
+                zo.attend(tree.keys[:tree.n_tokens], V[0][:tree.n_tokens], q[h], r["tokens"])
+            steps += 1
+        el = time.perf_counter() - t0
+    per_step_all_heads = el / max(steps, 1) * w.num_kv_heads
+    return dict(value=1.0 / per_step_all_heads, unit="queries/s", cores=1, kind="oracle",
+                sample=(f"KV head 0 of {w.num_kv_heads} (its {w.group} query heads), {steps} decode steps "
+                        f"(append+route+attend) in {el:.1f}s on 1 thread, scaled x{w.num_kv_heads} to all "
+                        f"heads; tree over {n0} tokens built first (untimed, {tb:.1f}s, all threads)"),
+                host_cpus=os.cpu_count())
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the path has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from hierarchical_tree_indexed_03_amd import zha
+
+    base = wc.NAMED[args.workload]
+    steps = args.steps if args.steps is not None else (base.steps or 64)
+    total = args.warmup + steps
+    w = base.with_(steps=total)
+    n0 = w.n_tokens
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+
+    t = time.perf_counter()
+    K, V = gen.kv_cache(w)
+    refs = gen.ref_queries(w)
+    queries = np.stack([gen.step_queries(w, s, n0 + s + (1 if w.appends else 0), gen.host_fetch(K))
+                        for s in range(total)])
+    log(f"[bench] inputs generated in {time.perf_counter() - t:.1f}s: {w.name} N={n0} steps={steps} warmup={args.warmup}")
+
+    Kd = torch.from_numpy(K).to(tdt).to(dev)
+    Vd = torch.from_numpy(V).to(tdt).to(dev)
+    Rd = torch.from_numpy(refs).to(tdt).to(dev)
+    Qd = torch.from_numpy(queries).to(tdt).to(dev)                    # [steps, Hq, d]
+    Kn = Kd[:, n0:n0 + total].transpose(0, 1).contiguous()            # [steps, Hkv, d]
+    Vn = Vd[:, n0:n0 + total].transpose(0, 1).contiguous()
+    out = torch.empty(w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    stats = torch.zeros(total, w.levels + 1, w.num_kv_heads, dtype=torch.int32, device=dev)
+
+    cfg = zha.make_config(w.head_dim, w.num_kv_heads, w.num_q_heads, w.block, w.levels, w.num_ref,
+                          w.capacity, w.dtype, w.top_p, w.keep_sink)
+    tree = zha.Tree(cfg)
+    h = tree.handle
+
+    # ---- tree build (timed separately; the last build is the one decoded against)
+    torch.cuda.synchronize()
+    build_ms = []
+    for _ in range(max(1, args.build_reps)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tree.build(Kd, Vd, n0, Rd)
+        e1.record()
+        torch.cuda.synchronize()
+        build_ms.append(e0.elapsed_time(e1))
+    build_s = min(build_ms) / 1e3
+    build_tok_s = n0 / build_s
+    build_bytes = n0 * w.num_kv_heads * (w.head_dim * (2 if w.dtype == "bf16" else 4) +
+                                        sum(w.num_ref * (w.head_dim + 1) * 4 / w.block ** l
+                                            for l in range(1, w.levels + 1)))
+    log(f"[bench] build {build_s * 1e3:.3f} ms -> {build_tok_s / 1e9:.3f} G tok/s")
+
+    def step(s):
+        if w.appends:
+            tree.append(Kn[s], Vn[s])
+        tree.decode(Qd[s], out, stats[s])
+
+    # ---- warmup
+    zha.zha_profile_start(h, "append")
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    app_ms, app_n = zha.zha_profile_stop(h)
+    # rank the launches of one extra (untimed, append-free) decode; one bracket per decode
+    # keeps each launch's timing undisturbed by the other brackets
+    keys = ["route_prep", "attend"] + [f"route_{k}.l{l}" for l in range(1, w.levels + 1)
+                                       for k in ("score", "select", "expand")]
+    probe_ms = {}
+    snap = tree.n_tokens
+    for key in keys:
+        zha.zha_profile_start(h, key)
+        tree.decode(Qd[min(args.warmup, total - 1)], out, None)
+        torch.cuda.synchronize()
+        ms, n = zha.zha_profile_stop(h)
+        probe_ms[key] = ms / max(n, 1)
+    assert tree.n_tokens == snap
+    if app_n:
+        probe_ms["append"] = app_ms / app_n
+    dominant = max(probe_ms, key=probe_ms.get)
+    log("[bench] per-launch ms: " + ", ".join(f"{k}={v:.4f}" for k, v in sorted(probe_ms.items(), key=lambda x: -x[1])[:8]))
+
+    # ---- timed region
+    zha.zha_profile_start(h, dominant)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for s in range(args.warmup, total):
+        step(s)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dom_ms, dom_n = zha.zha_profile_stop(h)
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / steps
+    qps = steps / wall
+    st = stats.cpu().numpy()
+    timed_stats = st[args.warmup:]
+    dom_bytes = [kernel_bytes(dominant, w, timed_stats[i], n0 + args.warmup + i + 1) for i in range(steps)]
+    dom_avg_ms = dom_ms / max(dom_n, 1)
+    roofline = None
+    if dom_bytes[0] is not None:
+        alg = float(np.mean(dom_bytes))
+        achieved = alg / (dom_avg_ms * 1e-3) / 1e9
+        roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_for(dominant, w.name),
+                        kernel=dominant, launches=dom_n, avg_launch_ms=round(dom_avg_ms, 4),
+                        algorithmic_bytes_per_launch=round(alg))
+    log(f"[bench] timed {steps} steps: {ms_per_step:.3f} ms/step (events {gpu_ms / steps:.3f}), "
+        f"{qps:.1f} queries/s; dominant {dominant} {dom_avg_ms:.4f} ms/launch")
+
+    # ---- decode-step bytes (router planes + gathered KV), from the routing stats
+    R, d, g, L = w.num_ref, w.head_dim, w.group, w.levels
+    plane = R * (d + 1) * 4
+    router_b = timed_stats[:, :L, :].sum(axis=(1, 2)) * plane
+    gather_b = timed_stats[:, L, :].sum(axis=1) * w.block * 2 * d * 2
+    step_bytes = float(np.mean(router_b + gather_b))
+
+    # ---- dense flash-decode over the same cache (baseline)
+    q_last = Qd[total - 1]
+    for _ in range(3):
+        tree.decode_dense(q_last, out)
+    torch.cuda.synchronize()
+    zha.zha_profile_start(h, "dense_attend")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.dense_reps):
+        tree.decode_dense(q_last, out)
+    e1.record()
+    torch.cuda.synchronize()
+    dense_ms_k, dense_n = zha.zha_profile_stop(h)
+    dense_ms = e0.elapsed_time(e1) / args.dense_reps
+    dense_bytes = tree.n_tokens * w.num_kv_heads * 2 * d * 2
+    log(f"[bench] dense decode {dense_ms:.3f} ms ({dense_bytes / dense_ms / 1e6:.0f} GB/s)")
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    cpu = None
+    if not args.no_cpu:
+        t = time.perf_counter()
+        cpu = cpu_baseline(w, K, V, refs, queries, n0, args.cpu_budget)
+        log(f"[bench] cpu baseline {cpu['value']:.4f} queries/s ({time.perf_counter() - t:.1f}s)")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(qps, 2),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}_{n0}", "kv_tokens": n0, "head_dim": d, "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "block": w.block, "levels": L, "num_ref": R, "top_p": w.top_p,
+                   "batch": 1, "layers": 1, "step": "append + decode"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "decode_step": {"alg_bytes": round(step_bytes), "achieved_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                        "router_bytes": round(float(np.mean(router_b))), "gather_bytes": round(float(np.mean(gather_b))),
+                        "frontier_union_per_level": timed_stats[:, :L, :].sum(axis=2).mean(axis=0).round(1).tolist(),
+                        "kept_blocks_union": float(timed_stats[:, L, :].sum(axis=1).mean())},
+        "build": {"ms": round(build_s * 1e3, 4), "tokens_per_s": round(build_tok_s), "alg_bytes": round(build_bytes),
+                  "frac_hbm": round(build_bytes / build_s / 1e9 / HBM_PEAK_GBS, 4)},
+        "dense": {"ms": round(dense_ms, 4), "queries_per_s": round(1e3 / dense_ms, 2),
+                  "kernel_ms": round(dense_ms_k / max(dense_n, 1), 4), "alg_bytes": dense_bytes,
+                  "frac_hbm": round(dense_bytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "zha_speedup": round(dense_ms / ms_per_step, 3)},
+        "kernel_ms": {k: round(v, 4) for k, v in sorted(probe_ms.items(), key=lambda x: -x[1])},
+        "src_sha": src_sha(),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -70,7 +70,8 @@ hipError_t launch_append(const AppendArgs& a, bool bf16, int D, int R, int hkv, 
 
 // Routing: prep (q to fp32, state reset, top frontier) then per level the step sequence.
 hipError_t launch_route_prep(const RouteArgs& a, bool bf16, int D, hipStream_t st);
-hipError_t launch_route_level(const RouteArgs& a, int D, int R, hipStream_t st);
+hipError_t launch_route_score(const RouteArgs& a, int D, int R, hipStream_t st);
+hipError_t launch_route_select(const RouteArgs& a, hipStream_t st);   // hist, select, classify, resolve
 hipError_t launch_route_expand(const RouteArgs& a, hipStream_t st);
 
 hipError_t launch_attend(const AttnArgs& a, bool bf16, int D, bool dense, hipStream_t st);

@@ -507,13 +507,17 @@ static unsigned grid_for(int64_t n, int64_t per, int64_t cap) {
   return (unsigned)(x < 1 ? 1 : x);
 }
 
-hipError_t launch_route_level(const RouteArgs& a, int D, int R, hipStream_t st) {
+hipError_t launch_route_score(const RouteArgs& a, int D, int R, hipStream_t st) {
 #define ZHA_CASE(DD, RR) else if (D == DD && R == RR) launch_score<DD, RR>(a, st);
   if (false) {}
   ZHA_CASE(64, 1) ZHA_CASE(64, 2) ZHA_CASE(64, 4) ZHA_CASE(64, 8) ZHA_CASE(64, 16)
   ZHA_CASE(128, 1) ZHA_CASE(128, 2) ZHA_CASE(128, 4) ZHA_CASE(128, 8) ZHA_CASE(128, 16)
   else return hipErrorInvalidValue;
 #undef ZHA_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_route_select(const RouteArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(route_hist_kernel, dim3(grid_for(a.nlevel, 2048, 256), (unsigned)a.hq), dim3(256), 0, st, a);
   hipLaunchKernelGGL(route_select_kernel, dim3((unsigned)a.hq), dim3(256), 0, st, a);
   hipLaunchKernelGGL(route_classify_kernel, dim3(grid_for(a.nlevel, 1024, 2048), (unsigned)a.hkv), dim3(256), 0, st, a);

@@ -12,8 +12,16 @@
 
 using namespace zha;
 
+// Event pairs around the launches whose key starts with the active prefix.
+struct Profiler {
+  bool on = false;
+  std::string prefix;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+};
+
 struct zha_tree {
   zha_config cfg;
+  Profiler prof;
   char* ws;
   size_t ws_bytes;
   Dev dev;
@@ -155,13 +163,44 @@ RouteArgs route_args(const zha_tree* t, const void* q) {
   return a;
 }
 
-zha_status route_one_level(zha_tree* t, RouteArgs& a, int lv, hipStream_t st) {
+// Brackets one launch with events when profiling covers `key`.
+struct ProfScope {
+  zha_tree* t;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  ProfScope(zha_tree* t_, const std::string& key, hipStream_t s) : t(t_), st(s) {
+    if (!t->prof.on || key.compare(0, t->prof.prefix.size(), t->prof.prefix) != 0) return;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) { a = b = nullptr; return; }
+    (void)hipEventRecord(a, st);
+  }
+  ~ProfScope() {
+    if (!a) return;
+    (void)hipEventRecord(b, st);
+    t->prof.ev.emplace_back(a, b);
+  }
+};
+
+std::string lvkey(const char* name, int lv) { return std::string(name) + ".l" + std::to_string(lv); }
+
+zha_status route_levels(zha_tree* t, RouteArgs& a, int lv, hipStream_t st, bool expand) {
   a.level = lv;
   a.nlevel = nodes_at(t->cfg, lv, t->N);
   a.nbelow = lv > 1 ? nodes_at(t->cfg, lv - 1, t->N) : 0;
-  hipError_t e = launch_route_level(a, t->cfg.head_dim, t->cfg.num_ref, st);
-  if (e != hipSuccess) return hip_fail(e, "route level launch");
-  e = launch_route_expand(a, st);
+  hipError_t e;
+  {
+    ProfScope ps(t, lvkey("route_score", lv), st);
+    e = launch_route_score(a, t->cfg.head_dim, t->cfg.num_ref, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "route score launch");
+  {
+    ProfScope ps(t, lvkey("route_select", lv), st);
+    e = launch_route_select(a, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "route select launch");
+  if (expand) {
+    ProfScope ps(t, lvkey("route_expand", lv), st);
+    e = launch_route_expand(a, st);
+  }
   if (e != hipSuccess) return hip_fail(e, "route expand launch");
   return ZHA_OK;
 }
@@ -184,9 +223,8 @@ zha_status zha_create(const zha_config* cfg, void* workspace, size_t workspace_b
   const size_t need = layout(*cfg, nullptr, nullptr);
   if (workspace_bytes < need)
     return fail(ZHA_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-  zha_tree* t = new (std::nothrow) zha_tree;
+  zha_tree* t = new (std::nothrow) zha_tree();
   if (!t) return fail(ZHA_E_INVALID, "host allocation failed");
-  memset(t, 0, sizeof *t);
   t->cfg = *cfg;
   t->ws = (char*)workspace;
   t->ws_bytes = workspace_bytes;
@@ -216,8 +254,12 @@ zha_status zha_tree_build(zha_tree* t, void* k_cache, void* v_cache, int64_t n_t
   a.sigma = 1.0f / sqrtf((float)c.head_dim);
   a.dev = t->dev;
   const int T = tile_tokens(c);
-  hipError_t e = launch_build_tile(a, c.dtype == ZHA_BF16, c.head_dim, c.num_ref, ceil_div(n_tokens, T),
-                                   c.num_kv_heads, T, stream);
+  hipError_t e;
+  {
+    ProfScope ps(t, "build_tile", stream);
+    e = launch_build_tile(a, c.dtype == ZHA_BF16, c.head_dim, c.num_ref, ceil_div(n_tokens, T),
+                          c.num_kv_heads, T, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "build tile launch");
   for (int v = a.m + 1; v <= c.levels; ++v) {
     ParentArgs p;
@@ -227,7 +269,10 @@ zha_status zha_tree_build(zha_tree* t, void* k_cache, void* v_cache, int64_t n_t
     p.b = c.block;
     p.nparent = nodes_at(c, v, n_tokens);
     p.nchild = nodes_at(c, v - 1, n_tokens);
-    e = launch_build_parent(p, c.head_dim, c.num_ref, c.num_kv_heads, stream);
+    {
+      ProfScope ps(t, lvkey("build_parent", v), stream);
+      e = launch_build_parent(p, c.head_dim, c.num_ref, c.num_kv_heads, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "build parent launch");
   }
   t->K = k_cache;
@@ -257,7 +302,11 @@ zha_status zha_tree_append(zha_tree* t, const void* k_new, const void* v_new, hi
   a.levels = c.levels;
   a.sigma = 1.0f / sqrtf((float)c.head_dim);
   a.dev = t->dev;
-  hipError_t e = launch_append(a, c.dtype == ZHA_BF16, c.head_dim, c.num_ref, c.num_kv_heads, stream);
+  hipError_t e;
+  {
+    ProfScope ps(t, "append", stream);
+    e = launch_append(a, c.dtype == ZHA_BF16, c.head_dim, c.num_ref, c.num_kv_heads, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "append launch");
   t->N += 1;
   return ZHA_OK;
@@ -271,10 +320,14 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
   const zha_config& c = t->cfg;
   RouteArgs r = route_args(t, q);
   r.nlevel = nodes_at(c, c.levels, t->N);
-  hipError_t e = launch_route_prep(r, c.dtype == ZHA_BF16, c.head_dim, stream);
+  hipError_t e;
+  {
+    ProfScope ps(t, "route_prep", stream);
+    e = launch_route_prep(r, c.dtype == ZHA_BF16, c.head_dim, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "route prep launch");
   for (int lv = c.levels; lv >= 1; --lv) {
-    zha_status s = route_one_level(t, r, lv, stream);
+    zha_status s = route_levels(t, r, lv, stream, true);
     if (s != ZHA_OK) return s;
   }
   AttnArgs a;
@@ -293,7 +346,10 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
   a.keep_sink = c.keep_sink;
   a.sigma = 1.0f / sqrtf((float)c.head_dim);
   a.out = out;
-  e = launch_attend_full(a, c.dtype == ZHA_BF16, c.head_dim, false, stats, c.levels, stream);
+  {
+    ProfScope ps(t, "attend", stream);
+    e = launch_attend_full(a, c.dtype == ZHA_BF16, c.head_dim, false, stats, c.levels, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ZHA_OK;
 }
@@ -320,7 +376,11 @@ zha_status zha_decode_dense(zha_tree* t, const void* q, float* out, hipStream_t 
   a.keep_sink = 0;
   a.sigma = 1.0f / sqrtf((float)c.head_dim);
   a.out = out;
-  hipError_t e = launch_attend(a, c.dtype == ZHA_BF16, c.head_dim, true, stream);
+  hipError_t e;
+  {
+    ProfScope ps(t, "dense_attend", stream);
+    e = launch_attend(a, c.dtype == ZHA_BF16, c.head_dim, true, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "dense attention launch");
   return ZHA_OK;
 }
@@ -413,19 +473,54 @@ zha_status zha_debug_route_level(zha_tree* t, int32_t level, const void* q, cons
   if (e == hipSuccess)
     e = hipMemcpyAsync(t->dev.cnt + (int64_t)level * H, counts, H * 4, hipMemcpyDeviceToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "frontier copy");
-  r.level = level;
-  r.nlevel = n;
-  r.nbelow = level > 1 ? nodes_at(c, level - 1, t->N) : 0;
-  e = launch_route_level(r, c.head_dim, c.num_ref, stream);
-  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  zha_status zs = route_levels(t, r, level, stream, false);
+  if (zs != ZHA_OK) return zs;
+  e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "route level");
   return ZHA_OK;
 }
 
 int64_t zha_num_tokens(const zha_tree* t) { return t ? t->N : -1; }
 
+zha_status zha_profile_start(zha_tree* t, const char* key_prefix) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!key_prefix) return fail(ZHA_E_INVALID, "key prefix is null");
+  if (t->prof.on) return fail(ZHA_E_STATE, "profiling already active");
+  t->prof.on = true;
+  t->prof.prefix = key_prefix;
+  t->prof.ev.clear();
+  return ZHA_OK;
+}
+
+zha_status zha_profile_stop(zha_tree* t, double* total_ms, int64_t* launches) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!t->prof.on) return fail(ZHA_E_STATE, "profiling not active");
+  double tot = 0.0;
+  hipError_t err = hipSuccess;
+  for (auto& pr : t->prof.ev) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    tot += ms;
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
+  const int64_t n = (int64_t)t->prof.ev.size();
+  t->prof.ev.clear();
+  t->prof.on = false;
+  if (err != hipSuccess) return hip_fail(err, "profile events");
+  if (total_ms) *total_ms = tot;
+  if (launches) *launches = n;
+  return ZHA_OK;
+}
+
 zha_status zha_destroy(zha_tree* t) {
   if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  for (auto& pr : t->prof.ev) {
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
   delete t;
   return ZHA_OK;
 }

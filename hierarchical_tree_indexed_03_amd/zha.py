@@ -50,6 +50,8 @@ def _load() -> ctypes.CDLL:
         "zha_debug_level": (I32, [P, I32, P, P, P]),
         "zha_debug_trace": (I32, [P, I32, I64, P, P, P, P, P, P]),
         "zha_debug_route_level": (I32, [P, I32, P, P, P, P, I64, P]),
+        "zha_profile_start": (I32, [P, ctypes.c_char_p]),
+        "zha_profile_stop": (I32, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
         "zha_num_tokens": (I64, [P]),
         "zha_destroy": (I32, [P]),
         "zha_status_string": (ctypes.c_char_p, [I32]),
@@ -64,7 +66,8 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 EXPORTED = ("zha_workspace_bytes", "zha_create", "zha_tree_build", "zha_tree_append", "zha_decode",
             "zha_decode_dense", "zha_debug_level", "zha_debug_trace", "zha_debug_route_level",
-            "zha_num_tokens", "zha_destroy", "zha_status_string", "zha_last_error")
+            "zha_profile_start", "zha_profile_stop", "zha_num_tokens", "zha_destroy", "zha_status_string",
+            "zha_last_error")
 
 
 def _p(x):
@@ -133,6 +136,16 @@ def zha_debug_trace(t, level: int, cap: int, nodes, masks, scores, keep, counts,
 def zha_debug_route_level(t, level: int, q, nodes, masks, counts, cap: int, stream=None):
     _check(_lib.zha_debug_route_level(t, int(level), _p(q), _p(nodes), _p(masks), _p(counts), int(cap),
                                       _s(stream)))
+
+
+def zha_profile_start(t, key_prefix: str):
+    _check(_lib.zha_profile_start(t, key_prefix.encode()))
+
+
+def zha_profile_stop(t) -> tuple[float, int]:
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(_lib.zha_profile_stop(t, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def zha_num_tokens(t) -> int:

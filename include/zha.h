@@ -140,6 +140,17 @@ zha_status zha_debug_route_level(zha_tree* t, int32_t level, const void* q,
                                  const int32_t* nodes, const uint32_t* masks,
                                  const int32_t* counts, int64_t cap, hipStream_t stream);
 
+/* Launch timing for measurement.  zha_profile_start makes every later launch of this
+ * handle whose key starts with `key_prefix` get a pair of HIP events on the launch's
+ * stream.  Keys: "build_tile", "build_parent.l<level>", "append", "route_prep",
+ * "route_score.l<level>", "route_select.l<level>" (histogram, boundary, classification
+ * and resolution), "route_expand.l<level>", "attend" (split-K attention and combine),
+ * "dense_attend".  zha_profile_stop synchronises on the recorded events and returns the
+ * summed elapsed milliseconds and the number of bracketed launches (either pointer
+ * nullable).  ZHA_E_STATE on start while active or stop while inactive. */
+zha_status zha_profile_start(zha_tree* t, const char* key_prefix);
+zha_status zha_profile_stop(zha_tree* t, double* total_ms, int64_t* launches);
+
 /* Tokens currently in the tree (host-side count; no synchronisation). */
 int64_t zha_num_tokens(const zha_tree* t);
 
