@@ -266,12 +266,33 @@ def main():
     dense_bytes = tree.n_tokens * w.num_kv_heads * 2 * d * 2
     log(f"[bench] dense decode {dense_ms:.3f} ms ({dense_bytes / dense_ms / 1e6:.0f} GB/s)")
 
-    if args.calib_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
+    # stream-read probe: practical HBM read bandwidth of a plain streaming kernel (2 GiB)
+    import ctypes
+    plib = ctypes.CDLL(os.path.join(ROOT, "hierarchical_tree_indexed_03_amd", "libzha_probe.so"))
+    plib.zha_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    plib.zha_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    sst = torch.cuda.current_stream().cuda_stream
+    nb = 1 << 31
+    buf = torch.empty(nb, dtype=torch.uint8, device=dev)
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    best = 0.0
+    for blocks in (1024, 2048, 4096):
+        plib.zha_probe_stream_read(buf.data_ptr(), nb, sink.data_ptr(), blocks, sst)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            plib.zha_probe_stream_read(buf.data_ptr(), nb, sink.data_ptr(), blocks, sst)
+        e1.record()
         torch.cuda.synchronize()
-        del a, b
+        best = max(best, nb * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    read_gbs = best
+    log(f"[bench] stream-read probe {read_gbs:.0f} GB/s")
+    if args.calib_copy:
+        dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        plib.zha_probe_copy(buf.data_ptr(), dst.data_ptr(), 1 << 30, 2048, sst)
+        torch.cuda.synchronize()
+        del dst
+    del buf
 
     cpu = None
     if not args.no_cpu:
@@ -307,6 +328,7 @@ def main():
                   "kernel_ms": round(dense_ms_k / max(dense_n, 1), 4), "alg_bytes": dense_bytes,
                   "frac_hbm": round(dense_bytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "zha_speedup": round(dense_ms / ms_per_step, 3)},
+        "hbm_read_probe_GBps": round(read_gbs, 1),
         "kernel_ms": {k: round(v, 4) for k, v in sorted(probe_ms.items(), key=lambda x: -x[1])},
         "src_sha": src_sha(),
     }

@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libzha.so")
+PROBE_OUT = os.path.join(HERE, "libzha_probe.so")   # benchmark-only measurement kernels
 OBJDIR = os.path.join(HERE, "_build")
 ARCH = os.environ.get("ZHA_OFFLOAD_ARCH", "gfx950")
 
@@ -60,6 +61,13 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, OUT)
+    probe_src = os.path.join(CSRC, "probe", "probe.hip")
+    tmp = PROBE_OUT + ".tmp"
+    cmd = [cc, *FLAGS, "-shared", "-fPIC", "-o", tmp, probe_src]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_OUT)
     return OUT
 
 

@@ -9,82 +9,89 @@
 // GPU organisation: split-K flash-decode.  A workgroup owns one KV head and a contiguous
 // slice of its gather list (the kept level-1 blocks of the group's union, each with the
 // mask of heads that kept it), or of all tokens for the dense baseline.  Each wave takes
-// 16 tokens at a time: QK^T for the whole GQA group is one MFMA chain (heads on rows,
-// tokens on columns; each lane reads a contiguous quarter of one key row), scores of heads
-// that did not keep the token's block are masked, online softmax runs per head, and P.V
-// accumulates in fp32 with each lane owning D/64 output dims of every head.  The four
-// waves merge in LDS and the workgroup writes one (max, sum, o) partial per head; a
-// combine kernel merges the splits and adds the sink.
+// 32 tokens at a time (all of the tile's K and V loads issued together; other waves of
+// the SIMD cover the latency).  S^T = K.Q^T for the whole GQA group is an MFMA
+// chain (tokens on rows, heads on columns; each lane reads a contiguous quarter of one key
+// row), scores of heads that did not keep the token's block are masked, online softmax
+// runs per head, and P.V accumulates in fp32 with each lane owning a 4-element slice of
+// the V rows of a subset of the tile's tokens.  The four waves merge in LDS and the
+// workgroup writes one (max, sum, o) partial per head; a combine kernel merges the splits
+// and adds the sink.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace zha {
 
-template <typename TIn, int D>
-struct QkOps;
+// V-row slices owned by one lane in P.V: 8 bytes (4 elements) of bf16, 16 bytes of fp32.
+template <typename TIn> struct Vec;
+template <> struct Vec<bf16_t> {
+  static constexpr int N = 4;
+  typedef uint2 T;
+  __device__ static void to_f32(const uint2& v, float* o) {
+    o[0] = bf16_bits_to_f32(v.x & 0xffffu); o[1] = bf16_bits_to_f32(v.x >> 16);
+    o[2] = bf16_bits_to_f32(v.y & 0xffffu); o[3] = bf16_bits_to_f32(v.y >> 16);
+  }
+  __device__ static uint2 zero() { return make_uint2(0, 0); }
+};
+template <> struct Vec<float> {
+  static constexpr int N = 4;
+  typedef uint4 T;
+  __device__ static void to_f32(const uint4& v, float* o) {
+    o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+  }
+  __device__ static uint4 zero() { return make_uint4(0, 0, 0, 0); }
+};
 
-template <int D>
-struct QkOps<bf16_t, D> {
-  static constexpr int NK = D / 32;
-  bf16x8 qa[NK];
-  __device__ void load_q(const bf16_t* q, int g, int lane) {
-    const int row = lane & 15, kg = lane >> 4;
+// S^T tile = K (16 tokens x D) . Q^T (D x 16 heads) on MFMA; the contraction index is
+// permuted so each lane reads one contiguous D/4 slice of its token's key row.
+template <typename TIn, int D> struct Qk;
+template <int D> struct Qk<bf16_t, D> {
+  static constexpr int NL = D / 32;           // 16-byte loads per lane per 16-token tile
+  bf16x8 q[NL];
+  __device__ void load_q(const bf16_t* qg, int g, int col, int kg) {
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
+    for (int kk = 0; kk < NL; ++kk) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < g) v = *(const uint4*)(q + row * D + kg * (D / 4) + kk * 8);
-      qa[kk] = __builtin_bit_cast(bf16x8, v);
+      if (col < g) v = *(const uint4*)(qg + col * D + kg * (D / 4) + kk * 8);
+      q[kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  __device__ f32x4 scores(const bf16_t* krow, bool valid, int lane) const {
-    const int kg = lane >> 4;
+  __device__ static void load_k(const bf16_t* krow, int kg, uint4* k) {
+#pragma unroll
+    for (int kk = 0; kk < NL; ++kk) k[kk] = *(const uint4*)(krow + kg * (D / 4) + kk * 8);
+  }
+  __device__ f32x4 mma(const uint4* k) const {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (valid) v = *(const uint4*)(krow + kg * (D / 4) + kk * 8);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], __builtin_bit_cast(bf16x8, v), acc, 0, 0, 0);
+    for (int kk = 0; kk < NL; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[kk]), q[kk], acc, 0, 0, 0);
+    return acc;
+  }
+};
+template <int D> struct Qk<float, D> {
+  static constexpr int NL = D / 16;           // float4 loads per lane per tile
+  float q[D / 4];
+  __device__ void load_q(const float* qg, int g, int col, int kg) {
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) q[i] = col < g ? qg[col * D + kg * (D / 4) + i] : 0.f;
+  }
+  __device__ static void load_k(const float* krow, int kg, uint4* k) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) k[i] = *(const uint4*)(krow + kg * (D / 4) + i * 4);
+  }
+  __device__ f32x4 mma(const uint4* k) const {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k[i].x), q[4 * i + 0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k[i].y), q[4 * i + 1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k[i].z), q[4 * i + 2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k[i].w), q[4 * i + 3], acc, 0, 0, 0);
     }
     return acc;
   }
 };
-
-template <int D>
-struct QkOps<float, D> {
-  float qa[D / 4];
-  __device__ void load_q(const float* q, int g, int lane) {
-    const int row = lane & 15, kg = lane >> 4;
-#pragma unroll
-    for (int kk = 0; kk < D / 4; ++kk) qa[kk] = row < g ? q[row * D + kk * 4 + kg] : 0.f;
-  }
-  __device__ f32x4 scores(const float* krow, bool valid, int lane) const {
-    const int kg = lane >> 4;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D / 4; ++kk) {
-      const float kvv = valid ? krow[kk * 4 + kg] : 0.f;
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[kk], kvv, acc, 0, 0, 0);
-    }
-    return acc;
-  }
-};
-
-template <int DPL>
-__device__ __forceinline__ void load_v(const float* p, float (&v)[DPL]) {
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) v[i] = p[i];
-}
-template <int DPL>
-__device__ __forceinline__ void load_v(const bf16_t* p, float (&v)[DPL]) {
-  if constexpr (DPL == 2) {
-    const uint32_t w = *(const uint32_t*)p;
-    v[0] = bf16_bits_to_f32(w & 0xffffu);
-    v[1] = bf16_bits_to_f32(w >> 16);
-  } else {
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) v[i] = to_f32(p[i]);
-  }
-}
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -92,12 +99,32 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+constexpr int ATILE = 32;   // tokens per wave iteration
+
+// Token range of split `split` out of F tokens: chunks are whole multiples of 4 waves x
+// one tile; splits beyond the data get an empty range.
+__device__ __forceinline__ void split_range(int64_t F, int splits, int split, int64_t& fb, int64_t& fe) {
+  int64_t chunk = (F + splits - 1) / splits;
+  const int64_t unit = 4 * ATILE;
+  chunk = (chunk + unit - 1) / unit * unit;
+  if (chunk < unit) chunk = unit;
+  fb = (int64_t)split * chunk;
+  fe = min(fb + chunk, F);
+}
+
 template <typename TIn, int D, bool DENSE>
 __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
-  constexpr int DPL = D / 64;
-  __shared__ float Pl[4][16][16];       // [wave][token][head]
-  __shared__ float Al[4][16];           // [wave][head] rescale factors
-  __shared__ int64_t Tl[4][16];         // [wave][token] token index or -1
+  using VT = typename Vec<TIn>::T;
+  constexpr int VEC = Vec<TIn>::N;            // elements of a V row per lane
+  constexpr int LPRV = D / VEC;               // lanes per V row
+  constexpr int TPI = 64 / LPRV;              // V rows per load instruction
+  constexpr int NV = ATILE / TPI;             // V loads per lane per tile
+  constexpr int NK = Qk<TIn, D>::NL;
+  constexpr int NST = ATILE / 16;
+  __shared__ int64_t Tl[4][ATILE];
+  __shared__ uint32_t Mk[4][ATILE];
+  __shared__ __align__(16) float Pl[4][ATILE][GMAX];
+  __shared__ float Al[4][GMAX];
   __shared__ float Ml[4][GMAX], Ll[4][GMAX];
   __shared__ float Ol[4][GMAX][D];
 
@@ -107,7 +134,6 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   const int g = a.g;
   const TIn* Kb = (const TIn*)a.K + (int64_t)kv * a.cap * D;
   const TIn* Vb = (const TIn*)a.V + (int64_t)kv * a.cap * D;
-  const TIn* qg = (const TIn*)a.q + (int64_t)kv * g * D;
 
   int64_t F;
   const int32_t* gnode = nullptr;
@@ -116,110 +142,124 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
     F = a.N;
   } else {
     const int64_t cap0 = a.dev.ncap[0];
-    F = (int64_t)a.dev.cnt[kv] * a.b;   // level-0 row of the counts: gather list size
+    F = (int64_t)a.dev.cnt[kv] * a.b;   // level-0 count: kept level-1 blocks of the union
     gnode = a.dev.node[0] + kv * cap0;
     gmask = a.dev.mask[0] + kv * cap0;
   }
-  int64_t chunk = (F + a.splits - 1) / a.splits;
-  chunk = (chunk + 63) / 64 * 64;
-  const int64_t fb = (int64_t)split * chunk;
-  const int64_t fe = min(fb + chunk, F);
+  int64_t fb, fe;
+  split_range(F, a.splits, split, fb, fe);
+  if (fb >= fe) return;
 
-  QkOps<TIn, D> qk;
-  qk.load_q(qg, g, lane);
+  Qk<TIn, D> qk;
+  qk.load_q((const TIn*)a.q + (int64_t)kv * g * D, g, col, kg);
 
-  float m[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { m[e] = -INFINITY; l[e] = 0.f; }
-  float o[GMAX][DPL];
+  float m = -INFINITY, l = 0.f;               // softmax state of head `col`
+  float o[GMAX][VEC];
 #pragma unroll
   for (int h = 0; h < GMAX; ++h)
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) o[h][i] = 0.f;
+    for (int i = 0; i < VEC; ++i) o[h][i] = 0.f;
 
-  for (int64_t f0 = fb + wave * 16; f0 < fe; f0 += 64) {
-    // token of this lane's column
-    const int64_t f = f0 + col;
-    bool valid = f < fe;
-    int64_t tok = 0;
-    uint32_t mk = 0xffffffffu;
-    if (valid) {
-      if constexpr (DENSE) {
-        tok = f;
-      } else {
-        const int64_t e = f / a.b;
-        tok = (int64_t)gnode[e] * a.b + (f - e * a.b);
-        mk = gmask[e];
-        valid = tok < a.N;
+  for (int64_t f0 = fb + wave * ATILE; f0 < fe; f0 += 4 * ATILE) {
+    if (lane < ATILE) {   // token indices and head masks of the tile
+      const int64_t f = f0 + lane;
+      int64_t tok = -1;
+      uint32_t mk = 0u;
+      if (f < fe) {
+        if constexpr (DENSE) {
+          tok = f;
+          mk = 0xffffffffu;
+        } else {
+          const int64_t e = f / a.b;
+          const int64_t t = (int64_t)gnode[e] * a.b + (f - e * a.b);
+          if (t < a.N) { tok = t; mk = gmask[e]; }
+        }
+      }
+      Tl[wave][lane] = tok;
+      Mk[wave][lane] = mk;
+    }
+    wave_sync_lds();
+    uint4 kf[NST][NK];
+    VT vf[NV];
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int64_t tk = Tl[wave][st * 16 + col];
+      if (tk >= 0) Qk<TIn, D>::load_k(Kb + tk * D, kg, kf[st]);
+      else
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) kf[st][kk] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int64_t tk = Tl[wave][i * TPI + lane / LPRV];
+      vf[i] = tk >= 0 ? *(const VT*)(Vb + tk * D + (lane % LPRV) * VEC) : Vec<TIn>::zero();
+    }
+    float sc[NST][4];
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const f32x4 acc = qk.mma(kf[st]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = st * 16 + kg * 4 + e;
+        const bool use = col < g && ((Mk[wave][t] >> col) & 1u);
+        sc[st][e] = use ? a.sigma * acc[e] : -INFINITY;
+        rmax = fmaxf(rmax, sc[st][e]);
       }
     }
-    const f32x4 acc = qk.scores(Kb + tok * D, valid, lane);
-    float s[4];
-    float rmax[4];
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+    const float mn = fmaxf(m, rmax);
+    const float alpha = (mn == -INFINITY) ? 1.f : expf(m - mn);
+    float rsum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int h = kg * 4 + e;
-      const bool use = valid && h < g && ((mk >> h) & 1u);
-      s[e] = use ? a.sigma * acc[e] : -INFINITY;
-      rmax[e] = s[e];
-    }
+    for (int st = 0; st < NST; ++st)
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rmax[e] = fmaxf(rmax[e], __shfl_xor(rmax[e], off));
-    float p[4], rsum[4], alpha[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float mn = fmaxf(m[e], rmax[e]);
-      alpha[e] = (mn == -INFINITY) ? 1.f : expf(m[e] - mn);
-      p[e] = (mn == -INFINITY) ? 0.f : expf(s[e] - mn);
-      rsum[e] = p[e];
-      m[e] = mn;
-    }
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rsum[e] += __shfl_xor(rsum[e], off);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      l[e] = l[e] * alpha[e] + rsum[e];
-      Pl[wave][col][kg * 4 + e] = p[e];
-      if (col == 0) Al[wave][kg * 4 + e] = alpha[e];
-    }
-    if (kg == 0) Tl[wave][col] = valid ? tok : -1;
+      for (int e = 0; e < 4; ++e) {
+        const float p = (mn == -INFINITY) ? 0.f : expf(sc[st][e] - mn);
+        rsum += p;
+        if (col < GMAX) Pl[wave][st * 16 + kg * 4 + e][col] = p;
+      }
+    rsum += __shfl_xor(rsum, 16);
+    rsum += __shfl_xor(rsum, 32);
+    l = l * alpha + rsum;
+    m = mn;
+    if (kg == 0 && col < GMAX) Al[wave][col] = alpha;
     wave_sync_lds();
-    // P.V: this lane owns dims [lane*DPL, lane*DPL + DPL) of every head.
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
       const float al = Al[wave][h];
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) o[h][i] *= al;
+      for (int i = 0; i < VEC; ++i) o[h][i] *= al;
     }
-    for (int t = 0; t < 16; ++t) {
-      const int64_t tk = Tl[wave][t];
-      if (tk < 0) continue;
-      float v[DPL];
-      load_v<DPL>(Vb + tk * D + lane * DPL, v);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int t = i * TPI + lane / LPRV;
+      float v[VEC];
+      Vec<TIn>::to_f32(vf[i], v);
       const float4 p0 = *(const float4*)&Pl[wave][t][0];
       const float4 p1 = *(const float4*)&Pl[wave][t][4];
-      const float ph[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      const float ph[GMAX] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
       for (int h = 0; h < GMAX; ++h)
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) o[h][i] += ph[h] * v[i];
+        for (int j = 0; j < VEC; ++j) o[h][j] += ph[h] * v[j];
     }
     wave_sync_lds();
   }
-  // merge the four waves
+  // lanes sharing output dims hold disjoint token subsets: sum them
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int h = kg * 4 + e;
-    if (col == 0 && h < GMAX) { Ml[wave][h] = m[e]; Ll[wave][h] = l[e]; }
-  }
+  for (int off = LPRV; off < 64; off <<= 1)
 #pragma unroll
-  for (int h = 0; h < GMAX; ++h)
+    for (int h = 0; h < GMAX; ++h)
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) Ol[wave][h][lane * DPL + i] = o[h][i];
+      for (int j = 0; j < VEC; ++j) o[h][j] += __shfl_xor(o[h][j], off);
+  if (kg == 0 && col < GMAX) { Ml[wave][col] = m; Ll[wave][col] = l; }
+  if (lane < LPRV)
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) Ol[wave][h][lane * VEC + j] = o[h][j];
   __syncthreads();
   for (int idx = threadIdx.x; idx < g * D; idx += 256) {
     const int h = idx / D, d = idx % D;
@@ -243,11 +283,22 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
 
 template <typename TIn, int D, bool DENSE>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t* stats, int levels) {
+  __shared__ float Ws[MAX_SPLITS];
   __shared__ float red[256];
+  __shared__ float Ored[256 / D][D];
   __shared__ float Ms, Ls_, S0;
   const int hq = blockIdx.x, kv = hq / a.g, gi = hq % a.g;
   const float* base = a.dev.apart + (int64_t)hq * MAX_SPLITS * (D + 2);
-  const int S = a.splits;
+  int64_t F;
+  if constexpr (DENSE) F = a.N;
+  else F = (int64_t)a.dev.cnt[kv] * a.b;
+  int S = 0;   // splits that own tokens
+  for (int s = 0; s < a.splits; ++s) {
+    int64_t fb, fe;
+    split_range(F, a.splits, s, fb, fe);
+    if (fb >= fe) break;
+    S = s + 1;
+  }
   float mloc = -INFINITY;
   for (int s = threadIdx.x; s < S; s += 256) mloc = fmaxf(mloc, base[(int64_t)s * (D + 2)]);
   red[threadIdx.x] = mloc;
@@ -260,11 +311,12 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t* stats
   __syncthreads();
   const float M = Ms;
   float lloc = 0.f;
-  if (M > -INFINITY)
-    for (int s = threadIdx.x; s < S; s += 256) {
-      const float* pp = base + (int64_t)s * (D + 2);
-      lloc += pp[1] * expf(pp[0] - M);
-    }
+  for (int s = threadIdx.x; s < S; s += 256) {
+    const float* pp = base + (int64_t)s * (D + 2);
+    const float w = (M > -INFINITY && pp[1] > 0.f) ? expf(pp[0] - M) : 0.f;
+    Ws[s] = w;
+    lloc += pp[1] * w;
+  }
   red[threadIdx.x] = lloc;
   __syncthreads();
   for (int off = 128; off > 0; off >>= 1) {
@@ -272,8 +324,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t* stats
     __syncthreads();
   }
   if (threadIdx.x == 0) Ls_ = red[0];
-  __syncthreads();
-  // sink: token 0 if this head did not keep block 0
+  // sink: token 0 when this head did not keep block 0
   bool add_sink = false;
   if constexpr (!DENSE) {
     if (a.keep_sink) {
@@ -285,6 +336,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t* stats
   }
   const TIn* K0 = (const TIn*)a.K + (int64_t)kv * a.cap * D;
   const TIn* V0 = (const TIn*)a.V + (int64_t)kv * a.cap * D;
+  __syncthreads();
   if (add_sink) {
     const TIn* qh = (const TIn*)a.q + (int64_t)hq * D;
     float part = 0.f;
@@ -298,18 +350,24 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t* stats
     if (threadIdx.x == 0) S0 = a.sigma * red[0];
     __syncthreads();
   }
+  {   // weighted sum of the split outputs: 256/D split groups per output dim
+    constexpr int G = 256 / D;
+    const int d = threadIdx.x % D, grp = threadIdx.x / D;
+    float O = 0.f;
+#pragma unroll 8
+    for (int s = grp; s < S; s += G) O += Ws[s] * base[(int64_t)s * (D + 2) + 2 + d];
+    Ored[grp][d] = O;
+  }
+  __syncthreads();
   for (int d = threadIdx.x; d < D; d += 256) {
     float O = 0.f;
-    if (M > -INFINITY)
-      for (int s = 0; s < S; ++s) {
-        const float* pp = base + (int64_t)s * (D + 2);
-        O += pp[2 + d] * expf(pp[0] - M);
-      }
-    float L = Ls_, Mx = M;
+#pragma unroll
+    for (int i = 0; i < 256 / D; ++i) O += Ored[i][d];
+    float L = Ls_;
     if (add_sink) {
       const float s0 = S0;
-      const float mn = fmaxf(Mx, s0);
-      const float sa = (Mx == -INFINITY) ? 0.f : expf(Mx - mn);
+      const float mn = fmaxf(M, s0);
+      const float sa = (M == -INFINITY) ? 0.f : expf(M - mn);
       const float sb = expf(s0 - mn);
       O = O * sa + to_f32(V0[d]) * sb;
       L = L * sa + sb;

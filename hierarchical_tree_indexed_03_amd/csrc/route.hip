@@ -29,6 +29,17 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+// Score-kernel tuning: tiles in flight per wave (R >= 8 / R < 8) and max blocks per KV head.
+#ifndef ZHA_SCORE_UN_WIDE
+#define ZHA_SCORE_UN_WIDE 2
+#endif
+#ifndef ZHA_SCORE_UN_NARROW
+#define ZHA_SCORE_UN_NARROW 1
+#endif
+#ifndef ZHA_SCORE_GRID
+#define ZHA_SCORE_GRID 1024
+#endif
+
 namespace zha {
 
 template <typename TIn, int D>
@@ -57,16 +68,20 @@ __global__ __launch_bounds__(256) void route_prep_kernel(RouteArgs a) {
 }
 
 // ------------------------------------------------------------------ score
+// Scores of the union frontier on fp32 MFMA: one 16x16 output tile = the 16 query-head rows
+// (the group's heads, zero-padded) x 16 columns = 16/R nodes x R planes.  The contraction
+// over d is permuted so that lane (column c, group kg) streams the contiguous 64-byte
+// pieces [64i + 16kg, +16) of its plane row; Q uses the same permutation.  A node's score is
+// the max over its R columns (plus the offsets c_j), taken across the R lanes of the node.
 template <int D, int R>
 __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
-  constexpr int LPR = D / 8;
-  constexpr int LPN = (R * LPR) < 64 ? R * LPR : 64;
-  constexpr int NPW = 64 / LPN;
-  constexpr int PPL = R * LPR / LPN;
-  constexpr int PSTRIDE = LPN / LPR;
-  __shared__ float red[4][GMAX];
+  constexpr int NPT = 16 / R;                 // nodes per 16-column tile
+  constexpr int NI = D / 16;                  // float4 loads per lane per tile
+  constexpr int UN = R >= 8 ? ZHA_SCORE_UN_WIDE : ZHA_SCORE_UN_NARROW;   // tiles in flight per wave
+  __shared__ float red[4][16];
   const int kv = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slot = lane / LPN, ln = lane % LPN, dc = ln % LPR, pj = ln / LPR;
+  const int col = lane & 15, kg = lane >> 4;
+  const int slot = col / R, plane = col % R;
   const int lv = a.level;
   const int64_t cnt = a.dev.cnt[lv * a.hkv + kv];
   const int64_t cap = a.dev.ncap[lv];
@@ -77,81 +92,68 @@ __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
   float* out = a.dev.score[lv] + (int64_t)kv * GMAX * cap;
   const int g = a.g;
 
-  float q[GMAX][8];
+  float qa[NI][4];
 #pragma unroll
-  for (int gi = 0; gi < GMAX; ++gi) {
-    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-    if (gi < g) {
-      const float* qp = a.dev.qf + (int64_t)(kv * g + gi) * D + dc * 8;
-      x0 = *(const float4*)qp;
-      x1 = *(const float4*)(qp + 4);
-    }
-    q[gi][0] = x0.x; q[gi][1] = x0.y; q[gi][2] = x0.z; q[gi][3] = x0.w;
-    q[gi][4] = x1.x; q[gi][5] = x1.y; q[gi][6] = x1.z; q[gi][7] = x1.w;
+  for (int i = 0; i < NI; ++i) {
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (col < g) x = *(const float4*)(a.dev.qf + (int64_t)(kv * g + col) * D + 16 * i + 4 * kg);
+    qa[i][0] = x.x; qa[i][1] = x.y; qa[i][2] = x.z; qa[i][3] = x.w;
   }
-  float runmax[GMAX];
-#pragma unroll
-  for (int gi = 0; gi < GMAX; ++gi) runmax[gi] = -INFINITY;
+  float runmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 
-  for (int64_t base = ((int64_t)blockIdx.x * 4 + wave) * NPW; base < cnt;
-       base += (int64_t)gridDim.x * 4 * NPW) {
-    const int64_t e = base + slot;
-    const bool valid = e < cnt;
-    const int64_t nid = valid ? nodes[e] : 0;
-    const uint32_t mk = valid ? masks[e] : 0u;
-    float best[GMAX];
+  const int64_t ntiles = (cnt + NPT - 1) / NPT;
+  for (int64_t t0 = ((int64_t)blockIdx.x * 4 + wave) * UN; t0 < ntiles; t0 += (int64_t)gridDim.x * 4 * UN) {
+    float4 sb[UN][NI];
+    float cj[UN];
+    int64_t ent[UN];
+    bool ok[UN];
 #pragma unroll
-    for (int gi = 0; gi < GMAX; ++gi) best[gi] = -INFINITY;
+    for (int u = 0; u < UN; ++u) {
+      ent[u] = (t0 + u) * NPT + slot;
+      ok[u] = (t0 + u) < ntiles && ent[u] < cnt;
+      const int64_t nid = ok[u] ? nodes[ent[u]] : 0;
+      const float* sp = S + (nid * R + plane) * D + 4 * kg;
 #pragma unroll
-    for (int k = 0; k < PPL; ++k) {
-      const int j = pj + k * PSTRIDE;
-      const float* sp = S + (nid * R + j) * D + dc * 8;
-      float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
-      if (valid) {
-        s0 = *(const float4*)sp;
-        s1 = *(const float4*)(sp + 4);
-      }
-      float dot[GMAX];
-#pragma unroll
-      for (int gi = 0; gi < GMAX; ++gi) {
-        float t = q[gi][0] * s0.x;
-        t += q[gi][1] * s0.y;
-        t += q[gi][2] * s0.z;
-        t += q[gi][3] * s0.w;
-        t += q[gi][4] * s1.x;
-        t += q[gi][5] * s1.y;
-        t += q[gi][6] * s1.z;
-        t += q[gi][7] * s1.w;
-        dot[gi] = t;
-      }
-#pragma unroll
-      for (int off = 1; off < LPR; off <<= 1)
-#pragma unroll
-        for (int gi = 0; gi < GMAX; ++gi) dot[gi] += __shfl_xor(dot[gi], off);
-      const float cj = valid ? C[nid * R + j] : 0.f;
-#pragma unroll
-      for (int gi = 0; gi < GMAX; ++gi) best[gi] = fmaxf(best[gi], dot[gi] + cj);
+      for (int i = 0; i < NI; ++i) sb[u][i] = ok[u] ? *(const float4*)(sp + 16 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      cj[u] = ok[u] ? C[nid * R + plane] : -INFINITY;
     }
 #pragma unroll
-    for (int off = LPR; off < LPN; off <<= 1)
+    for (int u = 0; u < UN; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int gi = 0; gi < GMAX; ++gi) best[gi] = fmaxf(best[gi], __shfl_xor(best[gi], off));
+      for (int i = 0; i < NI; ++i) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][0], sb[u][i].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][1], sb[u][i].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][2], sb[u][i].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][3], sb[u][i].w, acc, 0, 0, 0);
+      }
+      float v[4];
 #pragma unroll
-    for (int gi = 0; gi < GMAX; ++gi) {
-      if (valid && ln == gi && gi < g) out[(int64_t)gi * cap + e] = best[gi];
-      if ((mk >> gi) & 1u) runmax[gi] = fmaxf(runmax[gi], best[gi]);
+      for (int e = 0; e < 4; ++e) v[e] = acc[e] + cj[u];
+#pragma unroll
+      for (int off = 1; off < R; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], __shfl_xor(v[e], off));
+      const uint32_t mk = ok[u] ? masks[ent[u]] : 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int h = kg * 4 + e;
+        if (ok[u] && plane == 0 && h < g) out[(int64_t)h * cap + ent[u]] = v[e];
+        if ((mk >> h) & 1u) runmax[e] = fmaxf(runmax[e], v[e]);
+      }
     }
   }
+  // per-head max: lanes of one 16-lane row share kg, i.e. the heads 4kg..4kg+3
 #pragma unroll
-  for (int gi = 0; gi < GMAX; ++gi) {
-    float v = runmax[gi];
-    for (int off = 1; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
-    if (lane == 0) red[wave][gi] = v;
+  for (int e = 0; e < 4; ++e) {
+    float v = runmax[e];
+    for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (col == 0) red[wave][kg * 4 + e] = v;
   }
   __syncthreads();
   if (threadIdx.x < g) {
     const int gi = threadIdx.x;
-    float m = fmaxf(fmaxf(red[0][gi], red[1][gi]), fmaxf(red[2][gi], red[3][gi]));
+    const float m = fmaxf(fmaxf(red[0][gi], red[1][gi]), fmaxf(red[2][gi], red[3][gi]));
     if (m > -INFINITY) atomicMax(&a.dev.qs[lv * a.hq + kv * g + gi].maxkey, f2key(m));
   }
 }
@@ -492,11 +494,9 @@ hipError_t launch_route_prep(const RouteArgs& a, bool bf16, int D, hipStream_t s
 
 template <int D, int R>
 static void launch_score(const RouteArgs& a, hipStream_t st) {
-  constexpr int LPR = D / 8;
-  constexpr int LPN = (R * LPR) < 64 ? R * LPR : 64;
-  constexpr int NPB = 4 * (64 / LPN);   // nodes per block pass
+  constexpr int NPB = 4 * (16 / R) * (R >= 8 ? ZHA_SCORE_UN_WIDE : ZHA_SCORE_UN_NARROW);   // nodes per block pass
   int64_t x = (a.nlevel + NPB - 1) / NPB;
-  if (x > 2048) x = 2048;
+  if (x > ZHA_SCORE_GRID) x = ZHA_SCORE_GRID;
   if (x < 1) x = 1;
   hipLaunchKernelGGL((route_score_kernel<D, R>), dim3((unsigned)x, (unsigned)a.hkv), dim3(256), 0, st, a);
 }

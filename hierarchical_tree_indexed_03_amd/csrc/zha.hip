@@ -342,7 +342,7 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
   a.hq = c.num_q_heads;
   a.g = a.hq / a.hkv;
   a.b = c.block;
-  a.splits = attn_splits(t->N, 4096, 256);
+  a.splits = 256;   // splits beyond the gathered tokens exit at once
   a.keep_sink = c.keep_sink;
   a.sigma = 1.0f / sqrtf((float)c.head_dim);
   a.out = out;
@@ -372,7 +372,7 @@ zha_status zha_decode_dense(zha_tree* t, const void* q, float* out, hipStream_t 
   a.hq = c.num_q_heads;
   a.g = a.hq / a.hkv;
   a.b = c.block;
-  a.splits = attn_splits(t->N, 2048, MAX_SPLITS);
+  a.splits = attn_splits(t->N, 1024, MAX_SPLITS);
   a.keep_sink = 0;
   a.sigma = 1.0f / sqrtf((float)c.head_dim);
   a.out = out;

@@ -13,7 +13,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libzha.so")
+LIB_PATH = os.environ.get("ZHA_LIB_PATH") or os.path.join(_HERE, "libzha.so")
 
 ZHA_F32, ZHA_BF16 = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "capacity exceeded",
