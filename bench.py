@@ -146,14 +146,19 @@ def main():
     dev = torch.device("cuda:0")
 
     t = time.perf_counter()
-    K, V = gen.kv_cache(w)
+    Kd = torch.empty(w.num_kv_heads, w.capacity, w.head_dim, dtype=tdt, device=dev)
+    Vd = torch.empty_like(Kd)
+    for stream, hh, lo, hi, rows in gen.iter_kv_chunks(w):
+        (Kd if stream == gen.STREAM_K else Vd)[hh, lo:hi] = torch.from_numpy(rows).to(tdt).to(dev)
+    torch.cuda.synchronize()
     refs = gen.ref_queries(w)
-    queries = np.stack([gen.step_queries(w, s, n0 + s + (1 if w.appends else 0), gen.host_fetch(K))
-                        for s in range(total)])
+
+    def fetch(kv, idx):
+        return Kd[kv, torch.as_tensor(idx, device=dev)].float().cpu().numpy()
+
+    queries = np.stack([gen.step_queries(w, s, n0 + s + (1 if w.appends else 0), fetch) for s in range(total)])
     log(f"[bench] inputs generated in {time.perf_counter() - t:.1f}s: {w.name} N={n0} steps={steps} warmup={args.warmup}")
 
-    Kd = torch.from_numpy(K).to(tdt).to(dev)
-    Vd = torch.from_numpy(V).to(tdt).to(dev)
     Rd = torch.from_numpy(refs).to(tdt).to(dev)
     Qd = torch.from_numpy(queries).to(tdt).to(dev)                    # [steps, Hq, d]
     Kn = Kd[:, n0:n0 + total].transpose(0, 1).contiguous()            # [steps, Hkv, d]
@@ -297,7 +302,9 @@ def main():
     cpu = None
     if not args.no_cpu:
         t = time.perf_counter()
-        cpu = cpu_baseline(w, K, V, refs, queries, n0, args.cpu_budget)
+        K0 = Kd[:1].float().cpu().numpy()
+        V0 = Vd[:1].float().cpu().numpy()
+        cpu = cpu_baseline(w, K0, V0, refs, queries, n0, args.cpu_budget)
         log(f"[bench] cpu baseline {cpu['value']:.4f} queries/s ({time.perf_counter() - t:.1f}s)")
 
     rec = {

@@ -160,24 +160,32 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < VEC; ++i) o[h][i] = 0.f;
 
-  for (int64_t f0 = fb + wave * ATILE; f0 < fe; f0 += 4 * ATILE) {
-    if (lane < ATILE) {   // token indices and head masks of the tile
-      const int64_t f = f0 + lane;
-      int64_t tok = -1;
-      uint32_t mk = 0u;
-      if (f < fe) {
-        if constexpr (DENSE) {
-          tok = f;
-          mk = 0xffffffffu;
-        } else {
-          const int64_t e = f / a.b;
-          const int64_t t = (int64_t)gnode[e] * a.b + (f - e * a.b);
-          if (t < a.N) { tok = t; mk = gmask[e]; }
-        }
+  // Token index and head mask of tile position `lane` (the gather-list lookups of the next
+  // tile are issued before the current tile's K/V loads, so they are in flight together).
+  auto lookup = [&](int64_t f0, int64_t& tok, uint32_t& mk) {
+    const int64_t f = f0 + lane;
+    tok = -1;
+    mk = 0u;
+    if (lane < ATILE && f < fe) {
+      if constexpr (DENSE) {
+        tok = f;
+        mk = 0xffffffffu;
+      } else {
+        const int64_t e = f / a.b;
+        const int64_t t = (int64_t)gnode[e] * a.b + (f - e * a.b);
+        if (t < a.N) { tok = t; mk = gmask[e]; }
       }
-      Tl[wave][lane] = tok;
-      Mk[wave][lane] = mk;
     }
+  };
+  int64_t ntok;
+  uint32_t nmk;
+  lookup(fb + wave * ATILE, ntok, nmk);
+  for (int64_t f0 = fb + wave * ATILE; f0 < fe; f0 += 4 * ATILE) {
+    if (lane < ATILE) {
+      Tl[wave][lane] = ntok;
+      Mk[wave][lane] = nmk;
+    }
+    if (f0 + 4 * ATILE < fe) lookup(f0 + 4 * ATILE, ntok, nmk);
     wave_sync_lds();
     uint4 kf[NST][NK];
     VT vf[NV];

@@ -34,7 +34,7 @@
 #define ZHA_SCORE_UN_WIDE 2
 #endif
 #ifndef ZHA_SCORE_UN_NARROW
-#define ZHA_SCORE_UN_NARROW 1
+#define ZHA_SCORE_UN_NARROW 2
 #endif
 #ifndef ZHA_SCORE_GRID
 #define ZHA_SCORE_GRID 1024
@@ -264,28 +264,51 @@ __global__ __launch_bounds__(256) void route_classify_kernel(RouteArgs a) {
   const float* sc = a.dev.score[lv] + (int64_t)kv * GMAX * cap;
   uint32_t* keep = a.dev.keep[lv] + kv * cap;
   const int64_t ccap = a.dev.ncap[1];
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < cnt; e += (int64_t)gridDim.x * 256) {
-    const uint32_t mk = masks[e];
+  const int lane = threadIdx.x & 63;
+  // wave-uniform trip count so every lane takes part in the candidate ballots
+  for (int64_t eb = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63); eb < cnt; eb += (int64_t)gridDim.x * 256) {
+    const int64_t e = eb + lane;
+    const bool valid = e < cnt;
+    const uint32_t mk = valid ? masks[e] : 0u;
     uint32_t kb = 0;
     for (int gi = 0; gi < g; ++gi) {
-      if (!((mk >> gi) & 1u)) continue;
-      if (B1[gi] >= (uint32_t)NB1) { kb |= 1u << gi; continue; }
-      BinMass bm = bin_mass(sc[(int64_t)gi * cap + e], Ms[gi]);
-      if (bm.bin < B1[gi]) {
-        kb |= 1u << gi;
-      } else if (bm.bin == B1[gi]) {
+      bool cand = false;
+      uint64_t cmass = 0;
+      uint32_t csub = 0;
+      if ((mk >> gi) & 1u) {
+        if (B1[gi] >= (uint32_t)NB1) {
+          kb |= 1u << gi;
+        } else {
+          BinMass bm = bin_mass(sc[(int64_t)gi * cap + e], Ms[gi]);
+          if (bm.bin < B1[gi]) kb |= 1u << gi;
+          else if (bm.bin == B1[gi]) { cand = true; cmass = bm.mass; csub = bm.sub; }
+        }
+      }
+      const uint64_t ball = __ballot(cand);
+      if (ball) {
         const int hq = kv * g + gi;
-        atomicAdd((unsigned long long*)a.dev.mass2 + (int64_t)(lv * a.hq + hq) * NB2 + bm.sub,
-                  (unsigned long long)bm.mass);
-        const uint32_t pos = atomicAdd(&a.dev.qs[lv * a.hq + hq].ncand, 1u);
-        a.dev.cand[(int64_t)hq * ccap + pos] = (int32_t)e;
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&a.dev.qs[lv * a.hq + hq].ncand, (uint32_t)__popcll(ball));
+        base = __shfl(base, 0);
+        if (cand) {
+          const uint32_t pos = base + (uint32_t)__popcll(ball & ((1ull << lane) - 1ull));
+          a.dev.cand[(int64_t)hq * ccap + pos] = (int32_t)e;
+          atomicAdd((unsigned long long*)a.dev.mass2 + (int64_t)(lv * a.hq + hq) * NB2 + csub,
+                    (unsigned long long)cmass);
+        }
       }
     }
-    keep[e] = kb;
+    if (valid) keep[e] = kb;
   }
 }
 
 // ------------------------------------------------------------------ resolve
+__device__ __forceinline__ void wave_sync_lds_r() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ uint64_t rank_key(float s, int32_t e) {
   return ((uint64_t)(~f2key(s)) << 32) | (uint32_t)e;   // ascending = rank order
 }
@@ -408,8 +431,11 @@ __global__ __launch_bounds__(256) void route_expand_count_kernel(RouteArgs a) {
 }
 
 __global__ __launch_bounds__(256) void route_expand_emit_kernel(RouteArgs a) {
-  __shared__ int32_t red[4];
+  __shared__ int32_t red[4], red2[4];
   __shared__ int32_t ts[256];
+  __shared__ int32_t eoff[EXPAND_CHUNK + 1];   // exclusive output offset of each entry
+  __shared__ int32_t enode[EXPAND_CHUNK];
+  __shared__ uint32_t ekeep[EXPAND_CHUNK];
   const int kv = blockIdx.y, lv = a.level;
   const int64_t cnt = a.dev.cnt[lv * a.hkv + kv];
   const int64_t cap = a.dev.ncap[lv];
@@ -426,56 +452,61 @@ __global__ __launch_bounds__(256) void route_expand_emit_kernel(RouteArgs a) {
     pre += __shfl_xor(pre, off);
     tot += __shfl_xor(tot, off);
   }
-  __shared__ int32_t red2[4];
   if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6] = pre; red2[threadIdx.x >> 6] = tot; }
+  // each thread owns 4 consecutive entries of the chunk
+  const int64_t c0 = (int64_t)blockIdx.x * EXPAND_CHUNK;
+  int32_t cnt4[4];
+  int32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = threadIdx.x * 4 + i;
+    const int64_t e = c0 + j;
+    int32_t nd = 0;
+    uint32_t kb = 0;
+    cnt4[i] = 0;
+    if (e < cnt) {
+      nd = a.dev.node[lv][kv * cap + e];
+      kb = a.dev.keep[lv][kv * cap + e];
+      cnt4[i] = emitted(a, nd, kb);
+    }
+    enode[j] = nd;
+    ekeep[j] = kb;
+    mine += cnt4[i];
+  }
+  ts[threadIdx.x] = mine;
   __syncthreads();
   const int32_t base = red[0] + red[1] + red[2] + red[3];
   const int out_lv = lv - 1;
   if (blockIdx.x == 0 && threadIdx.x == 0)
     a.dev.cnt[out_lv * a.hkv + kv] = red2[0] + red2[1] + red2[2] + red2[3];
-  // each thread owns 4 consecutive entries of the chunk
-  const int64_t e0 = (int64_t)blockIdx.x * EXPAND_CHUNK + threadIdx.x * 4;
-  int32_t cnt4[4];
-  int64_t nid[4];
-  uint32_t kb[4];
-  int32_t mine = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t e = e0 + i;
-    nid[i] = 0; kb[i] = 0; cnt4[i] = 0;
-    if (e < cnt) {
-      nid[i] = a.dev.node[lv][kv * cap + e];
-      kb[i] = a.dev.keep[lv][kv * cap + e];
-      cnt4[i] = emitted(a, nid[i], kb[i]);
-    }
-    mine += cnt4[i];
-  }
-  ts[threadIdx.x] = mine;
-  __syncthreads();
   for (int off = 1; off < 256; off <<= 1) {
     const int32_t add = threadIdx.x >= off ? ts[threadIdx.x - off] : 0;
     __syncthreads();
     ts[threadIdx.x] += add;
     __syncthreads();
   }
-  int64_t pos = base + ts[threadIdx.x] - mine;
-  const int64_t ocap = a.dev.ncap[out_lv];
-  int32_t* onode = a.dev.node[out_lv] + kv * ocap;
-  uint32_t* omask = a.dev.mask[out_lv] + kv * ocap;
+  int32_t run = ts[threadIdx.x] - mine;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (!cnt4[i]) continue;
-    if (lv == 1) {
-      onode[pos] = (int32_t)nid[i];
-      omask[pos] = kb[i];
-      ++pos;
-    } else {
-      for (int c = 0; c < cnt4[i]; ++c) {
-        onode[pos] = (int32_t)(nid[i] * a.b + c);
-        omask[pos] = kb[i];
-        ++pos;
-      }
+    eoff[threadIdx.x * 4 + i] = run;
+    run += cnt4[i];
+  }
+  if (threadIdx.x == 255) eoff[EXPAND_CHUNK] = ts[255];
+  __syncthreads();
+  // coalesced emission: consecutive threads write consecutive output slots
+  const int32_t total = eoff[EXPAND_CHUNK];
+  const int64_t ocap = a.dev.ncap[out_lv];
+  int32_t* onode = a.dev.node[out_lv] + kv * ocap + base;
+  uint32_t* omask = a.dev.mask[out_lv] + kv * ocap + base;
+  for (int32_t o = threadIdx.x; o < total; o += 256) {
+    int lo = 0, hi = EXPAND_CHUNK - 1;   // last entry j with eoff[j] <= o
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (eoff[mid] <= o) lo = mid; else hi = mid - 1;
     }
+    const int32_t c = o - eoff[lo];
+    onode[o] = lv == 1 ? enode[lo] : enode[lo] * a.b + c;
+    omask[o] = ekeep[lo];
   }
 }
 

@@ -164,3 +164,16 @@ def test_planted_mistake_is_caught(monkeypatch, name, mut):
     monkeypatch.setattr(zo, name, mut(getattr(zo, name)))
     caught = [c.__name__ for c in pins.ALL if not c()[0]]
     assert caught, f"mutation of {name} passed every pin"
+
+
+def test_chunked_generation_matches_whole():
+    """The chunked K/V stream used for large caches yields the same values as the whole-
+    cache generator (inputs are identical on both sides of every comparison)."""
+    from workloads import gen
+    w = wc.DEEP.with_(n_tokens=3000, steps=2)
+    K, V = gen.kv_cache(w)
+    seen = 0
+    for s, h, lo, hi, rows in gen.iter_kv_chunks(w):
+        assert np.array_equal((K if s == gen.STREAM_K else V)[h, lo:hi], rows)
+        seen += hi - lo
+    assert seen == 2 * w.num_kv_heads * w.capacity

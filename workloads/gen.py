@@ -88,6 +88,31 @@ def token_rows(w: Workload, stream: int, head: int, start: int, stop: int) -> np
     return out
 
 
+def iter_kv_chunks(w: Workload, n: int | None = None, workers: int | None = None):
+    """Yields (stream, kv_head, start, stop, float32 rows [stop-start, d]) for every chunk of
+    the K (stream 0) and V (stream 1) caches over tokens [0, n), generated in parallel with a
+    bounded number of chunks alive at once.  Same values as kv_cache()."""
+    n = w.capacity if n is None else n
+    jobs = [(s, h, c) for s in (STREAM_K, STREAM_V) for h in range(w.num_kv_heads)
+            for c in range(0, -(-n // CHUNK))]
+    workers = workers or _workers()
+
+    def run(job):
+        s, h, c = job
+        lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
+        rows = round_storage(_chunk_rows(w.cfg_id, s, h, c, hi - lo, w.head_dim), w.dtype)
+        return s, h, lo, hi, rows
+
+    with cf.ThreadPoolExecutor(workers) as ex:
+        pending = []
+        for job in jobs:
+            pending.append(ex.submit(run, job))
+            if len(pending) >= 2 * workers:
+                yield pending.pop(0).result()
+        for f in pending:
+            yield f.result()
+
+
 def kv_cache(w: Workload, n: int | None = None) -> tuple[np.ndarray, np.ndarray]:
     """K, V as float32 arrays [Hkv, n, d] (n defaults to the capacity), storage-rounded."""
     n = w.capacity if n is None else n
