@@ -1,0 +1,176 @@
+"""GPU parity at the benchmark's full sizes, through the C ABI, in the launch configuration
+bench.py times (the library picks grids from the token count alone).
+
+* deep (256K, 6 levels, R 16) and wide (256K, 1 level, R 16): one append+decode step
+  compared end to end with the oracle (full oracle trees), plus the routing chain checks.
+* light sweep sizes (32K..1M, R 1): end to end for one step each.
+* ultra (16M tokens): sampled checks that the oracle can compute one by one —
+  planes of sampled nodes (oracle built from each node's own span), scores of sampled
+  frontier nodes, the top-p decision re-derived by the oracle from the GPU's own scores at
+  every level, the frontier = children-of-kept chain, and attention over the GPU's gathered
+  set for every query head.
+Tolerances: tests/parity.py.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import parity as P
+from oracle import zha_oracle as zo
+from workloads import configs as wc, gen
+
+pytestmark = pytest.mark.gpu
+
+
+def upload_chunked(w):
+    dt = P.torch_dtype(w)
+    Kd = torch.empty(w.num_kv_heads, w.capacity, w.head_dim, dtype=dt, device="cuda")
+    Vd = torch.empty_like(Kd)
+    for s, h, lo, hi, rows in gen.iter_kv_chunks(w):
+        (Kd if s == gen.STREAM_K else Vd)[h, lo:hi] = torch.from_numpy(rows).to(dt).cuda()
+    return Kd, Vd
+
+
+def fetch_rows(Kd):
+    return lambda kv, idx: Kd[kv, torch.as_tensor(np.asarray(idx), device="cuda")].float().cpu().numpy()
+
+
+def check_chain(w, t, q, n, routes_oracle=None, Kd=None, Vd=None, sample_scores=None):
+    """Per query head: frontier(l-1) = children of kept(l); kept(l) = top-p of the GPU's own
+    scores (oracle arithmetic, fp64 masses); gathered tokens -> attention parity."""
+    g, b, p = w.group, w.block, w.top_p
+    traces = {lv: t.trace(lv) for lv in range(0, w.levels + 1)}
+    for h in range(w.num_q_heads):
+        kv, gi = divmod(h, g)
+        exempt = set()
+        prev_kept = None
+        for lv in range(w.levels, 0, -1):
+            tr = traces[lv][kv]
+            nodes = tr["nodes"].numpy().astype(np.int64)
+            inm = ((tr["masks"].numpy().astype(np.int64) & 0xFFFFFFFF) >> gi) & 1 == 1
+            fr = nodes[inm]
+            if prev_kept is not None:
+                ch = (np.asarray(sorted(prev_kept))[:, None] * b + np.arange(b)[None, :]).ravel()
+                ch = ch[ch < w.nodes(lv, n)]
+                assert np.array_equal(np.sort(ch), fr), f"head {h} level {lv}: frontier != children of kept"
+            s_fr = tr["scores"][gi].numpy().astype(np.float64)[inm]
+            sel = zo.top_p(fr, s_fr, p)
+            kept = P.gpu_kept(tr, gi)
+            diff = np.array(sorted(set(kept.tolist()) ^ set(sel["kept"].tolist())), dtype=np.int64)
+            rec = dict(frontier=fr, scores=s_fr, **sel)
+            ok, bad = P.exempt_nodes(rec, p, diff)
+            assert not bad, f"head {h} level {lv}: kept set is not the top-p of the GPU scores: {bad[:4]}"
+            exempt |= set(ok)
+            prev_kept = set(kept.tolist())
+        blocks = P.gpu_frontier(traces[0][kv], gi)
+        assert set(blocks.tolist()) == prev_kept, f"head {h}: gather list != kept level-1 blocks"
+    return traces
+
+
+def attention_given_set(w, traces, o, q, n, Kd, Vd, heads):
+    for h in heads:
+        kv, gi = divmod(h, w.group)
+        toks = P.gpu_tokens(traces[0][kv], gi, w.block, n, w.keep_sink)
+        tk = torch.as_tensor(toks, device="cuda")
+        k = Kd[kv, tk].double().cpu().numpy()
+        v = Vd[kv, tk].double().cpu().numpy()
+        ref = zo.attend(k, v, q[h], np.arange(len(toks)))
+        err = P.out_err(o[h], ref)
+        assert err <= P.OUT_RTOL, f"head {h}: attention over the routed set err {err:.3e}"
+
+
+@pytest.mark.parametrize("name", ["deep", "wide"])
+def test_256k_end_to_end(name):
+    w = wc.NAMED[name].with_(steps=1)
+    K, V = gen.kv_cache(w)
+    refs = gen.ref_queries(w)
+    Kd, Vd = P.upload(K, w), P.upload(V, w)
+    t = P.make_tree(w)
+    t.build(Kd, Vd, w.n_tokens, P.upload(refs, w))
+    t.append(Kd[:, w.n_tokens].contiguous(), Vd[:, w.n_tokens].contiguous())
+    n = w.n_tokens + 1
+    q = gen.step_queries(w, 0, n, gen.host_fetch(K))
+    o = t.decode(P.upload(q, w)).cpu().numpy()
+    traces = check_chain(w, t, q, n)
+    attention_given_set(w, traces, o, q, n, Kd, Vd, range(w.num_q_heads))
+    # full oracle, end to end
+    trees = P.oracle_trees(w, K, refs, n)
+    o_ref, routes = zo.decode(trees, V, q, w.top_p, w.keep_sink, return_routes=True)
+    for h in range(w.num_q_heads):
+        kv, gi = divmod(h, w.group)
+        rep = P.compare_route(routes[h], {lv: traces[lv][kv] for lv in traces}, gi, w.block, w.top_p)
+        assert not rep["bad"], f"head {h}: {rep['bad'][:4]}"
+        if not rep["exempt"]:
+            assert P.out_err(o[h], o_ref[h]) <= P.OUT_RTOL
+    # dense decode at full size
+    od = t.decode_dense(P.upload(q, w)).cpu().numpy()
+    ref_d = zo.dense_decode(K, V, q, n)
+    assert P.out_err(od, ref_d) <= P.OUT_RTOL
+
+
+@pytest.mark.parametrize("n_tokens", wc.LIGHT_SIZES)
+def test_light_sweep_end_to_end(n_tokens):
+    w = wc.light(n_tokens, steps=1)
+    K, V = gen.kv_cache(w)
+    refs = gen.ref_queries(w)
+    Kd, Vd = P.upload(K, w), P.upload(V, w)
+    t = P.make_tree(w)
+    t.build(Kd, Vd, w.n_tokens, P.upload(refs, w))
+    t.append(Kd[:, w.n_tokens].contiguous(), Vd[:, w.n_tokens].contiguous())
+    n = w.n_tokens + 1
+    q = gen.step_queries(w, 0, n, gen.host_fetch(K))
+    o = t.decode(P.upload(q, w)).cpu().numpy()
+    traces = check_chain(w, t, q, n)
+    trees = P.oracle_trees(w, K, refs, n)
+    o_ref, routes = zo.decode(trees, V, q, w.top_p, w.keep_sink, return_routes=True)
+    for h in range(w.num_q_heads):
+        kv, gi = divmod(h, w.group)
+        rep = P.compare_route(routes[h], {lv: traces[lv][kv] for lv in traces}, gi, w.block, w.top_p)
+        assert not rep["bad"], f"head {h}: {rep['bad'][:4]}"
+        if not rep["exempt"]:
+            assert P.out_err(o[h], o_ref[h]) <= P.OUT_RTOL
+
+
+def test_ultra_16m_sampled():
+    w = wc.ULTRA.with_(steps=1)
+    Kd, Vd = upload_chunked(w)
+    refs = gen.ref_queries(w)
+    t = P.make_tree(w)
+    t.build(Kd, Vd, w.n_tokens, P.upload(refs, w))
+    t.append(Kd[:, w.n_tokens].contiguous(), Vd[:, w.n_tokens].contiguous())
+    n = w.n_tokens + 1
+    q = gen.step_queries(w, 0, n, fetch_rows(Kd))
+    o = t.decode(P.upload(q, w)).cpu().numpy()
+    traces = check_chain(w, t, q, n)
+    attention_given_set(w, traces, o, q, n, Kd, Vd, range(w.num_q_heads))
+    # sampled planes and scores against the oracle, per level, computed from node spans
+    rng = np.random.default_rng(0)
+    sig = 1.0 / math.sqrt(w.head_dim)
+    for lv in range(1, w.levels + 1):
+        s_gpu, c_gpu = t.level(lv)
+        nl = w.nodes(lv, n)
+        span = w.block ** lv
+        picks = sorted(set(rng.integers(0, nl, 3).tolist()) | {nl - 1})
+        if span > 300_000:
+            picks = [nl - 1]
+        for kv in range(w.num_kv_heads):
+            tr = traces[lv][kv]
+            tnodes = tr["nodes"].numpy().astype(np.int64)
+            for node in picks:
+                lo, hi = node * span, min((node + 1) * span, n)
+                keys = Kd[kv, lo:hi].double().cpu().numpy()
+                ot = zo.build_tree(keys, refs[kv], w.block, lv, hi - lo)
+                so, co = ot.levels[lv - 1][0][0], ot.levels[lv - 1][1][0]
+                sg, cg = s_gpu[kv, node].cpu().numpy(), c_gpu[kv, node].cpu().numpy()
+                assert np.max(np.abs(sg - so)) <= 1e-4 * max(1.0, np.max(np.abs(so))), f"s level {lv} node {node}"
+                assert np.max(np.abs(cg - co)) <= 1e-3, f"c level {lv} node {node}"
+                pos = int(np.searchsorted(tnodes, node))
+                if pos < len(tnodes) and tnodes[pos] == node:
+                    for g_ in range(w.group):
+                        ref = float(np.max(sig * (so @ q[kv * w.group + g_]) + co))
+                        got = float(tr["scores"][g_][pos])
+                        assert abs(got - ref) <= P.SCORE_TOL, f"score level {lv} node {node}: {got} vs {ref}"
