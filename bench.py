@@ -201,8 +201,8 @@ def main():
     app_ms, app_n = zha.zha_profile_stop(h)
     # rank the launches of one extra (untimed, append-free) decode; one bracket per decode
     # keeps each launch's timing undisturbed by the other brackets
-    keys = ["route_prep", "attend"] + [f"route_{k}.l{l}" for l in range(1, w.levels + 1)
-                                       for k in ("score", "select", "expand")]
+    keys = ["route_prep", "attend", "route_score.top", "route_select.top"] + [
+        f"route_{k}.l{l}" for l in range(1, w.levels + 1) for k in ("score", "select", "expand")]
     probe_ms = {}
     snap = tree.n_tokens
     for key in keys:

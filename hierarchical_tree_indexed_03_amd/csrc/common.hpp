@@ -7,13 +7,14 @@ namespace zha {
 
 constexpr int MAXL = 16;        // max summary levels
 constexpr int GMAX = 8;         // max query heads per KV head (group size)
-constexpr int NB1 = 2048;       // coarse top-p bins over delta = max score - score
-constexpr float BINS_PER_UNIT = 64.f;   // coarse bins per unit of score (covers delta < 32)
-constexpr int NB2 = 2048;       // fine sub-bins inside the boundary coarse bin
+constexpr int NB1 = 512;        // coarse top-p bins over delta = max score - score
+constexpr float BINS_PER_UNIT = 16.f;   // coarse bins per unit of score (covers delta < 32)
+constexpr int NB2 = 512;        // fine sub-bins inside the boundary coarse bin
 constexpr float MASS_SCALE = 1099511627776.0f;  // 2^40: fixed-point unit of probability mass
 constexpr int CAND_PAIRWISE = 256;  // boundary ties resolved pairwise in LDS up to this many
 constexpr int EXPAND_CHUNK = 1024;  // union-list entries per expand workgroup
 constexpr int MAX_SPLITS = 512;     // attention splits per KV head
+constexpr int SEL_P = 64;           // top-p histogram / classify workgroups per KV head (max)
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
@@ -59,7 +60,7 @@ struct QState {
   uint32_t maxkey;    // ordered key of the max score over the head's frontier
   uint32_t b1;        // boundary coarse bin; NB1 => keep every frontier node
   uint32_t b2;        // boundary fine sub-bin inside b1
-  uint32_t ncand;     // frontier nodes of this head that fell into bin b1
+  uint32_t ncand;     // frontier nodes of this head that fell into bin b1 (candidate list length)
   uint64_t total;     // sum of fixed-point masses (Z)
   uint64_t target;    // ceil(p * Z): the kept prefix must reach this mass
   uint64_t above1;    // mass of bins < b1
@@ -85,8 +86,7 @@ struct Dev {
   int32_t* part[MAXL + 1];  // [Hkv][nchunks(l)]        expand partial counts
   int32_t* cnt;             // [MAXL + 1][Hkv]
   QState* qs;               // [MAXL + 1][Hq]
-  uint64_t* mass1;          // [MAXL + 1][Hq][NB1]
-  uint64_t* mass2;          // [MAXL + 1][Hq][NB2]
+  uint64_t* hpart;          // [Hkv][SEL_P][GMAX][NB1] per-workgroup coarse mass histograms
   int32_t* cand;            // [Hq][ncap[1]]
   float* qf;                // [Hq][D] sigma * q in fp32
   float* apart;             // [Hq][MAX_SPLITS][D + 2] attention partials (m, l, o)

@@ -47,6 +47,10 @@ struct RouteArgs {
   int64_t nbelow;     // nodes at level-1 (children existence); unused at level 1
   float top_p;
   float sigma;
+  int32_t dense;      // score kernel: 1 = every node of levels `level` .. `level`-gridDim.z+1
+  int32_t dense_lo;   // lowest level handled by the multi-level selection kernel
+  int32_t sel_p;      // top-p histogram / classify workgroups per KV head at `level`
+  int64_t nl[MAXL + 1];   // nodes per level at N
 };
 
 struct AttnArgs {
@@ -73,6 +77,12 @@ hipError_t launch_route_prep(const RouteArgs& a, bool bf16, int D, hipStream_t s
 hipError_t launch_route_score(const RouteArgs& a, int D, int R, hipStream_t st);
 hipError_t launch_route_select(const RouteArgs& a, hipStream_t st);   // hist, select, classify, resolve
 hipError_t launch_route_expand(const RouteArgs& a, hipStream_t st);
+// Top levels with at most MLS_MAX nodes: score every node of levels `level`..`dense_lo`
+// in one launch, then select all of them top-down in one launch (one workgroup per KV
+// head), emitting the frontier of level `dense_lo - 1` (or the gather list).
+constexpr int MLS_MAX = 2112;   // 2048 + room for the nodes appends add
+hipError_t launch_route_dense_score(const RouteArgs& a, int D, int R, hipStream_t st);
+hipError_t launch_route_mls(const RouteArgs& a, hipStream_t st);
 
 hipError_t launch_attend(const AttnArgs& a, bool bf16, int D, bool dense, hipStream_t st);
 // Same, and copies the per-level union sizes into `stats` ([levels + 1][Hkv], nullable).

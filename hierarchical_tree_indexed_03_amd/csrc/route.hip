@@ -53,8 +53,6 @@ __global__ __launch_bounds__(256) void route_prep_kernel(RouteArgs a) {
     QState z = {};
     a.dev.qs[i] = z;
   }
-  for (int64_t i = tid; i < nq * NB1; i += nth) a.dev.mass1[i] = 0;
-  for (int64_t i = tid; i < nq * NB2; i += nth) a.dev.mass2[i] = 0;
   const int L = a.levels;
   const int64_t capL = a.dev.ncap[L];
   const uint32_t full = (a.g >= 32) ? 0xffffffffu : ((1u << a.g) - 1u);
@@ -82,8 +80,9 @@ __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
   const int kv = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const int slot = col / R, plane = col % R;
-  const int lv = a.level;
-  const int64_t cnt = a.dev.cnt[lv * a.hkv + kv];
+  const bool dense = a.dense != 0;            // every node of the level, no list
+  const int lv = dense ? a.level - (int)blockIdx.z : a.level;
+  const int64_t cnt = dense ? a.nl[lv] : a.dev.cnt[lv * a.hkv + kv];
   const int64_t cap = a.dev.ncap[lv];
   const int32_t* nodes = a.dev.node[lv] + kv * cap;
   const uint32_t* masks = a.dev.mask[lv] + kv * cap;
@@ -111,7 +110,7 @@ __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
     for (int u = 0; u < UN; ++u) {
       ent[u] = (t0 + u) * NPT + slot;
       ok[u] = (t0 + u) < ntiles && ent[u] < cnt;
-      const int64_t nid = ok[u] ? nodes[ent[u]] : 0;
+      const int64_t nid = ok[u] ? (dense ? ent[u] : (int64_t)nodes[ent[u]]) : 0;
       const float* sp = S + (nid * R + plane) * D + 4 * kg;
 #pragma unroll
       for (int i = 0; i < NI; ++i) sb[u][i] = ok[u] ? *(const float4*)(sp + 16 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -134,7 +133,7 @@ __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
       for (int off = 1; off < R; off <<= 1)
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], __shfl_xor(v[e], off));
-      const uint32_t mk = ok[u] ? masks[ent[u]] : 0u;
+      const uint32_t mk = (ok[u] && !dense) ? masks[ent[u]] : 0u;   // dense: max taken later
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int h = kg * 4 + e;
@@ -159,146 +158,227 @@ __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
 }
 
 // ------------------------------------------------------------------ histogram
-__global__ __launch_bounds__(256) void route_hist_kernel(RouteArgs a) {
-  __shared__ unsigned long long h[NB1];
-  const int hq = blockIdx.y, kv = hq / a.g, gi = hq % a.g, lv = a.level;
-  const uint32_t mk = a.dev.qs[lv * a.hq + hq].maxkey;
-  if (mk == 0u) return;   // empty frontier for this head
-  for (int i = threadIdx.x; i < NB1; i += 256) h[i] = 0ull;
+// Large levels pick each head's top-p set in four launches: partial coarse histograms
+// (hist), their reduction and the boundary bin (bound), keep / candidate classification
+// (classify) and the exact decision inside the boundary bin (resolve).  No step needs a
+// contended global atomic: partial histograms are plain stores and candidates are appended
+// in per-workgroup batches.
+constexpr int SEL_THREADS = 512;
+constexpr int HIST_U = 2;          // union entries per thread per iteration (loads issued together)
+constexpr int CAND_STAGE = 1024;   // candidates staged per head in LDS before a batch append
+
+// Each workgroup takes a contiguous range of the KV head's union list, reads every entry's
+// mask once and adds the node's mass to the coarse histogram of every head of the group
+// that has it in its frontier; the workgroup's histograms are stored whole.
+__global__ __launch_bounds__(SEL_THREADS) void route_hist_kernel(RouteArgs a) {
+  __shared__ unsigned long long h[GMAX][NB1];
+  __shared__ float Ms[GMAX];
+  const int kv = blockIdx.y, lv = a.level, g = a.g;
+  if (threadIdx.x < GMAX) {
+    const uint32_t mk = threadIdx.x < g ? a.dev.qs[lv * a.hq + kv * g + threadIdx.x].maxkey : 0u;
+    Ms[threadIdx.x] = mk ? key2f(mk) : -INFINITY;
+  }
+  for (int i = threadIdx.x; i < GMAX * NB1; i += SEL_THREADS) (&h[0][0])[i] = 0ull;
   __syncthreads();
-  const float M = key2f(mk);
   const int64_t cnt = a.dev.cnt[lv * a.hkv + kv];
   const int64_t cap = a.dev.ncap[lv];
+  const int64_t per = (cnt + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per, hi = lo + per < cnt ? lo + per : cnt;
   const uint32_t* masks = a.dev.mask[lv] + kv * cap;
-  const float* sc = a.dev.score[lv] + ((int64_t)kv * GMAX + gi) * cap;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < cnt; e += (int64_t)gridDim.x * 256) {
-    if ((masks[e] >> gi) & 1u) {
-      BinMass bm = bin_mass(sc[e], M);
-      atomicAdd(&h[bm.bin], (unsigned long long)bm.mass);
+  const float* sc = a.dev.score[lv] + (int64_t)kv * GMAX * cap;
+  for (int64_t e0 = lo + threadIdx.x; e0 < hi; e0 += SEL_THREADS * HIST_U) {
+    uint32_t mk[HIST_U];
+    float v[HIST_U][GMAX];
+#pragma unroll
+    for (int u = 0; u < HIST_U; ++u) {
+      const int64_t e = e0 + SEL_THREADS * u;
+      mk[u] = e < hi ? masks[e] : 0u;
+      // score rows exist for all GMAX heads; only entries with the head's bit are used
+#pragma unroll
+      for (int gi = 0; gi < GMAX; ++gi) v[u][gi] = (gi < g && e < hi) ? sc[(int64_t)gi * cap + e] : 0.f;
     }
+#pragma unroll
+    for (int u = 0; u < HIST_U; ++u)
+#pragma unroll
+      for (int gi = 0; gi < GMAX; ++gi)
+        if ((mk[u] >> gi) & 1u) {
+          const BinMass bm = bin_mass(v[u][gi], Ms[gi]);
+          atomicAdd(&h[gi][bm.bin], (unsigned long long)bm.mass);
+        }
   }
   __syncthreads();
-  unsigned long long* gh = (unsigned long long*)a.dev.mass1 + (int64_t)(lv * a.hq + hq) * NB1;
-  for (int i = threadIdx.x; i < NB1; i += 256)
-    if (h[i]) atomicAdd(&gh[i], h[i]);
+  uint64_t* out = a.dev.hpart + ((int64_t)kv * SEL_P + blockIdx.x) * GMAX * NB1;
+  for (int i = threadIdx.x; i < g * NB1; i += SEL_THREADS) out[i] = (&h[0][0])[i];
 }
 
-// Block-wide scan of NB (=2048) u64 bins held 8 per thread; finds the first bin where
-// base + inclusive prefix >= target.  Returns (bin, mass before it) via LDS.
-__device__ void find_boundary(const uint64_t* bins, uint64_t base, uint64_t target, uint64_t* tsum,
-                              uint32_t* out_bin, uint64_t* out_above, uint64_t* out_total) {
-  const int t = threadIdx.x;
-  uint64_t v[8];
-  uint64_t s = 0;
+// First bin (of 512 held 8 per lane) where base + inclusive prefix >= target; one wave.
+__device__ void wave_boundary512(const uint64_t* bins, uint64_t base, uint64_t target, int lane, uint32_t& bin,
+                                 uint64_t& above, uint64_t& total) {
+  uint64_t v[8], loc = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { v[i] = bins[t * 8 + i]; s += v[i]; }
-  tsum[t] = s;
-  __syncthreads();
-  // inclusive scan over 256 thread sums (Hillis-Steele in LDS)
-  for (int off = 1; off < 256; off <<= 1) {
-    uint64_t add = t >= off ? tsum[t - off] : 0ull;
-    __syncthreads();
-    tsum[t] += add;
-    __syncthreads();
+  for (int i = 0; i < 8; ++i) { v[i] = bins[lane * 8 + i]; loc += v[i]; }
+  uint64_t inc = loc;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
   }
-  uint64_t run = base + (t ? tsum[t - 1] : 0ull);
-  if (t == 255 && out_total) *out_total = tsum[255];
+  total = __shfl(inc, 63);
+  uint64_t run = base + inc - loc;
+  uint32_t fb = 0xffffffffu;
+  uint64_t fa = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    if (run < target && run + v[i] >= target) {
-      *out_bin = (uint32_t)(t * 8 + i);
-      *out_above = run;
-    }
+    if (fb == 0xffffffffu && run < target && run + v[i] >= target) { fb = lane * 8 + i; fa = run; }
     run += v[i];
   }
-  __syncthreads();
+  const uint64_t hit = __ballot(fb != 0xffffffffu);
+  const int src = hit ? __ffsll((long long)hit) - 1 : 0;
+  bin = __shfl(fb, src);
+  above = __shfl(fa, src);
 }
 
-__global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
-  __shared__ uint64_t tsum[256];
-  __shared__ uint32_t bin;
-  __shared__ uint64_t above, total;
-  const int hq = blockIdx.x, lv = a.level;
+// One workgroup per query head: sums the partial histograms bin by bin (fixed order) and
+// finds the boundary bin of the target mass ceil(p * Z).
+__global__ __launch_bounds__(NB1) void route_bound_kernel(RouteArgs a) {
+  __shared__ uint64_t hs[NB1];
+  const int hq = blockIdx.x, lv = a.level, kv = hq / a.g, gi = hq % a.g;
   QState* qs = a.dev.qs + lv * a.hq + hq;
-  const uint64_t* bins = a.dev.mass1 + (int64_t)(lv * a.hq + hq) * NB1;
-  if (threadIdx.x == 0) { bin = NB1; above = 0; total = 0; }
+  if (qs->maxkey == 0u) return;
+  const uint64_t* src = a.dev.hpart + ((int64_t)kv * SEL_P * GMAX + gi) * NB1 + threadIdx.x;
+  uint64_t sum = 0;
+  for (int p = 0; p < a.sel_p; ++p) sum += src[(int64_t)p * GMAX * NB1];
+  hs[threadIdx.x] = sum;
   __syncthreads();
-  // total first (target depends on it)
-  find_boundary(bins, 0, ~0ull, tsum, &bin, &above, &total);
-  const uint64_t Z = total;
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  uint32_t bb;
+  uint64_t above1, Z, dummy;
+  wave_boundary512(hs, 0, ~0ull, lane, bb, above1, Z);
+  uint32_t b1 = NB1;
   uint64_t T = 0;
-  bool keep_all = a.top_p >= 1.0f || qs->maxkey == 0u || Z == 0;
-  if (!keep_all) {
-    double t = ceil((double)a.top_p * (double)Z);
-    T = t < 1.0 ? 1ull : (uint64_t)t;
+  above1 = 0;
+  if (a.top_p < 1.0f && Z > 0) {
+    const double tt = ceil((double)a.top_p * (double)Z);
+    T = tt < 1.0 ? 1ull : (uint64_t)tt;
     if (T > Z) T = Z;
-    if (threadIdx.x == 0) { bin = NB1; above = 0; }
-    __syncthreads();
-    find_boundary(bins, 0, T, tsum, &bin, &above, nullptr);
+    wave_boundary512(hs, 0, T, lane, bb, above1, dummy);
+    b1 = bb;
   }
-  if (threadIdx.x == 0) {
+  if (lane == 0) {
     qs->total = Z;
     qs->target = T;
-    qs->b1 = keep_all ? (uint32_t)NB1 : bin;
-    qs->above1 = keep_all ? 0ull : above;
+    qs->b1 = b1;
+    qs->above1 = above1;
   }
 }
 
 // ------------------------------------------------------------------ classify
-__global__ __launch_bounds__(256) void route_classify_kernel(RouteArgs a) {
+__device__ __forceinline__ void wave_sync_lds_c() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int CLS_U = 2;          // union entries per lane per iteration
+constexpr int WAVE_STAGE = 128;   // candidates staged per (wave, head) in LDS
+
+// Nodes above the boundary bin are kept; nodes inside it become candidates.  Each wave
+// stages its candidates per head in LDS (spilling a batch to the head's list only when its
+// stage passes half full); at the end the workgroup appends what its waves hold with one
+// atomic per head.
+__global__ __launch_bounds__(SEL_THREADS) void route_classify_kernel(RouteArgs a) {
+  constexpr int NW = SEL_THREADS / 64;
   __shared__ float Ms[GMAX];
   __shared__ uint32_t B1[GMAX];
+  __shared__ int32_t stage[NW][GMAX][WAVE_STAGE];
+  __shared__ uint32_t wcnt_s[NW][GMAX];
+  __shared__ uint32_t bbase[GMAX];
   const int kv = blockIdx.y, lv = a.level, g = a.g;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (threadIdx.x < GMAX) {
-    const int gi = threadIdx.x;
-    if (gi < g) {
-      const QState* qs = a.dev.qs + lv * a.hq + kv * g + gi;
-      Ms[gi] = key2f(qs->maxkey);
-      B1[gi] = qs->b1;
+    uint32_t mk = 0, b1 = NB1;
+    if (threadIdx.x < g) {
+      const QState* qs = a.dev.qs + lv * a.hq + kv * g + threadIdx.x;
+      mk = qs->maxkey;
+      b1 = mk ? qs->b1 : NB1;
     }
+    Ms[threadIdx.x] = mk ? key2f(mk) : -INFINITY;
+    B1[threadIdx.x] = b1;
   }
   __syncthreads();
   const int64_t cnt = a.dev.cnt[lv * a.hkv + kv];
   const int64_t cap = a.dev.ncap[lv];
+  const int64_t per = (cnt + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per, hi = lo + per < cnt ? lo + per : cnt;
   const uint32_t* masks = a.dev.mask[lv] + kv * cap;
   const float* sc = a.dev.score[lv] + (int64_t)kv * GMAX * cap;
   uint32_t* keep = a.dev.keep[lv] + kv * cap;
   const int64_t ccap = a.dev.ncap[1];
-  const int lane = threadIdx.x & 63;
-  // wave-uniform trip count so every lane takes part in the candidate ballots
-  for (int64_t eb = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63); eb < cnt; eb += (int64_t)gridDim.x * 256) {
-    const int64_t e = eb + lane;
-    const bool valid = e < cnt;
-    const uint32_t mk = valid ? masks[e] : 0u;
-    uint32_t kb = 0;
-    for (int gi = 0; gi < g; ++gi) {
-      bool cand = false;
-      uint64_t cmass = 0;
-      uint32_t csub = 0;
-      if ((mk >> gi) & 1u) {
-        if (B1[gi] >= (uint32_t)NB1) {
-          kb |= 1u << gi;
-        } else {
-          BinMass bm = bin_mass(sc[(int64_t)gi * cap + e], Ms[gi]);
-          if (bm.bin < B1[gi]) kb |= 1u << gi;
-          else if (bm.bin == B1[gi]) { cand = true; cmass = bm.mass; csub = bm.sub; }
-        }
-      }
-      const uint64_t ball = __ballot(cand);
-      if (ball) {
-        const int hq = kv * g + gi;
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&a.dev.qs[lv * a.hq + hq].ncand, (uint32_t)__popcll(ball));
-        base = __shfl(base, 0);
-        if (cand) {
-          const uint32_t pos = base + (uint32_t)__popcll(ball & ((1ull << lane) - 1ull));
-          a.dev.cand[(int64_t)hq * ccap + pos] = (int32_t)e;
-          atomicAdd((unsigned long long*)a.dev.mass2 + (int64_t)(lv * a.hq + hq) * NB2 + csub,
-                    (unsigned long long)cmass);
-        }
-      }
+  uint32_t wcnt[GMAX];
+#pragma unroll
+  for (int gi = 0; gi < GMAX; ++gi) wcnt[gi] = 0;
+  // wave-uniform trip count so every lane takes part in the ballots
+  for (int64_t e0 = lo + (int64_t)wave * 64 * CLS_U; e0 < hi; e0 += SEL_THREADS * CLS_U) {
+    uint32_t mk[CLS_U];
+    float v[CLS_U][GMAX];
+#pragma unroll
+    for (int u = 0; u < CLS_U; ++u) {
+      const int64_t e = e0 + 64 * u + lane;
+      mk[u] = e < hi ? masks[e] : 0u;
+#pragma unroll
+      for (int gi = 0; gi < GMAX; ++gi) v[u][gi] = (gi < g && e < hi) ? sc[(int64_t)gi * cap + e] : 0.f;
     }
-    if (valid) keep[e] = kb;
+#pragma unroll
+    for (int u = 0; u < CLS_U; ++u) {
+      const int64_t e = e0 + 64 * u + lane;
+      uint32_t kb = 0;
+#pragma unroll
+      for (int gi = 0; gi < GMAX; ++gi) {
+        bool cand = false;
+        if ((mk[u] >> gi) & 1u) {
+          if (B1[gi] >= (uint32_t)NB1) {
+            kb |= 1u << gi;
+          } else {
+            const BinMass bm = bin_mass(v[u][gi], Ms[gi]);
+            if (bm.bin < B1[gi]) kb |= 1u << gi;
+            else cand = bm.bin == B1[gi];
+          }
+        }
+        const uint64_t ball = __ballot(cand);
+        if (ball) {
+          if (cand) stage[wave][gi][wcnt[gi] + __popcll(ball & ((1ull << lane) - 1ull))] = (int32_t)e;
+          wcnt[gi] += (uint32_t)__popcll(ball);
+          if (wcnt[gi] > WAVE_STAGE - 64) {   // spill this wave's batch for the head
+            wave_sync_lds_c();
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&a.dev.qs[lv * a.hq + kv * g + gi].ncand, wcnt[gi]);
+            base = __shfl(base, 0);
+            int32_t* dst = a.dev.cand + (int64_t)(kv * g + gi) * ccap + base;
+            for (uint32_t i = lane; i < wcnt[gi]; i += 64) dst[i] = stage[wave][gi][i];
+            wave_sync_lds_c();
+            wcnt[gi] = 0;
+          }
+        }
+      }
+      if (e < hi) keep[e] = kb;
+    }
+  }
+  if (lane < GMAX) wcnt_s[wave][lane] = 0;
+#pragma unroll
+  for (int gi = 0; gi < GMAX; ++gi)
+    if (lane == gi) wcnt_s[wave][gi] = wcnt[gi];
+  __syncthreads();
+  if (threadIdx.x < (unsigned)g) {
+    uint32_t n = 0;
+    for (int w = 0; w < NW; ++w) n += wcnt_s[w][threadIdx.x];
+    bbase[threadIdx.x] = n ? atomicAdd(&a.dev.qs[lv * a.hq + kv * g + threadIdx.x].ncand, n) : 0u;
+  }
+  __syncthreads();
+  for (int gi = 0; gi < g; ++gi) {
+    uint32_t off = bbase[gi];
+    for (int w = 0; w < wave; ++w) off += wcnt_s[w][gi];
+    int32_t* dst = a.dev.cand + (int64_t)(kv * g + gi) * ccap + off;
+    for (uint32_t i = lane; i < wcnt_s[wave][gi]; i += 64) dst[i] = stage[wave][gi][i];
   }
 }
 
@@ -314,7 +394,7 @@ __device__ __forceinline__ uint64_t rank_key(float s, int32_t e) {
 }
 
 __global__ __launch_bounds__(256) void route_resolve_kernel(RouteArgs a) {
-  __shared__ uint64_t tsum[256];
+  __shared__ unsigned long long h2[NB2];
   __shared__ uint32_t bin;
   __shared__ uint64_t above;
   __shared__ int32_t tie_e[CAND_PAIRWISE];
@@ -326,20 +406,32 @@ __global__ __launch_bounds__(256) void route_resolve_kernel(RouteArgs a) {
   const int hq = blockIdx.x, lv = a.level, kv = hq / a.g, gi = hq % a.g;
   QState* qs = a.dev.qs + lv * a.hq + hq;
   const uint32_t b1 = qs->b1;
-  if (b1 >= (uint32_t)NB1) return;
+  if (qs->maxkey == 0u || b1 >= (uint32_t)NB1) return;
   const uint64_t T = qs->target, above1 = qs->above1;
   const float M = key2f(qs->maxkey);
-  if (threadIdx.x == 0) { bin = NB2; above = 0; ntie = 0; }
-  __syncthreads();
-  find_boundary(a.dev.mass2 + (int64_t)(lv * a.hq + hq) * NB2, above1, T, tsum, &bin, &above, nullptr);
-  const uint32_t b2 = bin;
-  const uint64_t above2 = above;
   const int64_t cap = a.dev.ncap[lv];
   const float* sc = a.dev.score[lv] + ((int64_t)kv * GMAX + gi) * cap;
   uint32_t* keep = a.dev.keep[lv] + kv * cap;
   const int32_t* cand = a.dev.cand + (int64_t)hq * a.dev.ncap[1];
   const uint32_t ncand = qs->ncand;
   const uint32_t bit = 1u << gi;
+  // fine histogram of the boundary bin's candidates
+  for (int i = threadIdx.x; i < NB2; i += 256) h2[i] = 0ull;
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < ncand; i += 256) {
+    const BinMass bm = bin_mass(sc[cand[i]], M);
+    atomicAdd(&h2[bm.sub], (unsigned long long)bm.mass);
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    uint32_t bb;
+    uint64_t ab, dummy;
+    wave_boundary512((const uint64_t*)h2, above1, T, threadIdx.x, bb, ab, dummy);
+    if (threadIdx.x == 0) { bin = bb; above = ab; ntie = 0; }
+  }
+  __syncthreads();
+  const uint32_t b2 = bin;
+  const uint64_t above2 = above;
   for (uint32_t i = threadIdx.x; i < ncand; i += 256) {
     const int32_t e = cand[i];
     const float s = sc[e];
@@ -510,6 +602,279 @@ __global__ __launch_bounds__(256) void route_expand_emit_kernel(RouteArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ multi-level selection
+// Levels whose node count is at most MLS_MAX, selected top-down in one launch per KV head
+// after every node of those levels was scored.  One wave per query head.  Per level:
+// max of the head's frontier scores; the node's coarse bin (1/8 score unit) and fine
+// sub-bin (1/2048) packed in 16 bits in LDS; a wave-private 256-bin histogram of the
+// fixed-point masses; the boundary bin; a 256-sub-bin histogram of that bin; the boundary
+// sub-bin; exact rank order inside it.  The masses, the target and the rank rule are those
+// of the large-frontier path, so a node is kept here exactly when it would be kept there.
+// The frontier of the next level is the children of the kept nodes (a bitmap per head);
+// after the last level the kept nodes' children become the union list of the next level
+// (or the gather list).
+constexpr int MNB = 256;                 // coarse bins per head, 1/8 score unit each
+constexpr float M_BPU = 8.f;
+constexpr int MNB2 = 256;                // fine sub-bins inside the boundary bin
+constexpr int M_TIES = 64;               // boundary sub-bin nodes resolved in LDS
+constexpr uint16_t M_ABSENT = 0xffffu;   // not in the head's frontier
+
+__device__ __forceinline__ uint16_t mls_binsub(float score, float mx) {
+  const float delta = mx - score;
+  const float u = delta * M_BPU;
+  const uint32_t bin = u < (float)(MNB - 1) ? (uint32_t)u : (uint32_t)(MNB - 1);
+  uint32_t sub = 0;
+  if (bin < (uint32_t)(MNB - 1)) {
+    const float f = (u - (float)bin) * (float)MNB2;
+    sub = f < (float)(MNB2 - 1) ? (uint32_t)f : (uint32_t)(MNB2 - 1);
+  }
+  return (uint16_t)((bin << 8) | sub);   // never M_ABSENT: bin 255 always has sub 0
+}
+__device__ __forceinline__ uint64_t mls_mass(float score, float mx) {
+  const float delta = mx - score;                         // same expression as bin_mass
+  return (uint64_t)(expf(-delta) * MASS_SCALE);
+}
+
+// Out-of-line copy for the later passes, so the compiler does not keep every node's mass
+// alive in registers from the first pass to the last.
+__device__ __noinline__ uint64_t mls_mass_ni(float score, float mx) { return mls_mass(score, mx); }
+
+// First bin (of 256 held 4 per lane) where base + inclusive prefix >= target; one wave.
+__device__ void wave_boundary256(const uint64_t* bins, uint64_t base, uint64_t target, int lane, uint32_t& bin,
+                                 uint64_t& above, uint64_t& total) {
+  uint64_t v[4], loc = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = bins[lane * 4 + i]; loc += v[i]; }
+  uint64_t inc = loc;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
+  }
+  total = __shfl(inc, 63);
+  uint64_t run = base + inc - loc;
+  uint32_t fb = 0xffffffffu;
+  uint64_t fa = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (fb == 0xffffffffu && run < target && run + v[i] >= target) { fb = lane * 4 + i; fa = run; }
+    run += v[i];
+  }
+  const uint64_t hit = __ballot(fb != 0xffffffffu);
+  const int src = hit ? __ffsll((long long)hit) - 1 : 0;
+  bin = __shfl(fb, src);
+  above = __shfl(fa, src);
+}
+
+__global__ __launch_bounds__(GMAX * 64) void route_mls_kernel(RouteArgs a) {
+  constexpr int MPL = (MLS_MAX + 63) / 64;    // nodes per lane (node e = 64 i + lane)
+  constexpr int MW64 = MPL;                   // 64-bit bitmap words per head
+  __shared__ uint64_t h1[GMAX][MNB];
+  __shared__ uint64_t h2[GMAX][MNB2];
+  __shared__ uint64_t kbm[2][GMAX][MW64];     // kept nodes per head (this level / above)
+  __shared__ uint64_t fbm[GMAX][MW64];        // frontier per head (this level)
+  __shared__ int32_t ntie[GMAX];
+  __shared__ int32_t tie_e[GMAX][M_TIES];
+  __shared__ float tie_s[GMAX][M_TIES];
+  __shared__ uint64_t tie_m[GMAX][M_TIES];
+  __shared__ uint16_t bsl[GMAX][MPL * 64];    // bin | sub code of each node of the head
+  __shared__ int32_t eoff[MLS_MAX + 1];
+  __shared__ int32_t wsum[GMAX];
+  constexpr int NT = GMAX * 64;
+  const int kv = blockIdx.x, lane = threadIdx.x & 63, gi = threadIdx.x >> 6;
+  const int g = a.g, b = a.b;
+  const bool active = gi < g;
+  const bool keep_all = a.top_p >= 1.0f;
+  int pb = 0;   // kbm[pb] = kept bitmap of the level above
+  for (int lv = a.level; lv >= a.dense_lo; --lv) {
+    const int n = (int)a.nl[lv];
+    const int64_t cap = a.dev.ncap[lv];
+    const bool top = lv == a.level;
+    for (int i = lane; i < MW64; i += 64) { kbm[pb ^ 1][gi][i] = 0ull; fbm[gi][i] = 0ull; }
+    if (lane == 0) ntie[gi] = 0;
+    if (active) {
+      const float* S = a.dev.score[lv] + ((int64_t)kv * GMAX + gi) * cap;
+      // every score of the level in registers (unconditional loads, issued together)
+      float v[MPL];
+      const float* Sl = S + lane;   // one base register; node 64i + lane at Sl[64 i]
+#pragma unroll
+      for (int i = 0; i < MPL; ++i) v[i] = (64 * i + lane < n) ? Sl[64 * i] : -INFINITY;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < MPL; ++i) {
+        const int e = 64 * i + lane;
+        bool in = e < n;
+        if (!top) {
+          const int pn = e / b;
+          in = in && ((kbm[pb][gi][pn >> 6] >> (pn & 63)) & 1ull);
+        }
+        const uint64_t fw = __ballot(in);
+        if (lane == 0) fbm[gi][i] = fw;
+        if (!in) v[i] = -INFINITY;
+        mx = fmaxf(mx, v[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      if (mx > -INFINITY) {
+        uint32_t b1 = 0, b2 = 0;
+        uint64_t T = 0, above2 = 0;
+        uint16_t* bs = bsl[gi];
+        if (!keep_all) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { h1[gi][lane * 4 + i] = 0ull; h2[gi][lane * 4 + i] = 0ull; }
+          wave_sync_lds_r();
+        }
+        // codes to LDS (computed once), coarse histogram
+#pragma unroll
+        for (int i = 0; i < MPL; ++i) {
+          uint16_t code = M_ABSENT;
+          if (v[i] > -INFINITY) {
+            code = mls_binsub(v[i], mx);
+            if (!keep_all)
+              atomicAdd((unsigned long long*)&h1[gi][code >> 8], (unsigned long long)mls_mass(v[i], mx));
+          }
+          bs[64 * i + lane] = code;
+          __builtin_amdgcn_sched_barrier(0);   // keep one node's temporaries live at a time
+        }
+        wave_sync_lds_r();
+        if (!keep_all) {
+          uint64_t above1, Z, dummy;
+          wave_boundary256(h1[gi], 0, ~0ull, lane, b1, above1, Z);
+          const double tt = ceil((double)a.top_p * (double)Z);
+          T = tt < 1.0 ? 1ull : (uint64_t)tt;
+          if (T > Z) T = Z;
+          wave_boundary256(h1[gi], 0, T, lane, b1, above1, dummy);
+#pragma unroll
+          for (int i = 0; i < MPL; ++i) {
+            const uint16_t code = bs[64 * i + lane];
+            if (code != M_ABSENT && (uint32_t)(code >> 8) == b1)
+              atomicAdd((unsigned long long*)&h2[gi][code & 0xffu], (unsigned long long)mls_mass_ni(v[i], mx));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          wave_sync_lds_r();
+          wave_boundary256(h2[gi], above1, T, lane, b2, above2, dummy);
+        }
+        // kept bitmap above the boundary sub-bin; collect the boundary sub-bin's nodes
+#pragma unroll
+        for (int i = 0; i < MPL; ++i) {
+          bool kp = false;
+          const uint16_t code = bs[64 * i + lane];
+          if (code != M_ABSENT) {
+            const uint32_t bn = code >> 8, sb = code & 0xffu;
+            kp = keep_all || bn < b1 || (bn == b1 && sb < b2);
+            if (!kp && bn == b1 && sb == b2) {
+              const int k = atomicAdd(&ntie[gi], 1);
+              if (k < M_TIES) {
+                tie_e[gi][k] = 64 * i + lane; tie_s[gi][k] = v[i]; tie_m[gi][k] = mls_mass_ni(v[i], mx);
+              }
+            }
+          }
+          const uint64_t kw = __ballot(kp);
+          if (lane == 0) kbm[pb ^ 1][gi][i] = kw;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        wave_sync_lds_r();
+        const int nt = keep_all ? 0 : ntie[gi];
+        if (nt <= M_TIES) {
+          for (int x = lane; x < nt; x += 64) {
+            const uint64_t kx = rank_key(tie_s[gi][x], tie_e[gi][x]);
+            uint64_t ab = 0;
+            for (int y = 0; y < nt; ++y)
+              if (rank_key(tie_s[gi][y], tie_e[gi][y]) < kx) ab += tie_m[gi][y];
+            if (above2 + ab < T) {
+              const int e = tie_e[gi][x];
+              atomicOr((unsigned long long*)&kbm[pb ^ 1][gi][e >> 6], 1ull << (e & 63));
+            }
+          }
+        } else {
+          // many nodes in one sub-bin: exact rank order by a pass over the frontier
+          for (int x = lane; x < n; x += 64) {
+            if (!((fbm[gi][x >> 6] >> (x & 63)) & 1ull)) continue;
+            const float sx = S[x];
+            const uint16_t cx = mls_binsub(sx, mx);
+            if ((uint32_t)(cx >> 8) != b1 || (uint32_t)(cx & 0xffu) != b2) continue;
+            const uint64_t kx = rank_key(sx, x);
+            uint64_t ab = 0;
+            for (int y = 0; y < n; ++y) {
+              if (!((fbm[gi][y >> 6] >> (y & 63)) & 1ull)) continue;
+              const float sy = S[y];
+              if (mls_binsub(sy, mx) == cx && rank_key(sy, y) < kx) ab += mls_mass(sy, mx);
+            }
+            if (above2 + ab < T) atomicOr((unsigned long long*)&kbm[pb ^ 1][gi][x >> 6], 1ull << (x & 63));
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // trace of this level: every node listed; masks / keep = per-head bits of the node
+    for (int i = threadIdx.x; i < n; i += NT) {
+      uint32_t um = 0, uk = 0;
+      for (int h = 0; h < g; ++h) {
+        um |= (uint32_t)((fbm[h][i >> 6] >> (i & 63)) & 1ull) << h;
+        uk |= (uint32_t)((kbm[pb ^ 1][h][i >> 6] >> (i & 63)) & 1ull) << h;
+      }
+      a.dev.node[lv][kv * cap + i] = i;
+      a.dev.mask[lv][kv * cap + i] = um;
+      a.dev.keep[lv][kv * cap + i] = uk;
+    }
+    if (threadIdx.x == 0) a.dev.cnt[lv * a.hkv + kv] = n;
+    pb ^= 1;
+    __syncthreads();
+  }
+  // children of the last level's kept nodes -> union list of the level below (or gather
+  // list): per-node output offsets by a block scan; each thread then writes the children
+  // of its nodes (adjacent lanes, adjacent nodes)
+  const int lv = a.dense_lo;
+  const int n = (int)a.nl[lv];
+  const int64_t nbelow = lv > 1 ? a.nl[lv - 1] : 0;
+  constexpr int PER = (MLS_MAX + NT - 1) / NT;
+  auto kept_mask = [&](int e) -> uint32_t {
+    uint32_t uk = 0;
+    for (int h = 0; h < g; ++h) uk |= (uint32_t)((kbm[pb][h][e >> 6] >> (e & 63)) & 1ull) << h;
+    return uk;
+  };
+  auto nchild = [&](int e, uint32_t uk) -> int32_t {
+    if (!uk) return 0;
+    return lv == 1 ? 1 : (int32_t)min((int64_t)b, nbelow - (int64_t)e * b);
+  };
+  const int e0 = threadIdx.x * PER;
+  int32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = e0 + i;
+    if (e < n) mine += nchild(e, kept_mask(e));
+  }
+  int32_t inc = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
+  }
+  if (lane == 63) wsum[gi] = inc;
+  __syncthreads();
+  int32_t wbase = 0, total = 0;
+  for (int w = 0; w < GMAX; ++w) { if (w < gi) wbase += wsum[w]; total += wsum[w]; }
+  int32_t run = wbase + inc - mine;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = e0 + i;
+    if (e < n) { eoff[e] = run; run += nchild(e, kept_mask(e)); }
+  }
+  __syncthreads();
+  const int out_lv = lv - 1;
+  const int64_t ocap = a.dev.ncap[out_lv];
+  int32_t* onode = a.dev.node[out_lv] + kv * ocap;
+  uint32_t* omask = a.dev.mask[out_lv] + kv * ocap;
+  for (int e = threadIdx.x; e < n; e += NT) {
+    const uint32_t uk = kept_mask(e);
+    const int32_t c = nchild(e, uk);
+    const int32_t o = eoff[e];
+    for (int j = 0; j < c; ++j) {
+      onode[o + j] = lv == 1 ? e : e * b + j;
+      omask[o + j] = uk;
+    }
+  }
+  if (threadIdx.x == 0) a.dev.cnt[out_lv * a.hkv + kv] = total;
+}
+
 // ------------------------------------------------------------------ launchers
 hipError_t launch_route_prep(const RouteArgs& a, bool bf16, int D, hipStream_t st) {
   dim3 grid(256), block(256);
@@ -549,10 +914,40 @@ hipError_t launch_route_score(const RouteArgs& a, int D, int R, hipStream_t st) 
 }
 
 hipError_t launch_route_select(const RouteArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(route_hist_kernel, dim3(grid_for(a.nlevel, 2048, 256), (unsigned)a.hq), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(route_select_kernel, dim3((unsigned)a.hq), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(route_classify_kernel, dim3(grid_for(a.nlevel, 1024, 2048), (unsigned)a.hkv), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(route_resolve_kernel, dim3((unsigned)a.hq), dim3(256), 0, st, a);
+  RouteArgs b = a;
+  b.sel_p = (int32_t)grid_for(a.nlevel, 4096, SEL_P);
+  hipLaunchKernelGGL(route_hist_kernel, dim3((unsigned)b.sel_p, (unsigned)a.hkv), dim3(SEL_THREADS), 0, st, b);
+  hipLaunchKernelGGL(route_bound_kernel, dim3((unsigned)a.hq), dim3(NB1), 0, st, b);
+  hipLaunchKernelGGL(route_classify_kernel, dim3((unsigned)b.sel_p, (unsigned)a.hkv), dim3(SEL_THREADS), 0, st, b);
+  hipLaunchKernelGGL(route_resolve_kernel, dim3((unsigned)a.hq), dim3(256), 0, st, b);
+  return hipGetLastError();
+}
+
+template <int D, int R>
+static void launch_dense_score_t(const RouteArgs& a, int nlev, hipStream_t st) {
+  constexpr int NPB = 4 * (16 / R) * (R >= 8 ? ZHA_SCORE_UN_WIDE : ZHA_SCORE_UN_NARROW);
+  int64_t mx = 0;
+  for (int l = a.dense_lo; l <= a.level; ++l) mx = a.nl[l] > mx ? a.nl[l] : mx;
+  int64_t x = (mx + NPB - 1) / NPB;
+  if (x > ZHA_SCORE_GRID) x = ZHA_SCORE_GRID;
+  if (x < 1) x = 1;
+  hipLaunchKernelGGL((route_score_kernel<D, R>), dim3((unsigned)x, (unsigned)a.hkv, (unsigned)nlev), dim3(256), 0,
+                     st, a);
+}
+
+hipError_t launch_route_dense_score(const RouteArgs& a, int D, int R, hipStream_t st) {
+  const int nlev = a.level - a.dense_lo + 1;
+#define ZHA_CASE(DD, RR) else if (D == DD && R == RR) launch_dense_score_t<DD, RR>(a, nlev, st);
+  if (false) {}
+  ZHA_CASE(64, 1) ZHA_CASE(64, 2) ZHA_CASE(64, 4) ZHA_CASE(64, 8) ZHA_CASE(64, 16)
+  ZHA_CASE(128, 1) ZHA_CASE(128, 2) ZHA_CASE(128, 4) ZHA_CASE(128, 8) ZHA_CASE(128, 16)
+  else return hipErrorInvalidValue;
+#undef ZHA_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_route_mls(const RouteArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(route_mls_kernel, dim3((unsigned)a.hkv), dim3(GMAX * 64), 0, st, a);
   return hipGetLastError();
 }
 

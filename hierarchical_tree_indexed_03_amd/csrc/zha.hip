@@ -131,8 +131,7 @@ size_t layout(const zha_config& c, char* base, Dev* dev) {
   }
   d.cnt = (int32_t*)take((size_t)((MAXL + 1) * H) * 4);
   d.qs = (QState*)take((size_t)((L + 1) * Q) * sizeof(QState));
-  d.mass1 = (uint64_t*)take((size_t)((L + 1) * Q * NB1) * 8);
-  d.mass2 = (uint64_t*)take((size_t)((L + 1) * Q * NB2) * 8);
+  d.hpart = (uint64_t*)take((size_t)(H * SEL_P * GMAX * NB1) * 8);
   d.cand = (int32_t*)take((size_t)(Q * d.ncap[1]) * 4);
   d.qf = (float*)take((size_t)(Q * D) * 4);
   d.apart = (float*)take((size_t)(Q * MAX_SPLITS * (D + 2)) * 4);
@@ -167,6 +166,8 @@ RouteArgs route_args(const zha_tree* t, const void* q) {
   a.levels = t->cfg.levels;
   a.top_p = t->cfg.top_p;
   a.sigma = 1.0f / sqrtf((float)t->cfg.head_dim);
+  for (int l = 1; l <= t->cfg.levels; ++l) a.nl[l] = nodes_at(t->cfg, l, t->N);
+  a.nl[0] = a.nl[1];
   return a;
 }
 
@@ -333,7 +334,26 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
     e = launch_route_prep(r, c.dtype == ZHA_BF16, c.head_dim, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "route prep launch");
-  for (int lv = c.levels; lv >= 1; --lv) {
+  // top levels small enough for the one-launch multi-level selection
+  int lo = c.levels + 1;
+  while (lo > 1 && r.nl[lo - 1] <= MLS_MAX) --lo;
+  if (lo <= c.levels) {
+    r.level = c.levels;
+    r.dense = 1;
+    r.dense_lo = lo;
+    {
+      ProfScope ps(t, "route_score.top", stream);
+      e = launch_route_dense_score(r, c.head_dim, c.num_ref, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "route dense score launch");
+    {
+      ProfScope ps(t, "route_select.top", stream);
+      e = launch_route_mls(r, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "route multi-level select launch");
+    r.dense = 0;
+  }
+  for (int lv = lo - 1; lv >= 1; --lv) {
     zha_status s = route_levels(t, r, lv, stream, true);
     if (s != ZHA_OK) return s;
   }
