@@ -103,11 +103,14 @@ constexpr int ATILE = 32;   // tokens per wave iteration
 
 // Token range of split `split` out of F tokens: chunks are whole multiples of 4 waves x
 // one tile; splits beyond the data get an empty range.
-__device__ __forceinline__ void split_range(int64_t F, int splits, int split, int64_t& fb, int64_t& fe) {
+__device__ __forceinline__ int64_t split_chunk(int64_t F, int splits) {
   int64_t chunk = (F + splits - 1) / splits;
   const int64_t unit = 4 * ATILE;
   chunk = (chunk + unit - 1) / unit * unit;
-  if (chunk < unit) chunk = unit;
+  return chunk < unit ? unit : chunk;
+}
+__device__ __forceinline__ void split_range(int64_t F, int splits, int split, int64_t& fb, int64_t& fe) {
+  const int64_t chunk = split_chunk(F, splits);
   fb = (int64_t)split * chunk;
   fe = min(fb + chunk, F);
 }
@@ -290,48 +293,33 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
 }
 
 template <typename TIn, int D, bool DENSE>
-__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t* stats, int levels) {
-  __shared__ float Ws[MAX_SPLITS];
-  __shared__ float red[256];
-  __shared__ float Ored[256 / D][D];
-  __shared__ float Ms, Ls_, S0;
+__global__ __launch_bounds__(512) void combine_kernel(AttnArgs a, int32_t* stats, int levels) {
+  constexpr int NW = 8;        // waves: split rows are dealt round-robin to the waves
+  constexpr int VD = D / 64;   // output dims per lane
+  __shared__ float Wl[MAX_SPLITS];
+  __shared__ float redm[NW], redl[NW];
+  __shared__ float Ored[NW][D];
+  __shared__ float S0;
   const int hq = blockIdx.x, kv = hq / a.g, gi = hq % a.g;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* base = a.dev.apart + (int64_t)hq * MAX_SPLITS * (D + 2);
   int64_t F;
   if constexpr (DENSE) F = a.N;
   else F = (int64_t)a.dev.cnt[kv] * a.b;
-  int S = 0;   // splits that own tokens
-  for (int s = 0; s < a.splits; ++s) {
-    int64_t fb, fe;
-    split_range(F, a.splits, s, fb, fe);
-    if (fb >= fe) break;
-    S = s + 1;
+  // splits that own tokens (same chunking as the attention kernel)
+  int S = 0;
+  if (F > 0) {
+    const int64_t ch = split_chunk(F, a.splits);
+    const int64_t s = (F + ch - 1) / ch;
+    S = s < a.splits ? (int)s : a.splits;
   }
-  float mloc = -INFINITY;
-  for (int s = threadIdx.x; s < S; s += 256) mloc = fmaxf(mloc, base[(int64_t)s * (D + 2)]);
-  red[threadIdx.x] = mloc;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (threadIdx.x < off) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + off]);
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) Ms = red[0];
-  __syncthreads();
-  const float M = Ms;
-  float lloc = 0.f;
-  for (int s = threadIdx.x; s < S; s += 256) {
-    const float* pp = base + (int64_t)s * (D + 2);
-    const float w = (M > -INFINITY && pp[1] > 0.f) ? expf(pp[0] - M) : 0.f;
-    Ws[s] = w;
-    lloc += pp[1] * w;
-  }
-  red[threadIdx.x] = lloc;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) Ls_ = red[0];
+  // pass 1: max of the partial maxima
+  float ms = -INFINITY, ls = 0.f;
+  if ((int)threadIdx.x < S) { ms = base[(int64_t)threadIdx.x * (D + 2)]; ls = base[(int64_t)threadIdx.x * (D + 2) + 1]; }
+  float mx = ms;
+  for (int s = threadIdx.x + 512; s < S; s += 512) mx = fmaxf(mx, base[(int64_t)s * (D + 2)]);
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) redm[wave] = mx;
   // sink: token 0 when this head did not keep block 0
   bool add_sink = false;
   if constexpr (!DENSE) {
@@ -344,46 +332,75 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t* stats
   }
   const TIn* K0 = (const TIn*)a.K + (int64_t)kv * a.cap * D;
   const TIn* V0 = (const TIn*)a.V + (int64_t)kv * a.cap * D;
-  __syncthreads();
-  if (add_sink) {
+  if (add_sink && wave == NW - 1) {
     const TIn* qh = (const TIn*)a.q + (int64_t)hq * D;
     float part = 0.f;
-    for (int d = threadIdx.x; d < D; d += 256) part += to_f32(qh[d]) * to_f32(K0[d]);
-    red[threadIdx.x] = part;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-      if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) S0 = a.sigma * red[0];
-    __syncthreads();
-  }
-  {   // weighted sum of the split outputs: 256/D split groups per output dim
-    constexpr int G = 256 / D;
-    const int d = threadIdx.x % D, grp = threadIdx.x / D;
-    float O = 0.f;
-#pragma unroll 8
-    for (int s = grp; s < S; s += G) O += Ws[s] * base[(int64_t)s * (D + 2) + 2 + d];
-    Ored[grp][d] = O;
+#pragma unroll
+    for (int i = 0; i < VD; ++i) part += to_f32(qh[lane * VD + i]) * to_f32(K0[lane * VD + i]);
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    if (lane == 0) S0 = a.sigma * part;
   }
   __syncthreads();
-  for (int d = threadIdx.x; d < D; d += 256) {
-    float O = 0.f;
+  float M = redm[0];
 #pragma unroll
-    for (int i = 0; i < 256 / D; ++i) O += Ored[i][d];
-    float L = Ls_;
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, redm[w]);
+  // weights and the softmax denominator
+  float lsum = 0.f;
+  for (int s = threadIdx.x; s < S; s += 512) {
+    const float m_s = s == (int)threadIdx.x ? ms : base[(int64_t)s * (D + 2)];
+    const float l_s = s == (int)threadIdx.x ? ls : base[(int64_t)s * (D + 2) + 1];
+    const float w = (M > -INFINITY && l_s > 0.f) ? expf(m_s - M) : 0.f;
+    Wl[s] = w;
+    lsum += l_s * w;
+  }
+  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
+  if (lane == 0) redl[wave] = lsum;
+  __syncthreads();
+  // pass 2: weighted sum of the split outputs, rows round-robin over the waves
+  float O[VD];
+#pragma unroll
+  for (int i = 0; i < VD; ++i) O[i] = 0.f;
+  int s = wave;
+  for (; s + 7 * NW < S; s += 8 * NW) {
+    float v[8][VD];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < VD; ++i) v[u][i] = base[(int64_t)(s + u * NW) * (D + 2) + 2 + lane * VD + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = Wl[s + u * NW];
+#pragma unroll
+      for (int i = 0; i < VD; ++i) O[i] += w * v[u][i];
+    }
+  }
+  for (; s < S; s += NW) {
+    const float w = Wl[s];
+#pragma unroll
+    for (int i = 0; i < VD; ++i) O[i] += w * base[(int64_t)s * (D + 2) + 2 + lane * VD + i];
+  }
+#pragma unroll
+  for (int i = 0; i < VD; ++i) Ored[wave][lane * VD + i] = O[i];
+  __syncthreads();
+  for (int d = threadIdx.x; d < D; d += 512) {
+    float Ov = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Ov += Ored[w][d];
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) L += redl[w];
     if (add_sink) {
       const float s0 = S0;
       const float mn = fmaxf(M, s0);
       const float sa = (M == -INFINITY) ? 0.f : expf(M - mn);
       const float sb = expf(s0 - mn);
-      O = O * sa + to_f32(V0[d]) * sb;
+      Ov = Ov * sa + to_f32(V0[d]) * sb;
       L = L * sa + sb;
     }
-    a.out[(int64_t)hq * D + d] = L > 0.f ? O / L : 0.f;
+    a.out[(int64_t)hq * D + d] = L > 0.f ? Ov / L : 0.f;
   }
   if (stats && hq == 0) {
-    for (int i = threadIdx.x; i < (levels + 1) * a.hkv; i += 256) {
+    for (int i = threadIdx.x; i < (levels + 1) * a.hkv; i += 512) {
       const int row = i / a.hkv, k = i % a.hkv;
       const int lvl = row < levels ? levels - row : 0;
       stats[i] = a.dev.cnt[lvl * a.hkv + k];
@@ -394,7 +411,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t* stats
 template <typename TIn, int D, bool DENSE>
 static hipError_t launch_attend_t(const AttnArgs& a, int32_t* stats, int levels, hipStream_t st) {
   hipLaunchKernelGGL((attend_kernel<TIn, D, DENSE>), dim3((unsigned)a.splits, (unsigned)a.hkv), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((combine_kernel<TIn, D, DENSE>), dim3((unsigned)a.hq), dim3(256), 0, st, a, stats, levels);
+  hipLaunchKernelGGL((combine_kernel<TIn, D, DENSE>), dim3((unsigned)a.hq), dim3(512), 0, st, a, stats, levels);
   return hipGetLastError();
 }
 

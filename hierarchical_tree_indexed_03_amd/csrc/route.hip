@@ -246,7 +246,15 @@ __global__ __launch_bounds__(NB1) void route_bound_kernel(RouteArgs a) {
   if (qs->maxkey == 0u) return;
   const uint64_t* src = a.dev.hpart + ((int64_t)kv * SEL_P * GMAX + gi) * NB1 + threadIdx.x;
   uint64_t sum = 0;
-  for (int p = 0; p < a.sel_p; ++p) sum += src[(int64_t)p * GMAX * NB1];
+  int p = 0;
+  for (; p + 8 <= a.sel_p; p += 8) {
+    uint64_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = src[(int64_t)(p + i) * GMAX * NB1];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum += v[i];
+  }
+  for (; p < a.sel_p; ++p) sum += src[(int64_t)p * GMAX * NB1];
   hs[threadIdx.x] = sum;
   __syncthreads();
   if (threadIdx.x >= 64) return;
@@ -522,13 +530,17 @@ __global__ __launch_bounds__(256) void route_expand_count_kernel(RouteArgs a) {
     a.dev.part[lv][(int64_t)kv * gridDim.x + blockIdx.x] = red[0] + red[1] + red[2] + red[3];
 }
 
+// Children of the kept entries of one chunk, written to consecutive output slots.  The
+// union list is in ascending node order, so only the level's last node can have fewer than
+// b children and it is the last kept entry wherever it appears: output slot o of the chunk
+// is child o % b of the chunk's (o / b)-th kept entry (at level 1: the o-th kept block).
 __global__ __launch_bounds__(256) void route_expand_emit_kernel(RouteArgs a) {
-  __shared__ int32_t red[4], red2[4];
-  __shared__ int32_t ts[256];
-  __shared__ int32_t eoff[EXPAND_CHUNK + 1];   // exclusive output offset of each entry
-  __shared__ int32_t enode[EXPAND_CHUNK];
-  __shared__ uint32_t ekeep[EXPAND_CHUNK];
+  __shared__ int32_t red[4], red2[4], wk[4];
+  __shared__ int32_t knode[EXPAND_CHUNK];
+  __shared__ uint32_t kmask[EXPAND_CHUNK];
+  __shared__ int32_t total_s;
   const int kv = blockIdx.y, lv = a.level;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t cnt = a.dev.cnt[lv * a.hkv + kv];
   const int64_t cap = a.dev.ncap[lv];
   const int nch = gridDim.x;
@@ -544,61 +556,62 @@ __global__ __launch_bounds__(256) void route_expand_emit_kernel(RouteArgs a) {
     pre += __shfl_xor(pre, off);
     tot += __shfl_xor(tot, off);
   }
-  if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6] = pre; red2[threadIdx.x >> 6] = tot; }
-  // each thread owns 4 consecutive entries of the chunk
+  if (lane == 0) { red[wave] = pre; red2[wave] = tot; }
+  if (threadIdx.x == 0) total_s = 0;
   const int64_t c0 = (int64_t)blockIdx.x * EXPAND_CHUNK;
-  int32_t cnt4[4];
-  int32_t mine = 0;
+  int32_t nd[EXPAND_CHUNK / 256];
+  uint32_t kb[EXPAND_CHUNK / 256];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = threadIdx.x * 4 + i;
-    const int64_t e = c0 + j;
-    int32_t nd = 0;
-    uint32_t kb = 0;
-    cnt4[i] = 0;
-    if (e < cnt) {
-      nd = a.dev.node[lv][kv * cap + e];
-      kb = a.dev.keep[lv][kv * cap + e];
-      cnt4[i] = emitted(a, nd, kb);
-    }
-    enode[j] = nd;
-    ekeep[j] = kb;
-    mine += cnt4[i];
+  for (int r = 0; r < EXPAND_CHUNK / 256; ++r) {
+    const int64_t e = c0 + r * 256 + threadIdx.x;
+    nd[r] = e < cnt ? a.dev.node[lv][kv * cap + e] : 0;
+    kb[r] = e < cnt ? a.dev.keep[lv][kv * cap + e] : 0u;
   }
-  ts[threadIdx.x] = mine;
+  __syncthreads();
+  int32_t mycount = 0;
+  int32_t nk = 0;   // kept entries of the earlier rounds (same value in every thread)
+  // stable compaction of the kept entries, 256 entries a round; wk is read only between
+  // the round's two barriers, so the next round's writes cannot overtake a read
+#pragma unroll
+  for (int r = 0; r < EXPAND_CHUNK / 256; ++r) {
+    const bool k = kb[r] != 0u;
+    const uint64_t ball = __ballot(k);
+    if (lane == 0) wk[wave] = __popcll(ball);
+    __syncthreads();
+    int32_t off = nk;
+    for (int w = 0; w < wave; ++w) off += wk[w];
+    nk += wk[0] + wk[1] + wk[2] + wk[3];
+    if (k) {
+      const int32_t pos = off + __popcll(ball & ((1ull << lane) - 1ull));
+      knode[pos] = nd[r];
+      kmask[pos] = kb[r];
+      mycount += emitted(a, nd[r], kb[r]);
+    }
+    __syncthreads();
+  }
+  for (int off = 1; off < 64; off <<= 1) mycount += __shfl_xor(mycount, off);
+  if (lane == 0) atomicAdd(&total_s, mycount);
   __syncthreads();
   const int32_t base = red[0] + red[1] + red[2] + red[3];
   const int out_lv = lv - 1;
   if (blockIdx.x == 0 && threadIdx.x == 0)
     a.dev.cnt[out_lv * a.hkv + kv] = red2[0] + red2[1] + red2[2] + red2[3];
-  for (int off = 1; off < 256; off <<= 1) {
-    const int32_t add = threadIdx.x >= off ? ts[threadIdx.x - off] : 0;
-    __syncthreads();
-    ts[threadIdx.x] += add;
-    __syncthreads();
-  }
-  int32_t run = ts[threadIdx.x] - mine;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    eoff[threadIdx.x * 4 + i] = run;
-    run += cnt4[i];
-  }
-  if (threadIdx.x == 255) eoff[EXPAND_CHUNK] = ts[255];
-  __syncthreads();
-  // coalesced emission: consecutive threads write consecutive output slots
-  const int32_t total = eoff[EXPAND_CHUNK];
+  const int32_t total = total_s;
   const int64_t ocap = a.dev.ncap[out_lv];
   int32_t* onode = a.dev.node[out_lv] + kv * ocap + base;
   uint32_t* omask = a.dev.mask[out_lv] + kv * ocap + base;
-  for (int32_t o = threadIdx.x; o < total; o += 256) {
-    int lo = 0, hi = EXPAND_CHUNK - 1;   // last entry j with eoff[j] <= o
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (eoff[mid] <= o) lo = mid; else hi = mid - 1;
+  if (lv == 1) {
+    for (int32_t o = threadIdx.x; o < total; o += 256) {
+      onode[o] = knode[o];
+      omask[o] = kmask[o];
     }
-    const int32_t c = o - eoff[lo];
-    onode[o] = lv == 1 ? enode[lo] : enode[lo] * a.b + c;
-    omask[o] = ekeep[lo];
+  } else {
+    const int32_t b = a.b;
+    for (int32_t o = threadIdx.x; o < total; o += 256) {
+      const int32_t k = o / b, c = o - k * b;
+      onode[o] = knode[k] * b + c;
+      omask[o] = kmask[k];
+    }
   }
 }
 
