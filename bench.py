@@ -85,16 +85,17 @@ def src_sha():
 
 
 def traffic_for(kernel, workload):
-    """Measured HBM bytes per launch from a committed counter summary, if it was taken on
-    the current kernel sources."""
+    """Measured HBM bytes per launch (FETCH_SIZE + WRITE_SIZE counters scaled by a plain copy)
+    from the committed counter summary, if it was taken on the kernel's current sources."""
+    from hierarchical_tree_indexed_03_amd.prof_summary import kernel_sha
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        t = json.load(f)
-    if t.get("src_sha") != src_sha():
+        t = json.load(f).get("kernels", {}).get(kernel)
+    if not t or t.get("src_sha") != kernel_sha(kernel):
         return None
-    return t.get("kernels", {}).get(kernel)
+    return t.get("bytes")
 
 
 def cpu_baseline(w, K, V, refs, queries, n0, budget):

@@ -1,0 +1,200 @@
+// Router scoring.
+//
+// A node's score for a query is the max over its reference planes of q.s_j / sqrt(d) + c_j
+// (news summary "Zyphra releases the ZHA sparse attention method", section "Building the
+// tree"; blog "Zyphra Hierarchical Attention", section "Routing through the tree").
+//
+// GPU organisation.  The query heads of one GQA group share a KV head, hence a tree; the
+// router keeps, per KV head and level, the UNION of the group's frontiers as a node list
+// sorted by id with a bitmask of the heads whose frontier holds each node, so a node's
+// planes are read once per group.  The score kernel writes every head's score of every
+// union entry and the per-head max (ordered-integer atomics); the top levels, small enough
+// to score whole, are scored in one launch over several levels.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "route_util.hpp"
+
+// Score-kernel tuning: tiles in flight per wave (R >= 8 / R < 8) and max blocks per KV head.
+#ifndef ZHA_SCORE_UN_WIDE
+#define ZHA_SCORE_UN_WIDE 2
+#endif
+#ifndef ZHA_SCORE_UN_NARROW
+#define ZHA_SCORE_UN_NARROW 2
+#endif
+#ifndef ZHA_SCORE_GRID
+#define ZHA_SCORE_GRID 1024
+#endif
+
+namespace zha {
+
+template <typename TIn, int D>
+__global__ __launch_bounds__(256) void route_prep_kernel(RouteArgs a) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+  const TIn* q = (const TIn*)a.q;
+  for (int64_t i = tid; i < (int64_t)a.hq * D; i += nth) a.dev.qf[i] = a.sigma * to_f32(q[i]);
+  const int64_t nq = (int64_t)(a.levels + 1) * a.hq;
+  for (int64_t i = tid; i < nq; i += nth) {
+    QState z = {};
+    a.dev.qs[i] = z;
+  }
+  const int L = a.levels;
+  const int64_t capL = a.dev.ncap[L];
+  const uint32_t full = (a.g >= 32) ? 0xffffffffu : ((1u << a.g) - 1u);
+  for (int64_t i = tid; i < (int64_t)a.hkv * a.nlevel; i += nth) {
+    const int64_t kv = i / a.nlevel, n = i % a.nlevel;
+    a.dev.node[L][kv * capL + n] = (int32_t)n;
+    a.dev.mask[L][kv * capL + n] = full;
+  }
+  for (int64_t i = tid; i < (int64_t)(MAXL + 1) * a.hkv; i += nth)
+    a.dev.cnt[i] = (i / a.hkv == L) ? (int32_t)a.nlevel : 0;
+}
+
+// ------------------------------------------------------------------ score
+// Scores of the union frontier on fp32 MFMA: one 16x16 output tile = the 16 query-head rows
+// (the group's heads, zero-padded) x 16 columns = 16/R nodes x R planes.  The contraction
+// over d is permuted so that lane (column c, group kg) streams the contiguous 64-byte
+// pieces [64i + 16kg, +16) of its plane row; Q uses the same permutation.  A node's score is
+// the max over its R columns (plus the offsets c_j), taken across the R lanes of the node.
+template <int D, int R>
+__global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
+  constexpr int NPT = 16 / R;                 // nodes per 16-column tile
+  constexpr int NI = D / 16;                  // float4 loads per lane per tile
+  constexpr int UN = R >= 8 ? ZHA_SCORE_UN_WIDE : ZHA_SCORE_UN_NARROW;   // tiles in flight per wave
+  __shared__ float red[4][16];
+  const int kv = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int slot = col / R, plane = col % R;
+  const bool dense = a.dense != 0;            // every node of the level, no list
+  const int lv = dense ? a.level - (int)blockIdx.z : a.level;
+  const int64_t cnt = dense ? a.nl[lv] : a.dev.cnt[lv * a.hkv + kv];
+  const int64_t cap = a.dev.ncap[lv];
+  const int32_t* nodes = a.dev.node[lv] + kv * cap;
+  const uint32_t* masks = a.dev.mask[lv] + kv * cap;
+  const float* S = a.dev.s[lv] + (int64_t)kv * cap * R * D;
+  const float* C = a.dev.c[lv] + (int64_t)kv * cap * R;
+  float* out = a.dev.score[lv] + (int64_t)kv * GMAX * cap;
+  const int g = a.g;
+
+  float qa[NI][4];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (col < g) x = *(const float4*)(a.dev.qf + (int64_t)(kv * g + col) * D + 16 * i + 4 * kg);
+    qa[i][0] = x.x; qa[i][1] = x.y; qa[i][2] = x.z; qa[i][3] = x.w;
+  }
+  float runmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+
+  const int64_t ntiles = (cnt + NPT - 1) / NPT;
+  for (int64_t t0 = ((int64_t)blockIdx.x * 4 + wave) * UN; t0 < ntiles; t0 += (int64_t)gridDim.x * 4 * UN) {
+    float4 sb[UN][NI];
+    float cj[UN];
+    int64_t ent[UN];
+    bool ok[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      ent[u] = (t0 + u) * NPT + slot;
+      ok[u] = (t0 + u) < ntiles && ent[u] < cnt;
+      const int64_t nid = ok[u] ? (dense ? ent[u] : (int64_t)nodes[ent[u]]) : 0;
+      const float* sp = S + (nid * R + plane) * D + 4 * kg;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) sb[u][i] = ok[u] ? *(const float4*)(sp + 16 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      cj[u] = ok[u] ? C[nid * R + plane] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][0], sb[u][i].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][1], sb[u][i].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][2], sb[u][i].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][3], sb[u][i].w, acc, 0, 0, 0);
+      }
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[e] + cj[u];
+#pragma unroll
+      for (int off = 1; off < R; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], __shfl_xor(v[e], off));
+      const uint32_t mk = (ok[u] && !dense) ? masks[ent[u]] : 0u;   // dense: max taken later
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int h = kg * 4 + e;
+        if (ok[u] && plane == 0 && h < g) out[(int64_t)h * cap + ent[u]] = v[e];
+        if ((mk >> h) & 1u) runmax[e] = fmaxf(runmax[e], v[e]);
+      }
+    }
+  }
+  // per-head max: lanes of one 16-lane row share kg, i.e. the heads 4kg..4kg+3
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v = runmax[e];
+    for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (col == 0) red[wave][kg * 4 + e] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < g) {
+    const int gi = threadIdx.x;
+    const float m = fmaxf(fmaxf(red[0][gi], red[1][gi]), fmaxf(red[2][gi], red[3][gi]));
+    if (m > -INFINITY) atomicMax(&a.dev.qs[lv * a.hq + kv * g + gi].maxkey, f2key(m));
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_route_prep(const RouteArgs& a, bool bf16, int D, hipStream_t st) {
+  dim3 grid(256), block(256);
+  if (bf16) {
+    if (D == 64) hipLaunchKernelGGL((route_prep_kernel<bf16_t, 64>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((route_prep_kernel<bf16_t, 128>), grid, block, 0, st, a);
+  } else {
+    if (D == 64) hipLaunchKernelGGL((route_prep_kernel<float, 64>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((route_prep_kernel<float, 128>), grid, block, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int D, int R>
+static void launch_score(const RouteArgs& a, hipStream_t st) {
+  constexpr int NPB = 4 * (16 / R) * (R >= 8 ? ZHA_SCORE_UN_WIDE : ZHA_SCORE_UN_NARROW);   // nodes per block pass
+  int64_t x = (a.nlevel + NPB - 1) / NPB;
+  if (x > ZHA_SCORE_GRID) x = ZHA_SCORE_GRID;
+  if (x < 1) x = 1;
+  hipLaunchKernelGGL((route_score_kernel<D, R>), dim3((unsigned)x, (unsigned)a.hkv), dim3(256), 0, st, a);
+}
+
+hipError_t launch_route_score(const RouteArgs& a, int D, int R, hipStream_t st) {
+#define ZHA_CASE(DD, RR) else if (D == DD && R == RR) launch_score<DD, RR>(a, st);
+  if (false) {}
+  ZHA_CASE(64, 1) ZHA_CASE(64, 2) ZHA_CASE(64, 4) ZHA_CASE(64, 8) ZHA_CASE(64, 16)
+  ZHA_CASE(128, 1) ZHA_CASE(128, 2) ZHA_CASE(128, 4) ZHA_CASE(128, 8) ZHA_CASE(128, 16)
+  else return hipErrorInvalidValue;
+#undef ZHA_CASE
+  return hipGetLastError();
+}
+
+template <int D, int R>
+static void launch_dense_score_t(const RouteArgs& a, int nlev, hipStream_t st) {
+  constexpr int NPB = 4 * (16 / R) * (R >= 8 ? ZHA_SCORE_UN_WIDE : ZHA_SCORE_UN_NARROW);
+  int64_t mx = 0;
+  for (int l = a.dense_lo; l <= a.level; ++l) mx = a.nl[l] > mx ? a.nl[l] : mx;
+  int64_t x = (mx + NPB - 1) / NPB;
+  if (x > ZHA_SCORE_GRID) x = ZHA_SCORE_GRID;
+  if (x < 1) x = 1;
+  hipLaunchKernelGGL((route_score_kernel<D, R>), dim3((unsigned)x, (unsigned)a.hkv, (unsigned)nlev), dim3(256), 0,
+                     st, a);
+}
+
+hipError_t launch_route_dense_score(const RouteArgs& a, int D, int R, hipStream_t st) {
+  const int nlev = a.level - a.dense_lo + 1;
+#define ZHA_CASE(DD, RR) else if (D == DD && R == RR) launch_dense_score_t<DD, RR>(a, nlev, st);
+  if (false) {}
+  ZHA_CASE(64, 1) ZHA_CASE(64, 2) ZHA_CASE(64, 4) ZHA_CASE(64, 8) ZHA_CASE(64, 16)
+  ZHA_CASE(128, 1) ZHA_CASE(128, 2) ZHA_CASE(128, 4) ZHA_CASE(128, 8) ZHA_CASE(128, 16)
+  else return hipErrorInvalidValue;
+#undef ZHA_CASE
+  return hipGetLastError();
+}
+
+}  // namespace zha

@@ -1,0 +1,240 @@
+"""Summaries of rocprofv3 output for the ZHA decode path (CSV output, run on any host).
+
+    python -m hierarchical_tree_indexed_03_amd.prof_summary trace DIR WORKLOAD --cmd "..." [--out FILE]
+    python -m hierarchical_tree_indexed_03_amd.prof_summary pmc FETCH_DIR WRITE_DIR WORKLOAD --cmd "..." [--out FILE]
+
+``trace`` reads ``*_kernel_trace.csv`` (``rocprofv3 --kernel-trace --stats --output-format csv``)
+and attributes every dispatch of a decode (route_prep ... combine) to its router level: the
+general-path launches of a decode run from the highest general level down to level 1, so
+they are numbered from the end.  It prints a markdown table of per-level averages.
+
+``pmc`` reads two ``*_counter_collection.csv`` files (one run with ``--pmc FETCH_SIZE``, one with
+``--pmc WRITE_SIZE``), scales the counters by what they read for the plain 1 GiB copy kernel
+of the probe library (bench.py --calib-copy), and writes the measured HBM bytes per launch
+of level-1 scoring and of the attention kernel to ``profiles/traffic_<WORKLOAD>.json``, keyed
+by the hash of the sources of each kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+SHARED = ["common.hpp", "kernels.hpp", "route_util.hpp"]
+KERNEL_SRC = {
+    "route_score": ["score.hip"],
+    "route_select": ["select.hip"],
+    "route_expand": ["expand.hip"],
+    "attend": ["attend.hip"],
+    "dense_attend": ["attend.hip"],
+    "append": ["build.hip"],
+    "build": ["build.hip"],
+}
+CALIB_BYTES = 1 << 30
+
+
+def kernel_sha(key: str) -> str:
+    """Hash of the sources that define the kernels behind a profile key (plus shared headers)."""
+    files = KERNEL_SRC.get(key.split(".")[0])
+    if files is None:
+        files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp")))
+    h = hashlib.sha256()
+    for f in sorted(set(files) | set(SHARED)):
+        p = os.path.join(CSRC, f)
+        if os.path.exists(p):
+            with open(p, "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def short(name: str) -> str:
+    n = name.replace("zha::", "").replace("(anonymous namespace)::", "")
+    return n.split("(")[0].replace("void ", "")
+
+
+STAGE = {
+    "route_score_kernel": "score", "route_hist_kernel": "hist", "route_bound_kernel": "bound",
+    "route_classify_kernel": "classify", "route_resolve_kernel": "resolve",
+    "route_expand_count_kernel": "expand_count", "route_expand_emit_kernel": "expand_emit",
+}
+
+
+def decodes(rows):
+    """Splits time-ordered dispatches into decodes: lists from route_prep to combine."""
+    out, cur = [], None
+    for r in rows:
+        n = short(r["name"])
+        if n.startswith("route_prep_kernel"):
+            cur = [r]
+        elif cur is not None:
+            cur.append(r)
+            if n.startswith("combine_kernel"):
+                out.append(cur)
+                cur = None
+    return out
+
+
+def label(dec):
+    """(label, row) per dispatch of one decode: score.top / select.top for the top levels,
+    <stage>.l<level> for the general levels, the kernel's short name otherwise."""
+    names = [short(r["name"]).split("<")[0] for r in dec]
+    top = {i - 1 for i, n in enumerate(names) if n == "route_mls_kernel" and i > 0 and names[i - 1] == "route_score_kernel"}
+    general = [i for i, n in enumerate(names) if n == "route_score_kernel" and i not in top]
+    res = []
+    lv = None
+    for i, (n, r) in enumerate(zip(names, dec)):
+        if i in top:
+            res.append(("score.top", r))
+            continue
+        if n == "route_score_kernel":
+            lv = len(general) - general.index(i)
+        if n in STAGE and lv is not None:
+            res.append((f"{STAGE[n]}.l{lv}", r))
+        elif n == "route_mls_kernel":
+            res.append(("select.top", r))
+        else:
+            res.append((n.replace("_kernel", ""), r))
+    return res
+
+
+def read_trace(d):
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no kernel_trace.csv under {d}")
+    rows = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            rows.append(dict(name=r["Kernel_Name"], t0=int(r["Start_Timestamp"]), t1=int(r["End_Timestamp"]),
+                             gz=int(r.get("Grid_Size_Z", 1) or 1),
+                             grid=int(r.get("Grid_Size_X", 0) or 0) // max(1, int(r.get("Workgroup_Size_X", 1) or 1))))
+    rows.sort(key=lambda r: r["t0"])
+    return rows, files
+
+
+def cmd_trace(a):
+    rows, files = read_trace(a.dir)
+    decs = decodes(rows)
+    # the ZHA decodes are those whose attention is the routed (non-dense) kernel
+    decs = [d for d in decs if any("attend_kernel" in r["name"] and "false" in r["name"] for r in d)]
+    per = defaultdict(list)
+    step_us = []
+    for d in decs:
+        for lab, r in label(d):
+            per[lab].append((r["t1"] - r["t0"]) / 1e3)
+        step_us.append((d[-1]["t1"] - d[0]["t0"]) / 1e3)
+    order = sorted(per, key=lambda k: -sum(per[k]) / len(per[k]))
+    lines = [f"# rocprofv3 kernel trace: ZHA decode, workload `{a.workload}`", "",
+             "Command (from the repository root on the GPU host):", "", "```", a.cmd, "```", "",
+             "Summarised with:", "", "```",
+             f"python -m hierarchical_tree_indexed_03_amd.prof_summary trace {a.dir} {a.workload} --cmd '...'",
+             "```", "",
+             f"{len(decs)} routed decodes; decode span (route_prep start to combine end) "
+             f"avg {sum(step_us) / max(1, len(step_us)):.1f} us.  Per-level kernels are numbered from level 1 "
+             "(the last general level of each decode).", "",
+             "| launch | calls | avg us | min us | max us | share of decode |", "|---|---:|---:|---:|---:|---:|"]
+    tot = sum(sum(v) / len(decs) for v in per.values()) if decs else 1.0
+    for k in order:
+        v = per[k]
+        lines.append(f"| {k} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} | "
+                     f"{100 * sum(v) / len(decs) / tot:.1f}% |")
+    stats = glob.glob(os.path.join(a.dir, "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        lines += ["", "rocprofv3 --stats (all dispatches of the run, top 15):", "",
+                  "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+        for r in list(csv.DictReader(open(stats[0])))[:15]:
+            lines.append(f"| {short(r['Name'])[:60]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
+def read_pmc(d, counter):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no counter_collection.csv under {d}")
+    disp = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            k = int(r["Dispatch_Id"])
+            e = disp.setdefault(k, dict(name=r["Kernel_Name"], v=0.0,
+                                        gz=int(r.get("Grid_Size_Z", 1) or 1) if "Grid_Size_Z" in r else 1))
+            e["v"] += float(r["Counter_Value"])
+    return [dict(id=k, **disp[k]) for k in sorted(disp)]
+
+
+def pmc_groups(rows):
+    """Per dispatch list: calibration copy value, level-1 scoring values, attention values."""
+    calib = [r["v"] for r in rows if short(r["name"]) == "copy_kernel"]
+    l1, att = [], []
+    last_score = None
+    for r in rows:
+        n = short(r["name"])
+        if n.startswith("route_prep_kernel"):
+            last_score = None
+        elif n.startswith("route_score_kernel"):
+            last_score = r
+        elif n.startswith("attend_kernel") and "false" in r["name"]:
+            att.append(r["v"])
+            if last_score is not None:
+                l1.append(last_score["v"])
+    return calib, l1, att
+
+
+def cmd_pmc(a):
+    fetch = read_pmc(a.fetch_dir, "FETCH_SIZE")
+    write = read_pmc(a.write_dir, "WRITE_SIZE")
+    cf, f_l1, f_att = pmc_groups(fetch)
+    cw, w_l1, w_att = pmc_groups(write)
+    if not cf or not cw:
+        sys.exit("calibration copy kernel not found (run bench.py with --calib-copy)")
+    # counters are in KiB; scale each so the 1 GiB copy reads 1 GiB and writes 1 GiB
+    kf = CALIB_BYTES / (cf[-1] * 1024.0)
+    kw = CALIB_BYTES / (cw[-1] * 1024.0)
+    mean = lambda v: sum(v) / len(v) if v else None
+    out = {"workload": a.workload, "calib": {"copy_bytes": CALIB_BYTES, "fetch_kib": cf[-1], "write_kib": cw[-1],
+                                             "fetch_scale": kf, "write_scale": kw},
+           "command": a.cmd, "kernels": {}}
+    for key, fv, wv in (("route_score.l1", f_l1, w_l1), ("attend", f_att, w_att)):
+        if fv and wv:
+            fb, wb = mean(fv) * 1024 * kf, mean(wv) * 1024 * kw
+            out["kernels"][key] = {"src_sha": kernel_sha(key), "bytes": round(fb + wb), "fetch_bytes": round(fb),
+                                   "write_bytes": round(wb), "launches": [len(fv), len(wv)]}
+    path = a.out or os.path.join(ROOT, "profiles", f"traffic_{a.workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sp = ap.add_subparsers(dest="mode", required=True)
+    t = sp.add_parser("trace")
+    t.add_argument("dir")
+    t.add_argument("workload")
+    t.add_argument("--cmd", default="")
+    t.add_argument("--out", default=None)
+    p = sp.add_parser("pmc")
+    p.add_argument("fetch_dir")
+    p.add_argument("write_dir")
+    p.add_argument("workload")
+    p.add_argument("--cmd", default="")
+    p.add_argument("--out", default=None)
+    a = ap.parse_args()
+    cmd_trace(a) if a.mode == "trace" else cmd_pmc(a)
+
+
+if __name__ == "__main__":
+    main()
