@@ -52,20 +52,31 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_bytes(key, w, stats_rows, n_tokens):
+def node_bytes(w, level, key_form):
+    """Algorithmic bytes read to score one union-frontier node at `level`: its R planes
+    (R*(d+1) floats), or at level 1 in key form its b keys (bf16) plus R*b token weights and
+    R offsets; plus the 8-byte list entry and one float score per query head written."""
+    R, d, g, b = w.num_ref, w.head_dim, w.group, w.block
+    if level == 1 and key_form:
+        core = b * d * 2 + R * b * 4 + R * 4
+    else:
+        core = R * (d + 1) * 4
+    return core + 8 + g * 4
+
+
+def kernel_bytes(key, w, stats_rows, n_tokens, key_form):
     """Algorithmic HBM bytes of one launch of `key` given the routing stats of that step.
 
-    route_score.l<l>: per union-frontier node R*(d+1)*4 plane bytes + 8 bytes of list entry
-                      + 4 bytes per query head of the group for the score written;
-    attend:           per gathered token 2*d*2 bytes (K and V rows, bf16) + per KV head the
-                      sink row; partial results excluded;
+    route_score.l<l>: node_bytes per union-frontier node;
+    attend:           per gathered token 2*d*2 bytes (K and V rows, bf16); partial results
+                      excluded;
     dense_attend:     N * Hkv * 2 * d * 2 bytes.
     """
-    R, d, g, L = w.num_ref, w.head_dim, w.group, w.levels
+    d, L = w.head_dim, w.levels
     if key.startswith("route_score.l"):
         lv = int(key.split(".l")[1])
         u = stats_rows[L - lv].sum()
-        return float(u) * (R * (d + 1) * 4 + 8 + g * 4)
+        return float(u) * node_bytes(w, lv, key_form)
     if key == "attend":
         blocks = stats_rows[L].sum()
         return float(blocks) * w.block * 2 * d * 2
@@ -235,7 +246,8 @@ def main():
     qps = steps / wall
     st = stats.cpu().numpy()
     timed_stats = st[args.warmup:]
-    dom_bytes = [kernel_bytes(dominant, w, timed_stats[i], n0 + args.warmup + i + 1) for i in range(steps)]
+    key_form = zha.zha_level1_key_form(cfg) == 1
+    dom_bytes = [kernel_bytes(dominant, w, timed_stats[i], n0 + args.warmup + i + 1, key_form) for i in range(steps)]
     dom_avg_ms = dom_ms / max(dom_n, 1)
     roofline = None
     if dom_bytes[0] is not None:
@@ -250,8 +262,8 @@ def main():
 
     # ---- decode-step bytes (router planes + gathered KV), from the routing stats
     R, d, g, L = w.num_ref, w.head_dim, w.group, w.levels
-    plane = R * (d + 1) * 4
-    router_b = timed_stats[:, :L, :].sum(axis=(1, 2)) * plane
+    per_level = np.array([node_bytes(w, L - row, key_form) for row in range(L)], dtype=np.float64)
+    router_b = (timed_stats[:, :L, :].sum(axis=2) * per_level[None, :]).sum(axis=1)
     gather_b = timed_stats[:, L, :].sum(axis=1) * w.block * 2 * d * 2
     step_bytes = float(np.mean(router_b + gather_b))
 
@@ -326,7 +338,7 @@ def main():
                    "batch": 1, "layers": 1, "step": "append + decode"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "decode_step": {"alg_bytes": round(step_bytes), "achieved_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "decode_step": {"level1_key_form": key_form, "alg_bytes": round(step_bytes), "achieved_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                         "router_bytes": round(float(np.mean(router_b))), "gather_bytes": round(float(np.mean(gather_b))),
                         "frontier_union_per_level": timed_stats[:, :L, :].sum(axis=2).mean(axis=0).round(1).tolist(),
                         "kept_blocks_union": float(timed_stats[:, L, :].sum(axis=1).mean())},

@@ -164,6 +164,15 @@ __global__ __launch_bounds__(256) void build_tile_kernel(BuildArgs a) {
       Ws[idx] = t < nt ? expf(Zs[idx] - Ls[off[v] + (int)(t / bv) * R + j]) : 0.f;
     }
     __syncthreads();
+    if (v == 1 && a.dev.w1) {
+      // token weights of the level-1 planes, [node][j][token in block] (zero past the data)
+      const int b = a.b;
+      for (int idx = threadIdx.x; idx < nexist * R * b; idx += NT) {
+        const int node = idx / (R * b), j = (idx / b) % R, k = idx % b;
+        const int t = node * b + k;
+        a.dev.w1[((int64_t)kv * a.dev.ncap[1] + t0 / b + node) * R * b + j * b + k] = t < nt ? Ws[t * R + j] : 0.f;
+      }
+    }
     if constexpr (R >= 8) {
       const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
       const int col = lane & 15, kg = lane >> 4;
@@ -322,6 +331,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     a.dev.lse[1][gi] = lse;
   }
   __syncthreads();
+  if (a.dev.w1) {
+    for (int idx = threadIdx.x; idx < R * a.b; idx += NT) {
+      const int j = idx / a.b, k = idx % a.b;
+      a.dev.w1[((int64_t)kv * cap1 + n1) * R * a.b + idx] = k < nt ? expf(Zs[k * R + j] - Lj[j]) : 0.f;
+    }
+  }
   for (int it = threadIdx.x; it < R * (D / 4); it += NT) {
     const int j = it / (D / 4), dc = it % (D / 4);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);

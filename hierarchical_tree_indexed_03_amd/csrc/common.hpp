@@ -77,6 +77,8 @@ struct Dev {
   float* s[MAXL + 1];       // level l: [Hkv][ncap[l]][R][D]
   float* c[MAXL + 1];       // level l: [Hkv][ncap[l]][R]
   float* lse[MAXL + 1];     // level l: [Hkv][ncap[l]][R] log mass at r_j (build/append only)
+  float* w1;                // [Hkv][ncap[1]][R][b] token weights of the level-1 planes
+                            // (key-form scoring only; null otherwise)
   int64_t ncap[MAXL + 1];   // node capacity per level (index 0: gather list = ncap[1])
   // router, per level l = 0..L (0 = kept level-1 blocks)
   int32_t* node[MAXL + 1];  // [Hkv][ncap[l]]

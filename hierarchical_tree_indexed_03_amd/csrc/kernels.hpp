@@ -50,6 +50,9 @@ struct RouteArgs {
   int32_t dense;      // score kernel: 1 = every node of levels `level` .. `level`-gridDim.z+1
   int32_t dense_lo;   // lowest level handled by the multi-level selection kernel
   int32_t sel_p;      // top-p histogram / classify workgroups per KV head at `level`
+  int32_t key_form;   // level 1 scored from the block's keys and the planes' token weights
+  const void* K;      // key cache [Hkv][kcap][D] (key-form scoring)
+  int64_t kcap;
   int64_t nl[MAXL + 1];   // nodes per level at N
 };
 

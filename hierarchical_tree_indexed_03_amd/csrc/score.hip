@@ -13,6 +13,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "route_util.hpp"
+#include "qk_tile.hpp"
 
 // Score-kernel tuning: tiles in flight per wave (R >= 8 / R < 8) and max blocks per KV head.
 #ifndef ZHA_SCORE_UN_WIDE
@@ -142,6 +143,115 @@ __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
   }
 }
 
+
+// ------------------------------------------------------------------ key-form level 1
+// A level-1 plane's s_j is the softmax-weighted mean of its block's keys (weights w_jt over
+// the block's tokens at r_j), so q.s_j / sqrt(d) = sum_t w_jt (q.k_t / sqrt(d)): the scores
+// of a block follow from the group's logits on its b keys and the R x b stored weights.
+// Per 16-token tile (16/b nodes): the logits tile S^T = K.Q^T (bf16 MFMA, tokens x heads),
+// transposed through LDS, then per node one fp32 MFMA per 4 tokens, [planes x tokens] x
+// [tokens x heads] accumulated onto c_j, so each lane holds 4 planes of one head: the max
+// over planes is 3 in-lane maxima and 2 cross-lane steps.
+template <int D, int R, int B>
+__global__ __launch_bounds__(256) void route_score_keys_kernel(RouteArgs a) {
+  constexpr int NPT = 16 / B;                 // nodes per 16-token tile
+  constexpr int KS = (B + 3) / 4;             // fp32 MFMA steps per node
+  constexpr int UN = 2;                       // tiles in flight per wave
+  constexpr int NK = Qk<bf16_t, D>::NL;
+  __shared__ float Lt[4][16][17];             // per wave: logits [head][token]
+  __shared__ float red[4][16];
+  const int kv = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int lv = 1;
+  const int64_t cnt = a.dev.cnt[lv * a.hkv + kv];
+  const int64_t cap = a.dev.ncap[lv];
+  const int32_t* nodes = a.dev.node[lv] + kv * cap;
+  const uint32_t* masks = a.dev.mask[lv] + kv * cap;
+  const bf16_t* Kc = (const bf16_t*)a.K + (int64_t)kv * a.kcap * D;
+  const float* W = a.dev.w1 + (int64_t)kv * cap * R * B;
+  const float* C = a.dev.c[lv] + (int64_t)kv * cap * R;
+  float* out = a.dev.score[lv] + (int64_t)kv * GMAX * cap;
+  const int g = a.g;
+  const int64_t N = a.N;
+
+  Qk<bf16_t, D> qk;
+  qk.load_q((const bf16_t*)a.q + (int64_t)kv * g * D, g, col, kg);
+  float runmax = -INFINITY;                   // head `col`
+
+  const int64_t ntiles = (cnt + NPT - 1) / NPT;
+  for (int64_t t0 = ((int64_t)blockIdx.x * 4 + wave) * UN; t0 < ntiles; t0 += (int64_t)gridDim.x * 4 * UN) {
+    uint4 kf[UN][NK];
+    float wv[UN][NPT][KS];
+    f32x4 cj[UN][NPT];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      // the tile's 16 token rows: token `col` of node col / B; rows past the data read zeros
+      const int64_t e_row = (t0 + u) * NPT + col / B;
+      const bool row_ok = (t0 + u) < ntiles && e_row < cnt;
+      const int64_t tok = row_ok ? (int64_t)nodes[e_row] * B + col % B : 0;
+      if (row_ok && tok < N) {
+        Qk<bf16_t, D>::load_k(Kc + tok * D, kg, kf[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NK; ++i) kf[u][i] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int n = 0; n < NPT; ++n) {
+        const int64_t e = (t0 + u) * NPT + n;   // wave-uniform
+        const bool ok = (t0 + u) < ntiles && e < cnt;
+        const int64_t nid = ok ? nodes[e] : 0;
+        // A operand: lane (plane col, token 4s + kg) holds w[plane][token]
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const int k = 4 * s + kg;
+          wv[u][n][s] = (ok && col < R && k < B) ? W[(nid * R + col) * B + k] : 0.f;
+        }
+        // accumulator: c of planes 4kg..4kg+3 (absent planes -inf)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int j = 4 * kg + e4;
+          cj[u][n][e4] = (ok && j < R) ? C[nid * R + j] : -INFINITY;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const f32x4 st = qk.mma(kf[u]);          // S^T[token 4kg+e][head col]
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Lt[wave][col][kg * 4 + e] = a.sigma * st[e];
+      wave_sync_lds();
+#pragma unroll
+      for (int n = 0; n < NPT; ++n) {
+        f32x4 acc = cj[u][n];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const int k = 4 * s + kg;
+          // B operand: lane (head col, token k) holds the logit
+          const float lg = k < B ? Lt[wave][col][n * B + k] : 0.f;
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[u][n][s], lg, acc, 0, 0, 0);
+        }
+        // acc[e] = score of plane 4kg+e for head col
+        float v = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+        v = fmaxf(v, __shfl_xor(v, 16));
+        v = fmaxf(v, __shfl_xor(v, 32));
+        const int64_t e_ent = (t0 + u) * NPT + n;   // wave-uniform
+        const bool ok = (t0 + u) < ntiles && e_ent < cnt;
+        const uint32_t mk = ok ? masks[e_ent] : 0u;
+        if (ok && kg == 0 && col < g) out[(int64_t)col * cap + e_ent] = v;
+        if ((mk >> col) & 1u) runmax = fmaxf(runmax, v);
+      }
+      wave_sync_lds();
+    }
+  }
+  if (kg == 0) red[wave][col] = runmax;
+  __syncthreads();
+  if (threadIdx.x < g) {
+    const int gi = threadIdx.x;
+    const float m = fmaxf(fmaxf(red[0][gi], red[1][gi]), fmaxf(red[2][gi], red[3][gi]));
+    if (m > -INFINITY) atomicMax(&a.dev.qs[lv * a.hq + kv * g + gi].maxkey, f2key(m));
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 hipError_t launch_route_prep(const RouteArgs& a, bool bf16, int D, hipStream_t st) {
   dim3 grid(256), block(256);
@@ -164,7 +274,27 @@ static void launch_score(const RouteArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((route_score_kernel<D, R>), dim3((unsigned)x, (unsigned)a.hkv), dim3(256), 0, st, a);
 }
 
+template <int D, int R, int B>
+static void launch_score_keys(const RouteArgs& a, hipStream_t st) {
+  constexpr int NPB = 4 * (16 / B) * 2;   // nodes per block pass
+  int64_t x = (a.nlevel + NPB - 1) / NPB;
+  if (x > ZHA_SCORE_GRID) x = ZHA_SCORE_GRID;
+  if (x < 1) x = 1;
+  hipLaunchKernelGGL((route_score_keys_kernel<D, R, B>), dim3((unsigned)x, (unsigned)a.hkv), dim3(256), 0, st, a);
+}
+
 hipError_t launch_route_score(const RouteArgs& a, int D, int R, hipStream_t st) {
+  if (a.key_form && a.level == 1 && !a.dense) {
+#define ZHA_KCASE(DD, RR, BB) else if (D == DD && R == RR && a.b == BB) launch_score_keys<DD, RR, BB>(a, st);
+#define ZHA_KCASES(DD, RR) ZHA_KCASE(DD, RR, 2) ZHA_KCASE(DD, RR, 4) ZHA_KCASE(DD, RR, 8) ZHA_KCASE(DD, RR, 16)
+    if (false) {}
+    ZHA_KCASES(64, 2) ZHA_KCASES(64, 4) ZHA_KCASES(64, 8) ZHA_KCASES(64, 16)
+    ZHA_KCASES(128, 2) ZHA_KCASES(128, 4) ZHA_KCASES(128, 8) ZHA_KCASES(128, 16)
+    else return hipErrorInvalidValue;
+#undef ZHA_KCASES
+#undef ZHA_KCASE
+    return hipGetLastError();
+  }
 #define ZHA_CASE(DD, RR) else if (D == DD && R == RR) launch_score<DD, RR>(a, st);
   if (false) {}
   ZHA_CASE(64, 1) ZHA_CASE(64, 2) ZHA_CASE(64, 4) ZHA_CASE(64, 8) ZHA_CASE(64, 16)

@@ -66,6 +66,17 @@ int64_t ipow_sat(int64_t b, int l) {
 
 int64_t nodes_at(const zha_config& c, int level, int64_t n) { return ceil_div(n, ipow_sat(c.block, level)); }
 
+// Level 1 is scored from the block's keys and the planes' token weights (q.s_j is the
+// weighted sum of the block's logits q.k_t) when that reads fewer bytes than the planes:
+// b keys plus R*b weights against R planes of d floats.  bf16 keys, b in {2, 4, 8, 16}.
+bool key_form(const zha_config& c) {
+  if (c.dtype != ZHA_BF16) return false;
+  if (c.block != 2 && c.block != 4 && c.block != 8 && c.block != 16) return false;
+  const int64_t keys = (int64_t)c.block * c.head_dim * 2 + (int64_t)c.num_ref * c.block * 4;
+  const int64_t planes = (int64_t)c.num_ref * c.head_dim * 4;
+  return keys < planes;
+}
+
 int tile_tokens(const zha_config& c) { return c.block <= 128 ? 128 : 256; }
 
 int tile_levels(const zha_config& c) {
@@ -129,6 +140,7 @@ size_t layout(const zha_config& c, char* base, Dev* dev) {
       d.part[l] = (int32_t*)take((size_t)(H * ceil_div(d.ncap[l], EXPAND_CHUNK)) * 4);
     }
   }
+  if (key_form(c)) d.w1 = (float*)take((size_t)(H * d.ncap[1] * R * c.block) * 4);
   d.cnt = (int32_t*)take((size_t)((MAXL + 1) * H) * 4);
   d.qs = (QState*)take((size_t)((L + 1) * Q) * sizeof(QState));
   d.hpart = (uint64_t*)take((size_t)(H * SEL_P * GMAX * NB1) * 8);
@@ -166,6 +178,9 @@ RouteArgs route_args(const zha_tree* t, const void* q) {
   a.levels = t->cfg.levels;
   a.top_p = t->cfg.top_p;
   a.sigma = 1.0f / sqrtf((float)t->cfg.head_dim);
+  a.key_form = key_form(t->cfg) ? 1 : 0;
+  a.K = t->K;
+  a.kcap = t->cfg.capacity;
   for (int l = 1; l <= t->cfg.levels; ++l) a.nl[l] = nodes_at(t->cfg, l, t->N);
   a.nl[0] = a.nl[1];
   return a;
@@ -216,6 +231,11 @@ zha_status route_levels(zha_tree* t, RouteArgs& a, int lv, hipStream_t st, bool 
 }  // namespace
 
 extern "C" {
+
+int32_t zha_level1_key_form(const zha_config* cfg) {
+  if (validate(cfg) != ZHA_OK) return -1;
+  return key_form(*cfg) ? 1 : 0;
+}
 
 size_t zha_workspace_bytes(const zha_config* cfg) {
   if (validate(cfg) != ZHA_OK) return 0;
@@ -337,6 +357,7 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
   // top levels small enough for the one-launch multi-level selection
   int lo = c.levels + 1;
   while (lo > 1 && r.nl[lo - 1] <= MLS_MAX) --lo;
+  if (r.key_form && lo == 1) lo = 2;   // key-form level 1 is scored by its own kernel
   if (lo <= c.levels) {
     r.level = c.levels;
     r.dense = 1;

@@ -42,6 +42,7 @@ def _load() -> ctypes.CDLL:
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     sig = {
         "zha_workspace_bytes": (SZ, [ctypes.POINTER(zha_config)]),
+        "zha_level1_key_form": (I32, [ctypes.POINTER(zha_config)]),
         "zha_create": (I32, [ctypes.POINTER(zha_config), P, SZ, ctypes.POINTER(P)]),
         "zha_tree_build": (I32, [P, P, P, I64, P, P]),
         "zha_tree_append": (I32, [P, P, P, P]),
@@ -64,7 +65,7 @@ def _load() -> ctypes.CDLL:
 
 
 _lib = _load()
-EXPORTED = ("zha_workspace_bytes", "zha_create", "zha_tree_build", "zha_tree_append", "zha_decode",
+EXPORTED = ("zha_workspace_bytes", "zha_level1_key_form", "zha_create", "zha_tree_build", "zha_tree_append", "zha_decode",
             "zha_decode_dense", "zha_debug_level", "zha_debug_trace", "zha_debug_route_level",
             "zha_profile_start", "zha_profile_stop", "zha_num_tokens", "zha_destroy", "zha_status_string",
             "zha_last_error")
@@ -96,6 +97,10 @@ def make_config(head_dim, num_kv_heads, num_q_heads, block, levels, num_ref, cap
     dt = dtype if isinstance(dtype, int) else (ZHA_BF16 if dtype in ("bf16", torch.bfloat16) else ZHA_F32)
     return zha_config(head_dim, num_kv_heads, num_q_heads, block, levels, num_ref, capacity, dt,
                       float(top_p), int(bool(keep_sink)))
+
+
+def zha_level1_key_form(cfg: zha_config) -> int:
+    return int(_lib.zha_level1_key_form(ctypes.byref(cfg)))
 
 
 def zha_workspace_bytes(cfg: zha_config) -> int:

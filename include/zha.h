@@ -73,6 +73,14 @@ typedef struct zha_tree zha_tree;   /* opaque host-side handle */
  * attention scratch.  Returns 0 for an invalid or unsupported config. */
 size_t zha_workspace_bytes(const zha_config* cfg);
 
+/* How level 1 is scored for this config (news summary, "Building the tree": a level-1
+ * plane's s_j is the softmax-weighted mean of its block's keys, so q.s_j is the same weighted
+ * sum of the block's logits q.k_t).  Returns 1 when the library scores level 1 from the
+ * block's keys and the stored R x b token weights (bf16 keys, b in {2, 4, 8, 16}, and fewer
+ * bytes than the R planes), 0 when it reads the planes, -1 for an invalid config.  Host
+ * only; no side effects. */
+int32_t zha_level1_key_form(const zha_config* cfg);
+
 /* Creates a handle over a caller-owned device `workspace` (>= zha_workspace_bytes,
  * 256-byte aligned).  The workspace is borrowed until zha_destroy. */
 zha_status zha_create(const zha_config* cfg, void* workspace, size_t workspace_bytes,

@@ -24,7 +24,7 @@ def zha():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(zha_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(zha_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_match_header(zha):
@@ -81,6 +81,21 @@ def test_workspace_grows_with_capacity(zha):
     a = zha.zha_workspace_bytes(good(zha, capacity=1 << 16))
     b = zha.zha_workspace_bytes(good(zha, capacity=1 << 18))
     assert b > 3 * a
+
+
+def test_level1_key_form_choice(zha):
+    """Key-form level-1 scoring only where the b keys plus R x b weights take fewer bytes
+    than the R planes (bf16 keys, b a power of two up to 16)."""
+    assert zha.zha_level1_key_form(good(zha, block=4, num_ref=16, dtype=zha.ZHA_BF16)) == 1
+    assert zha.zha_level1_key_form(good(zha, block=8, num_ref=1, dtype=zha.ZHA_BF16)) == 0
+    assert zha.zha_level1_key_form(good(zha, block=256, num_ref=16, dtype=zha.ZHA_BF16)) == 0
+    assert zha.zha_level1_key_form(good(zha, block=4, num_ref=16, dtype=zha.ZHA_F32)) == 0
+    assert zha.zha_level1_key_form(good(zha, block=6, num_ref=16, dtype=zha.ZHA_BF16)) == 0
+    assert zha.zha_level1_key_form(good(zha, block=0)) == -1
+    # the token weights take extra workspace
+    ws_key = zha.zha_workspace_bytes(good(zha, block=4, num_ref=16, dtype=zha.ZHA_BF16))
+    ws_f32 = zha.zha_workspace_bytes(good(zha, block=4, num_ref=16, dtype=zha.ZHA_F32))
+    assert ws_key > ws_f32
 
 
 def test_call_order_and_arguments(zha):
