@@ -213,7 +213,7 @@ def main():
     app_ms, app_n = zha.zha_profile_stop(h)
     # rank the launches of one extra (untimed, append-free) decode; one bracket per decode
     # keeps each launch's timing undisturbed by the other brackets
-    keys = ["route_prep", "attend", "route_score.top", "route_select.top"] + [
+    keys = ["route_prep", "attend", "route_score.top", "route_select.top", "route_expand.top"] + [
         f"route_{k}.l{l}" for l in range(1, w.levels + 1) for k in ("score", "select", "expand")]
     probe_ms = {}
     snap = tree.n_tokens

@@ -15,6 +15,8 @@ constexpr int CAND_PAIRWISE = 256;  // boundary ties resolved pairwise in LDS up
 constexpr int EXPAND_CHUNK = 1024;  // union-list entries per expand workgroup
 constexpr int MAX_SPLITS = 512;     // attention splits per KV head
 constexpr int SEL_P = 64;           // top-p histogram / classify workgroups per KV head (max)
+constexpr int TD_MAX = 33792;       // nodes of a level selected top-down (32768 + room for appends)
+constexpr int TD_WORDS = TD_MAX / 32;
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
@@ -36,22 +38,31 @@ __device__ __forceinline__ float key2f(uint32_t k) {
 }
 
 // Top-p binning of one score relative to the head's max: everything that decides a node's
-// fate goes through these two functions so every kernel takes the same decision.
+// fate goes through these functions so every kernel takes the same decision.
+struct BinSub { uint32_t bin, sub; };
+__device__ __forceinline__ BinSub bin_of(float score, float maxs) {
+  BinSub r;
+  const float delta = maxs - score;                 // >= 0
+  const float u = delta * BINS_PER_UNIT;
+  r.bin = u < (float)(NB1 - 1) ? (uint32_t)u : (uint32_t)(NB1 - 1);
+  const float frac = u - (float)r.bin;              // in [0, 1) unless clamped
+  r.sub = 0;
+  if (r.bin < (uint32_t)(NB1 - 1)) {
+    const float f = frac * (float)NB2;
+    r.sub = f < (float)(NB2 - 1) ? (uint32_t)f : (uint32_t)(NB2 - 1);
+  }
+  return r;
+}
+__device__ __forceinline__ uint64_t mass_of(float score, float maxs) {
+  return (uint64_t)(expf(-(maxs - score)) * MASS_SCALE);   // in (0, 2^40]
+}
 struct BinMass { uint32_t bin, sub; uint64_t mass; };
 __device__ __forceinline__ BinMass bin_mass(float score, float maxs) {
+  const BinSub bs = bin_of(score, maxs);
   BinMass r;
-  float delta = maxs - score;                       // >= 0
-  float u = delta * BINS_PER_UNIT;
-  uint32_t bin = u < (float)(NB1 - 1) ? (uint32_t)u : (uint32_t)(NB1 - 1);
-  float frac = u - (float)bin;                      // in [0, 1) unless clamped
-  uint32_t sub = 0;
-  if (bin < (uint32_t)(NB1 - 1)) {
-    float f = frac * (float)NB2;
-    sub = f < (float)(NB2 - 1) ? (uint32_t)f : (uint32_t)(NB2 - 1);
-  }
-  r.bin = bin;
-  r.sub = sub;
-  r.mass = (uint64_t)(expf(-delta) * MASS_SCALE);   // in (0, 2^40]
+  r.bin = bs.bin;
+  r.sub = bs.sub;
+  r.mass = mass_of(score, maxs);
   return r;
 }
 
@@ -89,6 +100,7 @@ struct Dev {
   int32_t* cnt;             // [MAXL + 1][Hkv]
   QState* qs;               // [MAXL + 1][Hq]
   uint64_t* hpart;          // [Hkv][SEL_P][GMAX][NB1] per-workgroup coarse mass histograms
+  uint32_t* tdbits;         // [MAXL + 1][Hq][2][TD_WORDS] top-down frontier / kept bitmaps
   int32_t* cand;            // [Hq][ncap[1]]
   float* qf;                // [Hq][D] sigma * q in fp32
   float* apart;             // [Hq][MAX_SPLITS][D + 2] attention partials (m, l, o)

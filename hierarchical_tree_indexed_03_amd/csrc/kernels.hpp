@@ -78,14 +78,13 @@ hipError_t launch_append(const AppendArgs& a, bool bf16, int D, int R, int hkv, 
 // Routing: prep (q to fp32, state reset, top frontier) then per level the step sequence.
 hipError_t launch_route_prep(const RouteArgs& a, bool bf16, int D, hipStream_t st);
 hipError_t launch_route_score(const RouteArgs& a, int D, int R, hipStream_t st);
-hipError_t launch_route_select(const RouteArgs& a, hipStream_t st);   // hist, select, classify, resolve
+hipError_t launch_route_select(const RouteArgs& a, hipStream_t st);   // hist, bound, classify, resolve
 hipError_t launch_route_expand(const RouteArgs& a, hipStream_t st);
-// Top levels with at most MLS_MAX nodes: score every node of levels `level`..`dense_lo`
-// in one launch, then select all of them top-down in one launch (one workgroup per KV
-// head), emitting the frontier of level `dense_lo - 1` (or the gather list).
-constexpr int MLS_MAX = 2112;   // 2048 + room for the nodes appends add
+// Top levels with at most TD_MAX nodes: score every node of levels `level`..`dense_lo` in
+// one launch, then select all of them top-down (one workgroup per query head) and write
+// their dense union lists; the list expansion of level `dense_lo` follows.
 hipError_t launch_route_dense_score(const RouteArgs& a, int D, int R, hipStream_t st);
-hipError_t launch_route_mls(const RouteArgs& a, hipStream_t st);
+hipError_t launch_route_topdown(const RouteArgs& a, hipStream_t st);
 
 hipError_t launch_attend(const AttnArgs& a, bool bf16, int D, bool dense, hipStream_t st);
 // Same, and copies the per-level union sizes into `stats` ([levels + 1][Hkv], nullable).

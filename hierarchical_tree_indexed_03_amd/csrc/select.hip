@@ -208,9 +208,9 @@ __global__ __launch_bounds__(SEL_THREADS) void route_classify_kernel(RouteArgs a
           if (B1[gi] >= (uint32_t)NB1) {
             kb |= 1u << gi;
           } else {
-            const BinMass bm = bin_mass(v[u][gi], Ms[gi]);
-            if (bm.bin < B1[gi]) kb |= 1u << gi;
-            else cand = bm.bin == B1[gi];
+            const uint32_t bin = bin_of(v[u][gi], Ms[gi]).bin;
+            if (bin < B1[gi]) kb |= 1u << gi;
+            else cand = bin == B1[gi];
           }
         }
         const uint64_t ball = __ballot(cand);
@@ -294,12 +294,12 @@ __global__ __launch_bounds__(256) void route_resolve_kernel(RouteArgs a) {
   for (uint32_t i = threadIdx.x; i < ncand; i += 256) {
     const int32_t e = cand[i];
     const float s = sc[e];
-    BinMass bm = bin_mass(s, M);
-    if (bm.sub < b2) {
+    const uint32_t sub = bin_of(s, M).sub;
+    if (sub < b2) {
       atomicOr(&keep[e], bit);
-    } else if (bm.sub == b2) {
+    } else if (sub == b2) {
       const uint32_t k = atomicAdd(&ntie, 1u);
-      if (k < (uint32_t)CAND_PAIRWISE) { tie_e[k] = e; tie_s[k] = s; tie_m[k] = bm.mass; }
+      if (k < (uint32_t)CAND_PAIRWISE) { tie_e[k] = e; tie_s[k] = s; tie_m[k] = mass_of(s, M); }
     }
   }
   __syncthreads();
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(256) void route_resolve_kernel(RouteArgs a) {
 // ------------------------------------------------------------------ launchers
 hipError_t launch_route_select(const RouteArgs& a, hipStream_t st) {
   RouteArgs b = a;
-  b.sel_p = (int32_t)grid_for(a.nlevel, 4096, SEL_P);
+  b.sel_p = (int32_t)grid_for(a.nlevel, 1024, SEL_P);
   hipLaunchKernelGGL(route_hist_kernel, dim3((unsigned)b.sel_p, (unsigned)a.hkv), dim3(SEL_THREADS), 0, st, b);
   hipLaunchKernelGGL(route_bound_kernel, dim3((unsigned)a.hq), dim3(NB1), 0, st, b);
   hipLaunchKernelGGL(route_classify_kernel, dim3((unsigned)b.sel_p, (unsigned)a.hkv), dim3(SEL_THREADS), 0, st, b);

@@ -124,7 +124,8 @@ size_t layout(const zha_config& c, char* base, Dev* dev) {
   memset(&d, 0, sizeof d);
   const int64_t H = c.num_kv_heads, Q = c.num_q_heads, R = c.num_ref, D = c.head_dim;
   const int L = c.levels;
-  for (int l = 1; l <= L; ++l) d.ncap[l] = nodes_at(c, l, c.capacity);
+  // per-level strides rounded to 64 nodes: every per-head row starts 256-byte aligned
+  for (int l = 1; l <= L; ++l) d.ncap[l] = ceil_div(nodes_at(c, l, c.capacity), 64) * 64;
   d.ncap[0] = d.ncap[1];
   for (int l = 1; l <= L; ++l) {
     d.s[l] = (float*)take((size_t)(H * d.ncap[l] * R * D) * 4);
@@ -144,6 +145,7 @@ size_t layout(const zha_config& c, char* base, Dev* dev) {
   d.cnt = (int32_t*)take((size_t)((MAXL + 1) * H) * 4);
   d.qs = (QState*)take((size_t)((L + 1) * Q) * sizeof(QState));
   d.hpart = (uint64_t*)take((size_t)(H * SEL_P * GMAX * NB1) * 8);
+  d.tdbits = (uint32_t*)take((size_t)((L + 1) * Q * 2 * TD_WORDS) * 4);
   d.cand = (int32_t*)take((size_t)(Q * d.ncap[1]) * 4);
   d.qf = (float*)take((size_t)(Q * D) * 4);
   d.apart = (float*)take((size_t)(Q * MAX_SPLITS * (D + 2)) * 4);
@@ -354,9 +356,9 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
     e = launch_route_prep(r, c.dtype == ZHA_BF16, c.head_dim, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "route prep launch");
-  // top levels small enough for the one-launch multi-level selection
+  // top levels small enough to score whole and select top-down in one launch
   int lo = c.levels + 1;
-  while (lo > 1 && r.nl[lo - 1] <= MLS_MAX) --lo;
+  while (lo > 1 && r.nl[lo - 1] <= TD_MAX) --lo;
   if (r.key_form && lo == 1) lo = 2;   // key-form level 1 is scored by its own kernel
   if (lo <= c.levels) {
     r.level = c.levels;
@@ -369,10 +371,18 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
     if (e != hipSuccess) return hip_fail(e, "route dense score launch");
     {
       ProfScope ps(t, "route_select.top", stream);
-      e = launch_route_mls(r, stream);
+      e = launch_route_topdown(r, stream);
     }
-    if (e != hipSuccess) return hip_fail(e, "route multi-level select launch");
+    if (e != hipSuccess) return hip_fail(e, "route top-down select launch");
     r.dense = 0;
+    r.level = lo;
+    r.nlevel = r.nl[lo];
+    r.nbelow = lo > 1 ? r.nl[lo - 1] : 0;
+    {
+      ProfScope ps(t, "route_expand.top", stream);
+      e = launch_route_expand(r, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "route expand launch");
   }
   for (int lv = lo - 1; lv >= 1; --lv) {
     zha_status s = route_levels(t, r, lv, stream, true);
