@@ -64,9 +64,9 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
   // (TD_NONE outside the frontier)
   __shared__ __align__(16) uint32_t Cv[TD_MAX];
   __shared__ uint32_t kb2[2][TD_WORDS];        // kept bitmaps: level above / this level
-  __shared__ unsigned long long h[NB1];        // coarse, then fine, mass histogram
-  __shared__ unsigned long long dh[256];       // radix digits
+  __shared__ unsigned long long h[NB1];        // coarse, then fine mass histogram, then radix digits
   __shared__ int32_t cand[TD_CAND];
+  __shared__ float cand_s[TD_CAND];
   __shared__ int32_t tie_e[TD_TIES];
   __shared__ float tie_s[TD_TIES];
   __shared__ uint64_t tie_m[TD_TIES];
@@ -106,11 +106,16 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
         const int i = i00 + u * TD_THREADS;
         if (i >= n4) break;
         float x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        bool in4 = true;   // b a power of two >= 4: the four nodes share one parent
+        if (!top && lb >= 2) {
+          const int pn = (4 * i) >> lb;
+          in4 = (kp[pn >> 5] >> (pn & 31)) & 1u;
+        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int e = 4 * i + k;
-          bool in = e < n;
-          if (in && !top) {
+          bool in = in4 && e < n;
+          if (in && !top && lb < 2) {
             const int pn = lb >= 0 ? (e >> lb) : e / b;
             in = (kp[pn >> 5] >> (pn & 31)) & 1u;
           }
@@ -162,18 +167,30 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
     __syncthreads();
     const uint32_t b1 = s_b1;
     const uint64_t T = s_T;
-    // ---- frontier and kept words (64 nodes per wave step); boundary-bin nodes listed
-    for (int e0 = wave * 64; e0 < n; e0 += TD_THREADS) {
-      const int e = e0 + lane;
-      const uint32_t code = e < n ? Cv[e] : TD_NONE;
-      const bool in = code != TD_NONE;
-      const uint64_t fw = __ballot(in);
-      const uint64_t kw = __ballot(in && code < b1);
-      if (lane == 0) { gbits[e0 >> 5] = (uint32_t)fw; kc[e0 >> 5] = (uint32_t)kw; }
-      if (lane == 0 && (e0 >> 5) + 1 < nw) { gbits[(e0 >> 5) + 1] = (uint32_t)(fw >> 32); kc[(e0 >> 5) + 1] = (uint32_t)(kw >> 32); }
-      if (in && code == b1) {
-        const uint32_t k = atomicAdd(&s_ncand, 1u);
-        if (k < (uint32_t)TD_CAND) cand[k] = e;
+    // ---- frontier and kept words, one 32-node word per thread (read in a rotated order so
+    // the lanes of a wave hit distinct LDS banks); boundary-bin nodes listed
+    for (int w = tid; w < nw; w += TD_THREADS) {
+      uint32_t c[32];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {   // all 32 loads issued before any is used
+        const int e = 32 * w + ((k + lane) & 31);
+        c[k] = e < n ? Cv[e] : TD_NONE;
+      }
+      uint32_t fw = 0u, kw = 0u, cw = 0u;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const uint32_t bit = 1u << ((k + lane) & 31);
+        if (c[k] != TD_NONE) fw |= bit;
+        if (c[k] < b1) kw |= bit;
+        if (c[k] == b1) cw |= bit;
+      }
+      gbits[w] = fw;
+      kc[w] = kw;
+      while (cw) {   // boundary-bin nodes of this word
+        const int idx = __ffs(cw) - 1;
+        cw &= cw - 1u;
+        const uint32_t j = atomicAdd(&s_ncand, 1u);
+        if (j < (uint32_t)TD_CAND) cand[j] = 32 * w + idx;
       }
     }
     for (int i = tid; i < NB2; i += TD_THREADS) h[i] = 0ull;
@@ -182,16 +199,19 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
       // ---- the boundary bin: its nodes' scores again (global, recently written), fine bins
       const uint32_t nc = s_ncand;
       const bool listed = nc <= (uint32_t)TD_CAND;
+      // f(node, score) for every node of the boundary bin
       auto for_each_cand = [&](auto&& f) {
         if (listed) {
-          for (uint32_t i = tid; i < nc; i += TD_THREADS) f(cand[i]);
+          for (uint32_t i = tid; i < nc; i += TD_THREADS) f(cand[i], cand_s[i]);
         } else {
           for (int e = tid; e < n; e += TD_THREADS)
-            if (Cv[e] == b1) f(e);
+            if (Cv[e] == b1) f(e, S[e]);
         }
       };
-      for_each_cand([&](int e) {
-        const float x = S[e];
+      if (listed)
+        for (uint32_t i = tid; i < nc; i += TD_THREADS) cand_s[i] = S[cand[i]];
+      __syncthreads();
+      for_each_cand([&](int e, float x) {
         atomicAdd(&h[bin_of(x, M).sub], (unsigned long long)mass_of(x, M));
       });
       __syncthreads();
@@ -206,8 +226,7 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
       __syncthreads();
       const uint32_t b2 = s_b2;
       const uint64_t above2 = s_above2;
-      for_each_cand([&](int e) {
-        const float x = S[e];
+      for_each_cand([&](int e, float x) {
         const uint32_t sub = bin_of(x, M).sub;
         if (sub < b2) {
           atomicOr(&kc[e >> 5], 1u << (e & 31));
@@ -228,6 +247,7 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
         }
       } else {
         // radix select on the 64-bit rank key of the boundary sub-bin's nodes, 8 bits a pass
+        unsigned long long* dh = h;   // the fine histogram is no longer needed
         if (tid == 0) { s_prefix = 0; s_rabove = above2; }
         __syncthreads();
         for (int pass = 0; pass < 8; ++pass) {
@@ -236,8 +256,7 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
           for (int i = tid; i < 256; i += TD_THREADS) dh[i] = 0ull;
           __syncthreads();
           const uint64_t pf = s_prefix;
-          for_each_cand([&](int e) {
-            const float x = S[e];
+          for_each_cand([&](int e, float x) {
             if (bin_of(x, M).sub != b2) return;
             const uint64_t k = rank_key(x, e);
             if ((k & hi) == (pf & hi)) atomicAdd(&dh[(k >> shift) & 255u], (unsigned long long)mass_of(x, M));
@@ -253,8 +272,7 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
           __syncthreads();
         }
         const uint64_t kb = s_prefix;
-        for_each_cand([&](int e) {
-          const float x = S[e];
+        for_each_cand([&](int e, float x) {
           if (bin_of(x, M).sub == b2 && rank_key(x, e) <= kb) atomicOr(&kc[e >> 5], 1u << (e & 31));
         });
       }
