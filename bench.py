@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--dense-reps", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of timed oracle decode")
+    ap.add_argument("--cold-steps", type=int, default=32,
+                    help="extra steps timed one by one after a 1 GiB scratch write that evicts L2 and MALL")
+    ap.add_argument("--crossover", action="store_true",
+                    help="light-router sweep over N: ZHA vs dense decode, crossover context (own JSON line)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for traffic)")
     return ap.parse_args()
@@ -138,6 +142,112 @@ def cpu_baseline(w, K, V, refs, queries, n0, budget):
                 host_cpus=os.cpu_count())
 
 
+def crossover(args):
+    """ZHA step (append + decode) against dense flash-decode over the light-router sweep;
+    warm (back to back) and cold (after a 1 GiB scratch write) per N.  Crossover = the
+    smallest context where the ZHA step is faster, interpolated log-linearly in N."""
+    import torch
+    from hierarchical_tree_indexed_03_amd import zha
+    dev = torch.device("cuda:0")
+    steps = args.steps if args.steps is not None else 64
+    rows = []
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    for n0 in wc.LIGHT_SIZES:
+        total = args.warmup + steps + args.cold_steps
+        w = wc.light(n0, steps=total)
+        Kd = torch.empty(w.num_kv_heads, w.capacity, w.head_dim, dtype=torch.bfloat16, device=dev)
+        Vd = torch.empty_like(Kd)
+        for stream, hh, lo, hi, r in gen.iter_kv_chunks(w):
+            (Kd if stream == gen.STREAM_K else Vd)[hh, lo:hi] = torch.from_numpy(r).to(torch.bfloat16).to(dev)
+        fetch = lambda kv, idx: Kd[kv, torch.as_tensor(idx, device=dev)].float().cpu().numpy()
+        Qd = torch.from_numpy(np.stack([gen.step_queries(w, s_, n0 + s_ + 1, fetch) for s_ in range(total)])).to(torch.bfloat16).to(dev)
+        Kn = Kd[:, n0:n0 + total].transpose(0, 1).contiguous()
+        Vn = Vd[:, n0:n0 + total].transpose(0, 1).contiguous()
+        cfg = zha.make_config(w.head_dim, w.num_kv_heads, w.num_q_heads, w.block, w.levels, w.num_ref,
+                              w.capacity, w.dtype, w.top_p, w.keep_sink)
+        tree = zha.Tree(cfg)
+        tree.build(Kd, Vd, n0, torch.from_numpy(gen.ref_queries(w)).to(torch.bfloat16).to(dev))
+        out = torch.empty(w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+
+        def step(s_):
+            tree.append(Kn[s_], Vn[s_])
+            tree.decode(Qd[s_], out)
+
+        for s_ in range(args.warmup):
+            step(s_)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s_ in range(args.warmup, args.warmup + steps):
+            step(s_)
+        e1.record()
+        torch.cuda.synchronize()
+        zha_warm = e0.elapsed_time(e1) / steps
+        zc = []
+        for s_ in range(args.warmup + steps, total):
+            scratch.fill_(float(s_))
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            step(s_)
+            c1.record()
+            torch.cuda.synchronize()
+            zc.append(c0.elapsed_time(c1))
+        q_last = Qd[total - 1]
+        for _ in range(3):
+            tree.decode_dense(q_last, out)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.dense_reps):
+            tree.decode_dense(q_last, out)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_warm = e0.elapsed_time(e1) / args.dense_reps
+        dc = []
+        for i in range(min(args.cold_steps, 16)):
+            scratch.fill_(float(i))
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            tree.decode_dense(q_last, out)
+            c1.record()
+            torch.cuda.synchronize()
+            dc.append(c0.elapsed_time(c1))
+        row = {"n_tokens": n0, "levels": w.levels, "zha_ms_warm": round(zha_warm, 4),
+               "dense_ms_warm": round(dense_warm, 4),
+               "zha_ms_cold_median": round(float(np.median(zc)), 4) if zc else None,
+               "dense_ms_cold_median": round(float(np.median(dc)), 4) if dc else None}
+        rows.append(row)
+        log(f"[crossover] N={n0}: ZHA {row['zha_ms_warm']:.3f} ms warm / {row['zha_ms_cold_median']} cold, "
+            f"dense {row['dense_ms_warm']:.3f} ms warm / {row['dense_ms_cold_median']} cold")
+        tree.close()
+        del Kd, Vd, Kn, Vn, Qd
+        torch.cuda.empty_cache()
+
+    def cross(key_z, key_d):
+        ns = np.array([r["n_tokens"] for r in rows], dtype=np.float64)
+        rz = np.array([r[key_z] / r[key_d] if r[key_z] and r[key_d] else np.nan for r in rows])
+        for i, r in enumerate(rz):
+            if r < 1.0:
+                if i == 0:
+                    return {"tokens": None, "note": f"ZHA already faster at the smallest N ({int(ns[0])})"}
+                lr0, lr1 = np.log(rz[i - 1]), np.log(r)
+                t = (0.0 - lr0) / (lr1 - lr0)
+                return {"tokens": round(float(np.exp(np.log(ns[i - 1]) + t * (np.log(ns[i]) - np.log(ns[i - 1]))))),
+                        "between": [int(ns[i - 1]), int(ns[i])]}
+        return {"tokens": None, "note": f"ZHA slower than dense at every N up to {int(ns[-1])}"}
+
+    warm = cross("zha_ms_warm", "dense_ms_warm")
+    cold = cross("zha_ms_cold_median", "dense_ms_cold_median")
+    rec = {"metric": "crossover context, ZHA decode step vs dense flash-decode (light router: R=1, b=8, p=0.75)",
+           "value": warm.get("tokens"), "unit": "tokens", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+           "higher_is_better": False, "data": "synthetic", "dtype": "bf16+f32",
+           "config": {"workload": "light_sweep", "sizes": list(wc.LIGHT_SIZES), "kv_heads": 4, "q_heads": 32,
+                      "head_dim": 128, "step": "append + decode"},
+           "crossover_warm": warm, "crossover_cold": cold, "per_n": rows,
+           "modeled_reference": {"source": "the pages' H100 BF16 roofline model (modeled, not measured)",
+                                 "crossover_tokens": 48000}}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -149,9 +259,11 @@ def main():
     import torch
     from hierarchical_tree_indexed_03_amd import zha
 
+    if args.crossover:
+        return crossover(args)
     base = wc.NAMED[args.workload]
     steps = args.steps if args.steps is not None else (base.steps or 64)
-    total = args.warmup + steps
+    total = args.warmup + steps + args.cold_steps
     w = base.with_(steps=total)
     n0 = w.n_tokens
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -197,7 +309,8 @@ def main():
     build_tok_s = n0 / build_s
     build_bytes = n0 * w.num_kv_heads * (w.head_dim * (2 if w.dtype == "bf16" else 4) +
                                         sum(w.num_ref * (w.head_dim + 1) * 4 / w.block ** l
-                                            for l in range(1, w.levels + 1)))
+                                            for l in range(1, w.levels + 1)) +
+                                        (w.num_ref * 4 if zha.zha_level1_key_form(cfg) == 1 else 0))
     log(f"[bench] build {build_s * 1e3:.3f} ms -> {build_tok_s / 1e9:.3f} G tok/s")
 
     def step(s):
@@ -235,7 +348,7 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
-    for s in range(args.warmup, total):
+    for s in range(args.warmup, args.warmup + steps):
         step(s)
     ev1.record()
     torch.cuda.synchronize()
@@ -245,7 +358,7 @@ def main():
     ms_per_step = wall * 1e3 / steps
     qps = steps / wall
     st = stats.cpu().numpy()
-    timed_stats = st[args.warmup:]
+    timed_stats = st[args.warmup:args.warmup + steps]
     key_form = zha.zha_level1_key_form(cfg) == 1
     dom_bytes = [kernel_bytes(dominant, w, timed_stats[i], n0 + args.warmup + i + 1, key_form) for i in range(steps)]
     dom_avg_ms = dom_ms / max(dom_n, 1)
@@ -260,6 +373,25 @@ def main():
     log(f"[bench] timed {steps} steps: {ms_per_step:.3f} ms/step (events {gpu_ms / steps:.3f}), "
         f"{qps:.1f} queries/s; dominant {dominant} {dom_avg_ms:.4f} ms/launch")
 
+    # ---- cold steps: each after a 1 GiB scratch write (outside its timing) evicts L2 and MALL
+    cold = None
+    if args.cold_steps > 0:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cold_ms = []
+        for s_ in range(args.warmup + steps, total):
+            scratch.fill_(float(s_))
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            step(s_)
+            c1.record()
+            torch.cuda.synchronize()
+            cold_ms.append(c0.elapsed_time(c1))
+        del scratch
+        cm = np.array(cold_ms)
+        cold = {"steps": len(cm), "median_ms": round(float(np.median(cm)), 4), "p90_ms": round(float(np.percentile(cm, 90)), 4),
+                "queries_per_s_median": round(1e3 / float(np.median(cm)), 2)}
+        log(f"[bench] cold steps: median {cold['median_ms']:.3f} ms, p90 {cold['p90_ms']:.3f} ms")
+
     # ---- decode-step bytes (router planes + gathered KV), from the routing stats
     R, d, g, L = w.num_ref, w.head_dim, w.group, w.levels
     per_level = np.array([node_bytes(w, L - row, key_form) for row in range(L)], dtype=np.float64)
@@ -268,7 +400,7 @@ def main():
     step_bytes = float(np.mean(router_b + gather_b))
 
     # ---- dense flash-decode over the same cache (baseline)
-    q_last = Qd[total - 1]
+    q_last = Qd[args.warmup + steps - 1]
     for _ in range(3):
         tree.decode_dense(q_last, out)
     torch.cuda.synchronize()
@@ -338,6 +470,7 @@ def main():
                    "batch": 1, "layers": 1, "step": "append + decode"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cold": cold,
         "decode_step": {"level1_key_form": key_form, "alg_bytes": round(step_bytes), "achieved_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                         "router_bytes": round(float(np.mean(router_b))), "gather_bytes": round(float(np.mean(gather_b))),
                         "frontier_union_per_level": timed_stats[:, :L, :].sum(axis=2).mean(axis=0).round(1).tolist(),

@@ -100,6 +100,8 @@ __global__ __launch_bounds__(256) void build_tile_kernel(BuildArgs a) {
   const int kv = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * T;
   const int nt = (int)min((int64_t)T, a.N - t0);
+  // a new tree: the append's cached sibling aggregates no longer hold
+  if (blockIdx.x == 0 && threadIdx.x <= MAXL) a.dev.sibkey[(int64_t)kv * (MAXL + 1) + threadIdx.x] = -1;
   const TIn* Kg = (const TIn*)a.K + ((int64_t)kv * a.cap + t0) * D;
   const TIn* Rg = (const TIn*)a.refs + (int64_t)kv * R * D;
 
@@ -286,77 +288,192 @@ __global__ __launch_bounds__(256) void build_parent_kernel(ParentArgs a) {
   parent_nodes<D, R>(a.dev, a.level, kv, a.b, p0, np, a.nchild, Lp, Wp);
 }
 
+// b^e saturated at 2^62 (spans above every token count)
+__device__ __forceinline__ int64_t ipow64(int64_t b, int e) {
+  int64_t r = 1;
+  for (int i = 0; i < e; ++i) {
+    if (r > ((int64_t)1 << 62) / b) return (int64_t)1 << 62;
+    r *= b;
+  }
+  return r;
+}
+
 // Append one token per KV head and refresh the rightmost node of every level.
+//
+// The new token only changes the rightmost node of each level.  Level 1 is updated in place:
+// with z_j = r_j.k_new / sqrt(d), LSE' = logaddexp(LSE, z_j), the old softmax weights scale
+// by exp(LSE - LSE') and the new key enters with weight exp(z_j - LSE'), so s_j, A_j and the
+// stored token weights follow with no pass over the block's keys.  A parent is the
+// logsumexp / softmax-weighted mean over its children: its complete children (all but the
+// rightmost) are folded into one aggregate (LSE, A, s), kept in the workspace and rebuilt
+// only when that set of children changes (once every b^(v-1) tokens at level v); the
+// rightmost child is the node just refreshed one level down.  With the aggregates loaded,
+// each thread carries its own (plane, dim) elements up through every level with no barrier.
+// One workgroup per KV head.
 template <typename TIn, int D, int R>
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  constexpr int NT = 256;
-  __shared__ float Zs[256 * R];
-  __shared__ float Lj[R];
-  __shared__ float Lp[R];
-  __shared__ float Wp[256 * R];
-  const int kv = blockIdx.x;
-  const int64_t n = a.N;  // index of the new token
+__global__ __launch_bounds__(1024) void append_kernel(AppendArgs a) {
+  constexpr int NT = 1024;
+  constexpr int NW = NT / 64;
+  constexpr int RD = R * D;
+  constexpr int RS = SIB_LEVEL(R, D);         // aggregate per level: [j][LSE, A, s(D)], padded
+  __shared__ __align__(16) float Agg[(MAXL - 1) * RS];
+  __shared__ float zl[R], Lo[R], Ao[R];     // new-token logits; old level-1 LSE and A
+  __shared__ int64_t keyl[MAXL];              // per level v (index v-2): first child * 256 + count
+  __shared__ int64_t pvl[MAXL];               // per level v (index v-2): the refreshed node
+  __shared__ float Cf[MAXL][R][2];            // per level (index v-1), plane: weights of old, new
+  __shared__ int stale[MAXL];
+  const int kv = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t n = a.N;        // index of the new token
+  const int b = a.b, L = a.levels;
   TIn* Kc = (TIn*)a.K + (int64_t)kv * a.cap * D;
   TIn* Vc = (TIn*)a.V + (int64_t)kv * a.cap * D;
   const TIn* kn = (const TIn*)a.k_new + (int64_t)kv * D;
   const TIn* vn = (const TIn*)a.v_new + (int64_t)kv * D;
-  for (int i = threadIdx.x; i < D; i += NT) {
+  for (int i = tid; i < D; i += NT) {
     Kc[n * D + i] = kn[i];
     Vc[n * D + i] = vn[i];
   }
-  // level 1: block n1 holds tokens [n1*b, n] after the append
-  const int64_t n1 = n / a.b;
-  const int64_t tb = n1 * a.b;
-  const int nt = (int)(n - tb + 1);
+  const int64_t n1 = n / b;
+  const int k1 = (int)(n - n1 * b);           // position of the new token in its block
+  const int64_t g1 = (int64_t)kv * a.dev.ncap[1] + n1;
+  float* sib = a.dev.sib + (int64_t)kv * SIB_STRIDE(R, D);
+  int64_t* sibkey = a.dev.sibkey + (int64_t)kv * (MAXL + 1);
+  // cached aggregates of every level, and whether their set of children still holds
+  if (tid < L - 1) {
+    const int v = tid + 2;
+    const int64_t last = n / ipow64(b, v - 1), pv = n / ipow64(b, v), c0 = pv * b;
+    const int64_t key = c0 * 256 + (last - c0);
+    keyl[tid] = key;
+    pvl[tid] = pv;
+    stale[tid] = sibkey[v] != key;
+  }
+  {   // levels 2..L, float4 loads all issued together
+    constexpr int U = 8;
+    const int tot4 = (L - 1) * RS / 4;
+    const float4* src = (const float4*)(sib + 2 * RS);
+    for (int i0 = tid; i0 < tot4; i0 += NT * U) {
+      float4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = i0 + u * NT < tot4 ? src[i0 + u * NT] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (i0 + u * NT < tot4) ((float4*)Agg)[i0 + u * NT] = v[u];
+    }
+  }
+  // the old level-1 s of this thread's elements
+  constexpr int IT = (RD + NT - 1) / NT;
+  float sold[IT];
+#pragma unroll
+  for (int u = 0; u < IT; ++u) {
+    const int i = tid + u * NT;
+    sold[u] = (i < RD && k1) ? a.dev.s[1][g1 * RD + i] : 0.f;
+  }
+  if (tid < R) {
+    const float lo = k1 ? a.dev.lse[1][g1 * R + tid] : -INFINITY;
+    Lo[tid] = lo;
+    Ao[tid] = k1 ? lo - a.dev.c[1][g1 * R + tid] : 0.f;
+  }
+  // z_j = sigma r_j . k_new, one wave per reference query
   const TIn* Rg = (const TIn*)a.refs + (int64_t)kv * R * D;
-  for (int idx = threadIdx.x; idx < nt * R; idx += NT) {
-    const int t = idx / R, j = idx % R;
-    const TIn* kr = (tb + t == n) ? kn : Kc + (tb + t) * D;
-    float dot = 0.f;
-    for (int i = 0; i < D; ++i) dot += to_f32(kr[i]) * to_f32(Rg[j * D + i]);
-    Zs[idx] = a.sigma * dot;
+  for (int j = wave; j < R; j += NW) {
+    float part = 0.f;
+    for (int i = lane; i < D; i += 64) part += to_f32(Rg[j * D + i]) * to_f32(kn[i]);
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    if (lane == 0) zl[j] = a.sigma * part;
   }
   __syncthreads();
-  const int64_t cap1 = a.dev.ncap[1];
-  if (threadIdx.x < R) {
-    const int j = threadIdx.x;
-    float mx = -INFINITY, sum = 0.f, A = 0.f;
-    for (int t = 0; t < nt; ++t) mx = fmaxf(mx, Zs[t * R + j]);
-    for (int t = 0; t < nt; ++t) sum += expf(Zs[t * R + j] - mx);
-    const float lse = mx + logf(sum);
-    for (int t = 0; t < nt; ++t) A += expf(Zs[t * R + j] - lse) * Zs[t * R + j];
-    Lj[j] = lse;
-    const int64_t gi = ((int64_t)kv * cap1 + n1) * R + j;
-    a.dev.c[1][gi] = lse - A;
-    a.dev.lse[1][gi] = lse;
-  }
-  __syncthreads();
-  if (a.dev.w1) {
-    for (int idx = threadIdx.x; idx < R * a.b; idx += NT) {
-      const int j = idx / a.b, k = idx % a.b;
-      a.dev.w1[((int64_t)kv * cap1 + n1) * R * a.b + idx] = k < nt ? expf(Zs[k * R + j] - Lj[j]) : 0.f;
+  // rebuild the aggregates whose set of children changed (all threads, one level at a time)
+  for (int vi = 0; vi < L - 1; ++vi) {
+    if (!stale[vi]) continue;     // block-uniform
+    const int v = vi + 2;
+    const int64_t c0 = keyl[vi] >> 8;
+    const int nsib = (int)(keyl[vi] & 255);
+    const int64_t ccap = a.dev.ncap[v - 1];
+    const float* lse_c = a.dev.lse[v - 1] + ((int64_t)kv * ccap + c0) * R;
+    const float* c_c = a.dev.c[v - 1] + ((int64_t)kv * ccap + c0) * R;
+    const float* s_c = a.dev.s[v - 1] + ((int64_t)kv * ccap + c0) * RD;
+    float* ag = Agg + vi * RS;
+    for (int i = tid; i < R * (D + 2); i += NT) {
+      const int j = i / (D + 2), k = i % (D + 2);
+      float m = -INFINITY;
+      for (int c = 0; c < nsib; ++c) m = fmaxf(m, lse_c[c * R + j]);
+      float sum = 0.f, acc = 0.f;
+      for (int c = 0; c < nsib; ++c) {
+        const float lc = lse_c[c * R + j];
+        const float e = expf(lc - m);
+        sum += e;
+        acc += e * (k == 0 ? 0.f : k == 1 ? lc - c_c[c * R + j] : s_c[(int64_t)c * RD + j * D + k - 2]);
+      }
+      const float val = nsib == 0 ? (k == 0 ? -INFINITY : 0.f) : (k == 0 ? m + logf(sum) : acc / sum);
+      ag[i] = val;
+      sib[(int64_t)v * RS + i] = val;
     }
-  }
-  for (int it = threadIdx.x; it < R * (D / 4); it += NT) {
-    const int j = it / (D / 4), dc = it % (D / 4);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int t = 0; t < nt; ++t) {
-      const TIn* kr = (tb + t == n) ? kn : Kc + (tb + t) * D;
-      const float w = expf(Zs[t * R + j] - Lj[j]);
-      const float4 k4 = ld4_f32(kr + dc * 4);
-      acc.x += w * k4.x; acc.y += w * k4.y; acc.z += w * k4.z; acc.w += w * k4.w;
-    }
-    *(float4*)(a.dev.s[1] + (((int64_t)kv * cap1 + n1) * R + j) * D + dc * 4) = acc;
-  }
-  // levels 2..L: one parent each
-  int64_t span = a.b;
-  for (int v = 2; v <= a.levels; ++v) {
-    __threadfence();
     __syncthreads();
-    const int64_t nchild = (n + 1 + span - 1) / span;   // nodes at level v-1 after the append
-    span *= a.b;
-    const int64_t pv = n / span;
-    parent_nodes<D, R>(a.dev, v, kv, a.b, pv, 1, nchild, Lp, Wp);
+    if (tid == 0) sibkey[v] = keyl[vi];
+  }
+  // ---- per plane j, the chain of merges from level 1 to the top (one thread per plane):
+  // LSE and A of every refreshed node, and the weights (old, new) each level applies to s
+  if (tid < R) {
+    const int j = tid;
+    const float z = zl[j];
+    float lse, A, al, be;
+    if (k1 == 0) {
+      lse = z; A = z; al = 0.f; be = 1.f;
+    } else {
+      const float lo = Lo[j];
+      const float m = fmaxf(lo, z);
+      lse = m + logf(expf(lo - m) + expf(z - m));
+      al = expf(lo - lse);
+      be = expf(z - lse);
+      A = al * Ao[j] + be * z;
+    }
+    Cf[0][j][0] = al; Cf[0][j][1] = be;
+    a.dev.lse[1][g1 * R + j] = lse;
+    a.dev.c[1][g1 * R + j] = lse - A;
+    for (int v = 2; v <= L; ++v) {
+      const float* ag = Agg + (v - 2) * RS + j * (D + 2);
+      const float ls = ag[0];
+      float wa = 0.f, wb = 1.f;
+      if (ls != -INFINITY) {
+        const float m = fmaxf(ls, lse);
+        const float lp = m + logf(expf(ls - m) + expf(lse - m));
+        wa = expf(ls - lp);
+        wb = expf(lse - lp);
+        A = wa * ag[1] + wb * A;
+        lse = lp;
+      }
+      Cf[v - 1][j][0] = wa; Cf[v - 1][j][1] = wb;
+      const int64_t gp = (int64_t)kv * a.dev.ncap[v] + pvl[v - 2];
+      a.dev.lse[v][gp * R + j] = lse;
+      a.dev.c[v][gp * R + j] = lse - A;
+    }
+  }
+  __syncthreads();
+  // ---- s of every refreshed node: each thread carries its (plane j, dim d) elements up
+#pragma unroll
+  for (int u = 0; u < IT; ++u) {
+    const int i = tid + u * NT;
+    if (i >= RD) break;
+    const int j = i / D, d = i % D;
+    const float kd = to_f32(kn[d]);
+    float sv = Cf[0][j][0] * sold[u] + Cf[0][j][1] * kd;
+    a.dev.s[1][g1 * RD + i] = sv;
+    for (int v = 2; v <= L; ++v) {
+      sv = Cf[v - 1][j][0] * Agg[(v - 2) * RS + j * (D + 2) + 2 + d] + Cf[v - 1][j][1] * sv;
+      a.dev.s[v][((int64_t)kv * a.dev.ncap[v] + pvl[v - 2]) * RD + i] = sv;
+    }
+  }
+  // token weights of the level-1 planes (key-form scoring): old weights scale by
+  // exp(LSE - LSE'), the new token's weight is exp(z_j - LSE'), later slots stay zero
+  if (a.dev.w1) {
+    float* wg = a.dev.w1 + g1 * R * b;
+    for (int i = tid; i < R * b; i += NT) {
+      const int j = i / b, k = i % b;
+      float w = 0.f;
+      if (k < k1) w = Cf[0][j][0] * wg[i];
+      else if (k == k1) w = Cf[0][j][1];
+      wg[i] = w;
+    }
   }
 }
 
@@ -409,7 +526,7 @@ template <typename TIn>
 static hipError_t launch_append_t(const AppendArgs& a, int D, int R, int hkv, hipStream_t st) {
 #define ZHA_CASE(DD, RR)                                                                   \
   if (D == DD && R == RR) {                                                                \
-    hipLaunchKernelGGL((append_kernel<TIn, DD, RR>), dim3(hkv), dim3(256), 0, st, a);      \
+    hipLaunchKernelGGL((append_kernel<TIn, DD, RR>), dim3(hkv), dim3(1024), 0, st, a);     \
     return hipGetLastError();                                                              \
   }
   ZHA_CASE(64, 1) ZHA_CASE(64, 2) ZHA_CASE(64, 4) ZHA_CASE(64, 8) ZHA_CASE(64, 16)

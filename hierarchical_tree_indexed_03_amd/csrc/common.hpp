@@ -17,6 +17,10 @@ constexpr int MAX_SPLITS = 512;     // attention splits per KV head
 constexpr int SEL_P = 64;           // top-p histogram / classify workgroups per KV head (max)
 constexpr int TD_MAX = 33792;       // nodes of a level selected top-down (32768 + room for appends)
 constexpr int TD_WORDS = TD_MAX / 32;
+// the append's sibling aggregates: per level R x (D + 2) floats rounded to a multiple of 4
+// (16-byte aligned levels), (MAXL + 1) levels per KV head
+#define SIB_LEVEL(R, D) ((((R) * ((D) + 2)) + 3) & ~3)
+#define SIB_STRIDE(R, D) ((int64_t)(MAXL + 1) * SIB_LEVEL(R, D))
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
@@ -101,6 +105,9 @@ struct Dev {
   QState* qs;               // [MAXL + 1][Hq]
   uint64_t* hpart;          // [Hkv][SEL_P][GMAX][NB1] per-workgroup coarse mass histograms
   uint32_t* tdbits;         // [MAXL + 1][Hq][2][TD_WORDS] top-down frontier / kept bitmaps
+  float* sib;               // [Hkv][SIB_STRIDE] = [MAXL + 1][R][D + 2] per level: aggregate (LSE, A, s) of the
+                            // rightmost node's complete children (append)
+  int64_t* sibkey;          // [Hkv][MAXL + 1] first child * 256 + count it was built from; -1 none
   int32_t* cand;            // [Hq][ncap[1]]
   float* qf;                // [Hq][D] sigma * q in fp32
   float* apart;             // [Hq][MAX_SPLITS][D + 2] attention partials (m, l, o)

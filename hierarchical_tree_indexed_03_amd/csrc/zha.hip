@@ -146,6 +146,8 @@ size_t layout(const zha_config& c, char* base, Dev* dev) {
   d.qs = (QState*)take((size_t)((L + 1) * Q) * sizeof(QState));
   d.hpart = (uint64_t*)take((size_t)(H * SEL_P * GMAX * NB1) * 8);
   d.tdbits = (uint32_t*)take((size_t)((L + 1) * Q * 2 * TD_WORDS) * 4);
+  d.sib = (float*)take((size_t)(H * SIB_STRIDE(R, D)) * 4);
+  d.sibkey = (int64_t*)take((size_t)(H * (MAXL + 1)) * 8);
   d.cand = (int32_t*)take((size_t)(Q * d.ncap[1]) * 4);
   d.qf = (float*)take((size_t)(Q * D) * 4);
   d.apart = (float*)take((size_t)(Q * MAX_SPLITS * (D + 2)) * 4);
