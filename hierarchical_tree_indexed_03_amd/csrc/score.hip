@@ -15,15 +15,15 @@
 #include "route_util.hpp"
 #include "qk_tile.hpp"
 
-// Score-kernel tuning: tiles in flight per wave (R >= 8 / R < 8) and max blocks per KV head.
+// Score-kernel tuning: tiles in flight per wave (planes with R >= 8 / R < 8; key form).
 #ifndef ZHA_SCORE_UN_WIDE
 #define ZHA_SCORE_UN_WIDE 2
 #endif
 #ifndef ZHA_SCORE_UN_NARROW
 #define ZHA_SCORE_UN_NARROW 2
 #endif
-#ifndef ZHA_SCORE_GRID
-#define ZHA_SCORE_GRID 1024
+#ifndef ZHA_KEYS_UN
+#define ZHA_KEYS_UN 2
 #endif
 
 namespace zha {
@@ -156,7 +156,7 @@ template <int D, int R, int B>
 __global__ __launch_bounds__(256) void route_score_keys_kernel(RouteArgs a) {
   constexpr int NPT = 16 / B;                 // nodes per 16-token tile
   constexpr int KS = (B + 3) / 4;             // fp32 MFMA steps per node
-  constexpr int UN = 2;                       // tiles in flight per wave
+  constexpr int UN = ZHA_KEYS_UN;             // tiles in flight per wave
   constexpr int NK = Qk<bf16_t, D>::NL;
   __shared__ float Lt[4][16][17];             // per wave: logits [head][token]
   __shared__ float red[4][16];
@@ -265,22 +265,23 @@ hipError_t launch_route_prep(const RouteArgs& a, bool bf16, int D, hipStream_t s
   return hipGetLastError();
 }
 
+// Score grids hold one wave of resident workgroups over the KV heads (the node loop is
+// strided), so no workgroup of a second, partial wave trails the launch.
 template <int D, int R>
 static void launch_score(const RouteArgs& a, hipStream_t st) {
   constexpr int NPB = 4 * (16 / R) * (R >= 8 ? ZHA_SCORE_UN_WIDE : ZHA_SCORE_UN_NARROW);   // nodes per block pass
-  int64_t x = (a.nlevel + NPB - 1) / NPB;
-  if (x > ZHA_SCORE_GRID) x = ZHA_SCORE_GRID;
-  if (x < 1) x = 1;
-  hipLaunchKernelGGL((route_score_kernel<D, R>), dim3((unsigned)x, (unsigned)a.hkv), dim3(256), 0, st, a);
+  static const int per_cu = resident_per_cu(route_score_kernel<D, R>, 256);
+  const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
+  hipLaunchKernelGGL((route_score_kernel<D, R>), dim3(grid_for(a.nlevel, NPB, cap), (unsigned)a.hkv), dim3(256), 0, st, a);
 }
 
 template <int D, int R, int B>
 static void launch_score_keys(const RouteArgs& a, hipStream_t st) {
-  constexpr int NPB = 4 * (16 / B) * 2;   // nodes per block pass
-  int64_t x = (a.nlevel + NPB - 1) / NPB;
-  if (x > ZHA_SCORE_GRID) x = ZHA_SCORE_GRID;
-  if (x < 1) x = 1;
-  hipLaunchKernelGGL((route_score_keys_kernel<D, R, B>), dim3((unsigned)x, (unsigned)a.hkv), dim3(256), 0, st, a);
+  constexpr int NPB = 4 * (16 / B) * ZHA_KEYS_UN;   // nodes per block pass
+  static const int per_cu = resident_per_cu(route_score_keys_kernel<D, R, B>, 256);
+  const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
+  hipLaunchKernelGGL((route_score_keys_kernel<D, R, B>), dim3(grid_for(a.nlevel, NPB, cap), (unsigned)a.hkv), dim3(256),
+                     0, st, a);
 }
 
 hipError_t launch_route_score(const RouteArgs& a, int D, int R, hipStream_t st) {
@@ -309,11 +310,10 @@ static void launch_dense_score_t(const RouteArgs& a, int nlev, hipStream_t st) {
   constexpr int NPB = 4 * (16 / R) * (R >= 8 ? ZHA_SCORE_UN_WIDE : ZHA_SCORE_UN_NARROW);
   int64_t mx = 0;
   for (int l = a.dense_lo; l <= a.level; ++l) mx = a.nl[l] > mx ? a.nl[l] : mx;
-  int64_t x = (mx + NPB - 1) / NPB;
-  if (x > ZHA_SCORE_GRID) x = ZHA_SCORE_GRID;
-  if (x < 1) x = 1;
-  hipLaunchKernelGGL((route_score_kernel<D, R>), dim3((unsigned)x, (unsigned)a.hkv, (unsigned)nlev), dim3(256), 0,
-                     st, a);
+  static const int per_cu = resident_per_cu(route_score_kernel<D, R>, 256);
+  const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
+  hipLaunchKernelGGL((route_score_kernel<D, R>), dim3(grid_for(mx, NPB, cap), (unsigned)a.hkv, (unsigned)nlev), dim3(256),
+                     0, st, a);
 }
 
 hipError_t launch_route_dense_score(const RouteArgs& a, int D, int R, hipStream_t st) {

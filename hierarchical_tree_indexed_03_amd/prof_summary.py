@@ -61,10 +61,11 @@ def short(name: str) -> str:
 
 
 STAGE = {
-    "route_score_kernel": "score", "route_hist_kernel": "hist", "route_bound_kernel": "bound",
-    "route_classify_kernel": "classify", "route_resolve_kernel": "resolve",
+    "route_score_kernel": "score", "route_score_keys_kernel": "score", "route_hist_kernel": "hist",
+    "route_bound_kernel": "bound", "route_classify_kernel": "classify", "route_resolve_kernel": "resolve",
     "route_expand_count_kernel": "expand_count", "route_expand_emit_kernel": "expand_emit",
 }
+SCORES = ("route_score_kernel", "route_score_keys_kernel")
 
 
 def decodes(rows):
@@ -83,23 +84,27 @@ def decodes(rows):
 
 
 def label(dec):
-    """(label, row) per dispatch of one decode: score.top / select.top for the top levels,
-    <stage>.l<level> for the general levels, the kernel's short name otherwise."""
+    """(label, row) per dispatch of one decode.  The top levels (scored whole, selected
+    top-down) are labelled .top; each general level starts with its score launch and the
+    general levels are numbered from level 1 (the last one)."""
     names = [short(r["name"]).split("<")[0] for r in dec]
-    top = {i - 1 for i, n in enumerate(names) if n == "route_mls_kernel" and i > 0 and names[i - 1] == "route_score_kernel"}
-    general = [i for i, n in enumerate(names) if n == "route_score_kernel" and i not in top]
+    top_score = {i - 1 for i, n in enumerate(names) if n == "route_topdown_kernel" and i > 0 and names[i - 1] in SCORES}
+    general = [i for i, n in enumerate(names) if n in SCORES and i not in top_score]
     res = []
-    lv = None
+    lv = "top"
     for i, (n, r) in enumerate(zip(names, dec)):
-        if i in top:
+        if i in top_score:
             res.append(("score.top", r))
+            lv = "top"
             continue
-        if n == "route_score_kernel":
-            lv = len(general) - general.index(i)
-        if n in STAGE and lv is not None:
-            res.append((f"{STAGE[n]}.l{lv}", r))
-        elif n == "route_mls_kernel":
+        if n in SCORES:
+            lv = f"l{len(general) - general.index(i)}"
+        if n == "route_topdown_kernel":
             res.append(("select.top", r))
+        elif n == "route_topdown_union_kernel":
+            res.append(("union.top", r))
+        elif n in STAGE:
+            res.append((f"{STAGE[n]}.{lv}", r))
         else:
             res.append((n.replace("_kernel", ""), r))
     return res
@@ -184,7 +189,7 @@ def pmc_groups(rows):
         n = short(r["name"])
         if n.startswith("route_prep_kernel"):
             last_score = None
-        elif n.startswith("route_score_kernel"):
+        elif n.startswith("route_score_kernel") or n.startswith("route_score_keys_kernel"):
             last_score = r
         elif n.startswith("attend_kernel") and "false" in r["name"]:
             att.append(r["v"])
