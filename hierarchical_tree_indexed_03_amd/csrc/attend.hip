@@ -20,6 +20,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "qk_tile.hpp"
+#include "route_util.hpp"
 
 namespace zha {
 
@@ -44,11 +45,6 @@ template <> struct Vec<float> {
   __device__ static uint4 zero() { return make_uint4(0, 0, 0, 0); }
 };
 
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 constexpr int ATILE = 32;   // tokens per wave iteration
 
@@ -243,6 +239,199 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   }
 }
 
+// Dense bf16 flash-decode (the baseline): P.V on MFMA as well.  (The routed path keeps P.V on
+// the VALU: its short per-split streams are bound by the gather-list lookups and K/V load
+// latency, where the lighter kernel's higher occupancy wins.)  Per 32-token tile the probabilities are the
+// A operand ([heads x tokens], each lane already holds its head's 8 tokens, in the same
+// token order as the S^T tile); the V tile is written to LDS transposed ([dim][token], row
+// stride VS) and read back as the B operand, 16 output dims per MFMA.
+constexpr int VS = 36;   // LDS row stride of the transposed V tile (bf16): 8-byte aligned rows,
+                         // the two halves of a wave write disjoint banks
+
+__device__ __forceinline__ uint32_t f2bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;   // round to nearest even (finite inputs)
+}
+
+template <int D, bool DENSE>
+__global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
+  constexpr int NK = Qk<bf16_t, D>::NL;
+  constexpr int NST = ATILE / 16;             // = 2
+  constexpr int NM = D / 16;                  // output dim blocks (MFMAs per tile)
+  __shared__ int64_t Tl[4][ATILE];
+  __shared__ uint32_t Mk[4][ATILE];
+  __shared__ float Al[4][GMAX];
+  __shared__ float Ml[4][GMAX], Ll[4][GMAX];
+  // transposed V tiles during the loop; the waves' partial outputs after it
+  constexpr int VT_BYTES = 4 * D * VS * 2;
+  constexpr int OL_BYTES = 4 * GMAX * D * 4;
+  __shared__ __align__(16) unsigned char buf[VT_BYTES > OL_BYTES ? VT_BYTES : OL_BYTES];
+
+  const int kv = blockIdx.y, split = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int g = a.g;
+  const bf16_t* Kb = (const bf16_t*)a.K + (int64_t)kv * a.cap * D;
+  const bf16_t* Vb = (const bf16_t*)a.V + (int64_t)kv * a.cap * D;
+  uint16_t* Vt = (uint16_t*)buf + wave * D * VS;
+
+  int64_t F;
+  const int32_t* gnode = nullptr;
+  const uint32_t* gmask = nullptr;
+  if constexpr (DENSE) {
+    F = a.N;
+  } else {
+    const int64_t cap0 = a.dev.ncap[0];
+    F = (int64_t)a.dev.cnt[kv] * a.b;
+    gnode = a.dev.node[0] + kv * cap0;
+    gmask = a.dev.mask[0] + kv * cap0;
+  }
+  int64_t fb, fe;
+  split_range(F, a.splits, split, fb, fe);
+  if (fb >= fe) return;
+
+  Qk<bf16_t, D> qk;
+  qk.load_q((const bf16_t*)a.q + (int64_t)kv * g * D, g, col, kg);
+
+  float m = -INFINITY, l = 0.f;               // softmax state of head `col`
+  f32x4 acc[NM];
+#pragma unroll
+  for (int i = 0; i < NM; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto lookup = [&](int64_t f0, int64_t& tok, uint32_t& mk) {
+    const int64_t f = f0 + lane;
+    tok = -1;
+    mk = 0u;
+    if (lane < ATILE && f < fe) {
+      if constexpr (DENSE) {
+        tok = f;
+        mk = 0xffffffffu;
+      } else {
+        const int64_t e = f / a.b;
+        const int64_t t = (int64_t)gnode[e] * a.b + (f - e * a.b);
+        if (t < a.N) { tok = t; mk = gmask[e]; }
+      }
+    }
+  };
+  int64_t ntok;
+  uint32_t nmk;
+  lookup(fb + wave * ATILE, ntok, nmk);
+  const int vt = lane & 31, vc = lane >> 5;   // V loads: token vt, dims 16i + 8vc .. +7
+  for (int64_t f0 = fb + wave * ATILE; f0 < fe; f0 += 4 * ATILE) {
+    if (lane < ATILE) {
+      Tl[wave][lane] = ntok;
+      Mk[wave][lane] = nmk;
+    }
+    if (f0 + 4 * ATILE < fe) lookup(f0 + 4 * ATILE, ntok, nmk);
+    wave_sync_lds();
+    uint4 kf[NST][NK];
+    uint4 vv[NM];
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int64_t tk = Tl[wave][st * 16 + col];
+      if (tk >= 0) Qk<bf16_t, D>::load_k(Kb + tk * D, kg, kf[st]);
+      else
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) kf[st][kk] = make_uint4(0, 0, 0, 0);
+    }
+    {
+      const int64_t tk = Tl[wave][vt];
+#pragma unroll
+      for (int i = 0; i < NM; ++i)
+        vv[i] = tk >= 0 ? *(const uint4*)(Vb + tk * D + 16 * i + 8 * vc) : make_uint4(0, 0, 0, 0);
+    }
+    float sc[NST][4];
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const f32x4 s4 = qk.mma(kf[st]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = st * 16 + kg * 4 + e;
+        const bool use = col < g && ((Mk[wave][t] >> col) & 1u);
+        sc[st][e] = use ? a.sigma * s4[e] : -INFINITY;
+        rmax = fmaxf(rmax, sc[st][e]);
+      }
+    }
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+    const float mn = fmaxf(m, rmax);
+    const float alpha = (mn == -INFINITY) ? 1.f : expf(m - mn);
+    float rsum = 0.f;
+    uint32_t pb[4];                           // P row of head `col`, bf16 pairs, slot order
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const float p0 = (mn == -INFINITY) ? 0.f : expf(sc[st][e] - mn);
+        const float p1 = (mn == -INFINITY) ? 0.f : expf(sc[st][e + 1] - mn);
+        rsum += p0 + p1;
+        pb[st * 2 + e / 2] = f2bf16_bits(p0) | (f2bf16_bits(p1) << 16);
+      }
+    rsum += __shfl_xor(rsum, 16);
+    rsum += __shfl_xor(rsum, 32);
+    l = l * alpha + rsum;
+    m = mn;
+    if (kg == 0 && col < GMAX) Al[wave][col] = alpha;
+    // the V tile, transposed: Vt[dim][token]
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int d = 16 * i + 8 * vc + k;
+        Vt[d * VS + vt] = (uint16_t)((w4[k >> 1] >> (16 * (k & 1))) & 0xffffu);
+      }
+    }
+    wave_sync_lds();
+    float ah[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ah[e] = (4 * kg + e < GMAX) ? Al[wave][4 * kg + e] : 1.f;
+    const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(pb[0], pb[1], pb[2], pb[3]));
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][e] *= ah[e];
+      const uint16_t* row = Vt + (16 * i + col) * VS;
+      const uint2 lo = *(const uint2*)(row + 4 * kg);
+      const uint2 hi = *(const uint2*)(row + 16 + 4 * kg);
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, acc[i], 0, 0, 0);
+    }
+    wave_sync_lds();
+  }
+  __syncthreads();
+  // the waves' partials: acc[i][e] = head 4kg+e, dim 16i + col
+  float* Ol = (float*)buf;                    // [4][GMAX][D]
+  if (kg == 0 && col < GMAX) { Ml[wave][col] = m; Ll[wave][col] = l; }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int h = 4 * kg + e;
+    if (h < GMAX)
+#pragma unroll
+      for (int i = 0; i < NM; ++i) Ol[(wave * GMAX + h) * D + 16 * i + col] = acc[i][e];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < g * D; idx += 256) {
+    const int h = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, Ml[w][h]);
+    float L = 0.f, O = 0.f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float sw = expf(Ml[w][h] - M);
+        L += Ll[w][h] * sw;
+        O += Ol[(w * GMAX + h) * D + d] * sw;
+      }
+    }
+    float* pp = a.dev.apart + ((int64_t)(kv * g + h) * MAX_SPLITS + split) * (D + 2);
+    if (d == 0) { pp[0] = M; pp[1] = L; }
+    pp[2 + d] = O;
+  }
+}
+
 template <typename TIn, int D, bool DENSE>
 __global__ __launch_bounds__(512) void combine_kernel(AttnArgs a, int32_t* stats, int levels) {
   constexpr int NW = 8;        // waves: split rows are dealt round-robin to the waves
@@ -361,7 +550,10 @@ __global__ __launch_bounds__(512) void combine_kernel(AttnArgs a, int32_t* stats
 
 template <typename TIn, int D, bool DENSE>
 static hipError_t launch_attend_t(const AttnArgs& a, int32_t* stats, int levels, hipStream_t st) {
-  hipLaunchKernelGGL((attend_kernel<TIn, D, DENSE>), dim3((unsigned)a.splits, (unsigned)a.hkv), dim3(256), 0, st, a);
+  if constexpr (sizeof(TIn) == 2 && DENSE)
+    hipLaunchKernelGGL((attend_mfma_kernel<D, DENSE>), dim3((unsigned)a.splits, (unsigned)a.hkv), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attend_kernel<TIn, D, DENSE>), dim3((unsigned)a.splits, (unsigned)a.hkv), dim3(256), 0, st, a);
   hipLaunchKernelGGL((combine_kernel<TIn, D, DENSE>), dim3((unsigned)a.hq), dim3(512), 0, st, a, stats, levels);
   return hipGetLastError();
 }
@@ -377,6 +569,28 @@ hipError_t launch_attend_full(const AttnArgs& a, bool bf16, int D, bool dense, i
   }
 #undef ZHA_CASE
   return hipErrorInvalidValue;
+}
+
+template <typename TIn, int D, bool DENSE>
+static int resident_splits_t(int hkv) {
+  static const int per_cu = [] {
+    if constexpr (sizeof(TIn) == 2 && DENSE) return resident_per_cu(attend_mfma_kernel<D, DENSE>, 256);
+    else return resident_per_cu(attend_kernel<TIn, D, DENSE>, 256);
+  }();
+  const int s = per_cu * device_cus() / hkv;
+  return s > MAX_SPLITS ? MAX_SPLITS : (s < 1 ? 1 : s);
+}
+
+int attend_resident_splits(bool bf16, int D, bool dense, int hkv) {
+#define ZHA_CASE(T, DD, DN) \
+  if (D == DD && dense == DN) return resident_splits_t<T, DD, DN>(hkv);
+  if (bf16) {
+    ZHA_CASE(bf16_t, 64, false) ZHA_CASE(bf16_t, 64, true) ZHA_CASE(bf16_t, 128, false) ZHA_CASE(bf16_t, 128, true)
+  } else {
+    ZHA_CASE(float, 64, false) ZHA_CASE(float, 64, true) ZHA_CASE(float, 128, false) ZHA_CASE(float, 128, true)
+  }
+#undef ZHA_CASE
+  return 1;
 }
 
 hipError_t launch_attend(const AttnArgs& a, bool bf16, int D, bool dense, hipStream_t st) {

@@ -87,6 +87,8 @@ hipError_t launch_route_dense_score(const RouteArgs& a, int D, int R, hipStream_
 hipError_t launch_route_topdown(const RouteArgs& a, hipStream_t st);
 
 hipError_t launch_attend(const AttnArgs& a, bool bf16, int D, bool dense, hipStream_t st);
+// Attention workgroups resident on the GPU at once, per KV head (one wave of workgroups).
+int attend_resident_splits(bool bf16, int D, bool dense, int hkv);
 // Same, and copies the per-level union sizes into `stats` ([levels + 1][Hkv], nullable).
 hipError_t launch_attend_full(const AttnArgs& a, bool bf16, int D, bool dense, int32_t* stats, int levels,
                               hipStream_t st);

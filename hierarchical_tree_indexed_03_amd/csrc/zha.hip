@@ -162,13 +162,6 @@ int attn_splits(int64_t tokens, int64_t per_split, int max_splits) {
   return (int)s;
 }
 
-// Attention workgroups resident at once (256 CUs x 3 workgroups of 4 waves at the kernel's
-// register count), spread over the KV heads: one wave of workgroups, no tail.
-int attn_grid_splits(int hkv) {
-  int s = (768 + hkv - 1) / hkv;
-  return s > MAX_SPLITS ? MAX_SPLITS : (s < 1 ? 1 : s);
-}
-
 RouteArgs route_args(const zha_tree* t, const void* q) {
   RouteArgs a;
   memset(&a, 0, sizeof a);
@@ -402,7 +395,8 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
   a.hq = c.num_q_heads;
   a.g = a.hq / a.hkv;
   a.b = c.block;
-  a.splits = attn_grid_splits(c.num_kv_heads);   // splits beyond the gathered tokens exit at once
+  // one wave of resident workgroups; splits beyond the gathered tokens exit at once
+  a.splits = attend_resident_splits(c.dtype == ZHA_BF16, c.head_dim, false, c.num_kv_heads);
   a.keep_sink = c.keep_sink;
   a.sigma = 1.0f / sqrtf((float)c.head_dim);
   a.out = out;
@@ -432,7 +426,7 @@ zha_status zha_decode_dense(zha_tree* t, const void* q, float* out, hipStream_t 
   a.hq = c.num_q_heads;
   a.g = a.hq / a.hkv;
   a.b = c.block;
-  a.splits = attn_splits(t->N, 1024, attn_grid_splits(c.num_kv_heads));
+  a.splits = attn_splits(t->N, 1024, attend_resident_splits(c.dtype == ZHA_BF16, c.head_dim, true, c.num_kv_heads));
   a.keep_sink = 0;
   a.sigma = 1.0f / sqrtf((float)c.head_dim);
   a.out = out;
