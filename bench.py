@@ -68,10 +68,25 @@ def node_bytes(w, level, key_form):
     return core + 8 + g * 4
 
 
+TD_MAX = 33792   # the library's largest level selected top-down (scored whole)
+
+
+def top_levels(w, n_tokens, key_form):
+    """Levels scored whole and selected top-down: from the top down to the lowest level
+    with at most TD_MAX nodes (level 1 excluded when it is scored in key form)."""
+    lo = w.levels + 1
+    while lo > 1 and w.nodes(lo - 1, n_tokens) <= TD_MAX:
+        lo -= 1
+    if key_form and lo == 1:
+        lo = 2
+    return list(range(lo, w.levels + 1))
+
+
 def kernel_bytes(key, w, stats_rows, n_tokens, key_form):
     """Algorithmic HBM bytes of one launch of `key` given the routing stats of that step.
 
     route_score.l<l>: node_bytes per union-frontier node;
+    route_score.top:  node_bytes per node of every top-down level (all of them are scored);
     attend:           per gathered token 2*d*2 bytes (K and V rows, bf16); partial results
                       excluded;
     dense_attend:     N * Hkv * 2 * d * 2 bytes.
@@ -81,6 +96,9 @@ def kernel_bytes(key, w, stats_rows, n_tokens, key_form):
         lv = int(key.split(".l")[1])
         u = stats_rows[L - lv].sum()
         return float(u) * node_bytes(w, lv, key_form)
+    if key == "route_score.top":
+        # every node of the top-down levels (their union-list counts are the level sizes)
+        return float(sum(stats_rows[L - lv].sum() * node_bytes(w, lv, key_form) for lv in top_levels(w, n_tokens, key_form)))
     if key == "attend":
         blocks = stats_rows[L].sum()
         return float(blocks) * w.block * 2 * d * 2

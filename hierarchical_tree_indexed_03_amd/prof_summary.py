@@ -181,28 +181,23 @@ def read_pmc(d, counter):
 
 
 def pmc_groups(rows):
-    """Per dispatch list: calibration copy value, level-1 scoring values, attention values."""
+    """Calibration copy values and, per labelled launch of the routed decodes (score.top,
+    score.l1, attend, ...), the counter values of its dispatches."""
     calib = [r["v"] for r in rows if short(r["name"]) == "copy_kernel"]
-    l1, att = [], []
-    last_score = None
-    for r in rows:
-        n = short(r["name"])
-        if n.startswith("route_prep_kernel"):
-            last_score = None
-        elif n.startswith("route_score_kernel") or n.startswith("route_score_keys_kernel"):
-            last_score = r
-        elif n.startswith("attend_kernel") and "false" in r["name"]:
-            att.append(r["v"])
-            if last_score is not None:
-                l1.append(last_score["v"])
-    return calib, l1, att
+    per = defaultdict(list)
+    for d in decodes(rows):
+        if not any("attend_kernel" in r["name"] and "false" in r["name"] for r in d):
+            continue
+        for lab, r in label(d):
+            per[lab].append(r["v"])
+    return calib, per
 
 
 def cmd_pmc(a):
     fetch = read_pmc(a.fetch_dir, "FETCH_SIZE")
     write = read_pmc(a.write_dir, "WRITE_SIZE")
-    cf, f_l1, f_att = pmc_groups(fetch)
-    cw, w_l1, w_att = pmc_groups(write)
+    cf, fper = pmc_groups(fetch)
+    cw, wper = pmc_groups(write)
     if not cf or not cw:
         sys.exit("calibration copy kernel not found (run bench.py with --calib-copy)")
     # counters are in KiB; scale each so the 1 GiB copy reads 1 GiB and writes 1 GiB
@@ -212,7 +207,10 @@ def cmd_pmc(a):
     out = {"workload": a.workload, "calib": {"copy_bytes": CALIB_BYTES, "fetch_kib": cf[-1], "write_kib": cw[-1],
                                              "fetch_scale": kf, "write_scale": kw},
            "command": a.cmd, "kernels": {}}
-    for key, fv, wv in (("route_score.l1", f_l1, w_l1), ("attend", f_att, w_att)):
+    keymap = {"score.top": "route_score.top", "score.l1": "route_score.l1", "score.l2": "route_score.l2",
+              "attend": "attend"}
+    for lab, key in keymap.items():
+        fv, wv = fper.get(lab), wper.get(lab)
         if fv and wv:
             fb, wb = mean(fv) * 1024 * kf, mean(wv) * 1024 * kw
             out["kernels"][key] = {"src_sha": kernel_sha(key), "bytes": round(fb + wb), "fetch_bytes": round(fb),
