@@ -179,17 +179,45 @@ __global__ __launch_bounds__(256) void route_score_keys_kernel(RouteArgs a) {
   float runmax = -INFINITY;                   // head `col`
 
   const int64_t ntiles = (cnt + NPT - 1) / NPT;
-  for (int64_t t0 = ((int64_t)blockIdx.x * 4 + wave) * UN; t0 < ntiles; t0 += (int64_t)gridDim.x * 4 * UN) {
+  const int64_t tstride = (int64_t)gridDim.x * 4 * UN;
+  // node ids of a pass's tiles: the lane's token-row node, and each node of the tile
+  // (wave-uniform); the next pass's ids are loaded before this pass's keys
+  int32_t rid[UN], nid[UN][NPT];
+  uint32_t nmk[UN][NPT];
+  auto load_ids = [&](int64_t t0, int32_t (&r)[UN], int32_t (&nd)[UN][NPT], uint32_t (&mk)[UN][NPT]) {
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int64_t e_row = (t0 + u) * NPT + col / B;
+      r[u] = ((t0 + u) < ntiles && e_row < cnt) ? nodes[e_row] : -1;
+#pragma unroll
+      for (int n = 0; n < NPT; ++n) {
+        const int64_t e = (t0 + u) * NPT + n;
+        const bool ok = (t0 + u) < ntiles && e < cnt;
+        nd[u][n] = ok ? nodes[e] : -1;
+        mk[u][n] = ok ? masks[e] : 0u;
+      }
+    }
+  };
+  const int64_t tfirst = ((int64_t)blockIdx.x * 4 + wave) * UN;
+  if (tfirst < ntiles) load_ids(tfirst, rid, nid, nmk);
+  for (int64_t t0 = tfirst; t0 < ntiles; t0 += tstride) {
+    int32_t rcur[UN], ncur[UN][NPT];
+    uint32_t mcur[UN][NPT];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      rcur[u] = rid[u];
+#pragma unroll
+      for (int n = 0; n < NPT; ++n) { ncur[u][n] = nid[u][n]; mcur[u][n] = nmk[u][n]; }
+    }
+    if (t0 + tstride < ntiles) load_ids(t0 + tstride, rid, nid, nmk);
     uint4 kf[UN][NK];
     float wv[UN][NPT][KS];
     f32x4 cj[UN][NPT];
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
       // the tile's 16 token rows: token `col` of node col / B; rows past the data read zeros
-      const int64_t e_row = (t0 + u) * NPT + col / B;
-      const bool row_ok = (t0 + u) < ntiles && e_row < cnt;
-      const int64_t tok = row_ok ? (int64_t)nodes[e_row] * B + col % B : 0;
-      if (row_ok && tok < N) {
+      const int64_t tok = rcur[u] >= 0 ? (int64_t)rcur[u] * B + col % B : -1;
+      if (tok >= 0 && tok < N) {
         Qk<bf16_t, D>::load_k(Kc + tok * D, kg, kf[u]);
       } else {
 #pragma unroll
@@ -197,20 +225,19 @@ __global__ __launch_bounds__(256) void route_score_keys_kernel(RouteArgs a) {
       }
 #pragma unroll
       for (int n = 0; n < NPT; ++n) {
-        const int64_t e = (t0 + u) * NPT + n;   // wave-uniform
-        const bool ok = (t0 + u) < ntiles && e < cnt;
-        const int64_t nid = ok ? nodes[e] : 0;
+        const bool ok = ncur[u][n] >= 0;
+        const int64_t nd = ok ? ncur[u][n] : 0;
         // A operand: lane (plane col, token 4s + kg) holds w[plane][token]
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           const int k = 4 * s + kg;
-          wv[u][n][s] = (ok && col < R && k < B) ? W[(nid * R + col) * B + k] : 0.f;
+          wv[u][n][s] = (ok && col < R && k < B) ? W[(nd * R + col) * B + k] : 0.f;
         }
         // accumulator: c of planes 4kg..4kg+3 (absent planes -inf)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
           const int j = 4 * kg + e4;
-          cj[u][n][e4] = (ok && j < R) ? C[nid * R + j] : -INFINITY;
+          cj[u][n][e4] = (ok && j < R) ? C[nd * R + j] : -INFINITY;
         }
       }
     }
@@ -235,10 +262,9 @@ __global__ __launch_bounds__(256) void route_score_keys_kernel(RouteArgs a) {
         v = fmaxf(v, __shfl_xor(v, 16));
         v = fmaxf(v, __shfl_xor(v, 32));
         const int64_t e_ent = (t0 + u) * NPT + n;   // wave-uniform
-        const bool ok = (t0 + u) < ntiles && e_ent < cnt;
-        const uint32_t mk = ok ? masks[e_ent] : 0u;
+        const bool ok = ncur[u][n] >= 0;
         if (ok && kg == 0 && col < g) out[(int64_t)col * cap + e_ent] = v;
-        if ((mk >> col) & 1u) runmax = fmaxf(runmax, v);
+        if ((mcur[u][n] >> col) & 1u) runmax = fmaxf(runmax, v);
       }
       wave_sync_lds();
     }

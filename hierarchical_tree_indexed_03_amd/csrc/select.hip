@@ -112,16 +112,13 @@ __global__ __launch_bounds__(NB1) void route_bound_kernel(RouteArgs a) {
   QState* qs = a.dev.qs + lv * a.hq + hq;
   if (qs->maxkey == 0u) return;
   const uint64_t* src = a.dev.hpart + ((int64_t)kv * SEL_P * GMAX + gi) * NB1 + threadIdx.x;
+  // all partials' loads issued together, summed in a fixed order
+  uint64_t v[SEL_P];
+#pragma unroll
+  for (int p = 0; p < SEL_P; ++p) v[p] = p < a.sel_p ? src[(int64_t)p * GMAX * NB1] : 0ull;
   uint64_t sum = 0;
-  int p = 0;
-  for (; p + 8 <= a.sel_p; p += 8) {
-    uint64_t v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = src[(int64_t)(p + i) * GMAX * NB1];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sum += v[i];
-  }
-  for (; p < a.sel_p; ++p) sum += src[(int64_t)p * GMAX * NB1];
+  for (int p = 0; p < SEL_P; ++p) sum += v[p];
   hs[threadIdx.x] = sum;
   __syncthreads();
   if (threadIdx.x >= 64) return;

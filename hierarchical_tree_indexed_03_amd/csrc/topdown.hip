@@ -285,18 +285,34 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
 }
 
 // Dense union lists of the top-down levels: entry e = node e, mask / keep = the heads of the
-// group whose frontier holds / who kept node e.
+// group whose frontier holds / who kept node e.  A workgroup takes 2,048 nodes of one level
+// and KV head; the group's bitmap words for them go through LDS first.
+constexpr int UN_NODES = 2048;
 __global__ __launch_bounds__(256) void route_topdown_union_kernel(RouteArgs a) {
+  constexpr int W = UN_NODES / 32;
+  __shared__ uint32_t fb[GMAX][W], kb[GMAX][W];
   const int kv = blockIdx.y, lv = a.level - (int)blockIdx.z, g = a.g;
   const int64_t n = a.nl[lv];
   const int64_t cap = a.dev.ncap[lv];
+  const int64_t e0 = (int64_t)blockIdx.x * UN_NODES;
   if (blockIdx.x == 0 && threadIdx.x == 0) a.dev.cnt[lv * a.hkv + kv] = (int32_t)n;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+  if (e0 >= n) return;
+  const int64_t w0 = e0 / 32, nw = (n + 31) / 32;
+  for (int i = threadIdx.x; i < g * W; i += 256) {
+    const int gi = i / W, w = i % W;
+    const uint32_t* gb = a.dev.tdbits + (((int64_t)lv * a.hq + kv * g + gi) * 2) * TD_WORDS;
+    const bool ok = w0 + w < nw;
+    fb[gi][w] = ok ? gb[w0 + w] : 0u;
+    kb[gi][w] = ok ? gb[TD_WORDS + w0 + w] : 0u;
+  }
+  __syncthreads();
+  const int64_t e1 = e0 + UN_NODES < n ? e0 + UN_NODES : n;
+  for (int64_t e = e0 + threadIdx.x; e < e1; e += 256) {
+    const int w = (int)((e - e0) >> 5), bit = (int)(e & 31);
     uint32_t fm = 0, km = 0;
     for (int gi = 0; gi < g; ++gi) {
-      const uint32_t* gb = a.dev.tdbits + (((int64_t)lv * a.hq + kv * g + gi) * 2) * TD_WORDS;
-      fm |= ((gb[e >> 5] >> (e & 31)) & 1u) << gi;
-      km |= ((gb[TD_WORDS + (e >> 5)] >> (e & 31)) & 1u) << gi;
+      fm |= ((fb[gi][w] >> bit) & 1u) << gi;
+      km |= ((kb[gi][w] >> bit) & 1u) << gi;
     }
     a.dev.node[lv][kv * cap + e] = (int32_t)e;
     a.dev.mask[lv][kv * cap + e] = fm;
@@ -309,7 +325,7 @@ hipError_t launch_route_topdown(const RouteArgs& a, hipStream_t st) {
   const int nlev = a.level - a.dense_lo + 1;
   int64_t mx = 0;
   for (int l = a.dense_lo; l <= a.level; ++l) mx = a.nl[l] > mx ? a.nl[l] : mx;
-  hipLaunchKernelGGL(route_topdown_union_kernel, dim3(grid_for(mx, 1024, 64), (unsigned)a.hkv, (unsigned)nlev),
+  hipLaunchKernelGGL(route_topdown_union_kernel, dim3(grid_for(mx, UN_NODES, 1 << 20), (unsigned)a.hkv, (unsigned)nlev),
                      dim3(256), 0, st, a);
   return hipGetLastError();
 }
