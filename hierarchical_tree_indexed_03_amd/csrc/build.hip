@@ -20,6 +20,7 @@
 // A_j = sum_c w_cj A_cj, and c_j = LSE_j - A_j.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "route_util.hpp"
 
 namespace zha {
 
@@ -96,23 +97,40 @@ __global__ __launch_bounds__(256) void build_tile_kernel(BuildArgs a) {
   __shared__ float Ws[T * R];
   __shared__ float Ls[T * R];
   __shared__ float As[T * R];
+  // s of the last in-tile level, for the next level's recursion (R < 8 path)
+  constexpr int SR_HALF = R < 8 ? 2048 : 4;
+  __shared__ __align__(16) float Sr[2 * SR_HALF];
 
   const int kv = blockIdx.y;
-  const int64_t t0 = (int64_t)blockIdx.x * T;
-  const int nt = (int)min((int64_t)T, a.N - t0);
   // a new tree: the append's cached sibling aggregates no longer hold
   if (blockIdx.x == 0 && threadIdx.x <= MAXL) a.dev.sibkey[(int64_t)kv * (MAXL + 1) + threadIdx.x] = -1;
-  const TIn* Kg = (const TIn*)a.K + ((int64_t)kv * a.cap + t0) * D;
   const TIn* Rg = (const TIn*)a.refs + (int64_t)kv * R * D;
+  const int64_t ntiles = (a.N + T - 1) / T;
 
+  // Persistent workgroups: tiles blockIdx.x, + gridDim.x, ...; the next tile's keys are
+  // loaded into registers while the current tile is summarised.
   constexpr int CH = 16 / sizeof(TIn);
-  for (int i = threadIdx.x; i < T * D / CH; i += NT) {
-    int row = (i * CH) / D;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row < nt) v = *(const uint4*)(Kg + (int64_t)i * CH);
-    *(uint4*)(Ks + i * CH) = v;
-  }
+  constexpr int KPT = T * D / CH / NT;        // 16-byte key pieces per thread per tile
+  uint4 kreg[KPT];
+  auto load_tile = [&](int64_t tile) {
+    const int64_t tt0 = tile * T;
+    const int ntt = (int)min((int64_t)T, a.N - tt0);
+    const TIn* Kg = (const TIn*)a.K + ((int64_t)kv * a.cap + tt0) * D;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int i = threadIdx.x + u * NT;
+      const int row = (i * CH) / D;
+      kreg[u] = row < ntt ? *(const uint4*)(Kg + (int64_t)i * CH) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if ((int64_t)blockIdx.x < ntiles) load_tile(blockIdx.x);
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  const int64_t t0 = tile * T;
+  const int nt = (int)min((int64_t)T, a.N - t0);
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) *(uint4*)(Ks + (threadIdx.x + u * NT) * CH) = kreg[u];
   __syncthreads();
+  if (tile + gridDim.x < ntiles) load_tile(tile + gridDim.x);
   tile_logits<D, R, T>(Ks, Rg, a.sigma, nt, Zs);
   __syncthreads();
 
@@ -156,8 +174,10 @@ __global__ __launch_bounds__(256) void build_tile_kernel(BuildArgs a) {
     __syncthreads();
   }
 
-  // Weighted-mean keys s_j of every node of every in-tile level, straight from the keys.
+  // Weighted-mean keys s_j of every node of every in-tile level: from the keys (MFMA path,
+  // and level 1), or from the level below (VALU path, see there).
   bv = 1;
+  bool recur_ok = false;
   for (int v = 1; v <= a.m; ++v) {
     bv *= a.b;
     const int nexist = (int)((nt + bv - 1) / bv);
@@ -200,28 +220,53 @@ __global__ __launch_bounds__(256) void build_tile_kernel(BuildArgs a) {
         }
       }
     } else {
+      // level 1 from the keys; a higher in-tile level from the level below while that level
+      // fits the LDS buffer (s_parent = sum over children of exp(LSE_c - LSE_parent) s_c),
+      // else from the keys of its whole span
+      const int nprev = v == 1 ? 0 : (int)((nt + bv / a.b - 1) / (bv / a.b));
+      const bool from_children = v > 1 && nprev * R * D <= SR_HALF && recur_ok;
+      const float* Sprev = Sr + ((v - 1) & 1) * SR_HALF;
+      float* Scur = Sr + (v & 1) * SR_HALF;
+      const bool keep_cur = nexist * R * D <= SR_HALF;
       const int items = nexist * (D / 4);
       for (int it = threadIdx.x; it < items; it += NT) {
         const int node = it / (D / 4), dc = it % (D / 4);
-        const int ts = node * (int)bv, te = min(ts + (int)bv, nt);
         float4 acc[R];
 #pragma unroll
         for (int j = 0; j < R; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int t = ts; t < te; ++t) {
-          float4 k4 = ld4_f32(Ks + t * D + dc * 4);
+        if (from_children) {
+          const int cb = node * a.b, ce = min(cb + a.b, nprev);
+          for (int ch = cb; ch < ce; ++ch) {
 #pragma unroll
-          for (int j = 0; j < R; ++j) {
-            float w = Ws[t * R + j];
-            acc[j].x += w * k4.x; acc[j].y += w * k4.y; acc[j].z += w * k4.z; acc[j].w += w * k4.w;
+            for (int j = 0; j < R; ++j) {
+              const float w = expf(Ls[off[v - 1] + ch * R + j] - Ls[off[v] + node * R + j]);
+              const float4 s4 = *(const float4*)(Sprev + (ch * R + j) * D + dc * 4);
+              acc[j].x += w * s4.x; acc[j].y += w * s4.y; acc[j].z += w * s4.z; acc[j].w += w * s4.w;
+            }
+          }
+        } else {
+          const int ts = node * (int)bv, te = min(ts + (int)bv, nt);
+          for (int t = ts; t < te; ++t) {
+            float4 k4 = ld4_f32(Ks + t * D + dc * 4);
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+              float w = Ws[t * R + j];
+              acc[j].x += w * k4.x; acc[j].y += w * k4.y; acc[j].z += w * k4.z; acc[j].w += w * k4.w;
+            }
           }
         }
         const int64_t gnode = t0 / bv + node;
         float* sg = a.dev.s[v] + (((int64_t)kv * a.dev.ncap[v] + gnode) * R) * D + dc * 4;
 #pragma unroll
         for (int j = 0; j < R; ++j) *(float4*)(sg + (int64_t)j * D) = acc[j];
+        if (keep_cur)
+#pragma unroll
+          for (int j = 0; j < R; ++j) *(float4*)(Scur + (node * R + j) * D + dc * 4) = acc[j];
       }
+      recur_ok = keep_cur;
     }
     __syncthreads();
+  }
   }
 }
 
@@ -478,15 +523,25 @@ __global__ __launch_bounds__(1024) void append_kernel(AppendArgs a) {
 }
 
 // ---------------------------------------------------------------- host launchers
+// One wave of resident workgroups per launch, spread over the KV heads; each strides over
+// its tiles.
+template <typename TIn, int D, int R, int T>
+static void launch_build_tiles(const BuildArgs& a, int64_t ntiles, int hkv, hipStream_t st) {
+  static const int per_cu = resident_per_cu(build_tile_kernel<TIn, D, R, T>, 256);
+  int64_t x = (int64_t)per_cu * device_cus() / hkv;
+  if (x > ntiles) x = ntiles;
+  if (x < 1) x = 1;
+  hipLaunchKernelGGL((build_tile_kernel<TIn, D, R, T>), dim3((unsigned)x, (unsigned)hkv), dim3(256), 0, st, a);
+}
+
 template <typename TIn, int D, int R>
 static hipError_t launch_build_d(const BuildArgs& a, int64_t ntiles, int hkv, int T, hipStream_t st) {
-  dim3 grid((unsigned)ntiles, (unsigned)hkv);
   if (T == 128) {
-    hipLaunchKernelGGL((build_tile_kernel<TIn, D, R, 128>), grid, dim3(256), 0, st, a);
+    launch_build_tiles<TIn, D, R, 128>(a, ntiles, hkv, st);
   } else {
     // 256-token tiles (blocks of more than 128 keys) only where the tile fits in LDS
     if constexpr (sizeof(TIn) * 256 * D + 16 * 256 * R <= 160 * 1024)
-      hipLaunchKernelGGL((build_tile_kernel<TIn, D, R, 256>), grid, dim3(256), 0, st, a);
+      launch_build_tiles<TIn, D, R, 256>(a, ntiles, hkv, st);
     else
       return hipErrorInvalidValue;
   }
