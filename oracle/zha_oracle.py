@@ -22,8 +22,10 @@ level-l node n spans tokens [n*b^l, min((n+1)*b^l, N)).
 Parity pins: every function here is pinned by the CPU tests in ``tests/test_oracle_pins.py``
 (dense limit at p=1, convexity lower bound, exactness at q=r_j, recursion = direct
 per-span form, single-key blocks, nucleus selection for b=1, brute-force minimality,
-mass conservation, append = rebuild, geometry).  The exact routed sets at p<1 on the
-synthetic data are defined only by this oracle ("parity unpinned" beyond those pins).
+mass conservation, append = rebuild, geometry; for the bf16 router planes: rounding
+against torch's float32 -> bfloat16 cast and a brute-force nearest search, and the score
+perturbation bound).  The exact routed sets at p<1 on the synthetic data are defined only
+by this oracle ("parity unpinned" beyond those pins).
 """
 from __future__ import annotations
 
@@ -165,6 +167,36 @@ def append_token(tree: Tree, key: np.ndarray) -> None:
             s_all[node] = s[0]
             c_all[node] = c[0]
         tree.levels[lv - 1] = (s_all, c_all)
+
+
+# --------------------------------------------------------------------------- bf16 router planes
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value of each element, as float64 (normal range).
+
+    bfloat16 keeps 8 significant bits (the float32 exponent range, a 7-bit stored
+    mantissa); a value halfway between two neighbours goes to the one with an even last
+    bit.  Written from that definition: with x = m * 2^e and 1/2 <= |m| < 1, the kept
+    value is round(m * 2^8) * 2^(e-8), np.round rounding halves to even.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+
+
+def quantise_planes(tree: Tree, levels) -> Tree:
+    """The router's view of a tree whose planes at ``levels`` are stored with bf16 s.
+
+    The pages fix no storage precision for the planes (their routing arithmetic is fp32).
+    Stated quantiser: every element of s_j is rounded to the nearest bf16 value; the
+    offsets c_j stay as computed (fp32 storage on the GPU).  The tree itself is unchanged:
+    parents and appends keep using the full-precision planes, and only routing reads the
+    quantised copy.  Levels not listed keep their full-precision s.
+    """
+    out = list(tree.levels)
+    for lv in levels:
+        s, c = tree.levels[lv - 1]
+        out[lv - 1] = (bf16_round(s), c)
+    return dataclasses.replace(tree, levels=out)
 
 
 # --------------------------------------------------------------------------- routing

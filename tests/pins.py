@@ -238,6 +238,86 @@ def check_sink(seed=10):
     return bool(ok), "sink present and unique"
 
 
+# bf16 router planes.  Rounding of float32 inputs = torch's float32 -> bfloat16 cast
+# (round to nearest, ties to even), including values exactly halfway between two
+# bfloat16 neighbours with either parity of the kept last bit.
+def check_bf16_round_library(seed=11):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    hi = rng.integers(0x3000, 0x4f00, 4000, dtype=np.uint32)
+    half = ((hi << 16) | 0x8000).astype(np.uint32)
+    half = np.concatenate([half, half | np.uint32(0x80000000)]).view(np.float32)
+    x = np.concatenate([x, half, np.array([0.0, 1.0, -2.5, 3.0e-30], np.float32)])
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = zo.bf16_round(x.astype(np.float64))
+    bad = int(np.count_nonzero(got != want))
+    return bad == 0, f"{bad} of {x.size} roundings differ from torch's cast"
+
+
+# Rounding of float64 inputs = the nearest of all finite bfloat16 values, by brute force
+# over every bit pattern; exact midpoints of neighbours go to the even pattern.
+def check_bf16_round_nearest(seed=12):
+    rng = np.random.default_rng(seed)
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        vals = (pats << 16).view(np.float32).astype(np.float64)
+    fin = np.isfinite(vals) & ~((vals == 0) & (pats != 0))     # one zero
+    vals, pats = vals[fin], pats[fin]
+    order = np.argsort(vals, kind="stable")
+    vals, pats = vals[order], pats[order]
+    x = rng.standard_normal(5000) * np.exp(rng.uniform(-30, 30, 5000))
+    i = np.clip(np.searchsorted(vals, x), 1, len(vals) - 1)
+    lo, hi = vals[i - 1], vals[i]
+    want = np.where(x - lo < hi - x, lo, hi)
+    # constructed midpoints of neighbouring positive normal values
+    first = int(np.searchsorted(vals, 2.0 ** -126))
+    k = rng.integers(first, len(vals) - 2, 2000)
+    mid = (vals[k] + vals[k + 1]) / 2
+    want_mid = np.where(pats[k] % 2 == 0, vals[k], vals[k + 1])
+    got, got_mid = zo.bf16_round(x), zo.bf16_round(mid)
+    bad = int(np.count_nonzero(got != want)) + int(np.count_nonzero(got_mid != want_mid))
+    return bad == 0, f"{bad} roundings differ from the brute-force nearest value"
+
+
+# Quantised planes: the listed levels' s become bfloat16 values within half a unit
+# (2^-8 |s|), the offsets and the other levels are untouched, and each node's score moves
+# by at most max_j sigma * sum_i |q_i| |s~_ji - s_ji| (a max of planes moves by at most
+# the largest plane move).
+def check_quantised_planes(seed=13):
+    rng = np.random.default_rng(seed)
+    tree, keys, _ = rand_tree(rng, n=300, d=16, r=3, b=4, levels=3)
+    qt = zo.quantise_planes(tree, [1, 3])
+    d = keys.shape[1]
+    sig = 1.0 / math.sqrt(d)
+    moved = 0
+    for lv in range(1, 4):
+        s, c = tree.levels[lv - 1]
+        sq, cq = qt.levels[lv - 1]
+        if not np.array_equal(cq, c):
+            return False, f"level {lv}: offsets changed"
+        if lv == 2:
+            if not np.array_equal(sq, s):
+                return False, "level 2 (not listed) changed"
+            continue
+        f = torch.from_numpy(sq.astype(np.float32))
+        if not (np.array_equal(f.numpy().astype(np.float64), sq) and
+                torch.equal(f.to(torch.bfloat16).to(torch.float32), f)):
+            return False, f"level {lv}: s is not made of bfloat16 values"
+        if np.any(np.abs(sq - s) > 2.0 ** -8 * np.abs(s)):
+            return False, f"level {lv}: rounding error above half a unit"
+        nodes = np.arange(tree.nodes(lv))
+        for _ in range(10):
+            q = rng.standard_normal(d) * 3
+            a = zo.node_scores(tree, lv, nodes, q)
+            b = zo.node_scores(qt, lv, nodes, q)
+            bound = sig * np.max(np.abs(sq - s) @ np.abs(q), axis=1)
+            if np.any(np.abs(b - a) > bound * (1 + 1e-9) + 1e-15):
+                return False, f"level {lv}: score moved beyond the plane bound"
+            moved += int(np.count_nonzero(a != b))
+    return moved > 0, f"{moved} quantised scores moved"
+
+
 ALL = [check_dense_limit, check_convexity, check_exact_at_refs, check_recursion_direct,
        check_single_key, check_nucleus, check_minimal, check_mass_conservation, check_append,
-       check_masked_attention, check_sink]
+       check_masked_attention, check_sink, check_bf16_round_library, check_bf16_round_nearest,
+       check_quantised_planes]

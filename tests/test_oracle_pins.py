@@ -147,6 +147,28 @@ def _mut_children_shift(orig):
     return f
 
 
+def _mut_bf16_truncate(orig):
+    def f(x):
+        x = np.asarray(x, dtype=np.float64)
+        m, e = np.frexp(x)
+        return np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)
+    return f
+
+
+def _mut_quantise_offsets(orig):
+    def f(tree, levels):
+        qt = orig(tree, levels)
+        qt.levels = [(s, zo.bf16_round(c)) for s, c in qt.levels]
+        return qt
+    return f
+
+
+def _mut_quantise_next_level(orig):
+    def f(tree, levels):
+        return orig(tree, [lv + 1 for lv in levels if lv < tree.n_levels])
+    return f
+
+
 MUTATIONS = [
     ("level1_planes", _mut_level1_offset),
     ("parent_planes", _mut_parent_unweighted),
@@ -156,6 +178,9 @@ MUTATIONS = [
     ("attend", _mut_attend_unscaled),
     ("node_scores", _mut_scores_mean),
     ("children", _mut_children_shift),
+    ("bf16_round", _mut_bf16_truncate),
+    ("quantise_planes", _mut_quantise_offsets),
+    ("quantise_planes", _mut_quantise_next_level),
 ]
 
 
