@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="deep", help="deep | wide | ultra | light_<N> | tiny")
+    ap.add_argument("--planes", default="f32", choices=("f32", "bf16"),
+                    help="storage of the s vectors the router reads (bf16: a rounded copy)")
     ap.add_argument("--build-reps", type=int, default=3)
     ap.add_argument("--dense-reps", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -58,11 +60,14 @@ def parse():
 
 def node_bytes(w, level, key_form):
     """Algorithmic bytes read to score one union-frontier node at `level`: its R planes
-    (R*(d+1) floats), or at level 1 in key form its b keys (bf16) plus R*b token weights and
-    R offsets; plus the 8-byte list entry and one float score per query head written."""
+    (R*(d+1) floats; with bf16 router planes R*d bf16 plus R float offsets), or at level 1
+    in key form its b keys (bf16) plus R*b token weights and R offsets; plus the 8-byte list
+    entry and one float score per query head written."""
     R, d, g, b = w.num_ref, w.head_dim, w.group, w.block
     if level == 1 and key_form:
         core = b * d * 2 + R * b * 4 + R * 4
+    elif w.planes == "bf16":
+        core = R * d * 2 + R * 4
     else:
         core = R * (d + 1) * 4
     return core + 8 + g * 4
@@ -282,8 +287,9 @@ def main():
     base = wc.NAMED[args.workload]
     steps = args.steps if args.steps is not None else (base.steps or 64)
     total = args.warmup + steps + args.cold_steps
-    w = base.with_(steps=total)
+    w = base.with_(steps=total, planes=args.planes)
     n0 = w.n_tokens
+    prof_name = w.name if w.planes == "f32" else f"{w.name}_bf16planes"   # counter summaries
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
 
@@ -309,9 +315,10 @@ def main():
     stats = torch.zeros(total, w.levels + 1, w.num_kv_heads, dtype=torch.int32, device=dev)
 
     cfg = zha.make_config(w.head_dim, w.num_kv_heads, w.num_q_heads, w.block, w.levels, w.num_ref,
-                          w.capacity, w.dtype, w.top_p, w.keep_sink)
+                          w.capacity, w.dtype, w.top_p, w.keep_sink, w.planes)
     tree = zha.Tree(cfg)
     h = tree.handle
+    key_form = zha.zha_level1_key_form(cfg) == 1
 
     # ---- tree build (timed separately; the last build is the one decoded against)
     torch.cuda.synchronize()
@@ -325,10 +332,14 @@ def main():
         build_ms.append(e0.elapsed_time(e1))
     build_s = min(build_ms) / 1e3
     build_tok_s = n0 / build_s
+    # read the keys once; write every plane (plus the bf16 router copies of s, and the
+    # level-1 token weights in key form) once
+    copies = [l for l in range(1, w.levels + 1) if w.planes == "bf16" and not (l == 1 and key_form)]
     build_bytes = n0 * w.num_kv_heads * (w.head_dim * (2 if w.dtype == "bf16" else 4) +
                                         sum(w.num_ref * (w.head_dim + 1) * 4 / w.block ** l
                                             for l in range(1, w.levels + 1)) +
-                                        (w.num_ref * 4 if zha.zha_level1_key_form(cfg) == 1 else 0))
+                                        sum(w.num_ref * w.head_dim * 2 / w.block ** l for l in copies) +
+                                        (w.num_ref * 4 if key_form else 0))
     log(f"[bench] build {build_s * 1e3:.3f} ms -> {build_tok_s / 1e9:.3f} G tok/s")
 
     def step(s):
@@ -377,7 +388,6 @@ def main():
     qps = steps / wall
     st = stats.cpu().numpy()
     timed_stats = st[args.warmup:args.warmup + steps]
-    key_form = zha.zha_level1_key_form(cfg) == 1
     dom_bytes = [kernel_bytes(dominant, w, timed_stats[i], n0 + args.warmup + i + 1, key_form) for i in range(steps)]
     dom_avg_ms = dom_ms / max(dom_n, 1)
     roofline = None
@@ -385,7 +395,7 @@ def main():
         alg = float(np.mean(dom_bytes))
         achieved = alg / (dom_avg_ms * 1e-3) / 1e9
         roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_for(dominant, w.name),
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_for(dominant, prof_name),
                         kernel=dominant, launches=dom_n, avg_launch_ms=round(dom_avg_ms, 4),
                         algorithmic_bytes_per_launch=round(alg))
     log(f"[bench] timed {steps} steps: {ms_per_step:.3f} ms/step (events {gpu_ms / steps:.3f}), "
@@ -483,8 +493,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16+f32",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}_{n0}", "kv_tokens": n0, "head_dim": d, "q_heads": w.num_q_heads,
+        "config": {"workload": f"{w.name}_{n0}" + ("" if w.planes == "f32" else "_bf16planes"), "kv_tokens": n0, "head_dim": d, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "block": w.block, "levels": L, "num_ref": R, "top_p": w.top_p,
+                   "router_planes": w.planes,
                    "batch": 1, "layers": 1, "step": "append + decode"},
         "roofline": roofline,
         "cpu_baseline": cpu,

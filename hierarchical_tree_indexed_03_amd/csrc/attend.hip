@@ -248,11 +248,6 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
 constexpr int VS = 36;   // LDS row stride of the transposed V tile (bf16): 8-byte aligned rows,
                          // the two halves of a wave write disjoint banks
 
-__device__ __forceinline__ uint32_t f2bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;   // round to nearest even (finite inputs)
-}
-
 template <int D, bool DENSE>
 __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
   constexpr int NK = Qk<bf16_t, D>::NL;

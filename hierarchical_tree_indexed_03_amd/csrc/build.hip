@@ -83,6 +83,13 @@ __device__ void tile_logits(const float* Ks, const float* refs_g, float sigma, i
 }
 
 __device__ __forceinline__ float4 ld4_f32(const float* p) { return *(const float4*)p; }
+// four floats as bfloat16 (nearest, ties to even) at an 8-byte aligned address
+__device__ __forceinline__ void store_bf16x4(bf16_t* p, float4 v) {
+  uint2 w;
+  w.x = f2bf16_bits(v.x) | (f2bf16_bits(v.y) << 16);
+  w.y = f2bf16_bits(v.z) | (f2bf16_bits(v.w) << 16);
+  *(uint2*)p = w;
+}
 __device__ __forceinline__ float4 ld4_f32(const bf16_t* p) {
   uint2 v = *(const uint2*)p;
   return make_float4(bf16_bits_to_f32(v.x & 0xffffu), bf16_bits_to_f32(v.x >> 16),
@@ -212,11 +219,20 @@ __global__ __launch_bounds__(256) void build_tile_kernel(BuildArgs a) {
           acc = mfma_f32(w, kvv, acc);
         }
         const int64_t gnode = t0 / bv + node;
-        float* sg = a.dev.s[v] + (((int64_t)kv * a.dev.ncap[v] + gnode) * R) * D + n16 * 16 + col;
+        const int64_t so = (((int64_t)kv * a.dev.ncap[v] + gnode) * R) * D + n16 * 16 + col;
+        float* sg = a.dev.s[v] + so;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = kg * 4 + e;
           if (j < R) sg[(int64_t)j * D] = acc[e];
+        }
+        if (a.dev.sq[v]) {
+          uint16_t* qg = (uint16_t*)a.dev.sq[v] + so;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = kg * 4 + e;
+            if (j < R) qg[(int64_t)j * D] = (uint16_t)f2bf16_bits(acc[e]);
+          }
         }
       }
     } else {
@@ -256,9 +272,13 @@ __global__ __launch_bounds__(256) void build_tile_kernel(BuildArgs a) {
           }
         }
         const int64_t gnode = t0 / bv + node;
-        float* sg = a.dev.s[v] + (((int64_t)kv * a.dev.ncap[v] + gnode) * R) * D + dc * 4;
+        const int64_t so = (((int64_t)kv * a.dev.ncap[v] + gnode) * R) * D + dc * 4;
+        float* sg = a.dev.s[v] + so;
 #pragma unroll
         for (int j = 0; j < R; ++j) *(float4*)(sg + (int64_t)j * D) = acc[j];
+        if (a.dev.sq[v])
+#pragma unroll
+          for (int j = 0; j < R; ++j) store_bf16x4(a.dev.sq[v] + so + (int64_t)j * D, acc[j]);
         if (keep_cur)
 #pragma unroll
           for (int j = 0; j < R; ++j) *(float4*)(Scur + (node * R + j) * D + dc * 4) = acc[j];
@@ -312,7 +332,9 @@ __device__ void parent_nodes(const Dev& dev, int v, int kv, int b, int64_t p0, i
       const float4 s4 = *(const float4*)(s_c + (ch * R + j) * D + dc * 4);
       acc.x += w * s4.x; acc.y += w * s4.y; acc.z += w * s4.z; acc.w += w * s4.w;
     }
-    *(float4*)(dev.s[v] + (((int64_t)kv * pcap + gp) * R + j) * D + dc * 4) = acc;
+    const int64_t so = (((int64_t)kv * pcap + gp) * R + j) * D + dc * 4;
+    *(float4*)(dev.s[v] + so) = acc;
+    if (dev.sq[v]) store_bf16x4(dev.sq[v] + so, acc);
   }
 }
 
@@ -503,9 +525,12 @@ __global__ __launch_bounds__(1024) void append_kernel(AppendArgs a) {
     const float kd = to_f32(kn[d]);
     float sv = Cf[0][j][0] * sold[u] + Cf[0][j][1] * kd;
     a.dev.s[1][g1 * RD + i] = sv;
+    if (a.dev.sq[1]) a.dev.sq[1][g1 * RD + i].bits = (uint16_t)f2bf16_bits(sv);
     for (int v = 2; v <= L; ++v) {
       sv = Cf[v - 1][j][0] * Agg[(v - 2) * RS + j * (D + 2) + 2 + d] + Cf[v - 1][j][1] * sv;
-      a.dev.s[v][((int64_t)kv * a.dev.ncap[v] + pvl[v - 2]) * RD + i] = sv;
+      const int64_t si = ((int64_t)kv * a.dev.ncap[v] + pvl[v - 2]) * RD + i;
+      a.dev.s[v][si] = sv;
+      if (a.dev.sq[v]) a.dev.sq[v][si].bits = (uint16_t)f2bf16_bits(sv);
     }
   }
   // token weights of the level-1 planes (key-form scoring): old weights scale by

@@ -30,6 +30,11 @@ struct bf16_t { uint16_t bits; };   // storage type of bfloat16 tensors
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x.bits << 16); }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+// nearest bfloat16 (ties to even) of a finite float, as its 16 bits
+__device__ __forceinline__ uint32_t f2bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
 
 // Order-preserving map float -> uint32 (a < b  <=>  key(a) < key(b)).
 __device__ __forceinline__ uint32_t f2key(float f) {
@@ -92,6 +97,8 @@ struct Dev {
   float* s[MAXL + 1];       // level l: [Hkv][ncap[l]][R][D]
   float* c[MAXL + 1];       // level l: [Hkv][ncap[l]][R]
   float* lse[MAXL + 1];     // level l: [Hkv][ncap[l]][R] log mass at r_j (build/append only)
+  bf16_t* sq[MAXL + 1];     // level l: [Hkv][ncap[l]][R][D] the router's bf16 copy of s (bf16
+                            // router planes only; null at a level the router reads no planes of)
   float* w1;                // [Hkv][ncap[1]][R][b] token weights of the level-1 planes
                             // (key-form scoring only; null otherwise)
   int64_t ncap[MAXL + 1];   // node capacity per level (index 0: gather list = ncap[1])

@@ -51,6 +51,8 @@ struct RouteArgs {
   int32_t dense_lo;   // lowest level handled by the multi-level selection kernel
   int32_t sel_p;      // top-p histogram / classify workgroups per KV head at `level`
   int32_t key_form;   // level 1 scored from the block's keys and the planes' token weights
+  int32_t q_bf16;     // q (and the caches) are bf16; else fp32
+  int32_t planes_bf16;   // scores read the bf16 copies dev.sq
   const void* K;      // key cache [Hkv][kcap][D] (key-form scoring)
   int64_t kcap;
   int64_t nl[MAXL + 1];   // nodes per level at N

@@ -25,6 +25,9 @@
 #ifndef ZHA_KEYS_UN
 #define ZHA_KEYS_UN 2
 #endif
+#ifndef ZHA_SCORE_UN_BF16
+#define ZHA_SCORE_UN_BF16 4
+#endif
 
 namespace zha {
 
@@ -135,6 +138,128 @@ __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
     for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
     if (col == 0) red[wave][kg * 4 + e] = v;
   }
+  __syncthreads();
+  if (threadIdx.x < g) {
+    const int gi = threadIdx.x;
+    const float m = fmaxf(fmaxf(red[0][gi], red[1][gi]), fmaxf(red[2][gi], red[3][gi]));
+    if (m > -INFINITY) atomicMax(&a.dev.qs[lv * a.hq + kv * g + gi].maxkey, f2key(m));
+  }
+}
+
+
+// ------------------------------------------------------------------ bf16 router planes
+// A 16-row tile of bf16 plane rows (row c = node slot c / R, plane c % R) for one lane:
+// the contiguous D/4 slice [kg D/4, (kg+1) D/4) of its row, in the operand layout of
+// Qk<TQ, D> (bf16 as loaded; fp32 queries take the values widened to fp32).
+template <typename TQ, int D> struct PlaneRow;
+template <int D> struct PlaneRow<bf16_t, D> {
+  static constexpr int NL = Qk<bf16_t, D>::NL;
+  __device__ static void load(const bf16_t* row, int kg, bool ok, uint4* k) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) k[i] = ok ? *(const uint4*)(row + kg * (D / 4) + i * 8) : make_uint4(0, 0, 0, 0);
+  }
+};
+template <int D> struct PlaneRow<float, D> {
+  static constexpr int NL = Qk<float, D>::NL;
+  __device__ static void load(const bf16_t* row, int kg, bool ok, uint4* k) {
+#pragma unroll
+    for (int i = 0; i < NL / 2; ++i) {
+      const uint4 w = ok ? *(const uint4*)(row + kg * (D / 4) + i * 8) : make_uint4(0, 0, 0, 0);
+      k[2 * i] = make_uint4(w.x << 16, w.x & 0xffff0000u, w.y << 16, w.y & 0xffff0000u);
+      k[2 * i + 1] = make_uint4(w.z << 16, w.z & 0xffff0000u, w.w << 16, w.w & 0xffff0000u);
+    }
+  }
+};
+
+// Scores from the bf16 copies of s: the tile S = P (16 plane rows x D) . Q^T (D x 16 heads)
+// on MFMA against the raw query (bf16 x bf16 products are exact in the fp32 accumulator;
+// fp32 queries take the fp32 MFMA), then sigma * S + c_j.  Lane (head col, group kg) holds
+// rows 4kg..4kg+3 for head col; a node's R rows lie in-lane (R <= 4) or across the
+// lane groups kg (R = 8, 16), so the max over planes is in-lane then cross-lane.
+template <typename TQ, int D, int R>
+__global__ __launch_bounds__(256) void route_score_bf16_kernel(RouteArgs a) {
+  constexpr int NPT = 16 / R;                 // nodes per 16-row tile
+  constexpr int UN = ZHA_SCORE_UN_BF16;       // tiles in flight per wave
+  constexpr int NL = Qk<TQ, D>::NL;
+  constexpr int RL = R < 4 ? R : 4;           // rows of one node within a lane's 4 rows
+  constexpr int NPL = 4 / RL;                 // nodes within a lane's 4 rows
+  __shared__ float red[4][16];
+  const int kv = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const bool dense = a.dense != 0;            // every node of the level, no list
+  const int lv = dense ? a.level - (int)blockIdx.z : a.level;
+  const int64_t cnt = dense ? a.nl[lv] : a.dev.cnt[lv * a.hkv + kv];
+  const int64_t cap = a.dev.ncap[lv];
+  const int32_t* nodes = a.dev.node[lv] + kv * cap;
+  const uint32_t* masks = a.dev.mask[lv] + kv * cap;
+  const bf16_t* S = a.dev.sq[lv] + (int64_t)kv * cap * R * D;
+  const float* C = a.dev.c[lv] + (int64_t)kv * cap * R;
+  float* out = a.dev.score[lv] + (int64_t)kv * GMAX * cap;
+  const int g = a.g;
+  const float sigma = a.sigma;
+
+  Qk<TQ, D> qk;
+  qk.load_q((const TQ*)a.q + (int64_t)kv * g * D, g, col, kg);
+  float runmax = -INFINITY;                   // head col
+
+  const int64_t ntiles = (cnt + NPT - 1) / NPT;
+  for (int64_t t0 = ((int64_t)blockIdx.x * 4 + wave) * UN; t0 < ntiles; t0 += (int64_t)gridDim.x * 4 * UN) {
+    uint4 kf[UN][NL];
+    float cj[UN][4];
+    int64_t eo[UN][NPL];                      // union entries of the lane's output nodes
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const bool tok = (t0 + u) < ntiles;
+      // the lane's load row `col`
+      const int64_t e_row = (t0 + u) * NPT + col / R;
+      const bool okr = tok && e_row < cnt;
+      const int64_t nrow = okr ? (dense ? e_row : (int64_t)nodes[e_row]) : 0;
+      PlaneRow<TQ, D>::load(S + (nrow * R + col % R) * D, kg, okr, kf[u]);
+      // the lane's output rows 4kg + e
+#pragma unroll
+      for (int n = 0; n < NPL; ++n) {
+        const int r = 4 * kg + n * RL;
+        const int64_t e = (t0 + u) * NPT + r / R;
+        const bool ok = tok && e < cnt;
+        eo[u][n] = ok ? e : -1;
+        const int64_t nd = ok ? (dense ? e : (int64_t)nodes[e]) : 0;
+        if constexpr (RL == 4) {
+          const float4 c4 = ok ? *(const float4*)(C + nd * R + r % R) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+          cj[u][0] = c4.x; cj[u][1] = c4.y; cj[u][2] = c4.z; cj[u][3] = c4.w;
+        } else {
+#pragma unroll
+          for (int i = 0; i < RL; ++i) cj[u][n * RL + i] = ok ? C[nd * R + i] : -INFINITY;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const f32x4 acc = qk.mma(kf[u]);        // acc[e]: row 4kg+e, head col
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = sigma * acc[e] + cj[u][e];
+#pragma unroll
+      for (int o = 1; o < RL; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], v[e ^ o]);
+#pragma unroll
+      for (int o = 16; o < 4 * R; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], __shfl_xor(v[e], o));
+#pragma unroll
+      for (int n = 0; n < NPL; ++n) {
+        const int64_t e = eo[u][n];
+        const bool writer = ((4 * kg) % R) == 0;    // the node's first lane group
+        if (e >= 0 && writer && col < g) out[(int64_t)col * cap + e] = v[n * RL];
+        const uint32_t mk = (e >= 0 && !dense) ? masks[e] : 0u;   // dense: max taken later
+        if ((mk >> col) & 1u) runmax = fmaxf(runmax, v[n * RL]);
+      }
+    }
+  }
+  // per-head max over the wave's lane groups, then over the waves
+  runmax = fmaxf(runmax, __shfl_xor(runmax, 16));
+  runmax = fmaxf(runmax, __shfl_xor(runmax, 32));
+  if (kg == 0) red[wave][col] = runmax;
   __syncthreads();
   if (threadIdx.x < g) {
     const int gi = threadIdx.x;
@@ -293,12 +418,27 @@ hipError_t launch_route_prep(const RouteArgs& a, bool bf16, int D, hipStream_t s
 
 // Score grids hold one wave of resident workgroups over the KV heads (the node loop is
 // strided), so no workgroup of a second, partial wave trails the launch.
+template <typename TQ, int D, int R>
+static void launch_score_bf16(const RouteArgs& a, int nlev, int64_t nodes, hipStream_t st) {
+  constexpr int NPB = 4 * (16 / R) * ZHA_SCORE_UN_BF16;   // nodes per block pass
+  static const int per_cu = resident_per_cu(route_score_bf16_kernel<TQ, D, R>, 256);
+  const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
+  hipLaunchKernelGGL((route_score_bf16_kernel<TQ, D, R>), dim3(grid_for(nodes, NPB, cap), (unsigned)a.hkv, (unsigned)nlev),
+                     dim3(256), 0, st, a);
+}
+
 template <int D, int R>
-static void launch_score(const RouteArgs& a, hipStream_t st) {
+static void launch_score_planes(const RouteArgs& a, int nlev, int64_t nodes, hipStream_t st) {
+  if (a.planes_bf16) {
+    if (a.q_bf16) launch_score_bf16<bf16_t, D, R>(a, nlev, nodes, st);
+    else launch_score_bf16<float, D, R>(a, nlev, nodes, st);
+    return;
+  }
   constexpr int NPB = 4 * (16 / R) * (R >= 8 ? ZHA_SCORE_UN_WIDE : ZHA_SCORE_UN_NARROW);   // nodes per block pass
   static const int per_cu = resident_per_cu(route_score_kernel<D, R>, 256);
   const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
-  hipLaunchKernelGGL((route_score_kernel<D, R>), dim3(grid_for(a.nlevel, NPB, cap), (unsigned)a.hkv), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((route_score_kernel<D, R>), dim3(grid_for(nodes, NPB, cap), (unsigned)a.hkv, (unsigned)nlev), dim3(256),
+                     0, st, a);
 }
 
 template <int D, int R, int B>
@@ -322,7 +462,7 @@ hipError_t launch_route_score(const RouteArgs& a, int D, int R, hipStream_t st) 
 #undef ZHA_KCASE
     return hipGetLastError();
   }
-#define ZHA_CASE(DD, RR) else if (D == DD && R == RR) launch_score<DD, RR>(a, st);
+#define ZHA_CASE(DD, RR) else if (D == DD && R == RR) launch_score_planes<DD, RR>(a, 1, a.nlevel, st);
   if (false) {}
   ZHA_CASE(64, 1) ZHA_CASE(64, 2) ZHA_CASE(64, 4) ZHA_CASE(64, 8) ZHA_CASE(64, 16)
   ZHA_CASE(128, 1) ZHA_CASE(128, 2) ZHA_CASE(128, 4) ZHA_CASE(128, 8) ZHA_CASE(128, 16)
@@ -333,13 +473,9 @@ hipError_t launch_route_score(const RouteArgs& a, int D, int R, hipStream_t st) 
 
 template <int D, int R>
 static void launch_dense_score_t(const RouteArgs& a, int nlev, hipStream_t st) {
-  constexpr int NPB = 4 * (16 / R) * (R >= 8 ? ZHA_SCORE_UN_WIDE : ZHA_SCORE_UN_NARROW);
   int64_t mx = 0;
   for (int l = a.dense_lo; l <= a.level; ++l) mx = a.nl[l] > mx ? a.nl[l] : mx;
-  static const int per_cu = resident_per_cu(route_score_kernel<D, R>, 256);
-  const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
-  hipLaunchKernelGGL((route_score_kernel<D, R>), dim3(grid_for(mx, NPB, cap), (unsigned)a.hkv, (unsigned)nlev), dim3(256),
-                     0, st, a);
+  launch_score_planes<D, R>(a, nlev, mx, st);
 }
 
 hipError_t launch_route_dense_score(const RouteArgs& a, int D, int R, hipStream_t st) {

@@ -106,6 +106,8 @@ zha_status validate(const zha_config* c) {
   if (c->dtype != ZHA_F32 && c->dtype != ZHA_BF16) return fail(ZHA_E_INVALID, "dtype %d", c->dtype);
   if (!(c->top_p > 0.f && c->top_p <= 1.f)) return fail(ZHA_E_INVALID, "top_p %g outside (0, 1]", c->top_p);
   if (c->keep_sink != 0 && c->keep_sink != 1) return fail(ZHA_E_INVALID, "keep_sink %d", c->keep_sink);
+  if (c->plane_dtype != ZHA_F32 && c->plane_dtype != ZHA_BF16)
+    return fail(ZHA_E_INVALID, "plane_dtype %d", c->plane_dtype);
   if (c->dtype == ZHA_F32 && c->head_dim == 128 && c->block > 128)
     return fail(ZHA_E_UNSUPPORTED, "float32 keys with head_dim 128 need block <= 128");
   return ZHA_OK;
@@ -142,6 +144,8 @@ size_t layout(const zha_config& c, char* base, Dev* dev) {
     }
   }
   if (key_form(c)) d.w1 = (float*)take((size_t)(H * d.ncap[1] * R * c.block) * 4);
+  if (c.plane_dtype == ZHA_BF16)
+    for (int l = key_form(c) ? 2 : 1; l <= L; ++l) d.sq[l] = (bf16_t*)take((size_t)(H * d.ncap[l] * R * D) * 2);
   d.cnt = (int32_t*)take((size_t)((MAXL + 1) * H) * 4);
   d.qs = (QState*)take((size_t)((L + 1) * Q) * sizeof(QState));
   d.hpart = (uint64_t*)take((size_t)(H * SEL_P * GMAX * NB1) * 8);
@@ -176,6 +180,8 @@ RouteArgs route_args(const zha_tree* t, const void* q) {
   a.top_p = t->cfg.top_p;
   a.sigma = 1.0f / sqrtf((float)t->cfg.head_dim);
   a.key_form = key_form(t->cfg) ? 1 : 0;
+  a.q_bf16 = t->cfg.dtype == ZHA_BF16 ? 1 : 0;
+  a.planes_bf16 = t->cfg.plane_dtype == ZHA_BF16 ? 1 : 0;
   a.K = t->K;
   a.kcap = t->cfg.capacity;
   for (int l = 1; l <= t->cfg.levels; ++l) a.nl[l] = nodes_at(t->cfg, l, t->N);
@@ -454,6 +460,23 @@ zha_status zha_debug_level(zha_tree* t, int32_t level, float* s_out, float* c_ou
       e = hipMemcpyAsync((char*)c_out + kv * n * crow, (char*)t->dev.c[level] + kv * cap * crow, n * crow,
                          hipMemcpyDeviceToDevice, stream);
     if (e != hipSuccess) return hip_fail(e, "level copy");
+  }
+  return ZHA_OK;
+}
+
+zha_status zha_debug_router_planes(zha_tree* t, int32_t level, void* s_out, hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!t->built) return fail(ZHA_E_STATE, "no tree built");
+  if (level < 1 || level > t->cfg.levels) return fail(ZHA_E_INVALID, "level %d outside 1..%d", level, t->cfg.levels);
+  if (!s_out) return fail(ZHA_E_INVALID, "null output");
+  if (!t->dev.sq[level]) return fail(ZHA_E_INVALID, "no bf16 router planes at level %d", level);
+  const zha_config& c = t->cfg;
+  const int64_t n = nodes_at(c, level, t->N), cap = t->dev.ncap[level];
+  const size_t srow = (size_t)c.num_ref * c.head_dim * 2;
+  for (int kv = 0; kv < c.num_kv_heads; ++kv) {
+    hipError_t e = hipMemcpyAsync((char*)s_out + kv * n * srow, (char*)t->dev.sq[level] + kv * cap * srow, n * srow,
+                                  hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "router plane copy");
   }
   return ZHA_OK;
 }

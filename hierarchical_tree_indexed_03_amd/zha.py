@@ -32,7 +32,8 @@ class zha_config(ctypes.Structure):
                 ("num_q_heads", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("levels", ctypes.c_int32), ("num_ref", ctypes.c_int32),
                 ("capacity", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("top_p", ctypes.c_float), ("keep_sink", ctypes.c_int32)]
+                ("top_p", ctypes.c_float), ("keep_sink", ctypes.c_int32),
+                ("plane_dtype", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -49,6 +50,7 @@ def _load() -> ctypes.CDLL:
         "zha_decode": (I32, [P, P, P, P, P]),
         "zha_decode_dense": (I32, [P, P, P, P]),
         "zha_debug_level": (I32, [P, I32, P, P, P]),
+        "zha_debug_router_planes": (I32, [P, I32, P, P]),
         "zha_debug_trace": (I32, [P, I32, I64, P, P, P, P, P, P]),
         "zha_debug_route_level": (I32, [P, I32, P, P, P, P, I64, P]),
         "zha_profile_start": (I32, [P, ctypes.c_char_p]),
@@ -66,7 +68,7 @@ def _load() -> ctypes.CDLL:
 
 _lib = _load()
 EXPORTED = ("zha_workspace_bytes", "zha_level1_key_form", "zha_create", "zha_tree_build", "zha_tree_append", "zha_decode",
-            "zha_decode_dense", "zha_debug_level", "zha_debug_trace", "zha_debug_route_level",
+            "zha_decode_dense", "zha_debug_level", "zha_debug_router_planes", "zha_debug_trace", "zha_debug_route_level",
             "zha_profile_start", "zha_profile_stop", "zha_num_tokens", "zha_destroy", "zha_status_string",
             "zha_last_error")
 
@@ -92,11 +94,14 @@ def _check(status: int):
         raise ZhaError(status, (_lib.zha_last_error() or b"").decode())
 
 
+def _dtype(x) -> int:
+    return x if isinstance(x, int) else (ZHA_BF16 if x in ("bf16", torch.bfloat16) else ZHA_F32)
+
+
 def make_config(head_dim, num_kv_heads, num_q_heads, block, levels, num_ref, capacity, dtype, top_p,
-                keep_sink=True) -> zha_config:
-    dt = dtype if isinstance(dtype, int) else (ZHA_BF16 if dtype in ("bf16", torch.bfloat16) else ZHA_F32)
-    return zha_config(head_dim, num_kv_heads, num_q_heads, block, levels, num_ref, capacity, dt,
-                      float(top_p), int(bool(keep_sink)))
+                keep_sink=True, planes="f32") -> zha_config:
+    return zha_config(head_dim, num_kv_heads, num_q_heads, block, levels, num_ref, capacity, _dtype(dtype),
+                      float(top_p), int(bool(keep_sink)), _dtype(planes))
 
 
 def zha_level1_key_form(cfg: zha_config) -> int:
@@ -131,6 +136,10 @@ def zha_decode_dense(t, q, out, stream=None):
 
 def zha_debug_level(t, level: int, s_out, c_out, stream=None):
     _check(_lib.zha_debug_level(t, int(level), _p(s_out), _p(c_out), _s(stream)))
+
+
+def zha_debug_router_planes(t, level: int, s_out, stream=None):
+    _check(_lib.zha_debug_router_planes(t, int(level), _p(s_out), _s(stream)))
 
 
 def zha_debug_trace(t, level: int, cap: int, nodes, masks, scores, keep, counts, stream=None):
@@ -218,6 +227,14 @@ class Tree:
         cc = torch.empty(c.num_kv_heads, n, c.num_ref, dtype=torch.float32, device=self.workspace.device)
         zha_debug_level(self.handle, level, s, cc)
         return s, cc
+
+    def router_planes(self, level: int):
+        """The bf16 copy of s that routing reads at ``level`` ([Hkv, n, R, d] bfloat16)."""
+        c = self.cfg
+        s = torch.empty(c.num_kv_heads, self.nodes(level), c.num_ref, c.head_dim, dtype=torch.bfloat16,
+                        device=self.workspace.device)
+        zha_debug_router_planes(self.handle, level, s)
+        return s
 
     def trace(self, level: int):
         """Routing trace of the last decode at ``level`` (0 = kept level-1 blocks): per KV

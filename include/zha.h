@@ -22,7 +22,8 @@
  *     synchronises a stream, except where a call says so.
  *   - Tensors are dense, row-major, with the shapes given.  `dtype` (zha_dtype) fixes the
  *     element type of K, V, reference queries and decode queries: float32 or bfloat16.
- *     Tree planes and outputs are float32.
+ *     Tree planes and outputs are float32 (plus optional bfloat16 router copies of s,
+ *     see zha_config.plane_dtype).
  *   - Every call validates its arguments on the host before enqueueing any work; on any
  *     error it returns a non-zero zha_status, enqueues nothing and leaves the handle
  *     unchanged.  zha_last_error() then describes the failure (thread-local string).
@@ -64,6 +65,14 @@ typedef struct {
   int32_t dtype;          /* zha_dtype of K, V, reference and decode queries            */
   float top_p;            /* p in (0, 1]; p = 1 keeps every node (dense attention)     */
   int32_t keep_sink;      /* 1: token 0 is always attended                              */
+  int32_t plane_dtype;    /* zha_dtype of the s vectors the router reads (0 = float32).
+                           * ZHA_BF16: the tree is still built and kept in float32; each
+                           * plane the router scores from also gets a bfloat16 copy of s
+                           * (nearest value, ties to even) and routing reads that copy with
+                           * the float32 offset c_j, halving the plane bytes per node.  The
+                           * pages give no storage precision for the planes; this is a
+                           * stated quantiser.  A level-1 scored from the keys (see
+                           * zha_level1_key_form) reads no planes and keeps no copy.      */
 } zha_config;
 
 typedef struct zha_tree zha_tree;   /* opaque host-side handle */
@@ -123,6 +132,12 @@ zha_status zha_decode_dense(zha_tree* t, const void* q, float* out, hipStream_t 
  *   n_l = ceil(N / block^level).  Enqueued copies only (no synchronisation). */
 zha_status zha_debug_level(zha_tree* t, int32_t level, float* s_out, float* c_out,
                            hipStream_t stream);
+
+/* Copies the bfloat16 copy of s that routing reads at level `level` (bf16 router planes):
+ *   s_out (device) bfloat16 [Hkv][n_l][R][d].  ZHA_E_INVALID if the handle keeps no such
+ *   copy at that level (float32 router planes, or a level 1 scored from the keys).
+ *   Enqueued copies only (no synchronisation). */
+zha_status zha_debug_router_planes(zha_tree* t, int32_t level, void* s_out, hipStream_t stream);
 
 /* Routing trace of the last zha_decode / zha_debug_route_level on this handle, for level
  * `level` (levels..1; 0 = the kept level-1 blocks).  Copies into caller device buffers

@@ -7,6 +7,13 @@ Tolerances (stated once here, used by every GPU test):
     within the score tolerance (1e-4) of the boundary node's score (a near tie may swap
     order); end to end, the descendants of such a node are excluded from later levels;
   * outputs: max|o_gpu - o_ref| <= 1e-2 * max|o_ref| (bf16 inputs, fp32 accumulation).
+
+bf16 router planes: the oracle routes over its planes with s rounded to bf16 (oracle
+``quantise_planes``) at the levels the router reads planes at.  The GPU rounds its fp32 s,
+which lies within S_BAND of the oracle's fp64 s (checked element by element); an element
+of s within S_BAND of a bf16 rounding midpoint may round either way on the two sides.
+Each node's score tolerance therefore adds sigma * max_j sum_i |q_i| (hi_ji - lo_ji), hi and
+lo the roundings of s +- S_BAND (zero for every element away from a midpoint).
 """
 from __future__ import annotations
 
@@ -19,6 +26,7 @@ from workloads import configs as wc, gen
 SCORE_TOL = 1e-4
 BAND = 1e-5
 OUT_RTOL = 1e-2
+S_BAND = 1e-5
 
 
 def torch_dtype(w: wc.Workload):
@@ -28,8 +36,42 @@ def torch_dtype(w: wc.Workload):
 def make_tree(w: wc.Workload, top_p=None, capacity=None):
     from hierarchical_tree_indexed_03_amd import zha
     cfg = zha.make_config(w.head_dim, w.num_kv_heads, w.num_q_heads, w.block, w.levels, w.num_ref,
-                          capacity or w.capacity, w.dtype, w.top_p if top_p is None else top_p, w.keep_sink)
+                          capacity or w.capacity, w.dtype, w.top_p if top_p is None else top_p, w.keep_sink,
+                          w.planes)
     return zha.Tree(cfg)
+
+
+def key_form(w: wc.Workload) -> bool:
+    """Level 1 scored from its block's keys and the planes' token weights: bf16 keys, b in
+    {2, 4, 8, 16}, and b keys plus R x b fp32 weights take fewer bytes than R fp32 planes
+    (the library's rule, which test_abi checks through zha_level1_key_form)."""
+    return (w.dtype == "bf16" and w.block in (2, 4, 8, 16)
+            and w.block * w.head_dim * 2 + w.num_ref * w.block * 4 < w.num_ref * w.head_dim * 4)
+
+
+def router_levels(w: wc.Workload) -> list:
+    """Levels whose planes the router reads (all but a key-form level 1)."""
+    return [lv for lv in range(1, w.levels + 1) if not (lv == 1 and key_form(w))]
+
+
+def router_trees(w: wc.Workload, trees: list) -> list:
+    """The oracle trees as the router sees them: with bf16 router planes, s rounded to bf16
+    at the levels the router reads planes at."""
+    if w.planes != "bf16":
+        return trees
+    lv = router_levels(w)
+    return [zo.quantise_planes(t, lv) for t in trees]
+
+
+def flip_allowance(w: wc.Workload, tree, level: int, nodes, q) -> np.ndarray:
+    """Extra score tolerance per node for bf16 router planes (see the module docstring);
+    zero for f32 planes and for a key-form level 1.  ``tree`` is the full-precision tree."""
+    nodes = np.asarray(nodes, dtype=np.int64)
+    if w.planes != "bf16" or level not in router_levels(w):
+        return np.zeros(len(nodes))
+    s = tree.levels[level - 1][0][nodes]
+    gap = zo.bf16_round(s + S_BAND) - zo.bf16_round(s - S_BAND)
+    return np.max(gap @ np.abs(np.asarray(q, dtype=np.float64)), axis=1) / np.sqrt(len(q))
 
 
 def upload(x: np.ndarray, w: wc.Workload) -> torch.Tensor:
@@ -64,8 +106,10 @@ def gpu_scores(trace_level: dict, gi: int) -> dict:
     return dict(zip(nodes.tolist(), sc.tolist()))
 
 
-def exempt_nodes(rec: dict, p: float, diff: np.ndarray) -> tuple[list, list]:
-    """Split mismatching nodes into (exempt, failing) per the tolerance rule above."""
+def exempt_nodes(rec: dict, p: float, diff: np.ndarray, tol=None) -> tuple[list, list]:
+    """Split mismatching nodes into (exempt, failing) per the tolerance rule above.  ``tol``:
+    per-frontier-node score tolerance (default SCORE_TOL); a near tie allows the sum of the
+    node's and the boundary node's tolerances."""
     frontier = rec["frontier"]
     pos = {int(n): i for i, n in enumerate(frontier)}
     order = rec["order"]
@@ -73,21 +117,24 @@ def exempt_nodes(rec: dict, p: float, diff: np.ndarray) -> tuple[list, list]:
     rank[order] = np.arange(len(order))
     cum_before = rec["cum_before"]                 # in rank order
     k = rec["k"]
+    tol = np.full(len(frontier), SCORE_TOL) if tol is None else np.asarray(tol)
     boundary_score = rec["scores"][order[k - 1]] if k > 0 else np.inf
+    boundary_tol = tol[order[k - 1]] if k > 0 else 0.0
     ok, bad = [], []
     for n in diff.tolist():
         i = pos[n]
         cb = cum_before[rank[i]]
-        if abs(cb - p) <= BAND or abs(rec["scores"][i] - boundary_score) <= SCORE_TOL:
+        if abs(cb - p) <= BAND or abs(rec["scores"][i] - boundary_score) <= tol[i] + boundary_tol:
             ok.append(n)
         else:
             bad.append((n, float(cb), float(rec["scores"][i] - boundary_score)))
     return ok, bad
 
 
-def compare_route(route: dict, trace: dict, gi: int, b: int, p: float) -> dict:
+def compare_route(route: dict, trace: dict, gi: int, b: int, p: float, tol_fn=None) -> dict:
     """End-to-end set comparison of one query head.  ``trace[level]`` is the GPU trace of
-    that level for the head's KV head (level 0 = kept blocks).  Returns a report dict;
+    that level for the head's KV head (level 0 = kept blocks).  ``tol_fn(level, frontier)``
+    gives per-node score tolerances (default SCORE_TOL).  Returns a report dict;
     report["bad"] lists unexplained mismatches."""
     excluded = set()
     bad, exempt, n_levels = [], [], len(route["levels"])
@@ -102,7 +149,8 @@ def compare_route(route: dict, trace: dict, gi: int, b: int, p: float) -> dict:
         k_o = set(rec["kept"].tolist()) - excluded
         k_g = set(gpu_kept(tl, gi).tolist()) - excluded
         diff = np.array(sorted(k_o ^ k_g), dtype=np.int64)
-        ok, nb = exempt_nodes(rec, p, diff)
+        tol = None if tol_fn is None else tol_fn(lv, rec["frontier"])
+        ok, nb = exempt_nodes(rec, p, diff, tol)
         exempt += [(lv, n) for n in ok]
         bad += [("kept", lv) + x for x in nb]
         nxt = set()

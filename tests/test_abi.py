@@ -48,7 +48,7 @@ BAD = [
     (dict(num_q_heads=4 * 9), 2), (dict(block=1), 1), (dict(block=257), 1), (dict(levels=0), 1),
     (dict(levels=17), 1), (dict(num_ref=3), 2), (dict(capacity=0), 1), (dict(capacity=1 << 31), 1),
     (dict(dtype=5), 1), (dict(top_p=0.0), 1), (dict(top_p=1.5), 1), (dict(top_p=float("nan")), 1),
-    (dict(dtype="f32", block=256), 2),
+    (dict(dtype="f32", block=256), 2), (dict(planes=2), 1), (dict(planes=-1), 1),
 ]
 
 
@@ -98,6 +98,29 @@ def test_level1_key_form_choice(zha):
     assert ws_key > ws_f32
 
 
+def test_bf16_router_planes_workspace(zha):
+    """bf16 router planes add one bf16 copy of s per level the router reads planes at: every
+    level but a key-form level 1 (whose planes the router never reads)."""
+    D, H, cap = 128, 4, 1 << 18
+
+    def planes_bytes(levels, b, R):
+        # per-level node capacity rounded to 64 nodes, R x d bf16 per node, 256-byte slots
+        tot = 0
+        for lv in levels:
+            n = -(-cap // b ** lv)
+            n = -(-n // 64) * 64
+            tot += -(-(H * n * R * D * 2) // 256) * 256
+        return tot
+    # key-form level 1 (bf16, b 4, R 16): levels 2..6 get a copy
+    f = zha.zha_workspace_bytes(good(zha))
+    q = zha.zha_workspace_bytes(good(zha, planes="bf16"))
+    assert q - f == planes_bytes(range(2, 7), 4, 16)
+    # planes read at level 1 too (b 8, R 1)
+    f = zha.zha_workspace_bytes(good(zha, block=8, num_ref=1, levels=7))
+    q = zha.zha_workspace_bytes(good(zha, block=8, num_ref=1, levels=7, planes="bf16"))
+    assert q - f == planes_bytes(range(1, 8), 8, 1)
+
+
 def test_call_order_and_arguments(zha):
     """Handle created on a fake (never dereferenced) address: every call below must fail
     validation on the host and leave the handle as it was."""
@@ -110,6 +133,7 @@ def test_call_order_and_arguments(zha):
             (lambda: zha.zha_decode_dense(t, fake, fake), 5),
             (lambda: zha.zha_tree_append(t, fake, fake), 5),
             (lambda: zha.zha_debug_level(t, 1, fake, fake), 5),
+            (lambda: zha.zha_debug_router_planes(t, 2, fake), 5),
             (lambda: zha.zha_tree_build(t, fake, fake, 1001, fake), 3),
             (lambda: zha.zha_tree_build(t, fake, fake, 0, fake), 1),
             (lambda: zha.zha_tree_build(t, None, fake, 10, fake), 1),

@@ -1,0 +1,163 @@
+"""GPU parity of bf16 router planes (zha_config.plane_dtype = bf16) against the oracle.
+
+The oracle routes over its planes with s rounded to bf16 at every level the router reads
+planes at (all but a key-form level 1); offsets stay full precision.  Checked here:
+
+* the quantiser, element by element: the GPU's fp32 s lies within S_BAND of the oracle's
+  fp64 s, and the GPU's bf16 copy equals the oracle's rounding of s wherever the rounding
+  of s - S_BAND and s + S_BAND agree (else it lies between those two roundings);
+* teacher-forced scores on the oracle's frontiers, within SCORE_TOL plus each node's
+  rounding-flip allowance, and the kept sets (tests/parity.py rules);
+* decode end to end after appends (the append refreshes the bf16 copies).
+
+Geometries: f32 queries (fp32 MFMA on widened planes), the deep tree (key-form level 1,
+bf16 planes above it, selected top-down), one 256-key level (R 16), the light router
+(R 1) top-down and through the large-level path, and the 16M geometry at a small size.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import parity as P
+from oracle import zha_oracle as zo
+from workloads import configs as wc, gen
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny": wc.TINY.with_(planes="bf16"),
+    "deep_small": wc.DEEP.with_(n_tokens=16_384 + 37, steps=2, planes="bf16"),
+    "wide_small": wc.WIDE.with_(n_tokens=8_192 + 100, steps=2, planes="bf16"),
+    "light_small": wc.light(32_768, steps=2).with_(n_tokens=32_768 - 5, planes="bf16"),
+    # level 1 holds 36,001 nodes: scored from the union list, selected by the large-level path
+    "light_general": wc.light(288_003, steps=1).with_(num_kv_heads=1, num_q_heads=8, planes="bf16"),
+    "ultra_small": wc.ULTRA.with_(n_tokens=70_001, steps=2, planes="bf16"),
+}
+
+
+class Case:
+    def __init__(self, w: wc.Workload):
+        self.w = w
+        self.p = w.top_p
+        self.K, self.V, self.refs = P.host_inputs(w)
+        self.trees = P.oracle_trees(w, self.K, self.refs, w.n_tokens)
+        self.t = P.make_tree(w)
+        self.Kd, self.Vd = P.upload(self.K, w), P.upload(self.V, w)
+        self.t.build(self.Kd, self.Vd, w.n_tokens, P.upload(self.refs, w))
+        self.n = w.n_tokens
+
+    def append(self):
+        w, n = self.w, self.n
+        self.t.append(self.Kd[:, n].contiguous(), self.Vd[:, n].contiguous())
+        for h in range(w.num_kv_heads):
+            zo.append_token(self.trees[h], self.K[h, n])
+        self.n += 1
+
+    def queries(self, step):
+        return gen.step_queries(self.w, step, self.n, gen.host_fetch(self.K))
+
+    def tol_fn(self, kv, q):
+        tree = self.trees[kv]
+        return lambda lv, fr: P.SCORE_TOL + P.flip_allowance(self.w, tree, lv, fr, q)
+
+
+_CACHE = {}
+
+
+def case(name) -> Case:
+    if name not in _CACHE:
+        _CACHE.clear()
+        _CACHE[name] = Case(SMALL[name])
+    return _CACHE[name]
+
+
+def check_quantiser(c: Case):
+    w = c.w
+    for lv in range(1, w.levels + 1):
+        if lv not in P.router_levels(w):
+            from hierarchical_tree_indexed_03_amd import zha
+            with pytest.raises(zha.ZhaError):
+                c.t.router_planes(lv)
+            continue
+        s32 = c.t.level(lv)[0].cpu().numpy().astype(np.float64)
+        sq = c.t.router_planes(lv).float().cpu().numpy().astype(np.float64)
+        for h in range(w.num_kv_heads):
+            so = c.trees[h].levels[lv - 1][0]
+            err = float(np.max(np.abs(s32[h] - so)))
+            assert err <= P.S_BAND, f"level {lv} head {h}: fp32 s differs from the oracle by {err:.2e}"
+            lo, hi, mid = zo.bf16_round(so - P.S_BAND), zo.bf16_round(so + P.S_BAND), zo.bf16_round(so)
+            sure = lo == hi
+            assert np.array_equal(sq[h][sure], mid[sure]), f"level {lv} head {h}: bf16 copy differs"
+            # rounding is monotone: s_gpu within S_BAND of s rounds into [lo, hi]
+            assert np.all((sq[h] >= lo) & (sq[h] <= hi)), f"level {lv} head {h}: bf16 copy outside [lo, hi]"
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_router_planes_quantiser(name):
+    check_quantiser(case(name))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_teacher_forced_scores_and_sets(name):
+    c = case(name)
+    w = c.w
+    g = w.group
+    q = c.queries(100)
+    rt = P.router_trees(w, c.trees)
+    routes = [zo.route(rt[h // g], q[h], c.p, w.keep_sink) for h in range(w.num_q_heads)]
+    qd = P.upload(q, w)
+    for li in range(w.levels):
+        lv = w.levels - li
+        fronts = []
+        for kv in range(w.num_kv_heads):
+            fr = {}
+            for gi in range(g):
+                for n in routes[kv * g + gi]["levels"][li]["frontier"].tolist():
+                    fr[n] = fr.get(n, 0) | (1 << gi)
+            nodes = np.array(sorted(fr), dtype=np.int64)
+            fronts.append((nodes, np.array([fr[n] for n in nodes.tolist()], dtype=np.int64)))
+        tr = c.t.route_level(lv, qd, fronts)
+        for h in range(w.num_q_heads):
+            kv, gi = divmod(h, g)
+            rec = routes[h]["levels"][li]
+            gs = P.gpu_scores(tr[kv], gi)
+            sg = np.array([gs[n] for n in rec["frontier"].tolist()])
+            tol = c.tol_fn(kv, q[h])(lv, rec["frontier"])
+            over = np.abs(sg - rec["scores"]) - tol
+            assert np.all(over <= 0), (f"level {lv} head {h}: score error beyond tolerance by "
+                                       f"{float(np.max(over)):.3e}")
+            kept = P.gpu_kept(tr[kv], gi)
+            diff = np.array(sorted(set(kept.tolist()) ^ set(rec["kept"].tolist())), dtype=np.int64)
+            _, bad = P.exempt_nodes(rec, c.p, diff, tol)
+            assert not bad, f"level {lv} head {h}: unexplained set mismatch {bad[:5]}"
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_end_to_end(name):
+    c = case(name)
+    w = c.w
+    g = w.group
+    for step in range(max(1, w.steps)):
+        if w.appends and w.steps:
+            c.append()
+        q = c.queries(step)
+        o = c.t.decode(P.upload(q, w))
+        torch.cuda.synchronize()
+        o = o.cpu().numpy()
+        traces = {lv: c.t.trace(lv) for lv in range(0, w.levels + 1)}
+        o_ref, routes = zo.decode(P.router_trees(w, c.trees), c.V, q, c.p, w.keep_sink, return_routes=True)
+        for h in range(w.num_q_heads):
+            kv, gi = divmod(h, g)
+            tr = {lv: traces[lv][kv] for lv in traces}
+            rep = P.compare_route(routes[h], tr, gi, w.block, c.p, c.tol_fn(kv, q[h]))
+            assert not rep["bad"], f"step {step} head {h}: {rep['bad'][:5]}"
+            toks = P.gpu_tokens(tr[0], gi, w.block, c.n, w.keep_sink)
+            e1 = P.out_err(o[h], zo.attend(c.K[kv][:c.n], c.V[kv][:c.n], q[h], toks))
+            assert e1 <= P.OUT_RTOL, f"step {step} head {h}: attention over the GPU set err {e1:.3e}"
+            if not rep["exempt"]:
+                e2 = P.out_err(o[h], o_ref[h])
+                assert e2 <= P.OUT_RTOL, f"step {step} head {h}: output err {e2:.3e}"
+    # the appended rows' bf16 copies follow the refreshed planes
+    check_quantiser(c)

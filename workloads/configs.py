@@ -44,6 +44,7 @@ class Workload:
     plant_max: int = 16
     plant_scale: float = 4.0  # |q| before noise = plant_scale * sqrt(head_dim)
     noise: bool = True       # add N(0, I) to the planted query
+    planes: str = "f32"      # storage of the s vectors the router reads: "f32" or "bf16"
 
     @property
     def group(self) -> int:
