@@ -171,13 +171,124 @@ template <int D> struct PlaneRow<float, D> {
   }
 };
 
-// Scores from the bf16 copies of s: the tile S = P (16 plane rows x D) . Q^T (D x 16 heads)
-// on MFMA against the raw query (bf16 x bf16 products are exact in the fp32 accumulator;
-// fp32 queries take the fp32 MFMA), then sigma * S + c_j.  Lane (head col, group kg) holds
-// rows 4kg..4kg+3 for head col; a node's R rows lie in-lane (R <= 4) or across the
-// lane groups kg (R = 8, 16), so the max over planes is in-lane then cross-lane.
+// Scores from the bf16 copies of s: the tile Q (16 heads x D) . P^T (D x 16 plane rows) on
+// MFMA with the raw query as the A operand (bf16 x bf16 products are exact in the fp32
+// accumulator; fp32 queries take the fp32 MFMA on planes widened to fp32), then
+// sigma * acc + c_j.  Plane row c = (node slot c / R, plane c % R).  A lane (column col,
+// group kg) loads row col and receives that row's scores for heads 4kg..4kg+3, so a node's
+// id, offset and head mask are read by the lanes that read its planes; the max over a
+// node's R planes runs across R neighbouring lanes.  The next pass's node ids and masks are
+// loaded before this pass's planes.
 template <typename TQ, int D, int R>
 __global__ __launch_bounds__(256) void route_score_bf16_kernel(RouteArgs a) {
+  constexpr int NPT = 16 / R;                 // nodes per 16-row tile
+  constexpr int UN = ZHA_SCORE_UN_BF16;       // tiles in flight per wave
+  constexpr int NL = PlaneRow<TQ, D>::NL;
+  __shared__ float red[4][16];
+  const int kv = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int slot = col / R, plane = col % R;
+  const bool dense = a.dense != 0;            // every node of the level, no list
+  const int lv = dense ? a.level - (int)blockIdx.z : a.level;
+  const int64_t cnt = dense ? a.nl[lv] : a.dev.cnt[lv * a.hkv + kv];
+  const int64_t cap = a.dev.ncap[lv];
+  const int32_t* nodes = a.dev.node[lv] + kv * cap;
+  const uint32_t* masks = a.dev.mask[lv] + kv * cap;
+  const bf16_t* S = a.dev.sq[lv] + (int64_t)kv * cap * R * D;
+  const float* C = a.dev.c[lv] + (int64_t)kv * cap * R;
+  float* out = a.dev.score[lv] + (int64_t)kv * GMAX * cap;
+  const int g = a.g;
+  const float sigma = a.sigma;
+
+  // the A operand: head col's query, slice kg of the permuted contraction (zero past g)
+  Qk<TQ, D> qk;
+  qk.load_q((const TQ*)a.q + (int64_t)kv * g * D, g, col, kg);
+  float runmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // heads 4kg..4kg+3
+
+  const int64_t ntiles = (cnt + NPT - 1) / NPT;
+  const int64_t tstride = (int64_t)gridDim.x * 4 * UN;
+  int32_t nid[UN];                            // the lane's node per tile of the pass; -1 none
+  uint32_t nmk[UN];
+  auto load_ids = [&](int64_t t0, int32_t (&nd)[UN], uint32_t (&mk)[UN]) {
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int64_t e = (t0 + u) * NPT + slot;
+      const bool ok = (t0 + u) < ntiles && e < cnt;
+      nd[u] = ok ? (dense ? (int32_t)e : nodes[e]) : -1;
+      mk[u] = (ok && !dense) ? masks[e] : 0u;   // dense: the max is taken later
+    }
+  };
+  const int64_t tfirst = ((int64_t)blockIdx.x * 4 + wave) * UN;
+  if (tfirst < ntiles) load_ids(tfirst, nid, nmk);
+  for (int64_t t0 = tfirst; t0 < ntiles; t0 += tstride) {
+    int32_t ncur[UN];
+    uint32_t mcur[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) { ncur[u] = nid[u]; mcur[u] = nmk[u]; }
+    if (t0 + tstride < ntiles) load_ids(t0 + tstride, nid, nmk);
+    uint4 kf[UN][NL];
+    float cj[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const bool ok = ncur[u] >= 0;
+      const int64_t nd = ok ? ncur[u] : 0;
+      PlaneRow<TQ, D>::load(S + (nd * R + plane) * D, kg, ok, kf[u]);
+      cj[u] = ok ? C[nd * R + plane] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (sizeof(TQ) == 2) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qk.q[i], __builtin_bit_cast(bf16x8, kf[u][i]), acc, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qk.q[4 * i + 0], __uint_as_float(kf[u][i].x), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qk.q[4 * i + 1], __uint_as_float(kf[u][i].y), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qk.q[4 * i + 2], __uint_as_float(kf[u][i].z), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qk.q[4 * i + 3], __uint_as_float(kf[u][i].w), acc, 0, 0, 0);
+        }
+      }
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = sigma * acc[e] + cj[u];
+#pragma unroll
+      for (int off = 1; off < R; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], __shfl_xor(v[e], off));
+      const int64_t ent = (t0 + u) * NPT + slot;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int h = kg * 4 + e;
+        if (ncur[u] >= 0 && plane == 0 && h < g) out[(int64_t)h * cap + ent] = v[e];
+        if ((mcur[u] >> h) & 1u) runmax[e] = fmaxf(runmax[e], v[e]);
+      }
+    }
+  }
+  // per-head max: lanes of one 16-lane row share kg, i.e. the heads 4kg..4kg+3
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v = runmax[e];
+    for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (col == 0) red[wave][kg * 4 + e] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < g) {
+    const int gi = threadIdx.x;
+    const float m = fmaxf(fmaxf(red[0][gi], red[1][gi]), fmaxf(red[2][gi], red[3][gi]));
+    if (m > -INFINITY) atomicMax(&a.dev.qs[lv * a.hq + kv * g + gi].maxkey, f2key(m));
+  }
+}
+
+
+// The same scores with the tile transposed, S = P (16 plane rows x D) . Q^T (D x 16 heads):
+// lane (head col, group kg) holds rows 4kg..4kg+3 for head col, so with R >= 4 a node's
+// planes come four to a lane and the max over planes is three in-lane steps and R/8
+// cross-lane ones (R 16: 2 shuffles per head value instead of 4).  Used for R >= 8.
+template <typename TQ, int D, int R>
+__global__ __launch_bounds__(256) void route_score_bf16_rows_kernel(RouteArgs a) {
   constexpr int NPT = 16 / R;                 // nodes per 16-row tile
   constexpr int UN = ZHA_SCORE_UN_BF16;       // tiles in flight per wave
   constexpr int NL = Qk<TQ, D>::NL;
@@ -421,10 +532,17 @@ hipError_t launch_route_prep(const RouteArgs& a, bool bf16, int D, hipStream_t s
 template <typename TQ, int D, int R>
 static void launch_score_bf16(const RouteArgs& a, int nlev, int64_t nodes, hipStream_t st) {
   constexpr int NPB = 4 * (16 / R) * ZHA_SCORE_UN_BF16;   // nodes per block pass
-  static const int per_cu = resident_per_cu(route_score_bf16_kernel<TQ, D, R>, 256);
-  const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
-  hipLaunchKernelGGL((route_score_bf16_kernel<TQ, D, R>), dim3(grid_for(nodes, NPB, cap), (unsigned)a.hkv, (unsigned)nlev),
-                     dim3(256), 0, st, a);
+  if constexpr (R >= 8) {
+    static const int per_cu = resident_per_cu(route_score_bf16_rows_kernel<TQ, D, R>, 256);
+    const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
+    hipLaunchKernelGGL((route_score_bf16_rows_kernel<TQ, D, R>), dim3(grid_for(nodes, NPB, cap), (unsigned)a.hkv, (unsigned)nlev),
+                       dim3(256), 0, st, a);
+  } else {
+    static const int per_cu = resident_per_cu(route_score_bf16_kernel<TQ, D, R>, 256);
+    const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
+    hipLaunchKernelGGL((route_score_bf16_kernel<TQ, D, R>), dim3(grid_for(nodes, NPB, cap), (unsigned)a.hkv, (unsigned)nlev),
+                       dim3(256), 0, st, a);
+  }
 }
 
 template <int D, int R>

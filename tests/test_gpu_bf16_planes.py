@@ -10,7 +10,7 @@ planes at (all but a key-form level 1); offsets stay full precision.  Checked he
   rounding-flip allowance, and the kept sets (tests/parity.py rules);
 * decode end to end after appends (the append refreshes the bf16 copies).
 
-Geometries: f32 queries (fp32 MFMA on widened planes), the deep tree (key-form level 1,
+Geometries: f32 queries (fp32 MFMA on widened planes; R 4 and R 16), the deep tree (key-form level 1,
 bf16 planes above it, selected top-down), one 256-key level (R 16), the light router
 (R 1) top-down and through the large-level path, and the 16M geometry at a small size.
 """
@@ -28,6 +28,7 @@ pytestmark = pytest.mark.gpu
 
 SMALL = {
     "tiny": wc.TINY.with_(planes="bf16"),
+    "tiny_r16": wc.TINY.with_(num_ref=16, planes="bf16"),
     "deep_small": wc.DEEP.with_(n_tokens=16_384 + 37, steps=2, planes="bf16"),
     "wide_small": wc.WIDE.with_(n_tokens=8_192 + 100, steps=2, planes="bf16"),
     "light_small": wc.light(32_768, steps=2).with_(n_tokens=32_768 - 5, planes="bf16"),
