@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="deep", help="deep | wide | ultra | light_<N> | tiny")
     ap.add_argument("--planes", default="f32", choices=("f32", "bf16"),
                     help="storage of the s vectors the router reads (bf16: a rounded copy)")
+    ap.add_argument("--no-bf16-planes", action="store_true",
+                    help="skip the secondary measurement with bf16 router planes")
     ap.add_argument("--build-reps", type=int, default=3)
     ap.add_argument("--dense-reps", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -444,6 +446,70 @@ def main():
     dense_bytes = tree.n_tokens * w.num_kv_heads * 2 * d * 2
     log(f"[bench] dense decode {dense_ms:.3f} ms ({dense_bytes / dense_ms / 1e6:.0f} GB/s)")
 
+    # ---- the same warm steps with bf16 router planes: a second tree over the same caches
+    # (its appends rewrite rows n0.. with the values they already hold)
+    bf16_planes = None
+    if w.planes == "f32" and not args.no_bf16_planes:
+        w2 = w.with_(planes="bf16")
+        cfg2 = zha.make_config(w.head_dim, w.num_kv_heads, w.num_q_heads, w.block, w.levels, w.num_ref,
+                               w.capacity, w.dtype, w.top_p, w.keep_sink, "bf16")
+        tree2 = zha.Tree(cfg2)
+        b_ms = []
+        for _ in range(max(1, args.build_reps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            tree2.build(Kd, Vd, n0, Rd)
+            e1.record()
+            torch.cuda.synchronize()
+            b_ms.append(e0.elapsed_time(e1))
+        stats2 = torch.zeros_like(stats)
+
+        def step2(s_):
+            if w.appends:
+                tree2.append(Kn[s_], Vn[s_])
+            tree2.decode(Qd[s_], out, stats2[s_])
+        for s_ in range(args.warmup):
+            step2(s_)
+        probe2 = {}
+        for key in ("route_score.top", "route_score.l1", "route_score.l2", "attend"):
+            zha.zha_profile_start(tree2.handle, key)
+            tree2.decode(Qd[min(args.warmup, total - 1)], out, None)
+            torch.cuda.synchronize()
+            ms_, n_ = zha.zha_profile_stop(tree2.handle)
+            if n_:
+                probe2[key] = ms_ / n_
+        dom2 = max(probe2, key=probe2.get)
+        zha.zha_profile_start(tree2.handle, dom2)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for s_ in range(args.warmup, args.warmup + steps):
+            step2(s_)
+        torch.cuda.synchronize()
+        wall2 = time.perf_counter() - t2
+        d2_ms, d2_n = zha.zha_profile_stop(tree2.handle)
+        st2 = stats2.cpu().numpy()[args.warmup:args.warmup + steps]
+        per2 = np.array([node_bytes(w2, L - row, key_form) for row in range(L)], dtype=np.float64)
+        step2_b = float(np.mean((st2[:, :L, :].sum(axis=2) * per2[None, :]).sum(axis=1) +
+                                st2[:, L, :].sum(axis=1) * w.block * 2 * d * 2))
+        alg2 = float(np.mean([kernel_bytes(dom2, w2, st2[i], n0 + args.warmup + i + 1, key_form) for i in range(steps)]))
+        ach2 = alg2 / (d2_ms / max(d2_n, 1) * 1e-3) / 1e9
+        bf16_planes = {
+            "ms_per_step": round(wall2 * 1e3 / steps, 4), "queries_per_s": round(steps / wall2, 2),
+            "speedup_vs_f32_planes": round(ms_per_step / (wall2 * 1e3 / steps), 3),
+            "build_ms": round(min(b_ms), 4),
+            "decode_step_alg_bytes": round(step2_b),
+            "roofline": dict(bound="hbm", kernel=dom2, achieved=round(ach2, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=round(ach2 / HBM_PEAK_GBS, 4), avg_launch_ms=round(d2_ms / max(d2_n, 1), 4),
+                             algorithmic_bytes_per_launch=round(alg2),
+                             traffic=traffic_for(dom2, f"{w.name}_bf16planes")),
+            "kernel_ms": {k: round(v, 4) for k, v in sorted(probe2.items(), key=lambda x: -x[1])},
+        }
+        log(f"[bench] bf16 router planes: {bf16_planes['ms_per_step']:.3f} ms/step, "
+            f"{bf16_planes['queries_per_s']:.1f} queries/s; {dom2} {d2_ms / max(d2_n, 1):.4f} ms/launch "
+            f"({ach2 / HBM_PEAK_GBS:.3f} of HBM)")
+        tree2.close()
+        del tree2
+
     # stream-read probe: practical HBM read bandwidth of a plain streaming kernel (2 GiB)
     import ctypes
     plib = ctypes.CDLL(os.path.join(ROOT, "hierarchical_tree_indexed_03_amd", "libzha_probe.so"))
@@ -510,6 +576,7 @@ def main():
                   "kernel_ms": round(dense_ms_k / max(dense_n, 1), 4), "alg_bytes": dense_bytes,
                   "frac_hbm": round(dense_bytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "zha_speedup": round(dense_ms / ms_per_step, 3)},
+        "bf16_router_planes": bf16_planes,
         "hbm_read_probe_GBps": round(read_gbs, 1),
         "kernel_ms": {k: round(v, 4) for k, v in sorted(probe_ms.items(), key=lambda x: -x[1])},
         "src_sha": src_sha(),

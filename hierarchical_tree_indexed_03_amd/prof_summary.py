@@ -61,11 +61,12 @@ def short(name: str) -> str:
 
 
 STAGE = {
-    "route_score_kernel": "score", "route_score_keys_kernel": "score", "route_hist_kernel": "hist",
+    "route_score_kernel": "score", "route_score_keys_kernel": "score", "route_score_bf16_kernel": "score",
+    "route_score_bf16_rows_kernel": "score", "route_hist_kernel": "hist",
     "route_bound_kernel": "bound", "route_classify_kernel": "classify", "route_resolve_kernel": "resolve",
     "route_expand_count_kernel": "expand_count", "route_expand_emit_kernel": "expand_emit",
 }
-SCORES = ("route_score_kernel", "route_score_keys_kernel")
+SCORES = ("route_score_kernel", "route_score_keys_kernel", "route_score_bf16_kernel", "route_score_bf16_rows_kernel")
 
 
 def decodes(rows):
