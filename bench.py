@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--workload", default="deep", help="deep | wide | ultra | light_<N> | tiny")
     ap.add_argument("--planes", default="f32", choices=("f32", "bf16"),
                     help="storage of the s vectors the router reads (bf16: a rounded copy)")
+    ap.add_argument("--p-levels", default=None,
+                    help="per-level top-p schedule: p of levels 1..L comma-separated, or 'compound' "
+                         "for p^(1/L) at every level (the product over the levels is p)")
     ap.add_argument("--no-bf16-planes", action="store_true",
                     help="skip the secondary measurement with bf16 router planes")
     ap.add_argument("--build-reps", type=int, default=3)
@@ -321,6 +324,11 @@ def main():
     tree = zha.Tree(cfg)
     h = tree.handle
     key_form = zha.zha_level1_key_form(cfg) == 1
+    p_levels = None
+    if args.p_levels:
+        p_levels = ([w.top_p ** (1.0 / w.levels)] * w.levels if args.p_levels == "compound"
+                    else [float(x) for x in args.p_levels.split(",")])
+        tree.set_top_p_levels(p_levels)
 
     # ---- tree build (timed separately; the last build is the one decoded against)
     torch.cuda.synchronize()
@@ -454,6 +462,8 @@ def main():
         cfg2 = zha.make_config(w.head_dim, w.num_kv_heads, w.num_q_heads, w.block, w.levels, w.num_ref,
                                w.capacity, w.dtype, w.top_p, w.keep_sink, "bf16")
         tree2 = zha.Tree(cfg2)
+        if p_levels:
+            tree2.set_top_p_levels(p_levels)
         b_ms = []
         for _ in range(max(1, args.build_reps)):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -559,9 +569,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16+f32",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}_{n0}" + ("" if w.planes == "f32" else "_bf16planes"), "kv_tokens": n0, "head_dim": d, "q_heads": w.num_q_heads,
+        "config": {"workload": f"{w.name}_{n0}" + ("" if w.planes == "f32" else "_bf16planes") + ("_plevels" if p_levels else ""), "kv_tokens": n0, "head_dim": d, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "block": w.block, "levels": L, "num_ref": R, "top_p": w.top_p,
                    "router_planes": w.planes,
+                   "top_p_levels": [round(x, 6) for x in p_levels] if p_levels else None,
                    "batch": 1, "layers": 1, "step": "append + decode"},
         "roofline": roofline,
         "cpu_baseline": cpu,

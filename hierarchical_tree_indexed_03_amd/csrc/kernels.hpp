@@ -45,8 +45,8 @@ struct RouteArgs {
   int32_t level;      // level being routed
   int64_t nlevel;     // nodes at `level` (upper bound of every union frontier there)
   int64_t nbelow;     // nodes at level-1 (children existence); unused at level 1
-  float top_p;
   float sigma;
+  float top_p[MAXL + 1];  // p of the top-p decision at each level (index = level)
   int32_t dense;      // score kernel: 1 = every node of levels `level` .. `level`-gridDim.z+1
   int32_t dense_lo;   // lowest level handled by the multi-level selection kernel
   int32_t sel_p;      // top-p histogram / classify workgroups per KV head at `level`

@@ -129,8 +129,8 @@ __global__ __launch_bounds__(NB1) void route_bound_kernel(RouteArgs a) {
   uint32_t b1 = NB1;
   uint64_t T = 0;
   above1 = 0;
-  if (a.top_p < 1.0f && Z > 0) {
-    const double tt = ceil((double)a.top_p * (double)Z);
+  if (a.top_p[lv] < 1.0f && Z > 0) {
+    const double tt = ceil((double)a.top_p[lv] * (double)Z);
     T = tt < 1.0 ? 1ull : (uint64_t)tt;
     if (T > Z) T = Z;
     wave_boundary512(hs, 0, T, lane, bb, above1, dummy);

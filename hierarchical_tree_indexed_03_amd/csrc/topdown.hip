@@ -156,8 +156,8 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
       td_scan512(h, lane, v, excl, Z);
       uint32_t b1 = NB1;
       uint64_t T = 0, above1 = 0;
-      if (a.top_p < 1.0f && Z > 0) {
-        const double tt = ceil((double)a.top_p * (double)Z);
+      if (a.top_p[lv] < 1.0f && Z > 0) {
+        const double tt = ceil((double)a.top_p[lv] * (double)Z);
         T = tt < 1.0 ? 1ull : (uint64_t)tt;
         if (T > Z) T = Z;
         td_find(v, excl, T, b1, above1);

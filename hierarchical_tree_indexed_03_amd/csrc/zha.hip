@@ -30,6 +30,7 @@ struct zha_tree {
   void* K;
   void* V;
   const void* refs;
+  float top_p[MAXL + 1];  // p per level (index = level); cfg.top_p unless a schedule is set
 };
 
 namespace {
@@ -177,7 +178,7 @@ RouteArgs route_args(const zha_tree* t, const void* q) {
   a.g = a.hq / a.hkv;
   a.b = t->cfg.block;
   a.levels = t->cfg.levels;
-  a.top_p = t->cfg.top_p;
+  for (int l = 0; l <= MAXL; ++l) a.top_p[l] = t->top_p[l];
   a.sigma = 1.0f / sqrtf((float)t->cfg.head_dim);
   a.key_form = key_form(t->cfg) ? 1 : 0;
   a.q_bf16 = t->cfg.dtype == ZHA_BF16 ? 1 : 0;
@@ -257,6 +258,7 @@ zha_status zha_create(const zha_config* cfg, void* workspace, size_t workspace_b
   zha_tree* t = new (std::nothrow) zha_tree();
   if (!t) return fail(ZHA_E_INVALID, "host allocation failed");
   t->cfg = *cfg;
+  for (int l = 0; l <= MAXL; ++l) t->top_p[l] = cfg->top_p;
   t->ws = (char*)workspace;
   t->ws_bytes = workspace_bytes;
   layout(*cfg, t->ws, &t->dev);
@@ -554,6 +556,17 @@ zha_status zha_debug_route_level(zha_tree* t, int32_t level, const void* q, cons
   if (zs != ZHA_OK) return zs;
   e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "route level");
+  return ZHA_OK;
+}
+
+zha_status zha_set_top_p_levels(zha_tree* t, const float* p_levels) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  const int L = t->cfg.levels;
+  if (p_levels)
+    for (int l = 0; l < L; ++l)
+      if (!(p_levels[l] > 0.f && p_levels[l] <= 1.f))
+        return fail(ZHA_E_INVALID, "p of level %d is %g, outside (0, 1]", l + 1, p_levels[l]);
+  for (int l = 1; l <= L; ++l) t->top_p[l] = p_levels ? p_levels[l - 1] : t->cfg.top_p;
   return ZHA_OK;
 }
 

@@ -55,6 +55,7 @@ def _load() -> ctypes.CDLL:
         "zha_debug_route_level": (I32, [P, I32, P, P, P, P, I64, P]),
         "zha_profile_start": (I32, [P, ctypes.c_char_p]),
         "zha_profile_stop": (I32, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
+        "zha_set_top_p_levels": (I32, [P, ctypes.POINTER(ctypes.c_float)]),
         "zha_num_tokens": (I64, [P]),
         "zha_destroy": (I32, [P]),
         "zha_status_string": (ctypes.c_char_p, [I32]),
@@ -69,7 +70,7 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 EXPORTED = ("zha_workspace_bytes", "zha_level1_key_form", "zha_create", "zha_tree_build", "zha_tree_append", "zha_decode",
             "zha_decode_dense", "zha_debug_level", "zha_debug_router_planes", "zha_debug_trace", "zha_debug_route_level",
-            "zha_profile_start", "zha_profile_stop", "zha_num_tokens", "zha_destroy", "zha_status_string",
+            "zha_profile_start", "zha_profile_stop", "zha_set_top_p_levels", "zha_num_tokens", "zha_destroy", "zha_status_string",
             "zha_last_error")
 
 
@@ -162,6 +163,15 @@ def zha_profile_stop(t) -> tuple[float, int]:
     return ms.value, n.value
 
 
+def zha_set_top_p_levels(t, p_levels=None):
+    """p_levels: p of levels 1..L in order, or None to restore the config's top_p."""
+    if p_levels is None:
+        _check(_lib.zha_set_top_p_levels(t, None))
+        return
+    arr = (ctypes.c_float * len(p_levels))(*[float(x) for x in p_levels])
+    _check(_lib.zha_set_top_p_levels(t, arr))
+
+
 def zha_num_tokens(t) -> int:
     return int(_lib.zha_num_tokens(t))
 
@@ -199,6 +209,11 @@ class Tree:
 
     def append(self, k_new, v_new, stream=None):
         zha_tree_append(self.handle, k_new, v_new, stream)
+
+    def set_top_p_levels(self, p_levels=None):
+        if p_levels is not None and len(p_levels) != self.cfg.levels:
+            raise ValueError(f"need {self.cfg.levels} values, got {len(p_levels)}")
+        zha_set_top_p_levels(self.handle, p_levels)
 
     def decode(self, q, out=None, stats=None, stream=None):
         if out is None:

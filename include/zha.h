@@ -127,6 +127,15 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats,
  * out[h] = softmax(q_h.K^T/sqrt(d)) V for every query head. */
 zha_status zha_decode_dense(zha_tree* t, const void* q, float* out, hipStream_t stream);
 
+/* Sets the top-p threshold of each level for the following decodes (blog, "The narrow
+ * path": a fixed fraction kept at every level compounds over the depth, so the threshold
+ * has to change with depth and context; the pages give no formula, so the caller supplies
+ * it).  p_levels (host) [levels]: entry l-1 is p at level l, each in (0, 1]; the values are
+ * copied.  Null restores cfg.top_p at every level.  May be called at any time (before or
+ * after build, between decodes); a context-dependent schedule p_l(N) is set before each
+ * decode.  Host only; nothing is enqueued.  On error the schedule is left unchanged. */
+zha_status zha_set_top_p_levels(zha_tree* t, const float* p_levels);
+
 /* Copies level `level` (1..levels) of the tree into caller buffers:
  *   s_out (device) float32 [Hkv][n_l][R][d], c_out (device) float32 [Hkv][n_l][R] with
  *   n_l = ceil(N / block^level).  Enqueued copies only (no synchronisation). */

@@ -251,7 +251,18 @@ def children(tree: Tree, level: int, nodes: np.ndarray) -> np.ndarray:
     return ch[ch < tree.nodes(level - 1)]
 
 
-def route(tree: Tree, q: np.ndarray, p: float, keep_sink: bool = True) -> dict:
+def level_p(p, level: int) -> float:
+    """p of the top-p decision at ``level``: a single p for every level, or a schedule
+    whose entry level-1 is that level's p.
+
+    [blog] "The narrow path": keeping a fixed fraction at every level compounds over the
+    depth, so the threshold would have to change with depth and context; the pages give no
+    formula, so a schedule is an input.
+    """
+    return float(p) if np.ndim(p) == 0 else float(p[level - 1])
+
+
+def route(tree: Tree, q: np.ndarray, p, keep_sink: bool = True) -> dict:
     """Top-down routing of one query through one tree.
 
     [blog] "Routing through the tree": score the top level, keep the top-p set, expand
@@ -259,7 +270,7 @@ def route(tree: Tree, q: np.ndarray, p: float, keep_sink: bool = True) -> dict:
     selected keys; several branches may stay open.  [news]: the first token is always
     kept as an attention sink.  The level-1 top-p picks blocks and every existing token
     of a kept block is attended; the sink is added after routing (it takes no part in
-    the routing mass).
+    the routing mass).  ``p``: one value for every level, or one per level (level_p).
     """
     L = tree.n_levels
     frontier = np.arange(tree.nodes(L), dtype=np.int64)
@@ -267,7 +278,7 @@ def route(tree: Tree, q: np.ndarray, p: float, keep_sink: bool = True) -> dict:
     kept = frontier
     for lv in range(L, 0, -1):
         sc = node_scores(tree, lv, frontier, q)
-        sel = top_p(frontier, sc, p)
+        sel = top_p(frontier, sc, level_p(p, lv))
         per_level.append(dict(level=lv, frontier=frontier, scores=sc, **sel))
         kept = sel["kept"]
         if lv > 1:
@@ -294,7 +305,7 @@ def attend(keys: np.ndarray, values: np.ndarray, q: np.ndarray, tokens: np.ndarr
     return (w / np.sum(w)) @ v
 
 
-def decode(trees: list, values: np.ndarray, q: np.ndarray, p: float, keep_sink: bool = True,
+def decode(trees: list, values: np.ndarray, q: np.ndarray, p, keep_sink: bool = True,
            return_routes: bool = False):
     """One decode step for all query heads: q [Hq, d], one tree per KV head; query head h
     reads KV head h // (Hq / Hkv) (contiguous groups).  Returns o [Hq, d] (float64)."""

@@ -131,11 +131,12 @@ def exempt_nodes(rec: dict, p: float, diff: np.ndarray, tol=None) -> tuple[list,
     return ok, bad
 
 
-def compare_route(route: dict, trace: dict, gi: int, b: int, p: float, tol_fn=None) -> dict:
+def compare_route(route: dict, trace: dict, gi: int, b: int, p, tol_fn=None) -> dict:
     """End-to-end set comparison of one query head.  ``trace[level]`` is the GPU trace of
-    that level for the head's KV head (level 0 = kept blocks).  ``tol_fn(level, frontier)``
-    gives per-node score tolerances (default SCORE_TOL).  Returns a report dict;
-    report["bad"] lists unexplained mismatches."""
+    that level for the head's KV head (level 0 = kept blocks).  ``p``: one value, or one
+    per level (entry level-1).  ``tol_fn(level, frontier)`` gives per-node score tolerances
+    (default SCORE_TOL).  Returns a report dict; report["bad"] lists unexplained
+    mismatches."""
     excluded = set()
     bad, exempt, n_levels = [], [], len(route["levels"])
     for rec in route["levels"]:
@@ -150,7 +151,7 @@ def compare_route(route: dict, trace: dict, gi: int, b: int, p: float, tol_fn=No
         k_g = set(gpu_kept(tl, gi).tolist()) - excluded
         diff = np.array(sorted(k_o ^ k_g), dtype=np.int64)
         tol = None if tol_fn is None else tol_fn(lv, rec["frontier"])
-        ok, nb = exempt_nodes(rec, p, diff, tol)
+        ok, nb = exempt_nodes(rec, p if np.ndim(p) == 0 else p[lv - 1], diff, tol)
         exempt += [(lv, n) for n in ok]
         bad += [("kept", lv) + x for x in nb]
         nxt = set()

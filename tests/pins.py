@@ -317,7 +317,36 @@ def check_quantised_planes(seed=13):
     return moved > 0, f"{moved} quantised scores moved"
 
 
+# Per-level p: with p = 1 at every level but one, routing reduces to a textbook nucleus
+# selection at that level (over all its nodes, by softmax of their scores), and every
+# level below keeps all children of the selected nodes.  Checked for the top level and
+# for level 1 of a 3-level tree.
+def check_p_schedule(seed=14):
+    rng = np.random.default_rng(seed)
+    tree, keys, _ = rand_tree(rng, n=203, d=8, r=3, b=4, levels=3)
+    bad = 0
+    for _ in range(10):
+        q = rng.standard_normal(keys.shape[1]) * 3
+        for lv, p in ((1, 0.6), (3, 0.5)):
+            sched = [1.0, 1.0, 1.0]
+            sched[lv - 1] = p
+            nodes = np.arange(tree.nodes(lv))
+            pi = sp.softmax(zo.node_scores(tree, lv, nodes, q))
+            order = sorted(nodes.tolist(), key=lambda n: (-pi[n], n))
+            keep, mass = [], 0.0
+            for n in order:
+                keep.append(n)
+                mass += pi[n]
+                if mass >= p:
+                    break
+            span_l = tree.block ** lv
+            toks = {t for n in keep for t in range(n * span_l, min((n + 1) * span_l, tree.n_tokens))} | {0}
+            got = zo.route(tree, q, sched)
+            bad += set(got["tokens"].tolist()) != toks
+    return bad == 0, f"{bad} schedules routed differently from the nucleus selection"
+
+
 ALL = [check_dense_limit, check_convexity, check_exact_at_refs, check_recursion_direct,
        check_single_key, check_nucleus, check_minimal, check_mass_conservation, check_append,
        check_masked_attention, check_sink, check_bf16_round_library, check_bf16_round_nearest,
-       check_quantised_planes]
+       check_quantised_planes, check_p_schedule]

@@ -147,6 +147,24 @@ def test_call_order_and_arguments(zha):
         zha.zha_destroy(t)
 
 
+def test_top_p_levels_validation(zha):
+    """The per-level p schedule is checked on the host; a bad schedule leaves the old one."""
+    cfg = good(zha, capacity=1000, levels=3)
+    t = zha.zha_create(cfg, 0x100000, zha.zha_workspace_bytes(cfg))
+    try:
+        zha.zha_set_top_p_levels(t, [0.5, 0.9, 1.0])
+        zha.zha_set_top_p_levels(t, None)
+        for bad in ([0.5, 0.0, 1.0], [0.5, 1.5, 1.0], [float("nan"), 0.9, 0.9], [-0.1, 0.9, 0.9]):
+            with pytest.raises(zha.ZhaError) as e:
+                zha.zha_set_top_p_levels(t, bad)
+            assert e.value.status == 1
+    finally:
+        zha.zha_destroy(t)
+    with pytest.raises(zha.ZhaError) as e:
+        zha.zha_set_top_p_levels(None, [0.5])
+    assert e.value.status == 1
+
+
 def test_status_strings(zha):
     for s in range(7):
         assert zha.zha_status_string(s)

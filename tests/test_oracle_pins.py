@@ -169,6 +169,12 @@ def _mut_quantise_next_level(orig):
     return f
 
 
+def _mut_level_p_shift(orig):
+    def f(p, level):
+        return orig(p, min(level + 1, len(p))) if np.ndim(p) else orig(p, level)
+    return f
+
+
 MUTATIONS = [
     ("level1_planes", _mut_level1_offset),
     ("parent_planes", _mut_parent_unweighted),
@@ -181,6 +187,7 @@ MUTATIONS = [
     ("bf16_round", _mut_bf16_truncate),
     ("quantise_planes", _mut_quantise_offsets),
     ("quantise_planes", _mut_quantise_next_level),
+    ("level_p", _mut_level_p_shift),
 ]
 
 
