@@ -24,8 +24,10 @@ Parity pins: every function here is pinned by the CPU tests in ``tests/test_orac
 per-span form, single-key blocks, nucleus selection for b=1, brute-force minimality,
 mass conservation, append = rebuild, geometry; for the bf16 router planes: rounding
 against torch's float32 -> bfloat16 cast and a brute-force nearest search, and the score
-perturbation bound).  The exact routed sets at p<1 on the synthetic data are defined only
-by this oracle ("parity unpinned" beyond those pins).
+perturbation bound; for FP4 planes: a brute-force nearest search over the 16 codes,
+constructed halfway cases, the block-scale property and the same bound).  The exact
+routed sets at p<1 on the synthetic data are defined only by this oracle ("parity
+unpinned" beyond those pins).
 """
 from __future__ import annotations
 
@@ -183,19 +185,51 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
 
 
-def quantise_planes(tree: Tree, levels) -> Tree:
-    """The router's view of a tree whose planes at ``levels`` are stored with bf16 s.
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])   # FP4 magnitudes, codes 0..7
+MX_BLOCK = 32
+
+
+def mxfp4_round(x: np.ndarray) -> np.ndarray:
+    """OCP MX FP4 round trip of each row (last axis, a multiple of 32 long), as float64.
+
+    Each block of 32 consecutive elements shares a power-of-two scale X = 2^(floor(log2
+    amax) - 2), amax the block's largest magnitude and 2 the largest exponent of the E2M1
+    element format (largest value 6 = 1.5 * 2^2), so amax / X lies in [4, 8).  Each element
+    becomes the nearest of X * {0, 0.5, 1, 1.5, 2, 3, 4, 6} with its sign; a value halfway
+    between two of them takes the one whose mantissa bit is 0 (code even); magnitudes above
+    6X become 6X.  An all-zero block stays zero.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    xb = x.reshape(-1, MX_BLOCK)
+    amax = np.max(np.abs(xb), axis=1)
+    _, e = np.frexp(amax)                       # amax = m * 2^e, 1/2 <= m < 1
+    scale = np.where(amax > 0, np.ldexp(1.0, e - 1 - 2), 1.0)[:, None]
+    a = np.abs(xb) / scale
+    hi_i = np.clip(np.searchsorted(E2M1, a), 0, len(E2M1) - 1)
+    lo_i = np.clip(hi_i - 1, 0, len(E2M1) - 1)
+    lo, hi = E2M1[lo_i], E2M1[hi_i]
+    take_lo = (a - lo < hi - a) | ((a - lo == hi - a) & (lo_i % 2 == 0))
+    mag = np.where(a >= E2M1[-1], E2M1[-1], np.where(take_lo, lo, hi))
+    return (np.sign(xb) * mag * scale).reshape(x.shape)
+
+
+QUANTISERS = {"bf16": lambda s: bf16_round(s), "fp4": lambda s: mxfp4_round(s)}
+
+
+def quantise_planes(tree: Tree, levels, fmt: str = "bf16") -> Tree:
+    """The router's view of a tree whose planes at ``levels`` are stored with s quantised.
 
     The pages fix no storage precision for the planes (their routing arithmetic is fp32).
-    Stated quantiser: every element of s_j is rounded to the nearest bf16 value; the
-    offsets c_j stay as computed (fp32 storage on the GPU).  The tree itself is unchanged:
-    parents and appends keep using the full-precision planes, and only routing reads the
-    quantised copy.  Levels not listed keep their full-precision s.
+    Stated quantisers: "bf16", every element of s_j rounded to the nearest bf16 value;
+    "fp4", OCP MX FP4 with one power-of-two scale per 32 elements of each s_j
+    (mxfp4_round).  The offsets c_j stay as computed (fp32 storage on the GPU).  The tree
+    itself is unchanged: parents and appends keep using the full-precision planes, and only
+    routing reads the quantised copy.  Levels not listed keep their full-precision s.
     """
     out = list(tree.levels)
     for lv in levels:
         s, c = tree.levels[lv - 1]
-        out[lv - 1] = (bf16_round(s), c)
+        out[lv - 1] = (QUANTISERS[fmt](s), c)
     return dataclasses.replace(tree, levels=out)
 
 

@@ -346,7 +346,79 @@ def check_p_schedule(seed=14):
     return bad == 0, f"{bad} schedules routed differently from the nucleus selection"
 
 
+# FP4 router planes.  mxfp4_round against a brute-force search: per block of 32, the scale
+# is the power of two X with amax / X in [4, 8) (found by doubling from 2^-40), and each
+# element the nearest of the 16 codes times X (clamped at 6X), halfway cases to the even
+# code; plus constructed halfway cases of every pair of neighbouring magnitudes.
+def check_mxfp4_round(seed=15):
+    rng = np.random.default_rng(seed)
+    codes = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    bad = 0
+    for _ in range(300):
+        x = rng.standard_normal(32) * np.exp(rng.uniform(-8, 8))
+        if rng.random() < 0.2:
+            x[rng.integers(0, 32, 5)] = 0.0
+        amax = np.max(np.abs(x))
+        X = 2.0 ** -40
+        while amax / X >= 8:
+            X *= 2
+        want = np.empty(32)
+        for i, v in enumerate(x):
+            a = min(abs(v) / X, 6.0)
+            d = np.abs(codes - a)
+            best = np.nonzero(d == d.min())[0]
+            k = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+            want[i] = math.copysign(codes[k] * X, v)
+        bad += int(np.count_nonzero(zo.mxfp4_round(x) != want))
+    # halfway cases: a block with amax = 4X (X = 1/8) holding every midpoint of neighbours
+    X = 0.125
+    mids = (codes[:-1] + codes[1:]) / 2
+    block = np.zeros(32)
+    block[0] = 4 * X
+    block[1:1 + len(mids)] = mids * X
+    block[8:8 + len(mids)] = -mids * X
+    even = np.array([codes[i] if i % 2 == 0 else codes[i + 1] for i in range(len(mids))])
+    got = zo.mxfp4_round(block)
+    bad += int(np.count_nonzero(got[1:1 + len(mids)] != even * X))
+    bad += int(np.count_nonzero(got[8:8 + len(mids)] != -even * X))
+    return bad == 0, f"{bad} elements differ from the brute-force rounding"
+
+
+# FP4 planes: each block's largest quantised magnitude is 4X or 6X (amax / X in [4, 8)),
+# every element moves by at most 2X, the offsets stay, and each score moves by at most the
+# largest plane move, max_j sigma * sum_i |q_i| |s~_ji - s_ji|.
+def check_fp4_planes(seed=16):
+    rng = np.random.default_rng(seed)
+    tree, keys, _ = rand_tree(rng, n=300, d=64, r=2, b=4, levels=2)
+    qt = zo.quantise_planes(tree, [1, 2], "fp4")
+    sig = 1.0 / math.sqrt(keys.shape[1])
+    moved = 0
+    for lv in (1, 2):
+        s, c = tree.levels[lv - 1]
+        sq, cq = qt.levels[lv - 1]
+        if not np.array_equal(cq, c):
+            return False, f"level {lv}: offsets changed"
+        sb, qb = s.reshape(-1, 32), sq.reshape(-1, 32)
+        _, e = np.frexp(np.max(np.abs(sb), axis=1))
+        X = np.ldexp(1.0, e - 3)[:, None]
+        top = np.max(np.abs(qb), axis=1, keepdims=True) / X
+        if not np.all((top == 4) | (top == 6)):
+            return False, f"level {lv}: a block's largest code is not 4 or 6"
+        if np.any(np.abs(qb - sb) > 2 * X):
+            return False, f"level {lv}: an element moved by more than 2X"
+        nodes = np.arange(tree.nodes(lv))
+        for _ in range(10):
+            q = rng.standard_normal(keys.shape[1]) * 3
+            a = zo.node_scores(tree, lv, nodes, q)
+            b = zo.node_scores(qt, lv, nodes, q)
+            bound = sig * np.max(np.abs(sq - s) @ np.abs(q), axis=1)
+            if np.any(np.abs(b - a) > bound * (1 + 1e-9) + 1e-15):
+                return False, f"level {lv}: score moved beyond the plane bound"
+            moved += int(np.count_nonzero(a != b))
+    return moved > 0, f"{moved} quantised scores moved"
+
+
 ALL = [check_dense_limit, check_convexity, check_exact_at_refs, check_recursion_direct,
        check_single_key, check_nucleus, check_minimal, check_mass_conservation, check_append,
        check_masked_attention, check_sink, check_bf16_round_library, check_bf16_round_nearest,
-       check_quantised_planes, check_p_schedule]
+       check_quantised_planes, check_p_schedule, check_mxfp4_round, check_fp4_planes]

@@ -156,16 +156,37 @@ def _mut_bf16_truncate(orig):
 
 
 def _mut_quantise_offsets(orig):
-    def f(tree, levels):
-        qt = orig(tree, levels)
+    def f(tree, levels, fmt="bf16"):
+        qt = orig(tree, levels, fmt)
         qt.levels = [(s, zo.bf16_round(c)) for s, c in qt.levels]
         return qt
     return f
 
 
 def _mut_quantise_next_level(orig):
-    def f(tree, levels):
-        return orig(tree, [lv + 1 for lv in levels if lv < tree.n_levels])
+    def f(tree, levels, fmt="bf16"):
+        return orig(tree, [lv + 1 for lv in levels if lv < tree.n_levels], fmt)
+    return f
+
+
+def _mut_mxfp4_scale_low(orig):
+    # the block scale one power of two too small (amax / X in [8, 16): large values clamp)
+    def f(x):
+        x = np.asarray(x, dtype=np.float64)
+        xb = x.reshape(-1, zo.MX_BLOCK)
+        amax = np.max(np.abs(xb), axis=1)
+        _, e = np.frexp(amax)
+        sc = np.where(amax > 0, np.ldexp(1.0, e - 1 - 3), 1.0)[:, None]
+        a = np.abs(xb) / sc
+        idx = np.argmin(np.abs(a[..., None] - zo.E2M1), axis=-1)
+        return (np.sign(xb) * zo.E2M1[idx] * sc).reshape(x.shape)
+    return f
+
+
+def _mut_mxfp4_ties_away(orig):
+    # halfway cases rounded away from zero (the input nudged outward before rounding)
+    def f(x):
+        return orig(np.asarray(x, dtype=np.float64) * (1 + 1e-12))
     return f
 
 
@@ -188,6 +209,8 @@ MUTATIONS = [
     ("quantise_planes", _mut_quantise_offsets),
     ("quantise_planes", _mut_quantise_next_level),
     ("level_p", _mut_level_p_shift),
+    ("mxfp4_round", _mut_mxfp4_scale_low),
+    ("mxfp4_round", _mut_mxfp4_ties_away),
 ]
 
 
