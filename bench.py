@@ -43,13 +43,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="deep", help="deep | wide | ultra | light_<N> | tiny")
-    ap.add_argument("--planes", default="f32", choices=("f32", "bf16"),
-                    help="storage of the s vectors the router reads (bf16: a rounded copy)")
+    ap.add_argument("--planes", default="f32", choices=("f32", "bf16", "fp4"),
+                    help="storage of the s vectors the router reads (bf16 / fp4: a quantised copy)")
     ap.add_argument("--p-levels", default=None,
                     help="per-level top-p schedule: p of levels 1..L comma-separated, or 'compound' "
                          "for p^(1/L) at every level (the product over the levels is p)")
-    ap.add_argument("--no-bf16-planes", action="store_true",
-                    help="skip the secondary measurement with bf16 router planes")
+    ap.add_argument("--no-quant-planes", "--no-bf16-planes", dest="no_quant_planes", action="store_true",
+                    help="skip the secondary measurements with quantised (bf16, FP4) router planes")
     ap.add_argument("--build-reps", type=int, default=3)
     ap.add_argument("--dense-reps", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -65,7 +65,8 @@ def parse():
 
 def node_bytes(w, level, key_form):
     """Algorithmic bytes read to score one union-frontier node at `level`: its R planes
-    (R*(d+1) floats; with bf16 router planes R*d bf16 plus R float offsets), or at level 1
+    (R*(d+1) floats; with bf16 router planes R*d bf16 plus R float offsets; with MX FP4
+    ones R*d/2 code bytes, R*d/32 scale bytes and R float offsets), or at level 1
     in key form its b keys (bf16) plus R*b token weights and R offsets; plus the 8-byte list
     entry and one float score per query head written."""
     R, d, g, b = w.num_ref, w.head_dim, w.group, w.block
@@ -73,6 +74,8 @@ def node_bytes(w, level, key_form):
         core = b * d * 2 + R * b * 4 + R * 4
     elif w.planes == "bf16":
         core = R * d * 2 + R * 4
+    elif w.planes == "fp4":
+        core = R * (d // 2 + d // 32) + R * 4
     else:
         core = R * (d + 1) * 4
     return core + 8 + g * 4
@@ -294,7 +297,7 @@ def main():
     total = args.warmup + steps + args.cold_steps
     w = base.with_(steps=total, planes=args.planes)
     n0 = w.n_tokens
-    prof_name = w.name if w.planes == "f32" else f"{w.name}_bf16planes"   # counter summaries
+    prof_name = w.name if w.planes == "f32" else f"{w.name}_{w.planes}planes"   # counter summaries
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
 
@@ -344,11 +347,12 @@ def main():
     build_tok_s = n0 / build_s
     # read the keys once; write every plane (plus the bf16 router copies of s, and the
     # level-1 token weights in key form) once
-    copies = [l for l in range(1, w.levels + 1) if w.planes == "bf16" and not (l == 1 and key_form)]
+    copies = [l for l in range(1, w.levels + 1) if w.planes != "f32" and not (l == 1 and key_form)]
+    copy_b = {"f32": 0, "bf16": w.head_dim * 2, "fp4": w.head_dim // 2 + w.head_dim // 32}[w.planes]
     build_bytes = n0 * w.num_kv_heads * (w.head_dim * (2 if w.dtype == "bf16" else 4) +
                                         sum(w.num_ref * (w.head_dim + 1) * 4 / w.block ** l
                                             for l in range(1, w.levels + 1)) +
-                                        sum(w.num_ref * w.head_dim * 2 / w.block ** l for l in copies) +
+                                        sum(w.num_ref * copy_b / w.block ** l for l in copies) +
                                         (w.num_ref * 4 if key_form else 0))
     log(f"[bench] build {build_s * 1e3:.3f} ms -> {build_tok_s / 1e9:.3f} G tok/s")
 
@@ -454,13 +458,13 @@ def main():
     dense_bytes = tree.n_tokens * w.num_kv_heads * 2 * d * 2
     log(f"[bench] dense decode {dense_ms:.3f} ms ({dense_bytes / dense_ms / 1e6:.0f} GB/s)")
 
-    # ---- the same warm steps with bf16 router planes: a second tree over the same caches
-    # (its appends rewrite rows n0.. with the values they already hold)
-    bf16_planes = None
-    if w.planes == "f32" and not args.no_bf16_planes:
-        w2 = w.with_(planes="bf16")
+    # ---- the same warm steps with quantised router planes (bf16, MX FP4): a second tree
+    # over the same caches (its appends rewrite rows n0.. with the values they already hold)
+    quant = {}
+    for fmt in (("bf16", "fp4") if w.planes == "f32" and not args.no_quant_planes else ()):
+        w2 = w.with_(planes=fmt)
         cfg2 = zha.make_config(w.head_dim, w.num_kv_heads, w.num_q_heads, w.block, w.levels, w.num_ref,
-                               w.capacity, w.dtype, w.top_p, w.keep_sink, "bf16")
+                               w.capacity, w.dtype, w.top_p, w.keep_sink, fmt)
         tree2 = zha.Tree(cfg2)
         if p_levels:
             tree2.set_top_p_levels(p_levels)
@@ -503,7 +507,7 @@ def main():
                                 st2[:, L, :].sum(axis=1) * w.block * 2 * d * 2))
         alg2 = float(np.mean([kernel_bytes(dom2, w2, st2[i], n0 + args.warmup + i + 1, key_form) for i in range(steps)]))
         ach2 = alg2 / (d2_ms / max(d2_n, 1) * 1e-3) / 1e9
-        bf16_planes = {
+        quant[fmt] = {
             "ms_per_step": round(wall2 * 1e3 / steps, 4), "queries_per_s": round(steps / wall2, 2),
             "speedup_vs_f32_planes": round(ms_per_step / (wall2 * 1e3 / steps), 3),
             "build_ms": round(min(b_ms), 4),
@@ -511,11 +515,11 @@ def main():
             "roofline": dict(bound="hbm", kernel=dom2, achieved=round(ach2, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                              frac=round(ach2 / HBM_PEAK_GBS, 4), avg_launch_ms=round(d2_ms / max(d2_n, 1), 4),
                              algorithmic_bytes_per_launch=round(alg2),
-                             traffic=traffic_for(dom2, f"{w.name}_bf16planes")),
+                             traffic=traffic_for(dom2, f"{w.name}_{fmt}planes")),
             "kernel_ms": {k: round(v, 4) for k, v in sorted(probe2.items(), key=lambda x: -x[1])},
         }
-        log(f"[bench] bf16 router planes: {bf16_planes['ms_per_step']:.3f} ms/step, "
-            f"{bf16_planes['queries_per_s']:.1f} queries/s; {dom2} {d2_ms / max(d2_n, 1):.4f} ms/launch "
+        log(f"[bench] {fmt} router planes: {quant[fmt]['ms_per_step']:.3f} ms/step, "
+            f"{quant[fmt]['queries_per_s']:.1f} queries/s; {dom2} {d2_ms / max(d2_n, 1):.4f} ms/launch "
             f"({ach2 / HBM_PEAK_GBS:.3f} of HBM)")
         tree2.close()
         del tree2
@@ -569,7 +573,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16+f32",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}_{n0}" + ("" if w.planes == "f32" else "_bf16planes") + ("_plevels" if p_levels else ""), "kv_tokens": n0, "head_dim": d, "q_heads": w.num_q_heads,
+        "config": {"workload": f"{w.name}_{n0}" + ("" if w.planes == "f32" else f"_{w.planes}planes") + ("_plevels" if p_levels else ""), "kv_tokens": n0, "head_dim": d, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "block": w.block, "levels": L, "num_ref": R, "top_p": w.top_p,
                    "router_planes": w.planes,
                    "top_p_levels": [round(x, 6) for x in p_levels] if p_levels else None,
@@ -587,7 +591,8 @@ def main():
                   "kernel_ms": round(dense_ms_k / max(dense_n, 1), 4), "alg_bytes": dense_bytes,
                   "frac_hbm": round(dense_bytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "zha_speedup": round(dense_ms / ms_per_step, 3)},
-        "bf16_router_planes": bf16_planes,
+        "bf16_router_planes": quant.get("bf16"),
+        "fp4_router_planes": quant.get("fp4"),
         "hbm_read_probe_GBps": round(read_gbs, 1),
         "kernel_ms": {k: round(v, 4) for k, v in sorted(probe_ms.items(), key=lambda x: -x[1])},
         "src_sha": src_sha(),

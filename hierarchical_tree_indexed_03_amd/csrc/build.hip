@@ -83,6 +83,21 @@ __device__ void tile_logits(const float* Ks, const float* refs_g, float sigma, i
 }
 
 __device__ __forceinline__ float4 ld4_f32(const float* p) { return *(const float4*)p; }
+// MX FP4 of one element per lane, 32 consecutive elements in 32 consecutive lanes (element
+// index e, lane e mod 32; all 32 lanes active): block amax by butterfly, codes gathered
+// eight to a 32-bit word by the lane holding the word's first element.
+__device__ __forceinline__ void store_fp4_lane(uint8_t* q, uint8_t* x, int64_t e, float v) {
+  float am = fabsf(v);
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
+  const uint32_t sb = mx_scale_byte(am);
+  uint32_t w = e2m1_code(v, sb) << (4 * (int)(e & 7));
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) w |= __shfl_xor(w, o);
+  if ((e & 7) == 0) *(uint32_t*)(q + e / 2) = w;
+  if ((e & 31) == 0) x[e / 32] = (uint8_t)sb;
+}
+
 // four floats as bfloat16 (nearest, ties to even) at an 8-byte aligned address
 __device__ __forceinline__ void store_bf16x4(bf16_t* p, float4 v) {
   uint2 w;
@@ -526,11 +541,13 @@ __global__ __launch_bounds__(1024) void append_kernel(AppendArgs a) {
     float sv = Cf[0][j][0] * sold[u] + Cf[0][j][1] * kd;
     a.dev.s[1][g1 * RD + i] = sv;
     if (a.dev.sq[1]) a.dev.sq[1][g1 * RD + i].bits = (uint16_t)f2bf16_bits(sv);
+    if (a.dev.s4[1]) store_fp4_lane(a.dev.s4[1], a.dev.s4x[1], g1 * RD + i, sv);
     for (int v = 2; v <= L; ++v) {
       sv = Cf[v - 1][j][0] * Agg[(v - 2) * RS + j * (D + 2) + 2 + d] + Cf[v - 1][j][1] * sv;
       const int64_t si = ((int64_t)kv * a.dev.ncap[v] + pvl[v - 2]) * RD + i;
       a.dev.s[v][si] = sv;
       if (a.dev.sq[v]) a.dev.sq[v][si].bits = (uint16_t)f2bf16_bits(sv);
+      if (a.dev.s4[v]) store_fp4_lane(a.dev.s4[v], a.dev.s4x[v], si, sv);
     }
   }
   // token weights of the level-1 planes (key-form scoring): old weights scale by
@@ -595,6 +612,47 @@ hipError_t launch_build_parent(const ParentArgs& a, int D, int R, int hkv, hipSt
     dim3 grid((unsigned)((a.nparent + PPB - 1) / PPB), (unsigned)hkv);                     \
     hipLaunchKernelGGL((build_parent_kernel<DD, RR>), grid, dim3(256), 0, st, a);         \
     return hipGetLastError();                                                             \
+  }
+  ZHA_CASE(64, 1) ZHA_CASE(64, 2) ZHA_CASE(64, 4) ZHA_CASE(64, 8) ZHA_CASE(64, 16)
+  ZHA_CASE(128, 1) ZHA_CASE(128, 2) ZHA_CASE(128, 4) ZHA_CASE(128, 8) ZHA_CASE(128, 16)
+#undef ZHA_CASE
+  return hipErrorInvalidValue;
+}
+
+// MX FP4 copy of one level's s: a thread per 4 consecutive elements, 8 threads per
+// 32-element block (amax by 3 butterfly steps; a block's threads run the loop together);
+// each thread stores its 16 code bits, the block's first thread the scale byte.
+template <int D, int R>
+__global__ __launch_bounds__(256) void quantise_fp4_kernel(QuantArgs a) {
+  const int kv = blockIdx.y, v = a.level;
+  const int64_t cap = a.dev.ncap[v];
+  const int64_t items = a.nnode * R * (D / 4);
+  const float* S = a.dev.s[v] + (int64_t)kv * cap * R * D;
+  uint8_t* Q = a.dev.s4[v] + (int64_t)kv * cap * R * D / 2;
+  uint8_t* X = a.dev.s4x[v] + (int64_t)kv * cap * R * D / 32;
+  for (int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x; it < items; it += (int64_t)gridDim.x * 256) {
+    const float4 x = *(const float4*)(S + it * 4);
+    float am = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
+    am = fmaxf(am, __shfl_xor(am, 1));
+    am = fmaxf(am, __shfl_xor(am, 2));
+    am = fmaxf(am, __shfl_xor(am, 4));
+    const uint32_t sb = mx_scale_byte(am);
+    const uint32_t c = e2m1_code(x.x, sb) | (e2m1_code(x.y, sb) << 4) | (e2m1_code(x.z, sb) << 8) |
+                       (e2m1_code(x.w, sb) << 12);
+    *(uint16_t*)(Q + it * 2) = (uint16_t)c;
+    if ((it & 7) == 0) X[it / 8] = (uint8_t)sb;
+  }
+}
+
+hipError_t launch_quantise_fp4(const QuantArgs& a, int D, int R, int hkv, hipStream_t st) {
+  const int64_t items = a.nnode * R * (D / 4);
+  int64_t x = (items + 255) / 256;
+  if (x > 4096) x = 4096;
+  if (x < 1) x = 1;
+#define ZHA_CASE(DD, RR)                                                                               \
+  if (D == DD && R == RR) {                                                                            \
+    hipLaunchKernelGGL((quantise_fp4_kernel<DD, RR>), dim3((unsigned)x, (unsigned)hkv), dim3(256), 0, st, a); \
+    return hipGetLastError();                                                                          \
   }
   ZHA_CASE(64, 1) ZHA_CASE(64, 2) ZHA_CASE(64, 4) ZHA_CASE(64, 8) ZHA_CASE(64, 16)
   ZHA_CASE(128, 1) ZHA_CASE(128, 2) ZHA_CASE(128, 4) ZHA_CASE(128, 8) ZHA_CASE(128, 16)

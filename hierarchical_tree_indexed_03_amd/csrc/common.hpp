@@ -36,6 +36,20 @@ __device__ __forceinline__ uint32_t f2bf16_bits(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// OCP MX FP4 of 32 consecutive elements: scale X = 2^(floor(log2 amax) - 2), stored as the
+// biased exponent byte E8M0 = floor(log2 amax) - 2 + 127 (0 for an all-zero block); each
+// element the nearest of X*{0,.5,1,1.5,2,3,4,6} (ties to the even code, clamped at 6X).
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+  const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu);   // biased exponent of amax
+  return amax > 0.f ? (uint32_t)(e >= 2 ? e - 2 : 0) : 0u;
+}
+__device__ __forceinline__ uint32_t e2m1_code(float x, uint32_t scale_byte) {
+  // x / X exactly: a power-of-two scaling
+  const float a = fabsf(x) * __uint_as_float((uint32_t)(254 - (int)scale_byte) << 23);
+  const uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.f);
+  return m | (x < 0.f ? 8u : 0u);
+}
+
 // Order-preserving map float -> uint32 (a < b  <=>  key(a) < key(b)).
 __device__ __forceinline__ uint32_t f2key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -99,6 +113,9 @@ struct Dev {
   float* lse[MAXL + 1];     // level l: [Hkv][ncap[l]][R] log mass at r_j (build/append only)
   bf16_t* sq[MAXL + 1];     // level l: [Hkv][ncap[l]][R][D] the router's bf16 copy of s (bf16
                             // router planes only; null at a level the router reads no planes of)
+  uint8_t* s4[MAXL + 1];    // level l: [Hkv][ncap[l]][R][D/2] the router's FP4 copy of s (MX FP4
+                            // router planes only): E2M1 codes, element 2i in the low nibble of byte i
+  uint8_t* s4x[MAXL + 1];   // level l: [Hkv][ncap[l]][R][D/32] E8M0 scale of each 32 elements
   float* w1;                // [Hkv][ncap[1]][R][b] token weights of the level-1 planes
                             // (key-form scoring only; null otherwise)
   int64_t ncap[MAXL + 1];   // node capacity per level (index 0: gather list = ncap[1])

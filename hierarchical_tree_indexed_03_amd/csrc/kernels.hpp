@@ -23,6 +23,12 @@ struct ParentArgs {
   int64_t nchild;     // nodes at `level - 1`
 };
 
+struct QuantArgs {
+  Dev dev;
+  int32_t level;
+  int64_t nnode;      // nodes of the level to quantise (from node 0)
+};
+
 struct AppendArgs {
   void* K;
   void* V;
@@ -52,7 +58,7 @@ struct RouteArgs {
   int32_t sel_p;      // top-p histogram / classify workgroups per KV head at `level`
   int32_t key_form;   // level 1 scored from the block's keys and the planes' token weights
   int32_t q_bf16;     // q (and the caches) are bf16; else fp32
-  int32_t planes_bf16;   // scores read the bf16 copies dev.sq
+  int32_t planes;     // router planes read: 0 fp32 (dev.s), 1 bf16 (dev.sq), 2 MX FP4 (dev.s4, dev.s4x)
   const void* K;      // key cache [Hkv][kcap][D] (key-form scoring)
   int64_t kcap;
   int64_t nl[MAXL + 1];   // nodes per level at N
@@ -76,6 +82,8 @@ hipError_t launch_build_tile(const BuildArgs& a, bool bf16, int D, int R, int64_
                              hipStream_t st);
 hipError_t launch_build_parent(const ParentArgs& a, int D, int R, int hkv, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, bool bf16, int D, int R, int hkv, hipStream_t st);
+// MX FP4 router copies (dev.s4, dev.s4x) of one level's float32 s.
+hipError_t launch_quantise_fp4(const QuantArgs& a, int D, int R, int hkv, hipStream_t st);
 
 // Routing: prep (q to fp32, state reset, top frontier) then per level the step sequence.
 hipError_t launch_route_prep(const RouteArgs& a, bool bf16, int D, hipStream_t st);

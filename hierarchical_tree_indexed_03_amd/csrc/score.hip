@@ -171,6 +171,54 @@ template <int D> struct PlaneRow<float, D> {
   }
 };
 
+// The same slice of an MX FP4 row: D/8 bytes of E2M1 codes (element 2i in the low nibble of
+// byte i) and the scale byte of the slice's 32-element block, widened on the fly to bf16 by
+// the scaled conversion (code value times 2^(scale - 127), exact in bf16).
+__device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, float sc) {
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3)));
+}
+template <int D>
+__device__ __forceinline__ void load_fp4_slice(const uint8_t* row, const uint8_t* xrow, int kg, bool ok,
+                                               uint4 (&b)[D / 32]) {
+  uint32_t w[D / 32];
+  if constexpr (D == 128) {
+    const uint4 t = ok ? *(const uint4*)(row + kg * 16) : make_uint4(0, 0, 0, 0);
+    w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+  } else {
+    const uint2 t = ok ? *(const uint2*)(row + kg * 8) : make_uint2(0, 0);
+    w[0] = t.x; w[1] = t.y;
+  }
+  const uint32_t sb = ok ? (uint32_t)xrow[(kg * (D / 4)) / 32] : 0u;
+  const float sc = __uint_as_float(sb << 23);          // 2^(sb - 127); an all-zero block: 0
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) b[i] = fp4x8_to_bf16(w[i], sc);
+}
+template <typename TQ, int D> struct Fp4Row;
+template <int D> struct Fp4Row<bf16_t, D> {
+  static constexpr int NL = Qk<bf16_t, D>::NL;
+  __device__ static void load(const uint8_t* row, const uint8_t* xrow, int kg, bool ok, uint4* k) {
+    uint4 b[D / 32];
+    load_fp4_slice<D>(row, xrow, kg, ok, b);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) k[i] = b[i];
+  }
+};
+template <int D> struct Fp4Row<float, D> {
+  static constexpr int NL = Qk<float, D>::NL;
+  __device__ static void load(const uint8_t* row, const uint8_t* xrow, int kg, bool ok, uint4* k) {
+    uint4 b[D / 32];
+    load_fp4_slice<D>(row, xrow, kg, ok, b);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      k[2 * i] = make_uint4(b[i].x << 16, b[i].x & 0xffff0000u, b[i].y << 16, b[i].y & 0xffff0000u);
+      k[2 * i + 1] = make_uint4(b[i].z << 16, b[i].z & 0xffff0000u, b[i].w << 16, b[i].w & 0xffff0000u);
+    }
+  }
+};
+
 // Scores from the bf16 copies of s: the tile Q (16 heads x D) . P^T (D x 16 plane rows) on
 // MFMA with the raw query as the A operand (bf16 x bf16 products are exact in the fp32
 // accumulator; fp32 queries take the fp32 MFMA on planes widened to fp32), then
@@ -179,7 +227,8 @@ template <int D> struct PlaneRow<float, D> {
 // id, offset and head mask are read by the lanes that read its planes; the max over a
 // node's R planes runs across R neighbouring lanes.  The next pass's node ids and masks are
 // loaded before this pass's planes.
-template <typename TQ, int D, int R>
+// With FP4 = true the rows are the MX FP4 copies, widened to bf16 as they are loaded.
+template <typename TQ, int D, int R, bool FP4>
 __global__ __launch_bounds__(256) void route_score_bf16_kernel(RouteArgs a) {
   constexpr int NPT = 16 / R;                 // nodes per 16-row tile
   constexpr int UN = ZHA_SCORE_UN_BF16;       // tiles in flight per wave
@@ -194,7 +243,9 @@ __global__ __launch_bounds__(256) void route_score_bf16_kernel(RouteArgs a) {
   const int64_t cap = a.dev.ncap[lv];
   const int32_t* nodes = a.dev.node[lv] + kv * cap;
   const uint32_t* masks = a.dev.mask[lv] + kv * cap;
-  const bf16_t* S = a.dev.sq[lv] + (int64_t)kv * cap * R * D;
+  const bf16_t* S = FP4 ? nullptr : a.dev.sq[lv] + (int64_t)kv * cap * R * D;
+  const uint8_t* S4 = FP4 ? a.dev.s4[lv] + (int64_t)kv * cap * R * (D / 2) : nullptr;
+  const uint8_t* X4 = FP4 ? a.dev.s4x[lv] + (int64_t)kv * cap * R * (D / 32) : nullptr;
   const float* C = a.dev.c[lv] + (int64_t)kv * cap * R;
   float* out = a.dev.score[lv] + (int64_t)kv * GMAX * cap;
   const int g = a.g;
@@ -232,7 +283,10 @@ __global__ __launch_bounds__(256) void route_score_bf16_kernel(RouteArgs a) {
     for (int u = 0; u < UN; ++u) {
       const bool ok = ncur[u] >= 0;
       const int64_t nd = ok ? ncur[u] : 0;
-      PlaneRow<TQ, D>::load(S + (nd * R + plane) * D, kg, ok, kf[u]);
+      if constexpr (FP4)
+        Fp4Row<TQ, D>::load(S4 + (nd * R + plane) * (D / 2), X4 + (nd * R + plane) * (D / 32), kg, ok, kf[u]);
+      else
+        PlaneRow<TQ, D>::load(S + (nd * R + plane) * D, kg, ok, kf[u]);
       cj[u] = ok ? C[nd * R + plane] : -INFINITY;
     }
 #pragma unroll
@@ -538,16 +592,30 @@ static void launch_score_bf16(const RouteArgs& a, int nlev, int64_t nodes, hipSt
     hipLaunchKernelGGL((route_score_bf16_rows_kernel<TQ, D, R>), dim3(grid_for(nodes, NPB, cap), (unsigned)a.hkv, (unsigned)nlev),
                        dim3(256), 0, st, a);
   } else {
-    static const int per_cu = resident_per_cu(route_score_bf16_kernel<TQ, D, R>, 256);
+    static const int per_cu = resident_per_cu(route_score_bf16_kernel<TQ, D, R, false>, 256);
     const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
-    hipLaunchKernelGGL((route_score_bf16_kernel<TQ, D, R>), dim3(grid_for(nodes, NPB, cap), (unsigned)a.hkv, (unsigned)nlev),
+    hipLaunchKernelGGL((route_score_bf16_kernel<TQ, D, R, false>), dim3(grid_for(nodes, NPB, cap), (unsigned)a.hkv, (unsigned)nlev),
                        dim3(256), 0, st, a);
   }
 }
 
+template <typename TQ, int D, int R>
+static void launch_score_fp4(const RouteArgs& a, int nlev, int64_t nodes, hipStream_t st) {
+  constexpr int NPB = 4 * (16 / R) * ZHA_SCORE_UN_BF16;   // nodes per block pass
+  static const int per_cu = resident_per_cu(route_score_bf16_kernel<TQ, D, R, true>, 256);
+  const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
+  hipLaunchKernelGGL((route_score_bf16_kernel<TQ, D, R, true>), dim3(grid_for(nodes, NPB, cap), (unsigned)a.hkv, (unsigned)nlev),
+                     dim3(256), 0, st, a);
+}
+
 template <int D, int R>
 static void launch_score_planes(const RouteArgs& a, int nlev, int64_t nodes, hipStream_t st) {
-  if (a.planes_bf16) {
+  if (a.planes == 2) {
+    if (a.q_bf16) launch_score_fp4<bf16_t, D, R>(a, nlev, nodes, st);
+    else launch_score_fp4<float, D, R>(a, nlev, nodes, st);
+    return;
+  }
+  if (a.planes == 1) {
     if (a.q_bf16) launch_score_bf16<bf16_t, D, R>(a, nlev, nodes, st);
     else launch_score_bf16<float, D, R>(a, nlev, nodes, st);
     return;

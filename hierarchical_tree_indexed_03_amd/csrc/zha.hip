@@ -107,7 +107,7 @@ zha_status validate(const zha_config* c) {
   if (c->dtype != ZHA_F32 && c->dtype != ZHA_BF16) return fail(ZHA_E_INVALID, "dtype %d", c->dtype);
   if (!(c->top_p > 0.f && c->top_p <= 1.f)) return fail(ZHA_E_INVALID, "top_p %g outside (0, 1]", c->top_p);
   if (c->keep_sink != 0 && c->keep_sink != 1) return fail(ZHA_E_INVALID, "keep_sink %d", c->keep_sink);
-  if (c->plane_dtype != ZHA_F32 && c->plane_dtype != ZHA_BF16)
+  if (c->plane_dtype != ZHA_F32 && c->plane_dtype != ZHA_BF16 && c->plane_dtype != ZHA_MXFP4)
     return fail(ZHA_E_INVALID, "plane_dtype %d", c->plane_dtype);
   if (c->dtype == ZHA_F32 && c->head_dim == 128 && c->block > 128)
     return fail(ZHA_E_UNSUPPORTED, "float32 keys with head_dim 128 need block <= 128");
@@ -147,6 +147,11 @@ size_t layout(const zha_config& c, char* base, Dev* dev) {
   if (key_form(c)) d.w1 = (float*)take((size_t)(H * d.ncap[1] * R * c.block) * 4);
   if (c.plane_dtype == ZHA_BF16)
     for (int l = key_form(c) ? 2 : 1; l <= L; ++l) d.sq[l] = (bf16_t*)take((size_t)(H * d.ncap[l] * R * D) * 2);
+  if (c.plane_dtype == ZHA_MXFP4)
+    for (int l = key_form(c) ? 2 : 1; l <= L; ++l) {
+      d.s4[l] = (uint8_t*)take((size_t)(H * d.ncap[l] * R * D) / 2);
+      d.s4x[l] = (uint8_t*)take((size_t)(H * d.ncap[l] * R * D) / 32);
+    }
   d.cnt = (int32_t*)take((size_t)((MAXL + 1) * H) * 4);
   d.qs = (QState*)take((size_t)((L + 1) * Q) * sizeof(QState));
   d.hpart = (uint64_t*)take((size_t)(H * SEL_P * GMAX * NB1) * 8);
@@ -182,7 +187,7 @@ RouteArgs route_args(const zha_tree* t, const void* q) {
   a.sigma = 1.0f / sqrtf((float)t->cfg.head_dim);
   a.key_form = key_form(t->cfg) ? 1 : 0;
   a.q_bf16 = t->cfg.dtype == ZHA_BF16 ? 1 : 0;
-  a.planes_bf16 = t->cfg.plane_dtype == ZHA_BF16 ? 1 : 0;
+  a.planes = t->cfg.plane_dtype;
   a.K = t->K;
   a.kcap = t->cfg.capacity;
   for (int l = 1; l <= t->cfg.levels; ++l) a.nl[l] = nodes_at(t->cfg, l, t->N);
@@ -307,6 +312,20 @@ zha_status zha_tree_build(zha_tree* t, void* k_cache, void* v_cache, int64_t n_t
       e = launch_build_parent(p, c.head_dim, c.num_ref, c.num_kv_heads, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "build parent launch");
+  }
+  // FP4 router copies of every routed level, from the finished float32 planes
+  for (int v = 1; v <= c.levels; ++v) {
+    if (!t->dev.s4[v]) continue;
+    QuantArgs q;
+    memset(&q, 0, sizeof q);
+    q.dev = t->dev;
+    q.level = v;
+    q.nnode = nodes_at(c, v, n_tokens);
+    {
+      ProfScope ps(t, lvkey("build_quant", v), stream);
+      e = launch_quantise_fp4(q, c.head_dim, c.num_ref, c.num_kv_heads, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "fp4 quantise launch");
   }
   t->K = k_cache;
   t->V = v_cache;
@@ -466,18 +485,25 @@ zha_status zha_debug_level(zha_tree* t, int32_t level, float* s_out, float* c_ou
   return ZHA_OK;
 }
 
-zha_status zha_debug_router_planes(zha_tree* t, int32_t level, void* s_out, hipStream_t stream) {
+zha_status zha_debug_router_planes(zha_tree* t, int32_t level, void* s_out, void* scale_out, hipStream_t stream) {
   if (!t) return fail(ZHA_E_INVALID, "tree is null");
   if (!t->built) return fail(ZHA_E_STATE, "no tree built");
   if (level < 1 || level > t->cfg.levels) return fail(ZHA_E_INVALID, "level %d outside 1..%d", level, t->cfg.levels);
   if (!s_out) return fail(ZHA_E_INVALID, "null output");
-  if (!t->dev.sq[level]) return fail(ZHA_E_INVALID, "no bf16 router planes at level %d", level);
+  const bool fp4 = t->dev.s4[level] != nullptr;
+  if (!t->dev.sq[level] && !fp4) return fail(ZHA_E_INVALID, "no quantised router planes at level %d", level);
+  if (fp4 && !scale_out) return fail(ZHA_E_INVALID, "null scale output");
   const zha_config& c = t->cfg;
   const int64_t n = nodes_at(c, level, t->N), cap = t->dev.ncap[level];
-  const size_t srow = (size_t)c.num_ref * c.head_dim * 2;
+  const size_t rd = (size_t)c.num_ref * c.head_dim;
+  const size_t srow = fp4 ? rd / 2 : rd * 2, xrow = rd / 32;
+  const char* src = fp4 ? (const char*)t->dev.s4[level] : (const char*)t->dev.sq[level];
   for (int kv = 0; kv < c.num_kv_heads; ++kv) {
-    hipError_t e = hipMemcpyAsync((char*)s_out + kv * n * srow, (char*)t->dev.sq[level] + kv * cap * srow, n * srow,
+    hipError_t e = hipMemcpyAsync((char*)s_out + kv * n * srow, src + kv * cap * srow, n * srow,
                                   hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess && fp4)
+      e = hipMemcpyAsync((char*)scale_out + kv * n * xrow, (const char*)t->dev.s4x[level] + kv * cap * xrow, n * xrow,
+                         hipMemcpyDeviceToDevice, stream);
     if (e != hipSuccess) return hip_fail(e, "router plane copy");
   }
   return ZHA_OK;

@@ -15,7 +15,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("ZHA_LIB_PATH") or os.path.join(_HERE, "libzha.so")
 
-ZHA_F32, ZHA_BF16 = 0, 1
+ZHA_F32, ZHA_BF16, ZHA_MXFP4 = 0, 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "capacity exceeded",
           4: "workspace too small", 5: "call out of order", 6: "HIP runtime error"}
 GMAX = 8
@@ -50,7 +50,7 @@ def _load() -> ctypes.CDLL:
         "zha_decode": (I32, [P, P, P, P, P]),
         "zha_decode_dense": (I32, [P, P, P, P]),
         "zha_debug_level": (I32, [P, I32, P, P, P]),
-        "zha_debug_router_planes": (I32, [P, I32, P, P]),
+        "zha_debug_router_planes": (I32, [P, I32, P, P, P]),
         "zha_debug_trace": (I32, [P, I32, I64, P, P, P, P, P, P]),
         "zha_debug_route_level": (I32, [P, I32, P, P, P, P, I64, P]),
         "zha_profile_start": (I32, [P, ctypes.c_char_p]),
@@ -96,7 +96,11 @@ def _check(status: int):
 
 
 def _dtype(x) -> int:
-    return x if isinstance(x, int) else (ZHA_BF16 if x in ("bf16", torch.bfloat16) else ZHA_F32)
+    if isinstance(x, int):
+        return x
+    if x in ("bf16", torch.bfloat16):
+        return ZHA_BF16
+    return ZHA_MXFP4 if x in ("fp4", "mxfp4") else ZHA_F32
 
 
 def make_config(head_dim, num_kv_heads, num_q_heads, block, levels, num_ref, capacity, dtype, top_p,
@@ -139,8 +143,8 @@ def zha_debug_level(t, level: int, s_out, c_out, stream=None):
     _check(_lib.zha_debug_level(t, int(level), _p(s_out), _p(c_out), _s(stream)))
 
 
-def zha_debug_router_planes(t, level: int, s_out, stream=None):
-    _check(_lib.zha_debug_router_planes(t, int(level), _p(s_out), _s(stream)))
+def zha_debug_router_planes(t, level: int, s_out, scale_out=None, stream=None):
+    _check(_lib.zha_debug_router_planes(t, int(level), _p(s_out), _p(scale_out), _s(stream)))
 
 
 def zha_debug_trace(t, level: int, cap: int, nodes, masks, scores, keep, counts, stream=None):
@@ -244,10 +248,17 @@ class Tree:
         return s, cc
 
     def router_planes(self, level: int):
-        """The bf16 copy of s that routing reads at ``level`` ([Hkv, n, R, d] bfloat16)."""
+        """The quantised copy of s that routing reads at ``level``: bf16 planes give a
+        [Hkv, n, R, d] bfloat16 tensor; MX FP4 planes give (codes [Hkv, n, R, d/2] uint8,
+        scales [Hkv, n, R, d/32] uint8)."""
         c = self.cfg
-        s = torch.empty(c.num_kv_heads, self.nodes(level), c.num_ref, c.head_dim, dtype=torch.bfloat16,
-                        device=self.workspace.device)
+        n, dev = self.nodes(level), self.workspace.device
+        if c.plane_dtype == ZHA_MXFP4:
+            q = torch.empty(c.num_kv_heads, n, c.num_ref, c.head_dim // 2, dtype=torch.uint8, device=dev)
+            x = torch.empty(c.num_kv_heads, n, c.num_ref, c.head_dim // 32, dtype=torch.uint8, device=dev)
+            zha_debug_router_planes(self.handle, level, q, x)
+            return q, x
+        s = torch.empty(c.num_kv_heads, n, c.num_ref, c.head_dim, dtype=torch.bfloat16, device=dev)
         zha_debug_router_planes(self.handle, level, s)
         return s
 

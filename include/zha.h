@@ -52,7 +52,7 @@ typedef enum {
   ZHA_E_HIP = 6           /* a HIP runtime call failed; see zha_last_error()       */
 } zha_status;
 
-typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1 } zha_dtype;
+typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1, ZHA_MXFP4 = 2 /* router planes only */ } zha_dtype;
 
 typedef struct {
   int32_t head_dim;       /* d: 64 or 128                                               */
@@ -66,13 +66,19 @@ typedef struct {
   float top_p;            /* p in (0, 1]; p = 1 keeps every node (dense attention)     */
   int32_t keep_sink;      /* 1: token 0 is always attended                              */
   int32_t plane_dtype;    /* zha_dtype of the s vectors the router reads (0 = float32).
-                           * ZHA_BF16: the tree is still built and kept in float32; each
-                           * plane the router scores from also gets a bfloat16 copy of s
-                           * (nearest value, ties to even) and routing reads that copy with
-                           * the float32 offset c_j, halving the plane bytes per node.  The
-                           * pages give no storage precision for the planes; this is a
-                           * stated quantiser.  A level-1 scored from the keys (see
-                           * zha_level1_key_form) reads no planes and keeps no copy.      */
+                           * The tree is always built and kept in float32; with ZHA_BF16 or
+                           * ZHA_MXFP4 each plane the router scores from also gets a
+                           * quantised copy of s, and routing reads that copy with the
+                           * float32 offset c_j.  The pages give no storage precision for
+                           * the planes; these are stated quantisers:
+                           *   ZHA_BF16: each element the nearest bfloat16 (ties to even);
+                           *     R*(2d+4) bytes per node instead of R*(4d+4);
+                           *   ZHA_MXFP4: OCP MX FP4, per 32 elements one power-of-two
+                           *     scale X = 2^(floor(log2 amax) - 2) (one E8M0 byte) and
+                           *     E2M1 elements (nearest of X*{0,.5,1,1.5,2,3,4,6}, ties to
+                           *     the even code, clamped at 6X); R*(d/2+d/32+4) bytes.
+                           * A level 1 scored from the keys (see zha_level1_key_form)
+                           * reads no planes and keeps no copy.                           */
 } zha_config;
 
 typedef struct zha_tree zha_tree;   /* opaque host-side handle */
@@ -142,11 +148,17 @@ zha_status zha_set_top_p_levels(zha_tree* t, const float* p_levels);
 zha_status zha_debug_level(zha_tree* t, int32_t level, float* s_out, float* c_out,
                            hipStream_t stream);
 
-/* Copies the bfloat16 copy of s that routing reads at level `level` (bf16 router planes):
- *   s_out (device) bfloat16 [Hkv][n_l][R][d].  ZHA_E_INVALID if the handle keeps no such
- *   copy at that level (float32 router planes, or a level 1 scored from the keys).
- *   Enqueued copies only (no synchronisation). */
-zha_status zha_debug_router_planes(zha_tree* t, int32_t level, void* s_out, hipStream_t stream);
+/* Copies the quantised copy of s that routing reads at level `level`:
+ *   ZHA_BF16:  s_out (device) bfloat16 [Hkv][n_l][R][d]; scale_out unused (may be null);
+ *   ZHA_MXFP4: s_out (device) uint8 [Hkv][n_l][R][d/2], element 2i in the low 4 bits of
+ *              byte i and element 2i+1 in the high 4 bits (E2M1 codes: bit 3 the sign,
+ *              bits 0-2 the magnitude index into {0,.5,1,1.5,2,3,4,6});
+ *              scale_out (device) uint8 [Hkv][n_l][R][d/32], the E8M0 block scales
+ *              (X = 2^(byte - 127)).
+ * ZHA_E_INVALID if the handle keeps no such copy at that level (float32 router planes, or
+ * a level 1 scored from the keys).  Enqueued copies only (no synchronisation). */
+zha_status zha_debug_router_planes(zha_tree* t, int32_t level, void* s_out, void* scale_out,
+                                   hipStream_t stream);
 
 /* Routing trace of the last zha_decode / zha_debug_route_level on this handle, for level
  * `level` (levels..1; 0 = the kept level-1 blocks).  Copies into caller device buffers

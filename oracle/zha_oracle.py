@@ -189,7 +189,7 @@ E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])   # FP4 magnitudes, co
 MX_BLOCK = 32
 
 
-def mxfp4_round(x: np.ndarray) -> np.ndarray:
+def mxfp4_round(x: np.ndarray, scale_exp=None) -> np.ndarray:
     """OCP MX FP4 round trip of each row (last axis, a multiple of 32 long), as float64.
 
     Each block of 32 consecutive elements shares a power-of-two scale X = 2^(floor(log2
@@ -197,13 +197,18 @@ def mxfp4_round(x: np.ndarray) -> np.ndarray:
     element format (largest value 6 = 1.5 * 2^2), so amax / X lies in [4, 8).  Each element
     becomes the nearest of X * {0, 0.5, 1, 1.5, 2, 3, 4, 6} with its sign; a value halfway
     between two of them takes the one whose mantissa bit is 0 (code even); magnitudes above
-    6X become 6X.  An all-zero block stays zero.
+    6X become 6X.  An all-zero block stays zero.  ``scale_exp`` (one integer per block)
+    imposes log2 X instead (the comparison tests use it to bound the result when a block's
+    amax sits at a power of two).
     """
     x = np.asarray(x, dtype=np.float64)
     xb = x.reshape(-1, MX_BLOCK)
     amax = np.max(np.abs(xb), axis=1)
     _, e = np.frexp(amax)                       # amax = m * 2^e, 1/2 <= m < 1
-    scale = np.where(amax > 0, np.ldexp(1.0, e - 1 - 2), 1.0)[:, None]
+    if scale_exp is None:
+        scale = np.where(amax > 0, np.ldexp(1.0, e - 1 - 2), 1.0)[:, None]
+    else:
+        scale = np.ldexp(1.0, np.asarray(scale_exp, dtype=np.int64).reshape(-1))[:, None]
     a = np.abs(xb) / scale
     hi_i = np.clip(np.searchsorted(E2M1, a), 0, len(E2M1) - 1)
     lo_i = np.clip(hi_i - 1, 0, len(E2M1) - 1)

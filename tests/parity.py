@@ -8,12 +8,14 @@ Tolerances (stated once here, used by every GPU test):
     order); end to end, the descendants of such a node are excluded from later levels;
   * outputs: max|o_gpu - o_ref| <= 1e-2 * max|o_ref| (bf16 inputs, fp32 accumulation).
 
-bf16 router planes: the oracle routes over its planes with s rounded to bf16 (oracle
-``quantise_planes``) at the levels the router reads planes at.  The GPU rounds its fp32 s,
-which lies within S_BAND of the oracle's fp64 s (checked element by element); an element
-of s within S_BAND of a bf16 rounding midpoint may round either way on the two sides.
-Each node's score tolerance therefore adds sigma * max_j sum_i |q_i| (hi_ji - lo_ji), hi and
-lo the roundings of s +- S_BAND (zero for every element away from a midpoint).
+Quantised router planes (bf16, MX FP4): the oracle routes over its planes with s
+quantised (oracle ``quantise_planes``) at the levels the router reads planes at.  The GPU
+quantises its fp32 s, which lies within S_BAND of the oracle's fp64 s (checked element by
+element).  Quantisation is monotone in each element for a fixed block scale, so the GPU's
+value lies in [lo, hi]: lo / hi the quantisation of s - S_BAND / s + S_BAND, taken over
+every FP4 block scale that an amax within S_BAND can give.  Each node's score tolerance
+adds sigma * max_j sum_i |q_i| (hi_ji - lo_ji) (zero where lo = hi, which holds for every
+element away from a rounding midpoint or a scale boundary).
 """
 from __future__ import annotations
 
@@ -55,23 +57,56 @@ def router_levels(w: wc.Workload) -> list:
 
 
 def router_trees(w: wc.Workload, trees: list) -> list:
-    """The oracle trees as the router sees them: with bf16 router planes, s rounded to bf16
+    """The oracle trees as the router sees them: with quantised router planes, s quantised
     at the levels the router reads planes at."""
-    if w.planes != "bf16":
+    if w.planes == "f32":
         return trees
     lv = router_levels(w)
-    return [zo.quantise_planes(t, lv) for t in trees]
+    return [zo.quantise_planes(t, lv, w.planes) for t in trees]
+
+
+def quant_bounds(fmt: str, s: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """[lo, hi] of the quantised value of every element of s (rows of d) when each element
+    may move by up to S_BAND (see the module docstring)."""
+    if fmt == "bf16":
+        return zo.bf16_round(s - S_BAND), zo.bf16_round(s + S_BAND)
+    sb = s.reshape(-1, zo.MX_BLOCK)
+    amax = np.max(np.abs(sb), axis=1)
+    lo = hi = None
+    for a in (np.maximum(amax - S_BAND, 1e-300), amax + S_BAND):
+        _, e = np.frexp(a)
+        ql = zo.mxfp4_round(sb - S_BAND, e - 3)
+        qh = zo.mxfp4_round(sb + S_BAND, e - 3)
+        lo = ql if lo is None else np.minimum(lo, ql)
+        hi = qh if hi is None else np.maximum(hi, qh)
+    tiny = (amax <= S_BAND)[:, None]           # a block within the band of zero
+    lo = np.where(tiny, -3 * S_BAND, lo)
+    hi = np.where(tiny, 3 * S_BAND, hi)
+    return lo.reshape(s.shape), hi.reshape(s.shape)
 
 
 def flip_allowance(w: wc.Workload, tree, level: int, nodes, q) -> np.ndarray:
-    """Extra score tolerance per node for bf16 router planes (see the module docstring);
-    zero for f32 planes and for a key-form level 1.  ``tree`` is the full-precision tree."""
+    """Extra score tolerance per node for quantised router planes (see the module
+    docstring); zero for f32 planes and for a key-form level 1.  ``tree`` is the
+    full-precision tree."""
     nodes = np.asarray(nodes, dtype=np.int64)
-    if w.planes != "bf16" or level not in router_levels(w):
+    if w.planes == "f32" or level not in router_levels(w):
         return np.zeros(len(nodes))
     s = tree.levels[level - 1][0][nodes]
-    gap = zo.bf16_round(s + S_BAND) - zo.bf16_round(s - S_BAND)
-    return np.max(gap @ np.abs(np.asarray(q, dtype=np.float64)), axis=1) / np.sqrt(len(q))
+    lo, hi = quant_bounds(w.planes, s)
+    return np.max((hi - lo) @ np.abs(np.asarray(q, dtype=np.float64)), axis=1) / np.sqrt(len(q))
+
+
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+
+
+def decode_fp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Values of the GPU's MX FP4 copy (codes [..., d/2] uint8, scales [..., d/32] uint8),
+    following the layout zha.h documents."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    el = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(*codes.shape[:-1], -1)
+    x = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)
+    return E2M1_VALUES[el] * np.repeat(x, zo.MX_BLOCK, axis=-1)
 
 
 def upload(x: np.ndarray, w: wc.Workload) -> torch.Tensor:
@@ -154,6 +189,10 @@ def compare_route(route: dict, trace: dict, gi: int, b: int, p, tol_fn=None) -> 
         ok, nb = exempt_nodes(rec, p if np.ndim(p) == 0 else p[lv - 1], diff, tol)
         exempt += [(lv, n) for n in ok]
         bad += [("kept", lv) + x for x in nb]
+        if lv == 1:
+            # the gathered blocks are level-1 nodes: an exempt one is excluded itself
+            excluded = excluded | set(ok)
+            break
         nxt = set()
         for n in excluded | set(ok):
             nxt.update(range(n * b, n * b + b))

@@ -48,7 +48,7 @@ BAD = [
     (dict(num_q_heads=4 * 9), 2), (dict(block=1), 1), (dict(block=257), 1), (dict(levels=0), 1),
     (dict(levels=17), 1), (dict(num_ref=3), 2), (dict(capacity=0), 1), (dict(capacity=1 << 31), 1),
     (dict(dtype=5), 1), (dict(top_p=0.0), 1), (dict(top_p=1.5), 1), (dict(top_p=float("nan")), 1),
-    (dict(dtype="f32", block=256), 2), (dict(planes=2), 1), (dict(planes=-1), 1),
+    (dict(dtype="f32", block=256), 2), (dict(planes=3), 1), (dict(planes=-1), 1),
 ]
 
 
@@ -98,26 +98,31 @@ def test_level1_key_form_choice(zha):
     assert ws_key > ws_f32
 
 
-def test_bf16_router_planes_workspace(zha):
-    """bf16 router planes add one bf16 copy of s per level the router reads planes at: every
-    level but a key-form level 1 (whose planes the router never reads)."""
+@pytest.mark.parametrize("fmt", ["bf16", "fp4"])
+def test_quantised_router_planes_workspace(zha, fmt):
+    """Quantised router planes add one copy of s per level the router reads planes at: every
+    level but a key-form level 1 (whose planes the router never reads).  bf16: R x d x 2
+    bytes per node; MX FP4: R x d / 2 bytes of codes plus R x d / 32 scale bytes."""
     D, H, cap = 128, 4, 1 << 18
 
+    def slot(nbytes):
+        return -(-nbytes // 256) * 256
+
     def planes_bytes(levels, b, R):
-        # per-level node capacity rounded to 64 nodes, R x d bf16 per node, 256-byte slots
+        # per-level node capacity rounded to 64 nodes, 256-byte aligned slots
         tot = 0
         for lv in levels:
             n = -(-cap // b ** lv)
             n = -(-n // 64) * 64
-            tot += -(-(H * n * R * D * 2) // 256) * 256
+            tot += slot(H * n * R * D * 2) if fmt == "bf16" else slot(H * n * R * D // 2) + slot(H * n * R * D // 32)
         return tot
     # key-form level 1 (bf16, b 4, R 16): levels 2..6 get a copy
     f = zha.zha_workspace_bytes(good(zha))
-    q = zha.zha_workspace_bytes(good(zha, planes="bf16"))
+    q = zha.zha_workspace_bytes(good(zha, planes=fmt))
     assert q - f == planes_bytes(range(2, 7), 4, 16)
     # planes read at level 1 too (b 8, R 1)
     f = zha.zha_workspace_bytes(good(zha, block=8, num_ref=1, levels=7))
-    q = zha.zha_workspace_bytes(good(zha, block=8, num_ref=1, levels=7, planes="bf16"))
+    q = zha.zha_workspace_bytes(good(zha, block=8, num_ref=1, levels=7, planes=fmt))
     assert q - f == planes_bytes(range(1, 8), 8, 1)
 
 

@@ -1,11 +1,13 @@
-"""GPU parity of bf16 router planes (zha_config.plane_dtype = bf16) against the oracle.
+"""GPU parity of quantised router planes (zha_config.plane_dtype bf16 and MX FP4) against
+the oracle.
 
-The oracle routes over its planes with s rounded to bf16 at every level the router reads
-planes at (all but a key-form level 1); offsets stay full precision.  Checked here:
+The oracle routes over its planes with s quantised (bf16, or OCP MX FP4 with a scale per
+32 elements) at every level the router reads planes at (all but a key-form level 1);
+offsets stay full precision.  Checked here, for both formats:
 
 * the quantiser, element by element: the GPU's fp32 s lies within S_BAND of the oracle's
-  fp64 s, and the GPU's bf16 copy equals the oracle's rounding of s wherever the rounding
-  of s - S_BAND and s + S_BAND agree (else it lies between those two roundings);
+  fp64 s, and the GPU's quantised copy equals the oracle's quantisation of s wherever the
+  bounds [lo, hi] of tests/parity.py coincide (else it lies between them);
 * teacher-forced scores on the oracle's frontiers, within SCORE_TOL plus each node's
   rounding-flip allowance, and the kept sets (tests/parity.py rules);
 * decode end to end after appends (the append refreshes the bf16 copies).
@@ -26,16 +28,17 @@ from workloads import configs as wc, gen
 
 pytestmark = pytest.mark.gpu
 
-SMALL = {
-    "tiny": wc.TINY.with_(planes="bf16"),
-    "tiny_r16": wc.TINY.with_(num_ref=16, planes="bf16"),
-    "deep_small": wc.DEEP.with_(n_tokens=16_384 + 37, steps=2, planes="bf16"),
-    "wide_small": wc.WIDE.with_(n_tokens=8_192 + 100, steps=2, planes="bf16"),
-    "light_small": wc.light(32_768, steps=2).with_(n_tokens=32_768 - 5, planes="bf16"),
+GEOMS = {
+    "tiny": wc.TINY,
+    "tiny_r16": wc.TINY.with_(num_ref=16),
+    "deep_small": wc.DEEP.with_(n_tokens=16_384 + 37, steps=2),
+    "wide_small": wc.WIDE.with_(n_tokens=8_192 + 100, steps=2),
+    "light_small": wc.light(32_768, steps=2).with_(n_tokens=32_768 - 5),
     # level 1 holds 36,001 nodes: scored from the union list, selected by the large-level path
-    "light_general": wc.light(288_003, steps=1).with_(num_kv_heads=1, num_q_heads=8, planes="bf16"),
-    "ultra_small": wc.ULTRA.with_(n_tokens=70_001, steps=2, planes="bf16"),
+    "light_general": wc.light(288_003, steps=1).with_(num_kv_heads=1, num_q_heads=8),
+    "ultra_small": wc.ULTRA.with_(n_tokens=70_001, steps=2),
 }
+SMALL = {f"{fmt}-{name}": w.with_(planes=fmt) for fmt in ("bf16", "fp4") for name, w in GEOMS.items()}
 
 
 class Case:
@@ -83,15 +86,20 @@ def check_quantiser(c: Case):
                 c.t.router_planes(lv)
             continue
         s32 = c.t.level(lv)[0].cpu().numpy().astype(np.float64)
-        sq = c.t.router_planes(lv).float().cpu().numpy().astype(np.float64)
+        rp = c.t.router_planes(lv)
+        if w.planes == "fp4":
+            sq = P.decode_fp4(rp[0].cpu().numpy(), rp[1].cpu().numpy())
+        else:
+            sq = rp.float().cpu().numpy().astype(np.float64)
         for h in range(w.num_kv_heads):
             so = c.trees[h].levels[lv - 1][0]
             err = float(np.max(np.abs(s32[h] - so)))
             assert err <= P.S_BAND, f"level {lv} head {h}: fp32 s differs from the oracle by {err:.2e}"
-            lo, hi, mid = zo.bf16_round(so - P.S_BAND), zo.bf16_round(so + P.S_BAND), zo.bf16_round(so)
+            lo, hi = P.quant_bounds(w.planes, so)
+            mid = zo.QUANTISERS[w.planes](so)
             sure = lo == hi
             assert np.array_equal(sq[h][sure], mid[sure]), f"level {lv} head {h}: bf16 copy differs"
-            # rounding is monotone: s_gpu within S_BAND of s rounds into [lo, hi]
+            # quantisation is monotone for a fixed scale: s_gpu within S_BAND of s lands in [lo, hi]
             assert np.all((sq[h] >= lo) & (sq[h] <= hi)), f"level {lv} head {h}: bf16 copy outside [lo, hi]"
 
 
