@@ -145,8 +145,9 @@ __global__ __launch_bounds__(256) void build_tile_kernel(BuildArgs a) {
       kreg[u] = row < ntt ? *(const uint4*)(Kg + (int64_t)i * CH) : make_uint4(0, 0, 0, 0);
     }
   };
-  if ((int64_t)blockIdx.x < ntiles) load_tile(blockIdx.x);
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  // tiles a.tile0 .. ntiles-1 (a.tile0 > 0: the tail of a multi-token append)
+  if (a.tile0 + (int64_t)blockIdx.x < ntiles) load_tile(a.tile0 + blockIdx.x);
+  for (int64_t tile = a.tile0 + blockIdx.x; tile < ntiles; tile += gridDim.x) {
   const int64_t t0 = tile * T;
   const int nt = (int)min((int64_t)T, a.N - t0);
 #pragma unroll
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(256) void build_parent_kernel(ParentArgs a) {
   __shared__ float Lp[PPB * R];
   __shared__ float Wp[PPB * 256 * R];
   const int kv = blockIdx.y;
-  const int64_t p0 = (int64_t)blockIdx.x * PPB;
+  const int64_t p0 = a.first + (int64_t)blockIdx.x * PPB;
   const int np = (int)min((int64_t)PPB, a.nparent - p0);
   if (np <= 0) return;
   parent_nodes<D, R>(a.dev, a.level, kv, a.b, p0, np, a.nchild, Lp, Wp);
@@ -571,7 +572,7 @@ template <typename TIn, int D, int R, int T>
 static void launch_build_tiles(const BuildArgs& a, int64_t ntiles, int hkv, hipStream_t st) {
   static const int per_cu = resident_per_cu(build_tile_kernel<TIn, D, R, T>, 256);
   int64_t x = (int64_t)per_cu * device_cus() / hkv;
-  if (x > ntiles) x = ntiles;
+  if (x > ntiles - a.tile0) x = ntiles - a.tile0;
   if (x < 1) x = 1;
   hipLaunchKernelGGL((build_tile_kernel<TIn, D, R, T>), dim3((unsigned)x, (unsigned)hkv), dim3(256), 0, st, a);
 }
@@ -609,7 +610,7 @@ hipError_t launch_build_parent(const ParentArgs& a, int D, int R, int hkv, hipSt
 #define ZHA_CASE(DD, RR)                                                                  \
   if (D == DD && R == RR) {                                                               \
     constexpr int PPB = parents_per_block<DD, RR>();                                      \
-    dim3 grid((unsigned)((a.nparent + PPB - 1) / PPB), (unsigned)hkv);                     \
+    dim3 grid((unsigned)((a.nparent - a.first + PPB - 1) / PPB), (unsigned)hkv);           \
     hipLaunchKernelGGL((build_parent_kernel<DD, RR>), grid, dim3(256), 0, st, a);         \
     return hipGetLastError();                                                             \
   }
@@ -630,7 +631,8 @@ __global__ __launch_bounds__(256) void quantise_fp4_kernel(QuantArgs a) {
   const float* S = a.dev.s[v] + (int64_t)kv * cap * R * D;
   uint8_t* Q = a.dev.s4[v] + (int64_t)kv * cap * R * D / 2;
   uint8_t* X = a.dev.s4x[v] + (int64_t)kv * cap * R * D / 32;
-  for (int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x; it < items; it += (int64_t)gridDim.x * 256) {
+  for (int64_t it = a.first * R * (D / 4) + (int64_t)blockIdx.x * 256 + threadIdx.x; it < items;
+       it += (int64_t)gridDim.x * 256) {
     const float4 x = *(const float4*)(S + it * 4);
     float am = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
     am = fmaxf(am, __shfl_xor(am, 1));
@@ -645,7 +647,7 @@ __global__ __launch_bounds__(256) void quantise_fp4_kernel(QuantArgs a) {
 }
 
 hipError_t launch_quantise_fp4(const QuantArgs& a, int D, int R, int hkv, hipStream_t st) {
-  const int64_t items = a.nnode * R * (D / 4);
+  const int64_t items = (a.nnode - a.first) * R * (D / 4);
   int64_t x = (items + 255) / 256;
   if (x > 4096) x = 4096;
   if (x < 1) x = 1;

@@ -12,6 +12,7 @@ struct BuildArgs {
   int32_t b;
   int32_t m;          // levels built inside one tile
   float sigma;
+  int64_t tile0;      // first tile to build (0: the whole tree)
   Dev dev;
 };
 
@@ -21,12 +22,14 @@ struct ParentArgs {
   int32_t b;
   int64_t nparent;    // nodes at `level`
   int64_t nchild;     // nodes at `level - 1`
+  int64_t first;      // first parent to build (0: the whole level)
 };
 
 struct QuantArgs {
   Dev dev;
   int32_t level;
-  int64_t nnode;      // nodes of the level to quantise (from node 0)
+  int64_t first;      // nodes first .. nnode-1 of the level are quantised
+  int64_t nnode;
 };
 
 struct AppendArgs {

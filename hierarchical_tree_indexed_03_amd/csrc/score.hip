@@ -524,10 +524,17 @@ __global__ __launch_bounds__(256) void route_score_keys_kernel(RouteArgs a) {
           wv[u][n][s] = (ok && col < R && k < B) ? W[(nd * R + col) * B + k] : 0.f;
         }
         // accumulator: c of planes 4kg..4kg+3 (absent planes -inf)
+        if constexpr (R >= 4) {
+          const bool okc = ok && 4 * kg < R;
+          const float4 c4 = okc ? *(const float4*)(C + nd * R + 4 * kg)
+                                : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+          cj[u][n][0] = c4.x; cj[u][n][1] = c4.y; cj[u][n][2] = c4.z; cj[u][n][3] = c4.w;
+        } else {
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int j = 4 * kg + e4;
-          cj[u][n][e4] = (ok && j < R) ? C[nd * R + j] : -INFINITY;
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int j = 4 * kg + e4;
+            cj[u][n][e4] = (ok && j < R) ? C[nd * R + j] : -INFINITY;
+          }
         }
       }
     }

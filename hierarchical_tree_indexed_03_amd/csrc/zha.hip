@@ -271,6 +271,71 @@ zha_status zha_create(const zha_config* cfg, void* workspace, size_t workspace_b
   return ZHA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Builds every node that covers a token in [from, to) (from = 0: the whole tree over
+// [0, to)): the key tiles from the one holding token `from`, the parents from the one
+// holding it, and the FP4 router copies of those nodes.
+zha_status enqueue_build(zha_tree* t, const void* k_cache, const void* refs, int64_t from, int64_t to,
+                         hipStream_t stream) {
+  const zha_config& c = t->cfg;
+  BuildArgs a;
+  memset(&a, 0, sizeof a);
+  a.K = k_cache;
+  a.refs = refs;
+  a.cap = c.capacity;
+  a.N = to;
+  a.b = c.block;
+  a.m = tile_levels(c);
+  a.sigma = 1.0f / sqrtf((float)c.head_dim);
+  a.dev = t->dev;
+  const int T = tile_tokens(c);
+  a.tile0 = from / T;
+  hipError_t e;
+  {
+    ProfScope ps(t, "build_tile", stream);
+    e = launch_build_tile(a, c.dtype == ZHA_BF16, c.head_dim, c.num_ref, ceil_div(to, T), c.num_kv_heads, T, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "build tile launch");
+  for (int v = a.m + 1; v <= c.levels; ++v) {
+    ParentArgs p;
+    memset(&p, 0, sizeof p);
+    p.dev = t->dev;
+    p.level = v;
+    p.b = c.block;
+    p.nparent = nodes_at(c, v, to);
+    p.nchild = nodes_at(c, v - 1, to);
+    p.first = from / ipow_sat(c.block, v);
+    {
+      ProfScope ps(t, lvkey("build_parent", v), stream);
+      e = launch_build_parent(p, c.head_dim, c.num_ref, c.num_kv_heads, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "build parent launch");
+  }
+  // FP4 router copies of the rebuilt nodes of every routed level, from the finished planes
+  for (int v = 1; v <= c.levels; ++v) {
+    if (!t->dev.s4[v]) continue;
+    QuantArgs q;
+    memset(&q, 0, sizeof q);
+    q.dev = t->dev;
+    q.level = v;
+    q.first = from / ipow_sat(c.block, v);
+    q.nnode = nodes_at(c, v, to);
+    {
+      ProfScope ps(t, lvkey("build_quant", v), stream);
+      e = launch_quantise_fp4(q, c.head_dim, c.num_ref, c.num_kv_heads, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "fp4 quantise launch");
+  }
+  return ZHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 zha_status zha_tree_build(zha_tree* t, void* k_cache, void* v_cache, int64_t n_tokens, const void* ref_queries,
                           hipStream_t stream) {
   if (!t) return fail(ZHA_E_INVALID, "tree is null");
@@ -280,58 +345,36 @@ zha_status zha_tree_build(zha_tree* t, void* k_cache, void* v_cache, int64_t n_t
   if (n_tokens < 1) return fail(ZHA_E_INVALID, "n_tokens %lld < 1", (long long)n_tokens);
   if (n_tokens > t->cfg.capacity)
     return fail(ZHA_E_CAPACITY, "n_tokens %lld > capacity %lld", (long long)n_tokens, (long long)t->cfg.capacity);
-  const zha_config& c = t->cfg;
-  BuildArgs a;
-  memset(&a, 0, sizeof a);
-  a.K = k_cache;
-  a.refs = ref_queries;
-  a.cap = c.capacity;
-  a.N = n_tokens;
-  a.b = c.block;
-  a.m = tile_levels(c);
-  a.sigma = 1.0f / sqrtf((float)c.head_dim);
-  a.dev = t->dev;
-  const int T = tile_tokens(c);
-  hipError_t e;
-  {
-    ProfScope ps(t, "build_tile", stream);
-    e = launch_build_tile(a, c.dtype == ZHA_BF16, c.head_dim, c.num_ref, ceil_div(n_tokens, T),
-                          c.num_kv_heads, T, stream);
-  }
-  if (e != hipSuccess) return hip_fail(e, "build tile launch");
-  for (int v = a.m + 1; v <= c.levels; ++v) {
-    ParentArgs p;
-    memset(&p, 0, sizeof p);
-    p.dev = t->dev;
-    p.level = v;
-    p.b = c.block;
-    p.nparent = nodes_at(c, v, n_tokens);
-    p.nchild = nodes_at(c, v - 1, n_tokens);
-    {
-      ProfScope ps(t, lvkey("build_parent", v), stream);
-      e = launch_build_parent(p, c.head_dim, c.num_ref, c.num_kv_heads, stream);
-    }
-    if (e != hipSuccess) return hip_fail(e, "build parent launch");
-  }
-  // FP4 router copies of every routed level, from the finished float32 planes
-  for (int v = 1; v <= c.levels; ++v) {
-    if (!t->dev.s4[v]) continue;
-    QuantArgs q;
-    memset(&q, 0, sizeof q);
-    q.dev = t->dev;
-    q.level = v;
-    q.nnode = nodes_at(c, v, n_tokens);
-    {
-      ProfScope ps(t, lvkey("build_quant", v), stream);
-      e = launch_quantise_fp4(q, c.head_dim, c.num_ref, c.num_kv_heads, stream);
-    }
-    if (e != hipSuccess) return hip_fail(e, "fp4 quantise launch");
-  }
+  zha_status zs = enqueue_build(t, k_cache, ref_queries, 0, n_tokens, stream);
+  if (zs != ZHA_OK) return zs;
   t->K = k_cache;
   t->V = v_cache;
   t->refs = ref_queries;
   t->N = n_tokens;
   t->built = true;
+  return ZHA_OK;
+}
+
+zha_status zha_tree_append_n(zha_tree* t, const void* k_new, const void* v_new, int64_t m, hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!t->built) return fail(ZHA_E_STATE, "append before build");
+  if (!k_new || !v_new) return fail(ZHA_E_INVALID, "null k_new or v_new");
+  if (m < 1) return fail(ZHA_E_INVALID, "m %lld < 1", (long long)m);
+  if (t->N + m > t->cfg.capacity)
+    return fail(ZHA_E_CAPACITY, "%lld + %lld tokens > capacity %lld", (long long)t->N, (long long)m,
+                (long long)t->cfg.capacity);
+  const zha_config& c = t->cfg;
+  const size_t es = c.dtype == ZHA_BF16 ? 2 : 4, row = (size_t)c.head_dim * es;
+  // rows N .. N+m-1 of every KV head's caches
+  hipError_t e = hipMemcpy2DAsync((char*)t->K + (size_t)t->N * row, (size_t)c.capacity * row, k_new, (size_t)m * row,
+                                  (size_t)m * row, c.num_kv_heads, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess)
+    e = hipMemcpy2DAsync((char*)t->V + (size_t)t->N * row, (size_t)c.capacity * row, v_new, (size_t)m * row,
+                         (size_t)m * row, c.num_kv_heads, hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "cache row copy");
+  zha_status zs = enqueue_build(t, t->K, t->refs, t->N, t->N + m, stream);
+  if (zs != ZHA_OK) return zs;
+  t->N += m;
   return ZHA_OK;
 }
 

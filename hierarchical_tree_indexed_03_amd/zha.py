@@ -47,6 +47,7 @@ def _load() -> ctypes.CDLL:
         "zha_create": (I32, [ctypes.POINTER(zha_config), P, SZ, ctypes.POINTER(P)]),
         "zha_tree_build": (I32, [P, P, P, I64, P, P]),
         "zha_tree_append": (I32, [P, P, P, P]),
+        "zha_tree_append_n": (I32, [P, P, P, I64, P]),
         "zha_decode": (I32, [P, P, P, P, P]),
         "zha_decode_dense": (I32, [P, P, P, P]),
         "zha_debug_level": (I32, [P, I32, P, P, P]),
@@ -68,7 +69,8 @@ def _load() -> ctypes.CDLL:
 
 
 _lib = _load()
-EXPORTED = ("zha_workspace_bytes", "zha_level1_key_form", "zha_create", "zha_tree_build", "zha_tree_append", "zha_decode",
+EXPORTED = ("zha_workspace_bytes", "zha_level1_key_form", "zha_create", "zha_tree_build", "zha_tree_append",
+            "zha_tree_append_n", "zha_decode",
             "zha_decode_dense", "zha_debug_level", "zha_debug_router_planes", "zha_debug_trace", "zha_debug_route_level",
             "zha_profile_start", "zha_profile_stop", "zha_set_top_p_levels", "zha_num_tokens", "zha_destroy", "zha_status_string",
             "zha_last_error")
@@ -129,6 +131,10 @@ def zha_tree_build(t, k_cache, v_cache, n_tokens: int, ref_queries, stream=None)
 
 def zha_tree_append(t, k_new, v_new, stream=None):
     _check(_lib.zha_tree_append(t, _p(k_new), _p(v_new), _s(stream)))
+
+
+def zha_tree_append_n(t, k_new, v_new, m: int, stream=None):
+    _check(_lib.zha_tree_append_n(t, _p(k_new), _p(v_new), int(m), _s(stream)))
 
 
 def zha_decode(t, q, out, stats=None, stream=None):
@@ -213,6 +219,10 @@ class Tree:
 
     def append(self, k_new, v_new, stream=None):
         zha_tree_append(self.handle, k_new, v_new, stream)
+
+    def append_n(self, k_new, v_new, stream=None):
+        """k_new, v_new: [Hkv, m, d] device tensors."""
+        zha_tree_append_n(self.handle, k_new, v_new, k_new.shape[1], stream)
 
     def set_top_p_levels(self, p_levels=None):
         if p_levels is not None and len(p_levels) != self.cfg.levels:

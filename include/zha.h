@@ -113,6 +113,17 @@ zha_status zha_create(const zha_config* cfg, void* workspace, size_t workspace_b
 zha_status zha_tree_build(zha_tree* t, void* k_cache, void* v_cache, int64_t n_tokens,
                           const void* ref_queries, hipStream_t stream);
 
+/* Appends m >= 1 tokens to every KV head at once (a prompt chunk, or tokens accepted
+ * together): copies k_new/v_new ((device) [Hkv][m][d] dtype) into rows N..N+m-1 of the
+ * caches, then rebuilds every node whose span holds one of them: the key tiles from the
+ * one holding row N, and at each level the nodes from the one holding row N (the same
+ * kernels as zha_tree_build, so the result equals a build over N+m tokens).  Cost grows
+ * with m plus one tile and one node per level.  ZHA_E_CAPACITY when N + m > capacity.
+ * The pages state the tree is built over the KV cache and grows with it (blog,
+ * "Building the tree"); bulk growth is the build restricted to the new tail. */
+zha_status zha_tree_append_n(zha_tree* t, const void* k_new, const void* v_new, int64_t m,
+                             hipStream_t stream);
+
 /* Appends one token to every KV head: writes k_new/v_new ((device) [Hkv][d] dtype) into
  * row N of the caches, then refreshes the one node per level whose span holds the new
  * token.  ZHA_E_CAPACITY when N == capacity.  Equivalent to a rebuild over N+1 tokens. */
