@@ -50,6 +50,8 @@ def parse():
                          "for p^(1/L) at every level (the product over the levels is p)")
     ap.add_argument("--no-quant-planes", "--no-bf16-planes", dest="no_quant_planes", action="store_true",
                     help="skip the secondary measurements with quantised (bf16, FP4) router planes")
+    ap.add_argument("--append-chunk", type=int, default=4096,
+                    help="also time zha_tree_append_n of this many tokens onto a tree of N-m (0: skip)")
     ap.add_argument("--build-reps", type=int, default=3)
     ap.add_argument("--dense-reps", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -524,6 +526,32 @@ def main():
         tree2.close()
         del tree2
 
+    # ---- multi-token append: a tree over N0 - m tokens grows by m rows at once (the rows
+    # already hold their values, so the copy rewrites them unchanged)
+    append_n = None
+    m_app = args.append_chunk
+    if m_app > 0 and n0 > m_app:
+        tree3 = zha.Tree(cfg)
+        Kc, Vc = Kd[:, n0 - m_app:n0].contiguous(), Vd[:, n0 - m_app:n0].contiguous()
+        an_ms = []
+        for _ in range(3):
+            tree3.build(Kd, Vd, n0 - m_app, Rd)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            tree3.append_n(Kc, Vc)
+            e1.record()
+            torch.cuda.synchronize()
+            an_ms.append(e0.elapsed_time(e1))
+        am = float(np.median(an_ms))
+        append_n = {"tokens": m_app, "onto_tokens": n0 - m_app, "ms": round(am, 4),
+                    "tokens_per_s": round(m_app / (am * 1e-3)),
+                    "single_append_ms": round(probe_ms.get("append", float("nan")), 4)}
+        log(f"[bench] append_n of {m_app} tokens onto {n0 - m_app}: {am:.3f} ms "
+            f"({m_app / (am * 1e-3) / 1e6:.1f} M tok/s; one-token append {probe_ms.get('append', float('nan')):.4f} ms)")
+        tree3.close()
+        del tree3, Kc, Vc
+
     # stream-read probe: practical HBM read bandwidth of a plain streaming kernel (2 GiB)
     import ctypes
     plib = ctypes.CDLL(os.path.join(ROOT, "hierarchical_tree_indexed_03_amd", "libzha_probe.so"))
@@ -593,6 +621,7 @@ def main():
                   "zha_speedup": round(dense_ms / ms_per_step, 3)},
         "bf16_router_planes": quant.get("bf16"),
         "fp4_router_planes": quant.get("fp4"),
+        "append_n": append_n,
         "hbm_read_probe_GBps": round(read_gbs, 1),
         "kernel_ms": {k: round(v, 4) for k, v in sorted(probe_ms.items(), key=lambda x: -x[1])},
         "src_sha": src_sha(),
