@@ -549,8 +549,24 @@ def main():
                     "single_append_ms": round(probe_ms.get("append", float("nan")), 4)}
         log(f"[bench] append_n of {m_app} tokens onto {n0 - m_app}: {am:.3f} ms "
             f"({m_app / (am * 1e-3) / 1e6:.1f} M tok/s; one-token append {probe_ms.get('append', float('nan')):.4f} ms)")
+        # causal multi-query prefill of 64 tokens (append + routed decode per token)
+        mp = min(64, total)
+        tree3.build(Kd, Vd, n0 - mp, Rd)
+        pout = torch.empty(mp, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+        tree3.prefill(Kd[:, n0 - mp:n0].contiguous(), Vd[:, n0 - mp:n0].contiguous(), Qd[:mp].contiguous(), pout)
+        tree3.build(Kd, Vd, n0 - mp, Rd)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tree3.prefill(Kd[:, n0 - mp:n0].contiguous(), Vd[:, n0 - mp:n0].contiguous(), Qd[:mp].contiguous(), pout)
+        e1.record()
+        torch.cuda.synchronize()
+        pm = e0.elapsed_time(e1)
+        append_n["prefill"] = {"tokens": mp, "ms": round(pm, 4), "ms_per_token": round(pm / mp, 4),
+                               "tokens_per_s": round(mp / (pm * 1e-3), 1)}
+        log(f"[bench] prefill of {mp} tokens (append + decode each): {pm:.3f} ms, {pm / mp:.4f} ms/token")
         tree3.close()
-        del tree3, Kc, Vc
+        del tree3, Kc, Vc, pout
 
     # stream-read probe: practical HBM read bandwidth of a plain streaming kernel (2 GiB)
     import ctypes

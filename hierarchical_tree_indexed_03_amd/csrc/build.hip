@@ -410,8 +410,8 @@ __global__ __launch_bounds__(1024) void append_kernel(AppendArgs a) {
   const int b = a.b, L = a.levels;
   TIn* Kc = (TIn*)a.K + (int64_t)kv * a.cap * D;
   TIn* Vc = (TIn*)a.V + (int64_t)kv * a.cap * D;
-  const TIn* kn = (const TIn*)a.k_new + (int64_t)kv * D;
-  const TIn* vn = (const TIn*)a.v_new + (int64_t)kv * D;
+  const TIn* kn = (const TIn*)a.k_new + (int64_t)kv * a.new_stride;
+  const TIn* vn = (const TIn*)a.v_new + (int64_t)kv * a.new_stride;
   for (int i = tid; i < D; i += NT) {
     Kc[n * D + i] = kn[i];
     Vc[n * D + i] = vn[i];

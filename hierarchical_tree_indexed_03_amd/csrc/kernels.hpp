@@ -35,8 +35,9 @@ struct QuantArgs {
 struct AppendArgs {
   void* K;
   void* V;
-  const void* k_new;  // [Hkv][D]
+  const void* k_new;  // row of KV head kv at k_new + kv * new_stride elements
   const void* v_new;
+  int64_t new_stride; // elements between the KV heads' rows (D for a [Hkv][D] token)
   const void* refs;
   int64_t cap;
   int64_t N;          // index of the new token (tokens before the append)

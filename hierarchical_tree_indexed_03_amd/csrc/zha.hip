@@ -378,11 +378,13 @@ zha_status zha_tree_append_n(zha_tree* t, const void* k_new, const void* v_new, 
   return ZHA_OK;
 }
 
-zha_status zha_tree_append(zha_tree* t, const void* k_new, const void* v_new, hipStream_t stream) {
-  if (!t) return fail(ZHA_E_INVALID, "tree is null");
-  if (!t->built) return fail(ZHA_E_STATE, "append before build");
-  if (!k_new || !v_new) return fail(ZHA_E_INVALID, "null k_new or v_new");
-  if (t->N >= t->cfg.capacity) return fail(ZHA_E_CAPACITY, "cache full (%lld tokens)", (long long)t->N);
+}  // extern "C"
+
+namespace {
+
+// One-token append (validated by the caller); the new row of KV head kv is at
+// k_new + kv * stride elements.
+zha_status enqueue_append(zha_tree* t, const void* k_new, const void* v_new, int64_t stride, hipStream_t stream) {
   const zha_config& c = t->cfg;
   AppendArgs a;
   memset(&a, 0, sizeof a);
@@ -390,6 +392,7 @@ zha_status zha_tree_append(zha_tree* t, const void* k_new, const void* v_new, hi
   a.V = t->V;
   a.k_new = k_new;
   a.v_new = v_new;
+  a.new_stride = stride;
   a.refs = t->refs;
   a.cap = c.capacity;
   a.N = t->N;
@@ -405,6 +408,18 @@ zha_status zha_tree_append(zha_tree* t, const void* k_new, const void* v_new, hi
   if (e != hipSuccess) return hip_fail(e, "append launch");
   t->N += 1;
   return ZHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+zha_status zha_tree_append(zha_tree* t, const void* k_new, const void* v_new, hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!t->built) return fail(ZHA_E_STATE, "append before build");
+  if (!k_new || !v_new) return fail(ZHA_E_INVALID, "null k_new or v_new");
+  if (t->N >= t->cfg.capacity) return fail(ZHA_E_CAPACITY, "cache full (%lld tokens)", (long long)t->N);
+  return enqueue_append(t, k_new, v_new, t->cfg.head_dim, stream);
 }
 
 zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hipStream_t stream) {
@@ -475,6 +490,30 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
     e = launch_attend_full(a, c.dtype == ZHA_BF16, c.head_dim, false, stats, c.levels, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ZHA_OK;
+}
+
+zha_status zha_prefill(zha_tree* t, const void* k_new, const void* v_new, const void* q, float* out, int64_t m,
+                       int32_t* stats, hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!t->built) return fail(ZHA_E_STATE, "prefill before build");
+  if (!k_new || !v_new || !q || !out) return fail(ZHA_E_INVALID, "null k_new, v_new, q or out");
+  if ((uintptr_t)q % 16) return fail(ZHA_E_INVALID, "q must be 16-byte aligned");
+  if (m < 1) return fail(ZHA_E_INVALID, "m %lld < 1", (long long)m);
+  if (t->N + m > t->cfg.capacity)
+    return fail(ZHA_E_CAPACITY, "%lld + %lld tokens > capacity %lld", (long long)t->N, (long long)m,
+                (long long)t->cfg.capacity);
+  const zha_config& c = t->cfg;
+  const size_t es = c.dtype == ZHA_BF16 ? 2 : 4, d = (size_t)c.head_dim;
+  for (int64_t i = 0; i < m; ++i) {
+    // token i: row i of each KV head's [m][d] chunk
+    zha_status zs = enqueue_append(t, (const char*)k_new + (size_t)i * d * es, (const char*)v_new + (size_t)i * d * es,
+                                   m * (int64_t)d, stream);
+    if (zs != ZHA_OK) return zs;
+    zs = zha_decode(t, (const char*)q + (size_t)i * c.num_q_heads * d * es, out + (size_t)i * c.num_q_heads * d,
+                    stats ? stats + (size_t)i * (c.levels + 1) * c.num_kv_heads : nullptr, stream);
+    if (zs != ZHA_OK) return zs;
+  }
   return ZHA_OK;
 }
 

@@ -50,6 +50,7 @@ def _load() -> ctypes.CDLL:
         "zha_tree_append_n": (I32, [P, P, P, I64, P]),
         "zha_decode": (I32, [P, P, P, P, P]),
         "zha_decode_dense": (I32, [P, P, P, P]),
+        "zha_prefill": (I32, [P, P, P, P, P, I64, P, P]),
         "zha_debug_level": (I32, [P, I32, P, P, P]),
         "zha_debug_router_planes": (I32, [P, I32, P, P, P]),
         "zha_debug_trace": (I32, [P, I32, I64, P, P, P, P, P, P]),
@@ -70,7 +71,7 @@ def _load() -> ctypes.CDLL:
 
 _lib = _load()
 EXPORTED = ("zha_workspace_bytes", "zha_level1_key_form", "zha_create", "zha_tree_build", "zha_tree_append",
-            "zha_tree_append_n", "zha_decode",
+            "zha_tree_append_n", "zha_decode", "zha_prefill",
             "zha_decode_dense", "zha_debug_level", "zha_debug_router_planes", "zha_debug_trace", "zha_debug_route_level",
             "zha_profile_start", "zha_profile_stop", "zha_set_top_p_levels", "zha_num_tokens", "zha_destroy", "zha_status_string",
             "zha_last_error")
@@ -139,6 +140,10 @@ def zha_tree_append_n(t, k_new, v_new, m: int, stream=None):
 
 def zha_decode(t, q, out, stats=None, stream=None):
     _check(_lib.zha_decode(t, _p(q), _p(out), _p(stats), _s(stream)))
+
+
+def zha_prefill(t, k_new, v_new, q, out, m: int, stats=None, stream=None):
+    _check(_lib.zha_prefill(t, _p(k_new), _p(v_new), _p(q), _p(out), int(m), _p(stats), _s(stream)))
 
 
 def zha_decode_dense(t, q, out, stream=None):
@@ -233,6 +238,14 @@ class Tree:
         if out is None:
             out = torch.empty(self.cfg.num_q_heads, self.cfg.head_dim, dtype=torch.float32, device=q.device)
         zha_decode(self.handle, q, out, stats, stream)
+        return out
+
+    def prefill(self, k_new, v_new, q, out=None, stats=None, stream=None):
+        """k_new, v_new: [Hkv, m, d]; q: [m, Hq, d]; returns out [m, Hq, d] float32."""
+        m = k_new.shape[1]
+        if out is None:
+            out = torch.empty(m, self.cfg.num_q_heads, self.cfg.head_dim, dtype=torch.float32, device=q.device)
+        zha_prefill(self.handle, k_new, v_new, q, out, m, stats, stream)
         return out
 
     def decode_dense(self, q, out=None, stream=None):

@@ -140,6 +140,19 @@ zha_status zha_tree_append(zha_tree* t, const void* k_new, const void* v_new,
 zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats,
                       hipStream_t stream);
 
+/* Causal multi-query decode over a chunk of m new tokens (prefill with ZHA routing: the
+ * method's attention cost is subquadratic in the context as a whole, blog, "How is this
+ * subquadratic", and the paper's abstract).  For i = 0..m-1: appends token i
+ * (k_new/v_new (device) [Hkv][m][d]
+ * dtype, row i of each head) and decodes query row i (q (device) [m][Hq][d] dtype) into
+ * out (device) [m][Hq][d] float32, so query i routes over the tree of the tokens up to
+ * and including its own, exactly as m calls of zha_tree_append + zha_decode.
+ * stats (nullable) [m][levels + 1][Hkv] as in zha_decode.  ZHA_E_CAPACITY when
+ * N + m > capacity (nothing is enqueued).  All work is enqueued on `stream`; a HIP error
+ * part-way leaves the tokens appended before it in the tree. */
+zha_status zha_prefill(zha_tree* t, const void* k_new, const void* v_new, const void* q, float* out,
+                       int64_t m, int32_t* stats, hipStream_t stream);
+
 /* Dense decode over all N tokens (the baseline attention the method is compared with):
  * out[h] = softmax(q_h.K^T/sqrt(d)) V for every query head. */
 zha_status zha_decode_dense(zha_tree* t, const void* q, float* out, hipStream_t stream);

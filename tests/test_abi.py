@@ -140,6 +140,7 @@ def test_call_order_and_arguments(zha):
             (lambda: zha.zha_debug_level(t, 1, fake, fake), 5),
             (lambda: zha.zha_debug_router_planes(t, 2, fake), 5),
             (lambda: zha.zha_tree_append_n(t, fake, fake, 4), 5),
+            (lambda: zha.zha_prefill(t, fake, fake, fake, fake, 4), 5),
             (lambda: zha.zha_tree_build(t, fake, fake, 1001, fake), 3),
             (lambda: zha.zha_tree_build(t, fake, fake, 0, fake), 1),
             (lambda: zha.zha_tree_build(t, None, fake, 10, fake), 1),

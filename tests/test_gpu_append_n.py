@@ -114,3 +114,53 @@ def test_append_n_capacity():
     torch.cuda.synchronize()
     check_planes(w, t, [zo.build_tree(K[0], refs[0], w.block, w.levels, 110)])
     t.close()
+
+
+@pytest.mark.parametrize("name", ["deep_small", "tiny", "ultra_small"])
+def test_prefill_equals_append_then_decode(name):
+    """zha_prefill over a chunk = one zha_tree_append + zha_decode per token (bitwise: the
+    same kernels in the same order), and the last query matches the oracle end to end."""
+    base, n0, _ = CASES[name]
+    m = 24
+    w = base.with_(n_tokens=n0, steps=m, appends=True)
+    K, V, refs = P.host_inputs(w)
+    Kd, Vd = P.upload(K, w), P.upload(V, w)
+    Rd = P.upload(refs, w)
+    qs = np.stack([gen.step_queries(w, i, n0 + i + 1, gen.host_fetch(K)) for i in range(m)])
+    Qd = P.upload(qs, w)
+    kc, vc = Kd[:, n0:n0 + m].contiguous(), Vd[:, n0:n0 + m].contiguous()
+    # chunked prefill on one tree ...
+    t1 = P.make_tree(w, capacity=n0 + m)
+    t1.build(Kd, Vd, n0, Rd)
+    out1 = t1.prefill(kc, vc, Qd).cpu().numpy()
+    assert t1.n_tokens == n0 + m
+    traces = {lv: t1.trace(lv) for lv in range(0, w.levels + 1)}
+    # ... and token by token on another
+    t2 = P.make_tree(w, capacity=n0 + m)
+    t2.build(Kd, Vd, n0, Rd)
+    out2 = np.empty_like(out1)
+    for i in range(m):
+        t2.append(kc[:, i].contiguous(), vc[:, i].contiguous())
+        out2[i] = t2.decode(Qd[i].contiguous()).cpu().numpy()
+    assert np.array_equal(out1, out2), "prefill differs from append + decode"
+    # the last query against the oracle, with its routing trace
+    n = n0 + m
+    trees = [zo.build_tree(K[h], refs[h], w.block, w.levels, n) for h in range(w.num_kv_heads)]
+    o_ref, routes = zo.decode(trees, V, qs[-1], w.top_p, w.keep_sink, return_routes=True)
+    g = w.group
+    for h in range(w.num_q_heads):
+        kv, gi = divmod(h, g)
+        tr = {lv: traces[lv][kv] for lv in traces}
+        rep = P.compare_route(routes[h], tr, gi, w.block, w.top_p)
+        assert not rep["bad"], f"head {h}: {rep['bad'][:5]}"
+        toks = P.gpu_tokens(tr[0], gi, w.block, n, w.keep_sink)
+        assert P.out_err(out1[-1, h], zo.attend(K[kv][:n], V[kv][:n], qs[-1][h], toks)) <= P.OUT_RTOL
+        if not rep["exempt"]:
+            assert P.out_err(out1[-1, h], o_ref[h]) <= P.OUT_RTOL
+    # a chunk past the capacity is refused before anything is enqueued
+    from hierarchical_tree_indexed_03_amd import zha
+    with pytest.raises(zha.ZhaError) as e:
+        t1.prefill(kc[:, :1].contiguous(), vc[:, :1].contiguous(), Qd[:1].contiguous())
+    assert e.value.status == 3 and t1.n_tokens == n
+    t1.close()
+    t2.close()
