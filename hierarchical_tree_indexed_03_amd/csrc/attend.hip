@@ -543,14 +543,11 @@ __global__ __launch_bounds__(512) void combine_kernel(AttnArgs a, int32_t* stats
   }
 }
 
-// Routed attention on the MFMA P.V kernel too (bf16); off: the VALU P.V kernel.
-#ifndef ZHA_ROUTED_MFMA
-#define ZHA_ROUTED_MFMA 0
-#endif
-
+// Dense bf16 attention runs P.V on MFMA; routed attention keeps P.V on the VALU (its MFMA
+// variant measured slower on every routed workload: lower occupancy, short gathers).
 template <typename TIn, int D, bool DENSE>
 static hipError_t launch_attend_t(const AttnArgs& a, int32_t* stats, int levels, hipStream_t st) {
-  if constexpr (sizeof(TIn) == 2 && (DENSE || ZHA_ROUTED_MFMA))
+  if constexpr (sizeof(TIn) == 2 && DENSE)
     hipLaunchKernelGGL((attend_mfma_kernel<D, DENSE>), dim3((unsigned)a.splits, (unsigned)a.hkv), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((attend_kernel<TIn, D, DENSE>), dim3((unsigned)a.splits, (unsigned)a.hkv), dim3(256), 0, st, a);
@@ -574,7 +571,7 @@ hipError_t launch_attend_full(const AttnArgs& a, bool bf16, int D, bool dense, i
 template <typename TIn, int D, bool DENSE>
 static int resident_splits_t(int hkv) {
   static const int per_cu = [] {
-    if constexpr (sizeof(TIn) == 2 && (DENSE || ZHA_ROUTED_MFMA)) return resident_per_cu(attend_mfma_kernel<D, DENSE>, 256);
+    if constexpr (sizeof(TIn) == 2 && DENSE) return resident_per_cu(attend_mfma_kernel<D, DENSE>, 256);
     else return resident_per_cu(attend_kernel<TIn, D, DENSE>, 256);
   }();
   const int s = per_cu * device_cus() / hkv;
