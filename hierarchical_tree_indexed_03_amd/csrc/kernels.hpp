@@ -85,6 +85,11 @@ struct AttnArgs {
 hipError_t launch_build_tile(const BuildArgs& a, bool bf16, int D, int R, int64_t ntiles, int hkv, int T,
                              hipStream_t st);
 hipError_t launch_build_parent(const ParentArgs& a, int D, int R, int hkv, hipStream_t st);
+// Levels 1 and 2 (a.m = 1 or 2) for R <= 4 and b in {2, 4, 8}, keys held in registers;
+// tiles of narrow_tile_tokens(D, b) tokens.
+bool narrow_build(int R, int b);
+int narrow_tile_tokens(int D, int b);
+hipError_t launch_build_narrow(const BuildArgs& a, bool bf16, int D, int R, int hkv, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, bool bf16, int D, int R, int hkv, hipStream_t st);
 // MX FP4 router copies (dev.s4, dev.s4x) of one level's float32 s.
 hipError_t launch_quantise_fp4(const QuantArgs& a, int D, int R, int hkv, hipStream_t st);

@@ -288,15 +288,18 @@ zha_status enqueue_build(zha_tree* t, const void* k_cache, const void* refs, int
   a.cap = c.capacity;
   a.N = to;
   a.b = c.block;
-  a.m = tile_levels(c);
   a.sigma = 1.0f / sqrtf((float)c.head_dim);
   a.dev = t->dev;
-  const int T = tile_tokens(c);
+  const bool narrow = narrow_build(c.num_ref, c.block);
+  a.m = narrow ? (c.levels < 2 ? c.levels : 2) : tile_levels(c);
+  const int T = narrow ? narrow_tile_tokens(c.head_dim, c.block) : tile_tokens(c);
   a.tile0 = from / T;
   hipError_t e;
   {
     ProfScope ps(t, "build_tile", stream);
-    e = launch_build_tile(a, c.dtype == ZHA_BF16, c.head_dim, c.num_ref, ceil_div(to, T), c.num_kv_heads, T, stream);
+    e = narrow ? launch_build_narrow(a, c.dtype == ZHA_BF16, c.head_dim, c.num_ref, c.num_kv_heads, stream)
+               : launch_build_tile(a, c.dtype == ZHA_BF16, c.head_dim, c.num_ref, ceil_div(to, T), c.num_kv_heads, T,
+                                   stream);
   }
   if (e != hipSuccess) return hip_fail(e, "build tile launch");
   for (int v = a.m + 1; v <= c.levels; ++v) {
