@@ -318,7 +318,8 @@ zha_status enqueue_build(zha_tree* t, const void* k_cache, const void* refs, int
     if (e != hipSuccess) return hip_fail(e, "build parent launch");
   }
   // FP4 router copies of the rebuilt nodes of every routed level, from the finished planes
-  for (int v = 1; v <= c.levels; ++v) {
+  // (the narrow leaf kernel writes those of its own levels itself)
+  for (int v = narrow ? a.m + 1 : 1; v <= c.levels; ++v) {
     if (!t->dev.s4[v]) continue;
     QuantArgs q;
     memset(&q, 0, sizeof q);
