@@ -196,35 +196,46 @@ def crossover(args):
         Qd = torch.from_numpy(np.stack([gen.step_queries(w, s_, n0 + s_ + 1, fetch) for s_ in range(total)])).to(torch.bfloat16).to(dev)
         Kn = Kd[:, n0:n0 + total].transpose(0, 1).contiguous()
         Vn = Vd[:, n0:n0 + total].transpose(0, 1).contiguous()
-        cfg = zha.make_config(w.head_dim, w.num_kv_heads, w.num_q_heads, w.block, w.levels, w.num_ref,
-                              w.capacity, w.dtype, w.top_p, w.keep_sink)
-        tree = zha.Tree(cfg)
-        tree.build(Kd, Vd, n0, torch.from_numpy(gen.ref_queries(w)).to(torch.bfloat16).to(dev))
+        Rd = torch.from_numpy(gen.ref_queries(w)).to(torch.bfloat16).to(dev)
         out = torch.empty(w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+        zres = {}
+        # the ZHA step with fp32 router planes, then with bf16 and FP4 copies (a tree each over
+        # the same caches; their appends rewrite rows n0.. with the values they hold)
+        for fmt in ("f32", "bf16", "fp4"):
+            cfg = zha.make_config(w.head_dim, w.num_kv_heads, w.num_q_heads, w.block, w.levels, w.num_ref,
+                                  w.capacity, w.dtype, w.top_p, w.keep_sink, fmt)
+            tz = zha.Tree(cfg)
+            tz.build(Kd, Vd, n0, Rd)
 
-        def step(s_):
-            tree.append(Kn[s_], Vn[s_])
-            tree.decode(Qd[s_], out)
+            def step(s_):
+                tz.append(Kn[s_], Vn[s_])
+                tz.decode(Qd[s_], out)
 
-        for s_ in range(args.warmup):
-            step(s_)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for s_ in range(args.warmup, args.warmup + steps):
-            step(s_)
-        e1.record()
-        torch.cuda.synchronize()
-        zha_warm = e0.elapsed_time(e1) / steps
-        zc = []
-        for s_ in range(args.warmup + steps, total):
-            scratch.fill_(float(s_))
-            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            c0.record()
-            step(s_)
-            c1.record()
+            for s_ in range(args.warmup):
+                step(s_)
             torch.cuda.synchronize()
-            zc.append(c0.elapsed_time(c1))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for s_ in range(args.warmup, args.warmup + steps):
+                step(s_)
+            e1.record()
+            torch.cuda.synchronize()
+            zw = e0.elapsed_time(e1) / steps
+            zc = []
+            for s_ in range(args.warmup + steps, total):
+                scratch.fill_(float(s_))
+                c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                c0.record()
+                step(s_)
+                c1.record()
+                torch.cuda.synchronize()
+                zc.append(c0.elapsed_time(c1))
+            zres[fmt] = (zw, float(np.median(zc)) if zc else None)
+            if fmt == "f32":
+                tree = tz
+            else:
+                tz.close()
+        zha_warm, zha_cold = zres["f32"]
         q_last = Qd[total - 1]
         for _ in range(3):
             tree.decode_dense(q_last, out)
@@ -246,10 +257,14 @@ def crossover(args):
             dc.append(c0.elapsed_time(c1))
         row = {"n_tokens": n0, "levels": w.levels, "zha_ms_warm": round(zha_warm, 4),
                "dense_ms_warm": round(dense_warm, 4),
-               "zha_ms_cold_median": round(float(np.median(zc)), 4) if zc else None,
+               "zha_ms_cold_median": round(zha_cold, 4) if zha_cold else None,
                "dense_ms_cold_median": round(float(np.median(dc)), 4) if dc else None}
+        for fmt in ("bf16", "fp4"):
+            row[f"zha_ms_warm_{fmt}"] = round(zres[fmt][0], 4)
+            row[f"zha_ms_cold_median_{fmt}"] = round(zres[fmt][1], 4) if zres[fmt][1] else None
         rows.append(row)
-        log(f"[crossover] N={n0}: ZHA {row['zha_ms_warm']:.3f} ms warm / {row['zha_ms_cold_median']} cold, "
+        log(f"[crossover] N={n0}: ZHA {row['zha_ms_warm']:.3f} ms warm / {row['zha_ms_cold_median']} cold "
+            f"(bf16 planes {row['zha_ms_warm_bf16']:.3f}, FP4 {row['zha_ms_warm_fp4']:.3f} warm), "
             f"dense {row['dense_ms_warm']:.3f} ms warm / {row['dense_ms_cold_median']} cold")
         tree.close()
         del Kd, Vd, Kn, Vn, Qd
@@ -270,12 +285,14 @@ def crossover(args):
 
     warm = cross("zha_ms_warm", "dense_ms_warm")
     cold = cross("zha_ms_cold_median", "dense_ms_cold_median")
+    quant = {fmt: {"warm": cross(f"zha_ms_warm_{fmt}", "dense_ms_warm"),
+                   "cold": cross(f"zha_ms_cold_median_{fmt}", "dense_ms_cold_median")} for fmt in ("bf16", "fp4")}
     rec = {"metric": "crossover context, ZHA decode step vs dense flash-decode (light router: R=1, b=8, p=0.75)",
            "value": warm.get("tokens"), "unit": "tokens", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
            "higher_is_better": False, "data": "synthetic", "dtype": "bf16+f32",
            "config": {"workload": "light_sweep", "sizes": list(wc.LIGHT_SIZES), "kv_heads": 4, "q_heads": 32,
                       "head_dim": 128, "step": "append + decode"},
-           "crossover_warm": warm, "crossover_cold": cold, "per_n": rows,
+           "crossover_warm": warm, "crossover_cold": cold, "crossover_quantised_planes": quant, "per_n": rows,
            "modeled_reference": {"source": "the pages' H100 BF16 roofline model (modeled, not measured)",
                                  "crossover_tokens": 48000}}
     print(json.dumps(rec), flush=True)
