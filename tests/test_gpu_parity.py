@@ -22,6 +22,8 @@ SMALL = {
     "wide_small": wc.WIDE.with_(n_tokens=8_192 + 100, steps=3),
     "light_small": wc.light(32_768, steps=3).with_(n_tokens=32_768 - 5),
     "ultra_small": wc.ULTRA.with_(n_tokens=70_001, steps=2),
+    "light_d64": wc.light(32_768, steps=2).with_(n_tokens=20_000 + 3, head_dim=64),
+    "deep_d64_r4": wc.DEEP.with_(n_tokens=10_000 + 3, head_dim=64, num_ref=4, levels=4, steps=2),
 }
 
 

@@ -37,6 +37,10 @@ GEOMS = {
     # level 1 holds 36,001 nodes: scored from the union list, selected by the large-level path
     "light_general": wc.light(288_003, steps=1).with_(num_kv_heads=1, num_q_heads=8),
     "ultra_small": wc.ULTRA.with_(n_tokens=70_001, steps=2),
+    # head_dim 64 with bf16 keys: the narrow build and the scorers at d = 64
+    "light_d64": wc.light(32_768, steps=2).with_(n_tokens=20_000 + 3, head_dim=64),
+    # R 4, b 4 at d = 64: narrow build with key-form token weights, key-form level 1
+    "deep_d64_r4": wc.DEEP.with_(n_tokens=10_000 + 3, head_dim=64, num_ref=4, levels=4, steps=2),
 }
 SMALL = {f"{fmt}-{name}": w.with_(planes=fmt) for fmt in ("bf16", "fp4") for name, w in GEOMS.items()}
 
