@@ -31,6 +31,16 @@
 
 namespace zha {
 
+// Dense scoring of the top levels: the level of this workgroup (grid z).  The largest level
+// (the lowest) comes first, so its long-running workgroups are dispatched before the small
+// levels' ones, which then fill the tail.
+#ifndef ZHA_DENSE_LOW_FIRST
+#define ZHA_DENSE_LOW_FIRST 1
+#endif
+__device__ __forceinline__ int dense_level(const RouteArgs& a) {
+  return ZHA_DENSE_LOW_FIRST ? a.dense_lo + (int)blockIdx.z : a.level - (int)blockIdx.z;
+}
+
 template <typename TIn, int D>
 __global__ __launch_bounds__(256) void route_prep_kernel(RouteArgs a) {
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -70,7 +80,7 @@ __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
   const int col = lane & 15, kg = lane >> 4;
   const int slot = col / R, plane = col % R;
   const bool dense = a.dense != 0;            // every node of the level, no list
-  const int lv = dense ? a.level - (int)blockIdx.z : a.level;
+  const int lv = dense ? dense_level(a) : a.level;
   const int64_t cnt = dense ? a.nl[lv] : a.dev.cnt[lv * a.hkv + kv];
   const int64_t cap = a.dev.ncap[lv];
   const int32_t* nodes = a.dev.node[lv] + kv * cap;
@@ -238,7 +248,7 @@ __global__ __launch_bounds__(256) void route_score_bf16_kernel(RouteArgs a) {
   const int col = lane & 15, kg = lane >> 4;
   const int slot = col / R, plane = col % R;
   const bool dense = a.dense != 0;            // every node of the level, no list
-  const int lv = dense ? a.level - (int)blockIdx.z : a.level;
+  const int lv = dense ? dense_level(a) : a.level;
   const int64_t cnt = dense ? a.nl[lv] : a.dev.cnt[lv * a.hkv + kv];
   const int64_t cap = a.dev.ncap[lv];
   const int32_t* nodes = a.dev.node[lv] + kv * cap;
@@ -352,7 +362,7 @@ __global__ __launch_bounds__(256) void route_score_bf16_rows_kernel(RouteArgs a)
   const int kv = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const bool dense = a.dense != 0;            // every node of the level, no list
-  const int lv = dense ? a.level - (int)blockIdx.z : a.level;
+  const int lv = dense ? dense_level(a) : a.level;
   const int64_t cnt = dense ? a.nl[lv] : a.dev.cnt[lv * a.hkv + kv];
   const int64_t cap = a.dev.ncap[lv];
   const int32_t* nodes = a.dev.node[lv] + kv * cap;
