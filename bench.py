@@ -172,7 +172,18 @@ def cpu_baseline(w, K, V, refs, queries, n0, budget):
                 sample=(f"KV head 0 of {w.num_kv_heads} (its {w.group} query heads), {steps} decode steps "
                         f"(append+route+attend) in {el:.1f}s on 1 thread, scaled x{w.num_kv_heads} to all "
                         f"heads; tree over {n0} tokens built first (untimed, {tb:.1f}s, all threads)"),
-                host_cpus=os.cpu_count())
+                host_cpus=os.cpu_count(), cpu_model=_cpu_model())
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def crossover(args):
