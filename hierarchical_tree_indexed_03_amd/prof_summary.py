@@ -2,6 +2,7 @@
 
     python -m hierarchical_tree_indexed_03_amd.prof_summary trace DIR WORKLOAD --cmd "..." [--out FILE]
     python -m hierarchical_tree_indexed_03_amd.prof_summary pmc FETCH_DIR WRITE_DIR WORKLOAD --cmd "..." [--out FILE]
+    python -m hierarchical_tree_indexed_03_amd.prof_summary mfma DIR WORKLOAD --trace TRACE_DIR --cmd "..." [--out FILE]
 
 ``trace`` reads ``*_kernel_trace.csv`` (``rocprofv3 --kernel-trace --stats --output-format csv``)
 and attributes every dispatch of a decode (route_prep ... combine) to its router level: the
@@ -222,6 +223,69 @@ def cmd_pmc(a):
     print(json.dumps(out, indent=1))
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_BUSY_CU_CYCLES")
+SIMD_NUM = 256 * 4           # MI355X: 256 compute units x 4 SIMDs
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+
+
+def cmd_mfma(a):
+    """MFMA use of the build kernels from one counter run (MFMA_COUNTERS), with the kernel
+    durations of a kernel trace of the same workload (the counter run's own timestamps include
+    the collection).  Dispatches of one kernel are averaged."""
+    files = glob.glob(os.path.join(a.dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no counter_collection.csv under {a.dir}")
+    disp = defaultdict(lambda: defaultdict(list))
+    names = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            k = int(r["Dispatch_Id"])
+            disp[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            names[k] = short(r["Kernel_Name"])
+    dur = defaultdict(list)
+    if a.trace:
+        rows, _ = read_trace(a.trace)
+        for r in rows:
+            dur[short(r["name"])].append((r["t1"] - r["t0"]) / 1e3)
+    per = defaultdict(list)       # kernel -> [(util %, bf16 GFLOP, f32 GFLOP)] per dispatch
+    for k in sorted(disp):
+        n = names[k]
+        if not (n.startswith("build_") or n.startswith("quantise_")):
+            continue
+        v = disp[k]
+        busy = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"])
+        grbm = max(v["GRBM_GUI_ACTIVE"]) if v["GRBM_GUI_ACTIVE"] else 0.0
+        per[n].append((100.0 * busy / (grbm * SIMD_NUM) if grbm else 0.0,
+                       sum(v["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) * 512 / 1e9,
+                       sum(v["SQ_INSTS_VALU_MFMA_MOPS_F32"]) * 512 / 1e9))
+    lines = [f"# MFMA use of the tree build, workload `{a.workload}`", "",
+             "Counter run (from the repository root on the GPU host):", "", "```", a.cmd, "```", "",
+             "Durations come from the kernel trace of the same workload"
+             + (f" (`{a.trace_cmd}`)" if a.trace_cmd else "") + ".", "",
+             "Summarised with:", "", "```",
+             f"python -m hierarchical_tree_indexed_03_amd.prof_summary mfma gpurun_out/mfma_{a.workload} "
+             f"{a.workload} --trace gpurun_out/prof_{a.workload} --cmd '...' --trace-cmd '...'",
+             "```", "",
+             "MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES summed over the chip / (GRBM_GUI_ACTIVE x "
+             "1,024 SIMDs), the MfmaUtil expression of rocprofv3; MFMA flops = MOPS x 512.", "",
+             "| kernel | dispatches | MFMA util | bf16 MFMA GFLOP | f32 MFMA GFLOP | avg duration us "
+             "| bf16 TFLOP/s (of 2,500) | f32 TFLOP/s (of 157.3) |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for n, xs in per.items():
+        m = len(xs)
+        util, fb, ff = (sum(x[i] for x in xs) / m for i in range(3))
+        ds = dur.get(n)
+        d_us = sum(ds) / len(ds) if ds else float("nan")
+        lines.append(f"| {n[:60]} | {m} | {util:.1f}% | {fb:.2f} | {ff:.2f} | {d_us:.1f} | "
+                     f"{fb / d_us * 1e3:.1f} | {ff / d_us * 1e3:.1f} |")
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sp = ap.add_subparsers(dest="mode", required=True)
@@ -236,8 +300,15 @@ def main():
     p.add_argument("workload")
     p.add_argument("--cmd", default="")
     p.add_argument("--out", default=None)
+    m = sp.add_parser("mfma")
+    m.add_argument("dir")
+    m.add_argument("workload")
+    m.add_argument("--trace", default=None)
+    m.add_argument("--cmd", default="")
+    m.add_argument("--trace-cmd", default="")
+    m.add_argument("--out", default=None)
     a = ap.parse_args()
-    cmd_trace(a) if a.mode == "trace" else cmd_pmc(a)
+    {"trace": cmd_trace, "pmc": cmd_pmc, "mfma": cmd_mfma}[a.mode](a)
 
 
 if __name__ == "__main__":
