@@ -606,7 +606,7 @@ def main():
     buf = torch.empty(nb, dtype=torch.uint8, device=dev)
     sink = torch.empty(4096, dtype=torch.int32, device=dev)
     best = 0.0
-    for blocks in (1024, 2048, 4096):
+    for blocks in (256, 512, 1024, 2048, 4096):
         plib.zha_probe_stream_read(buf.data_ptr(), nb, sink.data_ptr(), blocks, sst)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()

@@ -17,16 +17,16 @@
 
 // Score-kernel tuning: tiles in flight per wave (planes with R >= 8 / R < 8; key form).
 #ifndef ZHA_SCORE_UN_WIDE
-#define ZHA_SCORE_UN_WIDE 2
+#define ZHA_SCORE_UN_WIDE 1
 #endif
 #ifndef ZHA_SCORE_UN_NARROW
 #define ZHA_SCORE_UN_NARROW 2
 #endif
 #ifndef ZHA_KEYS_UN
-#define ZHA_KEYS_UN 2
+#define ZHA_KEYS_UN 1
 #endif
 #ifndef ZHA_SCORE_UN_BF16
-#define ZHA_SCORE_UN_BF16 4
+#define ZHA_SCORE_UN_BF16 2
 #endif
 
 namespace zha {
