@@ -25,7 +25,9 @@ per-span form, single-key blocks, nucleus selection for b=1, brute-force minimal
 mass conservation, append = rebuild, geometry; for the bf16 router planes: rounding
 against torch's float32 -> bfloat16 cast and a brute-force nearest search, and the score
 perturbation bound; for FP4 planes: a brute-force nearest search over the 16 codes,
-constructed halfway cases, the block-scale property and the same bound).  The exact
+constructed halfway cases, the block-scale property and the same bound; for the
+reference-query fit: central differences of the loss, the exact level-1 router of
+single-key blocks, non-negativity and a brute-force loss).  The exact
 routed sets at p<1 on the synthetic data are defined only by this oracle ("parity
 unpinned" beyond those pins).
 """
@@ -169,6 +171,107 @@ def append_token(tree: Tree, key: np.ndarray) -> None:
             s_all[node] = s[0]
             c_all[node] = c[0]
         tree.levels[lv - 1] = (s_all, c_all)
+
+
+# --------------------------------------------------------------------------- reference-query fitting
+def node_log_mass(keys: np.ndarray, q: np.ndarray, block: int, level: int, n_tokens: int) -> np.ndarray:
+    """Dense attention mass of each level-``level`` node for query q, as a log.
+
+    [news] "How is ZHA trained onto existing models?": the fitting target is the dense
+    attention mass of every block at every level.  With z_t = sigma q.k_t over all
+    n_tokens keys, node n holds tokens [n b^l, (n+1) b^l) and its mass is
+    sum over those tokens of softmax(z)_t.  Returns log mass [n_l].
+    """
+    keys = np.asarray(keys, dtype=np.float64)[:n_tokens]
+    q = np.asarray(q, dtype=np.float64)
+    span = block ** level
+    nn = -(-n_tokens // span)
+    z = (keys @ q) / math.sqrt(q.shape[0])
+    zp = np.full(nn * span, -np.inf)
+    zp[:n_tokens] = z
+    return _logsumexp(zp.reshape(nn, span), axis=1) - _logsumexp(z, axis=0)
+
+
+def router_log_probs(tree: Tree, level: int, q: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """The router's estimated distribution over all nodes of a level for query q:
+    softmax of the node scores max_j(sigma q.s_j + c_j) over the level ([blog] "Routing
+    through the tree": the scores are estimates of each node's log attention mass).
+    Returns (log probabilities [n_l], arg-max plane [n_l], lowest index on a tie)."""
+    s, c = tree.levels[level - 1]
+    q = np.asarray(q, dtype=np.float64)
+    f = (s @ q) / math.sqrt(q.shape[0]) + c                   # [n_l, R]
+    am = np.argmax(f, axis=1)
+    sc = f[np.arange(f.shape[0]), am]
+    return sc - _logsumexp(sc, axis=0), am
+
+
+def fit_loss(keys: np.ndarray, refs: np.ndarray, block: int, levels: int, n_tokens: int,
+             queries: np.ndarray) -> float:
+    """KL fitting loss of the reference queries of one tree.
+
+    [blog] "Routing through the tree" and [news] "How is ZHA trained onto existing
+    models?": the model stays frozen and only the reference queries are trained, so that
+    at every level of the tree the router's probabilities reproduce how dense attention
+    spreads its mass over the nodes.  Readings: the divergence is KL(dense || router)
+    over all nodes of a level (the distillation direction: the dense mass is the target),
+    summed over the levels and averaged over the training queries; the tree is rebuilt
+    from the reference queries as in ``build_tree``.
+
+    queries [Q, d] (the training queries of the KV head's group)  ->  loss
+    """
+    tree = build_tree(keys, refs, block, levels, n_tokens)
+    total = 0.0
+    for q in np.asarray(queries, dtype=np.float64):
+        for lv in range(1, levels + 1):
+            logm = node_log_mass(keys, q, block, lv, n_tokens)
+            logpi, _ = router_log_probs(tree, lv, q)
+            m = np.exp(logm)
+            total += float(np.sum(np.where(m > 0, m * (logm - logpi), 0.0)))
+    return total / len(queries)
+
+
+def fit_grad(keys: np.ndarray, refs: np.ndarray, block: int, levels: int, n_tokens: int,
+             queries: np.ndarray) -> tuple[float, np.ndarray]:
+    """``fit_loss`` and its gradient with respect to the reference queries.
+
+    Node n's score for q is plane i*(q, n) at q (the arg-max plane; its gradient is the
+    subgradient of the max).  The plane of reference query r over the node's tokens is
+    LSE(r) + sigma (q - r).s(r), with s(r) = sum_t softmax_t(sigma r.k_t) k_t, so its
+    derivative in r is sigma^2 C (q - r) with C = sum_t w_t (k_t - s)(k_t - s)^T the
+    covariance of the node's keys under those weights.  The derivative of KL(m || pi) in
+    the node's score is pi - m.  Returns (loss, grad [R, d]).
+    """
+    keys = np.asarray(keys, dtype=np.float64)
+    refs = np.asarray(refs, dtype=np.float64)
+    queries = np.asarray(queries, dtype=np.float64)
+    d = keys.shape[1]
+    sig = 1.0 / math.sqrt(d)
+    tree = build_tree(keys, refs, block, levels, n_tokens)
+    grad = np.zeros_like(refs)
+    total = 0.0
+    for lv in range(1, levels + 1):
+        span = block ** lv
+        nn = tree.nodes(lv)
+        kp = np.zeros((nn * span, d))
+        kp[:n_tokens] = keys[:n_tokens]
+        kn = kp.reshape(nn, span, d)                          # the keys of each node
+        exists = (np.arange(nn * span) < n_tokens).reshape(nn, span)
+        s, _ = tree.levels[lv - 1]
+        for q in queries:
+            logm = node_log_mass(keys, q, block, lv, n_tokens)
+            logpi, am = router_log_probs(tree, lv, q)
+            m = np.exp(logm)
+            total += float(np.sum(np.where(m > 0, m * (logm - logpi), 0.0)))
+            g = np.exp(logpi) - m                             # d KL / d score
+            r = refs[am]                                      # [nn, d] each node's arg-max query
+            zr = sig * np.einsum("ntd,nd->nt", kn, r)
+            zr = np.where(exists, zr, -np.inf)
+            w = np.exp(zr - _logsumexp(zr, axis=1)[:, None])  # [nn, span]
+            diff = kn - s[np.arange(nn), am][:, None, :]      # k_t - s
+            a = np.einsum("ntd,nd->nt", diff, q[None, :] - r)
+            contrib = sig * sig * np.einsum("nt,ntd->nd", w * a, diff) * g[:, None]
+            np.add.at(grad, am, contrib)
+    return total / len(queries), grad / len(queries)
 
 
 # --------------------------------------------------------------------------- bf16 router planes

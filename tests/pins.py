@@ -418,7 +418,84 @@ def check_fp4_planes(seed=16):
     return moved > 0, f"{moved} quantised scores moved"
 
 
+# F3: the fitting gradient is the derivative of the fitting loss (central differences of
+# the loss, which rebuilds the tree at every perturbed point).
+def check_fit_grad_fd(seed=17):
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for (n, d, r, b, levels) in [(13, 8, 3, 2, 3), (37, 8, 1, 4, 2), (29, 6, 2, 3, 3)]:
+        keys = rng.standard_normal((n, d))
+        refs = rng.standard_normal((r, d))
+        qs = rng.standard_normal((3, d)) * 2
+        loss, g = zo.fit_grad(keys, refs, b, levels, n, qs)
+        if abs(loss - zo.fit_loss(keys, refs, b, levels, n, qs)) > 1e-12 * max(1.0, abs(loss)):
+            return False, "fit_grad's loss differs from fit_loss"
+        h = 1e-6
+        for i in range(r):
+            for k in range(d):
+                rp, rm = refs.copy(), refs.copy()
+                rp[i, k] += h
+                rm[i, k] -= h
+                num = (zo.fit_loss(keys, rp, b, levels, n, qs) - zo.fit_loss(keys, rm, b, levels, n, qs)) / (2 * h)
+                err = abs(num - g[i, k])
+                worst = max(worst, err)
+                if err > 1e-6 * max(1.0, abs(num)):
+                    return False, f"n={n} b={b}: d loss / d r[{i},{k}] {g[i, k]:.8f} vs difference {num:.8f}"
+    return True, f"worst gradient error {worst:.1e}"
+
+
+# F1: the fitting loss against a brute-force KL built from closed forms: each node's score
+# is the max over the reference queries of the tangent of the node's true log mass (SciPy
+# logsumexp / softmax over the node's span), the router distribution is the softmax of
+# those scores over the level, the target is the dense softmax summed over each span, and
+# the divergence is SciPy's relative entropy of the target to the router.
+def check_fit_loss_bruteforce(seed=18):
+    rng = np.random.default_rng(seed)
+    n, d, r, b, levels = 45, 8, 3, 3, 3
+    keys = rng.standard_normal((n, d))
+    refs = rng.standard_normal((r, d))
+    qs = rng.standard_normal((4, d)) * 2
+    sig = 1.0 / math.sqrt(d)
+    total = 0.0
+    for q in qs:
+        dense = sp.softmax(keys @ q * sig)
+        for lv in range(1, levels + 1):
+            nn = -(-n // b ** lv)
+            toks = [np.arange(j * b ** lv, min((j + 1) * b ** lv, n)) for j in range(nn)]
+            mass = np.array([dense[t].sum() for t in toks])
+            scores = []
+            for t in toks:
+                best = -np.inf
+                for rj in refs:
+                    w = sp.softmax(keys[t] @ rj * sig)
+                    tangent = true_lse(keys, rj, t) + sig * (q - rj) @ (w @ keys[t])
+                    best = max(best, tangent)
+                scores.append(best)
+            total += float(np.sum(sp.rel_entr(mass, sp.softmax(np.array(scores)))))
+    want = total / len(qs)
+    got = zo.fit_loss(keys, refs, b, levels, n, qs)
+    if not (got >= 0.0 and abs(got - want) <= 1e-10 * max(1.0, want)):
+        return False, f"loss {got:.12f} vs brute force {want:.12f}"
+    return True, f"loss {got:.6f}"
+
+
+# F2: single-key blocks make every tangent plane exact (the plane of one key is sigma q.k),
+# so the router reproduces dense attention at every level: zero loss and zero gradient.
+def check_fit_single_key(seed=19):
+    rng = np.random.default_rng(seed)
+    n, d = 17, 8
+    keys = rng.standard_normal((n, d))
+    refs = rng.standard_normal((2, d))
+    qs = rng.standard_normal((3, d)) * 3
+    loss, g = zo.fit_grad(keys, refs, 1, 2, n, qs)
+    if abs(loss) > 1e-12 or np.max(np.abs(g)) > 1e-12:
+        return False, f"b=1: loss {loss:.2e}, largest gradient {np.max(np.abs(g)):.2e}"
+    loss4 = zo.fit_loss(keys, refs, 4, 2, n, qs)
+    return loss4 > 1e-6, f"b=4 loss {loss4:.4f} (> 0)"
+
+
 ALL = [check_dense_limit, check_convexity, check_exact_at_refs, check_recursion_direct,
        check_single_key, check_nucleus, check_minimal, check_mass_conservation, check_append,
        check_masked_attention, check_sink, check_bf16_round_library, check_bf16_round_nearest,
-       check_quantised_planes, check_p_schedule, check_mxfp4_round, check_fp4_planes]
+       check_quantised_planes, check_p_schedule, check_mxfp4_round, check_fp4_planes,
+       check_fit_grad_fd, check_fit_loss_bruteforce, check_fit_single_key]

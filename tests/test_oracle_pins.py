@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import json
+import math
 import os
 
 import numpy as np
@@ -196,6 +197,51 @@ def _mut_level_p_shift(orig):
     return f
 
 
+def _mut_fit_grad_sign(orig):
+    def f(keys, refs, block, levels, n_tokens, queries):
+        loss, g = orig(keys, refs, block, levels, n_tokens, queries)
+        return loss, -g
+    return f
+
+
+def _mut_fit_grad_level1_only(orig):
+    def f(keys, refs, block, levels, n_tokens, queries):
+        loss, _ = orig(keys, refs, block, levels, n_tokens, queries)
+        _, g1 = orig(keys, refs, block, 1, n_tokens, queries)
+        return loss, g1
+    return f
+
+
+def _mut_fit_loss_reversed(orig):
+    def f(keys, refs, block, levels, n_tokens, queries):
+        tree = zo.build_tree(keys, refs, block, levels, n_tokens)
+        total = 0.0
+        for q in np.asarray(queries, dtype=np.float64):
+            for lv in range(1, levels + 1):
+                logm = zo.node_log_mass(keys, q, block, lv, n_tokens)
+                logpi, _ = zo.router_log_probs(tree, lv, q)
+                total += float(np.sum(np.exp(logpi) * (logpi - logm)))
+        return total / len(queries)
+    return f
+
+
+def _mut_node_mass_unnormalised(orig):
+    def f(keys, q, block, level, n_tokens):
+        z = np.asarray(keys, dtype=np.float64)[:n_tokens] @ np.asarray(q, dtype=np.float64) / math.sqrt(len(q))
+        return orig(keys, q, block, level, n_tokens) + float(np.max(z))
+    return f
+
+
+def _mut_router_first_plane(orig):
+    def f(tree, level, q):
+        s, c = tree.levels[level - 1]
+        q = np.asarray(q, dtype=np.float64)
+        sc = (s[:, 0, :] @ q) / math.sqrt(q.shape[0]) + c[:, 0]
+        lp = sc - np.log(np.sum(np.exp(sc - sc.max()))) - sc.max()
+        return lp, np.zeros(sc.shape[0], dtype=np.int64)
+    return f
+
+
 MUTATIONS = [
     ("level1_planes", _mut_level1_offset),
     ("parent_planes", _mut_parent_unweighted),
@@ -211,6 +257,11 @@ MUTATIONS = [
     ("level_p", _mut_level_p_shift),
     ("mxfp4_round", _mut_mxfp4_scale_low),
     ("mxfp4_round", _mut_mxfp4_ties_away),
+    ("fit_grad", _mut_fit_grad_sign),
+    ("fit_grad", _mut_fit_grad_level1_only),
+    ("fit_loss", _mut_fit_loss_reversed),
+    ("node_log_mass", _mut_node_mass_unnormalised),
+    ("router_log_probs", _mut_router_first_plane),
 ]
 
 
