@@ -60,6 +60,11 @@ def parse():
                     help="extra steps timed one by one after a 1 GiB scratch write that evicts L2 and MALL")
     ap.add_argument("--crossover", action="store_true",
                     help="light-router sweep over N: ZHA vs dense decode, crossover context (own JSON line)")
+    ap.add_argument("--fit", action="store_true",
+                    help="reference-query fitting (zha_fit_step) at a 32K-token context on the deep and light "
+                         "geometries: step time per stage, loss, routing before and after (own JSON line)")
+    ap.add_argument("--fit-lr", type=float, default=1.0, help="SGD step of --fit")
+    ap.add_argument("--fit-nq", type=int, default=8, help="training queries per query head and step in --fit")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for traffic)")
     return ap.parse_args()
@@ -309,6 +314,135 @@ def crossover(args):
     print(json.dumps(rec), flush=True)
 
 
+FIT_STAGES = ("fit.cast", "build", "fit.logits", "fit.mass", "fit.score", "fit.loss", "fit.alpha", "fit.grad")
+
+
+def fit_stage_bytes(stage, w, n, nq):
+    """Algorithmic HBM bytes of one fitting stage (all KV heads), Q = nq * g queries per head:
+    fit.logits  K once (2 B/element) + the logits z written (Q x N floats);
+    fit.mass    z read once + the node log masses written (Q floats per node of every level);
+    fit.score   every plane once (R (d+1) floats per node) + a score and an arg-max byte per
+                (query, node);
+    fit.loss    scores and log masses read, d loss / d score written, then read again with the
+                arg-max bytes for the per-node sums (Q x 17 bytes per node);
+    fit.alpha   K and z read once, alpha (R floats per token) written;
+    fit.grad    K and alpha read once."""
+    H, d, R, g = w.num_kv_heads, w.head_dim, w.num_ref, w.group
+    Q = nq * g
+    nodes = sum(-(-n // w.block ** lv) for lv in range(1, w.levels + 1))
+    kbytes = n * d * 2
+    per_head = {
+        "fit.logits": kbytes + Q * n * 4,
+        "fit.mass": Q * n * 4 + Q * nodes * 4,
+        "fit.score": nodes * R * (d + 1) * 4 + Q * nodes * 5,
+        "fit.loss": Q * nodes * (12 + 9) + nodes * R * 12,
+        "fit.alpha": kbytes + Q * n * 4 + n * R * 4,
+        "fit.grad": kbytes + n * R * 4,
+    }.get(stage)
+    return None if per_head is None else float(per_head * H)
+
+
+def fit_bench(args):
+    """Reference-query fitting with zha_fit_step at a 32K-token context (the pages fit at 32K)
+    on the deep geometry (b 4, L 6, R 16) and the light router (R 1, b 8).  Per geometry:
+    `steps` SGD steps on planted training queries (nq per query head, new ones every step),
+    timed as a whole and stage by stage; the loss before and after; and routing on held-out
+    planted queries with the initial and the fitted reference queries (kept blocks of the
+    union, and the relative distance of the routed output to dense decode)."""
+    import torch
+    from hierarchical_tree_indexed_03_amd import zha
+    dev = torch.device("cuda:0")
+    n = 32_768
+    steps = args.steps if args.steps is not None else 40
+    nq = args.fit_nq
+    n_eval = 16
+    res = []
+    for base in (wc.DEEP, wc.light(n)):
+        w = base.with_(n_tokens=n, steps=1)
+        dt = torch.bfloat16
+        K, V = gen.kv_cache(w)
+        Kd, Vd = (torch.from_numpy(x).to(dt).to(dev) for x in (K, V))
+        fetch = gen.host_fetch(K)
+        train = torch.from_numpy(np.stack([gen.step_queries(w, s_, n, fetch) for s_ in range(steps * nq)])).to(dt).to(dev)
+        held = torch.from_numpy(np.stack([gen.step_queries(w, 100_000 + s_, n, fetch) for s_ in range(n_eval)])).to(dt).to(dev)
+        del K, V
+        refs0 = torch.from_numpy(gen.ref_queries(w)).float().to(dev)
+        cfg = zha.make_config(w.head_dim, w.num_kv_heads, w.num_q_heads, w.block, w.levels, w.num_ref, n,
+                              w.dtype, w.top_p, w.keep_sink)
+        t = zha.Tree(cfg)
+        out = torch.empty(w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+        dense = torch.empty_like(out)
+        stats = torch.zeros(w.levels + 1, w.num_kv_heads, dtype=torch.int32, device=dev)
+
+        def route_eval(refs):
+            rb = refs.to(dt).contiguous()
+            t.build(Kd, Vd, n, rb)
+            kept, err = [], []
+            for e_ in range(n_eval):
+                t.decode(held[e_], out, stats)
+                t.decode_dense(held[e_], dense)
+                kept.append(int(stats[w.levels].sum().item()))
+                err.append(float(((out - dense).norm(dim=1) / dense.norm(dim=1)).mean().item()))
+            return dict(kept_blocks_union=float(np.mean(kept)), blocks=int(-(-n // w.block)) * w.num_kv_heads,
+                        out_rel_err_vs_dense=float(np.mean(err)))
+
+        before = route_eval(refs0)
+        refs = refs0.clone()
+        loss0, _ = t.fit_step(Kd, Vd, n, refs, train[:nq], lr=0.0, grad=False)
+        loss0 = float(loss0.mean().item())
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s_ in range(steps):
+            t.fit_step(Kd, Vd, n, refs, train[s_ * nq:(s_ + 1) * nq], lr=args.fit_lr, grad=False)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        loss1, _ = t.fit_step(Kd, Vd, n, refs, train[:nq], lr=0.0, grad=False)
+        loss1 = float(loss1.mean().item())
+        # per-stage times (lr = 0: the fitted queries stay as they are)
+        stage_ms = {}
+        for key in FIT_STAGES:
+            zha.zha_profile_start(t.handle, key)
+            for s_ in range(4):
+                t.fit_step(Kd, Vd, n, refs, train[s_ * nq:(s_ + 1) * nq], lr=0.0, grad=False)
+            torch.cuda.synchronize()
+            tot, cnt = zha.zha_profile_stop(t.handle)
+            stage_ms[key] = tot / 4
+        after = route_eval(refs)
+        dom = max((k for k in stage_ms if k.startswith("fit.")), key=stage_ms.get)
+        bts = fit_stage_bytes(dom, w, n, nq)
+        roof = None
+        if bts is not None:
+            ach = bts / (stage_ms[dom] * 1e-3) / 1e9
+            roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": 8000.0, "unit": "GB/s",
+                    "frac": round(ach / 8000.0, 4), "algorithmic_bytes_per_step": bts,
+                    "avg_stage_ms": round(stage_ms[dom], 4), "traffic": None}
+        Q = nq * w.group
+        row = {"geometry": w.name.split("_")[0], "n_tokens": n, "block": w.block, "levels": w.levels,
+               "num_ref": w.num_ref, "top_p": w.top_p, "train_queries_per_kv_head_per_step": Q, "steps": steps,
+               "lr": args.fit_lr, "ms_per_step": round(ms, 4),
+               "train_queries_per_s": round(Q * w.num_kv_heads / (ms * 1e-3), 1),
+               "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()}, "roofline": roof,
+               "loss_first_batch": {"before": round(loss0, 4), "after": round(loss1, 4)},
+               "held_out_routing": {"initial_refs": before, "fitted_refs": after}}
+        log(f"[fit] {row['geometry']}: {ms:.3f} ms/step ({row['train_queries_per_s']:.0f} training queries/s), "
+            f"loss {loss0:.3f} -> {loss1:.3f}; held-out kept blocks {before['kept_blocks_union']:.0f} -> "
+            f"{after['kept_blocks_union']:.0f}, output error vs dense {before['out_rel_err_vs_dense']:.4f} -> "
+            f"{after['out_rel_err_vs_dense']:.4f}; stages " + ", ".join(f"{k}={v:.3f}" for k, v in stage_ms.items()))
+        res.append(row)
+        t.close()
+        del Kd, Vd, train, held
+        torch.cuda.empty_cache()
+    top = res[0]
+    rec = {"metric": "reference-query fit step time (zha_fit_step, KL to dense node mass at every level)",
+           "value": top["ms_per_step"], "unit": "ms/step", "n_gpus": 1, "steps": steps, "warmup": 0,
+           "higher_is_better": False, "vs_baseline": None, "data": "synthetic (planted queries)",
+           "dtype": "bf16+f32", "config": {"workload": "fit_32k", "geometries": [r["geometry"] for r in res]},
+           "roofline": top["roofline"], "per_geometry": res}
+    print(json.dumps(rec))
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -322,6 +456,8 @@ def main():
 
     if args.crossover:
         return crossover(args)
+    if args.fit:
+        return fit_bench(args)
     base = wc.NAMED[args.workload]
     steps = args.steps if args.steps is not None else (base.steps or 64)
     total = args.warmup + steps + args.cold_steps

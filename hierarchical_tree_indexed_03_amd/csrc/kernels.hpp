@@ -82,6 +82,42 @@ struct AttnArgs {
   float* out;         // [Hq][D]
 };
 
+// One fitting step of the reference queries (fit.hip): buffers in the caller's fit
+// workspace, the tree's planes and log masses in dev.
+struct FitArgs {
+  Dev dev;
+  const void* K;          // [Hkv][cap][D] cache dtype
+  const void* q;          // [nq][Hq][D] cache dtype: the training queries
+  float* refs_master;     // [Hkv][R][D] float32 reference queries (the SGD update writes here)
+  void* refs_in;          // [Hkv][R][D] cache dtype: their rounding, which the tree is built from
+  float* refs_r;          // [Hkv][R][D] float32 values of refs_in
+  float* qf;              // [Hkv][Q][D] sigma * q, group order (qi = batch * g + head)
+  float* z;               // [Hkv][Q][zstride] dense logits sigma q.k_t
+  float* lt[MAXL + 1];    // [Hkv][Q][nstride[l]] logsumexp of the logits over each node
+  float* sc[MAXL + 1];    // router score of each node
+  float* gr[MAXL + 1];    // d loss / d score = (pi - m) / Q
+  uint8_t* am[MAXL + 1];  // arg-max plane of each score
+  float* wb[MAXL + 1];    // [Hkv][nstride[l]][R][2] per node and plane: W and beta
+  float* kl;              // [Hkv][Q][levels] KL(m || pi) per query and level
+  float* alpha;           // [Hkv][N][R]
+  float* part;            // [Hkv][nchunk][R][D] partial gradients
+  float* grad;            // [Hkv][R][D]
+  float* loss;            // [Hkv]
+  int64_t cap, N, zstride;
+  int64_t nl[MAXL + 1];       // nodes per level at N
+  int64_t nstride[MAXL + 1];  // row stride of the per-level arrays (nl rounded up to 64)
+  int32_t hkv, hq, g, Q, b, levels, R, D, nchunk;
+  float sigma, lr;
+};
+
+// The fitting step after the tree build, stage by stage (in this order): dense logits,
+// dense node log masses, router scores, loss and per-node sums, alpha per token, gradient
+// and update.
+enum FitStage { FIT_LOGITS = 0, FIT_MASS, FIT_SCORE, FIT_LOSS, FIT_ALPHA, FIT_GRAD, FIT_NSTAGE };
+hipError_t launch_fit_cast_refs(const FitArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_fit_stage(const FitArgs& a, bool bf16, int stage, hipStream_t st);
+int fit_chunk_tokens();
+
 hipError_t launch_build_tile(const BuildArgs& a, bool bf16, int D, int R, int64_t ntiles, int hkv, int T,
                              hipStream_t st);
 hipError_t launch_build_parent(const ParentArgs& a, int D, int R, int hkv, hipStream_t st);

@@ -1,4 +1,5 @@
 // Host side of the ZHA C ABI: argument validation, workspace layout, launch sequencing.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -336,9 +337,123 @@ zha_status enqueue_build(zha_tree* t, const void* k_cache, const void* refs, int
   return ZHA_OK;
 }
 
+constexpr int64_t FIT_MAX_Q = 4096;   // training queries per KV head in one fitting step
+
+// Lays out the fit workspace for n_tokens tokens and nq training queries per head; with
+// base == nullptr only the size is computed.
+size_t fit_layout(const zha_config& c, int64_t N, int64_t nq, char* base, FitArgs* fa) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    off = (off + 255) & ~(size_t)255;
+    char* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  };
+  FitArgs a;
+  memset(&a, 0, sizeof a);
+  const int64_t H = c.num_kv_heads, R = c.num_ref, D = c.head_dim, g = c.num_q_heads / c.num_kv_heads;
+  const int64_t Q = nq * g;
+  const int L = c.levels;
+  a.refs_in = take((size_t)(H * R * D) * 4);
+  a.refs_r = (float*)take((size_t)(H * R * D) * 4);
+  a.qf = (float*)take((size_t)(H * Q * D) * 4);
+  a.zstride = ceil_div(N, 64) * 64;
+  a.z = (float*)take((size_t)(H * Q * a.zstride) * 4);
+  for (int l = 1; l <= L; ++l) {
+    a.nl[l] = nodes_at(c, l, N);
+    a.nstride[l] = ceil_div(a.nl[l], 64) * 64;
+    a.lt[l] = (float*)take((size_t)(H * Q * a.nstride[l]) * 4);
+    a.sc[l] = (float*)take((size_t)(H * Q * a.nstride[l]) * 4);
+    a.gr[l] = (float*)take((size_t)(H * Q * a.nstride[l]) * 4);
+    a.am[l] = (uint8_t*)take((size_t)(H * Q * a.nstride[l]));
+    a.wb[l] = (float*)take((size_t)(H * a.nstride[l] * R * 2) * 4);
+  }
+  a.kl = (float*)take((size_t)(H * Q * L) * 4);
+  a.alpha = (float*)take((size_t)(H * N * R) * 4);
+  a.nchunk = (int32_t)ceil_div(N, fit_chunk_tokens());
+  a.part = (float*)take((size_t)(H * a.nchunk * R * D) * 4);
+  a.grad = (float*)take((size_t)(H * R * D) * 4);   // used when the caller wants no gradient
+  a.N = N;
+  a.Q = (int32_t)Q;
+  if (fa) *fa = a;
+  return (off + 255) & ~(size_t)255;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t zha_fit_workspace_bytes(const zha_config* cfg, int64_t n_tokens, int64_t nq) {
+  if (validate(cfg) != ZHA_OK) return 0;
+  if (n_tokens < 1 || n_tokens > cfg->capacity || nq < 1) return 0;
+  if (nq * (cfg->num_q_heads / cfg->num_kv_heads) > FIT_MAX_Q) return 0;
+  return fit_layout(*cfg, n_tokens, nq, nullptr, nullptr);
+}
+
+zha_status zha_fit_step(zha_tree* t, void* k_cache, void* v_cache, int64_t n_tokens, float* ref_queries,
+                        const void* q, int64_t nq, float lr, float* loss, float* grad, void* fit_ws,
+                        size_t fit_ws_bytes, hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  const zha_config& c = t->cfg;
+  if (!k_cache || !v_cache || !ref_queries || !q || !loss || !fit_ws)
+    return fail(ZHA_E_INVALID, "null cache, reference-query, query, loss or workspace pointer");
+  if (((uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)ref_queries | (uintptr_t)q | (uintptr_t)grad) % 16)
+    return fail(ZHA_E_INVALID, "cache, reference-query, query and gradient pointers must be 16-byte aligned");
+  if ((uintptr_t)fit_ws % 256) return fail(ZHA_E_INVALID, "fit workspace not 256-byte aligned");
+  if (n_tokens < 1) return fail(ZHA_E_INVALID, "n_tokens %lld < 1", (long long)n_tokens);
+  if (n_tokens > c.capacity)
+    return fail(ZHA_E_CAPACITY, "n_tokens %lld > capacity %lld", (long long)n_tokens, (long long)c.capacity);
+  const int64_t g = c.num_q_heads / c.num_kv_heads;
+  if (nq < 1 || nq * g > FIT_MAX_Q)
+    return fail(ZHA_E_INVALID, "nq %lld: between 1 and %lld training queries per KV head", (long long)nq,
+                (long long)(FIT_MAX_Q / g));
+  if (!std::isfinite(lr)) return fail(ZHA_E_INVALID, "lr is not finite");
+  const size_t need = fit_layout(c, n_tokens, nq, nullptr, nullptr);
+  if (fit_ws_bytes < need)
+    return fail(ZHA_E_WORKSPACE, "fit workspace %zu bytes < %zu needed", fit_ws_bytes, need);
+  FitArgs a;
+  fit_layout(c, n_tokens, nq, (char*)fit_ws, &a);
+  a.K = k_cache;
+  a.q = q;
+  a.refs_master = ref_queries;
+  a.loss = loss;
+  if (grad) a.grad = grad;
+  a.cap = c.capacity;
+  a.hkv = c.num_kv_heads;
+  a.hq = c.num_q_heads;
+  a.g = (int32_t)g;
+  a.b = c.block;
+  a.levels = c.levels;
+  a.R = c.num_ref;
+  a.D = c.head_dim;
+  a.sigma = 1.0f / sqrtf((float)c.head_dim);
+  a.lr = lr;
+  const bool bf16 = c.dtype == ZHA_BF16;
+  hipError_t e;
+  {
+    ProfScope ps(t, "fit.cast", stream);
+    e = launch_fit_cast_refs(a, bf16, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "fit cast launch");
+  zha_status zs = enqueue_build(t, k_cache, a.refs_in, 0, n_tokens, stream);
+  if (zs != ZHA_OK) return zs;
+  t->K = k_cache;
+  t->V = v_cache;
+  t->refs = a.refs_in;
+  t->N = n_tokens;
+  t->built = true;
+  a.dev = t->dev;
+  static const char* const stage_key[FIT_NSTAGE] = {"fit.logits", "fit.mass", "fit.score", "fit.loss", "fit.alpha",
+                                                     "fit.grad"};
+  for (int stage = 0; stage < FIT_NSTAGE; ++stage) {
+    {
+      ProfScope ps(t, stage_key[stage], stream);
+      e = launch_fit_stage(a, bf16, stage, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, stage_key[stage]);
+  }
+  return ZHA_OK;
+}
 
 zha_status zha_tree_build(zha_tree* t, void* k_cache, void* v_cache, int64_t n_tokens, const void* ref_queries,
                           hipStream_t stream) {

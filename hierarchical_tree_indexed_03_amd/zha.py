@@ -58,6 +58,8 @@ def _load() -> ctypes.CDLL:
         "zha_profile_start": (I32, [P, ctypes.c_char_p]),
         "zha_profile_stop": (I32, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
         "zha_set_top_p_levels": (I32, [P, ctypes.POINTER(ctypes.c_float)]),
+        "zha_fit_workspace_bytes": (SZ, [ctypes.POINTER(zha_config), I64, I64]),
+        "zha_fit_step": (I32, [P, P, P, I64, P, P, I64, ctypes.c_float, P, P, P, SZ, P]),
         "zha_num_tokens": (I64, [P]),
         "zha_destroy": (I32, [P]),
         "zha_status_string": (ctypes.c_char_p, [I32]),
@@ -73,8 +75,8 @@ _lib = _load()
 EXPORTED = ("zha_workspace_bytes", "zha_level1_key_form", "zha_create", "zha_tree_build", "zha_tree_append",
             "zha_tree_append_n", "zha_decode", "zha_prefill",
             "zha_decode_dense", "zha_debug_level", "zha_debug_router_planes", "zha_debug_trace", "zha_debug_route_level",
-            "zha_profile_start", "zha_profile_stop", "zha_set_top_p_levels", "zha_num_tokens", "zha_destroy", "zha_status_string",
-            "zha_last_error")
+            "zha_profile_start", "zha_profile_stop", "zha_set_top_p_levels", "zha_fit_workspace_bytes", "zha_fit_step",
+            "zha_num_tokens", "zha_destroy", "zha_status_string", "zha_last_error")
 
 
 def _p(x):
@@ -187,6 +189,16 @@ def zha_set_top_p_levels(t, p_levels=None):
     _check(_lib.zha_set_top_p_levels(t, arr))
 
 
+def zha_fit_workspace_bytes(cfg: zha_config, n_tokens: int, nq: int) -> int:
+    return _lib.zha_fit_workspace_bytes(ctypes.byref(cfg), n_tokens, nq)
+
+
+def zha_fit_step(t, k_cache, v_cache, n_tokens: int, ref_queries, q, nq: int, lr: float, loss, grad, fit_ws,
+                 fit_ws_bytes: int, stream=None):
+    _check(_lib.zha_fit_step(t, _p(k_cache), _p(v_cache), n_tokens, _p(ref_queries), _p(q), nq, lr, _p(loss),
+                             _p(grad), _p(fit_ws), fit_ws_bytes, _s(stream)))
+
+
 def zha_num_tokens(t) -> int:
     return int(_lib.zha_num_tokens(t))
 
@@ -253,6 +265,24 @@ class Tree:
             out = torch.empty(self.cfg.num_q_heads, self.cfg.head_dim, dtype=torch.float32, device=q.device)
         zha_decode_dense(self.handle, q, out, stream)
         return out
+
+    def fit_step(self, K, V, n_tokens, refs, q, lr=0.0, grad=True, stream=None):
+        """One fitting step of the reference queries: refs (float32 [Hkv, R, d]) are updated in
+        place by refs -= lr * grad.  q: [nq, Hq, d] training queries.  The tree is left built
+        over the rounded refs the loss was taken at.  Returns (loss [Hkv], grad [Hkv, R, d] or
+        None), device tensors."""
+        nq = q.shape[0]
+        need = zha_fit_workspace_bytes(self.cfg, n_tokens, nq)
+        if need == 0:
+            raise ValueError(f"no fit workspace for n_tokens={n_tokens}, nq={nq}")
+        ws = getattr(self, "_fit_ws", None)
+        if ws is None or ws.numel() < need:
+            ws = self._fit_ws = torch.empty(need, dtype=torch.uint8, device=refs.device)
+        loss = torch.empty(self.cfg.num_kv_heads, dtype=torch.float32, device=refs.device)
+        g = torch.empty_like(refs) if grad else None
+        self._keep = [K, V, refs, ws]
+        zha_fit_step(self.handle, K, V, n_tokens, refs, q, nq, lr, loss, g, ws, ws.numel(), stream)
+        return loss, g
 
     @property
     def n_tokens(self) -> int:

@@ -130,6 +130,42 @@ zha_status zha_tree_append_n(zha_tree* t, const void* k_new, const void* v_new, 
 zha_status zha_tree_append(zha_tree* t, const void* k_new, const void* v_new,
                            hipStream_t stream);
 
+/* Fitting the reference queries (blog, "Routing through the tree"; news summary, "How is
+ * ZHA trained onto existing models?": the model stays frozen, only the reference queries
+ * are trained, and a KL loss matches the router's probabilities to the dense attention
+ * mass of every node at every level).  One call is one step of gradient descent on
+ *   loss_kv = (1/Q) sum over the Q = nq * (Hq/Hkv) training queries of the KV head's group
+ *             sum over levels l of KL(m_l || pi_l),
+ *   m_l  = dense attention mass of each level-l node: sum over its tokens of
+ *          softmax_t(q.k_t / sqrt(d)) over all n_tokens keys,
+ *   pi_l = softmax over all level-l nodes of the router score max_j(q.s_j/sqrt(d) + c_j).
+ * Readings (the pages give neither): KL(dense || router), over every node of a level; the
+ * gradient of a node's score goes through its arg-max plane (lowest index on a tie); plain
+ * SGD.  Work size: n_tokens * (Q + (levels + 1) * R) * d multiply-adds per KV head.
+ *
+ * zha_fit_workspace_bytes: bytes of the device fit workspace for this config, n_tokens and
+ * nq (0 if invalid, or if nq * (Hq/Hkv) > 4096).  Host only.
+ *
+ * zha_fit_step:
+ *   k_cache, v_cache  (device) [Hkv][capacity][d] dtype, as for zha_tree_build.
+ *   n_tokens          1..capacity tokens the fit sees.
+ *   ref_queries       (device) float32 [Hkv][R][d]: the master copy.  The tree is built from
+ *                     its rounding to `dtype` (kept in fit_ws, which the handle then borrows
+ *                     like zha_tree_build's reference queries); loss and gradient are taken
+ *                     there; then ref_queries -= lr * grad in float32 (lr = 0: unchanged).
+ *   q                 (device) [nq][Hq][d] dtype: training queries, query head h of the
+ *                     group of KV head h / (Hq/Hkv).
+ *   loss              (device) float32 [Hkv]: loss_kv at the rounded reference queries.
+ *   grad              (device, nullable) float32 [Hkv][R][d]: its gradient.
+ *   fit_ws            (device) >= zha_fit_workspace_bytes, 256-byte aligned; caller-owned.
+ * Afterwards the handle holds a tree over the rounded pre-update reference queries;
+ * rebuild with zha_tree_build to route with the updated ones.  Errors as for
+ * zha_tree_build, plus ZHA_E_WORKSPACE for a short fit workspace. */
+size_t zha_fit_workspace_bytes(const zha_config* cfg, int64_t n_tokens, int64_t nq);
+zha_status zha_fit_step(zha_tree* t, void* k_cache, void* v_cache, int64_t n_tokens, float* ref_queries,
+                        const void* q, int64_t nq, float lr, float* loss, float* grad, void* fit_ws,
+                        size_t fit_ws_bytes, hipStream_t stream);
+
 /* One decode step for all query heads (blog, "Routing through the tree").
  *   q      (device) [Hq][d] dtype.
  *   out    (device) [Hq][d] float32: softmax attention over the routed tokens.

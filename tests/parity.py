@@ -216,3 +216,42 @@ def gpu_tokens(trace0: dict, gi: int, b: int, n_tokens: int, keep_sink=True) -> 
 
 def out_err(o_gpu: np.ndarray, o_ref: np.ndarray) -> float:
     return float(np.max(np.abs(o_gpu - o_ref)) / max(1e-30, np.max(np.abs(o_ref))))
+
+
+def fit_flip_allowance(keys, refs, block, levels, n_tokens, queries, tol=2 * SCORE_TOL) -> np.ndarray:
+    """Per-element allowance [R, d] for the fitting gradient: a (query, node) whose two best
+    planes lie within `tol` of each other may take either as its arg-max on the GPU, which
+    moves that pair's contribution g * sigma^2 C_p (q - r_p) between the two planes; the
+    allowance adds the absolute contribution of both (divided by the number of queries, as
+    the gradient is a mean)."""
+    import math
+    keys = np.asarray(keys, dtype=np.float64)
+    refs = np.asarray(refs, dtype=np.float64)
+    queries = np.asarray(queries, dtype=np.float64)
+    d = keys.shape[1]
+    sig = 1.0 / math.sqrt(d)
+    tree = zo.build_tree(keys, refs, block, levels, n_tokens)
+    allow = np.zeros_like(refs)
+    if refs.shape[0] < 2:
+        return allow
+    for lv in range(1, levels + 1):
+        s, c = tree.levels[lv - 1]
+        span = block ** lv
+        for q in queries:
+            f = sig * (s @ q) + c
+            top = np.sort(f, axis=1)
+            near = np.nonzero(top[:, -1] - top[:, -2] < tol)[0]
+            if near.size == 0:
+                continue
+            logm = zo.node_log_mass(keys, q, block, lv, n_tokens)
+            logpi, _ = zo.router_log_probs(tree, lv, q)
+            g = np.exp(logpi) - np.exp(logm)
+            for n in near:
+                toks = keys[n * span:min((n + 1) * span, n_tokens)]
+                for p in np.argsort(f[n])[-2:]:
+                    z = sig * toks @ refs[p]
+                    w = np.exp(z - np.max(z))
+                    w /= w.sum()
+                    diff = toks - s[n, p]
+                    allow[p] += np.abs(g[n] * sig * sig * ((w * (diff @ (q - refs[p]))) @ diff))
+    return allow / len(queries)
