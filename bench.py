@@ -317,6 +317,15 @@ def crossover(args):
 FIT_STAGES = ("fit.cast", "build", "fit.logits", "fit.mass", "fit.score", "fit.loss", "fit.alpha", "fit.grad")
 
 
+def fit_stage_flops(stage, w, n, nq):
+    """Algorithmic multiply-add work (as flops) of the MFMA stages: fit.score is
+    2 Q R d flops per node of every level on fp32 MFMA; fit.logits 2 Q d per token (bf16)."""
+    H, d, R, g = w.num_kv_heads, w.head_dim, w.num_ref, w.group
+    Q = nq * g
+    nodes = sum(-(-n // w.block ** lv) for lv in range(1, w.levels + 1))
+    return {"fit.score": 2.0 * Q * R * d * nodes * H}.get(stage)
+
+
 def fit_stage_bytes(stage, w, n, nq):
     """Algorithmic HBM bytes of one fitting stage (all KV heads), Q = nq * g queries per head:
     fit.logits  K once (2 B/element) + the logits z written (Q x N floats);
@@ -411,9 +420,15 @@ def fit_bench(args):
             stage_ms[key] = tot / 4
         after = route_eval(refs)
         dom = max((k for k in stage_ms if k.startswith("fit.")), key=stage_ms.get)
+        fl = fit_stage_flops(dom, w, n, nq)
         bts = fit_stage_bytes(dom, w, n, nq)
         roof = None
-        if bts is not None:
+        if fl is not None:
+            ach = fl / (stage_ms[dom] * 1e-3) / 1e12
+            roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": 157.3, "unit": "TFLOP/s",
+                    "dtype": "f32", "frac": round(ach / 157.3, 4), "algorithmic_flops_per_step": fl,
+                    "algorithmic_bytes_per_step": bts, "avg_stage_ms": round(stage_ms[dom], 4), "traffic": None}
+        elif bts is not None:
             ach = bts / (stage_ms[dom] * 1e-3) / 1e9
             roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": 8000.0, "unit": "GB/s",
                     "frac": round(ach / 8000.0, 4), "algorithmic_bytes_per_step": bts,

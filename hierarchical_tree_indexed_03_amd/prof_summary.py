@@ -3,6 +3,7 @@
     python -m hierarchical_tree_indexed_03_amd.prof_summary trace DIR WORKLOAD --cmd "..." [--out FILE]
     python -m hierarchical_tree_indexed_03_amd.prof_summary pmc FETCH_DIR WRITE_DIR WORKLOAD --cmd "..." [--out FILE]
     python -m hierarchical_tree_indexed_03_amd.prof_summary mfma DIR WORKLOAD --trace TRACE_DIR --cmd "..." [--out FILE]
+    python -m hierarchical_tree_indexed_03_amd.prof_summary stats DIR --prefix fit_,build_ --title "..." --cmd "..." [--out FILE]
 
 ``trace`` reads ``*_kernel_trace.csv`` (``rocprofv3 --kernel-trace --stats --output-format csv``)
 and attributes every dispatch of a decode (route_prep ... combine) to its router level: the
@@ -166,6 +167,31 @@ def cmd_trace(a):
     print(text)
 
 
+def cmd_stats(a):
+    """Per-kernel totals of a rocprofv3 --stats run, restricted to kernels whose short name
+    starts with one of a.prefix (comma separated)."""
+    stats = glob.glob(os.path.join(a.dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not stats:
+        sys.exit(f"no kernel_stats.csv under {a.dir}")
+    pre = tuple(p for p in a.prefix.split(",") if p)
+    rows = [r for r in csv.DictReader(open(stats[0])) if short(r["Name"]).startswith(pre)]
+    total = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+    lines = [f"# rocprofv3 kernel statistics: {a.title}", "", "Command (from the repository root on the GPU host):",
+             "", "```", a.cmd, "```", "", "Summarised with:", "", "```",
+             f"python -m hierarchical_tree_indexed_03_amd.prof_summary stats <dir> --prefix {a.prefix} --title '...' --cmd '...'",
+             "```", "", "| kernel | calls | avg us | min us | max us | share of these kernels |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| {short(r['Name'])[:70]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{100 * float(r['TotalDurationNs']) / total:.1f}% |")
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
 def read_pmc(d, counter):
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     if not files:
@@ -307,8 +333,14 @@ def main():
     m.add_argument("--cmd", default="")
     m.add_argument("--trace-cmd", default="")
     m.add_argument("--out", default=None)
+    x = sp.add_parser("stats")
+    x.add_argument("dir")
+    x.add_argument("--prefix", default="")
+    x.add_argument("--title", default="")
+    x.add_argument("--cmd", default="")
+    x.add_argument("--out", default=None)
     a = ap.parse_args()
-    {"trace": cmd_trace, "pmc": cmd_pmc, "mfma": cmd_mfma}[a.mode](a)
+    {"trace": cmd_trace, "pmc": cmd_pmc, "mfma": cmd_mfma, "stats": cmd_stats}[a.mode](a)
 
 
 if __name__ == "__main__":
