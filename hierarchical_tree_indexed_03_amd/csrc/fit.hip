@@ -259,19 +259,21 @@ __global__ __launch_bounds__(256) void fit_loss_kernel(FitArgs a) {
 
 // ------------------------------------------------------------------ per-node sums
 // wb[lv][kv][n][i] = (W_i, beta_i): W_i = sum of g over the queries whose arg-max plane at
-// the node is i, beta_i = (sum of g * score over them - W_i LSE_i) / sigma.
+// the node is i, beta_i = (sum of g * score over them - W_i LSE_i) / sigma.  One wave per
+// node: lane l takes queries l, l + 64, ...; the per-plane sums are reduced across the wave
+// in a fixed order.
 template <int R>
 __global__ __launch_bounds__(256) void fit_node_kernel(FitArgs a, int lv) {
+  const int lane = threadIdx.x & 63;
   const int64_t nn = a.nl[lv], st = a.nstride[lv];
   const int64_t total = (int64_t)a.hkv * nn;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+  for (int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); i < total; i += (int64_t)gridDim.x * 4) {
     const int kv = (int)(i / nn);
     const int64_t n = i % nn;
     float W[R], B[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) { W[r] = 0.f; B[r] = 0.f; }
-#pragma unroll 4
-    for (int qi = 0; qi < a.Q; ++qi) {
+    for (int qi = lane; qi < a.Q; qi += 64) {
       const int64_t o = ((int64_t)kv * a.Q + qi) * st + n;
       const int p = a.am[lv][o];
       const float g = a.gr[lv][o], s = a.sc[lv][o];
@@ -279,10 +281,20 @@ __global__ __launch_bounds__(256) void fit_node_kernel(FitArgs a, int lv) {
       for (int r = 0; r < R; ++r)
         if (p == r) { W[r] += g; B[r] += g * s; }
     }
-    const float* L = lse_row(a, lv, kv, n);
-    float2* out = (float2*)a.wb[lv] + ((int64_t)kv * st + n) * R;
 #pragma unroll
-    for (int r = 0; r < R; ++r) out[r] = make_float2(W[r], (B[r] - W[r] * L[r]) / a.sigma);
+    for (int r = 0; r < R; ++r)
+      for (int off = 32; off > 0; off >>= 1) {
+        W[r] += __shfl_xor(W[r], off);
+        B[r] += __shfl_xor(B[r], off);
+      }
+    if (lane < R) {
+      float w = 0.f, bsum = 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (lane == r) { w = W[r]; bsum = B[r]; }
+      const float L = lse_row(a, lv, kv, n)[lane];
+      ((float2*)a.wb[lv])[((int64_t)kv * st + n) * R + lane] = make_float2(w, (bsum - w * L) / a.sigma);
+    }
   }
 }
 
@@ -442,7 +454,7 @@ static hipError_t fit_stage_t(const FitArgs& a, int stage, hipStream_t st) {
     case FIT_LOSS:
       hipLaunchKernelGGL(fit_loss_kernel, dim3((unsigned)a.Q, (unsigned)a.levels, (unsigned)a.hkv), dim3(256), 0, st, a);
       for (int lv = 1; lv <= a.levels; ++lv)
-        hipLaunchKernelGGL((fit_node_kernel<R>), dim3(grid_n((int64_t)a.hkv * a.nl[lv], 256)), dim3(256), 0, st, a, lv);
+        hipLaunchKernelGGL((fit_node_kernel<R>), dim3(grid_n((int64_t)a.hkv * a.nl[lv], 4)), dim3(256), 0, st, a, lv);
       break;
     case FIT_ALPHA:
       hipLaunchKernelGGL((fit_alpha_kernel<TIn, D, R>), dim3((unsigned)((a.N + 255) / 256), (unsigned)a.hkv), dim3(256), 0, st, a);
