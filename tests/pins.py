@@ -418,7 +418,7 @@ def check_fp4_planes(seed=16):
     return moved > 0, f"{moved} quantised scores moved"
 
 
-# F3: the fitting gradient is the derivative of the fitting loss (central differences of
+# K3: the fitting gradient is the derivative of the fitting loss (central differences of
 # the loss, which rebuilds the tree at every perturbed point).
 def check_fit_grad_fd(seed=17):
     rng = np.random.default_rng(seed)
@@ -444,7 +444,7 @@ def check_fit_grad_fd(seed=17):
     return True, f"worst gradient error {worst:.1e}"
 
 
-# F1: the fitting loss against a brute-force KL built from closed forms: each node's score
+# K1: the fitting loss against a brute-force KL built from closed forms: each node's score
 # is the max over the reference queries of the tangent of the node's true log mass (SciPy
 # logsumexp / softmax over the node's span), the router distribution is the softmax of
 # those scores over the level, the target is the dense softmax summed over each span, and
@@ -479,7 +479,7 @@ def check_fit_loss_bruteforce(seed=18):
     return True, f"loss {got:.6f}"
 
 
-# F2: single-key blocks make every tangent plane exact (the plane of one key is sigma q.k),
+# K2: single-key blocks make every tangent plane exact (the plane of one key is sigma q.k),
 # so the router reproduces dense attention at every level: zero loss and zero gradient.
 def check_fit_single_key(seed=19):
     rng = np.random.default_rng(seed)
