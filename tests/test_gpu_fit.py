@@ -115,3 +115,30 @@ def test_fit_argument_errors():
     assert e.value.status == 4
     assert zha.zha_fit_workspace_bytes(t.cfg, w.n_tokens, 5000) == 0
     t.close()
+
+
+@pytest.mark.parametrize("geom,heads", [("deep", (0, 3)), ("light", (0,))])
+def test_fit_at_bench_size(geom, heads):
+    """The configuration bench.py --fit times: 32K tokens, 8 training queries per query head
+    (64 per KV head), the workload's own reference queries; loss and gradient of the listed
+    KV heads against the oracle (same tolerances)."""
+    n, nq = 32_768, 8
+    w = (wc.DEEP if geom == "deep" else wc.light(n)).with_(n_tokens=n, steps=1)
+    K, V, refs = P.host_inputs(w)
+    qs = np.stack([gen.step_queries(w, s, n, gen.host_fetch(K)) for s in range(nq)])
+    refs32 = refs.astype(np.float32)
+    t = P.make_tree(w)
+    Kd, Vd = P.upload(K, w), P.upload(V, w)
+    rt = torch.from_numpy(refs32).cuda()
+    loss, grad = t.fit_step(Kd, Vd, n, rt, P.upload(qs, w), lr=0.0)
+    loss, grad = loss.cpu().numpy(), grad.cpu().numpy()
+    ro = oracle_refs(w, refs32)
+    for kv in heads:
+        qg = group_queries(w, qs, kv)
+        lo, go = zo.fit_grad(K[kv], ro[kv], w.block, w.levels, n, qg)
+        assert abs(loss[kv] - lo) <= 2e-4 * w.levels + 1e-5 * abs(lo), f"head {kv}: loss {loss[kv]:.6f} vs {lo:.6f}"
+        allow = P.fit_flip_allowance(K[kv], ro[kv], w.block, w.levels, n, qg)
+        err = np.abs(grad[kv] - go)
+        tol = 2e-3 * np.max(np.abs(go)) + allow
+        assert np.all(err <= tol), f"head {kv}: gradient error {np.max(err - tol):.3e} above tolerance"
+    t.close()
