@@ -28,6 +28,9 @@ GEOMS = {
     "d64_r2_bf16": (wc.TINY.with_(num_ref=2, dtype="bf16", n_tokens=3001, block=8, levels=3), 4),
     "deep_small": (wc.DEEP.with_(n_tokens=4096 + 37, levels=4), 1),
     "light_small": (wc.light(32_768).with_(n_tokens=9000), 2),
+    # 80 training queries per KV head: two LDS query blocks in the scoring, two per lane in
+    # the per-node sums
+    "deep_q80": (wc.DEEP.with_(n_tokens=2048 + 5, levels=3, num_kv_heads=1, num_q_heads=8), 10),
 }
 
 
