@@ -372,8 +372,29 @@ def fit_bench(args):
         K, V = gen.kv_cache(w)
         Kd, Vd = (torch.from_numpy(x).to(dt).to(dev) for x in (K, V))
         fetch = gen.host_fetch(K)
-        train = torch.from_numpy(np.stack([gen.step_queries(w, s_, n, fetch) for s_ in range(steps * nq)])).to(dt).to(dev)
+        train_h = np.stack([gen.step_queries(w, s_, n, fetch) for s_ in range(steps * nq)])
+        train = torch.from_numpy(train_h).to(dt).to(dev)
         held = torch.from_numpy(np.stack([gen.step_queries(w, 100_000 + s_, n, fetch) for s_ in range(n_eval)])).to(dt).to(dev)
+        cpu = None
+        if not args.no_cpu and not res:
+            # the oracle's fit_grad on KV head 0 with its group's first batch of queries (one
+            # query per head), on one thread, scaled to a whole step (nq per head, all heads)
+            from threadpoolctl import threadpool_limits
+            from oracle import zha_oracle as zo
+            r0 = gen.ref_queries(w)[0].astype(np.float64)
+            calls = 0
+            with threadpool_limits(1):
+                c0 = time.perf_counter()
+                while calls < len(train_h) and time.perf_counter() - c0 < min(args.cpu_budget, 10.0):
+                    zo.fit_grad(K[0], r0, w.block, w.levels, n, train_h[calls, :w.group, :].astype(np.float64))
+                    calls += 1
+                el = time.perf_counter() - c0
+            per_step = el / calls * nq * w.num_kv_heads
+            cpu = {"value": round(per_step * 1e3, 1), "unit": "ms/step", "cores": 1, "kind": "oracle",
+                   "sample": (f"oracle.fit_grad on KV head 0 of {w.num_kv_heads}, {calls} calls with {w.group} training "
+                              f"queries each (one per query head) over {n} tokens: {el:.1f}s on 1 thread, scaled to a "
+                              f"step of {nq} queries per query head on every KV head"),
+                   "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}
         del K, V
         refs0 = torch.from_numpy(gen.ref_queries(w)).float().to(dev)
         cfg = zha.make_config(w.head_dim, w.num_kv_heads, w.num_q_heads, w.block, w.levels, w.num_ref, n,
@@ -440,7 +461,7 @@ def fit_bench(args):
                "train_queries_per_s": round(Q * w.num_kv_heads / (ms * 1e-3), 1),
                "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()}, "roofline": roof,
                "loss_first_batch": {"before": round(loss0, 4), "after": round(loss1, 4)},
-               "held_out_routing": {"initial_refs": before, "fitted_refs": after}}
+               "held_out_routing": {"initial_refs": before, "fitted_refs": after}, "cpu_baseline": cpu}
         log(f"[fit] {row['geometry']}: {ms:.3f} ms/step ({row['train_queries_per_s']:.0f} training queries/s), "
             f"loss {loss0:.3f} -> {loss1:.3f}; held-out kept blocks {before['kept_blocks_union']:.0f} -> "
             f"{after['kept_blocks_union']:.0f}, output error vs dense {before['out_rel_err_vs_dense']:.4f} -> "
@@ -454,7 +475,7 @@ def fit_bench(args):
            "value": top["ms_per_step"], "unit": "ms/step", "n_gpus": 1, "steps": steps, "warmup": 0,
            "higher_is_better": False, "vs_baseline": None, "data": "synthetic (planted queries)",
            "dtype": "bf16+f32", "config": {"workload": "fit_32k", "geometries": [r["geometry"] for r in res]},
-           "roofline": top["roofline"], "per_geometry": res}
+           "roofline": top["roofline"], "cpu_baseline": top["cpu_baseline"], "per_geometry": res}
     print(json.dumps(rec))
 
 
