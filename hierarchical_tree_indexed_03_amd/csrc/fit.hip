@@ -136,8 +136,8 @@ __global__ __launch_bounds__(256) void fit_lse_kernel(FitArgs a, int lv) {
 // (16/R nodes x R planes) against 16 queries at a time on fp32 MFMA, the contraction
 // permuted as in the decode's plane scoring (lane (col, kg) streams the 16-byte pieces
 // [16 i + 4 kg, +4) of its row); the max over a node's planes runs across R lanes, lowest
-// plane on a tie.  A wave holds one plane tile; the workgroup stages 64 queries at a time
-// in LDS (rows padded by 4 floats), which its four waves share.
+// plane on a tie.  The workgroup stages 64 queries at a time in LDS (rows padded by 4
+// floats); its four waves then stride over the level's plane tiles against them.
 constexpr int FIT_QB = 64;
 template <int D, int R>
 __global__ __launch_bounds__(256) void fit_score_kernel(FitArgs a, int lv) {
@@ -151,14 +151,7 @@ __global__ __launch_bounds__(256) void fit_score_kernel(FitArgs a, int lv) {
   const int64_t nn = a.nl[lv], cap = a.dev.ncap[lv], st = a.nstride[lv];
   const float* S = a.dev.s[lv] + (int64_t)kv * cap * R * D;
   const float* C = a.dev.c[lv] + (int64_t)kv * cap * R;
-  const int64_t tile = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t node = tile * NPT + slot;
-  const bool ok = node < nn;
-  const float* sp = S + ((ok ? node : 0) * R + plane) * D + 4 * kg;
-  float4 sb[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) sb[i] = ok ? *(const float4*)(sp + 16 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
-  const float cj = ok ? C[node * R + plane] : -INFINITY;
+  const int64_t ntiles = (nn + NPT - 1) / NPT;
   const float* qg = a.qf + (int64_t)kv * a.Q * D;
   for (int qb = 0; qb < a.Q; qb += FIT_QB) {
     __syncthreads();
@@ -169,38 +162,47 @@ __global__ __launch_bounds__(256) void fit_score_kernel(FitArgs a, int lv) {
       *(float4*)(qs + row * QS + 4 * c4) = v;
     }
     __syncthreads();
-    for (int qt = 0; qt < FIT_QB / 16 && qb + qt * 16 < a.Q; ++qt) {
-      const float* qp = qs + (qt * 16 + col) * QS + 4 * kg;   // A operand row of this lane
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < ntiles; tile += (int64_t)gridDim.x * 4) {
+      const int64_t node = tile * NPT + slot;
+      const bool ok = node < nn;
+      const float* sp = S + ((ok ? node : 0) * R + plane) * D + 4 * kg;
+      float4 sb[NI];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const float4 qv = *(const float4*)(qp + 16 * i);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.x, sb[i].x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.y, sb[i].y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.z, sb[i].z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.w, sb[i].w, acc, 0, 0, 0);
-      }
-      // acc[e]: query qb + qt*16 + 4 kg + e, plane row col
-      float v[4];
-      int im[4];
+      for (int i = 0; i < NI; ++i) sb[i] = ok ? *(const float4*)(sp + 16 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float cj = ok ? C[node * R + plane] : -INFINITY;
+      for (int qt = 0; qt < FIT_QB / 16 && qb + qt * 16 < a.Q; ++qt) {
+        const float* qp = qs + (qt * 16 + col) * QS + 4 * kg;   // A operand row of this lane
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { v[e] = acc[e] + cj; im[e] = plane; }
-#pragma unroll
-      for (int off = 1; off < R; off <<= 1)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float ov = __shfl_xor(v[e], off);
-          const int oi = __shfl_xor(im[e], off);
-          if (ov > v[e] || (ov == v[e] && oi < im[e])) { v[e] = ov; im[e] = oi; }
+        for (int i = 0; i < NI; ++i) {
+          const float4 qv = *(const float4*)(qp + 16 * i);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.x, sb[i].x, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.y, sb[i].y, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.z, sb[i].z, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.w, sb[i].w, acc, 0, 0, 0);
         }
-      if (ok && plane == 0) {
+        // acc[e]: query qb + qt*16 + 4 kg + e, plane row col
+        float v[4];
+        int im[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int qi = qb + qt * 16 + 4 * kg + e;
-          if (qi < a.Q) {
-            const int64_t o = ((int64_t)kv * a.Q + qi) * st + node;
-            a.sc[lv][o] = v[e];
-            a.am[lv][o] = (uint8_t)im[e];
+        for (int e = 0; e < 4; ++e) { v[e] = acc[e] + cj; im[e] = plane; }
+#pragma unroll
+        for (int off = 1; off < R; off <<= 1)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ov = __shfl_xor(v[e], off);
+            const int oi = __shfl_xor(im[e], off);
+            if (ov > v[e] || (ov == v[e] && oi < im[e])) { v[e] = ov; im[e] = oi; }
+          }
+        if (ok && plane == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int qi = qb + qt * 16 + 4 * kg + e;
+            if (qi < a.Q) {
+              const int64_t o = ((int64_t)kv * a.Q + qi) * st + node;
+              a.sc[lv][o] = v[e];
+              a.am[lv][o] = (uint8_t)im[e];
+            }
           }
         }
       }
@@ -448,7 +450,9 @@ static hipError_t fit_stage_t(const FitArgs& a, int stage, hipStream_t st) {
     case FIT_SCORE:
       for (int lv = 1; lv <= a.levels; ++lv) {
         const int64_t ntiles = (a.nl[lv] + 16 / R - 1) / (16 / R);
-        hipLaunchKernelGGL((fit_score_kernel<D, R>), dim3((unsigned)((ntiles + 3) / 4), (unsigned)a.hkv), dim3(256), 0, st, a, lv);
+        static const int per_cu = resident_per_cu(fit_score_kernel<D, R>, 256);
+        const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
+        hipLaunchKernelGGL((fit_score_kernel<D, R>), dim3(grid_for(ntiles, 4, cap), (unsigned)a.hkv), dim3(256), 0, st, a, lv);
       }
       break;
     case FIT_LOSS:
