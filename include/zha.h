@@ -158,9 +158,11 @@ zha_status zha_tree_append(zha_tree* t, const void* k_new, const void* v_new,
  *   loss              (device) float32 [Hkv]: loss_kv at the rounded reference queries.
  *   grad              (device, nullable) float32 [Hkv][R][d]: its gradient.
  *   fit_ws            (device) >= zha_fit_workspace_bytes, 256-byte aligned; caller-owned.
- * Afterwards the handle holds a tree over the rounded pre-update reference queries;
- * rebuild with zha_tree_build to route with the updated ones.  Errors as for
- * zha_tree_build, plus ZHA_E_WORKSPACE for a short fit workspace. */
+ * The router fitted is the float32-plane one (with bf16 or FP4 router copies configured,
+ * the build still writes them, and decode reads them).  Afterwards the handle holds a tree
+ * over the rounded pre-update reference queries; rebuild with zha_tree_build to route with
+ * the updated ones.  Errors as for zha_tree_build, plus ZHA_E_WORKSPACE for a short fit
+ * workspace. */
 size_t zha_fit_workspace_bytes(const zha_config* cfg, int64_t n_tokens, int64_t nq);
 zha_status zha_fit_step(zha_tree* t, void* k_cache, void* v_cache, int64_t n_tokens, float* ref_queries,
                         const void* q, int64_t nq, float lr, float* loss, float* grad, void* fit_ws,
