@@ -121,10 +121,12 @@ __global__ __launch_bounds__(256) void build_tile_kernel(BuildArgs a) {
   __shared__ float As[T * R];
   // s of the last in-tile level, for the next level's recursion (R < 8 path)
   constexpr int SR_HALF = R < 8 ? 2048 : 4;
-  // bf16 keys, R = 16, 128-token tiles: level 1's weighted means by the register path (a
-  // thread per (node, 4 columns) sums its block's b keys for all R planes), which issues far
-  // fewer instructions than one MFMA item per (node, 16 columns) for b-token blocks
-  constexpr bool L1_REG = R == 16 && sizeof(TIn) == 2 && T == 128;
+  // bf16 keys, R = 16, 128-token tiles: the weighted means of levels 1 and 2 by the register
+  // path (a thread per (node, 4 columns) sums the node's keys for all R planes), which issues
+  // far fewer instructions than one MFMA item per (node, 16 columns) over b or b^2 tokens;
+  // the levels above keep the MFMA items (measured: 0.79 ms against 1.03 ms for the deep
+  // tree at 256K, and 0.84 ms with every in-tile level on the register path)
+  constexpr bool L12_REG = R == 16 && sizeof(TIn) == 2 && T == 128;
   __shared__ __align__(16) float Sr[2 * SR_HALF];
 
   const int kv = blockIdx.y;
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(256) void build_tile_kernel(BuildArgs a) {
         a.dev.w1[((int64_t)kv * a.dev.ncap[1] + t0 / b + node) * R * b + j * b + k] = t < nt ? Ws[t * R + j] : 0.f;
       }
     }
-    if (R >= 8 && !(L1_REG && v == 1)) {
+    if (R >= 8 && !(L12_REG && v <= 2)) {
       const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
       const int col = lane & 15, kg = lane >> 4;
       const int items = nexist * (D / 16);
