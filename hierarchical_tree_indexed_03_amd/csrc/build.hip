@@ -174,31 +174,44 @@ __global__ __launch_bounds__(256) void build_tile_kernel(BuildArgs a) {
     const int nv = (int)(T / bv);
     const int nexist = (int)((nt + bv - 1) / bv);
     const int nprev_exist = (int)((nt + bprev - 1) / bprev);
-    for (int idx = threadIdx.x; idx < nv * R; idx += NT) {
+    // P threads per (node, plane) when there are fewer pairs than threads (wide nodes), the
+    // P partial max / sums combined across the group's lanes in a fixed order
+    int P = 1;
+    while (P < 64 && P * 2 * nv * R <= NT) P *= 2;
+    const int sub = threadIdx.x % P;
+    for (int idx = threadIdx.x / P; idx < nv * R; idx += NT / P) {
       const int node = idx / R, j = idx % R;
-      if (node >= nexist) continue;
-      float mx = -INFINITY, sum = 0.f, lse, A = 0.f;
+      if (node >= nexist) continue;   // the whole group skips together
+      const float* src;   // the node's children: the tokens' logits, or the level below
+      const float* Ac = nullptr;
+      int cb, ce;
       if (v == 1) {
-        const int tb = node * a.b, te = min(tb + a.b, nt);
-        for (int t = tb; t < te; ++t) mx = fmaxf(mx, Zs[t * R + j]);
-        for (int t = tb; t < te; ++t) sum += expf(Zs[t * R + j] - mx);
-        lse = mx + logf(sum);
-        for (int t = tb; t < te; ++t) A += expf(Zs[t * R + j] - lse) * Zs[t * R + j];
+        cb = node * a.b;
+        ce = min(cb + a.b, nt);
+        src = Zs;
       } else {
-        const int cb = node * a.b, ce = min(cb + a.b, nprev_exist);
-        const float* Lc = Ls + off[v - 1];
-        const float* Ac = As + off[v - 1];
-        for (int ch = cb; ch < ce; ++ch) mx = fmaxf(mx, Lc[ch * R + j]);
-        for (int ch = cb; ch < ce; ++ch) sum += expf(Lc[ch * R + j] - mx);
-        lse = mx + logf(sum);
-        for (int ch = cb; ch < ce; ++ch) A += expf(Lc[ch * R + j] - lse) * Ac[ch * R + j];
+        cb = node * a.b;
+        ce = min(cb + a.b, nprev_exist);
+        src = Ls + off[v - 1];
+        Ac = As + off[v - 1];
       }
-      Ls[off[v] + idx] = lse;
-      As[off[v] + idx] = A;
-      const int64_t gnode = t0 / bv + node;
-      const int64_t gi = ((int64_t)kv * a.dev.ncap[v] + gnode) * R + j;
-      a.dev.c[v][gi] = lse - A;
-      a.dev.lse[v][gi] = lse;
+      float mx = -INFINITY, sum = 0.f, A = 0.f;
+      for (int c = cb + sub; c < ce; c += P) mx = fmaxf(mx, src[c * R + j]);
+      for (int o = P / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      for (int c = cb + sub; c < ce; c += P) sum += expf(src[c * R + j] - mx);
+      for (int o = P / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+      const float lse = mx + logf(sum);
+      for (int c = cb + sub; c < ce; c += P)
+        A += expf(src[c * R + j] - lse) * (v == 1 ? src[c * R + j] : Ac[c * R + j]);
+      for (int o = P / 2; o > 0; o >>= 1) A += __shfl_xor(A, o);
+      if (sub == 0) {
+        Ls[off[v] + idx] = lse;
+        As[off[v] + idx] = A;
+        const int64_t gnode = t0 / bv + node;
+        const int64_t gi = ((int64_t)kv * a.dev.ncap[v] + gnode) * R + j;
+        a.dev.c[v][gi] = lse - A;
+        a.dev.lse[v][gi] = lse;
+      }
     }
     __syncthreads();
   }
