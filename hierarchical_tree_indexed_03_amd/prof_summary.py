@@ -290,8 +290,8 @@ def cmd_mfma(a):
              "Durations come from the kernel trace of the same workload"
              + (f" (`{a.trace_cmd}`)" if a.trace_cmd else "") + ".", "",
              "Summarised with:", "", "```",
-             f"python -m hierarchical_tree_indexed_03_amd.prof_summary mfma gpurun_out/mfma_{a.workload} "
-             f"{a.workload} --trace gpurun_out/prof_{a.workload} --cmd '...' --trace-cmd '...'",
+             f"python -m hierarchical_tree_indexed_03_amd.prof_summary mfma {a.dir} "
+             f"{a.workload} --trace {a.trace} --cmd '...' --trace-cmd '...'",
              "```", "",
              "MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES summed over the chip / (GRBM_GUI_ACTIVE x "
              "1,024 SIMDs), the MfmaUtil expression of rocprofv3; MFMA flops = MOPS x 512.", "",
