@@ -100,6 +100,9 @@ zha_status validate(const zha_config* c) {
   if (c->num_q_heads / c->num_kv_heads > GMAX)
     return fail(ZHA_E_UNSUPPORTED, "group size %d > %d", c->num_q_heads / c->num_kv_heads, GMAX);
   if (c->block < 2 || c->block > 256) return fail(ZHA_E_INVALID, "block %d outside 2..256", c->block);
+  // the build summarises 128- or 256-token tiles whose nodes must start on tile boundaries
+  if (c->block & (c->block - 1))
+    return fail(ZHA_E_UNSUPPORTED, "block %d is not a power of two", c->block);
   if (c->levels < 1 || c->levels > MAXL) return fail(ZHA_E_INVALID, "levels %d outside 1..%d", c->levels, MAXL);
   if (c->num_ref != 1 && c->num_ref != 2 && c->num_ref != 4 && c->num_ref != 8 && c->num_ref != 16)
     return fail(ZHA_E_UNSUPPORTED, "num_ref %d not built (1, 2, 4, 8, 16)", c->num_ref);

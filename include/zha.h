@@ -58,7 +58,8 @@ typedef struct {
   int32_t head_dim;       /* d: 64 or 128                                               */
   int32_t num_kv_heads;   /* Hkv >= 1: one tree per KV head                             */
   int32_t num_q_heads;    /* Hq: a multiple of Hkv with Hq/Hkv <= 8                     */
-  int32_t block;          /* b: 2..256 tokens per leaf block / children per node       */
+  int32_t block;          /* b: tokens per leaf block / children per node, a power of
+                             two in 2..256 (others: ZHA_E_UNSUPPORTED)                  */
   int32_t levels;         /* L: 1..16 summary levels                                    */
   int32_t num_ref;        /* R: 1, 2, 4, 8 or 16 reference queries per tree             */
   int64_t capacity;       /* max tokens the caches (and the tree) may hold              */

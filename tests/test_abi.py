@@ -49,6 +49,7 @@ BAD = [
     (dict(levels=17), 1), (dict(num_ref=3), 2), (dict(capacity=0), 1), (dict(capacity=1 << 31), 1),
     (dict(dtype=5), 1), (dict(top_p=0.0), 1), (dict(top_p=1.5), 1), (dict(top_p=float("nan")), 1),
     (dict(dtype="f32", block=256), 2), (dict(planes=3), 1), (dict(planes=-1), 1),
+    (dict(block=6), 2), (dict(block=100), 2), (dict(block=255), 2),
 ]
 
 
@@ -90,7 +91,9 @@ def test_level1_key_form_choice(zha):
     assert zha.zha_level1_key_form(good(zha, block=8, num_ref=1, dtype=zha.ZHA_BF16)) == 0
     assert zha.zha_level1_key_form(good(zha, block=256, num_ref=16, dtype=zha.ZHA_BF16)) == 0
     assert zha.zha_level1_key_form(good(zha, block=4, num_ref=16, dtype=zha.ZHA_F32)) == 0
-    assert zha.zha_level1_key_form(good(zha, block=6, num_ref=16, dtype=zha.ZHA_BF16)) == 0
+    assert zha.zha_level1_key_form(good(zha, block=16, num_ref=16, dtype=zha.ZHA_BF16)) == 1
+    assert zha.zha_level1_key_form(good(zha, block=32, num_ref=16, dtype=zha.ZHA_BF16)) == 0
+    assert zha.zha_level1_key_form(good(zha, block=6, num_ref=16, dtype=zha.ZHA_BF16)) == -1   # not a power of two
     assert zha.zha_level1_key_form(good(zha, block=0)) == -1
     # the token weights take extra workspace
     ws_key = zha.zha_workspace_bytes(good(zha, block=4, num_ref=16, dtype=zha.ZHA_BF16))
