@@ -24,6 +24,9 @@ SMALL = {
     "ultra_small": wc.ULTRA.with_(n_tokens=70_001, steps=2),
     "light_d64": wc.light(32_768, steps=2).with_(n_tokens=20_000 + 3, head_dim=64),
     "deep_d64_r4": wc.DEEP.with_(n_tokens=10_000 + 3, head_dim=64, num_ref=4, levels=4, steps=2),
+    # one or two (node, plane) pairs per build tile: each pair's log-sum-exp split over 64 lanes
+    "wide_r1": wc.WIDE.with_(n_tokens=6_144 + 77, num_ref=1, steps=2),
+    "b128_r2_f32": wc.WIDE.with_(block=128, levels=2, num_ref=2, dtype="f32", n_tokens=20_000 + 9, steps=2),
 }
 
 
