@@ -837,7 +837,10 @@ def main():
         "decode_step": {"level1_key_form": key_form, "alg_bytes": round(step_bytes), "achieved_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                         "router_bytes": round(float(np.mean(router_b))), "gather_bytes": round(float(np.mean(gather_b))),
                         "frontier_union_per_level": timed_stats[:, :L, :].sum(axis=2).mean(axis=0).round(1).tolist(),
-                        "kept_blocks_union": float(timed_stats[:, L, :].sum(axis=1).mean())},
+                        "kept_blocks_union": float(timed_stats[:, L, :].sum(axis=1).mean()),
+                        # per KV head (levels 1..L, then the kept blocks): a head's grid share is
+                        # fixed, so the largest sets the launch time
+                        "union_per_kv_head": timed_stats.mean(axis=0).round(1).tolist()},
         "build": {"ms": round(build_s * 1e3, 4), "tokens_per_s": round(build_tok_s), "alg_bytes": round(build_bytes),
                   "frac_hbm": round(build_bytes / build_s / 1e9 / HBM_PEAK_GBS, 4)},
         "dense": {"ms": round(dense_ms, 4), "queries_per_s": round(1e3 / dense_ms, 2),

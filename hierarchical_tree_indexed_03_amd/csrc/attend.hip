@@ -62,6 +62,55 @@ __device__ __forceinline__ void split_range(int64_t F, int splits, int split, in
   fe = min(fb + chunk, F);
 }
 
+// Routed attention: the KV heads keep different numbers of blocks, so their gather lists
+// are cut into chunks of one common length and each head gets as many splits as it has
+// chunks (a fixed number of splits per head would leave the launch waiting on the head
+// that kept the most).  The chunk covers all heads' tokens with a.splits x Hkv splits and
+// never gives one head more than MAX_SPLITS.  Every kernel derives it from the level-0
+// counts the same way.
+__device__ __forceinline__ int64_t routed_chunk(const AttnArgs& a) {
+  int64_t F = 0, Fmax = 0;
+  for (int k = 0; k < a.hkv; ++k) {
+    const int64_t f = (int64_t)a.dev.cnt[k] * a.b;
+    F += f;
+    Fmax = f > Fmax ? f : Fmax;
+  }
+  const int64_t c1 = split_chunk(F, a.splits * a.hkv), c2 = split_chunk(Fmax, MAX_SPLITS);
+  return c1 > c2 ? c1 : c2;
+}
+__device__ __forceinline__ int routed_splits(const AttnArgs& a, int kv, int64_t chunk) {
+  const int64_t f = (int64_t)a.dev.cnt[kv] * a.b;
+  return (int)((f + chunk - 1) / chunk);
+}
+
+// The workgroup's KV head, split and token range [fb, fe) of its gather list (or of all N
+// tokens for dense attention: grid (splits, Hkv)); false when it has no tokens.  Routed: a
+// one-dimensional grid of a.splits x Hkv + Hkv workgroups over the heads' splits in order.
+template <bool DENSE>
+__device__ __forceinline__ bool attn_work(const AttnArgs& a, int& kv, int& split, int64_t& fb, int64_t& fe) {
+  if constexpr (DENSE) {
+    kv = blockIdx.y;
+    split = blockIdx.x;
+    split_range(a.N, a.splits, split, fb, fe);
+    return fb < fe;
+  } else {
+    const int64_t ch = routed_chunk(a);
+    int x = blockIdx.x;
+    for (int k = 0; k < a.hkv; ++k) {
+      const int sk = routed_splits(a, k, ch);
+      if (x < sk) {
+        kv = k;
+        split = x;
+        fb = (int64_t)x * ch;
+        fe = min(fb + ch, (int64_t)a.dev.cnt[k] * a.b);
+        return true;
+      }
+      x -= sk;
+    }
+    return false;
+  }
+}
+
 template <typename TIn, int D, bool DENSE>
 __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   using VT = typename Vec<TIn>::T;
@@ -78,27 +127,23 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   __shared__ float Ml[4][GMAX], Ll[4][GMAX];
   __shared__ float Ol[4][GMAX][D];
 
-  const int kv = blockIdx.y, split = blockIdx.x;
+  int kv, split;
+  int64_t fb, fe;
+  if (!attn_work<DENSE>(a, kv, split, fb, fe)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const int g = a.g;
   const TIn* Kb = (const TIn*)a.K + (int64_t)kv * a.cap * D;
   const TIn* Vb = (const TIn*)a.V + (int64_t)kv * a.cap * D;
 
-  int64_t F;
+  // the gather list: kept level-1 blocks of the group's union (level-0 entries)
   const int32_t* gnode = nullptr;
   const uint32_t* gmask = nullptr;
-  if constexpr (DENSE) {
-    F = a.N;
-  } else {
+  if constexpr (!DENSE) {
     const int64_t cap0 = a.dev.ncap[0];
-    F = (int64_t)a.dev.cnt[kv] * a.b;   // level-0 count: kept level-1 blocks of the union
     gnode = a.dev.node[0] + kv * cap0;
     gmask = a.dev.mask[0] + kv * cap0;
   }
-  int64_t fb, fe;
-  split_range(F, a.splits, split, fb, fe);
-  if (fb >= fe) return;
 
   Qk<TIn, D> qk;
   qk.load_q((const TIn*)a.q + (int64_t)kv * g * D, g, col, kg);
@@ -262,7 +307,9 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
   constexpr int OL_BYTES = 4 * GMAX * D * 4;
   __shared__ __align__(16) unsigned char buf[VT_BYTES > OL_BYTES ? VT_BYTES : OL_BYTES];
 
-  const int kv = blockIdx.y, split = blockIdx.x;
+  int kv, split;
+  int64_t fb, fe;
+  if (!attn_work<DENSE>(a, kv, split, fb, fe)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const int g = a.g;
@@ -270,20 +317,13 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
   const bf16_t* Vb = (const bf16_t*)a.V + (int64_t)kv * a.cap * D;
   uint16_t* Vt = (uint16_t*)buf + wave * D * VS;
 
-  int64_t F;
   const int32_t* gnode = nullptr;
   const uint32_t* gmask = nullptr;
-  if constexpr (DENSE) {
-    F = a.N;
-  } else {
+  if constexpr (!DENSE) {
     const int64_t cap0 = a.dev.ncap[0];
-    F = (int64_t)a.dev.cnt[kv] * a.b;
     gnode = a.dev.node[0] + kv * cap0;
     gmask = a.dev.mask[0] + kv * cap0;
   }
-  int64_t fb, fe;
-  split_range(F, a.splits, split, fb, fe);
-  if (fb >= fe) return;
 
   Qk<bf16_t, D> qk;
   qk.load_q((const bf16_t*)a.q + (int64_t)kv * g * D, g, col, kg);
@@ -438,15 +478,17 @@ __global__ __launch_bounds__(512) void combine_kernel(AttnArgs a, int32_t* stats
   const int hq = blockIdx.x, kv = hq / a.g, gi = hq % a.g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* base = a.dev.apart + (int64_t)hq * MAX_SPLITS * (D + 2);
-  int64_t F;
-  if constexpr (DENSE) F = a.N;
-  else F = (int64_t)a.dev.cnt[kv] * a.b;
   // splits that own tokens (same chunking as the attention kernel)
   int S = 0;
-  if (F > 0) {
-    const int64_t ch = split_chunk(F, a.splits);
-    const int64_t s = (F + ch - 1) / ch;
-    S = s < a.splits ? (int)s : a.splits;
+  if constexpr (DENSE) {
+    const int64_t F = a.N;
+    if (F > 0) {
+      const int64_t ch = split_chunk(F, a.splits);
+      const int64_t s = (F + ch - 1) / ch;
+      S = s < a.splits ? (int)s : a.splits;
+    }
+  } else {
+    S = routed_splits(a, kv, routed_chunk(a));
   }
   // pass 1: max of the partial maxima
   float ms = -INFINITY, ls = 0.f;
@@ -547,10 +589,12 @@ __global__ __launch_bounds__(512) void combine_kernel(AttnArgs a, int32_t* stats
 // variant measured slower on every routed workload: lower occupancy, short gathers).
 template <typename TIn, int D, bool DENSE>
 static hipError_t launch_attend_t(const AttnArgs& a, int32_t* stats, int levels, hipStream_t st) {
+  // dense: (splits, Hkv); routed: one dimension over every head's splits (see attn_work)
+  const dim3 grid = DENSE ? dim3((unsigned)a.splits, (unsigned)a.hkv) : dim3((unsigned)(a.splits * a.hkv + a.hkv));
   if constexpr (sizeof(TIn) == 2 && DENSE)
-    hipLaunchKernelGGL((attend_mfma_kernel<D, DENSE>), dim3((unsigned)a.splits, (unsigned)a.hkv), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attend_mfma_kernel<D, DENSE>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((attend_kernel<TIn, D, DENSE>), dim3((unsigned)a.splits, (unsigned)a.hkv), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attend_kernel<TIn, D, DENSE>), grid, dim3(256), 0, st, a);
   hipLaunchKernelGGL((combine_kernel<TIn, D, DENSE>), dim3((unsigned)a.hq), dim3(512), 0, st, a, stats, levels);
   return hipGetLastError();
 }
