@@ -65,7 +65,9 @@ __device__ __forceinline__ void split_range(int64_t F, int splits, int split, in
 // Routed attention: the KV heads keep different numbers of blocks, so their gather lists
 // are cut into chunks of one common length and each head gets as many splits as it has
 // chunks (a fixed number of splits per head would leave the launch waiting on the head
-// that kept the most).  The chunk covers all heads' tokens with a.splits x Hkv splits and
+// that kept the most).  The chunk is sized for a.splits x Hkv - Hkv splits, so that the
+// heads' splits, each head's count rounded up, still fit the a.splits x Hkv workgroups of
+// one resident wave (a workgroup past it would run as a tail of one whole chunk), and it
 // never gives one head more than MAX_SPLITS.  Every kernel derives it from the level-0
 // counts the same way.
 __device__ __forceinline__ int64_t routed_chunk(const AttnArgs& a) {
@@ -75,7 +77,8 @@ __device__ __forceinline__ int64_t routed_chunk(const AttnArgs& a) {
     F += f;
     Fmax = f > Fmax ? f : Fmax;
   }
-  const int64_t c1 = split_chunk(F, a.splits * a.hkv), c2 = split_chunk(Fmax, MAX_SPLITS);
+  const int nsp = a.splits * a.hkv - a.hkv;
+  const int64_t c1 = split_chunk(F, nsp > 1 ? nsp : 1), c2 = split_chunk(Fmax, MAX_SPLITS);
   return c1 > c2 ? c1 : c2;
 }
 __device__ __forceinline__ int routed_splits(const AttnArgs& a, int kv, int64_t chunk) {
@@ -85,7 +88,7 @@ __device__ __forceinline__ int routed_splits(const AttnArgs& a, int kv, int64_t 
 
 // The workgroup's KV head, split and token range [fb, fe) of its gather list (or of all N
 // tokens for dense attention: grid (splits, Hkv)); false when it has no tokens.  Routed: a
-// one-dimensional grid of a.splits x Hkv + Hkv workgroups over the heads' splits in order.
+// one-dimensional grid of a.splits x Hkv workgroups over the heads' splits in order.
 template <bool DENSE>
 __device__ __forceinline__ bool attn_work(const AttnArgs& a, int& kv, int& split, int64_t& fb, int64_t& fe) {
   if constexpr (DENSE) {
@@ -590,7 +593,7 @@ __global__ __launch_bounds__(512) void combine_kernel(AttnArgs a, int32_t* stats
 template <typename TIn, int D, bool DENSE>
 static hipError_t launch_attend_t(const AttnArgs& a, int32_t* stats, int levels, hipStream_t st) {
   // dense: (splits, Hkv); routed: one dimension over every head's splits (see attn_work)
-  const dim3 grid = DENSE ? dim3((unsigned)a.splits, (unsigned)a.hkv) : dim3((unsigned)(a.splits * a.hkv + a.hkv));
+  const dim3 grid = DENSE ? dim3((unsigned)a.splits, (unsigned)a.hkv) : dim3((unsigned)(a.splits * a.hkv));
   if constexpr (sizeof(TIn) == 2 && DENSE)
     hipLaunchKernelGGL((attend_mfma_kernel<D, DENSE>), grid, dim3(256), 0, st, a);
   else
