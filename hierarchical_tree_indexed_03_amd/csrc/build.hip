@@ -245,14 +245,31 @@ __global__ __launch_bounds__(256) void build_tile_kernel(BuildArgs a) {
         const int node = it / (D / 16), n16 = it % (D / 16);
         const int ts = node * (int)bv;
         const int te = min(ts + (int)bv, nt);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int st = ts; st < te; st += 4) {
+        // four independent accumulation chains over 16-token groups (their LDS loads issued
+        // together), then the tail 4 tokens at a time; summed chain by chain at the end
+        f32x4 acc4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc4[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        int st = ts;
+        for (; st + 16 <= te; st += 16) {
+          float w[4], kvv[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int t = st + 4 * u + kg;
+            w[u] = col < R ? Ws[t * R + col] : 0.f;
+            kvv[u] = ld_f32(Ks + t * D + n16 * 16 + col);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc4[u] = mfma_f32(w[u], kvv[u], acc4[u]);
+        }
+        for (; st < te; st += 4) {
           const int t = st + kg;
           const bool ok = t < te;
           float w = (ok && col < R) ? Ws[t * R + col] : 0.f;
           float kvv = ok ? ld_f32(Ks + t * D + n16 * 16 + col) : 0.f;
-          acc = mfma_f32(w, kvv, acc);
+          acc4[0] = mfma_f32(w, kvv, acc4[0]);
         }
+        const f32x4 acc = ((acc4[0] + acc4[1]) + acc4[2]) + acc4[3];
         const int64_t gnode = t0 / bv + node;
         const int64_t so = (((int64_t)kv * a.dev.ncap[v] + gnode) * R) * D + n16 * 16 + col;
         float* sg = a.dev.s[v] + so;
