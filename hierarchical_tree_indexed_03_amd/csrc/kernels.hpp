@@ -59,6 +59,8 @@ struct RouteArgs {
   float top_p[MAXL + 1];  // p of the top-p decision at each level (index = level)
   int32_t dense;      // score kernel: 1 = every node of levels `level` .. `level`-gridDim.z+1
   int32_t dense_lo;   // lowest level handled by the multi-level selection kernel
+  int32_t tf;         // top-down selection: the top level's per-head frontier is given in
+                      // dev.tdbits (teacher forcing) instead of being every node
   int32_t sel_p;      // top-p histogram / classify workgroups per KV head at `level`
   int32_t key_form;   // level 1 scored from the block's keys and the planes' token weights
   int32_t q_bf16;     // q (and the caches) are bf16; else fp32
@@ -140,6 +142,9 @@ hipError_t launch_route_expand(const RouteArgs& a, hipStream_t st);
 // their dense union lists; the list expansion of level `dense_lo` follows.
 hipError_t launch_route_dense_score(const RouteArgs& a, int D, int R, hipStream_t st);
 hipError_t launch_route_topdown(const RouteArgs& a, hipStream_t st);
+// Per-head frontier bitmaps of level a.level in dev.tdbits from that level's union list
+// (dev.node / dev.mask / dev.cnt): the given frontier of a teacher-forced top-down level.
+hipError_t launch_route_td_seed(const RouteArgs& a, hipStream_t st);
 
 hipError_t launch_attend(const AttnArgs& a, bool bf16, int D, bool dense, hipStream_t st);
 // Attention workgroups resident on the GPU at once, per KV head (one wave of workgroups).

@@ -119,6 +119,7 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
             const int pn = lb >= 0 ? (e >> lb) : e / b;
             in = (kp[pn >> 5] >> (pn & 31)) & 1u;
           }
+          if (in && top && a.tf) in = (gbits[e >> 5] >> (e & 31)) & 1u;   // the given frontier
           if (!in) x[k] = -INFINITY;
           mx = fmaxf(mx, x[k]);
         }
@@ -318,6 +319,32 @@ __global__ __launch_bounds__(256) void route_topdown_union_kernel(RouteArgs a) {
     a.dev.mask[lv][kv * cap + e] = fm;
     a.dev.keep[lv][kv * cap + e] = km;
   }
+}
+
+// One workgroup per KV head: clears the group's frontier words of level a.level, then sets
+// the bit of every union-list entry for each head in its mask.
+__global__ __launch_bounds__(256) void route_td_seed_kernel(RouteArgs a) {
+  const int kv = blockIdx.x, lv = a.level, g = a.g;
+  const int64_t n = a.nl[lv], nw = (n + 31) / 32, cap = a.dev.ncap[lv];
+  for (int64_t i = threadIdx.x; i < (int64_t)g * nw; i += 256) {
+    const int gi = (int)(i / nw);
+    a.dev.tdbits[(((int64_t)lv * a.hq + kv * g + gi) * 2) * TD_WORDS + i % nw] = 0u;
+  }
+  __syncthreads();
+  const int64_t cnt = a.dev.cnt[lv * a.hkv + kv];
+  for (int64_t e = threadIdx.x; e < cnt; e += 256) {
+    const int32_t node = a.dev.node[lv][kv * cap + e];
+    const uint32_t mk = a.dev.mask[lv][kv * cap + e];
+    if (node < 0 || node >= n) continue;
+    for (int gi = 0; gi < g; ++gi)
+      if ((mk >> gi) & 1u)
+        atomicOr(&a.dev.tdbits[(((int64_t)lv * a.hq + kv * g + gi) * 2) * TD_WORDS + (node >> 5)], 1u << (node & 31));
+  }
+}
+
+hipError_t launch_route_td_seed(const RouteArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(route_td_seed_kernel, dim3((unsigned)a.hkv), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_route_topdown(const RouteArgs& a, hipStream_t st) {

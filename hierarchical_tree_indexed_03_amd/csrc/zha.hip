@@ -216,6 +216,15 @@ struct ProfScope {
   }
 };
 
+// Lowest level of the top levels that zha_decode scores whole and selects top-down: every
+// level from there up has at most TD_MAX nodes (a key-form level 1 keeps its own kernel).
+int topdown_lo(const RouteArgs& r) {
+  int lo = r.levels + 1;
+  while (lo > 1 && r.nl[lo - 1] <= TD_MAX) --lo;
+  if (r.key_form && lo == 1) lo = 2;
+  return lo;
+}
+
 std::string lvkey(const char* name, int lv) { return std::string(name) + ".l" + std::to_string(lv); }
 
 zha_status route_levels(zha_tree* t, RouteArgs& a, int lv, hipStream_t st, bool expand) {
@@ -559,9 +568,7 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
   }
   if (e != hipSuccess) return hip_fail(e, "route prep launch");
   // top levels small enough to score whole and select top-down in one launch
-  int lo = c.levels + 1;
-  while (lo > 1 && r.nl[lo - 1] <= TD_MAX) --lo;
-  if (r.key_form && lo == 1) lo = 2;   // key-form level 1 is scored by its own kernel
+  const int lo = topdown_lo(r);
   if (lo <= c.levels) {
     r.level = c.levels;
     r.dense = 1;
@@ -743,12 +750,14 @@ zha_status zha_debug_trace(zha_tree* t, int32_t level, int64_t cap, int32_t* nod
 }
 
 zha_status zha_debug_route_level(zha_tree* t, int32_t level, const void* q, const int32_t* nodes,
-                                 const uint32_t* masks, const int32_t* counts, int64_t cap, hipStream_t stream) {
+                                 const uint32_t* masks, const int32_t* counts, int64_t cap, int32_t path,
+                                 hipStream_t stream) {
   if (!t) return fail(ZHA_E_INVALID, "tree is null");
   if (!t->built) return fail(ZHA_E_STATE, "no tree built");
   const zha_config& c = t->cfg;
   if (level < 1 || level > c.levels) return fail(ZHA_E_INVALID, "level %d outside 1..%d", level, c.levels);
   if (!q || !nodes || !masks || !counts) return fail(ZHA_E_INVALID, "null input");
+  if (path != 0 && path != 1) return fail(ZHA_E_INVALID, "path %d is neither 0 nor 1", path);
   const int64_t n = nodes_at(c, level, t->N);
   const int H = c.num_kv_heads;
   std::vector<int32_t> hc(H);
@@ -782,8 +791,25 @@ zha_status zha_debug_route_level(zha_tree* t, int32_t level, const void* q, cons
   if (e == hipSuccess)
     e = hipMemcpyAsync(t->dev.cnt + (int64_t)level * H, counts, H * 4, hipMemcpyDeviceToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "frontier copy");
-  zha_status zs = route_levels(t, r, level, stream, false);
-  if (zs != ZHA_OK) return zs;
+  if (path == 0 && level >= topdown_lo(r)) {
+    // the decode's kernels for this level: every node scored, the top-down selection
+    // started from the given per-head frontiers, the dense union list
+    r.level = level;
+    r.dense_lo = level;
+    r.nlevel = r.nl[level];
+    e = launch_route_td_seed(r, stream);
+    if (e != hipSuccess) return hip_fail(e, "frontier seed launch");
+    r.dense = 1;
+    e = launch_route_dense_score(r, c.head_dim, c.num_ref, stream);
+    if (e != hipSuccess) return hip_fail(e, "route dense score launch");
+    r.dense = 0;
+    r.tf = 1;
+    e = launch_route_topdown(r, stream);
+    if (e != hipSuccess) return hip_fail(e, "route top-down select launch");
+  } else {
+    zha_status zs = route_levels(t, r, level, stream, false);
+    if (zs != ZHA_OK) return zs;
+  }
   e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "route level");
   return ZHA_OK;

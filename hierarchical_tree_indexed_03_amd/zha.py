@@ -54,7 +54,7 @@ def _load() -> ctypes.CDLL:
         "zha_debug_level": (I32, [P, I32, P, P, P]),
         "zha_debug_router_planes": (I32, [P, I32, P, P, P]),
         "zha_debug_trace": (I32, [P, I32, I64, P, P, P, P, P, P]),
-        "zha_debug_route_level": (I32, [P, I32, P, P, P, P, I64, P]),
+        "zha_debug_route_level": (I32, [P, I32, P, P, P, P, I64, I32, P]),
         "zha_profile_start": (I32, [P, ctypes.c_char_p]),
         "zha_profile_stop": (I32, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
         "zha_set_top_p_levels": (I32, [P, ctypes.POINTER(ctypes.c_float)]),
@@ -165,9 +165,9 @@ def zha_debug_trace(t, level: int, cap: int, nodes, masks, scores, keep, counts,
                                 _p(counts), _s(stream)))
 
 
-def zha_debug_route_level(t, level: int, q, nodes, masks, counts, cap: int, stream=None):
+def zha_debug_route_level(t, level: int, q, nodes, masks, counts, cap: int, path: int = 0, stream=None):
     _check(_lib.zha_debug_route_level(t, int(level), _p(q), _p(nodes), _p(masks), _p(counts), int(cap),
-                                      _s(stream)))
+                                      int(path), _s(stream)))
 
 
 def zha_profile_start(t, key_prefix: str):
@@ -336,9 +336,10 @@ class Tree:
                             keep=keep[kv, :n].cpu() if level else None))
         return out
 
-    def route_level(self, level: int, q, frontiers):
+    def route_level(self, level: int, q, frontiers, path: int = 0):
         """Teacher-forced routing of one level.  ``frontiers[kv]`` = (node ids ascending,
-        head masks) as int tensors; returns the trace of that level."""
+        head masks) as int tensors; ``path`` as zha_debug_route_level; returns the trace of
+        that level."""
         c = self.cfg
         cap = max(1, self.nodes(level))
         dev = self.workspace.device
@@ -350,7 +351,7 @@ class Tree:
             nodes[kv, :n] = torch.as_tensor(nd, dtype=torch.int32).to(dev)
             masks[kv, :n] = torch.as_tensor(mk, dtype=torch.int64).to(torch.int32).to(dev)
             counts[kv] = n
-        zha_debug_route_level(self.handle, level, q, nodes, masks, counts, cap)
+        zha_debug_route_level(self.handle, level, q, nodes, masks, counts, cap, path)
         return self.trace(level)
 
     def close(self):

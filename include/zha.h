@@ -240,12 +240,20 @@ zha_status zha_debug_trace(zha_tree* t, int32_t level, int64_t cap, int32_t* nod
                            hipStream_t stream);
 
 /* Teacher-forced routing of one level: scores the caller's union frontier (nodes/masks/
- * counts in the zha_debug_trace layout, with cap entries per KV head, device) for the
- * queries q and applies the per-head top-p; results are read with zha_debug_trace at
- * the same level.  Synchronises `stream`. */
+ * counts in the zha_debug_trace layout, with cap entries per KV head, device; node ids
+ * ascending) for the queries q and applies the per-head top-p (blog, "Routing through the
+ * tree"); results are read with zha_debug_trace at the same level.
+ *   path 0: the kernels zha_decode runs at this level.  On the top levels it selects
+ *           top-down (every level with at most 33,792 nodes up to the root, except a
+ *           level 1 scored from the keys) every node of the level is scored and the trace
+ *           holds every node (masks = the given frontier); elsewhere as path 1.
+ *   path 1: the large-level kernels: the union list is scored, then the per-head
+ *           histogram, boundary, classification and resolution launches.
+ * Synchronises `stream`. */
 zha_status zha_debug_route_level(zha_tree* t, int32_t level, const void* q,
                                  const int32_t* nodes, const uint32_t* masks,
-                                 const int32_t* counts, int64_t cap, hipStream_t stream);
+                                 const int32_t* counts, int64_t cap, int32_t path,
+                                 hipStream_t stream);
 
 /* Launch timing for measurement.  zha_profile_start makes every later launch of this
  * handle whose key starts with `key_prefix` get a pair of HIP events on the launch's

@@ -2,11 +2,20 @@
 
 Tolerances (stated once here, used by every GPU test):
   * router scores: |gpu - oracle| <= 1e-4 absolute (fp32 planes and scores);
-  * routed sets: identical, except a node whose oracle cumulative probability before it
-    lies within 1e-5 of p (its fate flips under rounding of the masses), or whose score is
-    within the score tolerance (1e-4) of the boundary node's score (a near tie may swap
-    order); end to end, the descendants of such a node are excluded from later levels;
-  * outputs: max|o_gpu - o_ref| <= 1e-2 * max|o_ref| (bf16 inputs, fp32 accumulation).
+  * routed sets: at every level the GPU's kept set must be the oracle's top-p of the same
+    frontier under the oracle's scores.  Two departures are explained, nothing else:
+      - the mass band: a node whose oracle cumulative probability before it (in oracle rank
+        order) lies within 1e-5 of p may be kept or dropped (the rounding of the masses may
+        flip it); this is the only way the kept count may differ;
+      - a near-tie swap: an oracle-kept node the GPU dropped, paired one to one with a node
+        the GPU kept instead, whose oracle scores differ by at most the two nodes' score
+        tolerances and which the GPU's own scores rank ahead of the dropped one.
+    End to end the comparison walks the GPU's own frontiers (each the existing children of
+    the GPU's kept nodes one level up), so a legitimate departure never masks a later
+    level; the number of departures is reported per test and bounded by stated rates;
+  * outputs: max|o_gpu - o_ref| <= 1e-2 * max|o_ref| (bf16 inputs, fp32 accumulation),
+    against attention over the GPU's gathered set always, and against the oracle's own
+    decode whenever the GPU took the oracle's route (no departure at any level).
 
 Quantised router planes (bf16, MX FP4): the oracle routes over its planes with s
 quantised (oracle ``quantise_planes``) at the levels the router reads planes at.  The GPU
@@ -141,68 +150,249 @@ def gpu_scores(trace_level: dict, gi: int) -> dict:
     return dict(zip(nodes.tolist(), sc.tolist()))
 
 
-def exempt_nodes(rec: dict, p: float, diff: np.ndarray, tol=None) -> tuple[list, list]:
-    """Split mismatching nodes into (exempt, failing) per the tolerance rule above.  ``tol``:
-    per-frontier-node score tolerance (default SCORE_TOL); a near tie allows the sum of the
-    node's and the boundary node's tolerances."""
-    frontier = rec["frontier"]
-    pos = {int(n): i for i, n in enumerate(frontier)}
-    order = rec["order"]
+def gpu_scores_on(trace_level: dict, gi: int, nodes) -> np.ndarray:
+    """GPU scores of head gi for the given nodes (each must be in the trace's list)."""
+    tn = trace_level["nodes"].numpy().astype(np.int64)
+    nodes = np.asarray(nodes, dtype=np.int64)
+    pos = np.searchsorted(tn, nodes)
+    assert np.all(pos < len(tn)) and np.array_equal(tn[np.minimum(pos, len(tn) - 1)], nodes), "node not in trace"
+    return trace_level["scores"][gi].numpy().astype(np.float64)[pos]
+
+
+def _rank_order(frontier: np.ndarray, scores: np.ndarray) -> np.ndarray:
+    """Position of every frontier node in the top-p rank order (score descending, equal
+    scores by node id ascending)."""
+    order = np.lexsort((frontier, -np.asarray(scores, dtype=np.float64)))
     rank = np.empty(len(order), np.int64)
     rank[order] = np.arange(len(order))
-    cum_before = rec["cum_before"]                 # in rank order
-    k = rec["k"]
-    tol = np.full(len(frontier), SCORE_TOL) if tol is None else np.asarray(tol)
-    boundary_score = rec["scores"][order[k - 1]] if k > 0 else np.inf
-    boundary_tol = tol[order[k - 1]] if k > 0 else 0.0
-    ok, bad = [], []
-    for n in diff.tolist():
-        i = pos[n]
-        cb = cum_before[rank[i]]
-        if abs(cb - p) <= BAND or abs(rec["scores"][i] - boundary_score) <= tol[i] + boundary_tol:
-            ok.append(n)
+    return rank
+
+
+def check_selection(frontier, s_ref, s_gpu, kept_gpu, p: float, tol=None) -> dict:
+    """One query head's top-p decision at one level, on a given frontier.
+
+    ``s_ref``: the oracle's scores of the frontier nodes; ``s_gpu``: the GPU's; ``kept_gpu``:
+    the nodes the GPU kept.  The expected set is the oracle's top_p of (frontier, s_ref).
+    A difference is explained only by
+      * the mass band: a node whose oracle cumulative probability before it lies within
+        BAND of p (the rounding of the masses may flip it); this is the only way the kept
+        count may differ;
+      * a near-tie swap: an oracle-kept node the GPU dropped, paired one to one with a node
+        the GPU kept instead, whose oracle scores differ by at most the two nodes' score
+        tolerances and which the GPU's own scores rank ahead of it.
+    Anything else is returned in ``bad``.  ``tol``: per-frontier-node score tolerance
+    (default SCORE_TOL)."""
+    frontier = np.asarray(frontier, dtype=np.int64)
+    s_ref = np.asarray(s_ref, dtype=np.float64)
+    s_gpu = np.asarray(s_gpu, dtype=np.float64)
+    tol = np.full(len(frontier), SCORE_TOL) if tol is None else np.asarray(tol, dtype=np.float64)
+    rec = zo.top_p(frontier, s_ref, p)
+    out = dict(bad=[], band=[], swap=[], k=rec["k"])
+    pos = {int(n): i for i, n in enumerate(frontier.tolist())}
+    kept_gpu = [int(n) for n in np.asarray(kept_gpu).tolist()]
+    stray = [n for n in kept_gpu if n not in pos]
+    if stray:
+        out["bad"].append(("outside frontier", stray[:5]))
+        return out
+    if len(frontier) == 0:
+        return out
+    rank = _rank_order(frontier, s_ref)
+    grank = _rank_order(frontier, s_gpu)
+    cb = rec["cum_before"]
+    k_o = set(rec["kept"].tolist())
+    k_g = set(kept_gpu)
+    in_band = lambda n: abs(cb[rank[pos[n]]] - p) <= BAND
+    dropped = sorted((n for n in k_o - k_g), key=lambda n: rank[pos[n]])
+    added = sorted((n for n in k_g - k_o), key=lambda n: rank[pos[n]])
+    out["band"] = [n for n in dropped + added if in_band(n)]
+    dropped = [n for n in dropped if not in_band(n)]
+    added = [n for n in added if not in_band(n)]
+    used = set()
+    bnd = s_ref[rec["order"][rec["k"] - 1]] if rec["k"] > 0 else np.inf
+    for d in dropped:
+        i = pos[d]
+        mate = None
+        for a in added:
+            j = pos[a]
+            if a in used:
+                continue
+            if abs(s_ref[i] - s_ref[j]) <= tol[i] + tol[j] and grank[j] < grank[i]:
+                mate = a
+                break
+        if mate is None:
+            out["bad"].append(("dropped", d, float(cb[rank[i]]), float(s_ref[i] - bnd)))
         else:
-            bad.append((n, float(cb), float(rec["scores"][i] - boundary_score)))
-    return ok, bad
+            used.add(mate)
+            out["swap"].append((d, mate))
+    for a in added:
+        if a not in used:
+            j = pos[a]
+            out["bad"].append(("added", a, float(cb[rank[j]]), float(s_ref[j] - bnd)))
+    return out
 
 
-def compare_route(route: dict, trace: dict, gi: int, b: int, p, tol_fn=None) -> dict:
-    """End-to-end set comparison of one query head.  ``trace[level]`` is the GPU trace of
-    that level for the head's KV head (level 0 = kept blocks).  ``p``: one value, or one
-    per level (entry level-1).  ``tol_fn(level, frontier)`` gives per-node score tolerances
-    (default SCORE_TOL).  Returns a report dict; report["bad"] lists unexplained
-    mismatches."""
-    excluded = set()
-    bad, exempt, n_levels = [], [], len(route["levels"])
-    for rec in route["levels"]:
-        lv = rec["level"]
-        tl = trace[lv]
-        f_o = set(rec["frontier"].tolist()) - excluded
-        f_g = set(gpu_frontier(tl, gi).tolist()) - excluded
-        if f_o != f_g:
-            bad.append(("frontier", lv, sorted(f_o ^ f_g)[:10]))
-            break
-        k_o = set(rec["kept"].tolist()) - excluded
-        k_g = set(gpu_kept(tl, gi).tolist()) - excluded
-        diff = np.array(sorted(k_o ^ k_g), dtype=np.int64)
-        tol = None if tol_fn is None else tol_fn(lv, rec["frontier"])
-        ok, nb = exempt_nodes(rec, p if np.ndim(p) == 0 else p[lv - 1], diff, tol)
-        exempt += [(lv, n) for n in ok]
-        bad += [("kept", lv) + x for x in nb]
-        if lv == 1:
-            # the gathered blocks are level-1 nodes: an exempt one is excluded itself
-            excluded = excluded | set(ok)
-            break
-        nxt = set()
-        for n in excluded | set(ok):
-            nxt.update(range(n * b, n * b + b))
-        excluded = nxt
-    # gathered blocks (level 0 of the trace) = kept level-1 blocks
-    k_o = set(route["blocks"].tolist()) - excluded
-    k_g = set(gpu_frontier(trace[0], gi).tolist()) - excluded
-    if k_o != k_g:
-        bad.append(("blocks", 0, sorted(k_o ^ k_g)[:10]))
-    return dict(bad=bad, exempt=exempt)
+def new_report() -> dict:
+    return dict(bad=[], band=0, swap=0, selections=0, same=True)
+
+
+def compare_route(tree, q, trace: dict, gi: int, p, tol_fn=None) -> dict:
+    """End-to-end check of one query head's routing, walking the GPU's own frontiers.
+
+    ``tree``: the oracle tree the router reads (for quantised router planes, the oracle's
+    quantised copy); ``trace[level]``: the GPU trace of the head's KV head (level 0 = the
+    gathered blocks).  At every level from the top:
+      * the GPU frontier must be every node (top level) or exactly the existing children
+        of the nodes the GPU kept one level up;
+      * the GPU score of every frontier node must be within the score tolerance of the
+        oracle's score of that node (``tol_fn(level, frontier)``, default SCORE_TOL);
+      * the GPU kept set must be the oracle's top-p of that frontier under the oracle's
+        scores (check_selection: the mass band and verified near-tie swaps only).
+    The gathered blocks must be the kept level-1 nodes.  ``same`` is True when no exemption
+    was used, i.e. the GPU took the oracle's own route, whose output the caller may then
+    compare with the oracle's.  ``p``: one value, or one per level (entry level-1)."""
+    rep = new_report()
+    L = tree.n_levels
+    prev = None
+    for lv in range(L, 0, -1):
+        fr = gpu_frontier(trace[lv], gi)
+        want = np.arange(tree.nodes(lv), dtype=np.int64) if prev is None else zo.children(tree, lv + 1, prev)
+        if not np.array_equal(fr, np.sort(want)):
+            rep["bad"].append(("frontier", lv, sorted(set(fr.tolist()) ^ set(want.tolist()))[:10]))
+            return rep
+        s_ref = zo.node_scores(tree, lv, fr, q)
+        s_gpu = gpu_scores_on(trace[lv], gi, fr)
+        tol = np.full(len(fr), SCORE_TOL) if tol_fn is None else np.asarray(tol_fn(lv, fr), dtype=np.float64)
+        over = np.abs(s_gpu - s_ref) - tol
+        if len(fr) and np.max(over) > 0:
+            i = int(np.argmax(over))
+            rep["bad"].append(("score", lv, int(fr[i]), float(s_gpu[i]), float(s_ref[i])))
+            return rep
+        sel = check_selection(fr, s_ref, s_gpu, gpu_kept(trace[lv], gi), zo.level_p(p, lv), tol)
+        rep["selections"] += 1
+        rep["band"] += len(sel["band"])
+        rep["swap"] += len(sel["swap"])
+        if sel["bad"]:
+            rep["bad"] += [("kept", lv) + tuple(x) for x in sel["bad"]]
+            return rep
+        prev = gpu_kept(trace[lv], gi)
+    blocks = gpu_frontier(trace[0], gi)
+    if not np.array_equal(blocks, prev):
+        rep["bad"].append(("blocks", sorted(set(blocks.tolist()) ^ set(prev.tolist()))[:10]))
+    rep["same"] = rep["band"] == 0 and rep["swap"] == 0
+    return rep
+
+
+def union_frontiers(routes: list, li: int, hkv: int, g: int) -> list:
+    """The group unions of the oracle routes' frontiers at entry li of route["levels"]:
+    per KV head (node ids ascending, head masks)."""
+    fronts = []
+    for kv in range(hkv):
+        fr = {}
+        for gi in range(g):
+            for n in routes[kv * g + gi]["levels"][li]["frontier"].tolist():
+                fr[n] = fr.get(n, 0) | (1 << gi)
+        nodes = np.array(sorted(fr), dtype=np.int64)
+        fronts.append((nodes, np.array([fr[n] for n in nodes.tolist()], dtype=np.int64)))
+    return fronts
+
+
+def teacher_forced(t, trees: list, q: np.ndarray, qd, p, keep_sink: bool, path: int = 0,
+                   tol_fn=None) -> dict:
+    """Teacher-forced routing through the C ABI: at every level the GPU routes the oracle's
+    own frontier (zha_debug_route_level; path 0 = the kernels zha_decode runs at that level,
+    1 = the list path), and its scores and kept sets are checked with check_selection.
+    ``trees``: the router's oracle trees per KV head; ``tol_fn(kv, q_head)`` returns a
+    per-level tolerance function as compare_route takes.  Returns a report (bad, band,
+    swap, selections, max score error)."""
+    hkv = len(trees)
+    hq = q.shape[0]
+    g = hq // hkv
+    L = trees[0].n_levels
+    routes = [zo.route(trees[h // g], q[h], p, keep_sink) for h in range(hq)]
+    rep = new_report()
+    rep["max_err"] = 0.0
+    for li in range(L):
+        lv = L - li
+        tr = t.route_level(lv, qd, union_frontiers(routes, li, hkv, g), path)
+        for h in range(hq):
+            kv, gi = divmod(h, g)
+            rec = routes[h]["levels"][li]
+            fr = rec["frontier"]
+            s_gpu = gpu_scores_on(tr[kv], gi, fr)
+            tol = (np.full(len(fr), SCORE_TOL) if tol_fn is None
+                   else np.asarray(tol_fn(kv, q[h])(lv, fr), dtype=np.float64))
+            err = np.abs(s_gpu - rec["scores"])
+            rep["max_err"] = max(rep["max_err"], float(np.max(err)) if len(fr) else 0.0)
+            if len(fr) and np.any(err > tol):
+                i = int(np.argmax(err - tol))
+                rep["bad"].append(("score", lv, h, int(fr[i]), float(s_gpu[i]), float(rec["scores"][i])))
+                continue
+            sel = check_selection(fr, rec["scores"], s_gpu, gpu_kept(tr[kv], gi), zo.level_p(p, lv), tol)
+            rep["selections"] += 1
+            rep["band"] += len(sel["band"])
+            rep["swap"] += len(sel["swap"])
+            rep["bad"] += [("kept", lv, h) + tuple(x) for x in sel["bad"]]
+    return rep
+
+
+# Exemptions expected at most: the masses are fixed-point on the GPU (about 1e-7 relative to
+# the oracle's), so a mass-band flip needs a boundary within ~1e-7 of p although the band is
+# 1e-5 wide; a swap needs two boundary-adjacent scores closer than the fp32 score error
+# (about 1e-6).  Both are rare on these inputs: over the whole GPU suite (about 15,000 level
+# selections) one band flip and no swap, apart from inputs built to sit exactly on p.
+MAX_BAND_RATE = 0.02
+MAX_SWAP_RATE = 0.02
+
+
+def merge_reports(reps) -> dict:
+    tot = new_report()
+    for r in reps:
+        tot["bad"] += r["bad"]
+        for k in ("band", "swap", "selections"):
+            tot[k] += r[k]
+        tot["same"] = tot["same"] and r.get("same", True)
+    return tot
+
+
+def assert_exemption_rates(label: str, reps, band_rate: float = MAX_BAND_RATE) -> dict:
+    """Prints the exemption counts of a test's level selections and fails when they exceed
+    the stated rates (band_rate, MAX_SWAP_RATE of the selections, at least 2 each).  Inputs
+    built to put the boundary exactly on p (equal masses) pass a band_rate of 1."""
+    tot = merge_reports(reps) if isinstance(reps, (list, tuple)) else reps
+    sel = tot["selections"]
+    print(f"[exemptions] {label}: {sel} level selections, {tot['band']} mass-band, {tot['swap']} near-tie swaps")
+    assert tot["band"] <= max(2, band_rate * sel), f"{label}: {tot['band']} mass-band exemptions in {sel}"
+    assert tot["swap"] <= max(2, MAX_SWAP_RATE * sel), f"{label}: {tot['swap']} near-tie swaps in {sel}"
+    return tot
+
+
+def check_decode(trees: list, K, V, q: np.ndarray, o: np.ndarray, traces: dict, p, keep_sink: bool, n: int,
+                 tol_fn=None, label: str = "") -> list:
+    """One decode step of every query head against the oracle: compare_route on the GPU's
+    trace (``traces[level][kv]``), attention over the GPU's gathered tokens, and the
+    oracle's own decode output whenever the GPU took the oracle's route.  ``trees``: the
+    router's oracle trees per KV head (their keys are the caches); ``K``, ``V``: host caches
+    [Hkv, >= n, d]; ``tol_fn(kv, q_head)`` -> per-level tolerance as compare_route takes.
+    Returns the per-head reports."""
+    hkv = len(trees)
+    hq = q.shape[0]
+    g = hq // hkv
+    b = trees[0].block
+    o_ref = zo.decode(trees, V, q, p, keep_sink)
+    reps = []
+    for h in range(hq):
+        kv, gi = divmod(h, g)
+        tr = {lv: traces[lv][kv] for lv in traces}
+        rep = compare_route(trees[kv], q[h], tr, gi, p, None if tol_fn is None else tol_fn(kv, q[h]))
+        assert not rep["bad"], f"{label} head {h}: {rep['bad'][:5]}"
+        toks = gpu_tokens(tr[0], gi, b, n, keep_sink)
+        e1 = out_err(o[h], zo.attend(K[kv][:n], V[kv][:n], q[h], toks))
+        assert e1 <= OUT_RTOL, f"{label} head {h}: attention over the GPU's set, error {e1:.3e}"
+        if rep["same"]:
+            e2 = out_err(o[h], o_ref[h])
+            assert e2 <= OUT_RTOL, f"{label} head {h}: output error {e2:.3e} against the oracle's decode"
+        reps.append(rep)
+    return reps
 
 
 def gpu_tokens(trace0: dict, gi: int, b: int, n_tokens: int, keep_sink=True) -> np.ndarray:

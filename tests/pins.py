@@ -212,6 +212,22 @@ def check_dense_limit(seed=8):
     return err < 1e-12, f"max |ZHA(p=1) - SDPA| = {err:.3e}"
 
 
+# Dense decode (the crossover baseline): every query head against torch SDPA over all n
+# tokens of its KV head, under the contiguous GQA mapping (query head h reads KV head
+# h // (Hq / Hkv)).  The caches hold rows past n that must not be attended.
+def check_dense_decode(seed=20):
+    rng = np.random.default_rng(seed)
+    hkv, hq, d, n, cap = 2, 6, 16, 131, 140
+    keys = rng.standard_normal((hkv, cap, d))
+    vals = rng.standard_normal((hkv, cap, d))
+    q = rng.standard_normal((hq, d)) * 3
+    o = zo.dense_decode(keys, vals, q, n)
+    g = hq // hkv
+    ref = np.stack([_sdpa(keys[h // g][:n], vals[h // g][:n], q[h]) for h in range(hq)])
+    err = np.max(np.abs(o - ref))
+    return err < 1e-12, f"max |dense_decode - SDPA per head| = {err:.3e}"
+
+
 # P11: attention over a given set equals masked dense attention.
 def check_masked_attention(seed=9):
     rng = np.random.default_rng(seed)
@@ -494,7 +510,7 @@ def check_fit_single_key(seed=19):
     return loss4 > 1e-6, f"b=4 loss {loss4:.4f} (> 0)"
 
 
-ALL = [check_dense_limit, check_convexity, check_exact_at_refs, check_recursion_direct,
+ALL = [check_dense_limit, check_dense_decode, check_convexity, check_exact_at_refs, check_recursion_direct,
        check_single_key, check_nucleus, check_minimal, check_mass_conservation, check_append,
        check_masked_attention, check_sink, check_bf16_round_library, check_bf16_round_nearest,
        check_quantised_planes, check_p_schedule, check_mxfp4_round, check_fp4_planes,

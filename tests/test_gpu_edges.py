@@ -5,8 +5,9 @@
   rank rule alone (equal scores ranked by node id).  Checked level by level on the GPU's
   own frontier (a boundary decision within 1e-5 of p changes the next frontier's size and
   with it every later boundary): the kept set must be exactly the oracle's top-p of that
-  frontier, except a node whose cumulative probability before it lies within 1e-5 of p,
-  and the attention must match over the GPU's gathered set.  One geometry sends
+  frontier, except a node whose cumulative probability before it lies within 1e-5 of p
+  (no near-tie swap can apply: equal scores rank by node id on both sides), and the
+  attention must match over the GPU's gathered set.  One geometry sends
   level 1 through the large-level path (more than 33,792 nodes) and the levels above
   through the top-down path; both hit their many-candidates and many-ties branches.
 * Degenerate sizes: one token (only the sink), fewer tokens than a block, exactly b^L
@@ -26,49 +27,14 @@ from workloads import configs as wc, gen
 pytestmark = pytest.mark.gpu
 
 
-def chain_compare(tree, q, trace, gi, p):
-    """Teacher-forced chain for one query head: at every level the GPU frontier is the
-    children of the GPU's kept nodes one level up, the GPU scores of that frontier match
-    the oracle's, and the GPU kept set is exactly the oracle's top-p of that frontier
-    (nodes whose cumulative probability before them is within 1e-5 of p excepted)."""
-    bad = []
-    L, b = tree.n_levels, tree.block
-    prev = None
-    for lv in range(L, 0, -1):
-        fr = P.gpu_frontier(trace[lv], gi)
-        want = np.arange(tree.nodes(L)) if prev is None else zo.children(tree, lv + 1, prev)
-        if not np.array_equal(fr, np.sort(want)):
-            return [("frontier", lv, len(fr), len(want))]
-        sc_o = zo.node_scores(tree, lv, fr, q)
-        sc_map = P.gpu_scores(trace[lv], gi)
-        sc_g = np.array([sc_map[int(n)] for n in fr], dtype=np.float64)
-        if len(fr) and np.max(np.abs(sc_g - sc_o)) > P.SCORE_TOL:
-            return [("scores", lv, float(np.max(np.abs(sc_g - sc_o))))]
-        sel = zo.top_p(fr, sc_g, p)
-        kept = P.gpu_kept(trace[lv], gi)
-        order = sel["order"]
-        rank = np.empty(len(order), np.int64)
-        rank[order] = np.arange(len(order))
-        pos = {int(n): i for i, n in enumerate(fr)}
-        for n in sorted(set(kept.tolist()) ^ set(sel["kept"].tolist())):
-            cb = sel["cum_before"][rank[pos[n]]]
-            if abs(cb - p) > P.BAND:
-                bad.append(("kept", lv, n, float(cb)))
-        if bad:
-            return bad
-        prev = kept
-    if set(P.gpu_frontier(trace[0], gi).tolist()) != set(prev.tolist()):
-        bad.append(("blocks",))
-    return bad
-
-
-def run_case(w, K, V, refs, n0, steps, p=None, strict=False, capacity=None):
+def run_case(w, K, V, refs, n0, steps, p=None, capacity=None):
     p = w.top_p if p is None else p
     t = P.make_tree(w, top_p=p, capacity=capacity)
     Kd, Vd = P.upload(K, w), P.upload(V, w)
     t.build(Kd, Vd, n0, P.upload(refs, w))
     trees = [zo.build_tree(K[h], refs[h], w.block, w.levels, n0) for h in range(w.num_kv_heads)]
     n = n0
+    reps = []
     for step in range(steps + 1):
         if step > 0:
             t.append(Kd[:, n].contiguous(), Vd[:, n].contiguous())
@@ -78,25 +44,9 @@ def run_case(w, K, V, refs, n0, steps, p=None, strict=False, capacity=None):
         q = gen.step_queries(w, step, n, gen.host_fetch(K))
         o = t.decode(P.upload(q, w)).cpu().numpy()
         traces = {lv: t.trace(lv) for lv in range(0, w.levels + 1)}
-        o_ref, routes = zo.decode(trees, V, q, p, w.keep_sink, return_routes=True)
-        for h in range(w.num_q_heads):
-            kv, gi = divmod(h, w.group)
-            tr = {lv: traces[lv][kv] for lv in traces}
-            if strict:
-                bad = chain_compare(trees[kv], q[h], tr, gi, p)
-                assert not bad, f"N={n} head {h}: {bad[:4]}"
-                exempt = True   # the sets follow the GPU's own boundary decisions
-            else:
-                rep = P.compare_route(routes[h], tr, gi, w.block, p)
-                assert not rep["bad"], f"N={n} head {h}: {rep['bad'][:4]}"
-                exempt = bool(rep["exempt"])
-            toks = P.gpu_tokens(tr[0], gi, w.block, n, w.keep_sink)
-            e1 = P.out_err(o[h], zo.attend(K[kv][:n], V[kv][:n], q[h], toks))
-            assert e1 <= P.OUT_RTOL, f"N={n} head {h}: attention over the GPU set err {e1:.3e}"
-            if not exempt:
-                e2 = P.out_err(o[h], o_ref[h])
-                assert e2 <= P.OUT_RTOL, f"N={n} head {h}: output err {e2:.3e}"
+        reps += P.check_decode(trees, K, V, q, o, traces, p, w.keep_sink, n, label=f"N={n}")
     t.close()
+    return P.merge_reports(reps)
 
 
 def tied_inputs(w):
@@ -114,7 +64,13 @@ def test_exact_ties(geom):
         # key-form level 1 (4,097 nodes) and top-down levels 2..6
         w = wc.DEEP.with_(n_tokens=16_384 + 5, steps=1, num_kv_heads=1, num_q_heads=8)
     K, V, refs = tied_inputs(w)
-    run_case(w, K, V, refs, w.n_tokens, w.steps, strict=True)
+    rep = run_case(w, K, V, refs, w.n_tokens, w.steps)
+    # equal scores are ranked by node id on both sides: no swap can explain a difference.
+    # Equal masses put the cumulative probability exactly on p wherever p times the
+    # frontier size is a whole number (p = 0.75 and frontiers of 8k children), where the
+    # fp64 sum and the integer masses may round either way: the band is expected there.
+    assert rep["swap"] == 0
+    P.assert_exemption_rates(f"exact ties {geom}", rep, band_rate=1.0)
 
 
 @pytest.mark.parametrize("n0", [1, 3, 4, 63, 64, 65])

@@ -38,34 +38,15 @@ def setup(name):
     return w, sched, K, V, trees, t, Kd, Vd
 
 
+@pytest.mark.parametrize("path", [0, 1], ids=["decode_path", "list_path"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_teacher_forced_sets(name):
+def test_teacher_forced_sets(name, path):
     w, sched, K, V, trees, t, _, _ = setup(name)
-    g = w.group
     q = gen.step_queries(w, 100, w.n_tokens, gen.host_fetch(K))
-    routes = [zo.route(trees[h // g], q[h], sched, w.keep_sink) for h in range(w.num_q_heads)]
-    qd = P.upload(q, w)
-    for li in range(w.levels):
-        lv = w.levels - li
-        fronts = []
-        for kv in range(w.num_kv_heads):
-            fr = {}
-            for gi in range(g):
-                for n in routes[kv * g + gi]["levels"][li]["frontier"].tolist():
-                    fr[n] = fr.get(n, 0) | (1 << gi)
-            nodes = np.array(sorted(fr), dtype=np.int64)
-            fronts.append((nodes, np.array([fr[n] for n in nodes.tolist()], dtype=np.int64)))
-        tr = t.route_level(lv, qd, fronts)
-        for h in range(w.num_q_heads):
-            kv, gi = divmod(h, g)
-            rec = routes[h]["levels"][li]
-            gs = P.gpu_scores(tr[kv], gi)
-            sg = np.array([gs[n] for n in rec["frontier"].tolist()])
-            assert np.max(np.abs(sg - rec["scores"])) <= P.SCORE_TOL
-            kept = P.gpu_kept(tr[kv], gi)
-            diff = np.array(sorted(set(kept.tolist()) ^ set(rec["kept"].tolist())), dtype=np.int64)
-            _, bad = P.exempt_nodes(rec, sched[lv - 1], diff)
-            assert not bad, f"level {lv} head {h}: unexplained set mismatch {bad[:5]}"
+    rep = P.teacher_forced(t, trees, q, P.upload(q, w), sched, w.keep_sink, path)
+    assert not rep["bad"], f"{rep['bad'][:5]}"
+    assert rep["max_err"] <= P.SCORE_TOL
+    P.assert_exemption_rates(f"{name} teacher-forced path {path}", rep)
     t.close()
 
 
@@ -73,8 +54,8 @@ def test_teacher_forced_sets(name):
 @pytest.mark.parametrize("varying", [False, True])
 def test_decode_end_to_end(name, varying):
     w, sched, K, V, trees, t, Kd, Vd = setup(name)
-    g = w.group
     n = w.n_tokens
+    reps = []
     for step in range(w.steps):
         if w.appends:
             t.append(Kd[:, n].contiguous(), Vd[:, n].contiguous())
@@ -89,28 +70,14 @@ def test_decode_end_to_end(name, varying):
         torch.cuda.synchronize()
         o = o.cpu().numpy()
         traces = {lv: t.trace(lv) for lv in range(0, w.levels + 1)}
-        o_ref, routes = zo.decode(trees, V, q, s, w.keep_sink, return_routes=True)
-        for h in range(w.num_q_heads):
-            kv, gi = divmod(h, g)
-            tr = {lv: traces[lv][kv] for lv in traces}
-            rep = P.compare_route(routes[h], tr, gi, w.block, s)
-            assert not rep["bad"], f"step {step} head {h}: {rep['bad'][:5]}"
-            toks = P.gpu_tokens(tr[0], gi, w.block, n, w.keep_sink)
-            e1 = P.out_err(o[h], zo.attend(K[kv][:n], V[kv][:n], q[h], toks))
-            assert e1 <= P.OUT_RTOL, f"step {step} head {h}: attention over the GPU set err {e1:.3e}"
-            if not rep["exempt"]:
-                e2 = P.out_err(o[h], o_ref[h])
-                assert e2 <= P.OUT_RTOL, f"step {step} head {h}: output err {e2:.3e}"
+        reps += P.check_decode(trees, K, V, q, o, traces, s, w.keep_sink, n, label=f"step {step}")
     # restoring the config's p: the next decode routes with it again
     t.set_top_p_levels(None)
     q = gen.step_queries(w, 50, n, gen.host_fetch(K))
-    t.decode(P.upload(q, w))
+    o = t.decode(P.upload(q, w))
     torch.cuda.synchronize()
+    o = o.cpu().numpy()
     traces = {lv: t.trace(lv) for lv in range(0, w.levels + 1)}
-    _, routes = zo.decode(trees, V, q, w.top_p, w.keep_sink, return_routes=True)
-    for h in range(w.num_q_heads):
-        kv, gi = divmod(h, g)
-        rep = P.compare_route(routes[h], {lv: traces[lv][kv] for lv in traces}, gi, w.block, w.top_p)
-        assert not rep["bad"], f"restored p, head {h}: {rep['bad'][:5]}"
+    reps += P.check_decode(trees, K, V, q, o, traces, w.top_p, w.keep_sink, n, label="restored p")
+    P.assert_exemption_rates(f"{name} end to end", reps)
     t.close()
-

@@ -83,62 +83,33 @@ def test_planes_match_oracle(name):
             assert es < 1e-4 and ec < 1e-3, f"level {lv} head {h}: s err {es:.2e}, c err {ec:.2e}"
 
 
+@pytest.mark.parametrize("path", [0, 1], ids=["decode_path", "list_path"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_teacher_forced_scores_and_sets(name):
+def test_teacher_forced_scores_and_sets(name, path):
+    """Every level routed from the oracle's own frontier: path 0 runs the kernels the
+    decode runs at that level (dense scoring and top-down selection on the top levels),
+    path 1 the large-level kernels."""
     c = case(name)
     w = c.w
     q = c.queries(100)
-    g = w.group
-    routes = [zo.route(c.trees[h // g], q[h], c.p, w.keep_sink) for h in range(w.num_q_heads)]
-    qd = P.upload(q, w)
-    worst = 0.0
-    for li in range(w.levels):
-        lv = w.levels - li
-        fronts = []
-        for kv in range(w.num_kv_heads):
-            fr = {}
-            for gi in range(g):
-                for n in routes[kv * g + gi]["levels"][li]["frontier"].tolist():
-                    fr[n] = fr.get(n, 0) | (1 << gi)
-            nodes = np.array(sorted(fr), dtype=np.int64)
-            fronts.append((nodes, np.array([fr[n] for n in nodes.tolist()], dtype=np.int64)))
-        tr = c.t.route_level(lv, qd, fronts)
-        for h in range(w.num_q_heads):
-            kv, gi = divmod(h, g)
-            rec = routes[h]["levels"][li]
-            gs = P.gpu_scores(tr[kv], gi)
-            sg = np.array([gs[n] for n in rec["frontier"].tolist()])
-            worst = max(worst, float(np.max(np.abs(sg - rec["scores"]))))
-            kept = P.gpu_kept(tr[kv], gi)
-            diff = np.array(sorted(set(kept.tolist()) ^ set(rec["kept"].tolist())), dtype=np.int64)
-            _, bad = P.exempt_nodes(rec, c.p, diff)
-            assert not bad, f"level {lv} head {h}: unexplained set mismatch {bad[:5]}"
-    assert worst <= P.SCORE_TOL, f"max score error {worst:.3e}"
+    rep = P.teacher_forced(c.t, c.trees, q, P.upload(q, w), c.p, w.keep_sink, path)
+    assert not rep["bad"], f"{rep['bad'][:5]}"
+    assert rep["max_err"] <= P.SCORE_TOL, f"max score error {rep['max_err']:.3e}"
+    P.assert_exemption_rates(f"{name} teacher-forced path {path}", rep)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_decode_end_to_end(name):
     c = case(name)
     w = c.w
-    g = w.group
+    reps = []
     for step in range(w.steps if w.steps else 1):
         if w.appends:
             c.append()
         q = c.queries(step)
         o, traces = c.decode(q)
-        o_ref, routes = zo.decode(c.trees, c.V, q, c.p, w.keep_sink, return_routes=True)
-        for h in range(w.num_q_heads):
-            kv, gi = divmod(h, g)
-            tr = {lv: traces[lv][kv] for lv in traces}
-            rep = P.compare_route(routes[h], tr, gi, w.block, c.p)
-            assert not rep["bad"], f"step {step} head {h}: {rep['bad'][:5]}"
-            toks = P.gpu_tokens(tr[0], gi, w.block, c.n, w.keep_sink)
-            o_given = zo.attend(c.K[kv][:c.n], c.V[kv][:c.n], q[h], toks)
-            e1 = P.out_err(o[h], o_given)
-            assert e1 <= P.OUT_RTOL, f"step {step} head {h}: attention over GPU set err {e1:.3e}"
-            if not rep["exempt"]:
-                e2 = P.out_err(o[h], o_ref[h])
-                assert e2 <= P.OUT_RTOL, f"step {step} head {h}: output err {e2:.3e}"
+        reps += P.check_decode(c.trees, c.K, c.V, q, o, traces, c.p, w.keep_sink, c.n, label=f"step {step}")
+    P.assert_exemption_rates(f"{name} end to end", reps)
 
 
 @pytest.mark.parametrize("name", ["tiny", "deep_small", "wide_small"])

@@ -112,46 +112,23 @@ def test_router_planes_quantiser(name):
     check_quantiser(case(name))
 
 
+@pytest.mark.parametrize("path", [0, 1], ids=["decode_path", "list_path"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_teacher_forced_scores_and_sets(name):
+def test_teacher_forced_scores_and_sets(name, path):
     c = case(name)
     w = c.w
-    g = w.group
     q = c.queries(100)
-    rt = P.router_trees(w, c.trees)
-    routes = [zo.route(rt[h // g], q[h], c.p, w.keep_sink) for h in range(w.num_q_heads)]
-    qd = P.upload(q, w)
-    for li in range(w.levels):
-        lv = w.levels - li
-        fronts = []
-        for kv in range(w.num_kv_heads):
-            fr = {}
-            for gi in range(g):
-                for n in routes[kv * g + gi]["levels"][li]["frontier"].tolist():
-                    fr[n] = fr.get(n, 0) | (1 << gi)
-            nodes = np.array(sorted(fr), dtype=np.int64)
-            fronts.append((nodes, np.array([fr[n] for n in nodes.tolist()], dtype=np.int64)))
-        tr = c.t.route_level(lv, qd, fronts)
-        for h in range(w.num_q_heads):
-            kv, gi = divmod(h, g)
-            rec = routes[h]["levels"][li]
-            gs = P.gpu_scores(tr[kv], gi)
-            sg = np.array([gs[n] for n in rec["frontier"].tolist()])
-            tol = c.tol_fn(kv, q[h])(lv, rec["frontier"])
-            over = np.abs(sg - rec["scores"]) - tol
-            assert np.all(over <= 0), (f"level {lv} head {h}: score error beyond tolerance by "
-                                       f"{float(np.max(over)):.3e}")
-            kept = P.gpu_kept(tr[kv], gi)
-            diff = np.array(sorted(set(kept.tolist()) ^ set(rec["kept"].tolist())), dtype=np.int64)
-            _, bad = P.exempt_nodes(rec, c.p, diff, tol)
-            assert not bad, f"level {lv} head {h}: unexplained set mismatch {bad[:5]}"
+    rep = P.teacher_forced(c.t, P.router_trees(w, c.trees), q, P.upload(q, w), c.p, w.keep_sink, path,
+                           tol_fn=c.tol_fn)
+    assert not rep["bad"], f"{rep['bad'][:5]}"
+    P.assert_exemption_rates(f"{name} teacher-forced path {path}", rep)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_decode_end_to_end(name):
     c = case(name)
     w = c.w
-    g = w.group
+    reps = []
     for step in range(max(1, w.steps)):
         if w.appends and w.steps:
             c.append()
@@ -160,17 +137,8 @@ def test_decode_end_to_end(name):
         torch.cuda.synchronize()
         o = o.cpu().numpy()
         traces = {lv: c.t.trace(lv) for lv in range(0, w.levels + 1)}
-        o_ref, routes = zo.decode(P.router_trees(w, c.trees), c.V, q, c.p, w.keep_sink, return_routes=True)
-        for h in range(w.num_q_heads):
-            kv, gi = divmod(h, g)
-            tr = {lv: traces[lv][kv] for lv in traces}
-            rep = P.compare_route(routes[h], tr, gi, w.block, c.p, c.tol_fn(kv, q[h]))
-            assert not rep["bad"], f"step {step} head {h}: {rep['bad'][:5]}"
-            toks = P.gpu_tokens(tr[0], gi, w.block, c.n, w.keep_sink)
-            e1 = P.out_err(o[h], zo.attend(c.K[kv][:c.n], c.V[kv][:c.n], q[h], toks))
-            assert e1 <= P.OUT_RTOL, f"step {step} head {h}: attention over the GPU set err {e1:.3e}"
-            if not rep["exempt"]:
-                e2 = P.out_err(o[h], o_ref[h])
-                assert e2 <= P.OUT_RTOL, f"step {step} head {h}: output err {e2:.3e}"
+        reps += P.check_decode(P.router_trees(w, c.trees), c.K, c.V, q, o, traces, c.p, w.keep_sink, c.n,
+                               tol_fn=c.tol_fn, label=f"step {step}")
+    P.assert_exemption_rates(f"{name} end to end", reps)
     # the appended rows' bf16 copies follow the refreshed planes
     check_quantiser(c)

@@ -242,6 +242,21 @@ def _mut_router_first_plane(orig):
     return f
 
 
+def _mut_dense_gqa_modulo(orig):
+    def f(keys, values, q, n_tokens):
+        hq = q.shape[0]
+        hkv = keys.shape[0]
+        tok = np.arange(n_tokens)
+        return np.stack([zo.attend(keys[h % hkv], values[h % hkv], q[h], tok) for h in range(hq)])
+    return f
+
+
+def _mut_dense_all_rows(orig):
+    def f(keys, values, q, n_tokens):
+        return orig(keys, values, q, keys.shape[1])
+    return f
+
+
 MUTATIONS = [
     ("level1_planes", _mut_level1_offset),
     ("parent_planes", _mut_parent_unweighted),
@@ -262,6 +277,8 @@ MUTATIONS = [
     ("fit_loss", _mut_fit_loss_reversed),
     ("node_log_mass", _mut_node_mass_unnormalised),
     ("router_log_probs", _mut_router_first_plane),
+    ("dense_decode", _mut_dense_gqa_modulo),
+    ("dense_decode", _mut_dense_all_rows),
 ]
 
 
