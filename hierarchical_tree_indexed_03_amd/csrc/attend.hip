@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
         O += Ol[w][h][d] * sc;
       }
     }
-    float* pp = a.dev.apart + ((int64_t)(kv * g + h) * MAX_SPLITS + split) * (D + 2);
+    float* pp = a.dev.apart + ((int64_t)(kv * g + h) * a.pstride + split) * (D + 2);
     if (d == 0) { pp[0] = M; pp[1] = L; }
     pp[2 + d] = O;
   }
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
         O += Ol[(w * GMAX + h) * D + d] * sw;
       }
     }
-    float* pp = a.dev.apart + ((int64_t)(kv * g + h) * MAX_SPLITS + split) * (D + 2);
+    float* pp = a.dev.apart + ((int64_t)(kv * g + h) * a.pstride + split) * (D + 2);
     if (d == 0) { pp[0] = M; pp[1] = L; }
     pp[2 + d] = O;
   }
@@ -480,7 +480,7 @@ __global__ __launch_bounds__(512) void combine_kernel(AttnArgs a, int32_t* stats
   __shared__ float S0;
   const int hq = blockIdx.x, kv = hq / a.g, gi = hq % a.g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float* base = a.dev.apart + (int64_t)hq * MAX_SPLITS * (D + 2);
+  const float* base = a.dev.apart + (int64_t)hq * a.pstride * (D + 2);
   // splits that own tokens (same chunking as the attention kernel)
   int S = 0;
   if constexpr (DENSE) {

@@ -79,6 +79,7 @@ struct AttnArgs {
   int64_t N;
   int32_t hkv, hq, g, b;
   int32_t splits;     // splits per KV head (grid.x)
+  int32_t pstride;    // partials per query head in dev.apart ([Hq][pstride][D + 2]), >= splits
   int32_t keep_sink;
   float sigma;
   float* out;         // [Hq][D]

@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -612,6 +613,7 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
   // one wave of resident workgroups; splits beyond the gathered tokens exit at once
   a.splits = attend_resident_splits(c.dtype == ZHA_BF16, c.head_dim, false, c.num_kv_heads);
   a.keep_sink = c.keep_sink;
+  a.pstride = MAX_SPLITS;
   a.sigma = 1.0f / sqrtf((float)c.head_dim);
   a.out = out;
   {
@@ -666,6 +668,7 @@ zha_status zha_decode_dense(zha_tree* t, const void* q, float* out, hipStream_t 
   a.b = c.block;
   a.splits = attn_splits(t->N, 1024, attend_resident_splits(c.dtype == ZHA_BF16, c.head_dim, true, c.num_kv_heads));
   a.keep_sink = 0;
+  a.pstride = MAX_SPLITS;
   a.sigma = 1.0f / sqrtf((float)c.head_dim);
   a.out = out;
   hipError_t e;
@@ -673,6 +676,88 @@ zha_status zha_decode_dense(zha_tree* t, const void* q, float* out, hipStream_t 
     ProfScope ps(t, "dense_attend", stream);
     e = launch_attend(a, c.dtype == ZHA_BF16, c.head_dim, true, stream);
   }
+  if (e != hipSuccess) return hip_fail(e, "dense attention launch");
+  return ZHA_OK;
+}
+
+}  // extern "C"
+
+// Scratch of the allocation-free dense decode: the split-K attention partials
+// [Hq][splits][D + 2] in a fixed array, one copy per GPU, held until the process ends.  Host
+// code never passes the array's name to a kernel: it takes the device address from
+// hipGetSymbolAddress once per device (with that device current) and uses that.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)4 << 20;
+static __device__ __align__(256) float scratch[STATIC_SCRATCH_BYTES / 4];
+
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[SCRATCH_MAX_DEVICES];
+
+// Device address of the current device's scratch array.
+zha_status scratch_for_current_device(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "current device");
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+    return fail(ZHA_E_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev, SCRATCH_MAX_DEVICES - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+    if (!p) return fail(ZHA_E_HIP, "static scratch address is null");
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ZHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+zha_status zha_decode_dense_static(const zha_config* cfg, const void* k_cache, const void* v_cache, int64_t n_tokens,
+                                   const void* q, float* out, hipStream_t stream) {
+  zha_status s = validate(cfg);
+  if (s != ZHA_OK) return s;
+  if (!k_cache || !v_cache || !q || !out) return fail(ZHA_E_INVALID, "null cache, q or out");
+  if (((uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)q) % 16)
+    return fail(ZHA_E_INVALID, "cache and q pointers must be 16-byte aligned");
+  if (n_tokens < 1) return fail(ZHA_E_INVALID, "n_tokens %lld < 1", (long long)n_tokens);
+  if (n_tokens > cfg->capacity)
+    return fail(ZHA_E_CAPACITY, "n_tokens %lld > capacity %lld", (long long)n_tokens, (long long)cfg->capacity);
+  const zha_config& c = *cfg;
+  // one split's partials over every query head; the splits per KV head are capped so that
+  // all partials fit the static array
+  const size_t per_split = (size_t)c.num_q_heads * (size_t)(c.head_dim + 2) * 4;
+  const int64_t fit = (int64_t)(STATIC_SCRATCH_BYTES / per_split);
+  if (fit < 1)
+    return fail(ZHA_E_WORKSPACE, "%d query heads of head_dim %d need %zu bytes of partials, above the %zu-byte static scratch",
+                c.num_q_heads, c.head_dim, per_split, STATIC_SCRATCH_BYTES);
+  float* sp = nullptr;
+  s = scratch_for_current_device(&sp);
+  if (s != ZHA_OK) return s;
+  AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.dev.apart = sp;
+  a.K = k_cache;
+  a.V = v_cache;
+  a.q = q;
+  a.cap = c.capacity;
+  a.N = n_tokens;
+  a.hkv = c.num_kv_heads;
+  a.hq = c.num_q_heads;
+  a.g = a.hq / a.hkv;
+  a.b = c.block;
+  const int resident = attend_resident_splits(c.dtype == ZHA_BF16, c.head_dim, true, c.num_kv_heads);
+  a.splits = attn_splits(n_tokens, 1024, (int)(fit < resident ? fit : resident));
+  a.pstride = a.splits;
+  a.keep_sink = 0;
+  a.sigma = 1.0f / sqrtf((float)c.head_dim);
+  a.out = out;
+  hipError_t e = launch_attend(a, c.dtype == ZHA_BF16, c.head_dim, true, stream);
   if (e != hipSuccess) return hip_fail(e, "dense attention launch");
   return ZHA_OK;
 }

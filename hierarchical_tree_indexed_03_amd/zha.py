@@ -50,6 +50,7 @@ def _load() -> ctypes.CDLL:
         "zha_tree_append_n": (I32, [P, P, P, I64, P]),
         "zha_decode": (I32, [P, P, P, P, P]),
         "zha_decode_dense": (I32, [P, P, P, P]),
+        "zha_decode_dense_static": (I32, [ctypes.POINTER(zha_config), P, P, I64, P, P, P]),
         "zha_prefill": (I32, [P, P, P, P, P, I64, P, P]),
         "zha_debug_level": (I32, [P, I32, P, P, P]),
         "zha_debug_router_planes": (I32, [P, I32, P, P, P]),
@@ -74,7 +75,7 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 EXPORTED = ("zha_workspace_bytes", "zha_level1_key_form", "zha_create", "zha_tree_build", "zha_tree_append",
             "zha_tree_append_n", "zha_decode", "zha_prefill",
-            "zha_decode_dense", "zha_debug_level", "zha_debug_router_planes", "zha_debug_trace", "zha_debug_route_level",
+            "zha_decode_dense", "zha_decode_dense_static", "zha_debug_level", "zha_debug_router_planes", "zha_debug_trace", "zha_debug_route_level",
             "zha_profile_start", "zha_profile_stop", "zha_set_top_p_levels", "zha_fit_workspace_bytes", "zha_fit_step",
             "zha_num_tokens", "zha_destroy", "zha_status_string", "zha_last_error")
 
@@ -150,6 +151,11 @@ def zha_prefill(t, k_new, v_new, q, out, m: int, stats=None, stream=None):
 
 def zha_decode_dense(t, q, out, stream=None):
     _check(_lib.zha_decode_dense(t, _p(q), _p(out), _s(stream)))
+
+
+def zha_decode_dense_static(cfg: zha_config, k_cache, v_cache, n_tokens: int, q, out, stream=None):
+    _check(_lib.zha_decode_dense_static(ctypes.byref(cfg), _p(k_cache), _p(v_cache), int(n_tokens), _p(q), _p(out),
+                                        _s(stream)))
 
 
 def zha_debug_level(t, level: int, s_out, c_out, stream=None):

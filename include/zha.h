@@ -196,6 +196,21 @@ zha_status zha_prefill(zha_tree* t, const void* k_new, const void* v_new, const 
  * out[h] = softmax(q_h.K^T/sqrt(d)) V for every query head. */
 zha_status zha_decode_dense(zha_tree* t, const void* q, float* out, hipStream_t stream);
 
+/* Dense decode as zha_decode_dense, allocation-free and without a handle or workspace: for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The caller passes only inputs and outputs:
+ *   cfg      (host) a valid config; head_dim, num_kv_heads, num_q_heads, capacity (the
+ *            caches' row count) and dtype are used.
+ *   k_cache, v_cache  (device) [Hkv][capacity][d] dtype; rows [0, n_tokens) are attended.
+ *   q        (device) [Hq][d] dtype;  out (device) [Hq][d] float32.
+ * Its split-K partials live in a fixed 4 MiB device array inside the library, one copy per
+ * GPU, held until the process ends; the splits per KV head are capped so that
+ * Hq * splits * (d + 2) * 4 bytes fit it.  ZHA_E_WORKSPACE if one split's partials
+ * (Hq * (d + 2) * 4 bytes) exceed it.  No allocation, no synchronisation.  Calls that
+ * overlap on one GPU (e.g. on two streams) share the array and race: serialise them. */
+zha_status zha_decode_dense_static(const zha_config* cfg, const void* k_cache, const void* v_cache,
+                                   int64_t n_tokens, const void* q, float* out, hipStream_t stream);
+
 /* Sets the top-p threshold of each level for the following decodes (blog, "The narrow
  * path": a fixed fraction kept at every level compounds over the depth, so the threshold
  * has to change with depth and context; the pages give no formula, so the caller supplies

@@ -178,3 +178,27 @@ def test_top_p_levels_validation(zha):
 def test_status_strings(zha):
     for s in range(7):
         assert zha.zha_status_string(s)
+
+
+def test_dense_static_argument_errors(zha):
+    """The allocation-free dense decode validates on the host before any HIP call."""
+    import ctypes as C
+    cfg = good(zha)
+    buf = C.create_string_buffer(64)
+    p = C.addressof(buf) + (-C.addressof(buf)) % 16
+    with pytest.raises(zha.ZhaError) as e:
+        zha.zha_decode_dense_static(cfg, None, p, 10, p, p)
+    assert e.value.status == 1
+    with pytest.raises(zha.ZhaError) as e:
+        zha.zha_decode_dense_static(cfg, p, p, 0, p, p)
+    assert e.value.status == 1
+    with pytest.raises(zha.ZhaError) as e:
+        zha.zha_decode_dense_static(cfg, p, p, (1 << 18) + 1, p, p)
+    assert e.value.status == 3
+    with pytest.raises(zha.ZhaError) as e:
+        zha.zha_decode_dense_static(good(zha, head_dim=96), p, p, 10, p, p)
+    assert e.value.status == 2
+    # one split's partials over 8,800 query heads exceed the 4 MiB static scratch
+    with pytest.raises(zha.ZhaError) as e:
+        zha.zha_decode_dense_static(good(zha, num_kv_heads=1100, num_q_heads=8800), p, p, 10, p, p)
+    assert e.value.status == 4 and "static scratch" in str(e.value)
