@@ -626,24 +626,47 @@ def main():
     log(f"[bench] timed {steps} steps: {ms_per_step:.3f} ms/step (events {gpu_ms / steps:.3f}), "
         f"{qps:.1f} queries/s; dominant {dominant} {dom_avg_ms:.4f} ms/launch")
 
-    # ---- cold steps: each after a 1 GiB scratch write (outside its timing) evicts L2 and MALL
+    # ---- cold steps: before each (outside its timing) the caches are evicted.  Primary: a
+    # 2 GiB streaming read of another buffer fills L2 and the Infinity Cache with clean
+    # lines, as the other layers' caches would between two decode steps of this layer.
+    # Also reported: a 1 GiB scratch write instead, which leaves 256 MB of dirty lines that
+    # the step's first misses must write back.
+    import ctypes
+    plib = ctypes.CDLL(os.path.join(ROOT, "hierarchical_tree_indexed_03_amd", "libzha_probe.so"))
+    plib.zha_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    plib.zha_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     cold = None
+    cold_write = None
+    n_cold_read = (args.cold_steps + 1) // 2
     if args.cold_steps > 0:
-        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        cold_ms = []
-        for s_ in range(args.warmup + steps, total):
-            scratch.fill_(float(s_))
+        sst = torch.cuda.current_stream().cuda_stream
+        flush_b = 1 << 31
+        flush_buf = torch.zeros(flush_b, dtype=torch.uint8, device=dev)
+        flush_sink = torch.empty(4096, dtype=torch.int32, device=dev)
+        cold_ms, cold_w_ms = [], []
+        for i_, s_ in enumerate(range(args.warmup + steps, total)):
+            by_read = i_ < n_cold_read
+            if by_read:
+                plib.zha_probe_stream_read(flush_buf.data_ptr(), flush_b, flush_sink.data_ptr(), 1024, sst)
+            else:
+                flush_buf[:1 << 30].fill_(s_ & 0xff)
             c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             c0.record()
             step(s_)
             c1.record()
             torch.cuda.synchronize()
-            cold_ms.append(c0.elapsed_time(c1))
-        del scratch
+            (cold_ms if by_read else cold_w_ms).append(c0.elapsed_time(c1))
+        del flush_buf
         cm = np.array(cold_ms)
-        cold = {"steps": len(cm), "median_ms": round(float(np.median(cm)), 4), "p90_ms": round(float(np.percentile(cm, 90)), 4),
+        cold = {"flush": "2 GiB streaming read of another buffer before each step", "steps": len(cm),
+                "median_ms": round(float(np.median(cm)), 4), "p90_ms": round(float(np.percentile(cm, 90)), 4),
                 "queries_per_s_median": round(1e3 / float(np.median(cm)), 2)}
-        log(f"[bench] cold steps: median {cold['median_ms']:.3f} ms, p90 {cold['p90_ms']:.3f} ms")
+        if cold_w_ms:
+            cw = np.array(cold_w_ms)
+            cold_write = {"flush": "1 GiB scratch write before each step", "steps": len(cw),
+                          "median_ms": round(float(np.median(cw)), 4), "p90_ms": round(float(np.percentile(cw, 90)), 4)}
+        log(f"[bench] cold steps: median {cold['median_ms']:.3f} ms, p90 {cold['p90_ms']:.3f} ms"
+            + (f"; after a scratch write instead: median {cold_write['median_ms']:.3f} ms" if cold_write else ""))
 
     # ---- decode-step bytes (router planes + gathered KV), from the routing stats
     R, d, g, L = w.num_ref, w.head_dim, w.group, w.levels
@@ -651,6 +674,27 @@ def main():
     router_b = (timed_stats[:, :L, :].sum(axis=2) * per_level[None, :]).sum(axis=1)
     gather_b = timed_stats[:, L, :].sum(axis=1) * w.block * 2 * d * 2
     step_bytes = float(np.mean(router_b + gather_b))
+    # the whole step against the HBM roofline: cold first (each step after the read flush),
+    # then warm (the timed steps back to back, the `value` line)
+    roofline_step = None
+    if cold:
+        cst = stats.cpu().numpy()[args.warmup + steps:args.warmup + steps + n_cold_read]
+        cold_bytes = float(np.mean((cst[:, :L, :].sum(axis=2) * per_level[None, :]).sum(axis=1) +
+                                   cst[:, L, :].sum(axis=1) * w.block * 2 * d * 2))
+        ach_c = cold_bytes / (cold["median_ms"] * 1e-3) / 1e9
+        ach_w = step_bytes / (ms_per_step * 1e-3) / 1e9
+        roofline_step = {
+            "bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "cold": {"achieved": round(ach_c, 1), "frac": round(ach_c / HBM_PEAK_GBS, 4), "ms": cold["median_ms"],
+                     "alg_bytes": round(cold_bytes)},
+            "warm": {"achieved": round(ach_w, 1), "frac": round(ach_w / HBM_PEAK_GBS, 4), "ms": round(ms_per_step, 4),
+                     "alg_bytes": round(step_bytes)},
+            "note": ("whole append+decode step: router bytes of the union frontiers plus the gathered K/V over the "
+                     "step time; cold = median step after a cache-evicting read.  `value` is the warm rate because "
+                     "the timed region is K consecutive steps between two synchronisations, which leaves no room "
+                     "for a flush between steps")}
+        log(f"[bench] step roofline: cold {ach_c:.0f} GB/s ({ach_c / HBM_PEAK_GBS:.3f}), warm {ach_w:.0f} GB/s "
+            f"({ach_w / HBM_PEAK_GBS:.3f})")
 
     # ---- dense flash-decode over the same cache (baseline)
     q_last = Qd[args.warmup + steps - 1]
@@ -778,10 +822,6 @@ def main():
         del tree3, Kc, Vc, pout
 
     # stream-read probe: practical HBM read bandwidth of a plain streaming kernel (2 GiB)
-    import ctypes
-    plib = ctypes.CDLL(os.path.join(ROOT, "hierarchical_tree_indexed_03_amd", "libzha_probe.so"))
-    plib.zha_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-    plib.zha_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     sst = torch.cuda.current_stream().cuda_stream
     nb = 1 << 31
     buf = torch.empty(nb, dtype=torch.uint8, device=dev)
@@ -832,8 +872,10 @@ def main():
                    "top_p_levels": [round(x, 6) for x in p_levels] if p_levels else None,
                    "batch": 1, "layers": 1, "step": "append + decode"},
         "roofline": roofline,
+        "roofline_step": roofline_step,
         "cpu_baseline": cpu,
         "cold": cold,
+        "cold_after_write": cold_write,
         "decode_step": {"level1_key_form": key_form, "alg_bytes": round(step_bytes), "achieved_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                         "router_bytes": round(float(np.mean(router_b))), "gather_bytes": round(float(np.mean(gather_b))),
                         "frontier_union_per_level": timed_stats[:, :L, :].sum(axis=2).mean(axis=0).round(1).tolist(),

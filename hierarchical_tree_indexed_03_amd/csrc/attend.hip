@@ -583,7 +583,7 @@ __global__ __launch_bounds__(512) void combine_kernel(AttnArgs a, int32_t* stats
     for (int i = threadIdx.x; i < (levels + 1) * a.hkv; i += 512) {
       const int row = i / a.hkv, k = i % a.hkv;
       const int lvl = row < levels ? levels - row : 0;
-      stats[i] = a.dev.cnt[lvl * a.hkv + k];
+      stats[i] = a.dev.ucnt[lvl * a.hkv + k];
     }
   }
 }

@@ -125,7 +125,9 @@ struct Dev {
   uint32_t* keep[MAXL + 1]; // [Hkv][ncap[l]]           (l >= 1)
   float* score[MAXL + 1];   // [Hkv][GMAX][ncap[l]]     (l >= 1)
   int32_t* part[MAXL + 1];  // [Hkv][nchunks(l)]        expand partial counts
-  int32_t* cnt;             // [MAXL + 1][Hkv]
+  int32_t* cnt;             // [MAXL + 1][Hkv] entries of each union list
+  int32_t* ucnt;            // [MAXL + 1][Hkv] entries some head's frontier holds (a dense list
+                            // may hold nodes of no head's frontier, with mask 0)
   QState* qs;               // [MAXL + 1][Hq]
   uint64_t* hpart;          // [Hkv][SEL_P][GMAX][NB1] per-workgroup coarse mass histograms
   uint32_t* tdbits;         // [MAXL + 1][Hq][2][TD_WORDS] top-down frontier / kept bitmaps

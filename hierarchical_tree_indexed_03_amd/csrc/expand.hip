@@ -98,8 +98,10 @@ __global__ __launch_bounds__(256) void route_expand_emit_kernel(RouteArgs a) {
   __syncthreads();
   const int32_t base = red[0] + red[1] + red[2] + red[3];
   const int out_lv = lv - 1;
-  if (blockIdx.x == 0 && threadIdx.x == 0)
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
     a.dev.cnt[out_lv * a.hkv + kv] = red2[0] + red2[1] + red2[2] + red2[3];
+    a.dev.ucnt[out_lv * a.hkv + kv] = red2[0] + red2[1] + red2[2] + red2[3];
+  }
   const int32_t total = total_s;
   const int64_t ocap = a.dev.ncap[out_lv];
   int32_t* onode = a.dev.node[out_lv] + kv * ocap + base;

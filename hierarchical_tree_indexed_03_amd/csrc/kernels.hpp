@@ -139,10 +139,15 @@ hipError_t launch_route_score(const RouteArgs& a, int D, int R, hipStream_t st);
 hipError_t launch_route_select(const RouteArgs& a, hipStream_t st);   // hist, bound, classify, resolve
 hipError_t launch_route_expand(const RouteArgs& a, hipStream_t st);
 // Top levels with at most TD_MAX nodes: score every node of levels `level`..`dense_lo` in
-// one launch, then select all of them top-down (one workgroup per query head) and write
-// their dense union lists; the list expansion of level `dense_lo` follows.
+// one launch, then select all of them top-down (one workgroup per query head).
 hipError_t launch_route_dense_score(const RouteArgs& a, int D, int R, hipStream_t st);
 hipError_t launch_route_topdown(const RouteArgs& a, hipStream_t st);
+// Dense union lists (node, frontier mask, keep mask) of the top-down levels
+// a.dense_lo .. a.level from the top-down bitmaps.
+hipError_t launch_route_td_lists(const RouteArgs& a, hipStream_t st);
+// The dense union list of level a.dense_lo - 1 (masks = the heads that kept each parent),
+// from the top-down kept bitmaps of level a.dense_lo (a.dense_lo >= 2).
+hipError_t launch_route_td_children(const RouteArgs& a, hipStream_t st);
 // Per-head frontier bitmaps of level a.level in dev.tdbits from that level's union list
 // (dev.node / dev.mask / dev.cnt): the given frontier of a teacher-forced top-down level.
 hipError_t launch_route_td_seed(const RouteArgs& a, hipStream_t st);

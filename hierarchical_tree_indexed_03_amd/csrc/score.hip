@@ -15,13 +15,7 @@
 #include "route_util.hpp"
 #include "qk_tile.hpp"
 
-// Score-kernel tuning: tiles in flight per wave (planes with R >= 8 / R < 8; key form).
-#ifndef ZHA_SCORE_UN_WIDE
-#define ZHA_SCORE_UN_WIDE 1
-#endif
-#ifndef ZHA_SCORE_UN_NARROW
-#define ZHA_SCORE_UN_NARROW 2
-#endif
+// Score-kernel tuning: tiles in flight per wave (key form; bf16 / FP4 planes).
 #ifndef ZHA_KEYS_UN
 #define ZHA_KEYS_UN 1
 #endif
@@ -60,25 +54,42 @@ __global__ __launch_bounds__(256) void route_prep_kernel(RouteArgs a) {
     a.dev.node[L][kv * capL + n] = (int32_t)n;
     a.dev.mask[L][kv * capL + n] = full;
   }
-  for (int64_t i = tid; i < (int64_t)(MAXL + 1) * a.hkv; i += nth)
-    a.dev.cnt[i] = (i / a.hkv == L) ? (int32_t)a.nlevel : 0;
+  // list sizes: the top level's list, and every level selected top-down (a.dense_lo ..
+  // L, all nodes scored); the others are written by the kernels that build their lists
+  for (int64_t i = tid; i < (int64_t)(MAXL + 1) * a.hkv; i += nth) {
+    const int lv = (int)(i / a.hkv);
+    const int32_t n = (lv == L || (lv >= a.dense_lo && lv <= L && a.dense_lo >= 1)) ? (int32_t)a.nl[lv] : 0;
+    a.dev.cnt[i] = n;
+    a.dev.ucnt[i] = n;
+  }
 }
 
 // ------------------------------------------------------------------ score
 // Scores of the union frontier on fp32 MFMA: one 16x16 output tile = the 16 query-head rows
-// (the group's heads, zero-padded) x 16 columns = 16/R nodes x R planes.  The contraction
-// over d is permuted so that lane (column c, group kg) streams the contiguous 64-byte
-// pieces [64i + 16kg, +16) of its plane row; Q uses the same permutation.  A node's score is
+// (the group's heads, zero-padded) x 16 columns = 16/R nodes x R planes.  A node's score is
 // the max over its R columns (plus the offsets c_j), taken across the R lanes of the node.
+//
+// Loading: each tile's 16 plane rows are read whole, RPI rows per load instruction (a row's
+// 4D bytes by D/4 consecutive lanes, 16 bytes each), so every instruction reads whole
+// 512-byte rows (d 128) instead of one 64-byte piece of each of 16 rows; the rows go through
+// LDS (rows padded by 16 bytes, so the MFMA-layout reads hit distinct banks) into the MFMA
+// operand layout: lane (column c, group kg) takes the pieces [64i + 16kg, +16) of row c, and
+// Q uses the same permutation of the contraction.  The next tile's loads are issued before
+// the current tile's MFMAs.
 template <int D, int R>
 __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
   constexpr int NPT = 16 / R;                 // nodes per 16-column tile
-  constexpr int NI = D / 16;                  // float4 loads per lane per tile
-  constexpr int UN = R >= 8 ? ZHA_SCORE_UN_WIDE : ZHA_SCORE_UN_NARROW;   // tiles in flight per wave
+  constexpr int NI = D / 16;                  // float4 MFMA operands per lane per tile
+  constexpr int LPR = D / 4;                  // lanes per row in a load instruction
+  constexpr int RPI = 64 / LPR;               // rows per load instruction
+  constexpr int NLD = 16 / RPI;               // load instructions per tile
+  constexpr int RS = D + 4;                   // LDS row stride in floats
+  __shared__ __align__(16) float stg[4][16 * RS];
   __shared__ float red[4][16];
   const int kv = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const int slot = col / R, plane = col % R;
+  const int lrow = lane / LPR, lcol = (lane % LPR) * 4;
   const bool dense = a.dense != 0;            // every node of the level, no list
   const int lv = dense ? dense_level(a) : a.level;
   const int64_t cnt = dense ? a.nl[lv] : a.dev.cnt[lv * a.hkv + kv];
@@ -88,6 +99,7 @@ __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
   const float* S = a.dev.s[lv] + (int64_t)kv * cap * R * D;
   const float* C = a.dev.c[lv] + (int64_t)kv * cap * R;
   float* out = a.dev.score[lv] + (int64_t)kv * GMAX * cap;
+  float* W = stg[wave];
   const int g = a.g;
 
   float qa[NI][4];
@@ -100,45 +112,61 @@ __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
   float runmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 
   const int64_t ntiles = (cnt + NPT - 1) / NPT;
-  for (int64_t t0 = ((int64_t)blockIdx.x * 4 + wave) * UN; t0 < ntiles; t0 += (int64_t)gridDim.x * 4 * UN) {
-    float4 sb[UN][NI];
-    float cj[UN];
-    int64_t ent[UN];
-    bool ok[UN];
+  const int64_t tstride = (int64_t)gridDim.x * 4;
+  // row `col` of a tile: its node (-1: none, or an entry of no head's frontier), mask and
+  // offset; then the tile's rows, whole rows per load instruction
+  int32_t rnid;
+  uint32_t rmk;
+  float rcj;
+  uint4 ld[NLD];
+  auto fetch = [&](int64_t t) {
+    const int64_t e = t * NPT + slot;
+    const bool ok = t < ntiles && e < cnt;
+    rmk = (ok && !dense) ? masks[e] : 0u;
+    rnid = (ok && (dense || rmk != 0u)) ? (dense ? (int32_t)e : nodes[e]) : -1;
+    rcj = rnid >= 0 ? C[(int64_t)rnid * R + plane] : -INFINITY;
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      ent[u] = (t0 + u) * NPT + slot;
-      ok[u] = (t0 + u) < ntiles && ent[u] < cnt;
-      const int64_t nid = ok[u] ? (dense ? ent[u] : (int64_t)nodes[ent[u]]) : 0;
-      const float* sp = S + (nid * R + plane) * D + 4 * kg;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) sb[u][i] = ok[u] ? *(const float4*)(sp + 16 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
-      cj[u] = ok[u] ? C[nid * R + plane] : -INFINITY;
+    for (int i = 0; i < NLD; ++i) {
+      const int r = lrow + RPI * i;
+      const int32_t nd = __shfl(rnid, r);
+      ld[i] = nd >= 0 ? *(const uint4*)(S + ((int64_t)nd * R + r % R) * D + lcol) : make_uint4(0, 0, 0, 0);
     }
+  };
+  int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t < ntiles) fetch(t);
+  for (; t < ntiles; t += tstride) {
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NLD; ++i) *(uint4*)(W + (lrow + RPI * i) * RS + lcol) = ld[i];
+    const int32_t nid = rnid;
+    const uint32_t mk = rmk;
+    const float cj = rcj;
+    wave_sync_lds();
+    if (t + tstride < ntiles) fetch(t + tstride);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][0], sb[u][i].x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][1], sb[u][i].y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][2], sb[u][i].z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][3], sb[u][i].w, acc, 0, 0, 0);
-      }
-      float v[4];
+    for (int i = 0; i < NI; ++i) {
+      const float4 sb = *(const float4*)(W + col * RS + 16 * i + 4 * kg);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][0], sb.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][1], sb.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][2], sb.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][3], sb.w, acc, 0, 0, 0);
+    }
+    wave_sync_lds();
+    float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[e] + cj[u];
+    for (int e = 0; e < 4; ++e) v[e] = acc[e] + cj;
 #pragma unroll
-      for (int off = 1; off < R; off <<= 1)
+    for (int off = 1; off < R; off <<= 1)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], __shfl_xor(v[e], off));
-      const uint32_t mk = (ok[u] && !dense) ? masks[ent[u]] : 0u;   // dense: max taken later
+      for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], __shfl_xor(v[e], off));
+    // dense: every head's score (the max is taken later); list mode: the scores of the heads
+    // whose frontier holds the node
+    const int64_t ent = t * NPT + slot;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int h = kg * 4 + e;
-        if (ok[u] && plane == 0 && h < g) out[(int64_t)h * cap + ent[u]] = v[e];
-        if ((mk >> h) & 1u) runmax[e] = fmaxf(runmax[e], v[e]);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int h = kg * 4 + e;
+      if (nid >= 0 && plane == 0 && h < g && (dense || ((mk >> h) & 1u))) out[(int64_t)h * cap + ent] = v[e];
+      if ((mk >> h) & 1u) runmax[e] = fmaxf(runmax[e], v[e]);
     }
   }
   // per-head max: lanes of one 16-lane row share kg, i.e. the heads 4kg..4kg+3
@@ -275,8 +303,9 @@ __global__ __launch_bounds__(256) void route_score_bf16_kernel(RouteArgs a) {
     for (int u = 0; u < UN; ++u) {
       const int64_t e = (t0 + u) * NPT + slot;
       const bool ok = (t0 + u) < ntiles && e < cnt;
-      nd[u] = ok ? (dense ? (int32_t)e : nodes[e]) : -1;
       mk[u] = (ok && !dense) ? masks[e] : 0u;   // dense: the max is taken later
+      // list mode: an entry of no head's frontier (mask 0) is not read
+      nd[u] = (ok && (dense || mk[u] != 0u)) ? (dense ? (int32_t)e : nodes[e]) : -1;
     }
   };
   const int64_t tfirst = ((int64_t)blockIdx.x * 4 + wave) * UN;
@@ -326,7 +355,7 @@ __global__ __launch_bounds__(256) void route_score_bf16_kernel(RouteArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int h = kg * 4 + e;
-        if (ncur[u] >= 0 && plane == 0 && h < g) out[(int64_t)h * cap + ent] = v[e];
+        if (ncur[u] >= 0 && plane == 0 && h < g && (dense || ((mcur[u] >> h) & 1u))) out[(int64_t)h * cap + ent] = v[e];
         if ((mcur[u] >> h) & 1u) runmax[e] = fmaxf(runmax[e], v[e]);
       }
     }
@@ -387,7 +416,8 @@ __global__ __launch_bounds__(256) void route_score_bf16_rows_kernel(RouteArgs a)
       const bool tok = (t0 + u) < ntiles;
       // the lane's load row `col`
       const int64_t e_row = (t0 + u) * NPT + col / R;
-      const bool okr = tok && e_row < cnt;
+      // list mode: an entry of no head's frontier (mask 0) is not read
+      const bool okr = tok && e_row < cnt && (dense || masks[e_row] != 0u);
       const int64_t nrow = okr ? (dense ? e_row : (int64_t)nodes[e_row]) : 0;
       PlaneRow<TQ, D>::load(S + (nrow * R + col % R) * D, kg, okr, kf[u]);
       // the lane's output rows 4kg + e
@@ -425,8 +455,8 @@ __global__ __launch_bounds__(256) void route_score_bf16_rows_kernel(RouteArgs a)
       for (int n = 0; n < NPL; ++n) {
         const int64_t e = eo[u][n];
         const bool writer = ((4 * kg) % R) == 0;    // the node's first lane group
-        if (e >= 0 && writer && col < g) out[(int64_t)col * cap + e] = v[n * RL];
         const uint32_t mk = (e >= 0 && !dense) ? masks[e] : 0u;   // dense: max taken later
+        if (e >= 0 && writer && col < g && (dense || ((mk >> col) & 1u))) out[(int64_t)col * cap + e] = v[n * RL];
         if ((mk >> col) & 1u) runmax = fmaxf(runmax, v[n * RL]);
       }
     }
@@ -487,14 +517,15 @@ __global__ __launch_bounds__(256) void route_score_keys_kernel(RouteArgs a) {
   auto load_ids = [&](int64_t t0, int32_t (&r)[UN], int32_t (&nd)[UN][NPT], uint32_t (&mk)[UN][NPT]) {
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
+      // an entry of no head's frontier (mask 0) is not read
       const int64_t e_row = (t0 + u) * NPT + col / B;
-      r[u] = ((t0 + u) < ntiles && e_row < cnt) ? nodes[e_row] : -1;
+      r[u] = ((t0 + u) < ntiles && e_row < cnt && masks[e_row] != 0u) ? nodes[e_row] : -1;
 #pragma unroll
       for (int n = 0; n < NPT; ++n) {
         const int64_t e = (t0 + u) * NPT + n;
         const bool ok = (t0 + u) < ntiles && e < cnt;
-        nd[u][n] = ok ? nodes[e] : -1;
         mk[u][n] = ok ? masks[e] : 0u;
+        nd[u][n] = mk[u][n] != 0u ? nodes[e] : -1;
       }
     }
   };
@@ -570,7 +601,7 @@ __global__ __launch_bounds__(256) void route_score_keys_kernel(RouteArgs a) {
         v = fmaxf(v, __shfl_xor(v, 32));
         const int64_t e_ent = (t0 + u) * NPT + n;   // wave-uniform
         const bool ok = ncur[u][n] >= 0;
-        if (ok && kg == 0 && col < g) out[(int64_t)col * cap + e_ent] = v;
+        if (ok && kg == 0 && col < g && ((mcur[u][n] >> col) & 1u)) out[(int64_t)col * cap + e_ent] = v;
         if ((mcur[u][n] >> col) & 1u) runmax = fmaxf(runmax, v);
       }
       wave_sync_lds();
@@ -637,7 +668,7 @@ static void launch_score_planes(const RouteArgs& a, int nlev, int64_t nodes, hip
     else launch_score_bf16<float, D, R>(a, nlev, nodes, st);
     return;
   }
-  constexpr int NPB = 4 * (16 / R) * (R >= 8 ? ZHA_SCORE_UN_WIDE : ZHA_SCORE_UN_NARROW);   // nodes per block pass
+  constexpr int NPB = 4 * (16 / R);   // nodes per block pass
   static const int per_cu = resident_per_cu(route_score_kernel<D, R>, 256);
   const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
   hipLaunchKernelGGL((route_score_kernel<D, R>), dim3(grid_for(nodes, NPB, cap), (unsigned)a.hkv, (unsigned)nlev), dim3(256),

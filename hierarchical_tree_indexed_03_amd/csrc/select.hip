@@ -60,9 +60,9 @@ __global__ __launch_bounds__(SEL_THREADS) void route_hist_kernel(RouteArgs a) {
     for (int u = 0; u < HIST_U; ++u) {
       const int64_t e = e0 + SEL_THREADS * u;
       mk[u] = e < hi ? masks[e] : 0u;
-      // score rows exist for all GMAX heads; only entries with the head's bit are used
+      // only the scores of heads whose frontier holds the entry are written and read
 #pragma unroll
-      for (int gi = 0; gi < GMAX; ++gi) v[u][gi] = (gi < g && e < hi) ? sc[(int64_t)gi * cap + e] : 0.f;
+      for (int gi = 0; gi < GMAX; ++gi) v[u][gi] = ((mk[u] >> gi) & 1u) ? sc[(int64_t)gi * cap + e] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < HIST_U; ++u)
@@ -191,8 +191,9 @@ __global__ __launch_bounds__(SEL_THREADS) void route_classify_kernel(RouteArgs a
     for (int u = 0; u < CLS_U; ++u) {
       const int64_t e = e0 + 64 * u + lane;
       mk[u] = e < hi ? masks[e] : 0u;
+      // only the scores of heads whose frontier holds the entry are written and read
 #pragma unroll
-      for (int gi = 0; gi < GMAX; ++gi) v[u][gi] = (gi < g && e < hi) ? sc[(int64_t)gi * cap + e] : 0.f;
+      for (int gi = 0; gi < GMAX; ++gi) v[u][gi] = ((mk[u] >> gi) & 1u) ? sc[(int64_t)gi * cap + e] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < CLS_U; ++u) {

@@ -10,10 +10,12 @@
 // as -inf), and the passes that follow run on LDS:
 //   max -> coarse mass histogram -> boundary bin -> fine histogram of that bin ->
 //   boundary sub-bin -> keep / tie classification -> exact rank order among the ties.
-// The head's frontier and kept bitmaps of each level go to global memory; a union kernel
-// then writes the group's dense union lists (node = position, mask of heads whose frontier
-// holds it, mask of heads that kept it), which the list expansion of the lowest such level
-// turns into the union list of the level below.
+// The head's frontier and kept bitmaps of each level go to global memory.  From them one
+// kernel writes the (dense) union list of the level below the lowest such level; another
+// writes the dense union lists of the selected levels themselves (node = position, mask of
+// heads whose frontier holds it, mask of heads that kept it) when they are needed: for a
+// trace, or when the lowest selected level is level 1 (its list expansion then gives the
+// gather list).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "route_util.hpp"
@@ -296,7 +298,10 @@ __global__ __launch_bounds__(256) void route_topdown_union_kernel(RouteArgs a) {
   const int64_t n = a.nl[lv];
   const int64_t cap = a.dev.ncap[lv];
   const int64_t e0 = (int64_t)blockIdx.x * UN_NODES;
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.dev.cnt[lv * a.hkv + kv] = (int32_t)n;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.dev.cnt[lv * a.hkv + kv] = (int32_t)n;
+    a.dev.ucnt[lv * a.hkv + kv] = (int32_t)n;
+  }
   if (e0 >= n) return;
   const int64_t w0 = e0 / 32, nw = (n + 31) / 32;
   for (int i = threadIdx.x; i < g * W; i += 256) {
@@ -347,13 +352,69 @@ hipError_t launch_route_td_seed(const RouteArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The union list of level dense_lo - 1, dense: entry c = node c for every node of that level,
+// its mask = the heads of the group that kept its parent at level dense_lo (0: no head's
+// frontier holds it; the large-level kernels then skip it).  Written straight from the
+// top-down kept bitmaps, so no compaction pass sits between the top-down selection and the
+// next level's scoring.  ucnt counts the entries some head holds.
+constexpr int CL_NODES = 4096;                 // children per workgroup
+constexpr int CL_WORDS = CL_NODES / 2 / 32 + 2;   // parent bitmap words they span (b >= 2)
+__global__ __launch_bounds__(256) void route_td_children_kernel(RouteArgs a) {
+  __shared__ uint32_t kb[GMAX][CL_WORDS];
+  __shared__ int32_t red[4];
+  const int kv = blockIdx.y, g = a.g, lo = a.dense_lo, lc = lo - 1;
+  const int64_t nc = a.nl[lc];
+  const int64_t capc = a.dev.ncap[lc];
+  const int lb = __ffs(a.b) - 1;               // b is a power of two
+  const int64_t c0 = (int64_t)blockIdx.x * CL_NODES;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.dev.cnt[lc * a.hkv + kv] = (int32_t)nc;
+  if (c0 >= nc) return;
+  const int64_t c1 = c0 + CL_NODES < nc ? c0 + CL_NODES : nc;
+  const int64_t w0 = (c0 >> lb) >> 5, w1 = (((c1 - 1) >> lb) >> 5) + 1;
+  const int nwd = (int)(w1 - w0);
+  for (int i = threadIdx.x; i < g * nwd; i += 256) {
+    const int gi = i / nwd, w = i % nwd;
+    kb[gi][w] = a.dev.tdbits[(((int64_t)lo * a.hq + kv * g + gi) * 2 + 1) * TD_WORDS + w0 + w];
+  }
+  __syncthreads();
+  int32_t nz = 0;
+  int32_t* onode = a.dev.node[lc] + kv * capc;
+  uint32_t* omask = a.dev.mask[lc] + kv * capc;
+  for (int64_t c = c0 + threadIdx.x; c < c1; c += 256) {
+    const int64_t pn = c >> lb;
+    const int w = (int)((pn >> 5) - w0), bit = (int)(pn & 31);
+    uint32_t km = 0;
+    for (int gi = 0; gi < g; ++gi) km |= ((kb[gi][w] >> bit) & 1u) << gi;
+    onode[c] = (int32_t)c;
+    omask[c] = km;
+    nz += km != 0u;
+  }
+  for (int off = 32; off > 0; off >>= 1) nz += __shfl_xor(nz, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = nz;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int32_t t = red[0] + red[1] + red[2] + red[3];
+    if (t) atomicAdd(&a.dev.ucnt[lc * a.hkv + kv], t);
+  }
+}
+
 hipError_t launch_route_topdown(const RouteArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(route_topdown_kernel, dim3((unsigned)a.hq), dim3(TD_THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_td_lists(const RouteArgs& a, hipStream_t st) {
   const int nlev = a.level - a.dense_lo + 1;
   int64_t mx = 0;
   for (int l = a.dense_lo; l <= a.level; ++l) mx = a.nl[l] > mx ? a.nl[l] : mx;
   hipLaunchKernelGGL(route_topdown_union_kernel, dim3(grid_for(mx, UN_NODES, 1 << 20), (unsigned)a.hkv, (unsigned)nlev),
                      dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_td_children(const RouteArgs& a, hipStream_t st) {
+  const int64_t nc = a.nl[a.dense_lo - 1];
+  hipLaunchKernelGGL(route_td_children_kernel, dim3(grid_for(nc, CL_NODES, 1 << 20), (unsigned)a.hkv), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -33,6 +33,11 @@ struct zha_tree {
   void* V;
   const void* refs;
   float top_p[MAXL + 1];  // p per level (index = level); cfg.top_p unless a schedule is set
+  // the top-down selection of the last routing call: its route arguments, whether its
+  // levels' dense union lists exist (they are written when a trace asks for them)
+  RouteArgs td_args;
+  bool td_valid;
+  bool td_lists;
 };
 
 namespace {
@@ -158,6 +163,7 @@ size_t layout(const zha_config& c, char* base, Dev* dev) {
       d.s4x[l] = (uint8_t*)take((size_t)(H * d.ncap[l] * R * D) / 32);
     }
   d.cnt = (int32_t*)take((size_t)((MAXL + 1) * H) * 4);
+  d.ucnt = (int32_t*)take((size_t)((MAXL + 1) * H) * 4);
   d.qs = (QState*)take((size_t)((L + 1) * Q) * sizeof(QState));
   d.hpart = (uint64_t*)take((size_t)(H * SEL_P * GMAX * NB1) * 8);
   d.tdbits = (uint32_t*)take((size_t)((L + 1) * Q * 2 * TD_WORDS) * 4);
@@ -562,18 +568,19 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
   const zha_config& c = t->cfg;
   RouteArgs r = route_args(t, q);
   r.nlevel = nodes_at(c, c.levels, t->N);
+  // top levels small enough to score whole and select top-down in one launch
+  const int lo = topdown_lo(r);
+  r.dense_lo = lo <= c.levels ? lo : 0;   // prep sets the list sizes of those levels
   hipError_t e;
   {
     ProfScope ps(t, "route_prep", stream);
     e = launch_route_prep(r, c.dtype == ZHA_BF16, c.head_dim, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "route prep launch");
-  // top levels small enough to score whole and select top-down in one launch
-  const int lo = topdown_lo(r);
+  t->td_valid = false;
   if (lo <= c.levels) {
     r.level = c.levels;
     r.dense = 1;
-    r.dense_lo = lo;
     {
       ProfScope ps(t, "route_score.top", stream);
       e = launch_route_dense_score(r, c.head_dim, c.num_ref, stream);
@@ -585,14 +592,24 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
     }
     if (e != hipSuccess) return hip_fail(e, "route top-down select launch");
     r.dense = 0;
-    r.level = lo;
-    r.nlevel = r.nl[lo];
-    r.nbelow = lo > 1 ? r.nl[lo - 1] : 0;
-    {
+    t->td_args = r;
+    t->td_valid = true;
+    t->td_lists = false;
+    if (lo >= 2) {
+      // the next level's union list straight from the kept bitmaps
       ProfScope ps(t, "route_expand.top", stream);
-      e = launch_route_expand(r, stream);
+      e = launch_route_td_children(r, stream);
+    } else {
+      // level 1 selected top-down: its dense lists, then the gather list
+      ProfScope ps(t, "route_expand.top", stream);
+      e = launch_route_td_lists(r, stream);
+      t->td_lists = true;
+      r.level = lo;
+      r.nlevel = r.nl[lo];
+      r.nbelow = 0;
+      if (e == hipSuccess) e = launch_route_expand(r, stream);
     }
-    if (e != hipSuccess) return hip_fail(e, "route expand launch");
+    if (e != hipSuccess) return hip_fail(e, "route top-down list launch");
   }
   for (int lv = lo - 1; lv >= 1; --lv) {
     zha_status s = route_levels(t, r, lv, stream, true);
@@ -816,6 +833,12 @@ zha_status zha_debug_trace(zha_tree* t, int32_t level, int64_t cap, int32_t* nod
   if (cap < n) return fail(ZHA_E_INVALID, "cap %lld < %lld nodes", (long long)cap, (long long)n);
   const int64_t dcap = t->dev.ncap[level];
   hipError_t e = hipSuccess;
+  if (t->td_valid && !t->td_lists && level >= t->td_args.dense_lo && level <= t->td_args.level) {
+    // the dense union lists of the last top-down selection, from its bitmaps
+    e = launch_route_td_lists(t->td_args, stream);
+    if (e != hipSuccess) return hip_fail(e, "top-down list launch");
+    t->td_lists = true;
+  }
   for (int kv = 0; kv < c.num_kv_heads && e == hipSuccess; ++kv) {
     e = hipMemcpyAsync(nodes + kv * cap, t->dev.node[level] + kv * dcap, n * 4, hipMemcpyDeviceToDevice, stream);
     if (e == hipSuccess)
@@ -890,8 +913,13 @@ zha_status zha_debug_route_level(zha_tree* t, int32_t level, const void* q, cons
     r.dense = 0;
     r.tf = 1;
     e = launch_route_topdown(r, stream);
+    if (e == hipSuccess) e = launch_route_td_lists(r, stream);
     if (e != hipSuccess) return hip_fail(e, "route top-down select launch");
+    t->td_args = r;
+    t->td_valid = true;
+    t->td_lists = true;
   } else {
+    t->td_valid = false;
     zha_status zs = route_levels(t, r, level, stream, false);
     if (zs != ZHA_OK) return zs;
   }

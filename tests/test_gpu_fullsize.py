@@ -169,7 +169,10 @@ def test_ultra_16m_sampled(planes):
                 if pos < len(tnodes) and tnodes[pos] == node:
                     routed = planes != "f32" and lv in P.router_levels(w)
                     sr = zo.QUANTISERS[planes](so) if routed else so
+                    mk = int(tr["masks"][pos]) & 0xFFFFFFFF
                     for g_ in range(w.group):
+                        if not (mk >> g_) & 1:
+                            continue        # scores exist for the heads whose frontier holds it
                         qh = q[kv * w.group + g_]
                         ref = float(np.max(sig * (sr @ qh) + co))
                         tol = P.SCORE_TOL
