@@ -65,6 +65,8 @@ def parse():
                          "geometries: step time per stage, loss, routing before and after (own JSON line)")
     ap.add_argument("--fit-lr", type=float, default=1.0, help="SGD step of --fit")
     ap.add_argument("--fit-nq", type=int, default=8, help="training queries per query head and step in --fit")
+    ap.add_argument("--cpu-sweep", action="store_true",
+                    help="time the CPU oracle on the light sweep and the 16M workload (no GPU work)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for traffic)")
     return ap.parse_args()
@@ -178,6 +180,112 @@ def cpu_baseline(w, K, V, refs, queries, n0, budget):
                         f"(append+route+attend) in {el:.1f}s on 1 thread, scaled x{w.num_kv_heads} to all "
                         f"heads; tree over {n0} tokens built first (untimed, {tb:.1f}s, all threads)"),
                 host_cpus=os.cpu_count(), cpu_model=_cpu_model())
+
+
+def _oracle_worker(args):
+    """One KV head's query group on one host thread (a separate process): the oracle tree over
+    the seeded cache, then append + route + attend steps of the group's planted queries until
+    `budget` seconds.  Inputs are regenerated from the seeds in the process."""
+    wname, n0, planes_f32, kv, budget, n_steps = args
+    from threadpoolctl import threadpool_limits
+    from oracle import zha_oracle as zo
+    w = wc.NAMED[wname].with_(steps=n_steps)
+    with threadpool_limits(1):
+        K = gen.token_rows(w, gen.STREAM_K, kv, 0, n0 + n_steps)
+        V = gen.token_rows(w, gen.STREAM_V, kv, 0, n0 + n_steps)
+        refs = gen.ref_queries(w)[kv]
+        tb0 = time.perf_counter()
+        tree = zo.build_tree(K, refs, w.block, w.levels, n0)
+        tb = time.perf_counter() - tb0
+        fetch = lambda _kv, idx: K[idx]
+        steps = 0
+        t0 = time.perf_counter()
+        while steps < n_steps and time.perf_counter() - t0 < budget:
+            if w.appends:
+                zo.append_token(tree, K[tree.n_tokens])
+            for gi in range(w.group):
+                q, _ = gen.planted_query(w, steps, kv * w.group + gi, tree.n_tokens, fetch)
+                r = zo.route(tree, q, w.top_p, w.keep_sink)
+                zo.attend(tree.keys[:tree.n_tokens], V[:tree.n_tokens], q, r["tokens"])
+            steps += 1
+        el = time.perf_counter() - t0
+    return kv, steps, el, tb
+
+
+def cpu_baseline_all_cores(w, n0, budget, n_steps):
+    """The oracle on all host cores: one process per KV head (its query group), all at once,
+    each on one thread; a step of the whole layer takes as long as the slowest process."""
+    import multiprocessing as mp
+    ctx = mp.get_context("spawn")
+    jobs = [(w.name, n0, True, kv, budget, n_steps) for kv in range(w.num_kv_heads)]
+    with ctx.Pool(len(jobs)) as pool:
+        res = pool.map(_oracle_worker, jobs)
+    per_step = max(el / max(st, 1) for _, st, el, _ in res)
+    return dict(value=1.0 / per_step, unit="queries/s", cores=len(jobs), kind="oracle",
+                sample=(f"{len(jobs)} processes at once, one per KV head (its {w.group} query heads) on one thread "
+                        f"each; {min(st for _, st, _, _ in res)}-{max(st for _, st, _, _ in res)} decode steps "
+                        f"(append+route+attend) in {budget:.0f}s each after building its tree "
+                        f"({max(tb for *_, tb in res):.1f}s); a step = the slowest process's step time"),
+                host_cpus=os.cpu_count(), cpu_model=_cpu_model())
+
+
+def cpu_sweep(args):
+    """The oracle on the light-router sweep (tree build plus 16 append+decode steps per N) and
+    on the 16M-token workload (tree build plus 8 steps), for KV head 0's query group on one
+    host thread, scaled to all KV heads.  The 16M tree is built level 1 chunk by chunk (the
+    oracle's level-1 summary of a 2^20-token chunk is that of its blocks)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import zha_oracle as zo
+    rows = []
+    cases = [(wc.light(n), 16) for n in wc.LIGHT_SIZES] + [(wc.ULTRA, 8)]
+    for base, n_steps in cases:
+        w = base.with_(steps=n_steps)
+        n0 = w.n_tokens
+        with threadpool_limits(1):
+            refs = gen.ref_queries(w)[0].astype(np.float64)
+            tb0 = time.perf_counter()
+            s1, c1, K = [], [], []
+            for lo in range(0, n0, gen.CHUNK):
+                hi = min(n0, lo + gen.CHUNK)
+                kr = gen.token_rows(w, gen.STREAM_K, 0, lo, hi)
+                K.append(kr)
+                s, c = zo.level1_planes(kr.astype(np.float64), refs, w.block)
+                s1.append(s)
+                c1.append(c)
+            levels = [(np.concatenate(s1), np.concatenate(c1))]
+            del s1, c1
+            for _ in range(2, w.levels + 1):
+                levels.append(zo.parent_planes(levels[-1][0], levels[-1][1], refs, w.block))
+            tb = time.perf_counter() - tb0
+            K.append(gen.token_rows(w, gen.STREAM_K, 0, n0, n0 + n_steps))
+            K = np.concatenate(K)
+            V = gen.token_rows(w, gen.STREAM_V, 0, 0, n0 + n_steps)     # untimed, like the keys
+            tree = zo.Tree(keys=K, refs=refs, block=w.block, n_levels=w.levels, n_tokens=n0, levels=levels)
+            fetch = lambda _kv, idx: K[idx]
+            t0 = time.perf_counter()
+            for st in range(n_steps):
+                zo.append_token(tree, K[tree.n_tokens])
+                for gi in range(w.group):
+                    q, _ = gen.planted_query(w, st, gi, tree.n_tokens, fetch)
+                    r = zo.route(tree, q, w.top_p, w.keep_sink)
+                    tk = r["tokens"]
+                    zo.attend(K[tk], V[tk], q, np.arange(len(tk)))
+            el = time.perf_counter() - t0
+        per_step = el / n_steps * w.num_kv_heads
+        row = {"workload": w.name, "kv_tokens": n0, "oracle_build_s_one_kv_head": round(tb, 2),
+               "oracle_build_tokens_per_s_all_heads": round(n0 / (tb * w.num_kv_heads), 1),
+               "steps": n_steps, "oracle_step_s_all_heads": round(per_step, 3),
+               "oracle_queries_per_s": round(1.0 / per_step, 4)}
+        log(f"[cpu-sweep] {row}")
+        rows.append(row)
+        del tree, levels, K, V
+    rec = {"metric": "oracle (CPU) build tokens/s and decode queries/s, light sweep and 16M",
+           "unit": "queries/s", "cores": 1, "kind": "oracle", "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(),
+           "sample": ("KV head 0's query group on one host thread, scaled to all KV heads: the tree build "
+                      "(the 16M one level 1 chunk by chunk), then append + route + attend steps; cache rows "
+                      "generated from the seeds beforehand, untimed"),
+           "per_workload": rows}
+    print(json.dumps(rec), flush=True)
 
 
 def _cpu_model() -> str:
@@ -499,6 +607,8 @@ def main():
     import torch
     from hierarchical_tree_indexed_03_amd import zha
 
+    if args.cpu_sweep:
+        return cpu_sweep(args)
     if args.crossover:
         return crossover(args)
     if args.fit:
@@ -852,6 +962,11 @@ def main():
         V0 = Vd[:1].float().cpu().numpy()
         cpu = cpu_baseline(w, K0, V0, refs, queries, n0, args.cpu_budget)
         log(f"[bench] cpu baseline {cpu['value']:.4f} queries/s ({time.perf_counter() - t:.1f}s)")
+        if w.n_tokens <= (1 << 20):
+            t = time.perf_counter()
+            cpu["all_cores"] = cpu_baseline_all_cores(w, n0, args.cpu_budget, total)
+            log(f"[bench] cpu baseline, {cpu['all_cores']['cores']} processes: {cpu['all_cores']['value']:.4f} "
+                f"queries/s ({time.perf_counter() - t:.1f}s)")
 
     rec = {
         "metric": METRIC,

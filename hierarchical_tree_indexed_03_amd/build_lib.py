@@ -1,6 +1,6 @@
 """Compiles the HIP sources under csrc/ into libzha.so (gfx950) next to this file.
 
-    python -m hierarchical_tree_indexed_03_amd.build_lib
+    python -m hierarchical_tree_indexed_03_amd.build_lib [--variant=debug|asan]
 """
 from __future__ import annotations
 
@@ -16,6 +16,18 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libzha.so")
 PROBE_OUT = os.path.join(HERE, "libzha_probe.so")   # benchmark-only measurement kernels
 OBJDIR = os.path.join(HERE, "_build")
+# variants: the same sources with the device invariant checks compiled in (-DZHA_DEBUG), and
+# the host side built with AddressSanitizer and UndefinedBehaviorSanitizer (device code as
+# usual) for the host-validation tests
+VARIANTS = {
+    "release": dict(out=OUT, objdir=OBJDIR, flags=[], link=[]),
+    "debug": dict(out=os.path.join(HERE, "libzha_debug.so"), objdir=os.path.join(HERE, "_build_debug"),
+                  flags=["-DZHA_DEBUG"], link=[]),
+    "asan": dict(out=os.path.join(HERE, "libzha_asan.so"), objdir=os.path.join(HERE, "_build_asan"),
+                 flags=["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                        "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"],
+                 link=["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]),
+}
 ARCH = os.environ.get("ZHA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -38,14 +50,18 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose: bool = False, variant: str = "release") -> str:
+    """Compiles every source of csrc/ into the variant's library (and, for the release
+    variant, the probe library); returns the library path."""
+    var = VARIANTS[variant]
+    objdir, out = var["objdir"], var["out"]
+    os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
     objs = []
 
     def compile_one(src):
-        obj = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
-        cmd = [cc, *FLAGS, "-c", src, "-o", obj]
+        obj = os.path.join(objdir, os.path.basename(src)[:-4] + ".o")
+        cmd = [cc, *FLAGS, *var["flags"], "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -55,12 +71,14 @@ def build(verbose: bool = False) -> str:
 
     with cf.ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
         objs = list(ex.map(compile_one, sources()))
-    tmp = OUT + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    tmp = out + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *var["link"], "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+    if variant != "release":
+        return out
     probe_src = os.path.join(CSRC, "probe", "probe.hip")
     tmp = PROBE_OUT + ".tmp"
     cmd = [cc, *FLAGS, "-shared", "-fPIC", "-o", tmp, probe_src]
@@ -72,4 +90,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    variant = next((a.split("=", 1)[1] for a in sys.argv[1:] if a.startswith("--variant=")), "release")
+    print(build(verbose="-v" in sys.argv, variant=variant))

@@ -104,6 +104,7 @@ __device__ __forceinline__ bool attn_work(const AttnArgs& a, int& kv, int& split
       if (x < sk) {
         kv = k;
         split = x;
+        ZHA_CHECK(a.dev, x < MAX_SPLITS, CHK_SPLITS);
         fb = (int64_t)x * ch;
         fe = min(fb + ch, (int64_t)a.dev.cnt[k] * a.b);
         return true;
@@ -171,6 +172,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
       } else {
         const int64_t e = f / a.b;
         const int64_t t = (int64_t)gnode[e] * a.b + (f - e * a.b);
+        ZHA_CHECK(a.dev, gnode[e] >= 0 && (int64_t)gnode[e] * a.b < a.N, CHK_TOKEN_RANGE);
         if (t < a.N) { tok = t; mk = gmask[e]; }
       }
     }
@@ -347,6 +349,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
       } else {
         const int64_t e = f / a.b;
         const int64_t t = (int64_t)gnode[e] * a.b + (f - e * a.b);
+        ZHA_CHECK(a.dev, gnode[e] >= 0 && (int64_t)gnode[e] * a.b < a.N, CHK_TOKEN_RANGE);
         if (t < a.N) { tok = t; mk = gmask[e]; }
       }
     }

@@ -50,6 +50,24 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, uint32_t scale_byte) {
   return m | (x < 0.f ? 8u : 0u);
 }
 
+// Device invariant checks, compiled in with -DZHA_DEBUG: a failed check sets its bit in the
+// handle's check word (read and cleared by zha_debug_check); nothing traps.
+enum CheckBit {
+  CHK_LIST_SIZE = 0,     // a union list longer than its level's node capacity
+  CHK_NODE_RANGE = 1,    // a union-list node id outside the level
+  CHK_CAND_RANGE = 2,    // a boundary-bin candidate past its list's capacity
+  CHK_EXPAND_RANGE = 3,  // an expanded list past the next level's capacity
+  CHK_TOKEN_RANGE = 4,   // an attended token at or past N
+  CHK_SPLITS = 5,        // attention splits past MAX_SPLITS
+  CHK_TD_SIZE = 6,       // a top-down level larger than TD_MAX
+};
+#ifdef ZHA_DEBUG
+#define ZHA_CHECK(devref, cond, bit) \
+  do { if (!(cond)) atomicOr((devref).err, 1u << (bit)); } while (0)
+#else
+#define ZHA_CHECK(devref, cond, bit) do { } while (0)
+#endif
+
 // Order-preserving map float -> uint32 (a < b  <=>  key(a) < key(b)).
 __device__ __forceinline__ uint32_t f2key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -137,6 +155,7 @@ struct Dev {
   int32_t* cand;            // [Hq][ncap[1]]
   float* qf;                // [Hq][D] sigma * q in fp32
   float* apart;             // [Hq][MAX_SPLITS][D + 2] attention partials (m, l, o)
+  uint32_t* err;            // invariant-check bits (debug builds)
 };
 
 }  // namespace zha

@@ -104,6 +104,7 @@ __global__ __launch_bounds__(256) void route_expand_emit_kernel(RouteArgs a) {
   }
   const int32_t total = total_s;
   const int64_t ocap = a.dev.ncap[out_lv];
+  ZHA_CHECK(a.dev, (int64_t)base + total <= ocap, CHK_EXPAND_RANGE);
   int32_t* onode = a.dev.node[out_lv] + kv * ocap + base;
   uint32_t* omask = a.dev.mask[out_lv] + kv * ocap + base;
   if (lv == 1) {

@@ -101,6 +101,7 @@ __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
   float* out = a.dev.score[lv] + (int64_t)kv * GMAX * cap;
   float* W = stg[wave];
   const int g = a.g;
+  ZHA_CHECK(a.dev, cnt <= cap, CHK_LIST_SIZE);
 
   float qa[NI][4];
 #pragma unroll
@@ -124,6 +125,7 @@ __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
     const bool ok = t < ntiles && e < cnt;
     rmk = (ok && !dense) ? masks[e] : 0u;
     rnid = (ok && (dense || rmk != 0u)) ? (dense ? (int32_t)e : nodes[e]) : -1;
+    ZHA_CHECK(a.dev, rnid < a.nl[lv], CHK_NODE_RANGE);
     rcj = rnid >= 0 ? C[(int64_t)rnid * R + plane] : -INFINITY;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
@@ -526,6 +528,7 @@ __global__ __launch_bounds__(256) void route_score_keys_kernel(RouteArgs a) {
         const bool ok = (t0 + u) < ntiles && e < cnt;
         mk[u][n] = ok ? masks[e] : 0u;
         nd[u][n] = mk[u][n] != 0u ? nodes[e] : -1;
+        ZHA_CHECK(a.dev, nd[u][n] < a.nl[lv], CHK_NODE_RANGE);
       }
     }
   };

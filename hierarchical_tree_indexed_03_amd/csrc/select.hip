@@ -220,6 +220,7 @@ __global__ __launch_bounds__(SEL_THREADS) void route_classify_kernel(RouteArgs a
             uint32_t base = 0;
             if (lane == 0) base = atomicAdd(&a.dev.qs[lv * a.hq + kv * g + gi].ncand, wcnt[gi]);
             base = __shfl(base, 0);
+            ZHA_CHECK(a.dev, (int64_t)base + wcnt[gi] <= ccap, CHK_CAND_RANGE);
             int32_t* dst = a.dev.cand + (int64_t)(kv * g + gi) * ccap + base;
             for (uint32_t i = lane; i < wcnt[gi]; i += 64) dst[i] = stage[wave][gi][i];
             wave_sync_lds();
@@ -244,6 +245,7 @@ __global__ __launch_bounds__(SEL_THREADS) void route_classify_kernel(RouteArgs a
   for (int gi = 0; gi < g; ++gi) {
     uint32_t off = bbase[gi];
     for (int w = 0; w < wave; ++w) off += wcnt_s[w][gi];
+    ZHA_CHECK(a.dev, (int64_t)off + wcnt_s[wave][gi] <= ccap, CHK_CAND_RANGE);
     int32_t* dst = a.dev.cand + (int64_t)(kv * g + gi) * ccap + off;
     for (uint32_t i = lane; i < wcnt_s[wave][gi]; i += 64) dst[i] = stage[wave][gi][i];
   }

@@ -86,6 +86,7 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
     const int n = (int)a.nl[lv];
     const int nw = (n + 31) >> 5;
     const bool top = lv == a.level;
+    ZHA_CHECK(a.dev, n <= TD_MAX, CHK_TD_SIZE);
     const int64_t cap = a.dev.ncap[lv];
     const float* S = a.dev.score[lv] + ((int64_t)kv * GMAX + gi) * cap;
     uint32_t* gbits = a.dev.tdbits + (((int64_t)lv * a.hq + hq) * 2) * TD_WORDS;   // [frontier | kept]

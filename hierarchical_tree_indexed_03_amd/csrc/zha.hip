@@ -172,6 +172,7 @@ size_t layout(const zha_config& c, char* base, Dev* dev) {
   d.cand = (int32_t*)take((size_t)(Q * d.ncap[1]) * 4);
   d.qf = (float*)take((size_t)(Q * D) * 4);
   d.apart = (float*)take((size_t)(Q * MAX_SPLITS * (D + 2)) * 4);
+  d.err = (uint32_t*)take(256);
   if (dev) *dev = d;
   return (off + 255) & ~(size_t)255;
 }
@@ -483,6 +484,12 @@ zha_status zha_tree_build(zha_tree* t, void* k_cache, void* v_cache, int64_t n_t
   if (n_tokens < 1) return fail(ZHA_E_INVALID, "n_tokens %lld < 1", (long long)n_tokens);
   if (n_tokens > t->cfg.capacity)
     return fail(ZHA_E_CAPACITY, "n_tokens %lld > capacity %lld", (long long)n_tokens, (long long)t->cfg.capacity);
+#ifdef ZHA_DEBUG
+  {
+    hipError_t e = hipMemsetAsync(t->dev.err, 0, 4, stream);   // debug builds: checks start clear
+    if (e != hipSuccess) return hip_fail(e, "check word");
+  }
+#endif
   zha_status zs = enqueue_build(t, k_cache, ref_queries, 0, n_tokens, stream);
   if (zs != ZHA_OK) return zs;
   t->K = k_cache;
@@ -937,6 +944,27 @@ zha_status zha_set_top_p_levels(zha_tree* t, const float* p_levels) {
         return fail(ZHA_E_INVALID, "p of level %d is %g, outside (0, 1]", l + 1, p_levels[l]);
   for (int l = 1; l <= L; ++l) t->top_p[l] = p_levels ? p_levels[l - 1] : t->cfg.top_p;
   return ZHA_OK;
+}
+
+zha_status zha_debug_check(zha_tree* t, uint32_t* flags, hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!flags) return fail(ZHA_E_INVALID, "flags is null");
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, t->dev.err, 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e == hipSuccess) e = hipMemsetAsync(t->dev.err, 0, 4, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "check word");
+  *flags = v;
+  return ZHA_OK;
+}
+
+int32_t zha_debug_checks_compiled(void) {
+#ifdef ZHA_DEBUG
+  return 1;
+#else
+  return 0;
+#endif
 }
 
 int64_t zha_num_tokens(const zha_tree* t) { return t ? t->N : -1; }

@@ -61,6 +61,8 @@ def _load() -> ctypes.CDLL:
         "zha_set_top_p_levels": (I32, [P, ctypes.POINTER(ctypes.c_float)]),
         "zha_fit_workspace_bytes": (SZ, [ctypes.POINTER(zha_config), I64, I64]),
         "zha_fit_step": (I32, [P, P, P, I64, P, P, I64, ctypes.c_float, P, P, P, SZ, P]),
+        "zha_debug_check": (I32, [P, ctypes.POINTER(ctypes.c_uint32), P]),
+        "zha_debug_checks_compiled": (I32, []),
         "zha_num_tokens": (I64, [P]),
         "zha_destroy": (I32, [P]),
         "zha_status_string": (ctypes.c_char_p, [I32]),
@@ -77,6 +79,7 @@ EXPORTED = ("zha_workspace_bytes", "zha_level1_key_form", "zha_create", "zha_tre
             "zha_tree_append_n", "zha_decode", "zha_prefill",
             "zha_decode_dense", "zha_decode_dense_static", "zha_debug_level", "zha_debug_router_planes", "zha_debug_trace", "zha_debug_route_level",
             "zha_profile_start", "zha_profile_stop", "zha_set_top_p_levels", "zha_fit_workspace_bytes", "zha_fit_step",
+            "zha_debug_check", "zha_debug_checks_compiled",
             "zha_num_tokens", "zha_destroy", "zha_status_string", "zha_last_error")
 
 
@@ -203,6 +206,16 @@ def zha_fit_step(t, k_cache, v_cache, n_tokens: int, ref_queries, q, nq: int, lr
                  fit_ws_bytes: int, stream=None):
     _check(_lib.zha_fit_step(t, _p(k_cache), _p(v_cache), n_tokens, _p(ref_queries), _p(q), nq, lr, _p(loss),
                              _p(grad), _p(fit_ws), fit_ws_bytes, _s(stream)))
+
+
+def zha_debug_check(t, stream=None) -> int:
+    v = ctypes.c_uint32()
+    _check(_lib.zha_debug_check(t, ctypes.byref(v), _s(stream)))
+    return int(v.value)
+
+
+def zha_debug_checks_compiled() -> int:
+    return int(_lib.zha_debug_checks_compiled())
 
 
 def zha_num_tokens(t) -> int:

@@ -281,6 +281,17 @@ zha_status zha_debug_route_level(zha_tree* t, int32_t level, const void* q,
 zha_status zha_profile_start(zha_tree* t, const char* key_prefix);
 zha_status zha_profile_stop(zha_tree* t, double* total_ms, int64_t* launches);
 
+/* Device invariant checks.  A library built with -DZHA_DEBUG (libzha_debug.so) compiles
+ * checks into the same kernels: a list longer than its level's capacity, a list node outside
+ * its level, a candidate or expanded list past its capacity, an attended block past N,
+ * attention splits past their maximum, a top-down level past its size limit.  A failed check
+ * sets its bit (bits 0..6 in that order) in the handle's check word; nothing traps.
+ * zha_debug_check copies the word into *flags (host) and clears it; synchronises `stream`.
+ * The word starts clear at each zha_tree_build in debug builds; in other builds it stays 0.
+ * zha_debug_checks_compiled returns 1 in a debug build, else 0. */
+zha_status zha_debug_check(zha_tree* t, uint32_t* flags, hipStream_t stream);
+int32_t zha_debug_checks_compiled(void);
+
 /* Tokens currently in the tree (host-side count; no synchronisation). */
 int64_t zha_num_tokens(const zha_tree* t);
 
