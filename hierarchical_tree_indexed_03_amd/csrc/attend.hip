@@ -70,10 +70,14 @@ __device__ __forceinline__ void split_range(int64_t F, int splits, int split, in
 // one resident wave (a workgroup past it would run as a tail of one whole chunk), and it
 // never gives one head more than MAX_SPLITS.  Every kernel derives it from the level-0
 // counts the same way.
+__device__ __forceinline__ const int32_t* qcnt(const AttnArgs& a) {
+  return a.dev.cnt + (int64_t)blockIdx.y * a.c_stride;   // this launch row's query
+}
 __device__ __forceinline__ int64_t routed_chunk(const AttnArgs& a) {
   int64_t F = 0, Fmax = 0;
+  const int32_t* cnt = qcnt(a);
   for (int k = 0; k < a.hkv; ++k) {
-    const int64_t f = (int64_t)a.dev.cnt[k] * a.b;
+    const int64_t f = (int64_t)cnt[k] * a.b;
     F += f;
     Fmax = f > Fmax ? f : Fmax;
   }
@@ -82,7 +86,7 @@ __device__ __forceinline__ int64_t routed_chunk(const AttnArgs& a) {
   return c1 > c2 ? c1 : c2;
 }
 __device__ __forceinline__ int routed_splits(const AttnArgs& a, int kv, int64_t chunk) {
-  const int64_t f = (int64_t)a.dev.cnt[kv] * a.b;
+  const int64_t f = (int64_t)qcnt(a)[kv] * a.b;
   return (int)((f + chunk - 1) / chunk);
 }
 
@@ -106,7 +110,7 @@ __device__ __forceinline__ bool attn_work(const AttnArgs& a, int& kv, int& split
         split = x;
         ZHA_CHECK(a.dev, x < MAX_SPLITS, CHK_SPLITS);
         fb = (int64_t)x * ch;
-        fe = min(fb + ch, (int64_t)a.dev.cnt[k] * a.b);
+        fe = min(fb + ch, (int64_t)qcnt(a)[k] * a.b);
         return true;
       }
       x -= sk;
@@ -145,12 +149,14 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   const uint32_t* gmask = nullptr;
   if constexpr (!DENSE) {
     const int64_t cap0 = a.dev.ncap[0];
-    gnode = a.dev.node[0] + kv * cap0;
-    gmask = a.dev.mask[0] + kv * cap0;
+    gnode = a.dev.node[0] + (int64_t)blockIdx.y * a.l_stride + kv * cap0;
+    gmask = a.dev.mask[0] + (int64_t)blockIdx.y * a.l_stride + kv * cap0;
   }
+  const int64_t qy = DENSE ? 0 : (int64_t)blockIdx.y;   // query of this launch row
+  const int64_t qN = a.N + qy * a.n_step;                // tokens the query may attend
 
   Qk<TIn, D> qk;
-  qk.load_q((const TIn*)a.q + (int64_t)kv * g * D, g, col, kg);
+  qk.load_q((const TIn*)a.q + qy * a.q_stride + (int64_t)kv * g * D, g, col, kg);
 
   float m = -INFINITY, l = 0.f;               // softmax state of head `col`
   float o[GMAX][VEC];
@@ -172,8 +178,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
       } else {
         const int64_t e = f / a.b;
         const int64_t t = (int64_t)gnode[e] * a.b + (f - e * a.b);
-        ZHA_CHECK(a.dev, gnode[e] >= 0 && (int64_t)gnode[e] * a.b < a.N, CHK_TOKEN_RANGE);
-        if (t < a.N) { tok = t; mk = gmask[e]; }
+        ZHA_CHECK(a.dev, gnode[e] >= 0 && (int64_t)gnode[e] * a.b < qN, CHK_TOKEN_RANGE);
+        if (t < qN) { tok = t; mk = gmask[e]; }
       }
     }
   };
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
         O += Ol[w][h][d] * sc;
       }
     }
-    float* pp = a.dev.apart + ((int64_t)(kv * g + h) * a.pstride + split) * (D + 2);
+    float* pp = a.dev.apart + qy * a.p_stride + ((int64_t)(kv * g + h) * a.pstride + split) * (D + 2);
     if (d == 0) { pp[0] = M; pp[1] = L; }
     pp[2 + d] = O;
   }
@@ -326,12 +332,14 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
   const uint32_t* gmask = nullptr;
   if constexpr (!DENSE) {
     const int64_t cap0 = a.dev.ncap[0];
-    gnode = a.dev.node[0] + kv * cap0;
-    gmask = a.dev.mask[0] + kv * cap0;
+    gnode = a.dev.node[0] + (int64_t)blockIdx.y * a.l_stride + kv * cap0;
+    gmask = a.dev.mask[0] + (int64_t)blockIdx.y * a.l_stride + kv * cap0;
   }
+  const int64_t qy = DENSE ? 0 : (int64_t)blockIdx.y;   // query of this launch row
+  const int64_t qN = a.N + qy * a.n_step;                // tokens the query may attend
 
   Qk<bf16_t, D> qk;
-  qk.load_q((const bf16_t*)a.q + (int64_t)kv * g * D, g, col, kg);
+  qk.load_q((const bf16_t*)a.q + qy * a.q_stride + (int64_t)kv * g * D, g, col, kg);
 
   float m = -INFINITY, l = 0.f;               // softmax state of head `col`
   f32x4 acc[NM];
@@ -349,8 +357,8 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
       } else {
         const int64_t e = f / a.b;
         const int64_t t = (int64_t)gnode[e] * a.b + (f - e * a.b);
-        ZHA_CHECK(a.dev, gnode[e] >= 0 && (int64_t)gnode[e] * a.b < a.N, CHK_TOKEN_RANGE);
-        if (t < a.N) { tok = t; mk = gmask[e]; }
+        ZHA_CHECK(a.dev, gnode[e] >= 0 && (int64_t)gnode[e] * a.b < qN, CHK_TOKEN_RANGE);
+        if (t < qN) { tok = t; mk = gmask[e]; }
       }
     }
   };
@@ -467,7 +475,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
         O += Ol[(w * GMAX + h) * D + d] * sw;
       }
     }
-    float* pp = a.dev.apart + ((int64_t)(kv * g + h) * a.pstride + split) * (D + 2);
+    float* pp = a.dev.apart + qy * a.p_stride + ((int64_t)(kv * g + h) * a.pstride + split) * (D + 2);
     if (d == 0) { pp[0] = M; pp[1] = L; }
     pp[2 + d] = O;
   }
@@ -483,7 +491,8 @@ __global__ __launch_bounds__(512) void combine_kernel(AttnArgs a, int32_t* stats
   __shared__ float S0;
   const int hq = blockIdx.x, kv = hq / a.g, gi = hq % a.g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float* base = a.dev.apart + (int64_t)hq * a.pstride * (D + 2);
+  const int64_t qy = blockIdx.y;              // query of this launch row (0 for a decode)
+  const float* base = a.dev.apart + qy * a.p_stride + (int64_t)hq * a.pstride * (D + 2);
   // splits that own tokens (same chunking as the attention kernel)
   int S = 0;
   if constexpr (DENSE) {
@@ -508,15 +517,15 @@ __global__ __launch_bounds__(512) void combine_kernel(AttnArgs a, int32_t* stats
   if constexpr (!DENSE) {
     if (a.keep_sink) {
       const int64_t cap0 = a.dev.ncap[0];
-      const bool kept0 = a.dev.cnt[kv] > 0 && a.dev.node[0][kv * cap0] == 0 &&
-                         ((a.dev.mask[0][kv * cap0] >> gi) & 1u);
+      const int64_t l0 = qy * a.l_stride + kv * cap0;
+      const bool kept0 = qcnt(a)[kv] > 0 && a.dev.node[0][l0] == 0 && ((a.dev.mask[0][l0] >> gi) & 1u);
       add_sink = !kept0;
     }
   }
   const TIn* K0 = (const TIn*)a.K + (int64_t)kv * a.cap * D;
   const TIn* V0 = (const TIn*)a.V + (int64_t)kv * a.cap * D;
   if (add_sink && wave == NW - 1) {
-    const TIn* qh = (const TIn*)a.q + (int64_t)hq * D;
+    const TIn* qh = (const TIn*)a.q + qy * a.q_stride + (int64_t)hq * D;
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < VD; ++i) part += to_f32(qh[lane * VD + i]) * to_f32(K0[lane * VD + i]);
@@ -580,9 +589,9 @@ __global__ __launch_bounds__(512) void combine_kernel(AttnArgs a, int32_t* stats
       Ov = Ov * sa + to_f32(V0[d]) * sb;
       L = L * sa + sb;
     }
-    a.out[(int64_t)hq * D + d] = L > 0.f ? Ov / L : 0.f;
+    a.out[qy * a.o_stride + (int64_t)hq * D + d] = L > 0.f ? Ov / L : 0.f;
   }
-  if (stats && hq == 0) {
+  if (stats && hq == 0 && qy == 0) {
     for (int i = threadIdx.x; i < (levels + 1) * a.hkv; i += 512) {
       const int row = i / a.hkv, k = i % a.hkv;
       const int lvl = row < levels ? levels - row : 0;
@@ -638,6 +647,25 @@ int attend_resident_splits(bool bf16, int D, bool dense, int hkv) {
   }
 #undef ZHA_CASE
   return 1;
+}
+
+template <typename TIn, int D>
+static hipError_t launch_attend_batch_t(const AttnArgs& a, int nq, hipStream_t st) {
+  hipLaunchKernelGGL((attend_kernel<TIn, D, false>), dim3((unsigned)(a.splits * a.hkv), (unsigned)nq), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((combine_kernel<TIn, D, false>), dim3((unsigned)a.hq, (unsigned)nq), dim3(512), 0, st, a,
+                     (int32_t*)nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_batch(const AttnArgs& a, bool bf16, int D, int nq, hipStream_t st) {
+  if (bf16) {
+    if (D == 64) return launch_attend_batch_t<bf16_t, 64>(a, nq, st);
+    if (D == 128) return launch_attend_batch_t<bf16_t, 128>(a, nq, st);
+  } else {
+    if (D == 64) return launch_attend_batch_t<float, 64>(a, nq, st);
+    if (D == 128) return launch_attend_batch_t<float, 128>(a, nq, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attend(const AttnArgs& a, bool bf16, int D, bool dense, hipStream_t st) {

@@ -83,7 +83,48 @@ struct AttnArgs {
   int32_t keep_sink;
   float sigma;
   float* out;         // [Hq][D]
+  // several queries in one routed launch (grid.y = query; a decode has one and zero strides):
+  // query y reads q + y * q_stride, its gather list at dev.node[0] / dev.mask[0] +
+  // y * l_stride and its counts at dev.cnt + y * c_stride, attends tokens below
+  // N + y * n_step, and writes its partials at dev.apart + y * p_stride and its output at
+  // out + y * o_stride
+  int64_t q_stride, l_stride, p_stride, o_stride;
+  int32_t c_stride, n_step;
 };
+
+// Batched causal prefill (prefill.hip): mb queries at positions N0 .. N0 + mb - 1, query i
+// routed over the tree of tokens [0, N0 + i]; pair p = i * g + gi is query i's head gi.
+struct PrefillArgs {
+  Dev dev;
+  const void* K;          // [Hkv][cap][D] cache dtype
+  const void* refs;       // [Hkv][R][D]
+  const void* q;          // [mb][Hq][D] cache dtype (this sub-batch)
+  int64_t cap;
+  int64_t N0;             // tokens before the sub-batch
+  int32_t mb, mbmax, P, hkv, hq, g, b, levels, R, D;
+  int32_t q_bf16;
+  float sigma;
+  float top_p[MAXL + 1];
+  int64_t nl[MAXL + 1];   // nodes per level of the tree over N0 + mb tokens
+  float* Qf;              // [Hkv][P][D] sigma * q in fp32
+  float* X;               // [Hkv][mbmax][levels + 1][R][D + 2] per query and level: its rightmost node
+                          // (s, c, LSE per plane) over the tokens up to its own
+  float* S;               // scores, level l at S + soff[l]: [Hkv][P][sstride[l]]
+  int64_t soff[MAXL + 1], sstride[MAXL + 1];
+  uint32_t* KB;           // kept bitmaps, level l at KB + koff[l]: [Hkv][P][kstride[l]] words
+  int64_t koff[MAXL + 1], kstride[MAXL + 1];
+  int32_t* L0node;        // [mbmax][Hkv][ncap1] gather list of each query (kept level-1 blocks)
+  uint32_t* L0mask;       // the heads of the query that kept each block
+  int32_t* cnt0;          // [mbmax][Hkv]
+};
+hipError_t launch_prefill_prefix(const PrefillArgs& a, bool bf16, int D, int R, hipStream_t st);
+hipError_t launch_prefill_qprep(const PrefillArgs& a, bool bf16, int D, hipStream_t st);
+hipError_t launch_prefill_score(const PrefillArgs& a, int D, int R, hipStream_t st);
+hipError_t launch_prefill_tail(const PrefillArgs& a, int D, int R, hipStream_t st);
+hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_prefill_gather(const PrefillArgs& a, hipStream_t st);
+// Routed attention and combine for a.nq... queries of one launch (grid.y = query).
+hipError_t launch_attend_batch(const AttnArgs& a, bool bf16, int D, int nq, hipStream_t st);
 
 // One fitting step of the reference queries (fit.hip): buffers in the caller's fit
 // workspace, the tree's planes and log masses in dev.

@@ -1,4 +1,5 @@
 // Host side of the ZHA C ABI: argument validation, workspace layout, launch sequencing.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -38,6 +39,9 @@ struct zha_tree {
   RouteArgs td_args;
   bool td_valid;
   bool td_lists;
+  // the last sub-batch of zha_prefill_batched (its buffers are in the caller's workspace)
+  PrefillArgs pf_args;
+  bool pf_valid;
 };
 
 namespace {
@@ -669,6 +673,207 @@ zha_status zha_prefill(zha_tree* t, const void* k_new, const void* v_new, const 
                     stats ? stats + (size_t)i * (c.levels + 1) * c.num_kv_heads : nullptr, stream);
     if (zs != ZHA_OK) return zs;
   }
+  return ZHA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int PF_MAX_BATCH = 128;   // queries per sub-batch
+constexpr int PF_SPLITS = 16;       // attention splits per query and KV head, at most
+
+// Lays out the batched-prefill workspace for sub-batches of up to `mbmax` queries; with
+// base == nullptr only the size is computed.  Level strides follow the tree's node
+// capacities, so every row starts 256-byte aligned.
+size_t prefill_layout(const zha_config& c, int mbmax, char* base, PrefillArgs* out, float** apart, int* pstride) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    off = (off + 255) & ~(size_t)255;
+    char* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  };
+  PrefillArgs a;
+  memset(&a, 0, sizeof a);
+  const int64_t H = c.num_kv_heads, Q = c.num_q_heads, R = c.num_ref, D = c.head_dim;
+  const int L = c.levels;
+  const int64_t P = (int64_t)mbmax * (Q / H);
+  int64_t ncap[MAXL + 1] = {0};
+  for (int l = 1; l <= L; ++l) ncap[l] = ceil_div(nodes_at(c, l, c.capacity), 64) * 64;
+  a.Qf = (float*)take((size_t)(H * P * D) * 4);
+  a.X = (float*)take((size_t)(H * mbmax * (L + 1) * R * (D + 2)) * 4);
+  int64_t so = 0, ko = 0;
+  for (int l = 1; l <= L; ++l) {
+    a.sstride[l] = ncap[l];
+    a.soff[l] = so;
+    so += H * P * ncap[l];
+    a.kstride[l] = ceil_div(ncap[l], 32 * 64) * 64;
+    a.koff[l] = ko;
+    ko += H * P * a.kstride[l];
+  }
+  a.S = (float*)take((size_t)so * 4);
+  a.KB = (uint32_t*)take((size_t)ko * 4);
+  a.L0node = (int32_t*)take((size_t)(mbmax * H * ncap[1]) * 4);
+  a.L0mask = (uint32_t*)take((size_t)(mbmax * H * ncap[1]) * 4);
+  a.cnt0 = (int32_t*)take((size_t)(mbmax * H) * 4);
+  const int ps = (int)std::min<int64_t>(MAX_SPLITS, (int64_t)PF_SPLITS * H);
+  float* ap = (float*)take((size_t)(mbmax * Q * ps * (D + 2)) * 4);
+  a.mbmax = mbmax;
+  if (out) *out = a;
+  if (apart) *apart = ap;
+  if (pstride) *pstride = ps;
+  return (off + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t zha_prefill_workspace_bytes(const zha_config* cfg, int32_t batch) {
+  if (validate(cfg) != ZHA_OK || batch < 1 || batch > PF_MAX_BATCH) return 0;
+  return prefill_layout(*cfg, batch, nullptr, nullptr, nullptr, nullptr);
+}
+
+zha_status zha_prefill_batched(zha_tree* t, const void* k_new, const void* v_new, const void* q, float* out,
+                               int64_t m, int32_t batch, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!t->built) return fail(ZHA_E_STATE, "prefill before build");
+  if (!k_new || !v_new || !q || !out) return fail(ZHA_E_INVALID, "null k_new, v_new, q or out");
+  if ((uintptr_t)q % 16) return fail(ZHA_E_INVALID, "q must be 16-byte aligned");
+  if (m < 1) return fail(ZHA_E_INVALID, "m %lld < 1", (long long)m);
+  if (batch < 1 || batch > PF_MAX_BATCH) return fail(ZHA_E_INVALID, "batch %d outside 1..%d", batch, PF_MAX_BATCH);
+  if (!workspace) return fail(ZHA_E_INVALID, "workspace is null");
+  if ((uintptr_t)workspace % 256) return fail(ZHA_E_INVALID, "workspace not 256-byte aligned");
+  const zha_config& c = t->cfg;
+  const size_t need = prefill_layout(c, batch, nullptr, nullptr, nullptr, nullptr);
+  if (workspace_bytes < need)
+    return fail(ZHA_E_WORKSPACE, "prefill workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (t->N + m > c.capacity)
+    return fail(ZHA_E_CAPACITY, "%lld + %lld tokens > capacity %lld", (long long)t->N, (long long)m,
+                (long long)c.capacity);
+  PrefillArgs a;
+  float* apart = nullptr;
+  int pstride = 0;
+  prefill_layout(c, batch, (char*)workspace, &a, &apart, &pstride);
+  const bool bf16 = c.dtype == ZHA_BF16;
+  const int D = c.head_dim, R = c.num_ref, H = c.num_kv_heads, Q = c.num_q_heads, g = Q / H;
+  const size_t es = bf16 ? 2 : 4, row = (size_t)D * es;
+  a.dev = t->dev;
+  a.K = t->K;
+  a.refs = t->refs;
+  a.cap = c.capacity;
+  a.hkv = H;
+  a.hq = Q;
+  a.g = g;
+  a.b = c.block;
+  a.levels = c.levels;
+  a.R = R;
+  a.D = D;
+  a.q_bf16 = bf16 ? 1 : 0;
+  a.sigma = 1.0f / sqrtf((float)D);
+  for (int l = 0; l <= MAXL; ++l) a.top_p[l] = t->top_p[l];
+  const int resident = attend_resident_splits(bf16, D, false, H);
+  t->pf_valid = false;
+  for (int64_t s0 = 0; s0 < m; s0 += batch) {
+    const int mb = (int)std::min<int64_t>(batch, m - s0);
+    const int64_t N0 = t->N;
+    // the sub-batch's tokens: rows s0 .. s0+mb-1 of each KV head's [m][d] chunk
+    hipError_t e = hipMemcpy2DAsync((char*)t->K + (size_t)N0 * row, (size_t)c.capacity * row,
+                                    (const char*)k_new + (size_t)s0 * row, (size_t)m * row, (size_t)mb * row, H,
+                                    hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync((char*)t->V + (size_t)N0 * row, (size_t)c.capacity * row,
+                           (const char*)v_new + (size_t)s0 * row, (size_t)m * row, (size_t)mb * row, H,
+                           hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "cache row copy");
+    zha_status zs = enqueue_build(t, t->K, t->refs, N0, N0 + mb, stream);
+    if (zs != ZHA_OK) return zs;
+    t->N = N0 + mb;
+    a.N0 = N0;
+    a.mb = mb;
+    a.P = mb * g;
+    a.q = (const char*)q + (size_t)s0 * Q * row;
+    for (int l = 1; l <= c.levels; ++l) a.nl[l] = nodes_at(c, l, N0 + mb);
+    a.nl[0] = a.nl[1];
+    {
+      ProfScope ps(t, "prefill_prep", stream);
+      e = launch_prefill_qprep(a, bf16, D, stream);
+      if (e == hipSuccess) e = launch_prefill_prefix(a, bf16, D, R, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill prep launch");
+    {
+      ProfScope ps(t, "prefill_score", stream);
+      e = launch_prefill_score(a, D, R, stream);
+      if (e == hipSuccess) e = launch_prefill_tail(a, D, R, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill score launch");
+    {
+      ProfScope ps(t, "prefill_select", stream);
+      e = launch_prefill_select(a, stream);
+      if (e == hipSuccess) e = launch_prefill_gather(a, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill select launch");
+    t->pf_args = a;
+    t->pf_valid = true;
+    AttnArgs at;
+    memset(&at, 0, sizeof at);
+    at.dev = t->dev;
+    at.dev.node[0] = a.L0node;
+    at.dev.mask[0] = a.L0mask;
+    at.dev.cnt = a.cnt0;
+    at.dev.apart = apart;
+    at.K = t->K;
+    at.V = t->V;
+    at.q = a.q;
+    at.cap = c.capacity;
+    at.N = N0 + 1;
+    at.n_step = 1;
+    at.hkv = H;
+    at.hq = Q;
+    at.g = g;
+    at.b = c.block;
+    at.splits = std::max(1, std::min(PF_SPLITS, resident / mb));
+    at.pstride = pstride;
+    at.keep_sink = c.keep_sink;
+    at.sigma = a.sigma;
+    at.out = out + (size_t)s0 * Q * D;
+    at.q_stride = (int64_t)Q * D;
+    at.l_stride = (int64_t)H * t->dev.ncap[1];
+    at.p_stride = (int64_t)Q * pstride * (D + 2);
+    at.o_stride = (int64_t)Q * D;
+    at.c_stride = H;
+    {
+      ProfScope ps(t, "prefill_attend", stream);
+      e = launch_attend_batch(at, bf16, D, mb, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  }
+  return ZHA_OK;
+}
+
+zha_status zha_debug_prefill_trace(zha_tree* t, int32_t level, float* scores, uint32_t* kept, float* own,
+                                   hipStream_t stream) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (!t->pf_valid) return fail(ZHA_E_STATE, "no batched prefill to trace");
+  const PrefillArgs& a = t->pf_args;
+  if (level < 1 || level > a.levels) return fail(ZHA_E_INVALID, "level %d outside 1..%d", level, a.levels);
+  const int64_t n = a.nl[level], nw = (n + 31) >> 5, rows = (int64_t)a.hkv * a.P;
+  hipError_t e = hipSuccess;
+  if (scores)
+    e = hipMemcpy2DAsync(scores, (size_t)n * 4, a.S + a.soff[level], (size_t)a.sstride[level] * 4, (size_t)n * 4,
+                         (size_t)rows, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess && kept)
+    e = hipMemcpy2DAsync(kept, (size_t)nw * 4, a.KB + a.koff[level], (size_t)a.kstride[level] * 4, (size_t)nw * 4,
+                         (size_t)rows, hipMemcpyDeviceToDevice, stream);
+  const int64_t node = (int64_t)a.R * (a.D + 2);
+  for (int kv = 0; own && e == hipSuccess && kv < a.hkv; ++kv)
+    e = hipMemcpy2DAsync(own + (int64_t)kv * a.mb * node, (size_t)node * 4,
+                         a.X + ((int64_t)kv * a.mbmax * (a.levels + 1) + level) * node,
+                         (size_t)(a.levels + 1) * node * 4, (size_t)node * 4, (size_t)a.mb, hipMemcpyDeviceToDevice,
+                         stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill trace copy");
   return ZHA_OK;
 }
 

@@ -52,6 +52,9 @@ def _load() -> ctypes.CDLL:
         "zha_decode_dense": (I32, [P, P, P, P]),
         "zha_decode_dense_static": (I32, [ctypes.POINTER(zha_config), P, P, I64, P, P, P]),
         "zha_prefill": (I32, [P, P, P, P, P, I64, P, P]),
+        "zha_prefill_workspace_bytes": (SZ, [ctypes.POINTER(zha_config), I32]),
+        "zha_prefill_batched": (I32, [P, P, P, P, P, I64, I32, P, SZ, P]),
+        "zha_debug_prefill_trace": (I32, [P, I32, P, P, P, P]),
         "zha_debug_level": (I32, [P, I32, P, P, P]),
         "zha_debug_router_planes": (I32, [P, I32, P, P, P]),
         "zha_debug_trace": (I32, [P, I32, I64, P, P, P, P, P, P]),
@@ -76,7 +79,8 @@ def _load() -> ctypes.CDLL:
 
 _lib = _load()
 EXPORTED = ("zha_workspace_bytes", "zha_level1_key_form", "zha_create", "zha_tree_build", "zha_tree_append",
-            "zha_tree_append_n", "zha_decode", "zha_prefill",
+            "zha_tree_append_n", "zha_decode", "zha_prefill", "zha_prefill_workspace_bytes", "zha_prefill_batched",
+            "zha_debug_prefill_trace",
             "zha_decode_dense", "zha_decode_dense_static", "zha_debug_level", "zha_debug_router_planes", "zha_debug_trace", "zha_debug_route_level",
             "zha_profile_start", "zha_profile_stop", "zha_set_top_p_levels", "zha_fit_workspace_bytes", "zha_fit_step",
             "zha_debug_check", "zha_debug_checks_compiled",
@@ -150,6 +154,19 @@ def zha_decode(t, q, out, stats=None, stream=None):
 
 def zha_prefill(t, k_new, v_new, q, out, m: int, stats=None, stream=None):
     _check(_lib.zha_prefill(t, _p(k_new), _p(v_new), _p(q), _p(out), int(m), _p(stats), _s(stream)))
+
+
+def zha_prefill_workspace_bytes(cfg: zha_config, batch: int) -> int:
+    return _lib.zha_prefill_workspace_bytes(ctypes.byref(cfg), batch)
+
+
+def zha_prefill_batched(t, k_new, v_new, q, out, m: int, batch: int, workspace, workspace_bytes: int, stream=None):
+    _check(_lib.zha_prefill_batched(t, _p(k_new), _p(v_new), _p(q), _p(out), m, batch, _p(workspace),
+                                    workspace_bytes, _s(stream)))
+
+
+def zha_debug_prefill_trace(t, level: int, scores, kept, own=None, stream=None):
+    _check(_lib.zha_debug_prefill_trace(t, level, _p(scores), _p(kept), _p(own), _s(stream)))
 
 
 def zha_decode_dense(t, q, out, stream=None):
@@ -278,6 +295,39 @@ class Tree:
             out = torch.empty(m, self.cfg.num_q_heads, self.cfg.head_dim, dtype=torch.float32, device=q.device)
         zha_prefill(self.handle, k_new, v_new, q, out, m, stats, stream)
         return out
+
+    def prefill_batched(self, k_new, v_new, q, batch: int, out=None, stream=None):
+        """Batched causal prefill: k_new, v_new [Hkv, m, d]; q [m, Hq, d]; ``batch`` queries
+        per sub-batch.  Returns out [m, Hq, d] float32.  The prefill workspace is kept on the
+        tree (grown when a larger batch needs more)."""
+        m = k_new.shape[1]
+        need = zha_prefill_workspace_bytes(self.cfg, batch)
+        if need == 0:
+            raise ValueError(f"no prefill workspace for batch={batch}")
+        ws = getattr(self, "_pf_ws", None)
+        if ws is None or ws.numel() < need:
+            ws = self._pf_ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if out is None:
+            out = torch.empty(m, self.cfg.num_q_heads, self.cfg.head_dim, dtype=torch.float32, device=q.device)
+        zha_prefill_batched(self.handle, k_new, v_new, q, out, m, batch, ws, ws.numel(), stream)
+        self._pf_last = (m - batch * ((m - 1) // batch), self.n_tokens)
+        return out
+
+    def prefill_trace(self, level: int):
+        """Scores [Hkv, P, n], kept bitmaps [Hkv, P, ceil(n/32)] (int32 words) and each
+        query's own rightmost node [Hkv, mb, R, d + 2] (s, c, LSE per plane) of the last
+        sub-batch of prefill_batched at ``level``, as CPU tensors, with (mb, N) of that
+        sub-batch."""
+        mb, n_end = self._pf_last
+        c = self.cfg
+        g = c.num_q_heads // c.num_kv_heads
+        n = -(-n_end // c.block ** level)
+        dev = self.workspace.device
+        scores = torch.empty(c.num_kv_heads, mb * g, n, dtype=torch.float32, device=dev)
+        kept = torch.empty(c.num_kv_heads, mb * g, (n + 31) // 32, dtype=torch.int32, device=dev)
+        own = torch.empty(c.num_kv_heads, mb, c.num_ref, c.head_dim + 2, dtype=torch.float32, device=dev)
+        zha_debug_prefill_trace(self.handle, level, scores, kept, own)
+        return scores.cpu(), kept.cpu(), own.cpu(), mb, n_end
 
     def decode_dense(self, q, out=None, stream=None):
         if out is None:

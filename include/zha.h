@@ -192,6 +192,51 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats,
 zha_status zha_prefill(zha_tree* t, const void* k_new, const void* v_new, const void* q, float* out,
                        int64_t m, int32_t* stats, hipStream_t stream);
 
+/* Bytes of device workspace zha_prefill_batched needs for sub-batches of up to `batch`
+ * queries (1..128) over a tree of this config's capacity; 0 for an invalid config or
+ * batch.  Dominated by the scores of every node for each (query, head) pair of a
+ * sub-batch: about batch * Hq * (capacity / block) * 4 * b / (b - 1) bytes. */
+size_t zha_prefill_workspace_bytes(const zha_config* cfg, int32_t batch);
+
+/* Causal multi-query prefill, batched: the same result as zha_prefill (query i routes over
+ * the tree of the tokens up to and including its own, blog, "Routing through the tree";
+ * the routing of a whole prompt stays subquadratic, blog, "How is this subquadratic"),
+ * computed `batch` queries at a time.  Per sub-batch of mb queries at positions
+ * N0 .. N0+mb-1: the mb tokens are appended (cache rows and the nodes that cover them),
+ * each query's own rightmost node of every level is built over the tokens up to its
+ * position (the tree's node arithmetic: logsumexp of the children's log masses, their
+ * softmax-weighted mean plane and offset), every node of every level is scored for all
+ * mb * Hq (query, head) pairs in one pass over the planes, the nodes right of a pair's own
+ * node drop out, each pair selects top-down with the fixed-point top-p rule of zha_decode,
+ * and the routed attention of the mb queries runs in one launch, query i attending tokens
+ * [0, N0 + i].  Scores use the float32 planes (whatever cfg.plane_dtype selects for decode).
+ *   k_new, v_new  (device) [Hkv][m][d] dtype;  q (device) [m][Hq][d] dtype, 16-byte aligned;
+ *   out           (device) [m][Hq][d] float32;
+ *   batch         queries per sub-batch, 1..128;
+ *   workspace     (device) at least zha_prefill_workspace_bytes(cfg, batch) bytes, 256-byte
+ *                 aligned, owned by the caller; it holds the last sub-batch's scores and kept
+ *                 bitmaps for zha_debug_prefill_trace until the next call that uses it.
+ * ZHA_E_CAPACITY when N + m > capacity, ZHA_E_WORKSPACE when the workspace is too small
+ * (nothing is enqueued).  All work is enqueued on `stream`; a HIP error part-way leaves
+ * the sub-batches appended before it in the tree. */
+zha_status zha_prefill_batched(zha_tree* t, const void* k_new, const void* v_new, const void* q, float* out,
+                               int64_t m, int32_t batch, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* The last sub-batch of zha_prefill_batched at `level` (1..levels), with mb its query
+ * count, N its end (tokens in the tree after it) and P = mb * Hq / Hkv its pairs, in pair
+ * order p = i * (Hq / Hkv) + head-in-group:
+ *   scores  (device, nullable) float32 [Hkv][P][n], n = ceil(N / block^level): the router
+ *           score of every node for every pair, -inf right of the pair's own node;
+ *   kept    (device, nullable) uint32 [Hkv][P][ceil(n / 32)]: the pair's kept bitmap (bit
+ *           e % 32 of word e / 32 = node e);
+ *   own     (device, nullable) float32 [Hkv][mb][R][d + 2]: query i's own rightmost node of
+ *           the level over the tokens up to its position, per plane (s [d], c, LSE).
+ * ZHA_E_STATE when no batched prefill ran on this tree.  Reads the caller's prefill
+ * workspace, which must still hold that call's contents. */
+zha_status zha_debug_prefill_trace(zha_tree* t, int32_t level, float* scores, uint32_t* kept, float* own,
+                                   hipStream_t stream);
+
 /* Dense decode over all N tokens (the baseline attention the method is compared with):
  * out[h] = softmax(q_h.K^T/sqrt(d)) V for every query head. */
 zha_status zha_decode_dense(zha_tree* t, const void* q, float* out, hipStream_t stream);

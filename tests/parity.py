@@ -395,6 +395,51 @@ def check_decode(trees: list, K, V, q: np.ndarray, o: np.ndarray, traces: dict, 
     return reps
 
 
+def kept_from_bits(words, n: int) -> np.ndarray:
+    """Node ids set in a kept bitmap (uint32 words, bit e % 32 of word e // 32 = node e)."""
+    w = np.ascontiguousarray(np.asarray(words).astype(np.int64) & 0xFFFFFFFF, dtype="<u4")
+    bits = np.unpackbits(w.view(np.uint8), bitorder="little")
+    return np.nonzero(bits[:n])[0].astype(np.int64)
+
+
+def compare_prefill_pair(tree, q, scores: dict, kept: dict, p) -> tuple:
+    """One (query, head) pair of a batched prefill against ``tree``, the oracle tree of the
+    tokens up to and including the query's own.  ``scores[lv]``: the GPU's score row of the
+    pair over every node of the sub-batch's tree at level lv; ``kept[lv]``: the node ids the
+    GPU kept.  At every level from the top:
+      * every node of the pair's tree scores within SCORE_TOL of the oracle's score (the
+        rightmost one is the pair's own version of that node), every node right of it
+        scores -inf;
+      * the GPU's kept set is the oracle's top-p of the GPU's frontier (every node at the
+        top, else the children of the GPU's kept nodes one level up), by check_selection.
+    Returns (report, kept level-1 blocks)."""
+    rep = new_report()
+    prev = None
+    for lv in range(tree.n_levels, 0, -1):
+        n = tree.nodes(lv)
+        row = np.asarray(scores[lv], dtype=np.float64)
+        if len(row) < n or np.any(row[n:] != -np.inf):
+            rep["bad"].append(("tail", lv, n, len(row)))
+            return rep, None
+        s_ref = zo.node_scores(tree, lv, np.arange(n, dtype=np.int64), q)
+        err = np.abs(row[:n] - s_ref)
+        if n and np.max(err) > SCORE_TOL:
+            i = int(np.argmax(err))
+            rep["bad"].append(("score", lv, i, float(row[i]), float(s_ref[i])))
+            return rep, None
+        fr = np.arange(n, dtype=np.int64) if prev is None else zo.children(tree, lv + 1, prev)
+        sel = check_selection(fr, s_ref[fr], row[fr], kept[lv], zo.level_p(p, lv))
+        rep["selections"] += 1
+        rep["band"] += len(sel["band"])
+        rep["swap"] += len(sel["swap"])
+        if sel["bad"]:
+            rep["bad"] += [("kept", lv) + tuple(x) for x in sel["bad"]]
+            return rep, None
+        prev = np.sort(np.asarray(kept[lv], dtype=np.int64))
+    rep["same"] = rep["band"] == 0 and rep["swap"] == 0
+    return rep, prev
+
+
 def gpu_tokens(trace0: dict, gi: int, b: int, n_tokens: int, keep_sink=True) -> np.ndarray:
     blocks = gpu_frontier(trace0, gi)
     tok = (blocks[:, None] * b + np.arange(b)[None, :]).ravel()

@@ -144,6 +144,8 @@ def test_call_order_and_arguments(zha):
             (lambda: zha.zha_debug_router_planes(t, 2, fake), 5),
             (lambda: zha.zha_tree_append_n(t, fake, fake, 4), 5),
             (lambda: zha.zha_prefill(t, fake, fake, fake, fake, 4), 5),
+            (lambda: zha.zha_prefill_batched(t, fake, fake, fake, fake, 4, 4, fake, 1 << 30), 5),
+            (lambda: zha.zha_debug_prefill_trace(t, 1, fake, fake), 5),
             (lambda: zha.zha_tree_build(t, fake, fake, 1001, fake), 3),
             (lambda: zha.zha_tree_build(t, fake, fake, 0, fake), 1),
             (lambda: zha.zha_tree_build(t, None, fake, 10, fake), 1),
@@ -202,3 +204,16 @@ def test_dense_static_argument_errors(zha):
     with pytest.raises(zha.ZhaError) as e:
         zha.zha_decode_dense_static(good(zha, num_kv_heads=1100, num_q_heads=8800), p, p, 10, p, p)
     assert e.value.status == 4 and "static scratch" in str(e.value)
+
+
+def test_prefill_workspace_bytes(zha):
+    """The batched-prefill workspace: 0 for a bad config or a batch outside 1..128, else
+    256-byte granular and growing with the batch and with the capacity."""
+    cfg = good(zha)
+    assert zha.zha_prefill_workspace_bytes(cfg, 0) == 0
+    assert zha.zha_prefill_workspace_bytes(cfg, 129) == 0
+    assert zha.zha_prefill_workspace_bytes(good(zha, head_dim=96), 4) == 0
+    a, b = zha.zha_prefill_workspace_bytes(cfg, 1), zha.zha_prefill_workspace_bytes(cfg, 128)
+    assert a > 0 and a % 256 == 0 and b % 256 == 0 and b > 64 * a
+    assert zha.zha_prefill_workspace_bytes(good(zha, capacity=1 << 20), 16) > \
+        3 * zha.zha_prefill_workspace_bytes(cfg, 16)
