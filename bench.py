@@ -928,6 +928,44 @@ def main():
         append_n["prefill"] = {"tokens": mp, "ms": round(pm, 4), "ms_per_token": round(pm / mp, 4),
                                "tokens_per_s": round(mp / (pm * 1e-3), 1)}
         log(f"[bench] prefill of {mp} tokens (append + decode each): {pm:.3f} ms, {pm / mp:.4f} ms/token")
+        # the same tokens through the batched causal prefill, several sub-batch sizes
+        Kc2, Vc2 = Kd[:, n0 - mp:n0].contiguous(), Vd[:, n0 - mp:n0].contiguous()
+        Qc2 = Qd[:mp].contiguous()
+        pout2 = torch.empty_like(pout)
+        batched = {}
+        for bt in (8, 16, 32, 64):
+            if bt > mp:
+                continue
+            tree3.build(Kd, Vd, n0 - mp, Rd)
+            tree3.prefill_batched(Kc2, Vc2, Qc2, bt, out=pout2)
+            b_ms = []
+            for _ in range(3):
+                tree3.build(Kd, Vd, n0 - mp, Rd)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                tree3.prefill_batched(Kc2, Vc2, Qc2, bt, out=pout2)
+                e1.record()
+                torch.cuda.synchronize()
+                b_ms.append(e0.elapsed_time(e1))
+            stage = {}
+            for key in ("prefill_prep", "prefill_score", "prefill_select", "prefill_attend", "build_tile"):
+                tree3.build(Kd, Vd, n0 - mp, Rd)
+                torch.cuda.synchronize()
+                zha.zha_profile_start(tree3.handle, key)
+                tree3.prefill_batched(Kc2, Vc2, Qc2, bt, out=pout2)
+                torch.cuda.synchronize()
+                ms_, n_ = zha.zha_profile_stop(tree3.handle)
+                stage[key] = round(ms_, 4)
+            bm = float(np.median(b_ms))
+            batched[str(bt)] = {"ms": round(bm, 4), "tokens_per_s": round(mp / (bm * 1e-3), 1),
+                                "speedup_vs_per_token": round(pm / bm, 3), "stage_ms": stage,
+                                "max_abs_diff_vs_per_token": round(float((pout2 - pout).abs().max()), 6)}
+            log(f"[bench] batched prefill of {mp} tokens, {bt} per sub-batch: {bm:.3f} ms "
+                f"({mp / (bm * 1e-3):.0f} tok/s, {pm / bm:.2f}x the per-token loop); stages " +
+                ", ".join(f"{k}={v:.3f}" for k, v in stage.items()))
+        append_n["prefill_batched"] = batched
+        del Kc2, Vc2, Qc2, pout2
         tree3.close()
         del tree3, Kc, Vc, pout
 

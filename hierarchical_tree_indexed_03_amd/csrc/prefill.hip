@@ -251,6 +251,281 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(PrefillArgs a) {
   }
 }
 
+// The same scores for bf16 queries on bf16 MFMA: each float32 plane element is split into
+// three bfloat16 terms s1 + s2 + s3 (s1 = bf16(s), s2 = bf16(s - s1), s3 = bf16(s - s1 - s2):
+// 24 significant bits, the float32 value up to its last bit), the query is bfloat16 already,
+// so every product q_e * s_ie is exact in float32 and q.s is accumulated in float32 as on the
+// float32 path, at three 16x16x32 MFMAs per 32 elements instead of eight 16x16x4.  A lane
+// holds D/4 consecutive elements of one plane row (read straight from global memory, no LDS
+// transpose: the 16x16x32 operand wants 8 consecutive elements per lane).
+__device__ __forceinline__ void split3(float x, uint32_t& h1, uint32_t& h2, uint32_t& h3) {
+  h1 = f2bf16_bits(x);
+  const float r1 = x - bf16_bits_to_f32(h1);
+  h2 = f2bf16_bits(r1);
+  const float r2 = r1 - bf16_bits_to_f32(h2);
+  h3 = f2bf16_bits(r2);
+}
+
+template <int D, int R>
+__global__ __launch_bounds__(256) void prefill_score_split_kernel(PrefillArgs a) {
+  constexpr int NPT = 16 / R;
+  constexpr int NL = D / 32;           // 8-element groups per lane
+  constexpr int EL = D / 4;            // elements per lane
+  const int kv = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int slot = col / R, plane = col % R;
+  const int lv = 1 + (int)blockIdx.z;
+  const int64_t n = a.nl[lv];
+  const int64_t cap = a.dev.ncap[lv];
+  const float* S = a.dev.s[lv] + (int64_t)kv * cap * R * D;
+  const float* C = a.dev.c[lv] + (int64_t)kv * cap * R;
+  const int64_t sst = a.sstride[lv];
+  float* out = a.S + a.soff[lv] + (int64_t)kv * a.P * sst;
+  const bf16_t* Q = (const bf16_t*)a.q;
+  const int P = a.P, g = a.g, npb = (P + 15) / 16;
+
+  auto load_q = [&](int pb, bf16x8 (&qa)[NL]) {
+    const int p = pb * 16 + col;
+    const bf16_t* qp = Q + ((int64_t)(p / g) * a.hq + (int64_t)kv * g + p % g) * D + kg * EL;
+#pragma unroll
+    for (int kk = 0; kk < NL; ++kk) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (p < P) v = *(const uint4*)(qp + kk * 8);
+      qa[kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  };
+  const int64_t ntiles = (n + NPT - 1) / NPT;
+  const int64_t tstride = (int64_t)gridDim.x * 4;
+  int32_t rnid;
+  float rcj;
+  float4 ld[EL / 4];
+  auto fetch = [&](int64_t t) {
+    const int64_t e = t * NPT + slot;
+    rnid = (t < ntiles && e < n) ? (int32_t)e : -1;
+    rcj = rnid >= 0 ? C[(int64_t)rnid * R + plane] : -INFINITY;
+    const float* row = S + ((int64_t)(rnid >= 0 ? rnid : 0) * R + plane) * D + kg * EL;
+#pragma unroll
+    for (int i = 0; i < EL / 4; ++i) ld[i] = rnid >= 0 ? *(const float4*)(row + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t < ntiles) fetch(t);
+  for (; t < ntiles; t += tstride) {
+    bf16x8 s1[NL], s2[NL], s3[NL];
+#pragma unroll
+    for (int kk = 0; kk < NL; ++kk) {
+      uint32_t w1[4], w2[4], w3[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 f = ld[2 * kk + u / 2];
+        const float x0 = (u & 1) ? f.z : f.x, x1 = (u & 1) ? f.w : f.y;
+        uint32_t a1, a2, a3, b1, b2, b3;
+        split3(x0, a1, a2, a3);
+        split3(x1, b1, b2, b3);
+        w1[u] = a1 | (b1 << 16);
+        w2[u] = a2 | (b2 << 16);
+        w3[u] = a3 | (b3 << 16);
+      }
+      s1[kk] = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
+      s2[kk] = __builtin_bit_cast(bf16x8, make_uint4(w2[0], w2[1], w2[2], w2[3]));
+      s3[kk] = __builtin_bit_cast(bf16x8, make_uint4(w3[0], w3[1], w3[2], w3[3]));
+    }
+    const int32_t nid = rnid;
+    const float cj = rcj;
+    if (t + tstride < ntiles) fetch(t + tstride);
+    bf16x8 qa[NL], qn[NL];
+    load_q(0, qa);
+    for (int pb = 0; pb < npb; ++pb) {
+      if (pb + 1 < npb) load_q(pb + 1, qn);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NL; ++kk) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], s3[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], s2[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], s1[kk], acc, 0, 0, 0);
+      }
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = a.sigma * acc[e] + cj;
+#pragma unroll
+      for (int off = 1; off < R; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], __shfl_xor(v[e], off));
+      if (nid >= 0 && plane == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int p = pb * 16 + kg * 4 + e;
+          if (p < P) out[(int64_t)p * sst + nid] = v[e];
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < NL; ++kk) qa[kk] = qn[kk];
+    }
+  }
+}
+
+// The split-bf16 scorer organised for reuse on both operands: a wave keeps the queries of 64
+// pairs (four 16-pair MFMA blocks) in registers for the whole launch and streams plane tiles
+// past them; a workgroup's four waves cover 256 pairs.  Each 16-row tile is read from HBM
+// once per workgroup (two float4 per thread), split once into its three bf16 terms and
+// staged in LDS in the MFMA operand layout (double-buffered: the next tile is loaded and
+// split while the current one is multiplied).  Scores go through LDS so that each pair's
+// row is written in 32-node (128-byte) runs: a workgroup takes 32 consecutive nodes at a
+// time.  Grid: (segment slots, Hkv * pair chunks of 256, levels).
+constexpr int SG_NODES = 32;
+
+template <int D, int R>
+__global__ __launch_bounds__(256) void prefill_score_seg_kernel(PrefillArgs a) {
+  constexpr int NPT = 16 / R;                  // nodes per 16-row tile
+  constexpr int TPS = SG_NODES / NPT;          // tiles per segment
+  constexpr int NL = D / 32;
+  constexpr int EL = D / 4;
+  constexpr int RW = D + 8;                    // staged row stride (bf16), 16 bytes of padding
+  constexpr int F4 = 16 * D / 4 / 256;         // float4 loads per thread per tile
+  static_assert(F4 >= 1, "tile of at least 256 float4");
+  __shared__ __align__(16) uint16_t stg[2][3][16 * RW];
+  __shared__ float cst[2][16];
+  __shared__ float buf[4][64][SG_NODES + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int kv = (int)blockIdx.y % a.hkv, chunk = (int)blockIdx.y / a.hkv;
+  const int lv = 1 + (int)blockIdx.z;
+  const int64_t n = a.nl[lv];
+  const int64_t cap = a.dev.ncap[lv];
+  const float* S = a.dev.s[lv] + (int64_t)kv * cap * R * D;
+  const float* C = a.dev.c[lv] + (int64_t)kv * cap * R;
+  const int64_t sst = a.sstride[lv];
+  float* out = a.S + a.soff[lv] + (int64_t)kv * a.P * sst;
+  const int P = a.P, g = a.g;
+  const int p0 = chunk * 256 + wave * 64;      // this wave's first pair
+  const int64_t nseg = (n + SG_NODES - 1) / SG_NODES;
+  if ((int64_t)blockIdx.x >= nseg || chunk * 256 >= P) return;   // whole workgroup
+  const bool active = p0 < P;
+  // the wave's 64 queries (bf16, exact), four MFMA blocks
+  bf16x8 qa[4][NL];
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb) {
+    const int p = p0 + pb * 16 + col;
+    const bf16_t* qp = (const bf16_t*)a.q + ((int64_t)(p / g) * a.hq + (int64_t)kv * g + p % g) * D + kg * EL;
+#pragma unroll
+    for (int kk = 0; kk < NL; ++kk) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (p < P) v = *(const uint4*)(qp + kk * 8);
+      qa[pb][kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  // tile loads: thread tid takes float4 number tid + 256 * i of the 16 x D tile
+  float4 ld[F4];
+  float ldc = -INFINITY;
+  auto fetch = [&](int64_t tile) {           // tile index within the level
+#pragma unroll
+    for (int i = 0; i < F4; ++i) {
+      const int f = tid + 256 * i;
+      const int r = f / (D / 4);
+      const int64_t e = tile * NPT + r / R;
+      ld[i] = e < n ? *(const float4*)(S + (e * R + r % R) * D + (f % (D / 4)) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (tid < 16) {
+      const int64_t e = tile * NPT + tid / R;
+      ldc = e < n ? C[e * R + tid % R] : -INFINITY;
+    }
+  };
+  auto stage = [&](int bsel) {               // split the fetched tile into stg[bsel]
+#pragma unroll
+    for (int i = 0; i < F4; ++i) {
+      const int f = tid + 256 * i;
+      const int r = f / (D / 4), c4 = (f % (D / 4)) * 4;
+      const float x[4] = {ld[i].x, ld[i].y, ld[i].z, ld[i].w};
+      uint32_t h[3][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) split3(x[u], h[0][u], h[1][u], h[2][u]);
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp)
+        *(uint2*)&stg[bsel][sp][r * RW + c4] = make_uint2(h[sp][0] | (h[sp][1] << 16), h[sp][2] | (h[sp][3] << 16));
+    }
+    if (tid < 16) cst[bsel][tid] = ldc;
+  };
+  float* B = &buf[wave][0][0];
+  const int64_t tiles_total = (n + NPT - 1) / NPT;
+  int64_t seg = blockIdx.x;
+  fetch(seg * TPS);
+  stage(0);
+  __syncthreads();
+  int cur = 0;
+  for (; seg < nseg; seg += gridDim.x) {
+    const int64_t node0 = seg * SG_NODES;
+    for (int tt = 0; tt < TPS; ++tt) {
+      // the next tile (of this segment, else of the next one) into registers
+      int64_t nxt = -1;
+      if (tt + 1 < TPS) nxt = seg * TPS + tt + 1;
+      else if (seg + gridDim.x < nseg) nxt = (seg + gridDim.x) * TPS;
+      if (nxt >= tiles_total) nxt = -1;
+      if (nxt >= 0) fetch(nxt);
+      if (active) {
+        bf16x8 s1[NL], s2[NL], s3[NL];
+#pragma unroll
+        for (int kk = 0; kk < NL; ++kk) {
+          const int off = col * RW + kg * EL + kk * 8;
+          s1[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)&stg[cur][0][off]);
+          s2[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)&stg[cur][1][off]);
+          s3[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)&stg[cur][2][off]);
+        }
+        // plane rows x pairs: lane (kg, col) gets rows 4kg..4kg+3 of pair col; four
+        // independent accumulation chains (one per 16-pair block), smallest terms first
+        f32x4 acc[4];
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NL; ++kk) {
+#pragma unroll
+          for (int pb = 0; pb < 4; ++pb) acc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s3[kk], qa[pb][kk], acc[pb], 0, 0, 0);
+#pragma unroll
+          for (int pb = 0; pb < 4; ++pb) acc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s2[kk], qa[pb][kk], acc[pb], 0, 0, 0);
+#pragma unroll
+          for (int pb = 0; pb < 4; ++pb) acc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s1[kk], qa[pb][kk], acc[pb], 0, 0, 0);
+        }
+        float cr[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cr[e] = cst[cur][4 * kg + e];
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = a.sigma * acc[pb][e] + cr[e];
+          // row 4kg+e is plane (4kg+e) % R of node (4kg+e) / R: the max over a node's
+          // planes within the lane's four rows, then across lane groups for R > 4
+          float* dst = B + (pb * 16 + col) * (SG_NODES + 1) + tt * NPT;
+          if constexpr (R == 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[4 * kg + e] = v[e];
+          } else if constexpr (R == 2) {
+            dst[2 * kg] = fmaxf(v[0], v[1]);
+            dst[2 * kg + 1] = fmaxf(v[2], v[3]);
+          } else {
+            float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+            if constexpr (R >= 8) m = fmaxf(m, __shfl_xor(m, 16));
+            if constexpr (R >= 16) m = fmaxf(m, __shfl_xor(m, 32));
+            if ((kg & (R / 4 - 1)) == 0) dst[(4 * kg) / R] = m;
+          }
+        }
+      }
+      if (nxt >= 0) stage(cur ^ 1);
+      __syncthreads();
+      cur ^= 1;
+    }
+    // the wave's 64 rows of this segment, 32 nodes each (the buffer is the wave's own)
+    const int64_t nn = min((int64_t)SG_NODES, n - node0);
+    if (active) {
+#pragma unroll 4
+      for (int r = 0; r < 64; r += 2) {
+        const int pr = r + (lane >> 5), j = lane & 31;
+        const int p = p0 + pr;
+        if (p < P && j < nn) out[(int64_t)p * sst + node0 + j] = B[pr * (SG_NODES + 1) + j];
+      }
+    }
+    wave_sync_lds();
+  }
+}
+
 // Each pair's tail: nodes right of its own rightmost node do not exist (-inf), the rightmost
 // node scores with the pair's own version of it.  Grid (P, Hkv, levels); one wave per
 // workgroup computes the R plane values of the own node.
@@ -280,6 +555,7 @@ __global__ __launch_bounds__(64) void prefill_tail_kernel(PrefillArgs a) {
 constexpr int PS_THREADS = 512;
 constexpr int PS_LIST = 8192;   // frontier nodes held in LDS (more: the level is read from global memory)
 constexpr int PS_TIES = 256;    // boundary sub-bin nodes resolved pairwise (more: radix select)
+constexpr int PS_KWORDS = 2048; // kept bitmap words built in LDS (a longer level: in global memory)
 
 // Kept bitmap words written earlier in the same workgroup (stores and L2 atomics): read at
 // agent scope so that no stale vector-cache line is returned.
@@ -339,8 +615,13 @@ __device__ __forceinline__ int32_t ps_scan(int32_t v, int32_t* wsum, int32_t& to
 
 // One workgroup per (pair, KV head) walks the levels from the top.  The level's frontier
 // (every node at the top, else the children of the nodes kept one level up, in node order)
-// is listed in LDS with its scores; a frontier longer than PS_LIST is read from global
-// memory on every pass instead.  Nodes outside the pair's tree score -inf and drop out.
+// is held in one of two ways for the passes that follow:
+//   list  at most PS_LIST nodes: node ids and scores in LDS;
+//   scan  a longer frontier: every pass reads the whole level from global memory (PS_UNROLL
+//         loads in flight per thread), the frontier test from the parents' kept bitmap.
+// Nodes outside the pair's tree score -inf and drop out.
+constexpr int PS_UNROLL = 8;
+
 __global__ __launch_bounds__(PS_THREADS) void prefill_select_kernel(PrefillArgs a) {
   constexpr int NW = PS_THREADS / 64;
   __shared__ int32_t fl[PS_LIST];
@@ -351,6 +632,7 @@ __global__ __launch_bounds__(PS_THREADS) void prefill_select_kernel(PrefillArgs 
   __shared__ uint64_t tie_m[PS_TIES];
   __shared__ float redm[NW];
   __shared__ int32_t wsum[NW];
+  __shared__ uint32_t kl[PS_KWORDS];
   __shared__ uint32_t s_b1, s_b2, s_ntie;
   __shared__ uint64_t s_T, s_above1, s_above2, s_prefix, s_rabove;
   static_assert(NB1 == 512 && NB2 == 512, "ps_find scans 512 bins");
@@ -365,16 +647,15 @@ __global__ __launch_bounds__(PS_THREADS) void prefill_select_kernel(PrefillArgs 
     const float* row = a.S + a.soff[lv] + ((int64_t)kv * a.P + p) * a.sstride[lv];
     uint32_t* kb = a.KB + a.koff[lv] + ((int64_t)kv * a.P + p) * a.kstride[lv];
     const uint32_t* kp = top ? nullptr : a.KB + a.koff[lv + 1] + ((int64_t)kv * a.P + p) * a.kstride[lv + 1];
-    for (int64_t w = tid; w < nw; w += PS_THREADS) kb[w] = 0u;
+    const bool lds_kept = nw <= PS_KWORDS;
     // ---- the frontier
     int64_t nf = 0;
+    const int64_t nwp = top ? 0 : (a.nl[lv + 1] + 31) >> 5;   // parent bitmap words
     if (top) {
       nf = n;
       if (n <= PS_LIST)
         for (int k = tid; k < (int)n; k += PS_THREADS) { fl[k] = k; fs[k] = row[k]; }
     } else {
-      const int64_t np = a.nl[lv + 1];
-      const int64_t nwp = (np + 31) >> 5;
       for (int64_t w0 = 0; w0 < nwp; w0 += PS_THREADS) {
         const int64_t w = w0 + tid;
         const uint32_t word = w < nwp ? ld_agent(kp + w) : 0u;
@@ -389,38 +670,63 @@ __global__ __launch_bounds__(PS_THREADS) void prefill_select_kernel(PrefillArgs 
           for (uint32_t r = word; r; r &= r - 1u) {
             const int64_t first = (32 * w + __ffs(r) - 1) << lb;
             const int64_t last = min(first + b, n);
-            for (int64_t e = first; e < last; ++e, ++off) { fl[off] = (int32_t)e; fs[off] = row[e]; }
+            for (int64_t e = first; e < last; ++e, ++off) fl[off] = (int32_t)e;
           }
         }
         nf += round;
       }
+      // the listed nodes' scores, all threads at once
+      if (nf <= PS_LIST) {
+        __syncthreads();
+        for (int64_t k = tid; k < nf; k += PS_THREADS) fs[k] = row[fl[k]];
+      }
     }
     const bool list = nf <= PS_LIST;
-    const int64_t count = list ? nf : n;
-    // (node, score) of entry k; -inf outside the frontier
-    auto get = [&](int64_t k, int64_t& e, float& x) {
+    // past the list: the parents' kept bitmap goes to LDS (in the list's space) when it fits
+    uint32_t* pbits = (uint32_t*)fl;
+    const bool lds_bits = !list && !top && nwp <= PS_LIST;
+    __syncthreads();
+    if (lds_bits)
+      for (int64_t w = tid; w < nwp; w += PS_THREADS) pbits[w] = ld_agent(kp + w);
+    // kept marks: LDS bitmap (copied out at the end) or the global one; a listed frontier
+    // sets bits one node at a time, so its bitmap starts cleared (the other modes write every
+    // word in their classification pass)
+    if (list) {
+      if (lds_kept)
+        for (int64_t w = tid; w < nw; w += PS_THREADS) kl[w] = 0u;
+      else
+        for (int64_t w = tid; w < nw; w += PS_THREADS) kb[w] = 0u;
+    }
+    __syncthreads();
+    auto in_front = [&](int64_t k) -> bool {
+      if (top) return true;
+      const int64_t pn = k >> lb;
+      return ((lds_bits ? pbits[pn >> 5] : ld_agent(kp + (pn >> 5))) >> (pn & 31)) & 1u;
+    };
+    // f(node, score) for every entry (score -inf outside the frontier)
+    auto each = [&](auto&& f) {
       if (list) {
-        e = fl[k];
-        x = fs[k];
+        for (int64_t k = tid; k < nf; k += PS_THREADS) f((int64_t)fl[k], fs[k]);
       } else {
-        e = k;
-        bool in = top;
-        if (!in) {
-          const int64_t pn = k >> lb;
-          in = (ld_agent(kp + (pn >> 5)) >> (pn & 31)) & 1u;
+        for (int64_t k0 = tid; k0 < n; k0 += (int64_t)PS_UNROLL * PS_THREADS) {
+          float xs[PS_UNROLL];
+#pragma unroll
+          for (int j = 0; j < PS_UNROLL; ++j) {
+            const int64_t k = k0 + (int64_t)j * PS_THREADS;
+            xs[j] = (k < n && in_front(k)) ? row[k] : -INFINITY;
+          }
+#pragma unroll
+          for (int j = 0; j < PS_UNROLL; ++j) f(k0 + (int64_t)j * PS_THREADS, xs[j]);
         }
-        x = in ? row[k] : -INFINITY;
       }
     };
-    __syncthreads();
+    auto keep = [&](int64_t e) {
+      if (lds_kept) atomicOr(&kl[e >> 5], 1u << (e & 31));
+      else atomicOr(&kb[e >> 5], 1u << (e & 31));
+    };
     // ---- max
     float mx = -INFINITY;
-    for (int64_t k = tid; k < count; k += PS_THREADS) {
-      int64_t e;
-      float x;
-      get(k, e, x);
-      mx = fmaxf(mx, x);
-    }
+    each([&](int64_t, float x) { mx = fmaxf(mx, x); });
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     if (lane == 0) redm[wave] = mx;
     for (int k = tid; k < NB1; k += PS_THREADS) h[k] = 0ull;
@@ -429,16 +735,14 @@ __global__ __launch_bounds__(PS_THREADS) void prefill_select_kernel(PrefillArgs 
 #pragma unroll
     for (int w = 1; w < NW; ++w) M = fmaxf(M, redm[w]);
     if (M == -INFINITY) {   // empty frontier: nothing kept here or below
+      for (int64_t w = tid; w < nw; w += PS_THREADS) kb[w] = 0u;
       __syncthreads();
       continue;
     }
     // ---- coarse histogram of the fixed-point masses
-    for (int64_t k = tid; k < count; k += PS_THREADS) {
-      int64_t e;
-      float x;
-      get(k, e, x);
+    each([&](int64_t, float x) {
       if (x != -INFINITY) atomicAdd(&h[bin_of(x, M).bin], (unsigned long long)mass_of(x, M));
-    }
+    });
     __syncthreads();
     if (wave == 0) {
       uint32_t bb;
@@ -461,14 +765,40 @@ __global__ __launch_bounds__(PS_THREADS) void prefill_select_kernel(PrefillArgs 
     // ---- nodes of the bins above the boundary bin are kept; the boundary bin's fine histogram
     for (int k = tid; k < NB2; k += PS_THREADS) h[k] = 0ull;
     __syncthreads();
-    for (int64_t k = tid; k < count; k += PS_THREADS) {
-      int64_t e;
-      float x;
-      get(k, e, x);
-      if (x == -INFINITY) continue;
-      const BinSub bs = bin_of(x, M);
-      if (bs.bin < b1) atomicOr(&kb[e >> 5], 1u << (e & 31));
-      else if (bs.bin == b1) atomicAdd(&h[bs.sub], (unsigned long long)mass_of(x, M));
+    if (list) {
+      each([&](int64_t e, float x) {
+        if (x == -INFINITY) return;
+        const BinSub bs = bin_of(x, M);
+        if (bs.bin < b1) keep(e);
+        else if (bs.bin == b1) atomicAdd(&h[bs.sub], (unsigned long long)mass_of(x, M));
+      });
+    } else {
+      // each wave's 64 consecutive nodes of a round give two kept words by one ballot
+      for (int64_t k0 = tid; k0 - lane < n; k0 += (int64_t)PS_UNROLL * PS_THREADS) {
+        float xs[PS_UNROLL];
+#pragma unroll
+        for (int j = 0; j < PS_UNROLL; ++j) {
+          const int64_t k = k0 + (int64_t)j * PS_THREADS;
+          xs[j] = (k < n && in_front(k)) ? row[k] : -INFINITY;
+        }
+#pragma unroll
+        for (int j = 0; j < PS_UNROLL; ++j) {
+          const float x = xs[j];
+          bool kept = false;
+          if (x != -INFINITY) {
+            const BinSub bs = bin_of(x, M);
+            kept = bs.bin < b1;
+            if (bs.bin == b1) atomicAdd(&h[bs.sub], (unsigned long long)mass_of(x, M));
+          }
+          const uint64_t m = __ballot(kept);
+          const int64_t w0 = (k0 - lane + (int64_t)j * PS_THREADS) >> 5;
+          if (lane < 2 && w0 + lane < nw) {
+            const uint32_t word = lane ? (uint32_t)(m >> 32) : (uint32_t)m;
+            if (lds_kept) kl[w0 + lane] = word;
+            else kb[w0 + lane] = word;
+          }
+        }
+      }
     }
     __syncthreads();
     if (b1 < (uint32_t)NB1) {
@@ -481,20 +811,17 @@ __global__ __launch_bounds__(PS_THREADS) void prefill_select_kernel(PrefillArgs 
       __syncthreads();
       const uint32_t b2 = s_b2;
       const uint64_t above2 = s_above2;
-      for (int64_t k = tid; k < count; k += PS_THREADS) {
-        int64_t e;
-        float x;
-        get(k, e, x);
-        if (x == -INFINITY) continue;
+      each([&](int64_t e, float x) {
+        if (x == -INFINITY) return;
         const BinSub bs = bin_of(x, M);
-        if (bs.bin != b1) continue;
+        if (bs.bin != b1) return;
         if (bs.sub < b2) {
-          atomicOr(&kb[e >> 5], 1u << (e & 31));
+          keep(e);
         } else if (bs.sub == b2) {
           const uint32_t j = atomicAdd(&s_ntie, 1u);
           if (j < (uint32_t)PS_TIES) { tie_e[j] = (int32_t)e; tie_s[j] = x; tie_m[j] = mass_of(x, M); }
         }
-      }
+      });
       __syncthreads();
       const uint32_t nt = s_ntie;
       if (nt <= (uint32_t)PS_TIES) {
@@ -505,7 +832,7 @@ __global__ __launch_bounds__(PS_THREADS) void prefill_select_kernel(PrefillArgs 
           const uint64_t kx = rank_key(tie_s[x], tie_e[x]);
           for (uint32_t y = 0; y < nt; ++y)
             if (rank_key(tie_s[y], tie_e[y]) < kx) ab += tie_m[y];
-          if (above2 + ab < T) atomicOr(&kb[tie_e[x] >> 5], 1u << (tie_e[x] & 31));
+          if (above2 + ab < T) keep(tie_e[x]);
         }
       } else {
         // radix select on the 64-bit rank key of the boundary sub-bin's nodes, 8 bits a pass
@@ -518,16 +845,13 @@ __global__ __launch_bounds__(PS_THREADS) void prefill_select_kernel(PrefillArgs 
           for (int k = tid; k < 256; k += PS_THREADS) dh[k] = 0ull;
           __syncthreads();
           const uint64_t pf = s_prefix;
-          for (int64_t k = tid; k < count; k += PS_THREADS) {
-            int64_t e;
-            float x;
-            get(k, e, x);
-            if (x == -INFINITY) continue;
+          each([&](int64_t e, float x) {
+            if (x == -INFINITY) return;
             const BinSub bs = bin_of(x, M);
-            if (bs.bin != b1 || bs.sub != b2) continue;
+            if (bs.bin != b1 || bs.sub != b2) return;
             const uint64_t rk = rank_key(x, (int32_t)e);
             if ((rk & hi) == (pf & hi)) atomicAdd(&dh[(rk >> shift) & 255u], (unsigned long long)mass_of(x, M));
-          }
+          });
           __syncthreads();
           if (tid == 0) {
             uint64_t run = s_rabove;
@@ -539,17 +863,18 @@ __global__ __launch_bounds__(PS_THREADS) void prefill_select_kernel(PrefillArgs 
           __syncthreads();
         }
         const uint64_t kbnd = s_prefix;
-        for (int64_t k = tid; k < count; k += PS_THREADS) {
-          int64_t e;
-          float x;
-          get(k, e, x);
-          if (x == -INFINITY) continue;
+        each([&](int64_t e, float x) {
+          if (x == -INFINITY) return;
           const BinSub bs = bin_of(x, M);
-          if (bs.bin == b1 && bs.sub == b2 && rank_key(x, (int32_t)e) <= kbnd) atomicOr(&kb[e >> 5], 1u << (e & 31));
-        }
+          if (bs.bin == b1 && bs.sub == b2 && rank_key(x, (int32_t)e) <= kbnd) keep(e);
+        });
       }
     }
     __syncthreads();
+    if (lds_kept) {
+      for (int64_t w = tid; w < nw; w += PS_THREADS) kb[w] = kl[w];
+      __syncthreads();
+    }
   }
 }
 
@@ -638,10 +963,21 @@ hipError_t launch_prefill_qprep(const PrefillArgs& a, bool bf16, int D, hipStrea
 
 template <int D, int R>
 static void launch_score_t(const PrefillArgs& a, hipStream_t st) {
-  static const int per_cu = resident_per_cu(prefill_score_kernel<D, R>, 256);
-  const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
-  hipLaunchKernelGGL((prefill_score_kernel<D, R>), dim3(grid_for(a.nl[1], 4 * (16 / R), cap), (unsigned)a.hkv,
-                                                         (unsigned)a.levels), dim3(256), 0, st, a);
+  if (a.q_bf16) {
+    static const int per_cu = resident_per_cu(prefill_score_seg_kernel<D, R>, 256);
+    const int nchunk = (a.P + 255) / 256;
+    const int64_t cap = (int64_t)per_cu * device_cus() / ((int64_t)a.hkv * nchunk);
+    hipLaunchKernelGGL((prefill_score_seg_kernel<D, R>),
+                       dim3(grid_for(a.nl[1], SG_NODES, cap < 1 ? 1 : cap), (unsigned)(a.hkv * nchunk),
+                            (unsigned)a.levels),
+                       dim3(256), 0, st, a);
+  } else {
+    static const int per_cu = resident_per_cu(prefill_score_kernel<D, R>, 256);
+    const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
+    hipLaunchKernelGGL((prefill_score_kernel<D, R>),
+                       dim3(grid_for(a.nl[1], 4 * (16 / R), cap), (unsigned)a.hkv, (unsigned)a.levels), dim3(256), 0,
+                       st, a);
+  }
 }
 
 hipError_t launch_prefill_score(const PrefillArgs& a, int D, int R, hipStream_t st) {

@@ -33,6 +33,13 @@ CASES = {
     "tiny_from_one": (wc.TINY, 1, 21, 5),
     "tiny_batch1": (wc.TINY, 4093, 3, 1),
     "deep_small": (wc.DEEP, 16_384 + 37, 24, 16),
+    # level 1 of 16K nodes nearly all in each head's frontier: past the LDS list, the level
+    # is read whole with the parents' kept bitmap in LDS
+    "deep_scan": (wc.DEEP, 65_536 + 100, 6, 6),
+    # more than 65,536 level-1 nodes: the kept bitmap is built in global memory, by words
+    # (a scanned level) and node by node (a listed one)
+    "deep_scan_wide": (wc.DEEP, 270_000, 3, 3),
+    "ultra_list_wide": (wc.ULTRA, 720_901, 4, 4),
     "ultra_small": (wc.ULTRA, 70_001, 20, 8),
     "wide_small": (wc.WIDE, 5_000, 20, 7),
     "light_bf16": (wc.light(32_768).with_(planes="bf16"), 32_768 - 5, 30, 30),
