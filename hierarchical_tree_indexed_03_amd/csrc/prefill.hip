@@ -251,127 +251,18 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(PrefillArgs a) {
   }
 }
 
-// The same scores for bf16 queries on bf16 MFMA: each float32 plane element is split into
-// three bfloat16 terms s1 + s2 + s3 (s1 = bf16(s), s2 = bf16(s - s1), s3 = bf16(s - s1 - s2):
-// 24 significant bits, the float32 value up to its last bit), the query is bfloat16 already,
-// so every product q_e * s_ie is exact in float32 and q.s is accumulated in float32 as on the
-// float32 path, at three 16x16x32 MFMAs per 32 elements instead of eight 16x16x4.  A lane
-// holds D/4 consecutive elements of one plane row (read straight from global memory, no LDS
-// transpose: the 16x16x32 operand wants 8 consecutive elements per lane).
-__device__ __forceinline__ void split3(float x, uint32_t& h1, uint32_t& h2, uint32_t& h3) {
-  h1 = f2bf16_bits(x);
-  const float r1 = x - bf16_bits_to_f32(h1);
-  h2 = f2bf16_bits(r1);
-  const float r2 = r1 - bf16_bits_to_f32(h2);
-  h3 = f2bf16_bits(r2);
-}
-
-template <int D, int R>
-__global__ __launch_bounds__(256) void prefill_score_split_kernel(PrefillArgs a) {
-  constexpr int NPT = 16 / R;
-  constexpr int NL = D / 32;           // 8-element groups per lane
-  constexpr int EL = D / 4;            // elements per lane
-  const int kv = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, kg = lane >> 4;
-  const int slot = col / R, plane = col % R;
-  const int lv = 1 + (int)blockIdx.z;
-  const int64_t n = a.nl[lv];
-  const int64_t cap = a.dev.ncap[lv];
-  const float* S = a.dev.s[lv] + (int64_t)kv * cap * R * D;
-  const float* C = a.dev.c[lv] + (int64_t)kv * cap * R;
-  const int64_t sst = a.sstride[lv];
-  float* out = a.S + a.soff[lv] + (int64_t)kv * a.P * sst;
-  const bf16_t* Q = (const bf16_t*)a.q;
-  const int P = a.P, g = a.g, npb = (P + 15) / 16;
-
-  auto load_q = [&](int pb, bf16x8 (&qa)[NL]) {
-    const int p = pb * 16 + col;
-    const bf16_t* qp = Q + ((int64_t)(p / g) * a.hq + (int64_t)kv * g + p % g) * D + kg * EL;
-#pragma unroll
-    for (int kk = 0; kk < NL; ++kk) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (p < P) v = *(const uint4*)(qp + kk * 8);
-      qa[kk] = __builtin_bit_cast(bf16x8, v);
-    }
-  };
-  const int64_t ntiles = (n + NPT - 1) / NPT;
-  const int64_t tstride = (int64_t)gridDim.x * 4;
-  int32_t rnid;
-  float rcj;
-  float4 ld[EL / 4];
-  auto fetch = [&](int64_t t) {
-    const int64_t e = t * NPT + slot;
-    rnid = (t < ntiles && e < n) ? (int32_t)e : -1;
-    rcj = rnid >= 0 ? C[(int64_t)rnid * R + plane] : -INFINITY;
-    const float* row = S + ((int64_t)(rnid >= 0 ? rnid : 0) * R + plane) * D + kg * EL;
-#pragma unroll
-    for (int i = 0; i < EL / 4; ++i) ld[i] = rnid >= 0 ? *(const float4*)(row + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
-  };
-  int64_t t = (int64_t)blockIdx.x * 4 + wave;
-  if (t < ntiles) fetch(t);
-  for (; t < ntiles; t += tstride) {
-    bf16x8 s1[NL], s2[NL], s3[NL];
-#pragma unroll
-    for (int kk = 0; kk < NL; ++kk) {
-      uint32_t w1[4], w2[4], w3[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float4 f = ld[2 * kk + u / 2];
-        const float x0 = (u & 1) ? f.z : f.x, x1 = (u & 1) ? f.w : f.y;
-        uint32_t a1, a2, a3, b1, b2, b3;
-        split3(x0, a1, a2, a3);
-        split3(x1, b1, b2, b3);
-        w1[u] = a1 | (b1 << 16);
-        w2[u] = a2 | (b2 << 16);
-        w3[u] = a3 | (b3 << 16);
-      }
-      s1[kk] = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
-      s2[kk] = __builtin_bit_cast(bf16x8, make_uint4(w2[0], w2[1], w2[2], w2[3]));
-      s3[kk] = __builtin_bit_cast(bf16x8, make_uint4(w3[0], w3[1], w3[2], w3[3]));
-    }
-    const int32_t nid = rnid;
-    const float cj = rcj;
-    if (t + tstride < ntiles) fetch(t + tstride);
-    bf16x8 qa[NL], qn[NL];
-    load_q(0, qa);
-    for (int pb = 0; pb < npb; ++pb) {
-      if (pb + 1 < npb) load_q(pb + 1, qn);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < NL; ++kk) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], s3[kk], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], s2[kk], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], s1[kk], acc, 0, 0, 0);
-      }
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = a.sigma * acc[e] + cj;
-#pragma unroll
-      for (int off = 1; off < R; off <<= 1)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], __shfl_xor(v[e], off));
-      if (nid >= 0 && plane == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int p = pb * 16 + kg * 4 + e;
-          if (p < P) out[(int64_t)p * sst + nid] = v[e];
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < NL; ++kk) qa[kk] = qn[kk];
-    }
-  }
-}
-
-// The split-bf16 scorer organised for reuse on both operands: a wave keeps the queries of 64
-// pairs (four 16-pair MFMA blocks) in registers for the whole launch and streams plane tiles
-// past them; a workgroup's four waves cover 256 pairs.  Each 16-row tile is read from HBM
-// once per workgroup (two float4 per thread), split once into its three bf16 terms and
-// staged in LDS in the MFMA operand layout (double-buffered: the next tile is loaded and
-// split while the current one is multiplied).  Scores go through LDS so that each pair's
-// row is written in 32-node (128-byte) runs: a workgroup takes 32 consecutive nodes at a
-// time.  Grid: (segment slots, Hkv * pair chunks of 256, levels).
-constexpr int SG_NODES = 32;
+// The same scores for bf16 queries on bf16 MFMA.  Each float32 plane element is split
+// exactly into three bfloat16 terms (24 significant bits in all); the query is bfloat16
+// already, so every product q_e * t_ie is exact in float32 and q.s accumulates in float32 as
+// on the float32 path, at three 16x16x32 MFMAs per 32 elements instead of eight 16x16x4.
+// Reuse on both operands: a wave keeps the queries of 64 pairs (four 16-pair MFMA blocks) in
+// registers for the whole launch and streams plane tiles past them; a workgroup's four
+// waves cover 256 pairs.  Each 16-row tile is read from HBM once per workgroup (two float4
+// per thread, four tiles in flight), split once and staged in LDS in the MFMA operand
+// layout (double-buffered).  Scores go through LDS so that each pair's row is written in
+// 16-node (64-byte) runs: a workgroup takes 16 consecutive nodes at a time.
+// Grid: (segment slots, Hkv * pair chunks of 256, levels).
+constexpr int SG_NODES = 16;
 
 template <int D, int R>
 __global__ __launch_bounds__(256) void prefill_score_seg_kernel(PrefillArgs a) {
@@ -413,53 +304,122 @@ __global__ __launch_bounds__(256) void prefill_score_seg_kernel(PrefillArgs a) {
       qa[pb][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  // tile loads: thread tid takes float4 number tid + 256 * i of the 16 x D tile
-  float4 ld[F4];
-  float ldc = -INFINITY;
-  auto fetch = [&](int64_t tile) {           // tile index within the level
+  // tile loads: thread tid takes float4 number tid + 256 * i of the 16 x D tile; NPF tiles
+  // in flight (the HBM latency is several tiles' worth of MFMA work)
+  constexpr int NPF = TPS < 4 ? TPS : 4;
+  float4 ld[NPF][F4];
+  float ldc[NPF];
+  // every load is unconditional and its value is not touched until the tile is staged
+  // (addresses clamped to the level's last node, nodes past it masked when staging): a load
+  // under a branch, or a use of its value, makes the compiler wait for every load in flight,
+  // which would drain the prefetch
+  auto fetch = [&](int64_t tile, float4 (&dst)[F4], float& dc) {
 #pragma unroll
     for (int i = 0; i < F4; ++i) {
       const int f = tid + 256 * i;
       const int r = f / (D / 4);
-      const int64_t e = tile * NPT + r / R;
-      ld[i] = e < n ? *(const float4*)(S + (e * R + r % R) * D + (f % (D / 4)) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int64_t e = min(tile * NPT + r / R, n - 1);
+      dst[i] = *(const float4*)(S + (e * R + r % R) * D + (f % (D / 4)) * 4);
     }
-    if (tid < 16) {
-      const int64_t e = tile * NPT + tid / R;
-      ldc = e < n ? C[e * R + tid % R] : -INFINITY;
-    }
+    const int rr = tid & 15;
+    dc = C[min(tile * NPT + rr / R, n - 1) * R + rr % R];
   };
-  auto stage = [&](int bsel) {               // split the fetched tile into stg[bsel]
+  // split a fetched tile into stg[bsel]: x = t1 + t2 + t3 exactly, each t the float with the
+  // low 16 bits cleared of what is left (8 significant bits each, 24 in all: a float32's
+  // whole significand), so the three are exact bfloat16 values; two elements' halves are
+  // packed into one word by a byte permute
+  auto stage = [&](const float4 (&src_raw)[F4], float sc_raw, int64_t tile, int bsel) {
+    float4 src[F4];
+#pragma unroll
+    for (int i = 0; i < F4; ++i) {
+      const int r = (tid + 256 * i) / (D / 4);
+      src[i] = tile * NPT + r / R < n ? src_raw[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const float sc = tile * NPT + (tid & 15) / R < n ? sc_raw : -INFINITY;
 #pragma unroll
     for (int i = 0; i < F4; ++i) {
       const int f = tid + 256 * i;
       const int r = f / (D / 4), c4 = (f % (D / 4)) * 4;
-      const float x[4] = {ld[i].x, ld[i].y, ld[i].z, ld[i].w};
-      uint32_t h[3][4];
+      const float x[4] = {src[i].x, src[i].y, src[i].z, src[i].w};
+      uint32_t t[3][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) split3(x[u], h[0][u], h[1][u], h[2][u]);
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t u1 = __float_as_uint(x[u]);
+        const float r1 = x[u] - __uint_as_float(u1 & 0xffff0000u);
+        const uint32_t u2 = __float_as_uint(r1);
+        const float r2 = r1 - __uint_as_float(u2 & 0xffff0000u);
+        t[0][u] = u1;
+        t[1][u] = u2;
+        t[2][u] = __float_as_uint(r2);
+      }
 #pragma unroll
-      for (int sp = 0; sp < 3; ++sp)
-        *(uint2*)&stg[bsel][sp][r * RW + c4] = make_uint2(h[sp][0] | (h[sp][1] << 16), h[sp][2] | (h[sp][3] << 16));
+      for (int sp = 0; sp < 3; ++sp)   // high halves: (t[u] >> 16) | (t[u + 1] & 0xffff0000)
+        *(uint2*)&stg[bsel][sp][r * RW + c4] =
+            make_uint2(__builtin_amdgcn_perm(t[sp][1], t[sp][0], 0x07060302u),
+                       __builtin_amdgcn_perm(t[sp][3], t[sp][2], 0x07060302u));
     }
-    if (tid < 16) cst[bsel][tid] = ldc;
+    if (tid < 16) cst[bsel][tid] = sc;
   };
   float* B = &buf[wave][0][0];
-  const int64_t tiles_total = (n + NPT - 1) / NPT;
-  int64_t seg = blockIdx.x;
-  fetch(seg * TPS);
-  stage(0);
+  // this workgroup's tiles in order: segments blockIdx.x, blockIdx.x + gridDim.x, ...
+  const int64_t nmine = (nseg - (int64_t)blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const int64_t Q = nmine * TPS;
+  auto tile_of = [&](int64_t q) { return ((int64_t)blockIdx.x + (q / TPS) * gridDim.x) * TPS + q % TPS; };
+  const int64_t last_tile = tile_of(Q - 1);
+  auto tile_at = [&](int64_t q) { return q < Q ? tile_of(q) : last_tile; };
+#pragma unroll
+  for (int j = 0; j < NPF; ++j) fetch(tile_at(j), ld[j], ldc[j]);
+  stage(ld[0], ldc[0], tile_at(0), 0);
   __syncthreads();
+  // the scores of tile q are finished (plane max, LDS buffer) while tile q + 1's MFMAs run
+  auto finish = [&](const f32x4 (&acc)[4], const float (&cr)[4], int64_t q) {
+    const int tt = (int)(q % TPS);
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = a.sigma * acc[pb][e] + cr[e];
+      // row 4kg+e is plane (4kg+e) % R of node (4kg+e) / R: the max over a node's planes
+      // within the lane's four rows, then across lane groups for R > 4
+      float* dst = B + (pb * 16 + col) * (SG_NODES + 1) + tt * NPT;
+      if constexpr (R == 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[4 * kg + e] = v[e];
+      } else if constexpr (R == 2) {
+        dst[2 * kg] = fmaxf(v[0], v[1]);
+        dst[2 * kg + 1] = fmaxf(v[2], v[3]);
+      } else {
+        float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+        if constexpr (R >= 8) m = fmaxf(m, __shfl_xor(m, 16));
+        if constexpr (R >= 16) m = fmaxf(m, __shfl_xor(m, 32));
+        if ((kg & (R / 4 - 1)) == 0) dst[(4 * kg) / R] = m;
+      }
+    }
+    if (tt == TPS - 1) {
+      // the wave's 64 rows of this segment (the buffer is the wave's own)
+      wave_sync_lds();
+      const int64_t node0 = ((int64_t)blockIdx.x + (q / TPS) * gridDim.x) * SG_NODES;
+      const int64_t nn = min((int64_t)SG_NODES, n - node0);
+      constexpr int RPI = 64 / SG_NODES;       // rows per store instruction
+#pragma unroll 4
+      for (int r = 0; r < 64; r += RPI) {
+        const int pr = r + lane / SG_NODES, jn = lane % SG_NODES;
+        const int p = p0 + pr;
+        if (p < P && jn < nn) out[(int64_t)p * sst + node0 + jn] = B[pr * (SG_NODES + 1) + jn];
+      }
+      wave_sync_lds();
+    }
+  };
+  f32x4 accp[4];
+  float crp[4];
   int cur = 0;
-  for (; seg < nseg; seg += gridDim.x) {
-    const int64_t node0 = seg * SG_NODES;
-    for (int tt = 0; tt < TPS; ++tt) {
-      // the next tile (of this segment, else of the next one) into registers
-      int64_t nxt = -1;
-      if (tt + 1 < TPS) nxt = seg * TPS + tt + 1;
-      else if (seg + gridDim.x < nseg) nxt = (seg + gridDim.x) * TPS;
-      if (nxt >= tiles_total) nxt = -1;
-      if (nxt >= 0) fetch(nxt);
+  for (int64_t q0 = 0; q0 < Q; q0 += NPF) {
+#pragma unroll
+    for (int j = 0; j < NPF; ++j) {
+      const int64_t q = q0 + j;
+      fetch(tile_at(q + NPF), ld[j], ldc[j]);   // tile q was staged already
+      f32x4 acc[4];
+      float cr[4];
       if (active) {
         bf16x8 s1[NL], s2[NL], s3[NL];
 #pragma unroll
@@ -469,9 +429,10 @@ __global__ __launch_bounds__(256) void prefill_score_seg_kernel(PrefillArgs a) {
           s2[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)&stg[cur][1][off]);
           s3[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)&stg[cur][2][off]);
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cr[e] = cst[cur][4 * kg + e];
         // plane rows x pairs: lane (kg, col) gets rows 4kg..4kg+3 of pair col; four
         // independent accumulation chains (one per 16-pair block), smallest terms first
-        f32x4 acc[4];
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -483,47 +444,18 @@ __global__ __launch_bounds__(256) void prefill_score_seg_kernel(PrefillArgs a) {
 #pragma unroll
           for (int pb = 0; pb < 4; ++pb) acc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s1[kk], qa[pb][kk], acc[pb], 0, 0, 0);
         }
-        float cr[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cr[e] = cst[cur][4 * kg + e];
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = a.sigma * acc[pb][e] + cr[e];
-          // row 4kg+e is plane (4kg+e) % R of node (4kg+e) / R: the max over a node's
-          // planes within the lane's four rows, then across lane groups for R > 4
-          float* dst = B + (pb * 16 + col) * (SG_NODES + 1) + tt * NPT;
-          if constexpr (R == 1) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dst[4 * kg + e] = v[e];
-          } else if constexpr (R == 2) {
-            dst[2 * kg] = fmaxf(v[0], v[1]);
-            dst[2 * kg + 1] = fmaxf(v[2], v[3]);
-          } else {
-            float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-            if constexpr (R >= 8) m = fmaxf(m, __shfl_xor(m, 16));
-            if constexpr (R >= 16) m = fmaxf(m, __shfl_xor(m, 32));
-            if ((kg & (R / 4 - 1)) == 0) dst[(4 * kg) / R] = m;
-          }
-        }
+        if (q > 0) finish(accp, crp, q - 1);
       }
-      if (nxt >= 0) stage(cur ^ 1);
+      if (q + 1 < Q) stage(ld[(j + 1) % NPF], ldc[(j + 1) % NPF], tile_of(q + 1), cur ^ 1);
       __syncthreads();
       cur ^= 1;
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) accp[pb] = acc[pb];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) crp[e] = cr[e];
     }
-    // the wave's 64 rows of this segment, 32 nodes each (the buffer is the wave's own)
-    const int64_t nn = min((int64_t)SG_NODES, n - node0);
-    if (active) {
-#pragma unroll 4
-      for (int r = 0; r < 64; r += 2) {
-        const int pr = r + (lane >> 5), j = lane & 31;
-        const int p = p0 + pr;
-        if (p < P && j < nn) out[(int64_t)p * sst + node0 + j] = B[pr * (SG_NODES + 1) + j];
-      }
-    }
-    wave_sync_lds();
   }
+  if (active) finish(accp, crp, Q - 1);
 }
 
 // Each pair's tail: nodes right of its own rightmost node do not exist (-inf), the rightmost
@@ -553,7 +485,7 @@ __global__ __launch_bounds__(64) void prefill_tail_kernel(PrefillArgs a) {
 
 // ---------------------------------------------------------------- per-pair selection
 constexpr int PS_THREADS = 512;
-constexpr int PS_LIST = 8192;   // frontier nodes held in LDS (more: the level is read from global memory)
+constexpr int PS_LIST = 6144;   // frontier nodes held in LDS (more: the level is read from global memory)
 constexpr int PS_TIES = 256;    // boundary sub-bin nodes resolved pairwise (more: radix select)
 constexpr int PS_KWORDS = 2048; // kept bitmap words built in LDS (a longer level: in global memory)
 
@@ -622,7 +554,7 @@ __device__ __forceinline__ int32_t ps_scan(int32_t v, int32_t* wsum, int32_t& to
 // Nodes outside the pair's tree score -inf and drop out.
 constexpr int PS_UNROLL = 8;
 
-__global__ __launch_bounds__(PS_THREADS) void prefill_select_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(PS_THREADS, 4) void prefill_select_kernel(PrefillArgs a) {
   constexpr int NW = PS_THREADS / 64;
   __shared__ int32_t fl[PS_LIST];
   __shared__ float fs[PS_LIST];

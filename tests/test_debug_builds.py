@@ -23,9 +23,12 @@ from test_abi import declared_functions  # noqa: E402
 
 
 def _lib(variant):
+    """The variant's library, built again when any source or header is newer than it."""
     from hierarchical_tree_indexed_03_amd import build_lib
     path = build_lib.VARIANTS[variant]["out"]
-    if not os.path.exists(path):
+    srcs = glob.glob(os.path.join(ROOT, "hierarchical_tree_indexed_03_amd", "csrc", "*.*")) + \
+        glob.glob(os.path.join(ROOT, "include", "*.h"))
+    if not os.path.exists(path) or os.path.getmtime(path) < max(os.path.getmtime(f) for f in srcs):
         build_lib.build(variant=variant)
     return path
 
