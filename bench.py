@@ -31,6 +31,7 @@ from workloads import configs as wc, gen  # noqa: E402
 
 METRIC = "ZHA decode queries/s per layer at 256K and 16M ctx; % HBM roofline; build tok/s"
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
 
 
 def log(*a):
@@ -60,6 +61,10 @@ def parse():
                     help="extra steps timed one by one after a 1 GiB scratch write that evicts L2 and MALL")
     ap.add_argument("--crossover", action="store_true",
                     help="light-router sweep over N: ZHA vs dense decode, crossover context (own JSON line)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time the batched causal prefill alone (its own JSON line)")
+    ap.add_argument("--prefill-tokens", type=int, default=64, help="tokens prefilled in --prefill")
+    ap.add_argument("--prefill-batch", default="8,16,32,64", help="sub-batch sizes of --prefill")
     ap.add_argument("--fit", action="store_true",
                     help="reference-query fitting (zha_fit_step) at a 32K-token context on the deep and light "
                          "geometries: step time per stage, loss, routing before and after (own JSON line)")
@@ -596,6 +601,106 @@ def fit_bench(args):
     print(json.dumps(rec))
 
 
+def prefill_legs(zha, tree, w, Kd, Vd, Qd, Rd, n0, mp, batches, dev):
+    """Causal prefill of the mp tokens before n0 onto a tree built over n0 - mp: the
+    per-token loop (zha_prefill: append + routed decode per token) once, then the batched
+    prefill (zha_prefill_batched) at each sub-batch size: median of 3 timed runs, the time of
+    each stage (HIP events around its launches in a separate run), and the scoring pass
+    against its bounds.  Inputs resident in HBM; every run starts from a fresh build
+    (untimed).  Returns (per_token, batched)."""
+    import torch
+    R, d, g, L = w.num_ref, w.head_dim, w.group, w.levels
+    Kc, Vc = Kd[:, n0 - mp:n0].contiguous(), Vd[:, n0 - mp:n0].contiguous()
+    Qc = Qd[:mp].contiguous()
+    pout = torch.empty(mp, w.num_q_heads, d, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        tree.build(Kd, Vd, n0 - mp, Rd)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    timed(lambda: tree.prefill(Kc, Vc, Qc, pout))
+    pm = timed(lambda: tree.prefill(Kc, Vc, Qc, pout))
+    per_token = {"tokens": mp, "onto_tokens": n0 - mp, "ms": round(pm, 4), "ms_per_token": round(pm / mp, 4),
+                 "tokens_per_s": round(mp / (pm * 1e-3), 1)}
+    log(f"[bench] prefill of {mp} tokens (append + decode each): {pm:.3f} ms, {pm / mp:.4f} ms/token")
+    pout2 = torch.empty_like(pout)
+    batched = {}
+    nodes_all = sum(-(-n0 // w.block ** l) for l in range(1, L + 1))
+    for bt in batches:
+        if bt > mp:
+            continue
+        timed(lambda: tree.prefill_batched(Kc, Vc, Qc, bt, out=pout2))
+        bm = float(np.median([timed(lambda: tree.prefill_batched(Kc, Vc, Qc, bt, out=pout2)) for _ in range(3)]))
+        stage = {}
+        for key in ("prefill_prep", "prefill_score", "prefill_select", "prefill_attend", "build_tile"):
+            tree.build(Kd, Vd, n0 - mp, Rd)
+            torch.cuda.synchronize()
+            zha.zha_profile_start(tree.handle, key)
+            tree.prefill_batched(Kc, Vc, Qc, bt, out=pout2)
+            torch.cuda.synchronize()
+            ms_, _ = zha.zha_profile_stop(tree.handle)
+            stage[key] = round(ms_, 4)
+        # the scoring pass against its bounds: every node's planes read once per sub-batch,
+        # 2 R d flops per (pair, node) counted in float32 (each computed as three bf16 MFMA
+        # products, so the MFMA ceiling for it is a third of the bf16 peak)
+        nsub = -(-mp // bt)
+        sb = w.num_kv_heads * nodes_all * R * (d + 1) * 4
+        sf = sum(2.0 * w.num_kv_heads * min(bt, mp - i * bt) * g * nodes_all * R * d for i in range(nsub))
+        sms = stage["prefill_score"] / nsub
+        score = {"ms_per_sub_batch": round(sms, 4), "alg_bytes": round(sb),
+                 "achieved_GBps": round(sb / (sms * 1e-3) / 1e9, 1),
+                 "frac_hbm": round(sb / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "fp32_TFLOPs": round(sf / nsub / (sms * 1e-3) / 1e12, 2),
+                 "frac_bf16_mfma_third": round(sf / nsub / (sms * 1e-3) / 1e12 / (BF16_PEAK_TFLOPS / 3), 4),
+                 "note": "score + tail launches per sub-batch (the tail is ~2% of it)"}
+        batched[str(bt)] = {"ms": round(bm, 4), "tokens_per_s": round(mp / (bm * 1e-3), 1),
+                            "speedup_vs_per_token": round(pm / bm, 3), "stage_ms": stage, "score": score,
+                            "max_abs_diff_vs_per_token": round(float((pout2 - pout).abs().max()), 6)}
+        log(f"[bench] batched prefill of {mp} tokens, {bt} per sub-batch: {bm:.3f} ms "
+            f"({mp / (bm * 1e-3):.0f} tok/s, {pm / bm:.2f}x the per-token loop); stages " +
+            ", ".join(f"{k}={v:.3f}" for k, v in stage.items()))
+    return per_token, batched
+
+
+def prefill_bench(args):
+    """`--prefill`: the batched causal prefill alone on one workload (deep by default): the
+    last `--prefill-tokens` tokens of the cache prefilled onto a tree over the rest, per
+    token and in sub-batches of each `--prefill-batch` size.  Prints its own JSON line."""
+    import torch
+    from hierarchical_tree_indexed_03_amd import zha
+    w = wc.NAMED[args.workload].with_(steps=0, appends=False)
+    n0, mp = w.n_tokens, args.prefill_tokens
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    Kd = torch.empty(w.num_kv_heads, w.capacity, w.head_dim, dtype=tdt, device=dev)
+    Vd = torch.empty_like(Kd)
+    for stream, hh, lo, hi, rows in gen.iter_kv_chunks(w):
+        (Kd if stream == gen.STREAM_K else Vd)[hh, lo:hi] = torch.from_numpy(rows).to(tdt).to(dev)
+    fetch = lambda kv, idx: Kd[kv, torch.as_tensor(idx, device=dev)].float().cpu().numpy()
+    Qd = torch.from_numpy(np.stack([gen.step_queries(w, s_, n0 - mp + s_ + 1, fetch) for s_ in range(mp)])).to(tdt).to(dev)
+    Rd = torch.from_numpy(gen.ref_queries(w)).to(tdt).to(dev)
+    cfg = zha.make_config(w.head_dim, w.num_kv_heads, w.num_q_heads, w.block, w.levels, w.num_ref,
+                          w.capacity, w.dtype, w.top_p, w.keep_sink, w.planes)
+    tree = zha.Tree(cfg)
+    batches = tuple(int(x) for x in args.prefill_batch.split(","))
+    per_token, batched = prefill_legs(zha, tree, w, Kd, Vd, Qd, Rd, n0, mp, batches, dev)
+    best = max(batched.values(), key=lambda r: r["tokens_per_s"])
+    rec = {"metric": "ZHA batched causal prefill tokens/s per layer", "value": best["tokens_per_s"],
+           "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "dtype": "bf16+f32", "data": "synthetic",
+           "config": {"workload": f"{w.name}_{n0}_prefill{mp}", "kv_tokens": n0, "prefill_tokens": mp,
+                      "head_dim": w.head_dim, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                      "block": w.block, "levels": w.levels, "num_ref": w.num_ref, "top_p": w.top_p},
+           "per_token_loop": per_token, "batched": batched, "src_sha": src_sha()}
+    print(json.dumps(rec), flush=True)
+    tree.close()
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -613,6 +718,8 @@ def main():
         return crossover(args)
     if args.fit:
         return fit_bench(args)
+    if args.prefill:
+        return prefill_bench(args)
     base = wc.NAMED[args.workload]
     steps = args.steps if args.steps is not None else (base.steps or 64)
     total = args.warmup + steps + args.cold_steps
@@ -912,62 +1019,12 @@ def main():
                     "single_append_ms": round(probe_ms.get("append", float("nan")), 4)}
         log(f"[bench] append_n of {m_app} tokens onto {n0 - m_app}: {am:.3f} ms "
             f"({m_app / (am * 1e-3) / 1e6:.1f} M tok/s; one-token append {probe_ms.get('append', float('nan')):.4f} ms)")
-        # causal multi-query prefill of 64 tokens (append + routed decode per token)
-        mp = min(64, total)
-        tree3.build(Kd, Vd, n0 - mp, Rd)
-        pout = torch.empty(mp, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
-        tree3.prefill(Kd[:, n0 - mp:n0].contiguous(), Vd[:, n0 - mp:n0].contiguous(), Qd[:mp].contiguous(), pout)
-        tree3.build(Kd, Vd, n0 - mp, Rd)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        tree3.prefill(Kd[:, n0 - mp:n0].contiguous(), Vd[:, n0 - mp:n0].contiguous(), Qd[:mp].contiguous(), pout)
-        e1.record()
-        torch.cuda.synchronize()
-        pm = e0.elapsed_time(e1)
-        append_n["prefill"] = {"tokens": mp, "ms": round(pm, 4), "ms_per_token": round(pm / mp, 4),
-                               "tokens_per_s": round(mp / (pm * 1e-3), 1)}
-        log(f"[bench] prefill of {mp} tokens (append + decode each): {pm:.3f} ms, {pm / mp:.4f} ms/token")
-        # the same tokens through the batched causal prefill, several sub-batch sizes
-        Kc2, Vc2 = Kd[:, n0 - mp:n0].contiguous(), Vd[:, n0 - mp:n0].contiguous()
-        Qc2 = Qd[:mp].contiguous()
-        pout2 = torch.empty_like(pout)
-        batched = {}
-        for bt in (8, 16, 32, 64):
-            if bt > mp:
-                continue
-            tree3.build(Kd, Vd, n0 - mp, Rd)
-            tree3.prefill_batched(Kc2, Vc2, Qc2, bt, out=pout2)
-            b_ms = []
-            for _ in range(3):
-                tree3.build(Kd, Vd, n0 - mp, Rd)
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                tree3.prefill_batched(Kc2, Vc2, Qc2, bt, out=pout2)
-                e1.record()
-                torch.cuda.synchronize()
-                b_ms.append(e0.elapsed_time(e1))
-            stage = {}
-            for key in ("prefill_prep", "prefill_score", "prefill_select", "prefill_attend", "build_tile"):
-                tree3.build(Kd, Vd, n0 - mp, Rd)
-                torch.cuda.synchronize()
-                zha.zha_profile_start(tree3.handle, key)
-                tree3.prefill_batched(Kc2, Vc2, Qc2, bt, out=pout2)
-                torch.cuda.synchronize()
-                ms_, n_ = zha.zha_profile_stop(tree3.handle)
-                stage[key] = round(ms_, 4)
-            bm = float(np.median(b_ms))
-            batched[str(bt)] = {"ms": round(bm, 4), "tokens_per_s": round(mp / (bm * 1e-3), 1),
-                                "speedup_vs_per_token": round(pm / bm, 3), "stage_ms": stage,
-                                "max_abs_diff_vs_per_token": round(float((pout2 - pout).abs().max()), 6)}
-            log(f"[bench] batched prefill of {mp} tokens, {bt} per sub-batch: {bm:.3f} ms "
-                f"({mp / (bm * 1e-3):.0f} tok/s, {pm / bm:.2f}x the per-token loop); stages " +
-                ", ".join(f"{k}={v:.3f}" for k, v in stage.items()))
+        # causal multi-query prefill of the last 64 tokens: per token, then batched
+        per_token, batched = prefill_legs(zha, tree3, w, Kd, Vd, Qd, Rd, n0, min(64, total), (8, 16, 32, 64), dev)
+        append_n["prefill"] = per_token
         append_n["prefill_batched"] = batched
-        del Kc2, Vc2, Qc2, pout2
         tree3.close()
-        del tree3, Kc, Vc, pout
+        del tree3, Kc, Vc
 
     # stream-read probe: practical HBM read bandwidth of a plain streaming kernel (2 GiB)
     sst = torch.cuda.current_stream().cuda_stream

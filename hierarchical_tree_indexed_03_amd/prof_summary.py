@@ -4,6 +4,7 @@
     python -m hierarchical_tree_indexed_03_amd.prof_summary pmc FETCH_DIR WRITE_DIR WORKLOAD --cmd "..." [--out FILE]
     python -m hierarchical_tree_indexed_03_amd.prof_summary mfma DIR WORKLOAD --trace TRACE_DIR --cmd "..." [--out FILE]
     python -m hierarchical_tree_indexed_03_amd.prof_summary stats DIR --prefix fit_,build_ --title "..." --cmd "..." [--out FILE]
+        [--fetch FETCH_DIR --write WRITE_DIR --fetch-scale 2.0 --write-scale 1.0]
 
 ``trace`` reads ``*_kernel_trace.csv`` (``rocprofv3 --kernel-trace --stats --output-format csv``)
 and attributes every dispatch of a decode (route_prep ... combine) to its router level: the
@@ -185,6 +186,22 @@ def cmd_stats(a):
         lines.append(f"| {short(r['Name'])[:70]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{100 * float(r['TotalDurationNs']) / total:.1f}% |")
+    if a.fetch and a.write:
+        # measured HBM bytes per dispatch: FETCH_SIZE and WRITE_SIZE (KiB) times the scale the
+        # same counters need on the plain 1 GiB copy kernel
+        per = defaultdict(lambda: [[], []])
+        for i, (d, c) in enumerate(((a.fetch, "FETCH_SIZE"), (a.write, "WRITE_SIZE"))):
+            for r in read_pmc(d, c):
+                if short(r["name"]).startswith(pre):
+                    per[short(r["name"])][i].append(r["v"])
+        lines += ["", f"Measured HBM traffic per dispatch (FETCH_SIZE x {a.fetch_scale}, WRITE_SIZE x "
+                      f"{a.write_scale}, the copy-kernel calibration):", "",
+                  "| kernel | dispatches | read MB | written MB |", "|---|---:|---:|---:|"]
+        for k in sorted(per, key=lambda k: -sum(per[k][0]) / max(1, len(per[k][0]))):
+            fv, wv = per[k]
+            if fv and wv:
+                lines.append(f"| {k[:70]} | {len(fv)} | {sum(fv) / len(fv) * 1024 * a.fetch_scale / 1e6:.1f} | "
+                             f"{sum(wv) / len(wv) * 1024 * a.write_scale / 1e6:.1f} |")
     text = "\n".join(lines) + "\n"
     if a.out:
         with open(a.out, "w") as f:
@@ -339,6 +356,10 @@ def main():
     x.add_argument("--title", default="")
     x.add_argument("--cmd", default="")
     x.add_argument("--out", default=None)
+    x.add_argument("--fetch", default=None, help="directory of a --pmc FETCH_SIZE run")
+    x.add_argument("--write", default=None, help="directory of a --pmc WRITE_SIZE run")
+    x.add_argument("--fetch-scale", type=float, default=2.0)
+    x.add_argument("--write-scale", type=float, default=1.0)
     a = ap.parse_args()
     {"trace": cmd_trace, "pmc": cmd_pmc, "mfma": cmd_mfma, "stats": cmd_stats}[a.mode](a)
 
