@@ -99,6 +99,8 @@ struct PrefillArgs {
   const void* K;          // [Hkv][cap][D] cache dtype
   const void* refs;       // [Hkv][R][D]
   const void* q;          // [mb][Hq][D] cache dtype (this sub-batch)
+  const void* V;          // [Hkv][cap][D] cache dtype
+  int32_t keep_sink;
   int64_t cap;
   int64_t N0;             // tokens before the sub-batch
   int32_t mb, mbmax, P, hkv, hq, g, b, levels, R, D;
@@ -123,6 +125,10 @@ hipError_t launch_prefill_score(const PrefillArgs& a, int D, int R, hipStream_t 
 hipError_t launch_prefill_tail(const PrefillArgs& a, int D, int R, hipStream_t st);
 hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_gather(const PrefillArgs& a, hipStream_t st);
+// Union attention of a sub-batch (bf16 caches): partials [Hkv][P][splits][D + 2] in `part`,
+// then the merged output of query i, head h at out + (i * Hq + h) * D.
+int prefill_attend_splits(int hkv, int P);
+hipError_t launch_prefill_attend(const PrefillArgs& a, float* part, float* out, int D, hipStream_t st);
 // Routed attention and combine for a.nq... queries of one launch (grid.y = query).
 hipError_t launch_attend_batch(const AttnArgs& a, bool bf16, int D, int nq, hipStream_t st);
 

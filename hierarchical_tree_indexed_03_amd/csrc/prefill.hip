@@ -29,6 +29,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "route_util.hpp"
+#include "qk_tile.hpp"
 
 namespace zha {
 
@@ -547,17 +548,20 @@ __device__ __forceinline__ int32_t ps_scan(int32_t v, int32_t* wsum, int32_t& to
 
 // One workgroup per (pair, KV head) walks the levels from the top.  The level's frontier
 // (every node at the top, else the children of the nodes kept one level up, in node order)
-// is held in one of two ways for the passes that follow:
-//   list  at most PS_LIST nodes: node ids and scores in LDS;
-//   scan  a longer frontier: every pass reads the whole level from global memory (PS_UNROLL
-//         loads in flight per thread), the frontier test from the parents' kept bitmap.
+// is held in one of three ways for the passes that follow:
+//   list    at most PS_LIST nodes: node ids and scores in LDS;
+//   sparse  a longer frontier covering under a quarter of its level: every pass walks the
+//           parents' kept bitmap (in LDS when it fits) and reads the kept parents' children;
+//   scan    a denser frontier: every pass reads the whole level from global memory
+//           (PS_UNROLL loads in flight per thread), the frontier test from that bitmap.
 // Nodes outside the pair's tree score -inf and drop out.
 constexpr int PS_UNROLL = 8;
 
 __global__ __launch_bounds__(PS_THREADS, 4) void prefill_select_kernel(PrefillArgs a) {
   constexpr int NW = PS_THREADS / 64;
-  __shared__ int32_t fl[PS_LIST];
-  __shared__ float fs[PS_LIST];
+  __shared__ uint32_t lbuf[2 * PS_LIST];   // the list (ids, scores), or the parents' kept bitmap
+  int32_t* fl = (int32_t*)lbuf;
+  float* fs = (float*)(lbuf + PS_LIST);
   __shared__ unsigned long long h[NB1];
   __shared__ int32_t tie_e[PS_TIES];
   __shared__ float tie_s[PS_TIES];
@@ -614,16 +618,17 @@ __global__ __launch_bounds__(PS_THREADS, 4) void prefill_select_kernel(PrefillAr
       }
     }
     const bool list = nf <= PS_LIST;
+    const bool sparse = !list && !top && nf * 4 < n;
     // past the list: the parents' kept bitmap goes to LDS (in the list's space) when it fits
-    uint32_t* pbits = (uint32_t*)fl;
-    const bool lds_bits = !list && !top && nwp <= PS_LIST;
+    uint32_t* pbits = lbuf;
+    const bool lds_bits = !list && !top && nwp <= 2 * PS_LIST;
     __syncthreads();
     if (lds_bits)
       for (int64_t w = tid; w < nwp; w += PS_THREADS) pbits[w] = ld_agent(kp + w);
-    // kept marks: LDS bitmap (copied out at the end) or the global one; a listed frontier
-    // sets bits one node at a time, so its bitmap starts cleared (the other modes write every
-    // word in their classification pass)
-    if (list) {
+    // kept marks: LDS bitmap (copied out at the end) or the global one; a listed or sparse
+    // frontier sets bits a node or a parent at a time, so its bitmap starts cleared (a
+    // scanned level writes every word in its classification pass)
+    if (list || sparse) {
       if (lds_kept)
         for (int64_t w = tid; w < nw; w += PS_THREADS) kl[w] = 0u;
       else
@@ -635,10 +640,18 @@ __global__ __launch_bounds__(PS_THREADS, 4) void prefill_select_kernel(PrefillAr
       const int64_t pn = k >> lb;
       return ((lds_bits ? pbits[pn >> 5] : ld_agent(kp + (pn >> 5))) >> (pn & 31)) & 1u;
     };
+    auto pword = [&](int64_t w) -> uint32_t { return lds_bits ? pbits[w] : ld_agent(kp + w); };
     // f(node, score) for every entry (score -inf outside the frontier)
     auto each = [&](auto&& f) {
       if (list) {
         for (int64_t k = tid; k < nf; k += PS_THREADS) f((int64_t)fl[k], fs[k]);
+      } else if (sparse) {
+        for (int64_t w = tid; w < nwp; w += PS_THREADS)
+          for (uint32_t r = pword(w); r; r &= r - 1u) {
+            const int64_t first = (32 * w + __ffs(r) - 1) << lb;
+            const int64_t last = min(first + b, n);
+            for (int64_t e = first; e < last; ++e) f(e, row[e]);
+          }
       } else {
         for (int64_t k0 = tid; k0 < n; k0 += (int64_t)PS_UNROLL * PS_THREADS) {
           float xs[PS_UNROLL];
@@ -704,6 +717,31 @@ __global__ __launch_bounds__(PS_THREADS, 4) void prefill_select_kernel(PrefillAr
         if (bs.bin < b1) keep(e);
         else if (bs.bin == b1) atomicAdd(&h[bs.sub], (unsigned long long)mass_of(x, M));
       });
+    } else if (sparse) {
+      // a kept parent's children share bitmap words with no other parent's (b a power of
+      // two): their kept bits go in with one atomic per word
+      uint32_t* kw = lds_kept ? kl : kb;
+      for (int64_t w = tid; w < nwp; w += PS_THREADS)
+        for (uint32_t r = pword(w); r; r &= r - 1u) {
+          const int64_t first = (32 * w + __ffs(r) - 1) << lb;
+          const int64_t last = min(first + b, n);
+          uint32_t m = 0u;
+          for (int64_t e = first; e < last; ++e) {
+            const float x = row[e];
+            if (x != -INFINITY) {
+              const BinSub bs = bin_of(x, M);
+              if (bs.bin < b1) m |= 1u << (e & 31);
+              else if (bs.bin == b1) atomicAdd(&h[bs.sub], (unsigned long long)mass_of(x, M));
+            }
+            if ((e & 31) == 31 || e + 1 == last) {
+              if (m) {
+                if (b >= 32) kw[e >> 5] = m;   // a whole word of this parent's
+                else atomicOr(&kw[e >> 5], m);
+              }
+              m = 0u;
+            }
+          }
+        }
     } else {
       // each wave's 64 consecutive nodes of a round give two kept words by one ballot
       for (int64_t k0 = tid; k0 - lane < n; k0 += (int64_t)PS_UNROLL * PS_THREADS) {
@@ -862,6 +900,226 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(PrefillArgs a) {
   if (tid == 0) a.cnt0[(int64_t)i * a.hkv + kv] = base;
 }
 
+// ---------------------------------------------------------------- union attention
+// The routed attention of a whole sub-batch on bf16 MFMA.  The queries of a sub-batch
+// keep overlapping block sets (on deep each head keeps about a quarter of the blocks and
+// their union is nearly all of them), so instead of one gather list per query the K/V
+// tiles are read once for all pairs: a workgroup takes a run of level-1 bitmap words
+// (32 blocks each) of one KV head and 128 pairs (a wave 32 of them, two MFMA blocks);
+// per word the wave ORs its pairs' kept words and skips the word, a 32-token tile, or a
+// 16-pair block's work on a tile, when none of those pairs keeps a block there; per tile
+// S^T = K.Q^T (tokens x pairs), each pair
+// masked to its own kept blocks, its tokens up to its position and the sink, an online
+// softmax per pair, and P.V with the V tile transposed through LDS (the dense MFMA
+// attention's scheme, with pairs in place of heads).  Partials (max, sum, o) per pair and
+// split are merged by prefill_combine_kernel.
+constexpr int PA_NPB = 2;        // 16-pair MFMA blocks per wave
+constexpr int PA_CHUNK = 4 * 16 * PA_NPB;   // pairs per workgroup
+constexpr int PA_WGS = 512;      // workgroups of one launch (two per compute unit)
+constexpr int PA_SPLITS = 128;   // splits per (KV head, pair chunk), at most
+constexpr int PA_VS = 36;        // LDS row stride of the transposed V tile (bf16)
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void prefill_attend_kernel(PrefillArgs a, float* part, int nsplit) {
+  constexpr int NK = D / 32;      // 8-element groups per lane of a K row or a query
+  constexpr int NM = D / 16;      // output dim blocks
+  __shared__ __align__(16) uint16_t vt_all[4][D * PA_VS];
+  __shared__ float al_all[4][PA_NPB][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int kv = (int)blockIdx.y % a.hkv, chunk = (int)blockIdx.y / a.hkv, split = blockIdx.x;
+  const int P = a.P, g = a.g, lb = __ffs(a.b) - 1;
+  const int p0 = chunk * PA_CHUNK + wave * 16 * PA_NPB;
+  if (p0 >= P) return;                        // a whole wave; no workgroup barriers below
+  const int64_t nend = a.N0 + a.mb;          // tokens in the tree
+  const int64_t nw = (a.nl[1] + 31) >> 5;
+  const int64_t wper = (nw + nsplit - 1) / nsplit;
+  const int64_t w0 = (int64_t)split * wper, w1 = min(nw, w0 + wper);
+  const bf16_t* Kb = (const bf16_t*)a.K + (int64_t)kv * a.cap * D;
+  const bf16_t* Vb = (const bf16_t*)a.V + (int64_t)kv * a.cap * D;
+  uint16_t* Vt = vt_all[wave];
+  // the queries of the wave's 16-pair blocks (B operand: pair col, 8 elements per group)
+  bf16x8 qf[PA_NPB][NK];
+  int64_t posc[PA_NPB];                       // position of pair col of each block
+#pragma unroll
+  for (int pb = 0; pb < PA_NPB; ++pb) {
+    const int p = p0 + pb * 16 + col;
+    posc[pb] = p < P ? a.N0 + p / g : -1;
+    const bf16_t* qp = (const bf16_t*)a.q + ((int64_t)(p / g) * a.hq + (int64_t)kv * g + p % g) * D + kg * (D / 4);
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (p < P) v = *(const uint4*)(qp + kk * 8);
+      qf[pb][kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  // lane j < 16 * PA_NPB reads the kept words of pair p0 + j
+  const bool lane_pair = lane < 16 * PA_NPB && p0 + lane < P;
+  const uint32_t* kbp = a.KB + a.koff[1] + ((int64_t)kv * a.P + p0 + (lane_pair ? lane : 0)) * a.kstride[1];
+  float m[PA_NPB], l[PA_NPB];
+  f32x4 acc[PA_NPB][NM];
+#pragma unroll
+  for (int pb = 0; pb < PA_NPB; ++pb) {
+    m[pb] = -INFINITY;
+    l[pb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) acc[pb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int vtk = lane & 31, vc = lane >> 5;  // V loads: token vtk, dims 16i + 8vc .. +7
+  for (int64_t w = w0; w < w1; ++w) {
+    const uint32_t kw = lane_pair ? kbp[w] : 0u;
+    uint32_t kc[PA_NPB], ab[PA_NPB];          // kept word of pair col of each block; the block's OR
+    uint32_t any = 0u;
+#pragma unroll
+    for (int pb = 0; pb < PA_NPB; ++pb) {
+      kc[pb] = __shfl(kw, pb * 16 + col);
+      uint32_t o = kc[pb];
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) o |= __shfl_xor(o, off);
+      if (a.keep_sink && w == 0) o |= 1u;     // the sink's block
+      ab[pb] = o;
+      any |= o;
+    }
+    if (!any) continue;
+    const int64_t tb = (w * 32) << lb;
+    const int64_t te = min(((w + 1) * 32) << lb, nend);
+    for (int64_t t0 = tb; t0 < te; t0 += 32) {
+      const int e0 = (int)((t0 >> lb) & 31);
+      const uint32_t span = lb >= 5 ? 1u : (1u << (32 >> lb)) - 1u;   // blocks of the tile
+      if (!((any >> e0) & span)) continue;
+      uint4 kf[2][NK];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int64_t tk = t0 + st * 16 + col;
+        if (tk < nend) Qk<bf16_t, D>::load_k(Kb + tk * D, kg, kf[st]);
+        else
+#pragma unroll
+          for (int kk = 0; kk < NK; ++kk) kf[st][kk] = make_uint4(0, 0, 0, 0);
+      }
+      uint4 vv[NM];
+      {
+        const int64_t tk = t0 + vtk;
+#pragma unroll
+        for (int i = 0; i < NM; ++i)
+          vv[i] = tk < nend ? *(const uint4*)(Vb + tk * D + 16 * i + 8 * vc) : make_uint4(0, 0, 0, 0);
+      }
+      uint32_t pbits[PA_NPB][4];              // P rows of pair col of each block, bf16 pairs
+      bool act[PA_NPB];                       // blocks with a pair keeping a block of the tile
+#pragma unroll
+      for (int pb = 0; pb < PA_NPB; ++pb) {
+        act[pb] = (ab[pb] >> e0) & span;
+        if (!act[pb]) continue;
+        float sc[2][4];
+        float rmax = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < NK; ++kk)
+            s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[st][kk]), qf[pb][kk], s4, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t tok = t0 + st * 16 + kg * 4 + e;
+            const bool kept = (kc[pb] >> ((tok >> lb) & 31)) & 1u;
+            const bool use = tok <= posc[pb] && (kept || (a.keep_sink && tok == 0));
+            sc[st][e] = use ? a.sigma * s4[e] : -INFINITY;
+            rmax = fmaxf(rmax, sc[st][e]);
+          }
+        }
+        rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
+        rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+        const float mn = fmaxf(m[pb], rmax);
+        const float alpha = mn == -INFINITY ? 1.f : expf(m[pb] - mn);
+        float rsum = 0.f;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const float q0 = mn == -INFINITY ? 0.f : expf(sc[st][e] - mn);
+            const float q1 = mn == -INFINITY ? 0.f : expf(sc[st][e + 1] - mn);
+            rsum += q0 + q1;
+            pbits[pb][st * 2 + e / 2] = f2bf16_bits(q0) | (f2bf16_bits(q1) << 16);
+          }
+        rsum += __shfl_xor(rsum, 16);
+        rsum += __shfl_xor(rsum, 32);
+        l[pb] = l[pb] * alpha + rsum;
+        m[pb] = mn;
+        if (kg == 0) al_all[wave][pb][col] = alpha;
+      }
+      // the V tile, transposed: Vt[dim][token]
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int d = 16 * i + 8 * vc + k;
+          Vt[d * PA_VS + vtk] = (uint16_t)((w4[k >> 1] >> (16 * (k & 1))) & 0xffffu);
+        }
+      }
+      wave_sync_lds();
+#pragma unroll
+      for (int pb = 0; pb < PA_NPB; ++pb) {
+        if (!act[pb]) continue;
+        float ah[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ah[e] = al_all[wave][pb][4 * kg + e];
+        const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(pbits[pb][0], pbits[pb][1], pbits[pb][2], pbits[pb][3]));
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[pb][i][e] *= ah[e];
+          const uint16_t* vrow = Vt + (16 * i + col) * PA_VS;
+          const uint2 lo = *(const uint2*)(vrow + 4 * kg);
+          const uint2 hi = *(const uint2*)(vrow + 16 + 4 * kg);
+          const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          acc[pb][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, acc[pb][i], 0, 0, 0);
+        }
+      }
+      wave_sync_lds();
+    }
+  }
+  // partials [Hkv][P][nsplit][D + 2]: acc[pb][i][e] = pair pb*16 + 4kg + e, dim 16i + col
+#pragma unroll
+  for (int pb = 0; pb < PA_NPB; ++pb) {
+    const int pc = p0 + pb * 16 + col;
+    if (kg == 0 && pc < P) {
+      float* pp = part + (((int64_t)kv * P + pc) * nsplit + split) * (D + 2);
+      pp[0] = m[pb];
+      pp[1] = l[pb];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pr = p0 + pb * 16 + 4 * kg + e;
+      if (pr < P) {
+        float* pp = part + (((int64_t)kv * P + pr) * nsplit + split) * (D + 2) + 2;
+#pragma unroll
+        for (int i = 0; i < NM; ++i) pp[16 * i + col] = acc[pb][i][e];
+      }
+    }
+  }
+}
+
+// Per pair: the splits merged (max-rescaled sums), o = sum / normaliser, written to the
+// query's output row.  Grid (P, Hkv), D threads.
+template <int D>
+__global__ __launch_bounds__(D) void prefill_combine_kernel(PrefillArgs a, const float* part, int nsplit, float* out) {
+  const int p = blockIdx.x, kv = blockIdx.y, d = threadIdx.x;
+  const float* pp = part + ((int64_t)kv * a.P + p) * nsplit * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[(int64_t)s * (D + 2)]);
+  float L = 0.f, O = 0.f;
+  if (M > -INFINITY)
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = pp[(int64_t)s * (D + 2)];
+      if (ms == -INFINITY) continue;
+      const float w = expf(ms - M);
+      L += pp[(int64_t)s * (D + 2) + 1] * w;
+      O += pp[(int64_t)s * (D + 2) + 2 + d] * w;
+    }
+  const int i = p / a.g, h = kv * a.g + p % a.g;
+  out[((int64_t)i * a.hq + h) * D + d] = L > 0.f ? O / L : 0.f;
+}
+
 // ---------------------------------------------------------------- launchers
 template <typename TIn, int D, int R>
 static void launch_prefix_t(const PrefillArgs& a, hipStream_t st) {
@@ -940,6 +1198,31 @@ hipError_t launch_prefill_select(const PrefillArgs& a, hipStream_t st) {
 
 hipError_t launch_prefill_gather(const PrefillArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(prefill_gather_kernel, dim3((unsigned)a.mb, (unsigned)a.hkv), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+int prefill_attend_splits(int hkv, int P) {
+  const int nchunk = (P + PA_CHUNK - 1) / PA_CHUNK;
+  int s = PA_WGS / (hkv * nchunk);
+  return s < 1 ? 1 : (s > PA_SPLITS ? PA_SPLITS : s);
+}
+
+hipError_t launch_prefill_attend(const PrefillArgs& a, float* part, float* out, int D, hipStream_t st) {
+  const int nchunk = (a.P + PA_CHUNK - 1) / PA_CHUNK;
+  const int ns = prefill_attend_splits(a.hkv, a.P);
+  if (D == 64) {
+    hipLaunchKernelGGL(prefill_attend_kernel<64>, dim3((unsigned)ns, (unsigned)(a.hkv * nchunk)), dim3(256), 0, st, a,
+                       part, ns);
+    hipLaunchKernelGGL(prefill_combine_kernel<64>, dim3((unsigned)a.P, (unsigned)a.hkv), dim3(64), 0, st, a,
+                       (const float*)part, ns, out);
+  } else if (D == 128) {
+    hipLaunchKernelGGL(prefill_attend_kernel<128>, dim3((unsigned)ns, (unsigned)(a.hkv * nchunk)), dim3(256), 0, st,
+                       a, part, ns);
+    hipLaunchKernelGGL(prefill_combine_kernel<128>, dim3((unsigned)a.P, (unsigned)a.hkv), dim3(128), 0, st, a,
+                       (const float*)part, ns, out);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -686,7 +686,8 @@ constexpr int PF_SPLITS = 16;       // attention splits per query and KV head, a
 // Lays out the batched-prefill workspace for sub-batches of up to `mbmax` queries; with
 // base == nullptr only the size is computed.  Level strides follow the tree's node
 // capacities, so every row starts 256-byte aligned.
-size_t prefill_layout(const zha_config& c, int mbmax, char* base, PrefillArgs* out, float** apart, int* pstride) {
+size_t prefill_layout(const zha_config& c, int mbmax, char* base, PrefillArgs* out, float** apart, int* pstride,
+                      float** upart = nullptr) {
   size_t off = 0;
   auto take = [&](size_t bytes) -> char* {
     off = (off + 255) & ~(size_t)255;
@@ -719,10 +720,19 @@ size_t prefill_layout(const zha_config& c, int mbmax, char* base, PrefillArgs* o
   a.cnt0 = (int32_t*)take((size_t)(mbmax * H) * 4);
   const int ps = (int)std::min<int64_t>(MAX_SPLITS, (int64_t)PF_SPLITS * H);
   float* ap = (float*)take((size_t)(mbmax * Q * ps * (D + 2)) * 4);
+  // union attention partials (bf16 caches): [Hkv][P'][splits(P')][D + 2] for every
+  // sub-batch size up to mbmax
+  int64_t up = 0;
+  for (int mb = 1; mb <= mbmax; ++mb) {
+    const int64_t pp = (int64_t)mb * (Q / H);
+    up = std::max<int64_t>(up, pp * prefill_attend_splits((int)H, (int)pp));
+  }
+  float* uap = c.dtype == ZHA_BF16 ? (float*)take((size_t)(H * up * (D + 2)) * 4) : nullptr;
   a.mbmax = mbmax;
   if (out) *out = a;
   if (apart) *apart = ap;
   if (pstride) *pstride = ps;
+  if (upart) *upart = uap;
   return (off + 255) & ~(size_t)255;
 }
 
@@ -755,13 +765,16 @@ zha_status zha_prefill_batched(zha_tree* t, const void* k_new, const void* v_new
                 (long long)c.capacity);
   PrefillArgs a;
   float* apart = nullptr;
+  float* upart = nullptr;
   int pstride = 0;
-  prefill_layout(c, batch, (char*)workspace, &a, &apart, &pstride);
+  prefill_layout(c, batch, (char*)workspace, &a, &apart, &pstride, &upart);
   const bool bf16 = c.dtype == ZHA_BF16;
   const int D = c.head_dim, R = c.num_ref, H = c.num_kv_heads, Q = c.num_q_heads, g = Q / H;
   const size_t es = bf16 ? 2 : 4, row = (size_t)D * es;
   a.dev = t->dev;
   a.K = t->K;
+  a.V = t->V;
+  a.keep_sink = c.keep_sink;
   a.refs = t->refs;
   a.cap = c.capacity;
   a.hkv = H;
@@ -775,6 +788,12 @@ zha_status zha_prefill_batched(zha_tree* t, const void* k_new, const void* v_new
   a.sigma = 1.0f / sqrtf((float)D);
   for (int l = 0; l <= MAXL; ++l) a.top_p[l] = t->top_p[l];
   const int resident = attend_resident_splits(bf16, D, false, H);
+  // attention: the union kernel reads each K/V tile once for all pairs of a sub-batch but
+  // each wave reads the tiles its 32 pairs keep, which pays where the heads keep most
+  // blocks (level-1 p >= 0.9: deep 256K 0.64 against 0.69 ms, wide 256K 1.0 against 2.1 ms
+  // per sub-batch of 32) and not where they keep few (ultra 16M, p 0.75: 24 against 7.5 ms);
+  // elsewhere one gather list per query
+  const bool union_attn = bf16 && t->top_p[1] >= 0.9f;
   t->pf_valid = false;
   for (int64_t s0 = 0; s0 < m; s0 += batch) {
     const int mb = (int)std::min<int64_t>(batch, m - s0);
@@ -812,11 +831,18 @@ zha_status zha_prefill_batched(zha_tree* t, const void* k_new, const void* v_new
     {
       ProfScope ps(t, "prefill_select", stream);
       e = launch_prefill_select(a, stream);
-      if (e == hipSuccess) e = launch_prefill_gather(a, stream);
+      if (e == hipSuccess && !union_attn) e = launch_prefill_gather(a, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "prefill select launch");
     t->pf_args = a;
     t->pf_valid = true;
+    if (union_attn) {
+      // the union attention over the kept bitmaps
+      ProfScope ps(t, "prefill_attend", stream);
+      e = launch_prefill_attend(a, upart, out + (size_t)s0 * Q * D, D, stream);
+      if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+      continue;
+    }
     AttnArgs at;
     memset(&at, 0, sizeof at);
     at.dev = t->dev;
