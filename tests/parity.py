@@ -3,17 +3,15 @@
 Tolerances (stated once here, used by every GPU test):
   * router scores: |gpu - oracle| <= 1e-4 absolute (fp32 planes and scores);
   * routed sets: at every level the GPU's kept set must be the oracle's top-p of the same
-    frontier under the oracle's scores.  Three departures are explained, nothing else:
-      - the mass band: a node whose oracle cumulative probability before it (in oracle rank
-        order) lies within 1e-5 of p may be kept or dropped (the rounding of the masses may
-        flip it);
+    frontier under the oracle's scores.  Two departures are explained, nothing else:
       - a near-tie swap: an oracle-kept node the GPU dropped, paired one to one with a node
         the GPU kept instead, whose oracle scores differ by at most the two nodes' score
-        tolerances and which the GPU's own scores rank ahead of the dropped one;
-      - the score band: the boundary node, when the oracle's cumulative probability before
-        it lies within what the measured score differences (each within tolerance) can move
-        it, and the GPU decided it exactly as the top-p of its own scores does.
-    The mass band and the score band are the only ways the kept count may differ.
+        tolerances and which the GPU's own scores rank ahead of the dropped one (pairs are
+        formed first, so that a swap whose added node happens to lie in the band does not
+        leave its dropped node unexplained);
+      - the mass band: a node whose oracle cumulative probability before it (in oracle rank
+        order) lies within 1e-5 of p may be kept or dropped (the rounding of the masses may
+        flip it); this is the only way the kept count may differ.
     End to end the comparison walks the GPU's own frontiers (each the existing children of
     the GPU's kept nodes one level up), so a legitimate departure never masks a later
     level; the number of departures is reported per test and bounded by stated rates;
@@ -184,12 +182,6 @@ def check_selection(frontier, s_ref, s_gpu, kept_gpu, p: float, tol=None) -> dic
       * a near-tie swap: an oracle-kept node the GPU dropped, paired one to one with a node
         the GPU kept instead, whose oracle scores differ by at most the two nodes' score
         tolerances and which the GPU's own scores rank ahead of it.
-      * the score band: with every GPU score of the frontier within its tolerance, a node
-        still unexplained whose oracle cumulative probability before it lies within the
-        reach of the measured score differences (expm1(max d - min d) + BAND, d = GPU
-        score - oracle score), and which the GPU decided exactly as the top-p of its own
-        scores does (or within BAND of p under them): the cut moved with the scores, not
-        with the selection;
     Anything else is returned in ``bad``.  ``tol``: per-frontier-node score tolerance
     (default SCORE_TOL)."""
     frontier = np.asarray(frontier, dtype=np.int64)
@@ -197,7 +189,7 @@ def check_selection(frontier, s_ref, s_gpu, kept_gpu, p: float, tol=None) -> dic
     s_gpu = np.asarray(s_gpu, dtype=np.float64)
     tol = np.full(len(frontier), SCORE_TOL) if tol is None else np.asarray(tol, dtype=np.float64)
     rec = zo.top_p(frontier, s_ref, p)
-    out = dict(bad=[], band=[], swap=[], sband=[], k=rec["k"])
+    out = dict(bad=[], band=[], swap=[], k=rec["k"])
     pos = {int(n): i for i, n in enumerate(frontier.tolist())}
     kept_gpu = [int(n) for n in np.asarray(kept_gpu).tolist()]
     stray = [n for n in kept_gpu if n not in pos]
@@ -215,7 +207,7 @@ def check_selection(frontier, s_ref, s_gpu, kept_gpu, p: float, tol=None) -> dic
     dropped = sorted((n for n in k_o - k_g), key=lambda n: rank[pos[n]])
     added = sorted((n for n in k_g - k_o), key=lambda n: rank[pos[n]])
     # near-tie swaps first (a swap's two nodes may also lie in the band; pairing them keeps
-    # the band for a node the cut itself moved), then the band, then the score band
+    # the band for a node the cut itself moved), then the band
     used, paired = set(), set()
     for d in dropped:
         i = pos[d]
@@ -232,31 +224,19 @@ def check_selection(frontier, s_ref, s_gpu, kept_gpu, p: float, tol=None) -> dic
     added = [n for n in added if n not in used]
     out["band"] = [n for n in dropped + added if in_band(n)]
     bnd = s_ref[rec["order"][rec["k"] - 1]] if rec["k"] > 0 else np.inf
-    unexplained = [("dropped", n) for n in dropped if not in_band(n)] + \
-        [("added", n) for n in added if not in_band(n)]
-    diff = s_gpu - s_ref
-    if unexplained and np.all(np.abs(diff) <= tol):   # (scores beyond tolerance explain nothing)
-        reach = float(np.expm1(np.max(diff) - np.min(diff))) + BAND
-        rec_g = zo.top_p(frontier, s_gpu, p)
-        kept_g = set(rec_g["kept"].tolist())
-        cb_g = rec_g["cum_before"]
-        for what, nd in unexplained:
-            i = pos[nd]
-            near = abs(cb[rank[i]] - p) <= reach
-            own = ((nd in kept_g) == (what == "added")) or abs(cb_g[grank[i]] - p) <= BAND
-            if near and own:
-                out["sband"].append(nd)
-            else:
-                out["bad"].append((what, nd, float(cb[rank[i]]), float(s_ref[i] - bnd)))
-    else:
-        for what, nd in unexplained:
-            i = pos[nd]
-            out["bad"].append((what, nd, float(cb[rank[i]]), float(s_ref[i] - bnd)))
+    for n in dropped:
+        if not in_band(n):
+            i = pos[n]
+            out["bad"].append(("dropped", n, float(cb[rank[i]]), float(s_ref[i] - bnd)))
+    for n in added:
+        if not in_band(n):
+            j = pos[n]
+            out["bad"].append(("added", n, float(cb[rank[j]]), float(s_ref[j] - bnd)))
     return out
 
 
 def new_report() -> dict:
-    return dict(bad=[], band=0, swap=0, sband=0, selections=0, same=True)
+    return dict(bad=[], band=0, swap=0, selections=0, same=True)
 
 
 def compare_route(tree, q, trace: dict, gi: int, p, tol_fn=None) -> dict:
@@ -295,7 +275,6 @@ def compare_route(tree, q, trace: dict, gi: int, p, tol_fn=None) -> dict:
         rep["selections"] += 1
         rep["band"] += len(sel["band"])
         rep["swap"] += len(sel["swap"])
-        rep["sband"] += len(sel["sband"])
         if sel["bad"]:
             rep["bad"] += [("kept", lv) + tuple(x) for x in sel["bad"]]
             return rep
@@ -303,7 +282,7 @@ def compare_route(tree, q, trace: dict, gi: int, p, tol_fn=None) -> dict:
     blocks = gpu_frontier(trace[0], gi)
     if not np.array_equal(blocks, prev):
         rep["bad"].append(("blocks", sorted(set(blocks.tolist()) ^ set(prev.tolist()))[:10]))
-    rep["same"] = rep["band"] == 0 and rep["swap"] == 0 and rep["sband"] == 0
+    rep["same"] = rep["band"] == 0 and rep["swap"] == 0
     return rep
 
 
@@ -356,7 +335,6 @@ def teacher_forced(t, trees: list, q: np.ndarray, qd, p, keep_sink: bool, path: 
             rep["selections"] += 1
             rep["band"] += len(sel["band"])
             rep["swap"] += len(sel["swap"])
-            rep["sband"] += len(sel["sband"])
             rep["bad"] += [("kept", lv, h) + tuple(x) for x in sel["bad"]]
     return rep
 
@@ -374,7 +352,7 @@ def merge_reports(reps) -> dict:
     tot = new_report()
     for r in reps:
         tot["bad"] += r["bad"]
-        for k in ("band", "swap", "sband", "selections"):
+        for k in ("band", "swap", "selections"):
             tot[k] += r.get(k, 0)
         tot["same"] = tot["same"] and r.get("same", True)
     return tot
@@ -386,10 +364,8 @@ def assert_exemption_rates(label: str, reps, band_rate: float = MAX_BAND_RATE) -
     built to put the boundary exactly on p (equal masses) pass a band_rate of 1."""
     tot = merge_reports(reps) if isinstance(reps, (list, tuple)) else reps
     sel = tot["selections"]
-    sb = tot.get("sband", 0)
-    print(f"[exemptions] {label}: {sel} level selections, {tot['band']} mass-band, {tot['swap']} near-tie swaps, "
-          f"{sb} score-band")
-    assert tot["band"] + sb <= max(2, band_rate * sel), f"{label}: {tot['band']} + {sb} band exemptions in {sel}"
+    print(f"[exemptions] {label}: {sel} level selections, {tot['band']} mass-band, {tot['swap']} near-tie swaps")
+    assert tot["band"] <= max(2, band_rate * sel), f"{label}: {tot['band']} mass-band exemptions in {sel}"
     assert tot["swap"] <= max(2, MAX_SWAP_RATE * sel), f"{label}: {tot['swap']} near-tie swaps in {sel}"
     return tot
 
@@ -460,12 +436,11 @@ def compare_prefill_pair(tree, q, scores: dict, kept: dict, p) -> tuple:
         rep["selections"] += 1
         rep["band"] += len(sel["band"])
         rep["swap"] += len(sel["swap"])
-        rep["sband"] += len(sel["sband"])
         if sel["bad"]:
             rep["bad"] += [("kept", lv) + tuple(x) for x in sel["bad"]]
             return rep, None
         prev = np.sort(np.asarray(kept[lv], dtype=np.int64))
-    rep["same"] = rep["band"] == 0 and rep["swap"] == 0 and rep["sband"] == 0
+    rep["same"] = rep["band"] == 0 and rep["swap"] == 0
     return rep, prev
 
 

@@ -196,44 +196,6 @@ def test_compare_route_walk():
         assert P.compare_route(tree, q, bad, 0, p)["bad"][0][0] == "kept"
 
 
-def test_score_band():
-    """A cut that moved with the scores: the oracle's boundary 1.5e-5 past p, GPU scores
-    within 4e-5 of the oracle's that put the GPU's own cumulative probability past p one node
-    earlier.  Accepted (and counted) when the GPU's set is the exact top-p of its own scores
-    and the boundary lies within the reach of the score differences; reported otherwise."""
-    rng = np.random.default_rng(5)
-    done = 0
-    for _ in range(40):
-        fr, s = frontier_case(rng, n=3_000, spread=0.5)
-        order_idx = np.lexsort((fr, -s))
-        rec0 = zo.top_p(fr, s, 0.5)
-        k = rec0["k"]
-        c = float(np.cumsum(rec0["pi"][order_idx])[k - 1])      # cumulative through node k-1
-        p = c + 1.5e-5
-        rec = zo.top_p(fr, s, p)
-        if rec["k"] != k + 1 or abs(rec["cum_before"][k] - p) <= P.BAND:
-            continue
-        delta = 4e-5
-        g = s - delta
-        g[order_idx[:k]] += 2 * delta                              # the top k a little higher
-        rec_g = zo.top_p(fr, g, p)
-        if rec_g["k"] != k:
-            continue
-        out = P.check_selection(fr, s, g, rec_g["kept"], p)
-        assert not out["bad"] and out["sband"] == [int(fr[order_idx[k]])], out
-        # the same set without score differences to explain it: a wrong cut
-        assert P.check_selection(fr, s, s, rec_g["kept"], p)["bad"]
-        # one node fewer than the GPU's own top-p: reported
-        assert P.check_selection(fr, s, g, np.sort(fr[order_idx[:k - 1]]), p)["bad"]
-        # the GPU's scores ask for k + 1 nodes but it kept k: reported
-        g2 = s + delta
-        g2[order_idx[:k]] -= 2 * delta
-        assert zo.top_p(fr, g2, p)["k"] == k + 1
-        assert P.check_selection(fr, s, g2, rec_g["kept"], p)["bad"]
-        done += 1
-    assert done >= 10, done
-
-
 def test_swap_whose_mate_lies_in_the_band():
     """A near-tie pair reversed by the GPU's scores where the added node's oracle cumulative
     probability lies in the band and the dropped node's does not: one swap, nothing bad

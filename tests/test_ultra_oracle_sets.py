@@ -100,11 +100,10 @@ def test_routed_sets_and_outputs(case):
             rep["selections"] += 1
             rep["band"] += len(sel["band"])
             rep["swap"] += len(sel["swap"])
-            rep["sband"] += len(sel["sband"])
             prev = kept
         blocks = rec[f"blocks_g{gi}"].astype(np.int64)
         assert np.array_equal(blocks, prev), f"head {gi}: gathered blocks != kept level-1 nodes"
-        rep["same"] = rep["band"] == 0 and rep["swap"] == 0 and rep["sband"] == 0
+        rep["same"] = rep["band"] == 0 and rep["swap"] == 0
         if rep["same"]:
             route = zo.route(tree, q, p)
             for lr in route["levels"]:
