@@ -481,6 +481,151 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
   }
 }
 
+// Dense bf16 flash-decode with the next tile's K and V loaded while the current one is
+// processed: the same arithmetic as attend_mfma_kernel<D, true> (QK and P.V on bf16 MFMA, V
+// transposed through LDS), with the loads of tile i + 1 issued before tile i's MFMAs.  The
+// loads are unconditional (rows past the split's end clamped to its last token and masked
+// afterwards), so the compiler keeps them in flight across the iteration.
+template <int D>
+__global__ __launch_bounds__(256, 2) void attend_dense_kernel(AttnArgs a) {
+  constexpr int NK = Qk<bf16_t, D>::NL;
+  constexpr int NST = ATILE / 16;             // = 2
+  constexpr int NM = D / 16;                  // output dim blocks (MFMAs per tile)
+  __shared__ float Al[4][GMAX];
+  __shared__ float Ml[4][GMAX], Ll[4][GMAX];
+  constexpr int VT_BYTES = 4 * D * VS * 2;
+  constexpr int OL_BYTES = 4 * GMAX * D * 4;
+  __shared__ __align__(16) unsigned char buf[VT_BYTES > OL_BYTES ? VT_BYTES : OL_BYTES];
+
+  int kv, split;
+  int64_t fb, fe;
+  if (!attn_work<true>(a, kv, split, fb, fe)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int g = a.g;
+  const bf16_t* Kb = (const bf16_t*)a.K + (int64_t)kv * a.cap * D;
+  const bf16_t* Vb = (const bf16_t*)a.V + (int64_t)kv * a.cap * D;
+  uint16_t* Vt = (uint16_t*)buf + wave * D * VS;
+
+  Qk<bf16_t, D> qk;
+  qk.load_q((const bf16_t*)a.q + (int64_t)kv * g * D, g, col, kg);
+
+  float m = -INFINITY, l = 0.f;               // softmax state of head `col`
+  f32x4 acc[NM];
+#pragma unroll
+  for (int i = 0; i < NM; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int vt = lane & 31, vc = lane >> 5;   // V loads: token vt, dims 16i + 8vc .. +7
+  auto load = [&](int64_t f0, uint4 (&kf)[NST][NK], uint4 (&vv)[NM]) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+      Qk<bf16_t, D>::load_k(Kb + min(f0 + st * 16 + col, fe - 1) * D, kg, kf[st]);
+    const int64_t tk = min(f0 + vt, fe - 1);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) vv[i] = *(const uint4*)(Vb + tk * D + 16 * i + 8 * vc);
+  };
+  // two register sets take turns (no copies: a copy of a register still being loaded makes
+  // the compiler wait for the load, which would drain the prefetch)
+  uint4 kfa[NST][NK], vva[NM], kfb[NST][NK], vvb[NM];
+  auto step = [&](int64_t f0, const uint4 (&kf)[NST][NK], const uint4 (&vv)[NM], uint4 (&kn)[NST][NK],
+                  uint4 (&vn)[NM]) {
+    load(f0 + 4 * ATILE, kn, vn);             // clamped: past the end it rereads the last row
+    float sc[NST][4];
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const f32x4 s4 = qk.mma(kf[st]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool use = col < g && f0 + st * 16 + kg * 4 + e < fe;
+        sc[st][e] = use ? a.sigma * s4[e] : -INFINITY;
+        rmax = fmaxf(rmax, sc[st][e]);
+      }
+    }
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+    const float mn = fmaxf(m, rmax);
+    const float alpha = (mn == -INFINITY) ? 1.f : expf(m - mn);
+    float rsum = 0.f;
+    uint32_t pb[4];                           // P row of head `col`, bf16 pairs, slot order
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const float p0 = (mn == -INFINITY) ? 0.f : expf(sc[st][e] - mn);
+        const float p1 = (mn == -INFINITY) ? 0.f : expf(sc[st][e + 1] - mn);
+        rsum += p0 + p1;
+        pb[st * 2 + e / 2] = f2bf16_bits(p0) | (f2bf16_bits(p1) << 16);
+      }
+    rsum += __shfl_xor(rsum, 16);
+    rsum += __shfl_xor(rsum, 32);
+    l = l * alpha + rsum;
+    m = mn;
+    if (kg == 0 && col < GMAX) Al[wave][col] = alpha;
+    // the V tile, transposed: Vt[dim][token] (rows past the end are weighted 0)
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int d = 16 * i + 8 * vc + k;
+        Vt[d * VS + vt] = (uint16_t)((w4[k >> 1] >> (16 * (k & 1))) & 0xffffu);
+      }
+    }
+    wave_sync_lds();
+    float ah[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ah[e] = (4 * kg + e < GMAX) ? Al[wave][4 * kg + e] : 1.f;
+    const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(pb[0], pb[1], pb[2], pb[3]));
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][e] *= ah[e];
+      const uint16_t* row = Vt + (16 * i + col) * VS;
+      const uint2 lo = *(const uint2*)(row + 4 * kg);
+      const uint2 hi = *(const uint2*)(row + 16 + 4 * kg);
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, acc[i], 0, 0, 0);
+    }
+    wave_sync_lds();
+  };
+  load(fb + wave * ATILE, kfa, vva);
+  for (int64_t f0 = fb + wave * ATILE; f0 < fe; f0 += 8 * ATILE) {
+    step(f0, kfa, vva, kfb, vvb);
+    if (f0 + 4 * ATILE >= fe) break;
+    step(f0 + 4 * ATILE, kfb, vvb, kfa, vva);
+  }
+  __syncthreads();
+  // the waves' partials: acc[i][e] = head 4kg+e, dim 16i + col
+  float* Ol = (float*)buf;                    // [4][GMAX][D]
+  if (kg == 0 && col < GMAX) { Ml[wave][col] = m; Ll[wave][col] = l; }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int h = 4 * kg + e;
+    if (h < GMAX)
+#pragma unroll
+      for (int i = 0; i < NM; ++i) Ol[(wave * GMAX + h) * D + 16 * i + col] = acc[i][e];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < g * D; idx += 256) {
+    const int h = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, Ml[w][h]);
+    float L = 0.f, O = 0.f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float sw = expf(Ml[w][h] - M);
+        L += Ll[w][h] * sw;
+        O += Ol[(w * GMAX + h) * D + d] * sw;
+      }
+    }
+    float* pp = a.dev.apart + ((int64_t)(kv * g + h) * a.pstride + split) * (D + 2);
+    if (d == 0) { pp[0] = M; pp[1] = L; }
+    pp[2 + d] = O;
+  }
+}
+
 template <typename TIn, int D, bool DENSE>
 __global__ __launch_bounds__(512) void combine_kernel(AttnArgs a, int32_t* stats, int levels) {
   constexpr int NW = 8;        // waves: split rows are dealt round-robin to the waves
@@ -607,7 +752,7 @@ static hipError_t launch_attend_t(const AttnArgs& a, int32_t* stats, int levels,
   // dense: (splits, Hkv); routed: one dimension over every head's splits (see attn_work)
   const dim3 grid = DENSE ? dim3((unsigned)a.splits, (unsigned)a.hkv) : dim3((unsigned)(a.splits * a.hkv));
   if constexpr (sizeof(TIn) == 2 && DENSE)
-    hipLaunchKernelGGL((attend_mfma_kernel<D, DENSE>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attend_dense_kernel<D>), grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((attend_kernel<TIn, D, DENSE>), grid, dim3(256), 0, st, a);
   hipLaunchKernelGGL((combine_kernel<TIn, D, DENSE>), dim3((unsigned)a.hq), dim3(512), 0, st, a, stats, levels);
@@ -630,7 +775,7 @@ hipError_t launch_attend_full(const AttnArgs& a, bool bf16, int D, bool dense, i
 template <typename TIn, int D, bool DENSE>
 static int resident_splits_t(int hkv) {
   static const int per_cu = [] {
-    if constexpr (sizeof(TIn) == 2 && DENSE) return resident_per_cu(attend_mfma_kernel<D, DENSE>, 256);
+    if constexpr (sizeof(TIn) == 2 && DENSE) return resident_per_cu(attend_dense_kernel<D>, 256);
     else return resident_per_cu(attend_kernel<TIn, D, DENSE>, 256);
   }();
   const int s = per_cu * device_cus() / hkv;
