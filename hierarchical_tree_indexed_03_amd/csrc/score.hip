@@ -15,10 +15,7 @@
 #include "route_util.hpp"
 #include "qk_tile.hpp"
 
-// Score-kernel tuning: tiles in flight per wave (key form; bf16 / FP4 planes).
-#ifndef ZHA_KEYS_UN
-#define ZHA_KEYS_UN 1
-#endif
+// Score-kernel tuning: tiles in flight per wave (bf16 / FP4 planes).
 #ifndef ZHA_SCORE_UN_BF16
 #define ZHA_SCORE_UN_BF16 2
 #endif
@@ -482,21 +479,92 @@ __global__ __launch_bounds__(256) void route_score_bf16_rows_kernel(RouteArgs a)
 // of a block follow from the group's logits on its b keys and the R x b stored weights.
 // Per 16-token tile (16/b nodes): the logits tile S^T = K.Q^T (bf16 MFMA, tokens x heads),
 // transposed through LDS, then per node one fp32 MFMA per 4 tokens, [planes x tokens] x
-// [tokens x heads] accumulated onto c_j, so each lane holds 4 planes of one head: the max
-// over planes is 3 in-lane maxima and 2 cross-lane steps.
+// [tokens x heads] accumulated onto c_j, so each lane holds 4 planes of one head.  The max
+// over a node's planes is 3 in-lane maxima and a maximum over the 4 lane rows; the tile's
+// nodes share the cross-row steps (a butterfly on the gfx950 row swaps), which leave each
+// row with the full maxima of its own nodes.
+
+// s_waitcnt vmcnt(n) with the export and LDS/scalar counters left free (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+// The scheduler may not move any instruction across it.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Row swaps (gfx950): permlane16_swap exchanges the odd 16-lane rows of x with the even rows
+// of y; permlane32_swap exchanges the upper 32 lanes of x with the lower 32 lanes of y.
+__device__ __forceinline__ void swap_rows16(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap_rows32(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+
+// Maxima over the 4 lane rows of NP per-lane values m[0..NP) (one per node).  On return
+// row r holds in out[i], i < max(NP/4, 1), the maximum of node key_row_node<NP>(i, r).
+//   step 1 (rows r, r^1): pairs (m[i], m[i + NP/2]); a row of parity p keeps node i + p*NP/2
+//   step 2 (rows r, r^2): pairs (A[i], A[i + NA/2]); rows 0, 1 keep the first, rows 2, 3 the
+//   second, each for its parity
+template <int NP>
+__device__ __forceinline__ int key_row_node(int i, int r) {
+  constexpr int NA = NP >= 2 ? NP / 2 : 1;
+  const int j = NA >= 2 ? i + (r >= 2 ? NA / 2 : 0) : i;
+  return NP >= 2 ? j + (r & 1) * (NP / 2) : 0;
+}
+template <int NP>
+__device__ __forceinline__ void key_row_max(const float (&m)[NP], float (&out)[NP >= 4 ? NP / 4 : 1]) {
+  constexpr int NA = NP >= 2 ? NP / 2 : 1;
+  float A[NA];
+  if constexpr (NP >= 2) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      float x = m[i], y = m[i + NA];
+      swap_rows16(x, y);
+      A[i] = fmaxf(x, y);
+    }
+  } else {
+    float x = m[0], y = m[0];
+    swap_rows16(x, y);
+    A[0] = fmaxf(x, y);
+  }
+  if constexpr (NA >= 2) {
+#pragma unroll
+    for (int i = 0; i < NA / 2; ++i) {
+      float x = A[i], y = A[i + NA / 2];
+      swap_rows32(x, y);
+      out[i] = fmaxf(x, y);
+    }
+  } else {
+    float x = A[0], y = A[0];
+    swap_rows32(x, y);
+    out[0] = fmaxf(x, y);
+  }
+}
+
 template <int D, int R, int B>
-__global__ __launch_bounds__(256) void route_score_keys_kernel(RouteArgs a) {
+__global__ __launch_bounds__(256, B >= 4 ? 4 : 1) void route_score_keys_kernel(RouteArgs a) {
   constexpr int NPT = 16 / B;                 // nodes per 16-token tile
   constexpr int KS = (B + 3) / 4;             // fp32 MFMA steps per node
-  constexpr int UN = ZHA_KEYS_UN;             // tiles in flight per wave
   constexpr int NK = Qk<bf16_t, D>::NL;
+  constexpr int NC = NPT >= 4 ? NPT / 4 : 1;  // node maxima per lane after the row steps
+  constexpr int NROW = NPT >= 4 ? 4 : NPT;    // lane rows that hold distinct nodes
   __shared__ float Lt[4][16][17];             // per wave: logits [head][token]
   __shared__ float red[4][16];
-  const int kv = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index through readfirstlane, so the compiler sees the tile loop as uniform
+  const int kv = blockIdx.y, lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, kg = lane >> 4;
   const int lv = 1;
-  const int64_t cnt = a.dev.cnt[lv * a.hkv + kv];
+  const int cnt = (int)a.dev.cnt[lv * a.hkv + kv];
   const int64_t cap = a.dev.ncap[lv];
+  const int nl = (int)a.nl[lv];
   const int32_t* nodes = a.dev.node[lv] + kv * cap;
   const uint32_t* masks = a.dev.mask[lv] + kv * cap;
   const bf16_t* Kc = (const bf16_t*)a.K + (int64_t)kv * a.kcap * D;
@@ -504,112 +572,145 @@ __global__ __launch_bounds__(256) void route_score_keys_kernel(RouteArgs a) {
   const float* C = a.dev.c[lv] + (int64_t)kv * cap * R;
   float* out = a.dev.score[lv] + (int64_t)kv * GMAX * cap;
   const int g = a.g;
-  const int64_t N = a.N;
+  const int N = (int)a.N;
 
   Qk<bf16_t, D> qk;
   qk.load_q((const bf16_t*)a.q + (int64_t)kv * g * D, g, col, kg);
-  float runmax = -INFINITY;                   // head `col`
+  float runmax = -INFINITY;                   // head `col`, over this lane row's nodes
 
-  const int64_t ntiles = (cnt + NPT - 1) / NPT;
-  const int64_t tstride = (int64_t)gridDim.x * 4 * UN;
-  // node ids of a pass's tiles: the lane's token-row node, and each node of the tile
-  // (wave-uniform); the next pass's ids are loaded before this pass's keys
-  int32_t rid[UN], nid[UN][NPT];
-  uint32_t nmk[UN][NPT];
-  auto load_ids = [&](int64_t t0, int32_t (&r)[UN], int32_t (&nd)[UN][NPT], uint32_t (&mk)[UN][NPT]) {
+  const int ntiles = (cnt + NPT - 1) / NPT;
+  const int tstride = (int)gridDim.x * 4;
+  const int tfirst = (int)blockIdx.x * 4 + wave;
+
+  // Two-stage pipeline per wave: the node ids of the tile after next and the keys, weights
+  // and c of the next tile are in flight while the current tile is scored.  Every load is
+  // unconditional at a clamped index (past the list's end: its last entry, a cache hit);
+  // validity is applied where the values are used, so no load waits on another.  The ids
+  // are per-lane vector loads (lane `col` holds the entry of its token row); a node's id and
+  // head mask reach the wave as the value of lane n * B, so no scalar-cache load (whose wait
+  // would share the LDS counter) sits in the pass.
+  int32_t rid;
+  uint32_t rmk;
+  auto load_ids = [&](int t) {
+    const int er = min(t * NPT + col / B, cnt - 1);
+    rid = nodes[er];
+    rmk = masks[er];
+  };
+  // a tile's operands and the head masks of its nodes
+  struct Tile {
+    uint4 kf[NK];
+    float wv[NPT][KS];
+    f32x4 cj[NPT];
+    uint32_t mk[NPT];                         // 0 past the list's end
+  };
+  // Token rows past the cache's end (a partial last block) read the last key: their weights
+  // are stored as exact zeros, so they add nothing to any plane's score.  Rows of entries
+  // that no head holds feed only scores that are never stored.
+  auto load_tile = [&](int t, Tile& x) {
+    // the tile's 16 token rows: token `col` of node col / B
+    const int tok = min(max(rid, 0), nl - 1) * B + col % B;
+    Qk<bf16_t, D>::load_k(Kc + (int64_t)min(tok, N - 1) * D, kg, x.kf);
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      // an entry of no head's frontier (mask 0) is not read
-      const int64_t e_row = (t0 + u) * NPT + col / B;
-      r[u] = ((t0 + u) < ntiles && e_row < cnt && masks[e_row] != 0u) ? nodes[e_row] : -1;
+    for (int n = 0; n < NPT; ++n) {
+      const int32_t nid = __builtin_amdgcn_readlane(rid, n * B);
+      x.mk[n] = t * NPT + n < cnt ? (uint32_t)__builtin_amdgcn_readlane((int32_t)rmk, n * B) : 0u;
+      ZHA_CHECK(a.dev, x.mk[n] == 0u || (nid >= 0 && nid < nl), CHK_NODE_RANGE);
+      const int64_t nd = min(max(nid, 0), nl - 1);
+      // A operand: lane (plane col, token 4s + kg) holds w[plane][token]
 #pragma unroll
-      for (int n = 0; n < NPT; ++n) {
-        const int64_t e = (t0 + u) * NPT + n;
-        const bool ok = (t0 + u) < ntiles && e < cnt;
-        mk[u][n] = ok ? masks[e] : 0u;
-        nd[u][n] = mk[u][n] != 0u ? nodes[e] : -1;
-        ZHA_CHECK(a.dev, nd[u][n] < a.nl[lv], CHK_NODE_RANGE);
+      for (int s = 0; s < KS; ++s) {
+        const int k = 4 * s + kg;
+        x.wv[n][s] = W[(nd * R + min(col, R - 1)) * B + min(k, B - 1)];
+      }
+      // accumulator: c of planes 4kg..4kg+3 (absent planes -inf where used)
+      if constexpr (R >= 4) {
+        const float4 c4 = *(const float4*)(C + nd * R + min(4 * kg, R - 4));
+        x.cj[n][0] = c4.x; x.cj[n][1] = c4.y; x.cj[n][2] = c4.z; x.cj[n][3] = c4.w;
+      } else {
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) x.cj[n][e4] = C[nd * R + min(4 * kg + e4, R - 1)];
       }
     }
   };
-  const int64_t tfirst = ((int64_t)blockIdx.x * 4 + wave) * UN;
-  if (tfirst < ntiles) load_ids(tfirst, rid, nid, nmk);
-  for (int64_t t0 = tfirst; t0 < ntiles; t0 += tstride) {
-    int32_t rcur[UN], ncur[UN][NPT];
-    uint32_t mcur[UN][NPT];
+  // A tile's scores are stored one pass later, after the next pass's loads are issued: the
+  // wait at a pass's start then finds those stores as old as the loads it waits for, instead
+  // of waiting for stores issued just before it.  Lane (col, row kg) stores head col's score
+  // of the nodes its row holds.
+  float pv[NC];
+  uint32_t pmk[NC];
+  int pt = 0;
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      rcur[u] = rid[u];
+  for (int i = 0; i < NC; ++i) { pv[i] = 0.f; pmk[i] = 0u; }
+  auto store_pending = [&]() {
 #pragma unroll
-      for (int n = 0; n < NPT; ++n) { ncur[u][n] = nid[u][n]; mcur[u][n] = nmk[u][n]; }
-    }
-    if (t0 + tstride < ntiles) load_ids(t0 + tstride, rid, nid, nmk);
-    uint4 kf[UN][NK];
-    float wv[UN][NPT][KS];
-    f32x4 cj[UN][NPT];
+    for (int i = 0; i < NC; ++i)
+      if (((pmk[i] >> col) & 1u) && kg < NROW && col < g)
+        out[(int64_t)col * cap + pt * NPT + key_row_node<NPT>(i, kg)] = pv[i];
+  };
+  auto score_tile = [&](int t, const Tile& x) {
+    const f32x4 st = qk.mma(x.kf);              // S^T[token 4kg+e][head col]
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      // the tile's 16 token rows: token `col` of node col / B; rows past the data read zeros
-      const int64_t tok = rcur[u] >= 0 ? (int64_t)rcur[u] * B + col % B : -1;
-      if (tok >= 0 && tok < N) {
-        Qk<bf16_t, D>::load_k(Kc + tok * D, kg, kf[u]);
-      } else {
+    for (int e = 0; e < 4; ++e) Lt[wave][col][kg * 4 + e] = a.sigma * st[e];
+    wave_sync_lds();
+    float m[NPT];
 #pragma unroll
-        for (int i = 0; i < NK; ++i) kf[u][i] = make_uint4(0, 0, 0, 0);
+    for (int n = 0; n < NPT; ++n) {
+      f32x4 acc;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) acc[e4] = 4 * kg + e4 < R ? x.cj[n][e4] : -INFINITY;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int k = 4 * s + kg;
+        // B operand: lane (head col, token k) holds the logit
+        const float lg = k < B ? Lt[wave][col][n * B + k] : 0.f;
+        const float w = col < R && k < B ? x.wv[n][s] : 0.f;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(w, lg, acc, 0, 0, 0);
       }
-#pragma unroll
-      for (int n = 0; n < NPT; ++n) {
-        const bool ok = ncur[u][n] >= 0;
-        const int64_t nd = ok ? ncur[u][n] : 0;
-        // A operand: lane (plane col, token 4s + kg) holds w[plane][token]
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const int k = 4 * s + kg;
-          wv[u][n][s] = (ok && col < R && k < B) ? W[(nd * R + col) * B + k] : 0.f;
-        }
-        // accumulator: c of planes 4kg..4kg+3 (absent planes -inf)
-        if constexpr (R >= 4) {
-          const bool okc = ok && 4 * kg < R;
-          const float4 c4 = okc ? *(const float4*)(C + nd * R + 4 * kg)
-                                : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-          cj[u][n][0] = c4.x; cj[u][n][1] = c4.y; cj[u][n][2] = c4.z; cj[u][n][3] = c4.w;
-        } else {
-#pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4) {
-            const int j = 4 * kg + e4;
-            cj[u][n][e4] = (ok && j < R) ? C[nd * R + j] : -INFINITY;
-          }
-        }
-      }
+      // acc[e] = score of plane 4kg+e for head col
+      m[n] = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
     }
+    float v[NC];
+    key_row_max<NPT>(m, v);
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const f32x4 st = qk.mma(kf[u]);          // S^T[token 4kg+e][head col]
+    for (int i = 0; i < NC; ++i) {
+      // the head mask of this row's node: NPT wave-uniform values, picked by the row
+      uint32_t mk = 0u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Lt[wave][col][kg * 4 + e] = a.sigma * st[e];
-      wave_sync_lds();
-#pragma unroll
-      for (int n = 0; n < NPT; ++n) {
-        f32x4 acc = cj[u][n];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const int k = 4 * s + kg;
-          // B operand: lane (head col, token k) holds the logit
-          const float lg = k < B ? Lt[wave][col][n * B + k] : 0.f;
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[u][n][s], lg, acc, 0, 0, 0);
-        }
-        // acc[e] = score of plane 4kg+e for head col
-        float v = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
-        v = fmaxf(v, __shfl_xor(v, 16));
-        v = fmaxf(v, __shfl_xor(v, 32));
-        const int64_t e_ent = (t0 + u) * NPT + n;   // wave-uniform
-        const bool ok = ncur[u][n] >= 0;
-        if (ok && kg == 0 && col < g && ((mcur[u][n] >> col) & 1u)) out[(int64_t)col * cap + e_ent] = v;
-        if ((mcur[u][n] >> col) & 1u) runmax = fmaxf(runmax, v);
-      }
-      wave_sync_lds();
+      for (int n = 0; n < NPT; ++n) mk = key_row_node<NPT>(i, kg) == n ? x.mk[n] : mk;
+      pv[i] = v[i];
+      pmk[i] = mk;
+      if (((mk >> col) & 1u) && kg < NROW) runmax = fmaxf(runmax, v[i]);
     }
+    pt = t;
+    wave_sync_lds();
+  };
+
+  // Each pass starts with an explicit wait for all of the previous pass's memory operations
+  // (its loads and the stores issued beside them, all as old as the pass); the compiler's
+  // own counting across the two alternating halves would otherwise wait inside the pass
+  // for some of the loads just issued.
+  if (tfirst < ntiles) {
+    Tile ta, tb;
+    load_ids(tfirst);
+    load_tile(tfirst, ta);
+    load_ids(tfirst + tstride);
+    for (int t = tfirst; t < ntiles; t += 2 * tstride) {
+      wait_vm<0>();
+      load_tile(t + tstride, tb);
+      load_ids(t + 2 * tstride);
+      store_pending();
+      score_tile(t, ta);
+      if (t + tstride >= ntiles) break;
+      wait_vm<0>();
+      load_tile(t + 2 * tstride, ta);
+      load_ids(t + 3 * tstride);
+      store_pending();
+      score_tile(t + tstride, tb);
+    }
+    store_pending();
   }
+  runmax = fmaxf(runmax, __shfl_xor(runmax, 16));
+  runmax = fmaxf(runmax, __shfl_xor(runmax, 32));
   if (kg == 0) red[wave][col] = runmax;
   __syncthreads();
   if (threadIdx.x < g) {
@@ -680,7 +781,7 @@ static void launch_score_planes(const RouteArgs& a, int nlev, int64_t nodes, hip
 
 template <int D, int R, int B>
 static void launch_score_keys(const RouteArgs& a, hipStream_t st) {
-  constexpr int NPB = 4 * (16 / B) * ZHA_KEYS_UN;   // nodes per block pass
+  constexpr int NPB = 4 * (16 / B);   // nodes per block pass
   static const int per_cu = resident_per_cu(route_score_keys_kernel<D, R, B>, 256);
   const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
   hipLaunchKernelGGL((route_score_keys_kernel<D, R, B>), dim3(grid_for(a.nlevel, NPB, cap), (unsigned)a.hkv), dim3(256),

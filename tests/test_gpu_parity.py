@@ -27,6 +27,11 @@ SMALL = {
     # one or two (node, plane) pairs per build tile: each pair's log-sum-exp split over 64 lanes
     "wide_r1": wc.WIDE.with_(n_tokens=6_144 + 77, num_ref=1, steps=2),
     "b128_r2_f32": wc.WIDE.with_(block=128, levels=2, num_ref=2, dtype="f32", n_tokens=20_000 + 9, steps=2),
+    # key-form level 1 at every block size it takes (8, 2 and 1 nodes per 16-token tile)
+    "keys_b2": wc.DEEP.with_(block=2, levels=8, n_tokens=12_000 + 7, steps=2),
+    "keys_b8": wc.DEEP.with_(block=8, levels=4, n_tokens=16_384 + 19, steps=2),
+    "keys_b16": wc.DEEP.with_(block=16, levels=3, n_tokens=20_000 + 3, steps=2),
+    "keys_b2_r2_d64": wc.DEEP.with_(block=2, num_ref=2, head_dim=64, levels=8, n_tokens=9_000 + 1, steps=2),
 }
 
 
