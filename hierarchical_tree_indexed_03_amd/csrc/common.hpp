@@ -24,6 +24,9 @@ constexpr int TD_WORDS = TD_MAX / 32;
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+// 16 bytes as a native vector (loads and stores of it stay register values, where a copy of
+// the uint4 struct can become a memcpy that keeps an array of them in scratch memory)
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
 struct bf16_t { uint16_t bits; };   // storage type of bfloat16 tensors
 

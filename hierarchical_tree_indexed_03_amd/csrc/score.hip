@@ -61,6 +61,17 @@ __global__ __launch_bounds__(256) void route_prep_kernel(RouteArgs a) {
   }
 }
 
+// s_waitcnt vmcnt(n) with the export and LDS/scalar counters left free (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+// The scheduler may not move any instruction across it.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ------------------------------------------------------------------ score
 // Scores of the union frontier on fp32 MFMA: one 16x16 output tile = the 16 query-head rows
 // (the group's heads, zero-padded) x 16 columns = 16/R nodes x R planes.  A node's score is
@@ -71,9 +82,15 @@ __global__ __launch_bounds__(256) void route_prep_kernel(RouteArgs a) {
 // 512-byte rows (d 128) instead of one 64-byte piece of each of 16 rows; the rows go through
 // LDS (rows padded by 16 bytes, so the MFMA-layout reads hit distinct banks) into the MFMA
 // operand layout: lane (column c, group kg) takes the pieces [64i + 16kg, +16) of row c, and
-// Q uses the same permutation of the contraction.  The next tile's loads are issued before
-// the current tile's MFMAs.
-template <int D, int R>
+// Q uses the same permutation of the contraction.
+//
+// Pipeline per wave: the next tile's rows and offsets are loaded while the current tile is
+// scored, and (list mode) the node ids of the tile after it.  Every load is unconditional at
+// a clamped index (past the list's end: its last entry) and validity is applied where the
+// values are used, so no load waits on another; a tile's scores are stored one pass later,
+// after the next pass's loads, so each pass's single wait finds every operation it waits for
+// as old as the pass.  DENSE: every node of the level (grid z: the level), no list.
+template <int D, int R, bool DENSE>
 __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
   constexpr int NPT = 16 / R;                 // nodes per 16-column tile
   constexpr int NI = D / 16;                  // float4 MFMA operands per lane per tile
@@ -83,14 +100,15 @@ __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
   constexpr int RS = D + 4;                   // LDS row stride in floats
   __shared__ __align__(16) float stg[4][16 * RS];
   __shared__ float red[4][16];
-  const int kv = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index through readfirstlane, so the compiler sees the tile loop as uniform
+  const int kv = blockIdx.y, lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, kg = lane >> 4;
   const int slot = col / R, plane = col % R;
   const int lrow = lane / LPR, lcol = (lane % LPR) * 4;
-  const bool dense = a.dense != 0;            // every node of the level, no list
-  const int lv = dense ? dense_level(a) : a.level;
-  const int64_t cnt = dense ? a.nl[lv] : a.dev.cnt[lv * a.hkv + kv];
+  const int lv = DENSE ? dense_level(a) : a.level;
+  const int64_t cnt = DENSE ? a.nl[lv] : a.dev.cnt[lv * a.hkv + kv];
   const int64_t cap = a.dev.ncap[lv];
+  const int64_t nl = a.nl[lv];
   const int32_t* nodes = a.dev.node[lv] + kv * cap;
   const uint32_t* masks = a.dev.mask[lv] + kv * cap;
   const float* S = a.dev.s[lv] + (int64_t)kv * cap * R * D;
@@ -111,75 +129,109 @@ __global__ __launch_bounds__(256) void route_score_kernel(RouteArgs a) {
 
   const int64_t ntiles = (cnt + NPT - 1) / NPT;
   const int64_t tstride = (int64_t)gridDim.x * 4;
-  // row `col` of a tile: its node (-1: none, or an entry of no head's frontier), mask and
-  // offset; then the tile's rows, whole rows per load instruction
-  int32_t rnid;
-  uint32_t rmk;
+  const int64_t tfirst = (int64_t)blockIdx.x * 4 + wave;
+  auto clamp_e = [&](int64_t e) __attribute__((always_inline)) { return e < cnt ? e : cnt - 1; };
+  auto clamp_n = [&](int64_t n) __attribute__((always_inline)) { return n < 0 ? (int64_t)0 : (n < nl ? n : nl - 1); };
+
+  // list mode: the node of each of the lane's NLD load rows, and its MFMA slot's node and
+  // head mask (row r of tile t: entry t * NPT + r / R)
+  int32_t lid[NLD], sid;
+  uint32_t smk;
+  auto load_ids = [&](int64_t t) __attribute__((always_inline)) {
+    if constexpr (!DENSE) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) lid[i] = nodes[clamp_e(t * NPT + (lrow + RPI * i) / R)];
+      const int64_t es = clamp_e(t * NPT + slot);
+      sid = nodes[es];
+      smk = masks[es];
+    }
+  };
+  // a tile's rows and the lane's offset c (rows of entries past the list read its last one)
+  u32x4 ld[NLD];
   float rcj;
-  uint4 ld[NLD];
-  auto fetch = [&](int64_t t) {
-    const int64_t e = t * NPT + slot;
-    const bool ok = t < ntiles && e < cnt;
-    rmk = (ok && !dense) ? masks[e] : 0u;
-    rnid = (ok && (dense || rmk != 0u)) ? (dense ? (int32_t)e : nodes[e]) : -1;
-    ZHA_CHECK(a.dev, rnid < a.nl[lv], CHK_NODE_RANGE);
-    rcj = rnid >= 0 ? C[(int64_t)rnid * R + plane] : -INFINITY;
+  uint32_t rmk;
+  auto fetch = [&](int64_t t) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int r = lrow + RPI * i;
-      const int32_t nd = __shfl(rnid, r);
-      ld[i] = nd >= 0 ? *(const uint4*)(S + ((int64_t)nd * R + r % R) * D + lcol) : make_uint4(0, 0, 0, 0);
+      const int64_t nd = DENSE ? clamp_e(t * NPT + r / R) : clamp_n(lid[i]);
+      ZHA_CHECK(a.dev, DENSE || t * NPT + r / R >= cnt || (lid[i] >= 0 && lid[i] < nl), CHK_NODE_RANGE);
+      ld[i] = *(const u32x4*)(S + (nd * R + r % R) * D + lcol);
     }
+    const int64_t es = t * NPT + slot;
+    const int64_t nd = DENSE ? clamp_e(es) : clamp_n(sid);
+    rcj = C[nd * R + plane];
+    // dense: every head's score of an entry of the level; list: the heads holding the entry
+    rmk = es < cnt ? (DENSE ? 0xffffffffu : smk) : 0u;
   };
-  int64_t t = (int64_t)blockIdx.x * 4 + wave;
-  if (t < ntiles) fetch(t);
-  for (; t < ntiles; t += tstride) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) *(uint4*)(W + (lrow + RPI * i) * RS + lcol) = ld[i];
-    const int32_t nid = rnid;
-    const uint32_t mk = rmk;
-    const float cj = rcj;
-    wave_sync_lds();
-    if (t + tstride < ntiles) fetch(t + tstride);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const float4 sb = *(const float4*)(W + col * RS + 16 * i + 4 * kg);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][0], sb.x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][1], sb.y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][2], sb.z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][3], sb.w, acc, 0, 0, 0);
-    }
-    wave_sync_lds();
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = acc[e] + cj;
-#pragma unroll
-    for (int off = 1; off < R; off <<= 1)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], __shfl_xor(v[e], off));
-    // dense: every head's score (the max is taken later); list mode: the scores of the heads
-    // whose frontier holds the node
-    const int64_t ent = t * NPT + slot;
+  // scores stored one pass late (lane (col, kg) with plane 0: heads 4kg..4kg+3 of its slot)
+  float pv[4] = {0.f, 0.f, 0.f, 0.f};
+  uint32_t pmk = 0u;
+  int64_t pent = 0;
+  auto store_pending = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int h = kg * 4 + e;
-      if (nid >= 0 && plane == 0 && h < g && (dense || ((mk >> h) & 1u))) out[(int64_t)h * cap + ent] = v[e];
-      if ((mk >> h) & 1u) runmax[e] = fmaxf(runmax[e], v[e]);
+      if (plane == 0 && h < g && ((pmk >> h) & 1u)) out[(int64_t)h * cap + pent] = pv[e];
     }
-  }
-  // per-head max: lanes of one 16-lane row share kg, i.e. the heads 4kg..4kg+3
+  };
+
+  if (tfirst < ntiles) {
+    load_ids(tfirst);
+    fetch(tfirst);
+    load_ids(tfirst + tstride);
+    for (int64_t t = tfirst; t < ntiles; t += tstride) {
+      wait_vm<0>();
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float v = runmax[e];
-    for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
-    if (col == 0) red[wave][kg * 4 + e] = v;
+      for (int i = 0; i < NLD; ++i) *(u32x4*)(W + (lrow + RPI * i) * RS + lcol) = ld[i];
+      const float cj = rcj;
+      const uint32_t mk = rmk;
+      wave_sync_lds();
+      fetch(t + tstride);
+      load_ids(t + 2 * tstride);
+      store_pending();
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const float4 sb = *(const float4*)(W + col * RS + 16 * i + 4 * kg);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][0], sb.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][1], sb.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][2], sb.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][3], sb.w, acc, 0, 0, 0);
+      }
+      wave_sync_lds();
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[e] + cj;
+#pragma unroll
+      for (int off = 1; off < R; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], __shfl_xor(v[e], off));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pv[e] = v[e];
+        // the per-head max of list mode (dense levels take theirs in the selection)
+        if (!DENSE && ((mk >> (kg * 4 + e)) & 1u)) runmax[e] = fmaxf(runmax[e], v[e]);
+      }
+      pmk = mk;
+      pent = t * NPT + slot;
+    }
+    store_pending();
   }
-  __syncthreads();
-  if (threadIdx.x < g) {
-    const int gi = threadIdx.x;
-    const float m = fmaxf(fmaxf(red[0][gi], red[1][gi]), fmaxf(red[2][gi], red[3][gi]));
-    if (m > -INFINITY) atomicMax(&a.dev.qs[lv * a.hq + kv * g + gi].maxkey, f2key(m));
+  if constexpr (!DENSE) {
+    // per-head max: lanes of one 16-lane row share kg, i.e. the heads 4kg..4kg+3
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = runmax[e];
+      for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+      if (col == 0) red[wave][kg * 4 + e] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < g) {
+      const int gi = threadIdx.x;
+      const float m = fmaxf(fmaxf(red[0][gi], red[1][gi]), fmaxf(red[2][gi], red[3][gi]));
+      if (m > -INFINITY) atomicMax(&a.dev.qs[lv * a.hq + kv * g + gi].maxkey, f2key(m));
+    }
   }
 }
 
@@ -484,17 +536,6 @@ __global__ __launch_bounds__(256) void route_score_bf16_rows_kernel(RouteArgs a)
 // nodes share the cross-row steps (a butterfly on the gfx950 row swaps), which leave each
 // row with the full maxima of its own nodes.
 
-// s_waitcnt vmcnt(n) with the export and LDS/scalar counters left free (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-// The scheduler may not move any instruction across it.
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // Row swaps (gfx950): permlane16_swap exchanges the odd 16-lane rows of x with the even rows
 // of y; permlane32_swap exchanges the upper 32 lanes of x with the lower 32 lanes of y.
 __device__ __forceinline__ void swap_rows16(float& x, float& y) {
@@ -773,10 +814,17 @@ static void launch_score_planes(const RouteArgs& a, int nlev, int64_t nodes, hip
     return;
   }
   constexpr int NPB = 4 * (16 / R);   // nodes per block pass
-  static const int per_cu = resident_per_cu(route_score_kernel<D, R>, 256);
-  const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
-  hipLaunchKernelGGL((route_score_kernel<D, R>), dim3(grid_for(nodes, NPB, cap), (unsigned)a.hkv, (unsigned)nlev), dim3(256),
-                     0, st, a);
+  if (a.dense) {
+    static const int per_cu = resident_per_cu(route_score_kernel<D, R, true>, 256);
+    const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
+    hipLaunchKernelGGL((route_score_kernel<D, R, true>), dim3(grid_for(nodes, NPB, cap), (unsigned)a.hkv, (unsigned)nlev),
+                       dim3(256), 0, st, a);
+  } else {
+    static const int per_cu = resident_per_cu(route_score_kernel<D, R, false>, 256);
+    const int64_t cap = (int64_t)per_cu * device_cus() / a.hkv;
+    hipLaunchKernelGGL((route_score_kernel<D, R, false>), dim3(grid_for(nodes, NPB, cap), (unsigned)a.hkv, (unsigned)nlev),
+                       dim3(256), 0, st, a);
+  }
 }
 
 template <int D, int R, int B>
