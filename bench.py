@@ -55,6 +55,8 @@ def parse():
                     help="also time zha_tree_append_n of this many tokens onto a tree of N-m (0: skip)")
     ap.add_argument("--build-reps", type=int, default=3)
     ap.add_argument("--dense-reps", type=int, default=20)
+    ap.add_argument("--route", default="auto", choices=("auto", "frontier", "keys"),
+                    help="decode scoring: the config's default, per-level union frontiers, or every level from the keys")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of timed oracle decode")
     ap.add_argument("--cold-steps", type=int, default=32,
@@ -109,6 +111,32 @@ def top_levels(w, n_tokens, key_form):
     return list(range(lo, w.levels + 1))
 
 
+AK_LC = 4   # the level whose nodes one all-keys score workgroup covers
+
+
+def allkeys_score_bytes(w, n_tokens):
+    """Algorithmic HBM bytes of one launch of the all-keys score kernel (every level from the
+    keys): per KV head the N keys (bf16) and their level-1 token weights (R floats a token),
+    each level-1..4 node's c and LSE (2R floats), one float score per query head written per
+    node of levels 1..4, and the level-4 dot products (R floats per query head) written."""
+    R, d, g = w.num_ref, w.head_dim, w.group
+    per = n_tokens * (2 * d + 4 * R)
+    for lv in range(1, AK_LC + 1):
+        per += w.nodes(lv, n_tokens) * (8 * R + 4 * g)
+    per += w.nodes(AK_LC, n_tokens) * g * R * 4
+    return float(per * w.num_kv_heads)
+
+
+def allkeys_upper_bytes(w, n_tokens):
+    """Bytes the top-down selection reads to derive the levels above level 4: the level-4 dot
+    products once per query head and each upper node's c and LSE once per query head."""
+    R, g = w.num_ref, w.group
+    per = w.nodes(AK_LC, n_tokens) * g * R * 4 * 2
+    for lv in range(AK_LC + 1, w.levels + 1):
+        per += w.nodes(lv, n_tokens) * 8 * R * g
+    return float(per * w.num_kv_heads)
+
+
 def kernel_bytes(key, w, stats_rows, n_tokens, key_form):
     """Algorithmic HBM bytes of one launch of `key` given the routing stats of that step.
 
@@ -119,6 +147,8 @@ def kernel_bytes(key, w, stats_rows, n_tokens, key_form):
     dense_attend:     N * Hkv * 2 * d * 2 bytes.
     """
     d, L = w.head_dim, w.levels
+    if key == "route_score.keys":
+        return allkeys_score_bytes(w, n_tokens)
     if key.startswith("route_score.l"):
         lv = int(key.split(".l")[1])
         u = stats_rows[L - lv].sum()
@@ -755,6 +785,8 @@ def main():
     tree = zha.Tree(cfg)
     h = tree.handle
     key_form = zha.zha_level1_key_form(cfg) == 1
+    tree.set_route_mode({"auto": 0, "frontier": 1, "keys": 2}[args.route])
+    allkeys = tree.route_mode == 2
     p_levels = None
     if args.p_levels:
         p_levels = ([w.top_p ** (1.0 / w.levels)] * w.levels if args.p_levels == "compound"
@@ -797,7 +829,8 @@ def main():
     app_ms, app_n = zha.zha_profile_stop(h)
     # rank the launches of one extra (untimed, append-free) decode; one bracket per decode
     # keeps each launch's timing undisturbed by the other brackets
-    keys = ["route_prep", "attend", "route_score.top", "route_select.top", "route_expand.top"] + [
+    keys = ["route_prep", "attend", "route_score.top", "route_select.top", "route_expand.top",
+            "route_score.keys", "route_select.keys", "route_expand.keys"] + [
         f"route_{k}.l{l}" for l in range(1, w.levels + 1) for k in ("score", "select", "expand")]
     probe_ms = {}
     snap = tree.n_tokens
@@ -889,6 +922,9 @@ def main():
     R, d, g, L = w.num_ref, w.head_dim, w.group, w.levels
     per_level = np.array([node_bytes(w, L - row, key_form) for row in range(L)], dtype=np.float64)
     router_b = (timed_stats[:, :L, :].sum(axis=2) * per_level[None, :]).sum(axis=1)
+    if allkeys:
+        router_b = np.array([allkeys_score_bytes(w, n0 + args.warmup + i + 1) + allkeys_upper_bytes(w, n0 + args.warmup + i + 1)
+                             for i in range(steps)])
     gather_b = timed_stats[:, L, :].sum(axis=1) * w.block * 2 * d * 2
     step_bytes = float(np.mean(router_b + gather_b))
     # the whole step against the HBM roofline: cold first (each step after the read flush),
@@ -896,8 +932,11 @@ def main():
     roofline_step = None
     if cold:
         cst = stats.cpu().numpy()[args.warmup + steps:args.warmup + steps + n_cold_read]
-        cold_bytes = float(np.mean((cst[:, :L, :].sum(axis=2) * per_level[None, :]).sum(axis=1) +
-                                   cst[:, L, :].sum(axis=1) * w.block * 2 * d * 2))
+        c_router = (cst[:, :L, :].sum(axis=2) * per_level[None, :]).sum(axis=1)
+        if allkeys:
+            c_router = np.array([allkeys_score_bytes(w, n0 + args.warmup + steps + i + 1) +
+                                 allkeys_upper_bytes(w, n0 + args.warmup + steps + i + 1) for i in range(len(cst))])
+        cold_bytes = float(np.mean(c_router + cst[:, L, :].sum(axis=1) * w.block * 2 * d * 2))
         ach_c = cold_bytes / (cold["median_ms"] * 1e-3) / 1e9
         ach_w = step_bytes / (ms_per_step * 1e-3) / 1e9
         roofline_step = {
@@ -933,11 +972,16 @@ def main():
     # ---- the same warm steps with quantised router planes (bf16, MX FP4): a second tree
     # over the same caches (its appends rewrite rows n0.. with the values they already hold)
     quant = {}
-    for fmt in (("bf16", "fp4") if w.planes == "f32" and not args.no_quant_planes else ()):
+    legs = ("bf16", "fp4") if w.planes == "f32" and not args.no_quant_planes else ()
+    if allkeys and not args.no_quant_planes:
+        legs = ("f32",) + legs     # the frontier path, which reads the planes, for comparison
+    for fmt in legs:
         w2 = w.with_(planes=fmt)
         cfg2 = zha.make_config(w.head_dim, w.num_kv_heads, w.num_q_heads, w.block, w.levels, w.num_ref,
                                w.capacity, w.dtype, w.top_p, w.keep_sink, fmt)
         tree2 = zha.Tree(cfg2)
+        if allkeys:
+            tree2.set_route_mode(1)
         if p_levels:
             tree2.set_top_p_levels(p_levels)
         b_ms = []
@@ -980,8 +1024,9 @@ def main():
         alg2 = float(np.mean([kernel_bytes(dom2, w2, st2[i], n0 + args.warmup + i + 1, key_form) for i in range(steps)]))
         ach2 = alg2 / (d2_ms / max(d2_n, 1) * 1e-3) / 1e9
         quant[fmt] = {
+            "route": "frontier" if tree2.route_mode == 1 else "keys",
             "ms_per_step": round(wall2 * 1e3 / steps, 4), "queries_per_s": round(steps / wall2, 2),
-            "speedup_vs_f32_planes": round(ms_per_step / (wall2 * 1e3 / steps), 3),
+            "speedup_vs_main_line": round(ms_per_step / (wall2 * 1e3 / steps), 3),
             "build_ms": round(min(b_ms), 4),
             "decode_step_alg_bytes": round(step2_b),
             "roofline": dict(bound="hbm", kernel=dom2, achieved=round(ach2, 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -990,7 +1035,7 @@ def main():
                              traffic=traffic_for(dom2, f"{w.name}_{fmt}planes")),
             "kernel_ms": {k: round(v, 4) for k, v in sorted(probe2.items(), key=lambda x: -x[1])},
         }
-        log(f"[bench] {fmt} router planes: {quant[fmt]['ms_per_step']:.3f} ms/step, "
+        log(f"[bench] {fmt} router planes ({quant[fmt]['route']}): {quant[fmt]['ms_per_step']:.3f} ms/step, "
             f"{quant[fmt]['queries_per_s']:.1f} queries/s; {dom2} {d2_ms / max(d2_n, 1):.4f} ms/launch "
             f"({ach2 / HBM_PEAK_GBS:.3f} of HBM)")
         tree2.close()
@@ -1086,7 +1131,7 @@ def main():
         "cpu_baseline": cpu,
         "cold": cold,
         "cold_after_write": cold_write,
-        "decode_step": {"level1_key_form": key_form, "alg_bytes": round(step_bytes), "achieved_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "decode_step": {"route": "keys" if allkeys else "frontier", "level1_key_form": key_form, "alg_bytes": round(step_bytes), "achieved_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                         "router_bytes": round(float(np.mean(router_b))), "gather_bytes": round(float(np.mean(gather_b))),
                         "frontier_union_per_level": timed_stats[:, :L, :].sum(axis=2).mean(axis=0).round(1).tolist(),
                         "kept_blocks_union": float(timed_stats[:, L, :].sum(axis=1).mean()),
@@ -1099,6 +1144,7 @@ def main():
                   "kernel_ms": round(dense_ms_k / max(dense_n, 1), 4), "alg_bytes": dense_bytes,
                   "frac_hbm": round(dense_bytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "zha_speedup": round(dense_ms / ms_per_step, 3)},
+        "frontier_route_f32_planes": quant.get("f32"),
         "bf16_router_planes": quant.get("bf16"),
         "fp4_router_planes": quant.get("fp4"),
         "append_n": append_n,

@@ -63,12 +63,28 @@ struct RouteArgs {
                       // dev.tdbits (teacher forcing) instead of being every node
   int32_t sel_p;      // top-p histogram / classify workgroups per KV head at `level`
   int32_t key_form;   // level 1 scored from the block's keys and the planes' token weights
+  int32_t nref;       // reference queries (planes per node)
+  int32_t allkeys;    // every level scored from the keys (route_score_allkeys_kernel) and
+                      // selected top-down with level 1 (route_topdown_keys_kernel)
   int32_t q_bf16;     // q (and the caches) are bf16; else fp32
   int32_t planes;     // router planes read: 0 fp32 (dev.s), 1 bf16 (dev.sq), 2 MX FP4 (dev.s4, dev.s4x)
   const void* K;      // key cache [Hkv][kcap][D] (key-form scoring)
   int64_t kcap;
   int64_t nl[MAXL + 1];   // nodes per level at N
 };
+
+// Top-down bitmaps of query head hq at level lv: frontier words, then (td_stride words
+// later) kept words.
+__device__ __forceinline__ int64_t td_stride(const RouteArgs& a, int lv) {
+  return (lv == 1 && a.allkeys) ? a.dev.ncap[1] / 32 : (int64_t)TD_WORDS;
+}
+__device__ __forceinline__ uint32_t* td_front_words(const RouteArgs& a, int lv, int hq) {
+  if (lv == 1 && a.allkeys) return a.dev.kb1 + (int64_t)hq * 2 * (a.dev.ncap[1] / 32);
+  return a.dev.tdbits + (((int64_t)lv * a.hq + hq) * 2) * TD_WORDS;
+}
+__device__ __forceinline__ uint32_t* td_kept_words(const RouteArgs& a, int lv, int hq) {
+  return td_front_words(a, lv, hq) + td_stride(a, lv);
+}
 
 struct AttnArgs {
   Dev dev;
@@ -198,6 +214,13 @@ hipError_t launch_route_td_children(const RouteArgs& a, hipStream_t st);
 // Per-head frontier bitmaps of level a.level in dev.tdbits from that level's union list
 // (dev.node / dev.mask / dev.cnt): the given frontier of a teacher-forced top-down level.
 hipError_t launch_route_td_seed(const RouteArgs& a, hipStream_t st);
+// Every level from the keys (a.allkeys): scores of levels 1..4 and the level-4 dot products
+// in one pass over the key cache; then the levels above level 4 derived, and every level
+// from a.level down to a.dense_lo selected top-down (one workgroup per query head); then the
+// gather list of the kept level-1 blocks per KV head.
+hipError_t launch_route_allkeys_score(const RouteArgs& a, int D, int R, hipStream_t st);
+hipError_t launch_route_topdown_keys(const RouteArgs& a, hipStream_t st);
+hipError_t launch_route_gather_list(const RouteArgs& a, hipStream_t st);
 
 hipError_t launch_attend(const AttnArgs& a, bool bf16, int D, bool dense, hipStream_t st);
 // Attention workgroups resident on the GPU at once, per KV head (one wave of workgroups).

@@ -288,6 +288,307 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
   }
 }
 
+// ------------------------------------------------------------------ every level from the keys
+// Top-down selection after route_score_allkeys_kernel scored levels 1..4 and wrote the
+// level-4 dot products.  First the levels above level 4 are derived from those (a parent's
+// D_j is its children's D_j weighted by exp(LSE_cj - LSE_j); its score max_j (D_j + c_j)),
+// held in LDS.  Then every level from a.level down to a.dense_lo is selected by the same
+// rule and fixed-point masses as the other top-down kernel, reading the scores of levels
+// 1..4 from global memory in three passes (max, coarse histogram, classification) so that
+// no per-node LDS array bounds the level size: level 1 of a deep tree has 65K nodes per head.
+
+// bit i of the byte x -> bits 4i..4i+3 (a block-4 parent's kept bit -> its children's bits)
+__device__ __forceinline__ uint32_t spread4(uint32_t x) {
+  x = (x | (x << 12)) & 0x000F000Fu;
+  x = (x | (x << 6)) & 0x03030303u;
+  x = (x | (x << 3)) & 0x11111111u;
+  return x * 0xFu;
+}
+
+constexpr int TK_THREADS = 1024;
+__global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArgs a) {
+  constexpr int NW = TK_THREADS / 64;
+  constexpr int KW = AK_N1 / 32;
+  __shared__ uint32_t kb2[2][KW];              // kept bitmaps: level above / this level
+  __shared__ uint32_t fbw[KW];                 // this level's frontier
+  __shared__ __align__(16) float Dup[AK_DUP];  // dot products of the levels above level 4
+  __shared__ __align__(16) float Sup[AK_SUP];  // their scores, each level 32-aligned
+  __shared__ unsigned long long h[NB1];        // coarse, then fine mass histogram, then radix digits
+  __shared__ int32_t cand[TD_CAND];
+  __shared__ float cand_s[TD_CAND];
+  __shared__ int32_t tie_e[TD_TIES];
+  __shared__ float tie_s[TD_TIES];
+  __shared__ uint64_t tie_m[TD_TIES];
+  __shared__ float redm[NW];
+  __shared__ uint32_t s_b1, s_b2, s_ncand, s_ntie;
+  __shared__ uint64_t s_T, s_above1, s_above2, s_prefix, s_rabove;
+  const int hq = blockIdx.x, kv = hq / a.g, gi = hq % a.g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = a.nref;
+
+  // ---- levels above level 4: dot products and scores
+  if (a.level > AK_LC) {
+    const int64_t cap4 = a.dev.ncap[AK_LC];
+    const float* kd = a.dev.kdots + ((int64_t)kv * cap4 * GMAX + gi) * R;   // node c at kd + c * GMAX * R
+    int64_t dpo = 0, dco = 0, so = 0;
+    for (int lv = AK_LC + 1; lv <= a.level; ++lv) {
+      const int64_t n = a.nl[lv], nc = a.nl[lv - 1];
+      const int64_t capl = a.dev.ncap[lv], capc = a.dev.ncap[lv - 1];
+      const float* lsep = a.dev.lse[lv] + kv * capl * R;
+      const float* lsec = a.dev.lse[lv - 1] + kv * capc * R;
+      const float* cp = a.dev.c[lv] + kv * capl * R;
+      for (int64_t i = tid; i < n * R; i += TK_THREADS) {
+        const int64_t node = i / R;
+        const int j = (int)(i % R);
+        const float lp = lsep[node * R + j];
+        float acc = 0.f;
+        for (int k = 0; k < AK_B; ++k) {
+          const int64_t c = node * AK_B + k;
+          if (c >= nc) break;
+          const float dc = lv - 1 == AK_LC ? kd[c * GMAX * R + j] : Dup[dpo + c * R + j];
+          acc += expf(lsec[c * R + j] - lp) * dc;
+        }
+        Dup[dco + i] = acc;
+      }
+      __syncthreads();
+      float* gs = a.dev.score[lv] + ((int64_t)kv * GMAX + gi) * capl;
+      for (int64_t node = tid; node < n; node += TK_THREADS) {
+        float m = -INFINITY;
+        for (int j = 0; j < R; ++j) m = fmaxf(m, Dup[dco + node * R + j] + cp[node * R + j]);
+        Sup[so + node] = m;
+        gs[node] = m;
+      }
+      __syncthreads();
+      dpo = dco;
+      dco += n * R;
+      so += (n + 31) & ~(int64_t)31;
+    }
+  }
+
+  // ---- the levels top-down
+  int pb = 0;   // kb2[pb] = kept bitmap of the level above
+  bool empty = false;
+  for (int lv = a.level; lv >= a.dense_lo; --lv) {
+    const int64_t n = a.nl[lv];
+    const int nw = (int)((n + 31) >> 5);
+    const bool top = lv == a.level;
+    ZHA_CHECK(a.dev, nw <= KW, CHK_TD_SIZE);
+    const float* S;
+    if (lv > AK_LC) {
+      int64_t so = 0;
+      for (int m = AK_LC + 1; m < lv; ++m) so += (a.nl[m] + 31) & ~(int64_t)31;
+      S = Sup + so;
+    } else {
+      S = a.dev.score[lv] + ((int64_t)kv * GMAX + gi) * a.dev.ncap[lv];
+    }
+    uint32_t* gf = td_front_words(a, lv, hq);
+    uint32_t* gk = td_kept_words(a, lv, hq);
+    uint32_t* kc = kb2[pb ^ 1];
+    const uint32_t* kp = kb2[pb];
+    // ---- the frontier: every node at the top (or the given frontier), else the children of
+    // the kept nodes one level up
+    for (int w = tid; w < nw; w += TK_THREADS) {
+      uint32_t f;
+      if (empty) f = 0u;
+      else if (top) f = a.tf ? gf[w] : ~0u;
+      else f = spread4((kp[w >> 2] >> (8 * (w & 3))) & 0xffu);
+      const int64_t rem = n - 32 * (int64_t)w;
+      if (rem < 32) f &= (1u << rem) - 1u;
+      fbw[w] = f;
+    }
+    for (int i = tid; i < NB1; i += TK_THREADS) h[i] = 0ull;
+    __syncthreads();
+    // ---- pass 1: the frontier's max score (a word's 32 scores as eight float4 loads)
+    float mx = -INFINITY;
+    for (int w = tid; w < nw; w += TK_THREADS) {
+      const uint32_t f = fbw[w];
+      if (!f) continue;
+      float4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = *(const float4*)(S + 32 * w + 4 * k);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((f >> (4 * k + e)) & 1u) mx = fmaxf(mx, x[e]);
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if (lane == 0) redm[wave] = mx;
+    __syncthreads();
+    float M = redm[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, redm[w]);
+    if (M == -INFINITY) {
+      // nothing in the frontier: nothing kept here or below
+      empty = true;
+      for (int w = tid; w < nw; w += TK_THREADS) { gf[w] = 0u; gk[w] = 0u; kc[w] = 0u; }
+      pb ^= 1;
+      __syncthreads();
+      continue;
+    }
+    // ---- pass 2: coarse histogram of the fixed-point masses
+    for (int w = tid; w < nw; w += TK_THREADS) {
+      const uint32_t f = fbw[w];
+      if (!f) continue;
+      float4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = *(const float4*)(S + 32 * w + 4 * k);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((f >> (4 * k + e)) & 1u) atomicAdd(&h[bin_of(x[e], M).bin], (unsigned long long)mass_of(x[e], M));
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      uint64_t v[8], excl, Z;
+      td_scan512(h, lane, v, excl, Z);
+      uint32_t b1 = NB1;
+      uint64_t T = 0, above1 = 0;
+      if (a.top_p[lv] < 1.0f && Z > 0) {
+        const double tt = ceil((double)a.top_p[lv] * (double)Z);
+        T = tt < 1.0 ? 1ull : (uint64_t)tt;
+        if (T > Z) T = Z;
+        td_find(v, excl, T, b1, above1);
+      }
+      if (lane == 0) { s_b1 = b1; s_T = T; s_above1 = above1; s_ncand = 0; s_ntie = 0; }
+    }
+    __syncthreads();
+    const uint32_t b1 = s_b1;
+    const uint64_t T = s_T;
+    // ---- pass 3: kept words (bins before the boundary bin), frontier words out, the
+    // boundary bin's nodes listed
+    for (int w = tid; w < nw; w += TK_THREADS) {
+      const uint32_t f = fbw[w];
+      uint32_t kw = 0u, cw = 0u;
+      if (f) {
+        float4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = *(const float4*)(S + 32 * w + 4 * k);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t bit = 1u << (4 * k + e);
+            if (!(f & bit)) continue;
+            const uint32_t code = bin_of(x[e], M).bin;
+            if (code < b1) kw |= bit;
+            else if (code == b1) cw |= bit;
+          }
+        }
+      }
+      gf[w] = f;
+      kc[w] = kw;
+      while (cw) {
+        const int idx = __ffs(cw) - 1;
+        cw &= cw - 1u;
+        const uint32_t j = atomicAdd(&s_ncand, 1u);
+        if (j < (uint32_t)TD_CAND) cand[j] = 32 * w + idx;
+      }
+    }
+    for (int i = tid; i < NB2; i += TK_THREADS) h[i] = 0ull;
+    __syncthreads();
+    if (b1 < (uint32_t)NB1) {
+      const uint32_t nc = s_ncand;
+      const bool listed = nc <= (uint32_t)TD_CAND;
+      // f(node, score) for every node of the boundary bin
+      auto for_each_cand = [&](auto&& fn) {
+        if (listed) {
+          for (uint32_t i = tid; i < nc; i += TK_THREADS) fn(cand[i], cand_s[i]);
+        } else {
+          for (int64_t e = tid; e < n; e += TK_THREADS) {
+            if (!((fbw[e >> 5] >> (e & 31)) & 1u)) continue;
+            const float x = S[e];
+            if (bin_of(x, M).bin == b1) fn((int)e, x);
+          }
+        }
+      };
+      if (listed)
+        for (uint32_t i = tid; i < nc; i += TK_THREADS) cand_s[i] = S[cand[i]];
+      __syncthreads();
+      for_each_cand([&](int e, float x) {
+        atomicAdd(&h[bin_of(x, M).sub], (unsigned long long)mass_of(x, M));
+      });
+      __syncthreads();
+      if (wave == 0) {
+        uint64_t v[8], excl, tot;
+        td_scan512(h, lane, v, excl, tot);
+        uint32_t b2;
+        uint64_t above2;
+        td_find(v, s_above1 + excl, T, b2, above2);
+        if (lane == 0) { s_b2 = b2; s_above2 = above2; }
+      }
+      __syncthreads();
+      const uint32_t b2 = s_b2;
+      const uint64_t above2 = s_above2;
+      for_each_cand([&](int e, float x) {
+        const uint32_t sub = bin_of(x, M).sub;
+        if (sub < b2) {
+          atomicOr(&kc[e >> 5], 1u << (e & 31));
+        } else if (sub == b2) {
+          const uint32_t k = atomicAdd(&s_ntie, 1u);
+          if (k < (uint32_t)TD_TIES) { tie_e[k] = e; tie_s[k] = x; tie_m[k] = mass_of(x, M); }
+        }
+      });
+      __syncthreads();
+      const uint32_t nt = s_ntie;
+      if (nt <= (uint32_t)TD_TIES) {
+        for (uint32_t x = tid; x < nt; x += TK_THREADS) {
+          uint64_t ab = 0;
+          const uint64_t kx = rank_key(tie_s[x], tie_e[x]);
+          for (uint32_t y = 0; y < nt; ++y)
+            if (rank_key(tie_s[y], tie_e[y]) < kx) ab += tie_m[y];
+          if (above2 + ab < T) atomicOr(&kc[tie_e[x] >> 5], 1u << (tie_e[x] & 31));
+        }
+      } else {
+        // radix select on the 64-bit rank key of the boundary sub-bin's nodes, 8 bits a pass
+        unsigned long long* dh = h;
+        if (tid == 0) { s_prefix = 0; s_rabove = above2; }
+        __syncthreads();
+        for (int pass = 0; pass < 8; ++pass) {
+          const int shift = 56 - 8 * pass;
+          const uint64_t hi = pass == 0 ? 0ull : (~0ull << (shift + 8));
+          for (int i = tid; i < 256; i += TK_THREADS) dh[i] = 0ull;
+          __syncthreads();
+          const uint64_t pf = s_prefix;
+          for_each_cand([&](int e, float x) {
+            if (bin_of(x, M).sub != b2) return;
+            const uint64_t k = rank_key(x, e);
+            if ((k & hi) == (pf & hi)) atomicAdd(&dh[(k >> shift) & 255u], (unsigned long long)mass_of(x, M));
+          });
+          __syncthreads();
+          if (tid == 0) {
+            uint64_t run = s_rabove;
+            for (int d = 0; d < 256; ++d) {
+              if (run + dh[d] >= T) { s_prefix = pf | ((uint64_t)d << shift); s_rabove = run; break; }
+              run += dh[d];
+            }
+          }
+          __syncthreads();
+        }
+        const uint64_t kb = s_prefix;
+        for_each_cand([&](int e, float x) {
+          if (bin_of(x, M).sub == b2 && rank_key(x, e) <= kb) atomicOr(&kc[e >> 5], 1u << (e & 31));
+        });
+      }
+      __syncthreads();
+    }
+    for (int w = tid; w < nw; w += TK_THREADS) gk[w] = kc[w];
+    pb ^= 1;
+    __syncthreads();
+  }
+}
+
+hipError_t launch_route_topdown_keys(const RouteArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(route_topdown_keys_kernel, dim3((unsigned)a.hq), dim3(TK_THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
 // Dense union lists of the top-down levels: entry e = node e, mask / keep = the heads of the
 // group whose frontier holds / who kept node e.  A workgroup takes 2,048 nodes of one level
 // and KV head; the group's bitmap words for them go through LDS first.
@@ -307,10 +608,10 @@ __global__ __launch_bounds__(256) void route_topdown_union_kernel(RouteArgs a) {
   const int64_t w0 = e0 / 32, nw = (n + 31) / 32;
   for (int i = threadIdx.x; i < g * W; i += 256) {
     const int gi = i / W, w = i % W;
-    const uint32_t* gb = a.dev.tdbits + (((int64_t)lv * a.hq + kv * g + gi) * 2) * TD_WORDS;
+    const uint32_t* gb = td_front_words(a, lv, kv * g + gi);
     const bool ok = w0 + w < nw;
     fb[gi][w] = ok ? gb[w0 + w] : 0u;
-    kb[gi][w] = ok ? gb[TD_WORDS + w0 + w] : 0u;
+    kb[gi][w] = ok ? gb[td_stride(a, lv) + w0 + w] : 0u;
   }
   __syncthreads();
   const int64_t e1 = e0 + UN_NODES < n ? e0 + UN_NODES : n;
@@ -334,7 +635,7 @@ __global__ __launch_bounds__(256) void route_td_seed_kernel(RouteArgs a) {
   const int64_t n = a.nl[lv], nw = (n + 31) / 32, cap = a.dev.ncap[lv];
   for (int64_t i = threadIdx.x; i < (int64_t)g * nw; i += 256) {
     const int gi = (int)(i / nw);
-    a.dev.tdbits[(((int64_t)lv * a.hq + kv * g + gi) * 2) * TD_WORDS + i % nw] = 0u;
+    td_front_words(a, lv, kv * g + gi)[i % nw] = 0u;
   }
   __syncthreads();
   const int64_t cnt = a.dev.cnt[lv * a.hkv + kv];
@@ -344,7 +645,7 @@ __global__ __launch_bounds__(256) void route_td_seed_kernel(RouteArgs a) {
     if (node < 0 || node >= n) continue;
     for (int gi = 0; gi < g; ++gi)
       if ((mk >> gi) & 1u)
-        atomicOr(&a.dev.tdbits[(((int64_t)lv * a.hq + kv * g + gi) * 2) * TD_WORDS + (node >> 5)], 1u << (node & 31));
+        atomicOr(&td_front_words(a, lv, kv * g + gi)[node >> 5], 1u << (node & 31));
   }
 }
 

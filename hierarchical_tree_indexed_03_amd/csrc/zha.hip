@@ -39,6 +39,9 @@ struct zha_tree {
   RouteArgs td_args;
   bool td_valid;
   bool td_lists;
+  // how decode scores the tree: 0 = by the config (allkeys_auto), 1 = frontier lists (planes,
+  // key-form level 1), 2 = every level from the keys
+  int32_t route_mode;
   // the last sub-batch of zha_prefill_batched (its buffers are in the caller's workspace)
   PrefillArgs pf_args;
   bool pf_valid;
@@ -87,6 +90,40 @@ bool key_form(const zha_config& c) {
   const int64_t keys = (int64_t)c.block * c.head_dim * 2 + (int64_t)c.num_ref * c.block * 4;
   const int64_t planes = (int64_t)c.num_ref * c.head_dim * 4;
   return keys < planes;
+}
+
+// Every level scored from the keys (allkeys.hip) is possible for block-4 key-form trees of at
+// least AK_LC levels whose level 1 and levels above level 4 fit the top-down kernel's LDS.
+bool allkeys_possible(const zha_config& c) {
+  if (!key_form(c) || c.block != AK_B || c.levels < AK_LC) return false;
+  if (c.num_ref % 4 || c.num_ref > 16) return false;
+  if (nodes_at(c, 1, c.capacity) > AK_N1) return false;
+  for (int l = 2; l <= c.levels; ++l)
+    if (nodes_at(c, l, c.capacity) > TD_MAX) return false;
+  int64_t dup = 0, sup = 0;
+  for (int l = AK_LC + 1; l <= c.levels; ++l) {
+    dup += nodes_at(c, l, c.capacity) * c.num_ref;
+    sup += ceil_div(nodes_at(c, l, c.capacity), 32) * 32;
+  }
+  return dup <= AK_DUP && sup <= AK_SUP;
+}
+
+// Bytes one decode reads to score every level from the keys, against the other path with
+// its level-1 frontier covering the whole level (its upper levels are scored whole anyway):
+// keys and token weights per token, (c, LSE) per node of levels 1..4, against the router
+// planes of levels 2..L plus the level-1 keys, token weights and offsets.  Counted at
+// capacity.
+bool allkeys_auto(const zha_config& c) {
+  if (!allkeys_possible(c)) return false;
+  const int64_t R = c.num_ref, D = c.head_dim, n = c.capacity;
+  int64_t keys = n * (2 * D + 4 * R);
+  for (int l = 1; l <= AK_LC; ++l) keys += nodes_at(c, l, n) * 8 * R;
+  const int64_t plane = c.plane_dtype == ZHA_BF16 ? R * (2 * D + 4)
+                        : c.plane_dtype == ZHA_MXFP4 ? R * (D / 2 + D / 32 + 4)
+                                                     : R * (D + 1) * 4;
+  int64_t other = n * (2 * D + 4 * R) + nodes_at(c, 1, n) * 4 * R;
+  for (int l = 2; l <= c.levels; ++l) other += nodes_at(c, l, n) * plane;
+  return keys <= other;
 }
 
 int tile_tokens(const zha_config& c) { return c.block <= 128 ? 128 : 256; }
@@ -171,6 +208,10 @@ size_t layout(const zha_config& c, char* base, Dev* dev) {
   d.qs = (QState*)take((size_t)((L + 1) * Q) * sizeof(QState));
   d.hpart = (uint64_t*)take((size_t)(H * SEL_P * GMAX * NB1) * 8);
   d.tdbits = (uint32_t*)take((size_t)((L + 1) * Q * 2 * TD_WORDS) * 4);
+  if (allkeys_possible(c)) {
+    d.kb1 = (uint32_t*)take((size_t)(Q * 2 * (d.ncap[1] / 32)) * 4);
+    d.kdots = (float*)take((size_t)(H * d.ncap[AK_LC] * GMAX * R) * 4);
+  }
   d.sib = (float*)take((size_t)(H * SIB_STRIDE(R, D)) * 4);
   d.sibkey = (int64_t*)take((size_t)(H * (MAXL + 1)) * 8);
   d.cand = (int32_t*)take((size_t)(Q * d.ncap[1]) * 4);
@@ -202,6 +243,8 @@ RouteArgs route_args(const zha_tree* t, const void* q) {
   for (int l = 0; l <= MAXL; ++l) a.top_p[l] = t->top_p[l];
   a.sigma = 1.0f / sqrtf((float)t->cfg.head_dim);
   a.key_form = key_form(t->cfg) ? 1 : 0;
+  a.nref = t->cfg.num_ref;
+  a.allkeys = t->route_mode == 2 || (t->route_mode == 0 && allkeys_auto(t->cfg)) ? 1 : 0;
   a.q_bf16 = t->cfg.dtype == ZHA_BF16 ? 1 : 0;
   a.planes = t->cfg.plane_dtype;
   a.K = t->K;
@@ -269,6 +312,26 @@ extern "C" {
 int32_t zha_level1_key_form(const zha_config* cfg) {
   if (validate(cfg) != ZHA_OK) return -1;
   return key_form(*cfg) ? 1 : 0;
+}
+
+int32_t zha_route_keys(const zha_config* cfg) {
+  if (validate(cfg) != ZHA_OK) return -1;
+  return allkeys_auto(*cfg) ? 1 : 0;
+}
+
+zha_status zha_set_route_mode(zha_tree* t, int32_t mode) {
+  if (!t) return fail(ZHA_E_INVALID, "tree is null");
+  if (mode < 0 || mode > 2) return fail(ZHA_E_INVALID, "route mode %d outside 0..2", mode);
+  if (mode == 2 && !allkeys_possible(t->cfg))
+    return fail(ZHA_E_UNSUPPORTED, "this config cannot score every level from the keys");
+  t->route_mode = mode;
+  t->td_valid = false;
+  return ZHA_OK;
+}
+
+int32_t zha_route_mode(const zha_tree* t) {
+  if (!t) return -1;
+  return (t->route_mode == 2 || (t->route_mode == 0 && allkeys_auto(t->cfg))) ? 2 : 1;
 }
 
 size_t zha_workspace_bytes(const zha_config* cfg) {
@@ -579,8 +642,9 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
   const zha_config& c = t->cfg;
   RouteArgs r = route_args(t, q);
   r.nlevel = nodes_at(c, c.levels, t->N);
-  // top levels small enough to score whole and select top-down in one launch
-  const int lo = topdown_lo(r);
+  // top levels small enough to score whole and select top-down in one launch (every level
+  // when all are scored from the keys)
+  const int lo = r.allkeys ? 1 : topdown_lo(r);
   r.dense_lo = lo <= c.levels ? lo : 0;   // prep sets the list sizes of those levels
   hipError_t e;
   {
@@ -589,7 +653,29 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
   }
   if (e != hipSuccess) return hip_fail(e, "route prep launch");
   t->td_valid = false;
-  if (lo <= c.levels) {
+  if (r.allkeys) {
+    // levels 1..4 and the level-4 dot products from one pass over the keys; the levels above
+    // derived and every level selected top-down; the union of the kept blocks
+    r.level = c.levels;
+    {
+      ProfScope ps(t, "route_score.keys", stream);
+      e = launch_route_allkeys_score(r, c.head_dim, c.num_ref, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "route key score launch");
+    {
+      ProfScope ps(t, "route_select.keys", stream);
+      e = launch_route_topdown_keys(r, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "route top-down select launch");
+    {
+      ProfScope ps(t, "route_expand.keys", stream);
+      e = launch_route_gather_list(r, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "gather list launch");
+    t->td_args = r;
+    t->td_valid = true;
+    t->td_lists = false;
+  } else if (lo <= c.levels) {
     r.level = c.levels;
     r.dense = 1;
     {
@@ -1137,7 +1223,24 @@ zha_status zha_debug_route_level(zha_tree* t, int32_t level, const void* q, cons
   if (e == hipSuccess)
     e = hipMemcpyAsync(t->dev.cnt + (int64_t)level * H, counts, H * 4, hipMemcpyDeviceToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "frontier copy");
-  if (path == 0 && level >= topdown_lo(r)) {
+  if (path == 0 && r.allkeys) {
+    // the decode's kernels: every node scored from the keys, the top-down selection of this
+    // level started from the given per-head frontiers, the dense union list
+    r.level = level;
+    r.dense_lo = level;
+    r.nlevel = r.nl[level];
+    e = launch_route_td_seed(r, stream);
+    if (e != hipSuccess) return hip_fail(e, "frontier seed launch");
+    e = launch_route_allkeys_score(r, c.head_dim, c.num_ref, stream);
+    if (e != hipSuccess) return hip_fail(e, "route key score launch");
+    r.tf = 1;
+    e = launch_route_topdown_keys(r, stream);
+    if (e == hipSuccess) e = launch_route_td_lists(r, stream);
+    if (e != hipSuccess) return hip_fail(e, "route top-down select launch");
+    t->td_args = r;
+    t->td_valid = true;
+    t->td_lists = true;
+  } else if (path == 0 && level >= topdown_lo(r)) {
     // the decode's kernels for this level: every node scored, the top-down selection
     // started from the given per-head frontiers, the dense union list
     r.level = level;

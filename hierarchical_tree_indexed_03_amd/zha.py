@@ -44,6 +44,9 @@ def _load() -> ctypes.CDLL:
     sig = {
         "zha_workspace_bytes": (SZ, [ctypes.POINTER(zha_config)]),
         "zha_level1_key_form": (I32, [ctypes.POINTER(zha_config)]),
+        "zha_route_keys": (I32, [ctypes.POINTER(zha_config)]),
+        "zha_set_route_mode": (I32, [P, I32]),
+        "zha_route_mode": (I32, [P]),
         "zha_create": (I32, [ctypes.POINTER(zha_config), P, SZ, ctypes.POINTER(P)]),
         "zha_tree_build": (I32, [P, P, P, I64, P, P]),
         "zha_tree_append": (I32, [P, P, P, P]),
@@ -78,7 +81,8 @@ def _load() -> ctypes.CDLL:
 
 
 _lib = _load()
-EXPORTED = ("zha_workspace_bytes", "zha_level1_key_form", "zha_create", "zha_tree_build", "zha_tree_append",
+EXPORTED = ("zha_workspace_bytes", "zha_level1_key_form", "zha_route_keys", "zha_set_route_mode", "zha_route_mode",
+            "zha_create", "zha_tree_build", "zha_tree_append",
             "zha_tree_append_n", "zha_decode", "zha_prefill", "zha_prefill_workspace_bytes", "zha_prefill_batched",
             "zha_debug_prefill_trace",
             "zha_decode_dense", "zha_decode_dense_static", "zha_debug_level", "zha_debug_router_planes", "zha_debug_trace", "zha_debug_route_level",
@@ -124,6 +128,18 @@ def make_config(head_dim, num_kv_heads, num_q_heads, block, levels, num_ref, cap
 
 def zha_level1_key_form(cfg: zha_config) -> int:
     return int(_lib.zha_level1_key_form(ctypes.byref(cfg)))
+
+
+def zha_route_keys(cfg: zha_config) -> int:
+    return int(_lib.zha_route_keys(ctypes.byref(cfg)))
+
+
+def zha_set_route_mode(t, mode: int):
+    _check(_lib.zha_set_route_mode(t, int(mode)))
+
+
+def zha_route_mode(t) -> int:
+    return int(_lib.zha_route_mode(t))
 
 
 def zha_workspace_bytes(cfg: zha_config) -> int:
@@ -281,6 +297,14 @@ class Tree:
         if p_levels is not None and len(p_levels) != self.cfg.levels:
             raise ValueError(f"need {self.cfg.levels} values, got {len(p_levels)}")
         zha_set_top_p_levels(self.handle, p_levels)
+
+    def set_route_mode(self, mode: int):
+        """0: the config's default, 1: union frontiers, 2: every level from the keys."""
+        zha_set_route_mode(self.handle, mode)
+
+    @property
+    def route_mode(self) -> int:
+        return zha_route_mode(self.handle)
 
     def decode(self, q, out=None, stats=None, stream=None):
         if out is None:

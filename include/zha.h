@@ -97,6 +97,21 @@ size_t zha_workspace_bytes(const zha_config* cfg);
  * only; no side effects. */
 int32_t zha_level1_key_form(const zha_config* cfg);
 
+/* Whether decode scores EVERY level from the keys for this config by default: 1 yes, 0 no,
+ * -1 invalid config.  A node's plane s_j is its children's s_j weighted by
+ * exp(LSE_cj - LSE_j) down to the keys (news summary, "Building the tree"; blog, "Building
+ * the tree": summaries grouped and compressed again), so q.s_j / sqrt(d) is the same
+ * weighted sum of the children's dot products, and every level's scores follow from one
+ * pass over the keys, the level-1 token weights and each node's (c_j, LSE_j): d*2 + R*4
+ * bytes per token plus 8R per node of levels 1..4, the levels above derived from level 4.
+ * Possible for bf16 keys, block 4, at least 4 levels, R in {4, 8, 16}, a level 1 scored
+ * from the keys (zha_level1_key_form) and at most 131,072 level-1 nodes at capacity (with
+ * levels 2.. at most 33,792 nodes and the levels above level 4 small enough for the
+ * selection's on-chip buffers).  Chosen by default when it reads no more bytes than the
+ * router planes of levels 2..L plus a level 1 scored whole from the keys.  Every level is
+ * then selected top-down, level 1 included, with the same top-p rule.  Host only. */
+int32_t zha_route_keys(const zha_config* cfg);
+
 /* Creates a handle over a caller-owned device `workspace` (>= zha_workspace_bytes,
  * 256-byte aligned).  The workspace is borrowed until zha_destroy. */
 zha_status zha_create(const zha_config* cfg, void* workspace, size_t workspace_bytes,
@@ -264,6 +279,18 @@ zha_status zha_decode_dense_static(const zha_config* cfg, const void* k_cache, c
  * after build, between decodes); a context-dependent schedule p_l(N) is set before each
  * decode.  Host only; nothing is enqueued.  On error the schedule is left unchanged. */
 zha_status zha_set_top_p_levels(zha_tree* t, const float* p_levels);
+
+/* Chooses how the following decodes score the tree: mode 0 = the config's default
+ * (zha_route_keys), 1 = per-level union frontiers (router planes, a level 1 from the keys
+ * where zha_level1_key_form says so), 2 = every level from the keys.  Both modes compute
+ * the same scores up to float32 rounding and apply the same selection rule.
+ * ZHA_E_UNSUPPORTED for mode 2 on a config that cannot take it; ZHA_E_INVALID for another
+ * mode.  Host only; nothing is enqueued; also used by zha_debug_route_level. */
+zha_status zha_set_route_mode(zha_tree* t, int32_t mode);
+
+/* The scoring the next decode uses: 1 = union frontiers, 2 = every level from the keys;
+ * -1 for a null handle.  Host only. */
+int32_t zha_route_mode(const zha_tree* t);
 
 /* Copies level `level` (1..levels) of the tree into caller buffers:
  *   s_out (device) float32 [Hkv][n_l][R][d], c_out (device) float32 [Hkv][n_l][R] with

@@ -62,15 +62,19 @@ def key_form(w: wc.Workload) -> bool:
             and w.block * w.head_dim * 2 + w.num_ref * w.block * 4 < w.num_ref * w.head_dim * 4)
 
 
-def router_levels(w: wc.Workload) -> list:
-    """Levels whose planes the router reads (all but a key-form level 1)."""
+def router_levels(w: wc.Workload, keys: bool = False) -> list:
+    """Levels whose planes the router reads (all but a key-form level 1; none when every
+    level is scored from the keys, ``keys``)."""
+    if keys:
+        return []
     return [lv for lv in range(1, w.levels + 1) if not (lv == 1 and key_form(w))]
 
 
-def router_trees(w: wc.Workload, trees: list) -> list:
+def router_trees(w: wc.Workload, trees: list, keys: bool = False) -> list:
     """The oracle trees as the router sees them: with quantised router planes, s quantised
-    at the levels the router reads planes at."""
-    if w.planes == "f32":
+    at the levels the router reads planes at (none when every level is scored from the
+    keys, ``keys``)."""
+    if w.planes == "f32" or keys:
         return trees
     lv = router_levels(w)
     return [zo.quantise_planes(t, lv, w.planes) for t in trees]
@@ -96,12 +100,12 @@ def quant_bounds(fmt: str, s: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return lo.reshape(s.shape), hi.reshape(s.shape)
 
 
-def flip_allowance(w: wc.Workload, tree, level: int, nodes, q) -> np.ndarray:
+def flip_allowance(w: wc.Workload, tree, level: int, nodes, q, keys: bool = False) -> np.ndarray:
     """Extra score tolerance per node for quantised router planes (see the module
-    docstring); zero for f32 planes and for a key-form level 1.  ``tree`` is the
-    full-precision tree."""
+    docstring); zero for f32 planes, for a key-form level 1 and for every level when all
+    are scored from the keys (``keys``).  ``tree`` is the full-precision tree."""
     nodes = np.asarray(nodes, dtype=np.int64)
-    if w.planes == "f32" or level not in router_levels(w):
+    if w.planes == "f32" or level not in router_levels(w, keys):
         return np.zeros(len(nodes))
     s = tree.levels[level - 1][0][nodes]
     lo, hi = quant_bounds(w.planes, s)

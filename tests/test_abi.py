@@ -101,6 +101,59 @@ def test_level1_key_form_choice(zha):
     assert ws_key > ws_f32
 
 
+def test_route_keys_choice(zha):
+    """Every level is scored from the keys by default on block-4 key-form trees of at least
+    four levels whose level 1 fits the selection (131,072 nodes at capacity), with every
+    plane format; never on trees whose router reads planes at level 1."""
+    assert zha.zha_route_keys(good(zha)) == 1
+    assert zha.zha_route_keys(good(zha, planes="bf16")) == 1
+    assert zha.zha_route_keys(good(zha, planes="fp4")) == 1
+    assert zha.zha_route_keys(good(zha, head_dim=64, num_ref=4, levels=4)) == 1
+    assert zha.zha_route_keys(good(zha, levels=3)) == 0                      # fewer than 4 levels
+    assert zha.zha_route_keys(good(zha, block=8, num_ref=1, levels=7)) == 0  # planes at level 1
+    assert zha.zha_route_keys(good(zha, block=256, levels=1)) == 0
+    assert zha.zha_route_keys(good(zha, block=2, levels=8)) == 0             # block 2
+    assert zha.zha_route_keys(good(zha, dtype="f32")) == 0
+    assert zha.zha_route_keys(good(zha, capacity=1 << 20)) == 0              # 262,144 level-1 nodes
+    assert zha.zha_route_keys(good(zha, capacity=1 << 19)) == 1              # 131,072
+    assert zha.zha_route_keys(good(zha, block=0)) == -1
+
+
+def test_route_mode_setting(zha):
+    """zha_set_route_mode is checked on the host; a refused mode leaves the old one."""
+    cfg = good(zha, capacity=1000)
+    t = zha.zha_create(cfg, 0x100000, zha.zha_workspace_bytes(cfg))
+    try:
+        assert zha.zha_route_mode(t) == 2
+        zha.zha_set_route_mode(t, 1)
+        assert zha.zha_route_mode(t) == 1
+        for bad in (3, -1):
+            with pytest.raises(zha.ZhaError) as e:
+                zha.zha_set_route_mode(t, bad)
+            assert e.value.status == 1
+        assert zha.zha_route_mode(t) == 1
+        zha.zha_set_route_mode(t, 2)
+        assert zha.zha_route_mode(t) == 2
+        zha.zha_set_route_mode(t, 0)
+        assert zha.zha_route_mode(t) == 2
+    finally:
+        zha.zha_destroy(t)
+    cfg = good(zha, capacity=1000, block=8, num_ref=1, levels=3)
+    t = zha.zha_create(cfg, 0x100000, zha.zha_workspace_bytes(cfg))
+    try:
+        assert zha.zha_route_mode(t) == 1
+        with pytest.raises(zha.ZhaError) as e:
+            zha.zha_set_route_mode(t, 2)
+        assert e.value.status == 2
+        assert zha.zha_route_mode(t) == 1
+    finally:
+        zha.zha_destroy(t)
+    assert zha.zha_route_mode(None) == -1
+    with pytest.raises(zha.ZhaError) as e:
+        zha.zha_set_route_mode(None, 0)
+    assert e.value.status == 1
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "fp4"])
 def test_quantised_router_planes_workspace(zha, fmt):
     """Quantised router planes add one copy of s per level the router reads planes at: every

@@ -79,8 +79,10 @@ def test_append_n_matches_rebuild(name):
     q = gen.step_queries(w, 7, n, gen.host_fetch(K))
     o = t.decode(P.upload(q, w)).cpu().numpy()
     traces = {lv: t.trace(lv) for lv in range(0, w.levels + 1)}
-    tol_fn = lambda kv, qh: (lambda lv, fr: P.SCORE_TOL + P.flip_allowance(w, trees[kv], lv, fr, qh))
-    reps = P.check_decode(P.router_trees(w, trees), K, V, q, o, traces, w.top_p, w.keep_sink, n, tol_fn=tol_fn)
+    keys = t.route_mode == 2   # every level scored from the keys: no plane copy is read
+    tol_fn = lambda kv, qh: (lambda lv, fr: P.SCORE_TOL + P.flip_allowance(w, trees[kv], lv, fr, qh, keys))
+    reps = P.check_decode(P.router_trees(w, trees, keys), K, V, q, o, traces, w.top_p, w.keep_sink, n,
+                          tol_fn=tol_fn)
     P.assert_exemption_rates(f"{name} after appends", reps)
     t.close()
 

@@ -91,6 +91,8 @@ def test_256k_end_to_end(name, planes):
     refs = gen.ref_queries(w)
     Kd, Vd = P.upload(K, w), P.upload(V, w)
     t = P.make_tree(w)
+    if planes != "f32":
+        t.set_route_mode(1)    # the union frontiers, which read the quantised plane copies
     t.build(Kd, Vd, w.n_tokens, P.upload(refs, w))
     t.append(Kd[:, w.n_tokens].contiguous(), Vd[:, w.n_tokens].contiguous())
     n = w.n_tokens + 1

@@ -32,16 +32,27 @@ SMALL = {
     "keys_b8": wc.DEEP.with_(block=8, levels=4, n_tokens=16_384 + 19, steps=2),
     "keys_b16": wc.DEEP.with_(block=16, levels=3, n_tokens=20_000 + 3, steps=2),
     "keys_b2_r2_d64": wc.DEEP.with_(block=2, num_ref=2, head_dim=64, levels=8, n_tokens=9_000 + 1, steps=2),
+    # the deep geometries again with the per-level union frontiers (their default scores every
+    # level from the keys)
+    "deep_small_frontier": wc.DEEP.with_(n_tokens=16_384 + 37, steps=3),
+    "deep_d64_r4_frontier": wc.DEEP.with_(n_tokens=10_000 + 3, head_dim=64, num_ref=4, levels=4, steps=2),
+    # every level from the keys with a top level above level 4 of more than one node and a
+    # ragged tail at every level; one with exactly four levels (no level derived above 4)
+    "keys_all_l7": wc.DEEP.with_(levels=7, n_tokens=40_000 + 13, steps=2),
+    "keys_all_r8_l4": wc.DEEP.with_(num_ref=8, levels=4, n_tokens=5_000 + 1, steps=2),
 }
+# route mode per case (0: the config's default; 1: union frontiers; 2: every level from the keys)
+ROUTE = {"deep_small_frontier": 1, "deep_d64_r4_frontier": 1}
 
 
 class Case:
-    def __init__(self, w: wc.Workload, top_p=None):
+    def __init__(self, w: wc.Workload, top_p=None, route=0):
         self.w = w
         self.p = w.top_p if top_p is None else top_p
         self.K, self.V, self.refs = P.host_inputs(w)
         self.trees = P.oracle_trees(w, self.K, self.refs, w.n_tokens)
         self.t = P.make_tree(w, top_p=self.p)
+        self.t.set_route_mode(route)
         self.Kd, self.Vd, self.Rd = P.upload(self.K, w), P.upload(self.V, w), P.upload(self.refs, w)
         self.t.build(self.Kd, self.Vd, w.n_tokens, self.Rd)
         self.n = w.n_tokens
@@ -70,8 +81,19 @@ _CACHE = {}
 def case(name) -> Case:
     if name not in _CACHE:
         _CACHE.clear()
-        _CACHE[name] = Case(SMALL[name])
+        _CACHE[name] = Case(SMALL[name], route=ROUTE.get(name, 0))
     return _CACHE[name]
+
+
+# the scoring each case's decode runs: every level from the keys on the block-4 key-form
+# geometries unless the case asks for the union frontiers
+ROUTE_EXPECT = {"deep_small": 2, "deep_d64_r4": 2, "keys_all_l7": 2, "keys_all_r8_l4": 2,
+                "deep_small_frontier": 1, "deep_d64_r4_frontier": 1, "keys_b2": 1, "wide_small": 1}
+
+
+@pytest.mark.parametrize("name", list(ROUTE_EXPECT))
+def test_route_mode_in_use(name):
+    assert case(name).t.route_mode == ROUTE_EXPECT[name]
 
 
 @pytest.mark.parametrize("name", list(SMALL))

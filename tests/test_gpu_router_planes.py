@@ -52,6 +52,7 @@ class Case:
         self.K, self.V, self.refs = P.host_inputs(w)
         self.trees = P.oracle_trees(w, self.K, self.refs, w.n_tokens)
         self.t = P.make_tree(w)
+        self.t.set_route_mode(1)   # the union frontiers, which read the quantised plane copies
         self.Kd, self.Vd = P.upload(self.K, w), P.upload(self.V, w)
         self.t.build(self.Kd, self.Vd, w.n_tokens, P.upload(self.refs, w))
         self.n = w.n_tokens
