@@ -137,9 +137,37 @@ def allkeys_upper_bytes(w, n_tokens):
     return float(per * w.num_kv_heads)
 
 
+def allkeys_select_bytes(w, stats_rows, n_tokens):
+    """Algorithmic HBM bytes of one launch of the top-down selection of the all-keys path:
+    per query head the score rows of levels 1..4 (one float per node), the level-4 dot
+    products and upper-level (c, LSE) it derives the levels above from, the upper levels'
+    scores and every level's frontier and kept bitmaps written; per KV head the gather list
+    of its kept blocks written (node id and head mask, 8 bytes a block)."""
+    L, Hq = w.levels, w.num_q_heads
+    per_head = sum(w.nodes(lv, n_tokens) * 4 for lv in range(1, AK_LC + 1))
+    per_head += sum(w.nodes(lv, n_tokens) * 4 for lv in range(AK_LC + 1, L + 1))
+    per_head += sum(2 * ((w.nodes(lv, n_tokens) + 31) // 32) * 4 for lv in range(1, L + 1))
+    return float(per_head * Hq + allkeys_upper_bytes(w, n_tokens) + stats_rows[L].sum() * 8)
+
+
+def append_bytes(w, key_form):
+    """Algorithmic HBM bytes of one single-token append: the new K and V rows written, and at
+    every level the rightmost node recomputed from its children (level 1: up to b keys, and
+    the token weights in key form; above: up to b child planes) and written."""
+    R, d, b, L = w.num_ref, w.head_dim, w.block, w.levels
+    kb = 2 if w.dtype == "bf16" else 4
+    plane = R * (d + 2) * 4                      # s, c and LSE of one node
+    per = 2 * d * kb                             # the new K and V rows
+    per += b * d * kb + plane + (R * b * 4 if key_form else 0)
+    per += (L - 1) * (b * plane + plane)
+    return float(per * w.num_kv_heads)
+
+
 def kernel_bytes(key, w, stats_rows, n_tokens, key_form):
     """Algorithmic HBM bytes of one launch of `key` given the routing stats of that step.
 
+    route_score.keys: allkeys_score_bytes; route_select.keys: allkeys_select_bytes;
+    append: append_bytes; route_prep: q in, sigma*q out and the per-level state zeroed;
     route_score.l<l>: node_bytes per union-frontier node;
     route_score.top:  node_bytes per node of every top-down level (all of them are scored);
     attend:           per gathered token 2*d*2 bytes (K and V rows, bf16); partial results
@@ -149,6 +177,13 @@ def kernel_bytes(key, w, stats_rows, n_tokens, key_form):
     d, L = w.head_dim, w.levels
     if key == "route_score.keys":
         return allkeys_score_bytes(w, n_tokens)
+    if key == "route_select.keys":
+        return allkeys_select_bytes(w, stats_rows, n_tokens)
+    if key == "append":
+        return append_bytes(w, key_form)
+    if key == "route_prep":
+        # q read (bf16), sigma*q written (fp32), per-level state zeroed
+        return float(w.num_q_heads * w.head_dim * (2 + 4) + (w.levels + 1) * w.num_q_heads * 64)
     if key.startswith("route_score.l"):
         lv = int(key.split(".l")[1])
         u = stats_rows[L - lv].sum()
@@ -873,6 +908,17 @@ def main():
                         frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_for(dominant, prof_name),
                         kernel=dominant, launches=dom_n, avg_launch_ms=round(dom_avg_ms, 4),
                         algorithmic_bytes_per_launch=round(alg))
+    # every decode kernel against the HBM roofline (per-launch times of the probe decode above,
+    # algorithmic bytes at the first timed step's routing stats), for the dominant one's context
+    kernel_roofline = {}
+    for key, ms in sorted(probe_ms.items(), key=lambda x: -x[1]):
+        if ms <= 0:
+            continue
+        kb = kernel_bytes(key, w, timed_stats[0], n0 + args.warmup + 1, key_form)
+        if kb is None:
+            continue
+        kernel_roofline[key] = {"ms": round(ms, 4), "alg_bytes": round(kb),
+                                "frac_hbm": round(kb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     log(f"[bench] timed {steps} steps: {ms_per_step:.3f} ms/step (events {gpu_ms / steps:.3f}), "
         f"{qps:.1f} queries/s; dominant {dominant} {dom_avg_ms:.4f} ms/launch")
 
@@ -1128,6 +1174,7 @@ def main():
                    "batch": 1, "layers": 1, "step": "append + decode"},
         "roofline": roofline,
         "roofline_step": roofline_step,
+        "roofline_kernels": kernel_roofline,
         "cpu_baseline": cpu,
         "cold": cold,
         "cold_after_write": cold_write,

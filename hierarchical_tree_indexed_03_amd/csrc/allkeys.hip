@@ -222,73 +222,4 @@ hipError_t launch_route_allkeys_score(const RouteArgs& a, int D, int R, hipStrea
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ gather list
-// The routed blocks of each KV head after a top-down selection that reached level 1: the
-// union over the group's heads of their kept level-1 nodes, ascending, each with the mask of
-// heads that kept it (dev.node[0], dev.mask[0], dev.cnt[0] / dev.ucnt[0]).  One workgroup per
-// KV head: per 32-node word the OR of the heads' kept words, a block-wide scan of their
-// popcounts, then every set bit written at its rank.
-constexpr int GL_THREADS = 1024;
-__global__ __launch_bounds__(GL_THREADS) void route_gather_list_kernel(RouteArgs a) {
-  constexpr int NW = GL_THREADS / 64;
-  __shared__ int32_t wsum[NW];
-  __shared__ int32_t s_base;
-  const int kv = blockIdx.x, g = a.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t n = a.nl[1];
-  const int nw = (int)((n + 31) / 32);
-  const int64_t cap0 = a.dev.ncap[0];
-  int32_t* onode = a.dev.node[0] + kv * cap0;
-  uint32_t* omask = a.dev.mask[0] + kv * cap0;
-  if (tid == 0) s_base = 0;
-  __syncthreads();
-  for (int w0 = 0; w0 < nw; w0 += GL_THREADS) {
-    const int w = w0 + tid;
-    uint32_t kw[GMAX];
-    uint32_t un = 0u;
-#pragma unroll
-    for (int gi = 0; gi < GMAX; ++gi) {
-      kw[gi] = (gi < g && w < nw) ? td_kept_words(a, 1, kv * g + gi)[w] : 0u;
-      un |= kw[gi];
-    }
-    const int c = __popc(un);
-    // block-wide exclusive scan of c
-    int inc = c;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(inc, off);
-      if (lane >= off) inc += t;
-    }
-    if (lane == 63) wsum[wave] = inc;
-    __syncthreads();
-    int before = s_base;
-    for (int v = 0; v < wave; ++v) before += wsum[v];
-    int total = 0;
-    for (int v = 0; v < NW; ++v) total += wsum[v];
-    int pos = before + inc - c;
-    while (un) {
-      const int bit = __ffs(un) - 1;
-      un &= un - 1u;
-      uint32_t mk = 0u;
-#pragma unroll
-      for (int gi = 0; gi < GMAX; ++gi) mk |= ((kw[gi] >> bit) & 1u) << gi;
-      ZHA_CHECK(a.dev, pos < cap0, CHK_EXPAND_RANGE);
-      onode[pos] = 32 * w + bit;
-      omask[pos] = mk;
-      ++pos;
-    }
-    __syncthreads();
-    if (tid == 0) s_base += total;
-    __syncthreads();
-  }
-  if (tid == 0) {
-    a.dev.cnt[kv] = s_base;
-    a.dev.ucnt[kv] = s_base;
-  }
-}
-
-hipError_t launch_route_gather_list(const RouteArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(route_gather_list_kernel, dim3((unsigned)a.hkv), dim3(GL_THREADS), 0, st, a);
-  return hipGetLastError();
-}
-
 }  // namespace zha

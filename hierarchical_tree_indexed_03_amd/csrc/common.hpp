@@ -19,13 +19,12 @@ constexpr int TD_MAX = 33792;       // nodes of a level selected top-down (32768
 constexpr int TD_WORDS = TD_MAX / 32;
 // Every level scored from the keys (block-4 trees with key-form level 1, at least 4 levels):
 // a score workgroup covers one level-4 node; the top-down selection takes level 1 from
-// global memory up to AK_N1 nodes, and keeps the dot products and scores of the levels above
-// level 4 in LDS (at most AK_DUP floats and AK_SUP scores).
+// global memory up to AK_N1 nodes, and keeps the dot products of the levels above level 4
+// in LDS (at most AK_DUP floats).
 constexpr int AK_B = 4;
 constexpr int AK_LC = 4;
 constexpr int AK_N1 = 131072;
 constexpr int AK_DUP = 12288;
-constexpr int AK_SUP = 1536;
 // the append's sibling aggregates: per level R x (D + 2) floats rounded to a multiple of 4
 // (16-byte aligned levels), (MAXL + 1) levels per KV head
 #define SIB_LEVEL(R, D) ((((R) * ((D) + 2)) + 3) & ~3)
@@ -164,6 +163,8 @@ struct Dev {
   uint32_t* kb1;            // [Hq][2][ncap[1] / 32] level-1 frontier / kept bitmaps when every level is
                             // scored from the keys (level 1 selected top-down); null otherwise
   float* kdots;             // [Hkv][ncap[4]][GMAX][R] level-4 dot products q.s_j / sqrt(d) of that path
+  uint32_t* tick;           // [Hkv] workgroups of each KV head done with that path's top-down selection
+                            // (zeroed by the prep kernel; the last one writes the gather list)
   float* sib;               // [Hkv][SIB_STRIDE] = [MAXL + 1][R][D + 2] per level: aggregate (LSE, A, s) of the
                             // rightmost node's complete children (append)
   int64_t* sibkey;          // [Hkv][MAXL + 1] first child * 256 + count it was built from; -1 none

@@ -220,7 +220,6 @@ hipError_t launch_route_td_seed(const RouteArgs& a, hipStream_t st);
 // gather list of the kept level-1 blocks per KV head.
 hipError_t launch_route_allkeys_score(const RouteArgs& a, int D, int R, hipStream_t st);
 hipError_t launch_route_topdown_keys(const RouteArgs& a, hipStream_t st);
-hipError_t launch_route_gather_list(const RouteArgs& a, hipStream_t st);
 
 hipError_t launch_attend(const AttnArgs& a, bool bf16, int D, bool dense, hipStream_t st);
 // Attention workgroups resident on the GPU at once, per KV head (one wave of workgroups).

@@ -59,6 +59,8 @@ __global__ __launch_bounds__(256) void route_prep_kernel(RouteArgs a) {
     a.dev.cnt[i] = n;
     a.dev.ucnt[i] = n;
   }
+  if (a.dev.tick)
+    for (int64_t i = tid; i < a.hkv; i += nth) a.dev.tick[i] = 0u;
 }
 
 // s_waitcnt vmcnt(n) with the export and LDS/scalar counters left free (gfx9 encoding:

@@ -290,12 +290,17 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
 
 // ------------------------------------------------------------------ every level from the keys
 // Top-down selection after route_score_allkeys_kernel scored levels 1..4 and wrote the
-// level-4 dot products.  First the levels above level 4 are derived from those (a parent's
-// D_j is its children's D_j weighted by exp(LSE_cj - LSE_j); its score max_j (D_j + c_j)),
-// held in LDS.  Then every level from a.level down to a.dense_lo is selected by the same
-// rule and fixed-point masses as the other top-down kernel, reading the scores of levels
-// 1..4 from global memory in three passes (max, coarse histogram, classification) so that
-// no per-node LDS array bounds the level size: level 1 of a deep tree has 65K nodes per head.
+// level-4 dot products.  One workgroup per query head.  First the levels above level 4 are
+// derived from those (a parent's D_j is its children's D_j weighted by exp(LSE_cj - LSE_j);
+// its score max_j (D_j + c_j)): dot products in LDS, scores to their global rows.  Then
+// every level from a.level down to a.dense_lo is selected by the same rule and fixed-point
+// masses as the other top-down kernel, reading the level's score row from global memory in
+// three passes (max, coarse histogram, classification) so that no per-node LDS array bounds
+// the level size: level 1 of a deep tree has 65K nodes per head.  In each pass a lane takes
+// four consecutive nodes (one float4, loaded only when one of them is in the frontier) of a
+// 256-node chunk per wave; the kept words come from eight lanes' nibbles.  When the
+// selection reaches level 1, the last workgroup of each KV head to finish writes the head's
+// gather list (the union of its query heads' kept blocks), so no further launch is needed.
 
 // bit i of the byte x -> bits 4i..4i+3 (a block-4 parent's kept bit -> its children's bits)
 __device__ __forceinline__ uint32_t spread4(uint32_t x) {
@@ -306,62 +311,143 @@ __device__ __forceinline__ uint32_t spread4(uint32_t x) {
 }
 
 constexpr int TK_THREADS = 1024;
+constexpr int TK_U = 6;   // 256-node chunks per wave and round of a selection pass
+
+// The routed blocks of KV head kv once every query head of its group has its level-1 kept
+// words: the union over the group's heads of their kept level-1 nodes, ascending, each with
+// the mask of heads that kept it (dev.node[0], dev.mask[0], dev.cnt[0] / dev.ucnt[0]).  Per
+// 32-node word the OR of the heads' kept words, a workgroup-wide scan of their popcounts,
+// then every set bit written at its rank.  wsum: TK_THREADS / 64 + 1 words of LDS.
+__device__ __forceinline__ void gather_list(const RouteArgs& a, int kv, uint32_t* wsum) {
+  constexpr int NW = TK_THREADS / 64;
+  const int g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t n = a.nl[1];
+  const int nw = (int)((n + 31) / 32);
+  const int64_t cap0 = a.dev.ncap[0];
+  int32_t* onode = a.dev.node[0] + kv * cap0;
+  uint32_t* omask = a.dev.mask[0] + kv * cap0;
+  uint32_t* s_base = wsum + NW;
+  if (tid == 0) *s_base = 0u;
+  __syncthreads();
+  for (int w0 = 0; w0 < nw; w0 += TK_THREADS) {
+    const int w = w0 + tid;
+    uint32_t kw[GMAX];
+    uint32_t un = 0u;
+#pragma unroll
+    for (int gi = 0; gi < GMAX; ++gi) {
+      kw[gi] = (gi < g && w < nw) ? td_kept_words(a, 1, kv * g + gi)[w] : 0u;
+      un |= kw[gi];
+    }
+    const int c = __popc(un);
+    int inc = c;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(inc, off);
+      if (lane >= off) inc += t;
+    }
+    if (lane == 63) wsum[wave] = (uint32_t)inc;
+    __syncthreads();
+    int before = (int)*s_base;
+    for (int v = 0; v < wave; ++v) before += (int)wsum[v];
+    int total = 0;
+    for (int v = 0; v < NW; ++v) total += (int)wsum[v];
+    int pos = before + inc - c;
+    while (un) {
+      const int bit = __ffs(un) - 1;
+      un &= un - 1u;
+      uint32_t mk = 0u;
+#pragma unroll
+      for (int gi = 0; gi < GMAX; ++gi) mk |= ((kw[gi] >> bit) & 1u) << gi;
+      ZHA_CHECK(a.dev, pos < cap0, CHK_EXPAND_RANGE);
+      onode[pos] = 32 * w + bit;
+      omask[pos] = mk;
+      ++pos;
+    }
+    __syncthreads();
+    if (tid == 0) *s_base += (uint32_t)total;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.dev.cnt[kv] = (int32_t)*s_base;
+    a.dev.ucnt[kv] = (int32_t)*s_base;
+  }
+}
 __global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArgs a) {
   constexpr int NW = TK_THREADS / 64;
   constexpr int KW = AK_N1 / 32;
   __shared__ uint32_t kb2[2][KW];              // kept bitmaps: level above / this level
   __shared__ uint32_t fbw[KW];                 // this level's frontier
   __shared__ __align__(16) float Dup[AK_DUP];  // dot products of the levels above level 4
-  __shared__ __align__(16) float Sup[AK_SUP];  // their scores, each level 32-aligned
   __shared__ unsigned long long h[NB1];        // coarse, then fine mass histogram, then radix digits
   __shared__ int32_t cand[TD_CAND];
   __shared__ float cand_s[TD_CAND];
   __shared__ int32_t tie_e[TD_TIES];
   __shared__ float tie_s[TD_TIES];
   __shared__ uint64_t tie_m[TD_TIES];
-  __shared__ float redm[NW];
+  __shared__ float redm[NW + 1];
   __shared__ uint32_t s_b1, s_b2, s_ncand, s_ntie;
   __shared__ uint64_t s_T, s_above1, s_above2, s_prefix, s_rabove;
   const int hq = blockIdx.x, kv = hq / a.g, gi = hq % a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = a.nref;
 
-  // ---- levels above level 4: dot products and scores
+  // ---- levels above level 4: dot products and scores.  Thread i of a pass takes item
+  // (node i / R, plane i % R); its R-lane group holds one node, whose score is the group's
+  // maximum.  All loads of a pass are issued before any is used (children past the level's
+  // end read the last child and weigh nothing).
   if (a.level > AK_LC) {
+    const int lr = __ffs(R) - 1;   // R is a power of two
     const int64_t cap4 = a.dev.ncap[AK_LC];
     const float* kd = a.dev.kdots + ((int64_t)kv * cap4 * GMAX + gi) * R;   // node c at kd + c * GMAX * R
-    int64_t dpo = 0, dco = 0, so = 0;
+    int dpo = 0, dco = 0;
     for (int lv = AK_LC + 1; lv <= a.level; ++lv) {
-      const int64_t n = a.nl[lv], nc = a.nl[lv - 1];
+      const int n = (int)a.nl[lv], nc = (int)a.nl[lv - 1];
       const int64_t capl = a.dev.ncap[lv], capc = a.dev.ncap[lv - 1];
       const float* lsep = a.dev.lse[lv] + kv * capl * R;
       const float* lsec = a.dev.lse[lv - 1] + kv * capc * R;
       const float* cp = a.dev.c[lv] + kv * capl * R;
-      for (int64_t i = tid; i < n * R; i += TK_THREADS) {
-        const int64_t node = i / R;
-        const int j = (int)(i % R);
-        const float lp = lsep[node * R + j];
-        float acc = 0.f;
-        for (int k = 0; k < AK_B; ++k) {
-          const int64_t c = node * AK_B + k;
-          if (c >= nc) break;
-          const float dc = lv - 1 == AK_LC ? kd[c * GMAX * R + j] : Dup[dpo + c * R + j];
-          acc += expf(lsec[c * R + j] - lp) * dc;
-        }
-        Dup[dco + i] = acc;
-      }
-      __syncthreads();
       float* gs = a.dev.score[lv] + ((int64_t)kv * GMAX + gi) * capl;
-      for (int64_t node = tid; node < n; node += TK_THREADS) {
-        float m = -INFINITY;
-        for (int j = 0; j < R; ++j) m = fmaxf(m, Dup[dco + node * R + j] + cp[node * R + j]);
-        Sup[so + node] = m;
-        gs[node] = m;
+      const bool from_kd = lv - 1 == AK_LC;
+      const int items = n << lr;
+      constexpr int UP = 4;
+      for (int i0 = 0; i0 < items; i0 += TK_THREADS * UP) {
+        float lp[UP], cv[UP], lc[UP][AK_B], dc[UP][AK_B];
+#pragma unroll
+        for (int u = 0; u < UP; ++u) {
+          int i = i0 + u * TK_THREADS + tid;
+          i = i < items ? i : items - 1;
+          const int node = i >> lr, j = i & (R - 1);
+          lp[u] = lsep[i];
+          cv[u] = cp[i];
+#pragma unroll
+          for (int k = 0; k < AK_B; ++k) {
+            int c = node * AK_B + k;
+            c = c < nc ? c : nc - 1;
+            lc[u][k] = lsec[(c << lr) + j];
+            // two loads under a uniform branch (a selected pointer would be a generic load)
+            if (from_kd) dc[u][k] = kd[(int64_t)c * GMAX * R + j];
+            else dc[u][k] = Dup[dpo + (c << lr) + j];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < UP; ++u) {
+          const int i = i0 + u * TK_THREADS + tid;
+          const int node = (i < items ? i : items - 1) >> lr;
+          float acc = 0.f;
+#pragma unroll
+          for (int k = 0; k < AK_B; ++k)
+            if (node * AK_B + k < nc) acc += expf(lc[u][k] - lp[u]) * dc[u][k];
+          float m = acc + cv[u];
+          for (int off = 1; off < R; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+          if (i < items) {
+            Dup[dco + i] = acc;
+            if ((i & (R - 1)) == 0) gs[node] = m;
+          }
+        }
       }
       __syncthreads();
       dpo = dco;
-      dco += n * R;
-      so += (n + 31) & ~(int64_t)31;
+      dco += items;
     }
   }
 
@@ -373,14 +459,10 @@ __global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArg
     const int nw = (int)((n + 31) >> 5);
     const bool top = lv == a.level;
     ZHA_CHECK(a.dev, nw <= KW, CHK_TD_SIZE);
-    const float* S;
-    if (lv > AK_LC) {
-      int64_t so = 0;
-      for (int m = AK_LC + 1; m < lv; ++m) so += (a.nl[m] + 31) & ~(int64_t)31;
-      S = Sup + so;
-    } else {
-      S = a.dev.score[lv] + ((int64_t)kv * GMAX + gi) * a.dev.ncap[lv];
-    }
+    // the level's scores: global rows at every level (those above level 4 were written by the
+    // pass above), so that every pass compiles to global loads, never to generic ones that
+    // would wait together with the LDS reads of the frontier bits
+    const float* S = a.dev.score[lv] + ((int64_t)kv * GMAX + gi) * a.dev.ncap[lv];
     uint32_t* gf = td_front_words(a, lv, hq);
     uint32_t* gk = td_kept_words(a, lv, hq);
     uint32_t* kc = kb2[pb ^ 1];
@@ -398,22 +480,40 @@ __global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArg
     }
     for (int i = tid; i < NB1; i += TK_THREADS) h[i] = 0ull;
     __syncthreads();
-    // ---- pass 1: the frontier's max score (a word's 32 scores as eight float4 loads)
+    // The passes below give lane l of a wave four consecutive nodes (one float4 of scores) of
+    // a 256-node chunk, TK_U chunks per wave and round with their loads issued first.  Rows
+    // of scores hold whole float4s: node capacities are multiples of 64, LDS levels 32-aligned.
+    // the frontier bits of the lane's four nodes of chunk u
+    auto front4 = [&](int64_t e0, int u) -> uint32_t {
+      const int64_t e = e0 + (int64_t)u * TK_THREADS * 4 + 4 * lane;
+      return e < n ? (fbw[e >> 5] >> (e & 31)) & 0xfu : 0u;
+    };
+    // a lane loads its four scores only when one of them is in the frontier (the others
+    // are never read)
+    auto load_chunks = [&](int64_t e0, float4 (&x)[TK_U]) {
+#pragma unroll
+      for (int u = 0; u < TK_U; ++u) {
+        const int64_t e = e0 + (int64_t)u * TK_THREADS * 4 + 4 * lane;
+        x[u] = front4(e0, u) ? *(const float4*)(S + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    constexpr int64_t ROUND = (int64_t)TK_THREADS * 4 * TK_U;   // nodes per round
+    // ---- pass 1: the frontier's max score; the frontier words out
     float mx = -INFINITY;
-    for (int w = tid; w < nw; w += TK_THREADS) {
-      const uint32_t f = fbw[w];
-      if (!f) continue;
-      float4 v[8];
+    for (int64_t e0 = 256 * wave; e0 < n; e0 += ROUND) {
+      float4 x[TK_U];
+      load_chunks(e0, x);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = *(const float4*)(S + 32 * w + 4 * k);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if ((f >> (4 * k + e)) & 1u) mx = fmaxf(mx, x[e]);
+      for (int u = 0; u < TK_U; ++u) {
+        if (e0 + (int64_t)u * TK_THREADS * 4 >= n) break;
+        const uint32_t fu = front4(e0, u);
+        mx = (fu & 1u) ? fmaxf(mx, x[u].x) : mx;
+        mx = (fu & 2u) ? fmaxf(mx, x[u].y) : mx;
+        mx = (fu & 4u) ? fmaxf(mx, x[u].z) : mx;
+        mx = (fu & 8u) ? fmaxf(mx, x[u].w) : mx;
       }
     }
+    for (int w = tid; w < nw; w += TK_THREADS) gf[w] = fbw[w];
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     if (lane == 0) redm[wave] = mx;
     __syncthreads();
@@ -429,18 +529,17 @@ __global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArg
       continue;
     }
     // ---- pass 2: coarse histogram of the fixed-point masses
-    for (int w = tid; w < nw; w += TK_THREADS) {
-      const uint32_t f = fbw[w];
-      if (!f) continue;
-      float4 v[8];
+    for (int64_t e0 = 256 * wave; e0 < n; e0 += ROUND) {
+      float4 x[TK_U];
+      load_chunks(e0, x);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = *(const float4*)(S + 32 * w + 4 * k);
+      for (int u = 0; u < TK_U; ++u) {
+        if (e0 + (int64_t)u * TK_THREADS * 4 >= n) break;
+        const uint32_t fu = front4(e0, u);
+        const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if ((f >> (4 * k + e)) & 1u) atomicAdd(&h[bin_of(x[e], M).bin], (unsigned long long)mass_of(x[e], M));
+        for (int k = 0; k < 4; ++k)
+          if ((fu >> k) & 1u) atomicAdd(&h[bin_of(xs[k], M).bin], (unsigned long long)mass_of(xs[k], M));
       }
     }
     __syncthreads();
@@ -460,35 +559,39 @@ __global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArg
     __syncthreads();
     const uint32_t b1 = s_b1;
     const uint64_t T = s_T;
-    // ---- pass 3: kept words (bins before the boundary bin), frontier words out, the
-    // boundary bin's nodes listed
-    for (int w = tid; w < nw; w += TK_THREADS) {
-      const uint32_t f = fbw[w];
-      uint32_t kw = 0u, cw = 0u;
-      if (f) {
-        float4 v[8];
+    // ---- pass 3: kept words (bins before the boundary bin), the nibbles of eight lanes
+    // to a word; the boundary bin's nodes (and scores) listed
+    for (int64_t e0 = 256 * wave; e0 < n; e0 += ROUND) {
+      float4 x[TK_U];
+      load_chunks(e0, x);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = *(const float4*)(S + 32 * w + 4 * k);
+      for (int u = 0; u < TK_U; ++u) {
+        if (e0 + (int64_t)u * TK_THREADS * 4 >= n) break;
+        const uint32_t fu = front4(e0, u);
+        const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+        uint32_t kn = 0u, cn = 0u;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t code = bin_of(xs[k], M).bin;
+          const uint32_t in = (fu >> k) & 1u;
+          kn |= (in & (code < b1 ? 1u : 0u)) << k;
+          cn |= (in & (code == b1 ? 1u : 0u)) << k;
+        }
+        const int64_t e = e0 + (int64_t)u * TK_THREADS * 4 + 4 * lane;
+        uint32_t word = kn << (4 * (lane & 7));
+        word |= __shfl_xor(word, 1);
+        word |= __shfl_xor(word, 2);
+        word |= __shfl_xor(word, 4);
+        if ((lane & 7) == 0 && e < n) kc[e >> 5] = word;
+        if (cn) {
+          uint32_t j = atomicAdd(&s_ncand, (uint32_t)__popc(cn));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t bit = 1u << (4 * k + e);
-            if (!(f & bit)) continue;
-            const uint32_t code = bin_of(x[e], M).bin;
-            if (code < b1) kw |= bit;
-            else if (code == b1) cw |= bit;
+          for (int k = 0; k < 4; ++k) {
+            if (!((cn >> k) & 1u)) continue;
+            if (j < (uint32_t)TD_CAND) { cand[j] = (int32_t)(e + k); cand_s[j] = xs[k]; }
+            ++j;
           }
         }
-      }
-      gf[w] = f;
-      kc[w] = kw;
-      while (cw) {
-        const int idx = __ffs(cw) - 1;
-        cw &= cw - 1u;
-        const uint32_t j = atomicAdd(&s_ncand, 1u);
-        if (j < (uint32_t)TD_CAND) cand[j] = 32 * w + idx;
       }
     }
     for (int i = tid; i < NB2; i += TK_THREADS) h[i] = 0ull;
@@ -508,9 +611,6 @@ __global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArg
           }
         }
       };
-      if (listed)
-        for (uint32_t i = tid; i < nc; i += TK_THREADS) cand_s[i] = S[cand[i]];
-      __syncthreads();
       for_each_cand([&](int e, float x) {
         atomicAdd(&h[bin_of(x, M).sub], (unsigned long long)mass_of(x, M));
       });
@@ -582,6 +682,20 @@ __global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArg
     pb ^= 1;
     __syncthreads();
   }
+
+  // ---- the gather list of the KV head (a decode that reached level 1), written by the last
+  // of its g workgroups to finish: each thread's kept words are made visible device-wide
+  // before the workgroup counts itself done, and the last one reads the others' after its
+  // count
+  if (a.tf || a.dense_lo != 1) return;
+  __shared__ uint32_t s_last;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&a.dev.tick[kv], 1u) == (uint32_t)(a.g - 1) ? 1u : 0u;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  gather_list(a, kv, (uint32_t*)redm);
 }
 
 hipError_t launch_route_topdown_keys(const RouteArgs& a, hipStream_t st) {

@@ -100,12 +100,9 @@ bool allkeys_possible(const zha_config& c) {
   if (nodes_at(c, 1, c.capacity) > AK_N1) return false;
   for (int l = 2; l <= c.levels; ++l)
     if (nodes_at(c, l, c.capacity) > TD_MAX) return false;
-  int64_t dup = 0, sup = 0;
-  for (int l = AK_LC + 1; l <= c.levels; ++l) {
-    dup += nodes_at(c, l, c.capacity) * c.num_ref;
-    sup += ceil_div(nodes_at(c, l, c.capacity), 32) * 32;
-  }
-  return dup <= AK_DUP && sup <= AK_SUP;
+  int64_t dup = 0;
+  for (int l = AK_LC + 1; l <= c.levels; ++l) dup += nodes_at(c, l, c.capacity) * c.num_ref;
+  return dup <= AK_DUP;
 }
 
 // Bytes one decode reads to score every level from the keys, against the other path with
@@ -211,6 +208,7 @@ size_t layout(const zha_config& c, char* base, Dev* dev) {
   if (allkeys_possible(c)) {
     d.kb1 = (uint32_t*)take((size_t)(Q * 2 * (d.ncap[1] / 32)) * 4);
     d.kdots = (float*)take((size_t)(H * d.ncap[AK_LC] * GMAX * R) * 4);
+    d.tick = (uint32_t*)take((size_t)H * 4);
   }
   d.sib = (float*)take((size_t)(H * SIB_STRIDE(R, D)) * 4);
   d.sibkey = (int64_t*)take((size_t)(H * (MAXL + 1)) * 8);
@@ -655,7 +653,8 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
   t->td_valid = false;
   if (r.allkeys) {
     // levels 1..4 and the level-4 dot products from one pass over the keys; the levels above
-    // derived and every level selected top-down; the union of the kept blocks
+    // derived and every level selected top-down; the union of the kept blocks written by the
+    // selection's last workgroup of each KV head
     r.level = c.levels;
     {
       ProfScope ps(t, "route_score.keys", stream);
@@ -667,11 +666,6 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
       e = launch_route_topdown_keys(r, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "route top-down select launch");
-    {
-      ProfScope ps(t, "route_expand.keys", stream);
-      e = launch_route_gather_list(r, stream);
-    }
-    if (e != hipSuccess) return hip_fail(e, "gather list launch");
     t->td_args = r;
     t->td_valid = true;
     t->td_lists = false;
