@@ -311,7 +311,9 @@ __device__ __forceinline__ uint32_t spread4(uint32_t x) {
 }
 
 constexpr int TK_THREADS = 1024;
-constexpr int TK_U = 6;   // 256-node chunks per wave and round of a selection pass
+constexpr int TK_U = 5;   // 256-node chunks per wave and round of a selection pass
+constexpr int TK_PL = 16384;        // kept parents listed for the level below
+constexpr int TK_LIST_MIN = 16384;  // levels above this many nodes are passed over by parent
 
 // The routed blocks of KV head kv once every query head of its group has its level-1 kept
 // words: the union over the group's heads of their kept level-1 nodes, ascending, each with
@@ -386,10 +388,16 @@ __global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArg
   __shared__ uint64_t tie_m[TD_TIES];
   __shared__ float redm[NW + 1];
   __shared__ uint32_t s_b1, s_b2, s_ncand, s_ntie;
+  // the kept nodes of the level above, ascending, when the level below is large (its frontier
+  // is their children, four each: the passes then take one kept parent per lane instead of
+  // every node slot); s_np > TK_PL: not listed
+  __shared__ uint16_t plist[TK_PL];
+  __shared__ uint32_t s_np, s_lbase;
   __shared__ uint64_t s_T, s_above1, s_above2, s_prefix, s_rabove;
   const int hq = blockIdx.x, kv = hq / a.g, gi = hq % a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = a.nref;
+  if (tid == 0) s_np = TK_PL + 1;
 
   // ---- levels above level 4: dot products and scores.  Thread i of a pass takes item
   // (node i / R, plane i % R); its R-lane group holds one node, whose score is the group's
@@ -467,8 +475,10 @@ __global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArg
     uint32_t* gk = td_kept_words(a, lv, hq);
     uint32_t* kc = kb2[pb ^ 1];
     const uint32_t* kp = kb2[pb];
+    const uint32_t np = s_np;
+    const bool lst = !top && !empty && np <= (uint32_t)TK_PL;   // kept parents listed
     // ---- the frontier: every node at the top (or the given frontier), else the children of
-    // the kept nodes one level up
+    // the kept nodes one level up (list mode: this level's kept words start clear)
     for (int w = tid; w < nw; w += TK_THREADS) {
       uint32_t f;
       if (empty) f = 0u;
@@ -477,6 +487,7 @@ __global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArg
       const int64_t rem = n - 32 * (int64_t)w;
       if (rem < 32) f &= (1u << rem) - 1u;
       fbw[w] = f;
+      if (lst) kc[w] = 0u;
     }
     for (int i = tid; i < NB1; i += TK_THREADS) h[i] = 0ull;
     __syncthreads();
@@ -498,9 +509,32 @@ __global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArg
       }
     };
     constexpr int64_t ROUND = (int64_t)TK_THREADS * 4 * TK_U;   // nodes per round
+    // list mode: thread t takes listed parents t, t + TK_THREADS, ...; the float4 of its four
+    // children (all in the frontier; those at or past n are not nodes)
+    auto load_listed = [&](int i0, float4 (&x)[TK_U]) {
+#pragma unroll
+      for (int u = 0; u < TK_U; ++u) {
+        const int i = i0 + u * TK_THREADS + tid;
+        x[u] = *(const float4*)(S + 4 * (int64_t)plist[i < (int)np ? i : (int)np - 1]);
+      }
+    };
     // ---- pass 1: the frontier's max score; the frontier words out
     float mx = -INFINITY;
-    for (int64_t e0 = 256 * wave; e0 < n; e0 += ROUND) {
+    if (lst) {
+      for (int i0 = 0; i0 < (int)np; i0 += TK_THREADS * TK_U) {
+        float4 x[TK_U];
+        load_listed(i0, x);
+#pragma unroll
+        for (int u = 0; u < TK_U; ++u) {
+          const int i = i0 + u * TK_THREADS + tid;
+          if (i >= (int)np) break;
+          const int64_t e = 4 * (int64_t)plist[i];
+          const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) mx = e + k < n ? fmaxf(mx, xs[k]) : mx;
+        }
+      }
+    } else for (int64_t e0 = 256 * wave; e0 < n; e0 += ROUND) {
       float4 x[TK_U];
       load_chunks(e0, x);
 #pragma unroll
@@ -529,7 +563,22 @@ __global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArg
       continue;
     }
     // ---- pass 2: coarse histogram of the fixed-point masses
-    for (int64_t e0 = 256 * wave; e0 < n; e0 += ROUND) {
+    if (lst) {
+      for (int i0 = 0; i0 < (int)np; i0 += TK_THREADS * TK_U) {
+        float4 x[TK_U];
+        load_listed(i0, x);
+#pragma unroll
+        for (int u = 0; u < TK_U; ++u) {
+          const int i = i0 + u * TK_THREADS + tid;
+          if (i >= (int)np) break;
+          const int64_t e = 4 * (int64_t)plist[i];
+          const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (e + k < n) atomicAdd(&h[bin_of(xs[k], M).bin], (unsigned long long)mass_of(xs[k], M));
+        }
+      }
+    } else for (int64_t e0 = 256 * wave; e0 < n; e0 += ROUND) {
       float4 x[TK_U];
       load_chunks(e0, x);
 #pragma unroll
@@ -560,8 +609,39 @@ __global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArg
     const uint32_t b1 = s_b1;
     const uint64_t T = s_T;
     // ---- pass 3: kept words (bins before the boundary bin), the nibbles of eight lanes
-    // to a word; the boundary bin's nodes (and scores) listed
-    for (int64_t e0 = 256 * wave; e0 < n; e0 += ROUND) {
+    // to a word (list mode: each parent's nibble OR-ed in); the boundary bin's nodes (and
+    // scores) listed
+    if (lst) {
+      for (int i0 = 0; i0 < (int)np; i0 += TK_THREADS * TK_U) {
+        float4 x[TK_U];
+        load_listed(i0, x);
+#pragma unroll
+        for (int u = 0; u < TK_U; ++u) {
+          const int i = i0 + u * TK_THREADS + tid;
+          if (i >= (int)np) break;
+          const int64_t e = 4 * (int64_t)plist[i];
+          const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+          uint32_t kn = 0u, cn = 0u;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t code = bin_of(xs[k], M).bin;
+            const uint32_t in = e + k < n ? 1u : 0u;
+            kn |= (in & (code < b1 ? 1u : 0u)) << k;
+            cn |= (in & (code == b1 ? 1u : 0u)) << k;
+          }
+          if (kn) atomicOr(&kc[e >> 5], kn << (e & 31));
+          if (cn) {
+            uint32_t j = atomicAdd(&s_ncand, (uint32_t)__popc(cn));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              if (!((cn >> k) & 1u)) continue;
+              if (j < (uint32_t)TD_CAND) { cand[j] = (int32_t)(e + k); cand_s[j] = xs[k]; }
+              ++j;
+            }
+          }
+        }
+      }
+    } else for (int64_t e0 = 256 * wave; e0 < n; e0 += ROUND) {
       float4 x[TK_U];
       load_chunks(e0, x);
 #pragma unroll
@@ -680,6 +760,44 @@ __global__ __launch_bounds__(TK_THREADS) void route_topdown_keys_kernel(RouteArg
     }
     for (int w = tid; w < nw; w += TK_THREADS) gk[w] = kc[w];
     pb ^= 1;
+    __syncthreads();
+    // ---- the kept nodes listed for a large level below (ascending: per 32-node word the
+    // popcounts scanned across the workgroup, then each set bit written at its rank)
+    if (lv - 1 >= a.dense_lo && a.nl[lv - 1] > TK_LIST_MIN) {
+      uint32_t* wsum = (uint32_t*)redm;
+      if (tid == 0) s_lbase = 0u;
+      __syncthreads();
+      for (int w0 = 0; w0 < nw; w0 += TK_THREADS) {
+        const int w = w0 + tid;
+        uint32_t word = w < nw ? kb2[pb][w] : 0u;
+        const int c = __popc(word);
+        int inc = c;
+        for (int off = 1; off < 64; off <<= 1) {
+          const int t = __shfl_up(inc, off);
+          if (lane >= off) inc += t;
+        }
+        if (lane == 63) wsum[wave] = (uint32_t)inc;
+        __syncthreads();
+        int pos = (int)s_lbase, total = 0;
+        for (int v = 0; v < NW; ++v) {
+          if (v < wave) pos += (int)wsum[v];
+          total += (int)wsum[v];
+        }
+        pos += inc - c;
+        while (word) {
+          const int bit = __ffs(word) - 1;
+          word &= word - 1u;
+          if (pos < TK_PL) plist[pos] = (uint16_t)(32 * w + bit);
+          ++pos;
+        }
+        __syncthreads();
+        if (tid == 0) s_lbase += (uint32_t)total;
+        __syncthreads();
+      }
+      if (tid == 0) s_np = s_lbase <= (uint32_t)TK_PL ? s_lbase : (uint32_t)TK_PL + 1u;
+    } else if (tid == 0) {
+      s_np = TK_PL + 1;
+    }
     __syncthreads();
   }
 

@@ -38,6 +38,8 @@ KERNEL_SRC = {
     "route_expand": ["expand.hip"],
     "attend": ["attend.hip"],
     "dense_attend": ["attend.hip"],
+    "route_score.keys": ["allkeys.hip"],
+    "route_select.keys": ["topdown.hip"],
     "append": ["build.hip"],
     "build": ["build.hip"],
 }
@@ -46,7 +48,7 @@ CALIB_BYTES = 1 << 30
 
 def kernel_sha(key: str) -> str:
     """Hash of the sources that define the kernels behind a profile key (plus shared headers)."""
-    files = KERNEL_SRC.get(key.split(".")[0])
+    files = KERNEL_SRC.get(key) or KERNEL_SRC.get(key.split(".")[0])
     if files is None:
         files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp")))
     h = hashlib.sha256()
@@ -103,7 +105,11 @@ def label(dec):
             continue
         if n in SCORES:
             lv = f"l{len(general) - general.index(i)}"
-        if n == "route_topdown_kernel":
+        if n == "route_score_allkeys_kernel":
+            res.append(("score.keys", r))
+        elif n == "route_topdown_keys_kernel":
+            res.append(("select.keys", r))
+        elif n == "route_topdown_kernel":
             res.append(("select.top", r))
         elif n == "route_topdown_union_kernel":
             res.append(("union.top", r))
@@ -253,7 +259,7 @@ def cmd_pmc(a):
                                              "fetch_scale": kf, "write_scale": kw},
            "command": a.cmd, "kernels": {}}
     keymap = {"score.top": "route_score.top", "score.l1": "route_score.l1", "score.l2": "route_score.l2",
-              "attend": "attend"}
+              "score.keys": "route_score.keys", "select.keys": "route_select.keys", "attend": "attend"}
     for lab, key in keymap.items():
         fv, wv = fper.get(lab), wper.get(lab)
         if fv and wv:
