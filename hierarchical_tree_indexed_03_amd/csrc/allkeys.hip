@@ -43,7 +43,7 @@ __device__ __forceinline__ void rows_transpose4(float (&v)[4]) {
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *(const f32x4*)p; }
 
 template <int D, int R>
-__global__ __launch_bounds__(256) void route_score_allkeys_kernel(RouteArgs a) {
+__global__ __launch_bounds__(256, 4) void route_score_allkeys_kernel(RouteArgs a) {
   static_assert(R % 4 == 0 && R <= 16, "planes in whole lane rows");
   constexpr int B = AK_B;
   constexpr int NK = Qk<bf16_t, D>::NL;
@@ -65,6 +65,18 @@ __global__ __launch_bounds__(256) void route_score_allkeys_kernel(RouteArgs a) {
   const float sigma = a.sigma;
   const bool rowv = kg < NV;                     // this lane row holds real planes
   const int pr = 4 * (rowv ? kg : NV - 1);       // first plane of the lane row (clamped)
+
+  // the route prep of this path: every level's list size (the whole level; level 0, the
+  // gather list, is written by the selection) and the selection's arrival counts cleared
+  if (a.prep_fold && u == 0 && kv == 0) {
+    for (int i = threadIdx.x; i < (MAXL + 1) * a.hkv; i += blockDim.x) {
+      const int lv = i / a.hkv;
+      const int32_t n = (lv >= 1 && lv <= a.levels) ? (int32_t)a.nl[lv] : 0;
+      a.dev.cnt[i] = n;
+      a.dev.ucnt[i] = n;
+    }
+    for (int i = threadIdx.x; i < a.hkv; i += blockDim.x) a.dev.tick[i] = 0u;
+  }
 
   Qk<bf16_t, D> qk;
   qk.load_q((const bf16_t*)a.q + (int64_t)kv * g * D, g, col, kg);

@@ -66,6 +66,8 @@ struct RouteArgs {
   int32_t nref;       // reference queries (planes per node)
   int32_t allkeys;    // every level scored from the keys (route_score_allkeys_kernel) and
                       // selected top-down with level 1 (route_topdown_keys_kernel)
+  int32_t prep_fold;  // route_score_allkeys_kernel also does the route prep's part of that path
+                      // (list sizes, arrival counts): the decode then launches no prep kernel
   int32_t q_bf16;     // q (and the caches) are bf16; else fp32
   int32_t planes;     // router planes read: 0 fp32 (dev.s), 1 bf16 (dev.sq), 2 MX FP4 (dev.s4, dev.s4x)
   const void* K;      // key cache [Hkv][kcap][D] (key-form scoring)

@@ -644,14 +644,17 @@ zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats, hi
   // when all are scored from the keys)
   const int lo = r.allkeys ? 1 : topdown_lo(r);
   r.dense_lo = lo <= c.levels ? lo : 0;   // prep sets the list sizes of those levels
-  hipError_t e;
-  {
+  hipError_t e = hipSuccess;
+  if (!r.allkeys) {
     ProfScope ps(t, "route_prep", stream);
     e = launch_route_prep(r, c.dtype == ZHA_BF16, c.head_dim, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "route prep launch");
   t->td_valid = false;
   if (r.allkeys) {
+    // (no prep launch: the score kernel's first workgroup sets the list sizes and clears the
+    // selection's arrival counts; nothing else of the prep is read on this path)
+    r.prep_fold = 1;
     // levels 1..4 and the level-4 dot products from one pass over the keys; the levels above
     // derived and every level selected top-down; the union of the kept blocks written by the
     // selection's last workgroup of each KV head
