@@ -75,11 +75,12 @@ SCORES = ("route_score_kernel", "route_score_keys_kernel", "route_score_bf16_ker
 
 
 def decodes(rows):
-    """Splits time-ordered dispatches into decodes: lists from route_prep to combine."""
+    """Splits time-ordered dispatches into decodes: lists from route_prep (or, on the keys
+    route, which launches no prep, from its scoring) to combine."""
     out, cur = [], None
     for r in rows:
         n = short(r["name"])
-        if n.startswith("route_prep_kernel"):
+        if n.startswith("route_prep_kernel") or (n.startswith("route_score_allkeys_kernel") and cur is None):
             cur = [r]
         elif cur is not None:
             cur.append(r)
@@ -151,7 +152,7 @@ def cmd_trace(a):
              "Summarised with:", "", "```",
              f"python -m hierarchical_tree_indexed_03_amd.prof_summary trace {a.dir} {a.workload} --cmd '...'",
              "```", "",
-             f"{len(decs)} routed decodes; decode span (route_prep start to combine end) "
+             f"{len(decs)} routed decodes; decode span (first routing launch start to combine end) "
              f"avg {sum(step_us) / max(1, len(step_us)):.1f} us.  Per-level kernels are numbered from level 1 "
              "(the last general level of each decode).", "",
              "| launch | calls | avg us | min us | max us | share of decode |", "|---|---:|---:|---:|---:|---:|"]
