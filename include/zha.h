@@ -190,6 +190,8 @@ zha_status zha_fit_step(zha_tree* t, void* k_cache, void* v_cache, int64_t n_tok
  *   stats  (device, nullable) int32 [levels + 1][Hkv]: row i < levels holds the size of
  *          the union (over the group's query heads) of the frontier scored at level
  *          levels - i; the last row holds the number of kept level-1 blocks (union).
+ *          On the keys route (zha_route_mode 2) every node of every level is scored, so
+ *          rows i < levels hold the level sizes.
  * Routing state stays on the device; nothing is read back to the host. */
 zha_status zha_decode(zha_tree* t, const void* q, float* out, int32_t* stats,
                       hipStream_t stream);
