@@ -298,9 +298,13 @@ __global__ __launch_bounds__(TD_THREADS) void route_topdown_kernel(RouteArgs a) 
 // three passes (max, coarse histogram, classification) so that no per-node LDS array bounds
 // the level size: level 1 of a deep tree has 65K nodes per head.  In each pass a lane takes
 // four consecutive nodes (one float4, loaded only when one of them is in the frontier) of a
-// 256-node chunk per wave; the kept words come from eight lanes' nibbles.  When the
-// selection reaches level 1, the last workgroup of each KV head to finish writes the head's
-// gather list (the union of its query heads' kept blocks), so no further launch is needed.
+// 256-node chunk per wave; the kept words come from eight lanes' nibbles.  A level of more
+// than TK_LIST_MIN nodes is passed over by kept parent instead: the level above lists its
+// kept nodes in LDS (ascending, uint16), and a thread takes one parent and the float4 of its
+// four children, all of them frontier nodes, so no lane works on a node outside the
+// frontier.  When the selection reaches level 1, the last workgroup of each KV head to
+// finish writes the head's gather list (the union of its query heads' kept blocks), so no
+// further launch is needed.
 
 // bit i of the byte x -> bits 4i..4i+3 (a block-4 parent's kept bit -> its children's bits)
 __device__ __forceinline__ uint32_t spread4(uint32_t x) {
