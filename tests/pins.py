@@ -85,6 +85,36 @@ def check_recursion_direct(seed=2):
     return worst < 1e-10, f"max |recursive - direct| = {worst:.3e}"
 
 
+# R20: every node's router score follows from the keys upwards.  With D_j = sigma q.s_j, a
+# level-1 node's D_j is its keys' sigma q.k_t weighted by exp(sigma r_j.k_t - LSE_j), and a
+# parent's is its children's D_j weighted by exp(LSE_cj - LSE_j); max_j (D_j + c_j) is then
+# the plane score at every level.  (LSE_j is recovered from the planes as c_j + sigma r_j.s_j.)
+def check_scores_from_keys(seed=21):
+    rng = np.random.default_rng(seed)
+    tree, keys, refs = rand_tree(rng, n=1001, d=8, r=4, b=4, levels=4)
+    sig = 1.0 / math.sqrt(keys.shape[1])
+    q = rng.standard_normal(keys.shape[1]) * 2.0
+    worst = 0.0
+    d_below = lse_below = None
+    for lv in range(1, tree.n_levels + 1):
+        s, c = tree.levels[lv - 1]
+        lse = c + sig * np.einsum("njd,jd->nj", s, refs)
+        nn = tree.nodes(lv)
+        dots = np.zeros((nn, refs.shape[0]))
+        for n in range(nn):
+            if lv == 1:
+                toks = span(tree, 1, n)
+                w = np.exp(sig * keys[toks] @ refs.T - lse[n])            # [tokens, R]
+                dots[n] = w.T @ (sig * keys[toks] @ q)
+            else:
+                ch = np.arange(n * tree.block, min((n + 1) * tree.block, tree.nodes(lv - 1)))
+                dots[n] = np.sum(np.exp(lse_below[ch] - lse[n]) * d_below[ch], axis=0)
+        score = np.max(dots + c, axis=1)
+        worst = max(worst, np.max(np.abs(score - zo.node_scores(tree, lv, np.arange(nn), q))))
+        d_below, lse_below = dots, lse
+    return worst < 1e-9, f"max |score from the keys - plane score| = {worst:.3e}"
+
+
 # P5: single-key nodes are exact: s_j = k, c_j = 0, score = sigma q.k.
 def check_single_key(seed=3):
     rng = np.random.default_rng(seed)
@@ -511,6 +541,7 @@ def check_fit_single_key(seed=19):
 
 
 ALL = [check_dense_limit, check_dense_decode, check_convexity, check_exact_at_refs, check_recursion_direct,
+       check_scores_from_keys,
        check_single_key, check_nucleus, check_minimal, check_mass_conservation, check_append,
        check_masked_attention, check_sink, check_bf16_round_library, check_bf16_round_nearest,
        check_quantised_planes, check_p_schedule, check_mxfp4_round, check_fp4_planes,
